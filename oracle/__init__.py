@@ -1,0 +1,238 @@
+"""CPU oracle of the LittleBit linear layer forward (fp64).
+
+TEST INFRASTRUCTURE ONLY: only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package.  The product path (the HIP library
+and its Python binding) never imports it, and it never imports them.
+
+Two independent formulations live here:
+
+* the factorised forward, in plain C (lb_oracle.c, built with gcc), in the
+  order of Proposition 1 on the sesamedisk page ("What the method actually
+  computes"): scale by g, contract with sign(V), scale by l, contract with
+  sign(U), scale by h, sum the residual path;
+* the dense reconstruction W = sum_p diag(h_p) sign(U_p) diag(l_p)
+  sign(V_p)^T diag(g_p) (the same proposition read as one matrix), in numpy,
+  used to pin the factorised C code on small shapes.
+
+Inputs are widened to fp64 exactly (fp16 scales, bf16 or fp32 activations).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "lb_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liblb_oracle.so")
+_lib = None
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_fp = ctypes.POINTER(ctypes.c_float)
+_u32p = ctypes.POINTER(ctypes.c_uint32)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_i64 = ctypes.c_int64
+
+
+def build(force: bool = False) -> str:
+    """Compile lb_oracle.c with gcc (OpenMP) into liblb_oracle.so."""
+    if force or not os.path.exists(_LIB_PATH) or \
+            os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(_LIB_PATH)
+        L.oracle_rank_for_budget.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, _i64p, _i64p]
+        L.oracle_rank_for_budget.restype = ctypes.c_int
+        L.oracle_pack_signs.argtypes = [_fp, _i64, _i64, ctypes.c_int, _u32p, _i64]
+        L.oracle_pack_signs.restype = None
+        L.oracle_unpack_signs.argtypes = [_u32p, _i64, _i64, ctypes.c_int, _i64, _dp]
+        L.oracle_unpack_signs.restype = None
+        L.oracle_linear_forward.argtypes = [_dp, _i64, _i64, _i64, _i64, ctypes.c_int,
+                                            _fp, _fp, _dp, _dp, _dp, _dp, ctypes.c_int]
+        L.oracle_linear_forward.restype = None
+        L.oracle_linear_forward_rows.argtypes = [_dp, _i64, _i64, _i64, _i64, ctypes.c_int,
+                                                 _fp, _fp, _dp, _dp, _dp, _i64p, _i64, _dp,
+                                                 ctypes.c_int]
+        L.oracle_linear_forward_rows.restype = None
+        L.oracle_mlp_forward.argtypes = ([_dp, _i64, _i64, _i64, ctypes.c_int, _i64, _i64]
+                                         + [_fp, _fp, _dp, _dp, _dp] * 3 + [_dp, ctypes.c_int])
+        L.oracle_mlp_forward.restype = None
+        L.oracle_silu.argtypes = [ctypes.c_double]
+        L.oracle_silu.restype = ctypes.c_double
+        L.oracle_max_threads.argtypes = []
+        L.oracle_max_threads.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray, typ):
+    return a.ctypes.data_as(typ)
+
+
+# ----------------------------------------------------------------------------
+# exact widening of the storage types to fp64
+# ----------------------------------------------------------------------------
+
+def widen_f16(bits: np.ndarray) -> np.ndarray:
+    """fp16 bit patterns (uint16) -> fp64, exactly."""
+    return np.ascontiguousarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def widen_bf16(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> fp64, exactly (bf16 is the top half of fp32)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def widen_x(x: np.ndarray) -> np.ndarray:
+    if x.dtype == np.uint16:
+        return widen_bf16(x)
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+# ----------------------------------------------------------------------------
+# rank rule and packing
+# ----------------------------------------------------------------------------
+
+def rank_for_budget(d_in: int, d_out: int, b_num: int, b_den: int, residual: bool):
+    """(r_total, r_path) from the bit budget b = b_num / b_den, exact integers."""
+    r = ctypes.c_int64()
+    rp = ctypes.c_int64()
+    rc = lib().oracle_rank_for_budget(d_in, d_out, b_num, b_den, int(residual),
+                                      ctypes.byref(r), ctypes.byref(rp))
+    if rc != 0:
+        raise ValueError("rank rounds to zero for this budget")
+    return r.value, rp.value
+
+
+def pack_signs(src: np.ndarray, axis: int, ld: Optional[int] = None) -> np.ndarray:
+    """Packed sign words of src (float32 [rows][cols]); see lb_oracle.c."""
+    src = np.ascontiguousarray(src, dtype=np.float32)
+    rows, cols = src.shape
+    n_pack, n_other = (rows, cols) if axis == 0 else (cols, rows)
+    ld = n_other if ld is None else ld
+    assert ld >= n_other
+    out = np.empty(((n_pack + 31) // 32, ld), np.uint32)
+    lib().oracle_pack_signs(_ptr(src, _fp), rows, cols, axis, _ptr(out, _u32p), ld)
+    return out
+
+
+def unpack_signs(words: np.ndarray, rows: int, cols: int, axis: int) -> np.ndarray:
+    words = np.ascontiguousarray(words, dtype=np.uint32)
+    out = np.empty((rows, cols), np.float64)
+    lib().oracle_unpack_signs(_ptr(words, _u32p), rows, cols, axis, words.shape[1],
+                              _ptr(out, _dp))
+    return out
+
+
+# ----------------------------------------------------------------------------
+# forward
+# ----------------------------------------------------------------------------
+
+def linear_forward(x: np.ndarray, U: np.ndarray, V: np.ndarray, h: np.ndarray,
+                   g: np.ndarray, l: np.ndarray, nthreads: int = 0) -> np.ndarray:
+    """Factorised forward (C).  x: fp32 [T][d_in] or bf16 bits; U [P][d_out][r_p],
+    V [P][d_in][r_p] float32; h, g, l fp16 bits [P][*] (or float64 arrays)."""
+    xd = widen_x(x)
+    T, d_in = xd.shape
+    P, d_out, r_p = U.shape
+    assert V.shape == (P, d_in, r_p)
+    U = np.ascontiguousarray(U, dtype=np.float32)
+    V = np.ascontiguousarray(V, dtype=np.float32)
+    hd, gd, ldd = (_scale64(s) for s in (h, g, l))
+    y = np.empty((T, d_out), np.float64)
+    lib().oracle_linear_forward(_ptr(xd, _dp), T, d_in, d_out, r_p, P,
+                                _ptr(U, _fp), _ptr(V, _fp), _ptr(hd, _dp), _ptr(gd, _dp),
+                                _ptr(ldd, _dp), _ptr(y, _dp), nthreads)
+    return y
+
+
+def linear_forward_rows(x: np.ndarray, U, V, h, g, l, rows: Sequence[int],
+                        nthreads: int = 0) -> np.ndarray:
+    """Output rows `rows` (indices into d_out) of the factorised forward: [T][len(rows)]."""
+    xd = widen_x(x)
+    T, d_in = xd.shape
+    P, d_out, r_p = U.shape
+    U = np.ascontiguousarray(U, dtype=np.float32)
+    V = np.ascontiguousarray(V, dtype=np.float32)
+    hd, gd, ldd = (_scale64(s) for s in (h, g, l))
+    idx = np.ascontiguousarray(rows, dtype=np.int64)
+    y = np.empty((T, len(idx)), np.float64)
+    lib().oracle_linear_forward_rows(_ptr(xd, _dp), T, d_in, d_out, r_p, P,
+                                     _ptr(U, _fp), _ptr(V, _fp), _ptr(hd, _dp), _ptr(gd, _dp),
+                                     _ptr(ldd, _dp), _ptr(idx, _i64p), len(idx), _ptr(y, _dp),
+                                     nthreads)
+    return y
+
+
+def mlp_forward(x: np.ndarray, gate, up, down, nthreads: int = 0) -> np.ndarray:
+    """SwiGLU block y = down(silu(gate(x)) * up(x)).  gate/up/down are objects
+    with U, V, h, g, l attributes (see synth.LayerInputs)."""
+    xd = widen_x(x)
+    T, d_model = xd.shape
+    P, d_ff, r_gu = gate.U.shape
+    r_dn = down.U.shape[2]
+    arrays = []
+    for f in (gate, up, down):
+        arrays += [np.ascontiguousarray(f.U, np.float32), np.ascontiguousarray(f.V, np.float32)]
+        arrays += [_scale64(s) for s in (f.h, f.g, f.l)]
+    ptrs = [_ptr(a, _fp if a.dtype == np.float32 else _dp) for a in arrays]
+    y = np.empty((T, d_model), np.float64)
+    lib().oracle_mlp_forward(_ptr(xd, _dp), T, d_model, d_ff, P, r_gu, r_dn, *ptrs,
+                             _ptr(y, _dp), nthreads)
+    return y
+
+
+def _scale64(s: np.ndarray) -> np.ndarray:
+    if s.dtype == np.uint16:
+        return widen_f16(s)
+    return np.ascontiguousarray(s, dtype=np.float64)
+
+
+def silu(z: float) -> float:
+    return lib().oracle_silu(z)
+
+
+def max_threads() -> int:
+    return lib().oracle_max_threads()
+
+
+# ----------------------------------------------------------------------------
+# dense reconstruction (numpy, fp64) -- the second formulation
+# ----------------------------------------------------------------------------
+
+def dense_weight(U: np.ndarray, V: np.ndarray, h, g, l) -> np.ndarray:
+    """W [d_out][d_in] = sum_p diag(h_p) S_Up diag(l_p) S_Vp^T diag(g_p)."""
+    P, d_out, r_p = U.shape
+    d_in = V.shape[1]
+    hd, gd, ldd = (_scale64(s).reshape(P, -1) for s in (h, g, l))
+    W = np.zeros((d_out, d_in), np.float64)
+    for p in range(P):
+        SU = np.where(U[p] < 0, -1.0, 1.0)
+        SV = np.where(V[p] < 0, -1.0, 1.0)
+        W += (hd[p][:, None] * SU) @ (ldd[p][:, None] * SV.T) * gd[p][None, :]
+    return W
+
+
+def dense_forward(x: np.ndarray, U, V, h, g, l) -> np.ndarray:
+    return widen_x(x) @ dense_weight(U, V, h, g, l).T
+
+
+def rel_l2(got: np.ndarray, ref: np.ndarray) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.linalg.norm(ref.ravel())
+    num = np.linalg.norm((got - ref).ravel())
+    return float(num / den) if den > 0 else float(num)

@@ -1,0 +1,366 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+None of these tests uses a GPU.  Each pin is something other than the oracle's
+own formula: numbers printed on the pages, closed forms (Walsh/Hadamard, the
+all-plus-one rank-1 case), a second formulation (the dense weight), brute force
+over every sign pattern of a tiny layer, and exact invariants.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _pages():
+    with open(os.path.join(GOLD, "page_numbers.json")) as f:
+        return json.load(f)
+
+
+# ----------------------------------------------------------------------------
+# rank rule and bit accounting
+# ----------------------------------------------------------------------------
+
+def test_rank_kv_cache_pin():
+    """sesamedisk, 'The real result': k/v cache the latent state, up to 21.3x
+    smaller on Llama2-7B (d = 4096) at 0.1 bpw.  21.3 = 4096 / 192 only if the
+    rank rule rounds floor(204.8) = 204 down to 192 (a multiple of 32)."""
+    pages = _pages()["kv_cache_reduction_llama2_7b"]
+    r, rp = oracle.rank_for_budget(4096, 4096, 1, 10, True)
+    assert r == 192 and rp == 96
+    assert round(4096 / r, 1) == pages["value"]
+
+
+def test_rank_budget_ratio_pin():
+    """littlebitllm hero: 0.55 bits per weight, linear layers ~29x smaller than
+    BF16.  On a square 5120 layer the rule lands exactly on the budget."""
+    r, _ = oracle.rank_for_budget(5120, 5120, 55, 100, True)
+    bpw = r * (5120 + 5120) / (5120 * 5120)
+    assert bpw == pytest.approx(0.55, abs=0)
+    assert round(16 / bpw) == _pages()["linear_layers_vs_bf16_at_0p55_bpw"]["value"]
+
+
+@pytest.mark.parametrize("d_in,d_out,bn,bd,res,r,rp", [
+    (1024, 1024, 1, 1, False, 512, 512),
+    (1024, 3072, 55, 100, True, 416, 208),
+    (3072, 1024, 55, 100, True, 416, 208),
+    (4096, 4096, 1, 1, True, 2048, 1024),
+    (4096, 11008, 1, 1, True, 2976, 1488),
+    (5120, 5120, 55, 100, True, 1408, 704),
+    (5120, 1024, 55, 100, True, 448, 224),
+    (5120, 17408, 55, 100, True, 2176, 1088),   # exactly 2176: a float evaluation can land on 2175.99...
+    (8192, 8192, 1, 10, True, 384, 192),
+    (8192, 1024, 1, 10, True, 64, 32),
+    (8192, 28672, 1, 10, True, 608, 304),
+])
+def test_rank_table(d_in, d_out, bn, bd, res, r, rp):
+    """Hand-computed with exact fractions: floor(b*d_in*d_out/(d_in+d_out)),
+    then down to a multiple of 32; half per path with the residual."""
+    assert oracle.rank_for_budget(d_in, d_out, bn, bd, res) == (r, rp)
+
+
+def test_rank_rejects_zero():
+    with pytest.raises(ValueError):
+        oracle.rank_for_budget(64, 64, 1, 10, False)   # floor(3.2) = 3 -> 0
+
+
+def _model_gb(dims, bn, bd):
+    """Bytes of a Llama-2-shaped model with LittleBit linears: packed sign bits
+    of both paths, fp16 scales (h, g, l per path), BF16 embeddings and lm_head,
+    fp16 norms.  Decimal GB."""
+    d, ff, L, kv, vocab = dims["d"], dims["ff"], dims["layers"], dims["kv"], dims["vocab"]
+    shapes = [(d, d), (d, kv), (d, kv), (d, d), (d, ff), (d, ff), (ff, d)]
+    total = 0
+    for (din, dout) in shapes:
+        r, rp = oracle.rank_for_budget(din, dout, bn, bd, True)
+        total += r * (din + dout) / 8            # sign bits, both paths
+        total += 2 * 2 * (din + dout + rp)       # fp16 scales, both paths
+    total *= L
+    total += 2 * vocab * d * 2                   # embeddings + lm_head, BF16
+    total += (2 * L + 1) * d * 2                 # norms
+    return total / 1e9
+
+
+def _fp16_gb(dims):
+    d, ff, L, kv, vocab = dims["d"], dims["ff"], dims["layers"], dims["kv"], dims["vocab"]
+    per_layer = 2 * d * d + 2 * d * kv + 3 * d * ff
+    return (L * per_layer + 2 * vocab * d + (2 * L + 1) * d) * 2 / 1e9
+
+
+@pytest.mark.parametrize("model", ["llama2_7b", "llama2_13b", "llama2_70b"])
+def test_model_size_pin(model):
+    """sesamedisk, 'The real result': at 0.1 bpw Llama2-7B/13B/70B shrink to
+    0.63/0.84/1.98 GB (13.49/26.06/138 GB in FP16).  The accounting here
+    (factor bits + fp16 scales + BF16 embeddings) lands within 5%; the
+    remaining few percent are not explained by the pages."""
+    pages = _pages()
+    dims = pages["model_dims_not_on_pages"][model]
+    want = pages["model_size_gb_at_0p1_bpw"][model]
+    assert _fp16_gb(dims) == pytest.approx(want["fp16"], rel=0.005)
+    assert _model_gb(dims, 1, 10) == pytest.approx(want["littlebit"], rel=0.05)
+
+
+def test_memory_reduction_pin():
+    """mlsanity abstract: ~31x memory reduction at 0.1 BPW; Llama2-13B under 0.9 GB."""
+    pages = _pages()
+    dims = pages["model_dims_not_on_pages"]["llama2_13b"]
+    lb = _model_gb(dims, 1, 10)
+    assert lb < pages["memory_reduction_0p1_bpw"]["llama2_13b_below_gb"]
+    assert round(_fp16_gb(dims) / lb / 5) * 5 in (30, 35) and \
+        abs(_fp16_gb(dims) / lb - 31) < 2.0
+
+
+# ----------------------------------------------------------------------------
+# sign packing
+# ----------------------------------------------------------------------------
+
+def _hadamard(n):
+    i = np.arange(n)
+    par = np.vectorize(lambda v: bin(v).count("1") & 1)(i[:, None] & i[None, :])
+    return np.where(par == 1, -1.0, 1.0).astype(np.float32)
+
+
+def test_pack_walsh_golden():
+    """Packed words of the 32x32 Sylvester-Hadamard matrix are the Walsh
+    functions (tests/golden/pack_walsh.txt, derived by hand)."""
+    H = _hadamard(32)
+    want = {}
+    with open(os.path.join(GOLD, "pack_walsh.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            c, w = line.split()
+            want[int(c)] = int(w, 16)
+    for axis in (0, 1):
+        words = oracle.pack_signs(H, axis)
+        assert words.shape == (1, 32)
+        for c, w in want.items():
+            assert int(words[0, c]) == w, (axis, c, hex(int(words[0, c])))
+
+
+def test_pack_hand_example():
+    """A 3 x 35 matrix packed along axis 1: row r, word 0 holds columns 0..31,
+    word 1 holds columns 32..34 in bits 0..2 (the rest of the word is 0)."""
+    M = np.ones((3, 35), np.float32)
+    M[0, 0] = -1.0           # bit 0 of (w0, r0)
+    M[0, 31] = -2.5          # bit 31 of (w0, r0)
+    M[1, 33] = -0.001        # bit 1 of (w1, r1)
+    M[2, 5] = -0.0           # negative zero is not < 0: +1
+    M[2, 34] = -7.0          # bit 2 of (w1, r2)
+    words = oracle.pack_signs(M, 1, ld=4)
+    assert words.shape == (2, 4)
+    assert words.tolist() == [[0x80000001, 0, 0, 0], [0, 0x2, 0x4, 0]]
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 1), (31, 33), (64, 7), (70, 129)])
+@pytest.mark.parametrize("axis", [0, 1])
+def test_pack_roundtrip(rows, cols, axis):
+    rng = np.random.default_rng(rows * 1000 + cols)
+    M = rng.standard_normal((rows, cols)).astype(np.float32)
+    M.flat[::7] = 0.0
+    M.flat[::11] = -0.0
+    M.flat[::13] = np.nan
+    n_other = cols if axis == 0 else rows
+    words = oracle.pack_signs(M, axis, ld=n_other + 3)
+    back = oracle.unpack_signs(words, rows, cols, axis)
+    assert np.array_equal(back, np.where(M < 0, -1.0, 1.0))
+    # padding words and tail bits are zero
+    assert not words[:, n_other:].any()
+    n_pack = rows if axis == 0 else cols
+    if n_pack % 32:
+        assert not (words[-1] >> np.uint32(n_pack % 32)).any()
+
+
+# ----------------------------------------------------------------------------
+# the factorised forward
+# ----------------------------------------------------------------------------
+
+def _rand_layer(rng, d_in, d_out, r_p, P):
+    U = rng.standard_normal((P, d_out, r_p)).astype(np.float32)
+    V = rng.standard_normal((P, d_in, r_p)).astype(np.float32)
+    h = rng.uniform(0.5, 1.5, (P, d_out))
+    g = rng.uniform(0.5, 1.5, (P, d_in))
+    l = rng.uniform(0.5, 1.5, (P, r_p))
+    return U, V, h, g, l
+
+
+@pytest.mark.parametrize("d_in,d_out,r_p,P,T", [(5, 7, 3, 1, 2), (64, 48, 32, 2, 3),
+                                                (33, 65, 17, 2, 1)])
+def test_forward_matches_dense_weight(d_in, d_out, r_p, P, T):
+    rng = np.random.default_rng(d_in + d_out)
+    U, V, h, g, l = _rand_layer(rng, d_in, d_out, r_p, P)
+    x = rng.standard_normal((T, d_in))
+    y = oracle.linear_forward(x, U, V, h, g, l)
+    yd = oracle.dense_forward(x, U, V, h, g, l)
+    assert oracle.rel_l2(y, yd) <= 1e-12
+
+
+def test_forward_integer_regime_bit_equal():
+    """Integer x and power-of-two scales: every fp64 sum is exact, so the
+    factorised and dense formulations agree bit for bit."""
+    rng = np.random.default_rng(7)
+    P, d_in, d_out, r_p, T = 2, 40, 24, 12, 3
+    U, V, _, _, _ = _rand_layer(rng, d_in, d_out, r_p, P)
+    pw = lambda shape: 2.0 ** rng.integers(-1, 2, shape)
+    h, g, l = pw((P, d_out)), pw((P, d_in)), pw((P, r_p))
+    x = rng.integers(-4, 5, (T, d_in)).astype(np.float64)
+    y = oracle.linear_forward(x, U, V, h, g, l)
+    assert np.array_equal(y, oracle.dense_forward(x, U, V, h, g, l))
+
+
+def test_forward_bruteforce_every_sign_pattern():
+    """d_in = d_out = 3, r = 2: all 2^12 sign patterns of (U, V) against the
+    explicitly summed definition y_j = sum_k sum_i h_j S_U[j,k] l_k S_V[i,k] g_i x_i."""
+    h = np.array([[1.0, 0.5, 2.0]])
+    g = np.array([[0.5, 1.0, 1.5]])
+    l = np.array([[2.0, 0.25]])
+    x = np.array([[1.0, -2.0, 3.0]])
+    for bits in range(1 << 12):
+        s = np.array([-1.0 if (bits >> q) & 1 else 1.0 for q in range(12)], np.float32)
+        U = s[:6].reshape(1, 3, 2)
+        V = s[6:].reshape(1, 3, 2)
+        y = oracle.linear_forward(x, U, V, h, g, l)
+        for j in range(3):
+            want = 0.0
+            for k in range(2):
+                for i in range(3):
+                    want += h[0, j] * U[0, j, k] * l[0, k] * V[0, i, k] * g[0, i] * x[0, i]
+            assert y[0, j] == want, (bits, j)
+
+
+def test_forward_all_plus_closed_form():
+    """All signs +1: W is rank 1, y_j = h_j * (sum_k l_k) * (g . x)."""
+    rng = np.random.default_rng(3)
+    d_in, d_out, r_p = 50, 20, 8
+    U = np.ones((1, d_out, r_p), np.float32)
+    V = np.ones((1, d_in, r_p), np.float32)
+    h = 2.0 ** rng.integers(-1, 2, (1, d_out))
+    g = 2.0 ** rng.integers(-1, 2, (1, d_in))
+    l = 2.0 ** rng.integers(-1, 2, (1, r_p))
+    x = rng.integers(-3, 4, (2, d_in)).astype(np.float64)
+    y = oracle.linear_forward(x, U, V, h, g, l)
+    want = h[0][None, :] * l.sum() * (x @ g[0])[:, None]
+    assert np.array_equal(y, want)
+
+
+@pytest.mark.parametrize("n", [2, 8, 32, 64])
+def test_forward_hadamard_closed_form(n):
+    """S_U = S_V = H_n (Sylvester), l = 1/n: H H^T = n I, so W = diag(h * g)
+    and y = h * g * x exactly (all partial sums are small integers times powers
+    of two)."""
+    rng = np.random.default_rng(n)
+    H = _hadamard(n)
+    U = H[None]
+    V = H[None]
+    h = 2.0 ** rng.integers(-2, 3, (1, n))
+    g = 2.0 ** rng.integers(-2, 3, (1, n))
+    l = np.full((1, n), 1.0 / n)
+    x = rng.integers(-15, 16, (3, n)).astype(np.float64)
+    y = oracle.linear_forward(x, U, V, h, g, l)
+    assert np.array_equal(y, x * (h[0] * g[0])[None, :])
+
+
+def test_forward_invariants():
+    rng = np.random.default_rng(11)
+    P, d_in, d_out, r_p, T = 2, 64, 40, 16, 2
+    U, V, h, g, l = _rand_layer(rng, d_in, d_out, r_p, P)
+    x = rng.standard_normal((T, d_in))
+    y = oracle.linear_forward(x, U, V, h, g, l)
+    # flipping latent column k in both U and V leaves y unchanged
+    U2, V2 = U.copy(), V.copy()
+    U2[:, :, 3] *= -1
+    V2[:, :, 3] *= -1
+    assert np.array_equal(oracle.linear_forward(x, U2, V2, h, g, l), y)
+    # odd in x
+    assert np.array_equal(oracle.linear_forward(-x, U, V, h, g, l), -y)
+    # (2h, l/2) gives the same output
+    assert np.array_equal(oracle.linear_forward(x, U, V, 2 * h, g, l / 2), y)
+    # residual path equal to the first path doubles the output
+    U1, V1 = U[:1], V[:1]
+    y1 = oracle.linear_forward(x, U1, V1, h[:1], g[:1], l[:1])
+    yy = oracle.linear_forward(x, np.concatenate([U1, U1]), np.concatenate([V1, V1]),
+                               np.concatenate([h[:1]] * 2), np.concatenate([g[:1]] * 2),
+                               np.concatenate([l[:1]] * 2))
+    assert np.array_equal(yy, 2 * y1)
+    # the residual path adds: y(P=2) = y(path 0) + y(path 1)
+    y0 = oracle.linear_forward(x, U[:1], V[:1], h[:1], g[:1], l[:1])
+    y1b = oracle.linear_forward(x, U[1:], V[1:], h[1:], g[1:], l[1:])
+    assert np.allclose(y, y0 + y1b, rtol=1e-13, atol=1e-13)
+    # latent permutation of (U, V, l)
+    perm = rng.permutation(r_p)
+    yp = oracle.linear_forward(x, U[:, :, perm], V[:, :, perm], h, g, l[:, perm])
+    assert oracle.rel_l2(yp, y) < 1e-13
+
+
+def test_forward_rows_matches_full():
+    rng = np.random.default_rng(5)
+    U, V, h, g, l = _rand_layer(rng, 96, 70, 24, 2)
+    x = rng.standard_normal((3, 96))
+    y = oracle.linear_forward(x, U, V, h, g, l)
+    rows = [0, 5, 69, 33]
+    assert np.array_equal(oracle.linear_forward_rows(x, U, V, h, g, l, rows), y[:, rows])
+
+
+def test_forward_thread_count_does_not_change_result():
+    rng = np.random.default_rng(9)
+    U, V, h, g, l = _rand_layer(rng, 300, 200, 64, 2)
+    x = rng.standard_normal((4, 300))
+    assert np.array_equal(oracle.linear_forward(x, U, V, h, g, l, nthreads=1),
+                          oracle.linear_forward(x, U, V, h, g, l, nthreads=4))
+
+
+def test_storage_widening_exact():
+    """fp16 scale and bf16 activation bit patterns widen exactly."""
+    assert oracle.widen_f16(np.array([0x3C00, 0xBC00, 0x3800, 0x0001, 0x7BFF], np.uint16)).tolist() == \
+        [1.0, -1.0, 0.5, 2.0 ** -24, 65504.0]
+    assert oracle.widen_bf16(np.array([0x3F80, 0xC000, 0x3F81], np.uint16)).tolist() == \
+        [1.0, -2.0, 1.0 + 2.0 ** -7]
+
+
+# ----------------------------------------------------------------------------
+# SwiGLU block
+# ----------------------------------------------------------------------------
+
+def test_silu_special_values():
+    assert oracle.silu(0.0) == 0.0
+    assert oracle.silu(1.0) == pytest.approx(1.0 / (1.0 + math.exp(-1.0)), rel=1e-15)
+    assert oracle.silu(50.0) == pytest.approx(50.0, rel=1e-15)
+    v = oracle.silu(-1000.0)
+    assert v == 0.0 and math.copysign(1.0, v) == -1.0      # -0, not NaN
+    assert oracle.silu(-2.0) == pytest.approx(-2.0 / (1.0 + math.exp(2.0)), rel=1e-15)
+
+
+def test_mlp_hadamard_identity_closed_form():
+    """gate, up and down are identity layers (Hadamard factors, l = 1/n, unit
+    h and g), so the block reduces to y = silu(x) * x."""
+    n = 32
+    H = _hadamard(n)[None]
+    one = np.ones((1, n))
+    lay = synth.LayerInputs(n, n, n, 1, H, H, one, one, one / n)
+    rng = np.random.default_rng(2)
+    x = rng.integers(-6, 7, (3, n)).astype(np.float64)
+    y = oracle.mlp_forward(x, lay, lay, lay)
+    want = x / (1.0 + np.exp(-x)) * x
+    # the down layer sums non-integer values, so allow fp64 rounding
+    assert np.allclose(y, want, rtol=1e-13, atol=1e-13)
+
+
+def test_mlp_matches_composed_linears():
+    rng = np.random.default_rng(4)
+    P, d, ff = 2, 48, 80
+    mk = lambda din, dout, rp: synth.LayerInputs(din, dout, rp, P, *_rand_layer(rng, din, dout, rp, P))
+    gate, up, down = mk(d, ff, 16), mk(d, ff, 16), mk(ff, d, 16)
+    x = rng.standard_normal((2, d))
+    y = oracle.mlp_forward(x, gate, up, down)
+    zg = oracle.dense_forward(x, gate.U, gate.V, gate.h, gate.g, gate.l)
+    zu = oracle.dense_forward(x, up.U, up.V, up.h, up.g, up.l)
+    a = zg / (1.0 + np.exp(-zg)) * zu
+    yd = oracle.dense_forward(a, down.U, down.V, down.h, down.g, down.l)
+    assert oracle.rel_l2(y, yd) < 1e-12
