@@ -152,3 +152,34 @@ WORKLOADS: Dict[str, Workload] = {
 def layer_seed(layer: int, linear_index: int) -> int:
     """Seed of linear `linear_index` in stack layer `layer` (layer l uses seed l)."""
     return layer * 16 + linear_index
+
+
+# ----------------------------------------------------------------------------
+# device-side generation for large layer stacks
+# ----------------------------------------------------------------------------
+
+def device_layer(seed: int, d_in: int, d_out: int, r_path: int, paths: int, device="cuda"):
+    """The same distributions drawn on the GPU with torch's seeded generator
+    (for layer stacks too large to draw on the host quickly).  Returns float32
+    U [P][d_out][r_path], V [P][d_in][r_path] and float16 h, g, l, all on
+    `device`.  Draw order: U, V, h, g, l."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    U = torch.randn((paths, d_out, r_path), generator=gen, device=device, dtype=torch.float32)
+    V = torch.randn((paths, d_in, r_path), generator=gen, device=device, dtype=torch.float32)
+    unif = lambda shape: (torch.rand(shape, generator=gen, device=device, dtype=torch.float32)
+                          + 0.5).to(torch.float16)
+    h = unif((paths, d_out))
+    g = unif((paths, d_in))
+    l = unif((paths, r_path))
+    return U, V, h, g, l
+
+
+def device_activations(seed: int, T: int, d: int, dtype: str, device="cuda"):
+    """x [T][d] ~ N(0, 1) drawn on the GPU, as float32 or bfloat16 (RNE)."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    x = torch.randn((T, d), generator=gen, device=device, dtype=torch.float32)
+    return x if dtype == "f32" else x.to(torch.bfloat16)

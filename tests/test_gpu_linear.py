@@ -1,0 +1,212 @@
+"""GPU parity of lb_linear_forward against the fp64 oracle.
+
+Tolerances (relative L2 over the whole output, or over the sampled outputs):
+1e-3 for fp32 outputs and 8e-3 for bf16 outputs.  In the exact-integer
+regimes every partial sum is exactly representable, so the GPU must match the
+oracle bit for bit.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import TOL, dev_layer, say, torch_or_skip, x_to_dev, y_to_np
+
+pytestmark = pytest.mark.gpu
+
+DECODE_PATHS = ["valu", "decode"]
+PATH_FLAG = {"auto": 0, "decode": 1, "prefill": 2, "valu": 3}
+
+
+def _run(inp, x, out_dtype, path, T):
+    torch = torch_or_skip()
+    import binarized_rank_linear_amd as lb
+    layer = dev_layer(inp)
+    xd = x_to_dev(x)
+    od = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    say("linear", inp.d_in, inp.d_out, inp.r_path, inp.paths, "T", T, out_dtype, path)
+    y = lb.linear_forward(xd, layer, od, PATH_FLAG[path])
+    torch.cuda.synchronize()
+    return y
+
+
+def _check(inp, x, out_dtype, path, rows=None, tokens=None):
+    T = x.shape[0]
+    y = y_to_np(_run(inp, x, out_dtype, path, T))
+    xs = x if tokens is None else x[tokens]
+    if rows is None:
+        ref = oracle.linear_forward(xs, inp.U, inp.V, inp.h, inp.g, inp.l)
+        got = y if tokens is None else y[tokens]
+    else:
+        ref = oracle.linear_forward_rows(xs, inp.U, inp.V, inp.h, inp.g, inp.l, rows)
+        got = (y if tokens is None else y[tokens])[:, rows]
+    err = oracle.rel_l2(got, ref)
+    assert err <= TOL[out_dtype], err
+    return err
+
+
+# ---- configuration 1: 1024 x 1024, 1.0 bpw -> r = 512, no residual, fp32 ----
+
+@pytest.mark.parametrize("T", [1, 8])
+@pytest.mark.parametrize("path", ["auto", "valu", "decode"])
+def test_config1_single_linear(T, path):
+    r, rp = oracle.rank_for_budget(1024, 1024, 1, 1, False)
+    inp = synth.layer_inputs(0, 1024, 1024, rp, 1)
+    x = synth.activations(synth.activation_seed(0), T, 1024, "f32")
+    _check(inp, x, "f32", path)
+
+
+# ---- ragged shapes spanning several tiles ----
+
+@pytest.mark.parametrize("d_in,d_out,r_p,P", [(1000, 1100, 48, 2), (100, 70, 16, 2),
+                                              (96, 1, 32, 1), (2080, 515, 200, 2),
+                                              (32, 4096, 8, 1)])
+@pytest.mark.parametrize("T", [1, 3, 17, 32])
+@pytest.mark.parametrize("path", DECODE_PATHS)
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_ragged_shapes(d_in, d_out, r_p, P, T, path, dt):
+    inp = synth.layer_inputs(d_in + d_out, d_in, d_out, r_p, P)
+    x = synth.activations(T + d_in, T, d_in, dt)
+    _check(inp, x, dt, path)
+
+
+@pytest.mark.parametrize("T", [33, 100])
+def test_more_tokens_than_decode_width_fp32(T):
+    """fp32 outputs above 32 tokens run the plain decode kernels in chunks."""
+    inp = synth.layer_inputs(5, 512, 384, 64, 2)
+    x = synth.activations(6, T, 512, "f32")
+    _check(inp, x, "f32", "auto")
+
+
+# ---- the configurations' linears at full size ----
+
+def _cfg_linear(key, name):
+    w = synth.WORKLOADS[key]
+    sh = [s for s in w.linears if s.name == name][0]
+    r, rp = oracle.rank_for_budget(sh.d_in, sh.d_out, w.b_num, w.b_den, w.residual)
+    inp = synth.layer_inputs(w.linears.index(sh), sh.d_in, sh.d_out, rp, 2 if w.residual else 1)
+    return w, sh, inp
+
+
+@pytest.mark.parametrize("key,name,T", [
+    ("c3", "q", 1), ("c3", "q", 4), ("c3", "q", 32), ("c3", "gate", 1), ("c3", "gate", 4),
+    ("c3", "down", 1), ("c3", "down", 32),
+    ("c4", "q", 1), ("c4", "k", 1), ("c4", "gate", 1), ("c4", "down", 1),
+    ("c5", "q", 1), ("c5", "k", 1), ("c5", "gate", 1), ("c5", "down", 1), ("c5", "down", 4)])
+@pytest.mark.parametrize("path", ["auto", "valu"])
+def test_config_linears_decode(key, name, T, path):
+    w, sh, inp = _cfg_linear(key, name)
+    x = synth.activations(synth.activation_seed(T), T, sh.d_in, w.dtype)
+    rows = None if sh.d_out * T <= 8192 * 4 else np.linspace(0, sh.d_out - 1, 2048).astype(np.int64)
+    _check(inp, x, w.dtype, path, rows=rows)
+
+
+@pytest.mark.parametrize("key,name", [("c4", "q"), ("c4", "k"), ("c4", "gate"), ("c4", "down"),
+                                      ("c5", "q"), ("c5", "k"), ("c5", "gate"), ("c5", "down")])
+def test_config_linears_prefill_sampled(key, name):
+    """T = 2048 through the GEMM path; checked on 24 sampled tokens x 1024 sampled rows."""
+    w, sh, inp = _cfg_linear(key, name)
+    T = 2048
+    x = synth.activations(synth.activation_seed(T), T, sh.d_in, w.dtype)
+    tokens = np.array([0, 1, 2, 63, 64, 127, 128, 255, 256, 511, 777, 1023, 1024, 1200, 1500,
+                       1791, 1792, 1919, 2000, 2040, 2044, 2045, 2046, 2047])
+    rows = np.unique(np.linspace(0, sh.d_out - 1, 1024).astype(np.int64))
+    _check(inp, x, w.dtype, "auto", rows=rows, tokens=tokens)
+
+
+# ---- exact regimes ----
+
+def _pow2(rng, shape, lo=-1, hi=1):
+    return synth.f16_bits(2.0 ** rng.integers(lo, hi + 1, shape))
+
+
+@pytest.mark.parametrize("path", DECODE_PATHS + ["prefill"])
+def test_exact_integer_regime_bit_exact(path):
+    """x in {-1, 0, 1}, power-of-two scales: every partial sum is an exact
+    small dyadic number, so fp32 output equals the oracle bit for bit (bf16
+    output for the GEMM path equals the oracle rounded to bf16)."""
+    rng = np.random.default_rng(1)
+    P, d_in, d_out, r_p, T = 2, 1024, 700, 96, (64 if path == "prefill" else 5)
+    base = synth.layer_inputs(9, d_in, d_out, r_p, P)
+    inp = synth.LayerInputs(d_in, d_out, r_p, P, base.U, base.V, _pow2(rng, (P, d_out)),
+                            _pow2(rng, (P, d_in), 0, 0), _pow2(rng, (P, r_p)))
+    x = rng.integers(-1, 2, (T, d_in)).astype(np.float32)
+    ref = oracle.linear_forward(x, inp.U, inp.V, inp.h, inp.g, inp.l)
+    if path == "prefill":
+        xb = synth.f32_to_bf16_bits(x)
+        y = _run(inp, xb, "bf16", path, T).cpu().view(__import__("torch").int16).numpy().view(np.uint16)
+        assert np.array_equal(y, synth.f32_to_bf16_bits(ref.astype(np.float32)))
+    else:
+        y = _run(inp, x, "f32", path, T).cpu().numpy()
+        assert np.array_equal(y.astype(np.float64), ref)
+
+
+def _hadamard(n):
+    i = np.arange(n)
+    par = np.array([[bin(a & b).count("1") & 1 for b in i] for a in i])
+    return np.where(par == 1, -1.0, 1.0).astype(np.float32)
+
+
+@pytest.mark.parametrize("path,n,xmax", [("valu", 1024, 15), ("valu", 256, 15),
+                                         ("decode", 256, 1), ("decode", 64, 3)])
+def test_hadamard_closed_form_bit_exact(path, n, xmax):
+    """S_U = S_V = H_n, l = 1/n: W = diag(h*g), so y = h*g*x exactly,
+    independently of the oracle."""
+    rng = np.random.default_rng(n)
+    H = _hadamard(n)[None]
+    h = _pow2(rng, (1, n), -1, 1)
+    g = _pow2(rng, (1, n), 0, 0) if xmax == 1 else _pow2(rng, (1, n), -1, 1)
+    l = synth.f16_bits(np.full((1, n), 1.0 / n))
+    inp = synth.LayerInputs(n, n, n, 1, H, H, h, g, l)
+    x = rng.integers(-xmax, xmax + 1, (4, n)).astype(np.float32)
+    y = _run(inp, x, "f32", path, 4).cpu().numpy()
+    want = x * (oracle.widen_f16(h[0]) * oracle.widen_f16(g[0]))[None, :]
+    assert np.array_equal(y.astype(np.float64), want)
+
+
+@pytest.mark.parametrize("path", DECODE_PATHS)
+def test_invariants_bit_exact(path):
+    torch = torch_or_skip()
+    inp = synth.layer_inputs(21, 640, 900, 80, 2)
+    x = synth.activations(22, 6, 640, "f32")
+    y = _run(inp, x, "f32", path, 6).cpu().numpy()
+    # odd in x
+    yn = _run(inp, -x, "f32", path, 6).cpu().numpy()
+    assert np.array_equal(yn, -y)
+    # (2h, l/2) leaves y unchanged
+    h2 = synth.f16_bits(oracle.widen_f16(inp.h) * 2)
+    l2 = synth.f16_bits(oracle.widen_f16(inp.l) / 2)
+    inp2 = synth.LayerInputs(inp.d_in, inp.d_out, inp.r_path, 2, inp.U, inp.V, h2, inp.g, l2)
+    assert np.array_equal(_run(inp2, x, "f32", path, 6).cpu().numpy(), y)
+    # flipping latent column 5 of both factors leaves y unchanged
+    U, V = inp.U.copy(), inp.V.copy()
+    U[:, :, 5] *= -1
+    V[:, :, 5] *= -1
+    inp3 = synth.LayerInputs(inp.d_in, inp.d_out, inp.r_path, 2, U, V, inp.h, inp.g, inp.l)
+    assert np.array_equal(_run(inp3, x, "f32", path, 6).cpu().numpy(), y)
+    # residual path equal to the first doubles the single-path output
+    one = synth.LayerInputs(inp.d_in, inp.d_out, inp.r_path, 1, inp.U[:1], inp.V[:1], inp.h[:1],
+                            inp.g[:1], inp.l[:1])
+    dup = synth.LayerInputs(inp.d_in, inp.d_out, inp.r_path, 2, inp.U[[0, 0]], inp.V[[0, 0]],
+                            inp.h[[0, 0]], inp.g[[0, 0]], inp.l[[0, 0]])
+    y1 = _run(one, x, "f32", path, 6).cpu().numpy()
+    assert np.array_equal(_run(dup, x, "f32", path, 6).cpu().numpy(), 2 * y1)
+
+
+def test_zero_tokens_is_a_noop():
+    torch = torch_or_skip()
+    import binarized_rank_linear_amd as lb
+    inp = synth.layer_inputs(3, 256, 128, 32, 2)
+    layer = dev_layer(inp)
+    x = torch.empty((0, 256), device="cuda")
+    y = lb.linear_forward(x, layer, torch.float32)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 128)
+
+
+@pytest.mark.parametrize("path", ["decode", "prefill"])
+def test_decode_and_prefill_agree(path):
+    """The same bf16 request through both kernel families, both near the oracle."""
+    inp = synth.layer_inputs(40, 2048, 1536, 160, 2)
+    x = synth.activations(41, 32, 2048, "bf16")
+    _check(inp, x, "bf16", path)

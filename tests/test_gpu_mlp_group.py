@@ -1,0 +1,92 @@
+"""GPU parity of the SwiGLU block and of layer groups (stacks)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import TOL, dev_layer, host_layer_from_dev, say, torch_or_skip, x_to_dev, y_to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _mlp_layers(seed_base=0):
+    w = synth.WORKLOADS["c2"]
+    out = []
+    for i, sh in enumerate(w.linears):
+        r, rp = oracle.rank_for_budget(sh.d_in, sh.d_out, w.b_num, w.b_den, w.residual)
+        out.append(synth.layer_inputs(seed_base + i, sh.d_in, sh.d_out, rp, 2))
+    return w, out
+
+
+@pytest.mark.parametrize("T", [1, 16, 5])
+@pytest.mark.parametrize("path", [0, 3])
+def test_config2_mlp_block(T, path):
+    torch = torch_or_skip()
+    import binarized_rank_linear_amd as lb
+    w, (g, u, d) = _mlp_layers()
+    x = synth.activations(synth.activation_seed(T), T, 1024, "bf16")
+    say("mlp c2 T", T, "path", path)
+    y = lb.mlp_forward(x_to_dev(x), dev_layer(g), dev_layer(u), dev_layer(d), torch.bfloat16,
+                       flags=path)
+    torch.cuda.synchronize()
+    ref = oracle.mlp_forward(x, g, u, d)
+    err = oracle.rel_l2(y_to_np(y), ref)
+    assert err <= TOL["bf16"], err
+
+
+def test_mlp_prefill_sampled():
+    torch = torch_or_skip()
+    import binarized_rank_linear_amd as lb
+    w, (g, u, d) = _mlp_layers(10)
+    T = 96
+    x = synth.activations(7, T, 1024, "bf16")
+    say("mlp c2 prefill T", T)
+    y = lb.mlp_forward(x_to_dev(x), dev_layer(g), dev_layer(u), dev_layer(d), torch.bfloat16)
+    torch.cuda.synchronize()
+    tok = np.array([0, 31, 32, 63, 95])
+    ref = oracle.mlp_forward(x[tok], g, u, d)
+    err = oracle.rel_l2(y_to_np(y)[tok], ref)
+    assert err <= TOL["bf16"], err
+
+
+def _stack_check(key, layers, T, check_layers, rows_per=512):
+    torch = torch_or_skip()
+    import binarized_rank_linear_amd as lb
+    from binarized_rank_linear_amd.stack import LayerStack
+    w = synth.WORKLOADS[key]
+    kept = {}
+
+    def make(L, i, di, do, rp, P):
+        U, V, h, g, l = synth.device_layer(synth.layer_seed(L, i), di, do, rp, P)
+        if L in check_layers:
+            kept[(L, i)] = host_layer_from_dev(U, V, h, g, l)
+        return U, V, h, g, l
+
+    say("stack", key, layers, "T", T)
+    st = LayerStack([(s.name, s.d_in, s.d_out) for s in w.linears], layers, w.b_num, w.b_den,
+                    w.residual, make)
+    widths = sorted({s.d_in for s in w.linears})
+    xs = {d: synth.device_activations(synth.activation_seed(d), T, d, w.dtype) for d in widths}
+    st.bind(T, xs, torch.bfloat16)
+    st.group.run()
+    torch.cuda.synchronize()
+    for L in check_layers:
+        for i, sh in enumerate(w.linears):
+            inp = kept[(L, i)]
+            x = xs[sh.d_in].float().cpu().numpy()
+            rows = np.unique(np.linspace(0, sh.d_out - 1, rows_per).astype(np.int64))
+            ref = oracle.linear_forward_rows(x, inp.U, inp.V, inp.h, inp.g, inp.l, rows)
+            got = y_to_np(st.outputs[L][i])[:, rows]
+            err = oracle.rel_l2(got, ref)
+            assert err <= TOL["bf16"], (L, sh.name, err)
+
+
+@pytest.mark.parametrize("key,T", [("c3", 4), ("c4", 1), ("c5", 1), ("c3", 32)])
+def test_small_stack_all_layers(key, T):
+    _stack_check(key, 2, T, {0, 1})
+
+
+def test_full_c5_stack_sampled_layers():
+    """The 80-layer Llama2-70B-shaped stack as the benchmark runs it (one
+    group, T = 1); layers 0, 40 and 79 are checked on sampled rows."""
+    _stack_check("c5", 80, 1, {0, 40, 79})
