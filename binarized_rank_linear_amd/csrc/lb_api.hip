@@ -31,11 +31,13 @@ enum class Path { Valu, MfmaDecode, Gemm };
 int choose_path(unsigned flags, int64_t T, int y_dtype, Path *out) {
     switch (flags & LB_PATH_MASK) {
         case LB_PATH_AUTO:
-            if (T <= kDecodeMaxT) *out = Path::MfmaDecode;
-            else *out = y_dtype == LB_BF16 ? Path::Gemm : Path::Valu;
+            if (T <= kDecodeMaxT)
+                *out = mfma_decode_supported(T, y_dtype) ? Path::MfmaDecode : Path::Valu;
+            else
+                *out = y_dtype == LB_BF16 ? Path::Gemm : Path::Valu;
             return LB_OK;
         case LB_PATH_DECODE:
-            *out = T <= kDecodeMaxT ? Path::MfmaDecode : Path::Valu;
+            *out = mfma_decode_supported(T, y_dtype) ? Path::MfmaDecode : Path::Valu;
             return LB_OK;
         case LB_PATH_PREFILL:
             if (y_dtype != LB_BF16) return LB_EUNSUPPORTED;
@@ -292,7 +294,14 @@ struct GroupRecord {
     int x_dtype, y_dtype;
     unsigned flags;
     size_t ws_bytes;
+    bool fused;                       // matrix-core group kernels (two launches per run)
+    std::vector<uint8_t> state;       // their host-side launch state
 };
+
+bool group_fused(unsigned flags, int64_t T, int y_dtype) {
+    const unsigned p = flags & LB_PATH_MASK;
+    return (p == LB_PATH_AUTO || p == LB_PATH_DECODE) && mfma_decode_supported(T, y_dtype);
+}
 std::mutex g_groups_mu;
 std::unordered_map<void *, GroupRecord> g_groups;
 
@@ -308,6 +317,24 @@ int group_linear(const lb_linear_desc &d, int64_t T, int x_dtype, int y_dtype, L
 size_t lb_grouped_workspace_bytes(const lb_linear_desc *descs, int n, int64_t T, unsigned flags) {
     if (!descs || n <= 0 || T <= 0 || T > kDecodeMaxT) return 0;
     size_t need = 0;
+    // the fused kernels' table and per-linear scratch (sized for bf16 outputs,
+    // the larger of fp32 when that needs more)
+    {
+        std::vector<Linear> ls((size_t)n);
+        bool ok = true;
+        for (int i = 0; i < n && ok; ++i) {
+            Linear &a = ls[(size_t)i];
+            a = Linear{};
+            ok = check_shape(descs[i].d_in, descs[i].d_out, descs[i].r, T, descs[i].residual, &a) == LB_OK;
+            a.x_dtype = a.y_dtype = LB_BF16;
+        }
+        if (ok)
+            for (int yd : {LB_BF16, LB_F32})
+                if (group_fused(flags, T, yd)) {
+                    const size_t b = mfma_group_workspace_bytes(ls.data(), n, T, yd);
+                    if (b > need) need = b;
+                }
+    }
     for (int i = 0; i < n; ++i) {
         const size_t b = lb_linear_workspace_bytes(descs[i].d_in, descs[i].d_out, descs[i].r, T,
                                                    descs[i].residual, flags);
@@ -319,7 +346,6 @@ size_t lb_grouped_workspace_bytes(const lb_linear_desc *descs, int n, int64_t T,
 
 int lb_grouped_prepare(const lb_linear_desc *descs, int n, int64_t T, int x_dtype, int y_dtype,
                        void *ws, size_t ws_bytes, unsigned flags, void *stream) {
-    (void)stream;
     if (!descs || n <= 0 || T <= 0 || T > kDecodeMaxT) return LB_EINVAL;
     Path p;
     int rc;
@@ -331,14 +357,24 @@ int lb_grouped_prepare(const lb_linear_desc *descs, int n, int64_t T, int x_dtyp
     const size_t need = lb_grouped_workspace_bytes(descs, n, T, flags);
     if (!ws || ws_bytes < need) return LB_EWORKSPACE;
     if (!aligned(ws, 256)) return LB_EALIGN;
+    GroupRecord rec;
+    rec.descs.assign(descs, descs + n);
+    rec.T = T;
+    rec.x_dtype = x_dtype;
+    rec.y_dtype = y_dtype;
+    rec.flags = flags;
+    rec.ws_bytes = ws_bytes;
+    rec.fused = group_fused(flags, T, y_dtype);
+    if (rec.fused) {
+        std::vector<Linear> ls((size_t)n);
+        for (int i = 0; i < n; ++i) group_linear(descs[i], T, x_dtype, y_dtype, &ls[(size_t)i]);
+        rec.state.assign(mfma_group_state_bytes(), 0);
+        if ((rc = mfma_group_prepare(ls.data(), n, T, y_dtype, ws, ws_bytes, rec.state.data(),
+                                     (hipStream_t)stream)))
+            return rc;
+    }
     std::lock_guard<std::mutex> lk(g_groups_mu);
-    GroupRecord &g = g_groups[ws];
-    g.descs.assign(descs, descs + n);
-    g.T = T;
-    g.x_dtype = x_dtype;
-    g.y_dtype = y_dtype;
-    g.flags = flags;
-    g.ws_bytes = ws_bytes;
+    g_groups[ws] = std::move(rec);
     return LB_OK;
 }
 
@@ -350,6 +386,7 @@ int lb_grouped_run(void *ws, void *stream) {
         if (it == g_groups.end()) return LB_EINVAL;
         g = it->second;
     }
+    if (g.fused) return mfma_group_run(g.state.data(), (hipStream_t)stream);
     void *lws = (char *)ws + 256;
     for (const lb_linear_desc &d : g.descs) {
         const int rc = lb_linear_forward(d.x, g.x_dtype, d.y, g.y_dtype, &d.w, d.d_in, d.d_out, d.r,

@@ -76,8 +76,15 @@ size_t valu_workspace_bytes(const Linear &a);
 int valu_forward(const Linear &a, void *ws, hipStream_t s);
 
 // Matrix-core decode path (fp4 signs x fp8 activation limbs).
+bool mfma_decode_supported(int64_t T, int y_dtype);
 size_t mfma_decode_workspace_bytes(const Linear &a);
 int mfma_decode_forward(const Linear &a, void *ws, hipStream_t s);
+// Groups of independent linears on the matrix-core decode path: two launches per run.
+size_t mfma_group_workspace_bytes(const Linear *ls, int n, int64_t T, int y_dtype);
+size_t mfma_group_state_bytes();
+int mfma_group_prepare(const Linear *ls, int n, int64_t T, int y_dtype, void *ws, size_t ws_bytes,
+                       void *host_state, hipStream_t s);
+int mfma_group_run(const void *host_state, hipStream_t s);
 
 // GEMM (prefill) path.
 size_t gemm_workspace_bytes(const Linear &a);
