@@ -1,0 +1,227 @@
+#!/usr/bin/env python3
+"""Benchmark of the LittleBit layer forward on one MI355X.
+
+One step is one forward pass of the token batch through a stack of seeded
+synthetic LittleBit linears: by default the Llama2-70B-shaped decoder-layer
+linears (q/o 8192x8192, k/v 8192x1024, gate/up 8192x28672, down 28672x8192) at
+0.1 bits per weight with the residual path, 80 independent layers, decode T=1,
+run as one group (two kernel launches per pass).  The stack holds ~0.8 GB of
+packed signs, more than three times the 256 MB Infinity Cache, so every pass
+streams from HBM.  Prints ONE JSON line.
+
+The prefill leg times the same shapes at T=2048 (one layer, the GEMM path)
+and reports it beside the decode figure.  The CPU baseline times the fp64
+oracle on one layer of the same stack and scales to the stack.
+
+    python bench.py [--steps K] [--warmup W] [--workload c5] [--tokens 1]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
+METRIC = "LittleBit layer tok/s at T=1 and T=2048; % HBM BW / % MFMA peak"
+
+
+def _log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def linear_bytes(d_in, d_out, r, P, T, act_bytes=2):
+    """Algorithmic bytes of one linear forward, split by stage: tight sign
+    bits, fp16 scales, activations in and out (padding excluded)."""
+    r_p = r // P
+    s1 = r * d_in // 8 + 2 * P * (d_in + r_p) + T * d_in * act_bytes
+    s2 = r * d_out // 8 + 2 * P * d_out + T * d_out * act_bytes
+    return s1, s2
+
+
+def build_stack(w, layers, T):
+    import torch
+    import synth
+    from binarized_rank_linear_amd.stack import LayerStack
+
+    def make(L, i, di, do, rp, P):
+        return synth.device_layer(synth.layer_seed(L, i), di, do, rp, P)
+
+    t0 = time.time()
+    st = LayerStack([(s.name, s.d_in, s.d_out) for s in w.linears], layers, w.b_num, w.b_den,
+                    w.residual, make)
+    widths = sorted({s.d_in for s in w.linears})
+    xs = {d: synth.device_activations(synth.activation_seed(d), T, d, w.dtype) for d in widths}
+    st.bind(T, xs, torch.bfloat16 if w.dtype == "bf16" else torch.float32)
+    torch.cuda.synchronize()
+    _log("stack of %d layers packed in %.1f s (%.1f MB of packed words)"
+         % (layers, time.time() - t0, st.packed_bytes() / 1e6))
+    return st, xs
+
+
+def time_decode(st, steps, warmup):
+    """Times `steps` passes; HIP events bracket each stage kernel on the
+    launch stream."""
+    import torch
+    s = torch.cuda.current_stream()
+    g = st.group
+    for _ in range(warmup):
+        g.run_stage(1)
+        g.run_stage(2)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        ev[k][0].record(s)
+        g.run_stage(1)
+        ev[k][1].record(s)
+        g.run_stage(2)
+        ev[k][2].record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    s1 = sum(e[0].elapsed_time(e[1]) for e in ev) / steps * 1e-3
+    s2 = sum(e[1].elapsed_time(e[2]) for e in ev) / steps * 1e-3
+    return wall / steps, s1, s2
+
+
+def cpu_baseline(w, T, layers):
+    """fp64 oracle on one layer of the stack (all its linears), scaled to L layers."""
+    import numpy as np
+    import oracle
+    import synth
+    t_layer = 0.0
+    for i, sh in enumerate(w.linears):
+        r, rp = oracle.rank_for_budget(sh.d_in, sh.d_out, w.b_num, w.b_den, w.residual)
+        inp = synth.layer_inputs(i, sh.d_in, sh.d_out, rp, 2 if w.residual else 1)
+        x = synth.activations(synth.activation_seed(T), T, sh.d_in, w.dtype)
+        t0 = time.perf_counter()
+        oracle.linear_forward(x, inp.U, inp.V, inp.h, inp.g, inp.l)
+        t_layer += time.perf_counter() - t0
+    cores = oracle.max_threads()
+    return {"value": T / (t_layer * layers), "unit": "tok/s", "cores": cores, "kind": "oracle",
+            "sample": "one layer (%d linears) at T=%d timed once, scaled to the %d-layer stack"
+                      % (len(w.linears), T, layers)}
+
+
+def prefill_leg(w, T, steps):
+    """One layer of the workload's linears at T tokens through the GEMM path."""
+    import torch
+    import synth
+    import binarized_rank_linear_amd as lb
+    layer = []
+    for i, sh in enumerate(w.linears):
+        r, rp = lb.rank_for_budget(sh.d_in, sh.d_out, w.b_num, w.b_den, w.residual)
+        U, V, h, g, l = synth.device_layer(synth.layer_seed(0, i), sh.d_in, sh.d_out, rp,
+                                           2 if w.residual else 1)
+        layer.append(lb.PackedLinear.from_factors(U, V, h, g, l))
+        del U, V
+    xs = {d: synth.device_activations(7 + d, T, d, "bf16") for d in {s.d_in for s in w.linears}}
+    ys = [torch.empty((T, lin.d_out), dtype=torch.bfloat16, device="cuda") for lin in layer]
+    wss = [lb.workspace(lb.linear_workspace_bytes(lin, T, lb.LB_PATH_PREFILL)) for lin in layer]
+
+    def run():
+        for lin, y, ws in zip(layer, ys, wss):
+            lb.linear_forward(xs[lin.d_in], lin, torch.bfloat16, lb.LB_PATH_PREFILL, ws=ws, out=y)
+
+    run()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / steps
+    flops = sum(2 * T * lin.r * (lin.d_in + lin.d_out) for lin in layer)
+    return {"workload": "one layer of the same linears, T=%d (GEMM path)" % T, "T": T,
+            "tok_per_s": T / t, "ms_per_layer": t * 1e3,
+            "roofline": {"bound": "mfma", "achieved": flops / t / 1e12, "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": flops / t / 1e12 / BF16_PEAK_TFLOPS}}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c5", choices=["c3", "c4", "c5"])
+    ap.add_argument("--tokens", type=int, default=1)
+    ap.add_argument("--layers", type=int, default=0, help="stack depth (default: the workload's)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the T=2048 prefill leg")
+    ap.add_argument("--prefill-tokens", type=int, default=2048)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: the LittleBit stack fits one MI355X and this build "
+              "has no multi-GPU path (see the sharding notes in DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = synth.WORKLOADS[args.workload]
+    layers = args.layers or w.layers
+    T = args.tokens
+
+    st, _ = build_stack(w, layers, T)
+    P = 2 if w.residual else 1
+    b1 = b2 = 0
+    for row in st.linears:
+        for lin in row:
+            s1, s2 = linear_bytes(lin.d_in, lin.d_out, lin.r, P, T)
+            b1 += s1
+            b2 += s2
+    step_s, s1_s, s2_s = time_decode(st, args.steps, args.warmup)
+    bw1 = b1 / s1_s / 1e9
+    bw2 = b2 / s2_s / 1e9
+    dominant = (2, b2, s2_s, bw2) if b2 >= b1 else (1, b1, s1_s, bw1)
+    _log("pass %.1f us (stage 1 %.1f us at %.0f GB/s, stage 2 %.1f us at %.0f GB/s)"
+         % (step_s * 1e6, s1_s * 1e6, bw1, s2_s * 1e6, bw2))
+
+    out = {
+        "metric": METRIC,
+        "value": T / step_s,
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e2m1 x e4m3 -> f32 (bf16 in/out)",
+        "data": "synthetic",
+        "config": {
+            "workload": "%s, decode T=%d, %d-layer stack as one group" % (w.title, T, layers),
+            "tokens": T, "layers": layers,
+            "linears_per_layer": [[s.name, s.d_in, s.d_out] for s in w.linears],
+            "algorithmic_bytes_per_pass": b1 + b2,
+            "packed_bytes_per_pass": st.packed_bytes() + st.scale_bytes(),
+        },
+        "roofline": {"bound": "hbm", "achieved": dominant[3], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": dominant[3] / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "k_stage%d" % dominant[0],
+                     "pass_GBs": (b1 + b2) / step_s / 1e9,
+                     "pass_frac": (b1 + b2) / step_s / 1e9 / HBM_PEAK_GBS,
+                     "stage1_us": s1_s * 1e6, "stage2_us": s2_s * 1e6},
+    }
+    del st
+    torch.cuda.empty_cache()
+    if not args.no_prefill and args.prefill_tokens > 32:
+        try:
+            out["prefill"] = prefill_leg(w, args.prefill_tokens, max(3, args.steps // 50))
+        except Exception as e:  # report, do not hide
+            out["prefill"] = {"error": repr(e)}
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(w, T, layers)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

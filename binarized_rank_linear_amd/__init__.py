@@ -100,6 +100,8 @@ def lib() -> ctypes.CDLL:
         L.lb_grouped_prepare.restype = ctypes.c_int
         L.lb_grouped_run.argtypes = [_vp, _vp]
         L.lb_grouped_run.restype = ctypes.c_int
+        L.lb_grouped_run_stage.argtypes = [_vp, ctypes.c_int, _vp]
+        L.lb_grouped_run_stage.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -320,3 +322,7 @@ class Group:
 
     def run(self, stream=None):
         _check(lib().lb_grouped_run(self.ws.data_ptr(), _stream_ptr(stream)), "lb_grouped_run")
+
+    def run_stage(self, stage: int, stream=None):
+        _check(lib().lb_grouped_run_stage(self.ws.data_ptr(), stage, _stream_ptr(stream)),
+               "lb_grouped_run_stage")

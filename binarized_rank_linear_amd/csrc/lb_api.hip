@@ -396,4 +396,17 @@ int lb_grouped_run(void *ws, void *stream) {
     return LB_OK;
 }
 
+int lb_grouped_run_stage(void *ws, int stage, void *stream) {
+    if (stage != 1 && stage != 2) return LB_EINVAL;
+    GroupRecord g;
+    {
+        std::lock_guard<std::mutex> lk(g_groups_mu);
+        auto it = g_groups.find(ws);
+        if (it == g_groups.end()) return LB_EINVAL;
+        if (!it->second.fused) return LB_EUNSUPPORTED;
+        g.state = it->second.state;
+    }
+    return mfma_group_run(g.state.data(), (hipStream_t)stream, stage);
+}
+
 }  // extern "C"

@@ -17,16 +17,20 @@
 // one 16-byte load gives a lane four consecutive rows of one plane and a wave
 // covers 64 rows x 4 planes (four 16-row MFMA instances share one B operand).
 //
-// Two launches per call or per group of linears:
+// Three launches per call or per group of linears (the kernel boundaries are
+// the only cross-workgroup synchronisation: a device-scope fence would write
+// back the whole L2 of an XCD on gfx950):
 //   stage 1: item = (linear, path, chunk of d_in, group of 256 latents).  The
-//            workgroup turns g (.) x for its chunk into fp8 limbs in LDS, streams
-//            the V planes and writes partial latent sums.  The last workgroup
-//            of each (linear, path, latent group) -- found with an atomic
-//            counter -- adds the chunk partials in chunk order, scales by l and
-//            writes the stage-2 B operand (limbs of t) in MFMA lane order.
+//            workgroup issues its V-plane loads, turns g (.) x for its chunk
+//            into fp8 limbs in LDS meanwhile, and writes partial latent sums.
+//   latent:  item = (linear, path, group of 256 latents): adds the chunk
+//            partials in chunk order, scales by l and writes the stage-2 B
+//            operands (limbs of t) in MFMA lane order.
 //   stage 2: item = (linear, block of output rows).  The workgroup copies the
-//            B operand of its linear into LDS, streams the U planes of both
+//            B operands of its linear into LDS, streams the U planes of both
 //            paths and writes y = sum_p h_p * z_p.
+#include <vector>
+
 #include "lb_internal.h"
 
 namespace lb {
@@ -44,6 +48,7 @@ constexpr int kRG = kWaves * kTile;       // stage-1 latent rows per workgroup
 constexpr int kBop = 64 * 32;             // bytes of one fp8 B operand (64 lanes x 32)
 constexpr int kBopS = kBop + 64;          // plus one scale byte per lane
 constexpr int kLdsBudget = 64 * 1024;
+constexpr int kMaxKcg = 16;               // K-groups per stage-1 chunk (loads in flight per wave)
 
 // Per-linear schedule and workspace pointers (device-resident for groups).
 struct MLin {
@@ -54,24 +59,23 @@ struct MLin {
     int64_t ld_v, ld_u, d_in, d_out;
     int32_t r_p, P;
     int32_t kw_v, kw_u;   // planes of V (per path) and of U (per path)
-    int32_t kcg;          // K-groups (128 inputs) per stage-1 chunk
+    int32_t kcg;          // K-groups (128 inputs) per stage-1 chunk, <= kMaxKcg
     int32_t nchunks;      // stage-1 chunks along d_in
     int32_t nrg;          // 256-latent groups per path
     int32_t kg2;          // stage-2 K-groups per path
     int32_t rows2;        // output rows per stage-2 item
     int32_t n2;           // stage-2 items
-    int64_t item1, item2; // first item of this linear in each stage
+    int64_t item1, itemF, item2;   // first item of this linear in each launch
     float *part;          // [nchunks][T][P*r_p]
     uint8_t *tb;          // [P][kg2][NB] operands of kBopS bytes
-    uint32_t *cnt;        // [P][nrg]
 };
 
 struct MRun {
-    int T, NL, NB, x_dtype, y_dtype;
-    int64_t items1, items2;
+    int T, x_dtype, y_dtype;
+    int ops2;                  // B operands the stage-2 LDS holds at once
+    int64_t items1, itemsF, items2;
     const MLin *table;         // null: the single linear passed by value
-    const int32_t *lin1;       // item -> linear (stage 1), null for one linear
-    const int32_t *lin2;
+    const int32_t *lin1, *linF, *lin2;   // item -> linear, per launch
 };
 
 __device__ __forceinline__ float ldexp2(float v, int e) { return __builtin_amdgcn_ldexpf(v, e); }
@@ -195,14 +199,42 @@ __device__ __forceinline__ MLin pick(const MRun &run, const MLin &single, const 
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
+// Store 16 consecutive outputs y[off + row0 .. row0 + 16) (rows < d_out),
+// vectorised when aligned and whole.
+__device__ __forceinline__ void store_rows16(void *y, int dtype, int64_t off, int64_t row0,
+                                             int64_t d_out, const float (&v)[16]) {
+    const int64_t e0 = off + row0;
+    if (dtype == LB_BF16) {
+        if (row0 + 16 <= d_out && ((uintptr_t)((uint16_t *)y + e0) & 15) == 0) {
+            v4u a, b;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                a[q] = (uint32_t)f32_to_bf16(v[2 * q]) | ((uint32_t)f32_to_bf16(v[2 * q + 1]) << 16);
+                b[q] = (uint32_t)f32_to_bf16(v[8 + 2 * q]) | ((uint32_t)f32_to_bf16(v[9 + 2 * q]) << 16);
+            }
+            v4u *p = (v4u *)((uint16_t *)y + e0);
+            p[0] = a;
+            p[1] = b;
+            return;
+        }
+    } else if (row0 + 16 <= d_out && ((uintptr_t)((float *)y + e0) & 15) == 0) {
+        v4f *p = (v4f *)((float *)y + e0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) p[q] = v4f{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+        return;
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+        if (row0 + q < d_out) store_act(y, dtype, e0 + q, v[q]);
+}
+
 // ---------------------------------------------------------------------------
-// stage 1
+// stage 1: partial latent sums u = sign(V_p)^T (g_p (.) x) over one chunk
 // ---------------------------------------------------------------------------
 
 template <int NL, int NB>
 __global__ __launch_bounds__(kThreads) void k_stage1(MRun run, MLin single) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    __shared__ int s_last;
     const MLin L = pick(run, single, run.lin1);
     const int64_t local = (int64_t)blockIdx.x - L.item1;
     const int rg = (int)(local % L.nrg);
@@ -210,7 +242,22 @@ __global__ __launch_bounds__(kThreads) void k_stage1(MRun run, MLin single) {
     const int p = (int)(local / ((int64_t)L.nrg * L.nchunks));
     const int T = run.T;
     const int lane = threadIdx.x & 63, wave = wave_id();
+    const int r16 = lane & 15, gq = lane >> 4;
     constexpr int TPB = 16 / NL;
+
+    // ---- the V-plane loads go out first; the limb work below hides them ----
+    const int row0 = rg * kRG + wave * kTile;
+    const int row = row0 + 4 * r16;
+    const bool active = row0 < L.r_p;                            // wave-uniform
+    const uint32_t *vb = L.v_bits + (int64_t)p * L.kw_v * L.ld_v;
+    const int plane0 = c * L.kcg * 4;
+    v4u w[kMaxKcg];
+#pragma unroll
+    for (int j = 0; j < kMaxKcg; ++j) {
+        const int plane = plane0 + 4 * j + gq;
+        const bool ok = active && j < L.kcg && plane < L.kw_v && row < L.r_p;
+        w[j] = load_rows(vb + (int64_t)plane * L.ld_v + row, ok);
+    }
 
     // ---- B operands: fp8 limbs of g_p (.) x over this chunk -----------------
     clear_ops(smem, L.kcg * NB);
@@ -232,117 +279,102 @@ __global__ __launch_bounds__(kThreads) void k_stage1(MRun run, MLin single) {
         }
     }
     __syncthreads();
+    if (!active) return;
 
-    // ---- stream V planes of this chunk for one 64-latent tile per wave ------
-    const int row0 = rg * kRG + wave * kTile;
-    const int r16 = lane & 15, gq = lane >> 4;
-    const int row = row0 + 4 * r16;
-    if (row0 < L.r_p) {
-        v4f acc[4][NB];
+    v4f acc[4][NB];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[m][b] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < kMaxKcg; ++j) {
+        if (j >= L.kcg) continue;                               // uniform; keeps w[] in registers
+        const uint8_t *ops = smem + j * NB * kBopS;
+        v8i bo[NB];
+        int sb[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            bo[b] = load_bop(ops + b * kBopS);
+            sb[b] = ops[b * kBopS + kBop + lane];
+        }
+        const uint32_t ws[4] = {w[j][0], w[j][1], w[j][2], w[j][3]};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const v8i a = unpack_word(ws[m]);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) acc[m][b] = mfma(a, bo[b], acc[m][b], sb[b]);
+        }
+    }
+
+    // ---- partial latent sums: lanes holding a token's first limb write 16 rows
+    const int64_t R = (int64_t)L.P * L.r_p;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const int n = b * TPB + r16 / NL;
+        const bool writer = (r16 % NL) == 0 && r16 / NL < TPB && n < T;
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
-            for (int b = 0; b < NB; ++b) acc[m][b] = v4f{0.f, 0.f, 0.f, 0.f};
-        const uint32_t *vb = L.v_bits + (int64_t)p * L.kw_v * L.ld_v;
-        const int plane0 = c * L.kcg * 4;
-        for (int k0 = 0; k0 < L.kcg; k0 += 8) {
-            v4u w[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int plane = plane0 + 4 * (k0 + j) + gq;
-                const bool ok = (k0 + j) < L.kcg && plane < L.kw_v && row < L.r_p;
-                w[j] = load_rows(vb + (int64_t)plane * L.ld_v + row, ok);
+            for (int i = 0; i < 4; ++i) {
+                const float sum = limb_sum<NL>(acc[m][b][i]);
+                const int k = row0 + 16 * gq + 4 * i + m;
+                if (writer && k < L.r_p)
+                    L.part[((int64_t)c * T + n) * R + (int64_t)p * L.r_p + k] = sum;
             }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                if (k0 + j >= L.kcg) break;
-                const uint8_t *ops = smem + (k0 + j) * NB * kBopS;
-                v8i bo[NB];
-                int sb[NB];
-#pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    bo[b] = load_bop(ops + b * kBopS);
-                    sb[b] = ops[b * kBopS + kBop + lane];
-                }
-                const uint32_t ws[4] = {w[j][0], w[j][1], w[j][2], w[j][3]};
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const v8i a = unpack_word(ws[m]);
-#pragma unroll
-                    for (int b = 0; b < NB; ++b) acc[m][b] = mfma(a, bo[b], acc[m][b], sb[b]);
-                }
-            }
-        }
-        // ---- partial latent sums: lanes holding a token's first limb write 16 rows
-        const int64_t R = (int64_t)L.P * L.r_p;
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            const int cin = r16;
-            const int n = b * TPB + cin / NL;
-            const bool writer = (cin % NL) == 0 && cin / NL < TPB && n < T;
-#pragma unroll
-            for (int m = 0; m < 4; ++m)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float s = limb_sum<NL>(acc[m][b][i]);
-                    const int k = row0 + 16 * gq + 4 * i + m;
-                    if (writer && k < L.r_p)
-                        L.part[((int64_t)c * T + n) * R + (int64_t)p * L.r_p + k] = s;
-                }
-        }
     }
+}
 
-    // ---- the last chunk of this (path, latent group) builds the stage-2 operands
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned old = atomicAdd(&L.cnt[p * L.nrg + rg], 1u);
-        s_last = (old == (unsigned)(L.nchunks - 1));
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
+// ---------------------------------------------------------------------------
+// latents: t = l (.) sum over chunks, as the stage-2 B operands
+// ---------------------------------------------------------------------------
 
+template <int NL, int NB>
+__global__ __launch_bounds__(kThreads) void k_latent(MRun run, MLin single) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const MLin L = pick(run, single, run.linF);
+    const int64_t local = (int64_t)blockIdx.x - L.itemF;
+    const int rg = (int)(local % L.nrg);
+    const int p = (int)(local / L.nrg);
+    const int T = run.T;
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int kg_first = rg * 2;                                  // 256 latents = 2 K-groups
     const int kg_count = (int)imin(2, L.kg2 - kg_first);
     clear_ops(smem, kg_count * NB);
     __syncthreads();
-    {
-        const int64_t R = (int64_t)L.P * L.r_p;
-        const int blocks = kg_count * 4;
-        const int units = T * blocks;
-        const uint16_t *lp = L.l + (int64_t)p * L.r_p;
-        for (int u0 = 2 * wave; u0 < units; u0 += 2 * kWaves) {
-            const int u = u0 + (lane >> 5);
-            const bool ok = u < units;
-            const int n = ok ? u / blocks : 0;
-            const int e = ok ? (u % blocks) * 32 + (lane & 31) : 0;   // latent in group
-            const int k = rg * kRG + e;
-            float v = 0.0f;
-            if (ok && k < L.r_p) {
-                float s = 0.0f;
-                for (int cc = 0; cc < L.nchunks; ++cc)
-                    s += L.part[((int64_t)cc * T + n) * R + (int64_t)p * L.r_p + k];
-                v = f16_to_f32(lp[k]) * s;
-            }
-            emit_limbs<NL>(v, e & 127, n, ok, smem + (e >> 7) * NB * kBopS);
+    const int64_t R = (int64_t)L.P * L.r_p;
+    const int blocks = kg_count * 4;
+    const int units = T * blocks;
+    const uint16_t *lp = L.l + (int64_t)p * L.r_p;
+    for (int u0 = 2 * wave; u0 < units; u0 += 2 * kWaves) {
+        const int u = u0 + (lane >> 5);
+        const bool ok = u < units;
+        const int n = ok ? u / blocks : 0;
+        const int e = ok ? (u % blocks) * 32 + (lane & 31) : 0;   // latent in group
+        const int k = rg * kRG + e;
+        float v = 0.0f;
+        if (ok && k < L.r_p) {
+            float sum = 0.0f;
+            for (int cc = 0; cc < L.nchunks; ++cc)
+                sum += L.part[((int64_t)cc * T + n) * R + (int64_t)p * L.r_p + k];
+            v = f16_to_f32(lp[k]) * sum;
         }
+        emit_limbs<NL>(v, e & 127, n, ok, smem + (e >> 7) * NB * kBopS);
     }
     __syncthreads();
-    {
-        const int4 *src = (const int4 *)smem;
-        int4 *dst = (int4 *)(L.tb + ((int64_t)p * L.kg2 + kg_first) * NB * kBopS);
-        const int vecs = kg_count * NB * kBopS / 16;
-        for (int i = threadIdx.x; i < vecs; i += kThreads) dst[i] = src[i];
-    }
-    if (threadIdx.x == 0) L.cnt[p * L.nrg + rg] = 0u;   // ready for the next call
+    const int4 *src = (const int4 *)smem;
+    int4 *dst = (int4 *)(L.tb + ((int64_t)p * L.kg2 + kg_first) * NB * kBopS);
+    const int vecs = kg_count * NB * kBopS / 16;
+    for (int i = threadIdx.x; i < vecs; i += kThreads) dst[i] = src[i];
 }
 
 // ---------------------------------------------------------------------------
-// stage 2
+// stage 2: y = sum_p h_p (.) (sign(U_p) t_p)
 // ---------------------------------------------------------------------------
 
-template <int NL, int NB, int TW>
+// One wave's view of a stage-2 work item: 64-row tiles one after another; the
+// U-plane loads of the next batch go out before the current batch is
+// multiplied, and h for the tile's rows is fetched before its last batch.
+template <int NL, int NB>
 __global__ __launch_bounds__(kThreads) void k_stage2(MRun run, MLin single) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const MLin L = pick(run, single, run.lin2);
@@ -351,103 +383,144 @@ __global__ __launch_bounds__(kThreads) void k_stage2(MRun run, MLin single) {
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int r16 = lane & 15, gq = lane >> 4;
     constexpr int TPB = 16 / NL;
-    const int64_t base = local * L.rows2 + (int64_t)wave * TW * kTile;
 
-    v4f acc[TW][2][4][NB];
-#pragma unroll
-    for (int t = 0; t < TW; ++t)
-#pragma unroll
-        for (int p = 0; p < 2; ++p)
-#pragma unroll
-            for (int m = 0; m < 4; ++m)
-#pragma unroll
-                for (int b = 0; b < NB; ++b) acc[t][p][m][b] = v4f{0.f, 0.f, 0.f, 0.f};
+    const int steps = L.P * L.kg2;                 // (path, K-group) pairs, path-major
+    const int ops = run.ops2;                      // steps the LDS holds (a multiple of 8 when < steps)
+    const bool fits = steps <= ops;
+    const int nbat = (int)cdiv(steps, 8);          // 8-step batches per tile
+    const int64_t row_begin = local * L.rows2;
+    const int tiles = (int)imin(L.rows2 / kRG, cdiv(L.d_out - row_begin, kRG));
+    const int units = tiles * nbat;
 
-    const int chunk = kLdsBudget / (NB * kBopS);
+    if (fits) {
+        const int4 *src = (const int4 *)L.tb;
+        int4 *dst = (int4 *)smem;
+        const int vecs = steps * NB * kBopS / 16;
+        for (int i = threadIdx.x; i < vecs; i += kThreads) dst[i] = src[i];
+    }
+
+    auto issue = [&](v4u (&w)[8], int u) {
+        const int t = u / nbat, b = u % nbat;
+        const int64_t row = row_begin + (int64_t)t * kRG + wave * kTile + 4 * r16;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        if (p >= L.P) break;                            // uniform
-        for (int k0 = 0; k0 < L.kg2; k0 += chunk) {
-            const int ns = (int)imin(chunk, L.kg2 - k0);
-            __syncthreads();
-            {
-                const int4 *src = (const int4 *)(L.tb + ((int64_t)p * L.kg2 + k0) * NB * kBopS);
-                int4 *dst = (int4 *)smem;
-                const int vecs = ns * NB * kBopS / 16;
-                for (int i = threadIdx.x; i < vecs; i += kThreads) dst[i] = src[i];
-            }
-            __syncthreads();
-            const uint32_t *ub = L.u_bits + (int64_t)p * L.kw_u * L.ld_u;
+        for (int j = 0; j < 8; ++j) {
+            const int st = b * 8 + j;
+            const int pp = st / L.kg2, kg = st % L.kg2;
+            const int plane = 4 * kg + gq;
+            const bool ok = st < steps && plane < L.kw_u && row < L.d_out;
+            w[j] = load_rows(L.u_bits + ((int64_t)pp * L.kw_u + plane) * L.ld_u + row, ok);
+        }
+    };
+
+    v4f acc[2][4][NB];
 #pragma unroll
-            for (int t = 0; t < TW; ++t) {
-                const int64_t row = base + t * kTile + 4 * r16;
-                const bool row_ok = row < L.d_out;
-                for (int j0 = 0; j0 < ns; j0 += 8) {
-                    v4u w[8];
+    for (int p = 0; p < 2; ++p)
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const int plane = 4 * (k0 + j0 + j) + gq;
-                        const bool ok = (j0 + j) < ns && plane < L.kw_u && row_ok;
-                        w[j] = load_rows(ub + (int64_t)plane * L.ld_u + row, ok);
-                    }
+        for (int m = 0; m < 4; ++m)
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        if (j0 + j >= ns) break;                    // uniform
-                        const uint8_t *ops = smem + (j0 + j) * NB * kBopS;
-                        v8i bo[NB];
-                        int sb[NB];
+            for (int b = 0; b < NB; ++b) acc[p][m][b] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    v4u wc[8];
+    issue(wc, 0);
+    for (int u = 0; u < units; ++u) {
+        const int t = u / nbat, bt = u % nbat;
+        const int64_t rowb = row_begin + (int64_t)t * kRG + wave * kTile + 16 * gq;   // this lane's 16 rows
+        const bool last = bt == nbat - 1;
+        // h of this lane's 16 rows, before the last batch of the tile
+        uint32_t hw[2][8];
+        if (last) {
 #pragma unroll
-                        for (int b = 0; b < NB; ++b) {
-                            bo[b] = load_bop(ops + b * kBopS);
-                            sb[b] = ops[b * kBopS + kBop + lane];
-                        }
-                        const uint32_t ws[4] = {w[j][0], w[j][1], w[j][2], w[j][3]};
+            for (int p = 0; p < 2; ++p) {
+                const uint16_t *hp = L.h + (int64_t)p * L.d_out + rowb;
+                const bool vec = p < L.P && rowb + 16 <= L.d_out && ((uintptr_t)hp & 15) == 0;
+                if (vec) {
+                    const v4u a = *(const v4u *)hp, b2 = *(const v4u *)(hp + 8);
 #pragma unroll
-                        for (int m = 0; m < 4; ++m) {
-                            const v8i a = unpack_word(ws[m]);
+                    for (int q = 0; q < 4; ++q) { hw[p][q] = a[q]; hw[p][4 + q] = b2[q]; }
+                } else {
 #pragma unroll
-                            for (int b = 0; b < NB; ++b) acc[t][p][m][b] = mfma(a, bo[b], acc[t][p][m][b], sb[b]);
-                        }
+                    for (int q = 0; q < 8; ++q) {
+                        const uint32_t lo = (p < L.P && rowb + 2 * q < L.d_out) ? hp[2 * q] : 0u;
+                        const uint32_t hi = (p < L.P && rowb + 2 * q + 1 < L.d_out) ? hp[2 * q + 1] : 0u;
+                        hw[p][q] = lo | (hi << 16);
                     }
                 }
             }
         }
-    }
-
-    // ---- epilogue: y = sum_p h_p z_p, one lane per (token, 16 rows) -----------
+        v4u wn[8];
+        if (u + 1 < units) issue(wn, u + 1);
+        if (!fits && (bt * 8) % ops == 0) {        // next chunk of B operands
+            const int s0 = bt * 8;
+            const int ns = (int)imin(ops, steps - s0);
+            __syncthreads();
+            const int4 *src = (const int4 *)(L.tb + (int64_t)s0 * NB * kBopS);
+            int4 *dst = (int4 *)smem;
+            const int vecs = ns * NB * kBopS / 16;
+            for (int i = threadIdx.x; i < vecs; i += kThreads) dst[i] = src[i];
+        }
+        if (u == 0 || !fits) __syncthreads();
+        const int lds0 = fits ? 0 : ((bt * 8) / ops) * ops;    // first step held in LDS
 #pragma unroll
-    for (int t = 0; t < TW; ++t) {
-        const int64_t rowb = base + t * kTile + 16 * gq;    // this lane's 16 rows
+        for (int j = 0; j < 8; ++j) {
+            const int st = bt * 8 + j;
+            if (st >= steps) continue;                          // uniform
+            const int pp = st / L.kg2;                          // uniform
+            const uint8_t *opp = smem + (st - lds0) * NB * kBopS;
+            v8i bo[NB];
+            int sb[NB];
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            const int cin = r16;
-            const int n = b * TPB + cin / NL;
-            const bool writer = (cin % NL) == 0 && cin / NL < TPB && n < T;
-            float z[2][16];
+            for (int b = 0; b < NB; ++b) {
+                bo[b] = load_bop(opp + b * kBopS);
+                sb[b] = opp[b * kBopS + kBop + lane];
+            }
+            const uint32_t ws[4] = {wc[j][0], wc[j][1], wc[j][2], wc[j][3]};
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const v8i a = unpack_word(ws[m]);
+                if (pp == 0) {
+#pragma unroll
+                    for (int b = 0; b < NB; ++b) acc[0][m][b] = mfma(a, bo[b], acc[0][m][b], sb[b]);
+                } else {
+#pragma unroll
+                    for (int b = 0; b < NB; ++b) acc[1][m][b] = mfma(a, bo[b], acc[1][m][b], sb[b]);
+                }
+            }
+        }
+        if (last) {
+            // y = sum_p h_p z_p for this lane's 16 rows and the token its column carries
+            float hv[2][16];
+#pragma unroll
+            for (int p = 0; p < 2; ++p)
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    hv[p][2 * q] = f16_to_f32((uint16_t)(hw[p][q] & 0xffffu));
+                    hv[p][2 * q + 1] = f16_to_f32((uint16_t)(hw[p][q] >> 16));
+                }
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const int n = b * TPB + r16 / NL;
+                const bool writer = (r16 % NL) == 0 && r16 / NL < TPB && n < T;
+                float yv[16];
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float z0 = limb_sum<NL>(acc[0][m][b][i]);
+                        const float z1 = limb_sum<NL>(acc[1][m][b][i]);
+                        yv[4 * i + m] = hv[0][4 * i + m] * z0 + hv[1][4 * i + m] * z1;
+                    }
+                if (writer) store_rows16(L.y, run.y_dtype, (int64_t)n * L.d_out, rowb, L.d_out, yv);
+            }
 #pragma unroll
             for (int p = 0; p < 2; ++p)
 #pragma unroll
                 for (int m = 0; m < 4; ++m)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) z[p][4 * i + m] = limb_sum<NL>(acc[t][p][m][b][i]);
-            if (writer) {
-#pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    const int64_t j = rowb + q;
-                    if (j < L.d_out) {
-                        float y = f16_to_f32(L.h[j]) * z[0][q];
-                        if (L.P == 2) y += f16_to_f32(L.h[L.d_out + j]) * z[1][q];
-                        store_act(L.y, run.y_dtype, (int64_t)n * L.d_out + j, y);
-                    }
-                }
-            }
+                    for (int b = 0; b < NB; ++b) acc[p][m][b] = v4f{0.f, 0.f, 0.f, 0.f};
         }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) wc[j] = wn[j];
     }
-}
-
-__global__ void k_fill_u32(uint32_t *p, int64_t n, uint32_t v) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < n) p[i] = v;
 }
 
 // ---------------------------------------------------------------------------
@@ -455,7 +528,7 @@ __global__ void k_fill_u32(uint32_t *p, int64_t n, uint32_t v) {
 // ---------------------------------------------------------------------------
 
 struct Shape {
-    int NL, NB, TW;
+    int NL, NB;
 };
 
 bool shape_for(int64_t T, int y_dtype, Shape *s) {
@@ -464,14 +537,25 @@ bool shape_for(int64_t T, int y_dtype, Shape *s) {
     s->NB = (int)cdiv(T, tpb);
     if (s->NB == 3) s->NB = 4;
     if (s->NB > 4 || T < 1) return false;
-    s->TW = s->NB == 1 ? 2 : 1;
     return true;
 }
 
 size_t rup256(size_t n) { return (n + 255) & ~(size_t)255; }
 
+int kcg_cap(const Shape &s) { return (int)imin(kMaxKcg, kLdsBudget / (s.NB * kBopS)); }
+// B operands the stage-2 LDS holds: all steps of the largest linear when they
+// fit, else a multiple of the 8-step batch.
+int ops2_for(const Shape &s, int steps_max) {
+    int cap = kLdsBudget / (s.NB * kBopS);
+    if (cap < 8) cap = 8;                       // one batch; may exceed 64 KB (see launch_all)
+    return steps_max <= cap ? steps_max : (cap / 8) * 8;
+}
+
+constexpr int kTilesPerItem2 = 8;   // 64-row tiles per wave in one stage-2 item
+
 // Fill the schedule fields of m and return the workspace bytes it needs.
 size_t plan_linear(const Linear &a, const Shape &s, bool many, MLin *m) {
+    *m = MLin{};
     m->x = a.x;
     m->y = a.y;
     m->v_bits = a.v_bits;
@@ -488,7 +572,7 @@ size_t plan_linear(const Linear &a, const Shape &s, bool many, MLin *m) {
     m->kw_v = (int32_t)a.kw_v();
     m->kw_u = (int32_t)a.kw_u();
     m->nrg = (int32_t)cdiv(a.r_p, kRG);
-    int kcg = (int)imin(8, kLdsBudget / (s.NB * kBopS));
+    int kcg = kcg_cap(s);
     const int64_t kgv = cdiv(m->kw_v, 4);
     if (!many)   // a lone linear: smaller chunks until the chip has work
         while (kcg > 1 && a.P * m->nrg * cdiv(kgv, kcg) < 512) kcg = (kcg + 1) / 2;
@@ -496,46 +580,65 @@ size_t plan_linear(const Linear &a, const Shape &s, bool many, MLin *m) {
     m->kcg = kcg;
     m->nchunks = (int32_t)cdiv(kgv, kcg);
     m->kg2 = (int32_t)cdiv(m->kw_u, 4);
-    m->rows2 = kWaves * s.TW * kTile;
+    m->rows2 = kRG * kTilesPerItem2;
     m->n2 = (int32_t)cdiv(a.d_out, m->rows2);
-    const size_t cnt = rup256((size_t)a.P * m->nrg * 4);
     const size_t part = rup256((size_t)m->nchunks * a.T * a.P * a.r_p * 4);
     const size_t tb = rup256((size_t)a.P * m->kg2 * s.NB * kBopS);
-    return cnt + part + tb;
+    return part + tb;
 }
 
-void bind_ws(MLin *m, const Linear &a, const Shape &s, uint8_t *ws) {
-    const size_t cnt = rup256((size_t)a.P * m->nrg * 4);
+void bind_ws(MLin *m, const Linear &a, uint8_t *ws) {
     const size_t part = rup256((size_t)m->nchunks * a.T * a.P * a.r_p * 4);
-    m->cnt = (uint32_t *)ws;
-    m->part = (float *)(ws + cnt);
-    m->tb = ws + cnt + part;
+    m->part = (float *)ws;
+    m->tb = ws + part;
 }
 
-size_t lds1(const Shape &s, int kcg) { return (size_t)(kcg > 2 ? kcg : 2) * s.NB * kBopS; }
-size_t lds2(const Shape &s) { return (size_t)(kLdsBudget / (s.NB * kBopS)) * s.NB * kBopS; }
+int64_t items1_of(const MLin &m) { return (int64_t)m.P * m.nchunks * m.nrg; }
+int64_t itemsF_of(const MLin &m) { return (int64_t)m.P * m.nrg; }
 
-template <int NL, int NB, int TW>
-int launch_pair(const MRun &run, const MLin &single, int kcg_max, hipStream_t st) {
-    Shape s{NL, NB, TW};
-    k_stage1<NL, NB><<<(unsigned)run.items1, kThreads, lds1(s, kcg_max), st>>>(run, single);
-    if (int rc = last_launch_status()) return rc;
-    k_stage2<NL, NB, TW><<<(unsigned)run.items2, kThreads, lds2(s), st>>>(run, single);
-    return last_launch_status();
+// stage_mask: bit 0 = stage 1 and the latent pass, bit 1 = stage 2.
+template <int NL, int NB>
+int launch_all(const MRun &run, const MLin &single, int kcg_max, hipStream_t st, int stage_mask) {
+    const size_t l1 = (size_t)(kcg_max > 2 ? kcg_max : 2) * NB * kBopS;
+    if (stage_mask & 1) {
+        k_stage1<NL, NB><<<(unsigned)run.items1, kThreads, l1, st>>>(run, single);
+        if (int rc = last_launch_status()) return rc;
+        k_latent<NL, NB><<<(unsigned)run.itemsF, kThreads, (size_t)2 * NB * kBopS, st>>>(run, single);
+        if (int rc = last_launch_status()) return rc;
+    }
+    if (stage_mask & 2) {
+        const size_t l2 = (size_t)run.ops2 * NB * kBopS;
+        if (run.ops2 < 1 || l2 > 160 * 1024) return LB_EUNSUPPORTED;
+        if (l2 > 64 * 1024) {
+            static bool raised = false;    // once per instantiation (idempotent if raced)
+            if (!raised) {
+                // the largest request this instantiation makes: one 8-step batch
+                const int most = (int)imax((int64_t)l2, (int64_t)8 * NB * kBopS);
+                if (hipFuncSetAttribute((const void *)k_stage2<NL, NB>,
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, most) != hipSuccess)
+                    return LB_EHIP;
+                raised = true;
+            }
+        }
+        k_stage2<NL, NB><<<(unsigned)run.items2, kThreads, l2, st>>>(run, single);
+        if (int rc = last_launch_status()) return rc;
+    }
+    return LB_OK;
 }
 
-int launch_shape(const Shape &s, const MRun &run, const MLin &single, int kcg_max, hipStream_t st) {
+int launch_shape(const Shape &s, const MRun &run, const MLin &single, int kcg_max, hipStream_t st,
+                 int stage_mask = 3) {
     if (s.NL == 2) {
         switch (s.NB) {
-            case 1: return launch_pair<2, 1, 2>(run, single, kcg_max, st);
-            case 2: return launch_pair<2, 2, 1>(run, single, kcg_max, st);
-            case 4: return launch_pair<2, 4, 1>(run, single, kcg_max, st);
+            case 1: return launch_all<2, 1>(run, single, kcg_max, st, stage_mask);
+            case 2: return launch_all<2, 2>(run, single, kcg_max, st, stage_mask);
+            case 4: return launch_all<2, 4>(run, single, kcg_max, st, stage_mask);
         }
     } else {
         switch (s.NB) {
-            case 1: return launch_pair<3, 1, 2>(run, single, kcg_max, st);
-            case 2: return launch_pair<3, 2, 1>(run, single, kcg_max, st);
-            case 4: return launch_pair<3, 4, 1>(run, single, kcg_max, st);
+            case 1: return launch_all<3, 1>(run, single, kcg_max, st, stage_mask);
+            case 2: return launch_all<3, 2>(run, single, kcg_max, st, stage_mask);
+            case 4: return launch_all<3, 4>(run, single, kcg_max, st, stage_mask);
         }
     }
     return LB_EUNSUPPORTED;
@@ -554,7 +657,7 @@ size_t mfma_decode_workspace_bytes(const Linear &a) {
     for (int yd : {LB_BF16, LB_F32}) {
         Shape s;
         if (!shape_for(a.T, yd, &s)) continue;
-        MLin m{};
+        MLin m;
         const size_t b = plan_linear(a, s, false, &m);
         if (b > need) need = b;
     }
@@ -564,23 +667,18 @@ size_t mfma_decode_workspace_bytes(const Linear &a) {
 int mfma_decode_forward(const Linear &a, void *ws, hipStream_t st) {
     Shape s;
     if (!shape_for(a.T, a.y_dtype, &s)) return LB_EUNSUPPORTED;
-    MLin m{};
+    MLin m;
     plan_linear(a, s, false, &m);
-    bind_ws(&m, a, s, (uint8_t *)ws);
-    m.item1 = 0;
-    m.item2 = 0;
+    bind_ws(&m, a, (uint8_t *)ws);
     MRun run{};
     run.T = (int)a.T;
-    run.NL = s.NL;
-    run.NB = s.NB;
     run.x_dtype = a.x_dtype;
     run.y_dtype = a.y_dtype;
-    run.items1 = (int64_t)a.P * m.nchunks * m.nrg;
+    run.ops2 = ops2_for(s, a.P * m.kg2);
+    run.items1 = items1_of(m);
+    run.itemsF = itemsF_of(m);
     run.items2 = m.n2;
     run.table = nullptr;
-    const int64_t ncnt = (int64_t)a.P * m.nrg;
-    k_fill_u32<<<(unsigned)cdiv(ncnt, 256), 256, 0, st>>>(m.cnt, ncnt, 0u);
-    if (int rc = last_launch_status()) return rc;
     return launch_shape(s, run, m, m.kcg, st);
 }
 
@@ -596,72 +694,71 @@ size_t mfma_group_workspace_bytes(const Linear *ls, int n, int64_t T, int y_dtyp
     Shape s;
     if (!shape_for(T, y_dtype, &s)) return 0;
     size_t need = 256 + rup256(sizeof(MLin) * n);
-    int64_t i1 = 0, i2 = 0;
+    int64_t i1 = 0, iF = 0, i2 = 0;
     for (int j = 0; j < n; ++j) {
-        MLin m{};
+        MLin m;
         need += plan_linear(ls[j], s, true, &m);
-        i1 += (int64_t)ls[j].P * m.nchunks * m.nrg;
+        i1 += items1_of(m);
+        iF += itemsF_of(m);
         i2 += m.n2;
     }
-    need += rup256((size_t)i1 * 4) + rup256((size_t)i2 * 4);
+    need += rup256((size_t)i1 * 4) + rup256((size_t)iF * 4) + rup256((size_t)i2 * 4);
     return need;
 }
 
 int mfma_group_prepare(const Linear *ls, int n, int64_t T, int y_dtype, void *ws, size_t ws_bytes,
                        void *host_state, hipStream_t st) {
+    (void)st;
     MGroupHost *hs = (MGroupHost *)host_state;
     if (!shape_for(T, y_dtype, &hs->s)) return LB_EUNSUPPORTED;
     if (ws_bytes < mfma_group_workspace_bytes(ls, n, T, y_dtype)) return LB_EWORKSPACE;
     uint8_t *w = (uint8_t *)ws;
     MLin *table_dev = (MLin *)(w + 256);
     uint8_t *cur = w + 256 + rup256(sizeof(MLin) * n);
-    MLin *tab = new MLin[n];
-    int64_t i1 = 0, i2 = 0;
-    int kcg_max = 1;
+    std::vector<MLin> tab((size_t)n);
+    int64_t i1 = 0, iF = 0, i2 = 0;
+    int kcg_max = 1, steps_max = 1;
     for (int j = 0; j < n; ++j) {
-        MLin &m = tab[j];
+        MLin &m = tab[(size_t)j];
         const size_t b = plan_linear(ls[j], hs->s, true, &m);
-        bind_ws(&m, ls[j], hs->s, cur);
+        bind_ws(&m, ls[j], cur);
         cur += b;
         m.item1 = i1;
+        m.itemF = iF;
         m.item2 = i2;
-        i1 += (int64_t)ls[j].P * m.nchunks * m.nrg;
+        i1 += items1_of(m);
+        iF += itemsF_of(m);
         i2 += m.n2;
         if (m.kcg > kcg_max) kcg_max = m.kcg;
+        if (m.P * m.kg2 > steps_max) steps_max = m.P * m.kg2;
     }
     int32_t *lin1 = (int32_t *)cur;
-    int32_t *lin2 = (int32_t *)(cur + rup256((size_t)i1 * 4));
-    int32_t *h1 = new int32_t[i1], *h2 = new int32_t[i2];
+    int32_t *linF = (int32_t *)(cur + rup256((size_t)i1 * 4));
+    int32_t *lin2 = (int32_t *)(cur + rup256((size_t)i1 * 4) + rup256((size_t)iF * 4));
+    std::vector<int32_t> h1((size_t)i1), hF((size_t)iF), h2((size_t)i2);
     for (int j = 0; j < n; ++j) {
-        const int64_t c1 = (int64_t)ls[j].P * tab[j].nchunks * tab[j].nrg;
-        for (int64_t k = 0; k < c1; ++k) h1[tab[j].item1 + k] = j;
-        for (int64_t k = 0; k < tab[j].n2; ++k) h2[tab[j].item2 + k] = j;
+        const MLin &m = tab[(size_t)j];
+        for (int64_t k = 0; k < items1_of(m); ++k) h1[(size_t)(m.item1 + k)] = j;
+        for (int64_t k = 0; k < itemsF_of(m); ++k) hF[(size_t)(m.itemF + k)] = j;
+        for (int64_t k = 0; k < m.n2; ++k) h2[(size_t)(m.item2 + k)] = j;
     }
-    int rc = LB_OK;
-    if (hipMemcpy(table_dev, tab, sizeof(MLin) * n, hipMemcpyHostToDevice) != hipSuccess ||
-        hipMemcpy(lin1, h1, (size_t)i1 * 4, hipMemcpyHostToDevice) != hipSuccess ||
-        hipMemcpy(lin2, h2, (size_t)i2 * 4, hipMemcpyHostToDevice) != hipSuccess)
-        rc = LB_EHIP;
-    // counters start at zero; every run leaves them at zero
-    for (int j = 0; j < n && rc == LB_OK; ++j)
-        if (hipMemsetAsync(tab[j].cnt, 0, (size_t)ls[j].P * tab[j].nrg * 4, st) != hipSuccess)
-            rc = LB_EHIP;
-    if (rc == LB_OK && hipStreamSynchronize(st) != hipSuccess) rc = LB_EHIP;
-    delete[] tab;
-    delete[] h1;
-    delete[] h2;
-    if (rc) return rc;
+    if (hipMemcpy(table_dev, tab.data(), sizeof(MLin) * n, hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(lin1, h1.data(), (size_t)i1 * 4, hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(linF, hF.data(), (size_t)iF * 4, hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(lin2, h2.data(), (size_t)i2 * 4, hipMemcpyHostToDevice) != hipSuccess)
+        return LB_EHIP;
     MRun &run = hs->run;
     run = MRun{};
     run.T = (int)T;
-    run.NL = hs->s.NL;
-    run.NB = hs->s.NB;
     run.x_dtype = ls[0].x_dtype;
     run.y_dtype = y_dtype;
+    run.ops2 = ops2_for(hs->s, steps_max);
     run.items1 = i1;
+    run.itemsF = iF;
     run.items2 = i2;
     run.table = table_dev;
     run.lin1 = lin1;
+    run.linF = linF;
     run.lin2 = lin2;
     hs->kcg_max = kcg_max;
     return LB_OK;
@@ -669,10 +766,10 @@ int mfma_group_prepare(const Linear *ls, int n, int64_t T, int y_dtype, void *ws
 
 size_t mfma_group_state_bytes() { return sizeof(MGroupHost); }
 
-int mfma_group_run(const void *host_state, hipStream_t st) {
+int mfma_group_run(const void *host_state, hipStream_t st, int stage_mask) {
     const MGroupHost *hs = (const MGroupHost *)host_state;
     MLin dummy{};
-    return launch_shape(hs->s, hs->run, dummy, hs->kcg_max, st);
+    return launch_shape(hs->s, hs->run, dummy, hs->kcg_max, st, stage_mask);
 }
 
 }  // namespace lb

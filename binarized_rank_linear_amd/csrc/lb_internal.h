@@ -84,7 +84,7 @@ size_t mfma_group_workspace_bytes(const Linear *ls, int n, int64_t T, int y_dtyp
 size_t mfma_group_state_bytes();
 int mfma_group_prepare(const Linear *ls, int n, int64_t T, int y_dtype, void *ws, size_t ws_bytes,
                        void *host_state, hipStream_t s);
-int mfma_group_run(const void *host_state, hipStream_t s);
+int mfma_group_run(const void *host_state, hipStream_t s, int stage_mask = 3);
 
 // GEMM (prefill) path.
 size_t gemm_workspace_bytes(const Linear &a);

@@ -191,6 +191,15 @@ int lb_grouped_prepare(const lb_linear_desc *descs, int n, int64_t T, int x_dtyp
  * Runs on the same workspace race. */
 int lb_grouped_run(void *ws, void *stream);
 
+/* One half of lb_grouped_run: stage 1 (all first contractions, sign(V)^T
+ * applied to g (.) x, and the rank-r latents) or stage 2 (all second
+ * contractions and the outputs).  Running stage 1 then stage 2 on one stream
+ * equals lb_grouped_run; stage 2 reads what the preceding stage 1 wrote.
+ * For timing and scheduling the two kernels separately.  LB_EINVAL for a
+ * stage other than 1 or 2; LB_EUNSUPPORTED for a group prepared for a path
+ * that does not run as two group kernels. */
+int lb_grouped_run_stage(void *ws, int stage, void *stream);
+
 #ifdef __cplusplus
 }
 #endif
