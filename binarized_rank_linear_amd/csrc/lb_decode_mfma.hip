@@ -162,17 +162,37 @@ __device__ __forceinline__ void clear_ops(uint8_t *ops, int count) {
     }
 }
 
+// (x & mask) | one with mask = 0x88888888 in an SGPR and one = 0x22222222 in
+// a VGPR: a single v_and_or_b32 (VOP3 on gfx950 takes no literal operand, so
+// the compiler would otherwise split it into an AND and an OR).
+struct Nib {
+    uint32_t mask, one;
+};
+
+__device__ __forceinline__ uint32_t sign_nibbles(uint32_t x, const Nib &k) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(k.mask), "v"(k.one));
+    return r;
+}
+
 // fp4 sign operand of one plane word: slot 8q+i <- bit 4i+q, as +-1.0.
-__device__ __forceinline__ v8i unpack_word(uint32_t w) {
+__device__ __forceinline__ v8i unpack_word(uint32_t w, const Nib &one) {
     v8i a;
-    a[0] = (int)(((w << 3) & 0x88888888u) | 0x22222222u);
-    a[1] = (int)(((w << 2) & 0x88888888u) | 0x22222222u);
-    a[2] = (int)(((w << 1) & 0x88888888u) | 0x22222222u);
-    a[3] = (int)((w & 0x88888888u) | 0x22222222u);
+    a[0] = (int)sign_nibbles(w << 3, one);
+    a[1] = (int)sign_nibbles(w << 2, one);
+    a[2] = (int)sign_nibbles(w << 1, one);
+    a[3] = (int)sign_nibbles(w, one);
     a[4] = a[5] = a[6] = a[7] = 0;
     return a;
 }
 
+// The two constants of sign_nibbles in registers, opaque to constant folding.
+__device__ __forceinline__ Nib nibble_constants() {
+    Nib k;
+    asm volatile("s_mov_b32 %0, 0x88888888" : "=s"(k.mask));
+    asm volatile("v_mov_b32 %0, 0x22222222" : "=v"(k.one));
+    return k;
+}
 __device__ __forceinline__ v8i load_op(const uint8_t *op) {
     const int4 *p = (const int4 *)(op + (threadIdx.x & 63) * 32);
     const int4 lo = p[0], hi = p[1];
@@ -187,10 +207,17 @@ __device__ __forceinline__ v4f mfma(const v8i &act, const v8i &sg, v4f c, int sa
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(act, sg, c, 0, 4, 0, sa, 0, 127);
 }
 
-// Four consecutive rows of one plane (16-byte load), or zeros when out of range.
-__device__ __forceinline__ v4u load_rows(const uint32_t *p, bool ok) {
-    if (!ok) return v4u{0u, 0u, 0u, 0u};
-    return __builtin_nontemporal_load((const v4u *)p);
+// Buffer descriptor of `bytes` bytes at p (raw, stride 0; gfx9-family dword 3).
+// Loads past `bytes` return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int64_t bytes) {
+    const int n = bytes > 0x7fffffff ? 0x7fffffff : (int)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, n, 0x00020000);
+}
+
+// Four consecutive rows of one plane: a 16-byte nontemporal load at byte
+// offset voff of the descriptor (zeros when out of range).
+__device__ __forceinline__ v4u load_rows(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 2);
 }
 
 // The linear of a work item, as a wave-uniform value (matrix instructions
@@ -250,20 +277,22 @@ __global__ __launch_bounds__(kThreads) void k_stage1(MRun run, MLin single) {
     const int T = run.T;
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int r16 = lane & 15, gq = lane >> 4;
+    const Nib one = nibble_constants();
 
     // ---- the V-plane loads go out first; the limb work below hides them ----
     const int row0 = rg * kRG + wave * kTile;
     const int row = row0 + 4 * r16;
     const bool active = row0 < L.r_p;                            // wave-uniform
-    const uint32_t *vb = L.v_bits + (int64_t)p * L.kw_v * L.ld_v;
+    // planes of this path only: planes past d_in read as zeros (their inputs are zero too)
+    const __amdgpu_buffer_rsrc_t rv =
+        make_rsrc(L.v_bits + (int64_t)p * L.kw_v * L.ld_v, (int64_t)L.kw_v * L.ld_v * 4);
     const int plane0 = c * L.kcg * 4;
+    const uint32_t vo = (uint32_t)(((int64_t)(plane0 + gq) * L.ld_v + row) * 4);
+    const uint32_t vstep = (uint32_t)(4 * L.ld_v * 4);                 // one K-group of planes
     v4u w[kMaxKcg];
 #pragma unroll
-    for (int j = 0; j < kMaxKcg; ++j) {
-        const int plane = plane0 + 4 * j + gq;
-        const bool ok = active && j < L.kcg && plane < L.kw_v && row < L.r_p;
-        w[j] = load_rows(vb + (int64_t)plane * L.ld_v + row, ok);
-    }
+    for (int j = 0; j < kMaxKcg; ++j)
+        w[j] = (active && j < L.kcg) ? load_rows(rv, vo + j * vstep) : v4u{0u, 0u, 0u, 0u};
 
     // ---- A operands: fp8 limbs of g_p (.) x over this chunk -----------------
     clear_ops(smem, L.kcg * NB1);
@@ -307,7 +336,7 @@ __global__ __launch_bounds__(kThreads) void k_stage1(MRun run, MLin single) {
         const uint32_t ws[4] = {w[j][0], w[j][1], w[j][2], w[j][3]};
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const v8i sg = unpack_word(ws[m]);
+            const v8i sg = unpack_word(ws[m], one);
 #pragma unroll
             for (int b = 0; b < NB1; ++b) acc[m][b] = mfma(ao[b], sg, acc[m][b], sa[b]);
         }
@@ -397,6 +426,7 @@ __global__ __launch_bounds__(kThreads) void k_stage2(MRun run, MLin single) {
     const int T = run.T;
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int r16 = lane & 15, gq = lane >> 4;
+    const Nib one = nibble_constants();
 
     const int steps = L.P * L.kg2;                 // (path, K-group) pairs, path-major
     const int ops = run.ops2;                      // steps the LDS holds (a multiple of kBatch when < steps)
@@ -413,16 +443,20 @@ __global__ __launch_bounds__(kThreads) void k_stage2(MRun run, MLin single) {
         for (int i = threadIdx.x; i < vecs; i += kThreads) dst[i] = src[i];
     }
 
+    // all U planes of the linear; rows and planes past the end read as zeros
+    const __amdgpu_buffer_rsrc_t ru = make_rsrc(L.u_bits, (int64_t)L.P * L.kw_u * L.ld_u * 4);
+    const uint32_t uo = (uint32_t)(((int64_t)gq * L.ld_u + wave * kTile + 4 * r16) * 4);
     auto issue = [&](v4u (&w)[kBatch], int u) {
         const int t = u / nbat, b = u % nbat;
-        const int64_t row = row_begin + (int64_t)t * kRG + wave * kTile + 4 * r16;
+        const int64_t rowt = row_begin + (int64_t)t * kRG;                 // uniform
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
             const int st = b * kBatch + j;
             const int pp = st / L.kg2, kg = st % L.kg2;
-            const int plane = 4 * kg + gq;
-            const bool ok = st < steps && plane < L.kw_u && row < L.d_out;
-            w[j] = load_rows(L.u_bits + ((int64_t)pp * L.kw_u + plane) * L.ld_u + row, ok);
+            const uint32_t so = (uint32_t)((((int64_t)pp * L.kw_u + 4 * kg) * L.ld_u + rowt) * 4);
+            // a path's last K-group may reach into the next path's planes: those
+            // pair with zero activations
+            w[j] = st < steps ? load_rows(ru, uo + so) : v4u{0u, 0u, 0u, 0u};
         }
     };
 
@@ -485,7 +519,7 @@ __global__ __launch_bounds__(kThreads) void k_stage2(MRun run, MLin single) {
             const uint32_t ws[4] = {wc[j][0], wc[j][1], wc[j][2], wc[j][3]};
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                const v8i sg = unpack_word(ws[m]);
+                const v8i sg = unpack_word(ws[m], one);
 #pragma unroll
                 for (int b = 0; b < NB2; ++b) acc[m][b] = mfma(ao[b], sg, acc[m][b], sa[b]);
             }
