@@ -22,19 +22,22 @@
 // Data layout: packed planes (littlebit.h) put word (w, row) at w*ld + row, so
 // one 16-byte load gives a lane four consecutive rows of one plane and a wave
 // covers 64 rows x 4 planes (four 16-column MFMA instances share one A operand).
+// Activation operands are kept "compact" in global memory: only the rows in use
+// (a 144-byte record each: 128 fp8 bytes in lane-group order, 4 scales), and
+// expanded into the MFMA lane layout in LDS by the kernel that consumes them.
 //
-// Three launches per call or per group of linears (kernel boundaries are the
+// Four launches per call or per group of linears (kernel boundaries are the
 // only cross-workgroup synchronisation: a device-scope fence would write back
 // the whole L2 of an XCD on gfx950):
-//   stage 1: item = (linear, path, chunk of d_in, group of 256 latents).  The
-//            workgroup issues its V-plane loads, turns g (.) x for its chunk
-//            into fp8 limbs in LDS meanwhile, and writes partial latent sums.
+//   prep:    item = (linear, path, range of d_in): fp8 limbs of g (.) x.
+//   stage 1: item = (linear, path, chunk of d_in, group of 256 latents): loads
+//            its operands (before the plane loads, since loads complete in
+//            order), streams the V planes and writes partial latent sums.
 //   latent:  item = (linear, path, group of 256 latents): adds the chunk
-//            partials in chunk order, scales by l and writes the stage-2 A
-//            operands (limbs of t) in MFMA lane order.
-//   stage 2: item = (linear, block of output rows).  The workgroup copies the
-//            A operands of its linear into LDS and each wave walks 64-row tiles,
-//            streaming the U planes of both paths into one accumulator set.
+//            partials in chunk order, scales by l and writes the stage-2
+//            operands (limbs of t).
+//   stage 2: item = (linear, block of output rows): each wave walks 64-row
+//            tiles, streaming the U planes of both paths into one accumulator set.
 #include <vector>
 
 #include "lb_internal.h"
@@ -54,10 +57,12 @@ constexpr int kTile = 64;                 // weight rows per wave tile (4 MFMA i
 constexpr int kRG = kWaves * kTile;       // stage-1 latent rows per workgroup
 constexpr int kOp = 64 * 32;              // bytes of one fp8 operand (64 lanes x 32)
 constexpr int kOpS = kOp + 64;            // plus one scale byte per lane
+constexpr int kRec = 144;                 // compact record: 128 fp8 bytes, 4 scales, padding
 constexpr int kLdsBudget = 64 * 1024;
 constexpr int kMaxKcg = 16;               // K-groups per stage-1 chunk (loads in flight per wave)
 constexpr int kBatch = 8;                 // stage-2 steps per load batch
 constexpr int kTilesPerItem2 = 8;         // 64-row tiles per wave in one stage-2 item
+constexpr int kPreVec = 8;                // operand vectors a thread loads before the plane loads
 
 // Activation-row layout of the A operands.  Stage 1 (one path): token n uses
 // rows (n % TPM1)*S1 + q, S1 = 2 (two limbs) or 4 (three limbs).  Stage 2 (both
@@ -80,23 +85,29 @@ struct MLin {
     int64_t ld_v, ld_u, d_in, d_out;
     int32_t r_p, P;
     int32_t kw_v, kw_u;   // planes of V (per path) and of U (per path)
+    int32_t kgv;          // K-groups of V per path
     int32_t kcg;          // K-groups (128 inputs) per stage-1 chunk, <= kMaxKcg
     int32_t nchunks;      // stage-1 chunks along d_in
+    int32_t kcp;          // K-groups per prep item
+    int32_t nprep;        // prep items per path
     int32_t nrg;          // 256-latent groups per path
     int32_t kg2;          // stage-2 K-groups per path
     int32_t rows2;        // output rows per stage-2 item
     int32_t n2;           // stage-2 items
-    int64_t item1, itemF, item2;   // first item of this linear in each launch
+    int32_t R1, R2;       // activation rows in use (compact records per operand)
+    int32_t pad_;
+    int64_t item0, item1, itemF, item2;   // first item of this linear in each launch
     float *part;          // [nchunks][T][P*r_p]
-    uint8_t *tb;          // [P][kg2][NB2] operands of kOpS bytes
+    uint8_t *pa;          // stage-1 operands, compact: [P][kgv][NB1][R1][kRec]
+    uint8_t *tb;          // stage-2 operands, compact: [P][kg2][NB2][R2][kRec]
 };
 
 struct MRun {
     int T, x_dtype, y_dtype;
     int ops2;                  // stage-2 operands (steps) the LDS holds at once
-    int64_t items1, itemsF, items2;
+    int64_t items0, items1, itemsF, items2;
     const MLin *table;         // null: the single linear passed by value
-    const int32_t *lin1, *linF, *lin2;   // item -> linear, per launch
+    const int32_t *lin0, *lin1, *linF, *lin2;   // item -> linear, per launch
 };
 
 __device__ __forceinline__ float ldexp2(float v, int e) { return __builtin_amdgcn_ldexpf(v, e); }
@@ -109,32 +120,34 @@ __device__ __forceinline__ float from_fp8(uint32_t b) {
     return __builtin_amdgcn_cvt_f32_fp8((int)b, 0);
 }
 
-// Byte offset of (element e of a 128-element K-group, activation row c) in one
-// fp8 operand.  The fp4 sign operand holds bit 4i+q of plane word g in MFMA slot
-// s = 8q+i (fp4 lanes carry K = 32g+s); an fp8 operand holds K in lane group
-// (K mod 64)/16 at byte (K mod 16) + 16*(K >= 64) (measured layout of the
-// f8f6f4 instruction; the scale of K-block g sits in lane c + 16g).
-__device__ __forceinline__ int op_offset(int e, int c) {
+// Where element e of a 128-element K-group goes.  The fp4 sign operand holds
+// bit 4i+q of plane word g in MFMA slot s = 8q+i (fp4 lanes carry K = 32g+s);
+// an fp8 operand holds K in lane group gp = (K mod 64)/16 at byte
+// sp = (K mod 16) + 16*(K >= 64) (measured layout of the f8f6f4 instruction).
+// In the LDS operand, activation row c of lane group gp is lane c + 16*gp
+// (32 bytes); the scale of K-block g of row c sits in lane c + 16*g.
+// In a compact record the row's four lane-group pieces follow each other.
+__device__ __forceinline__ int rec_offset(int e) {
     const int g = e >> 5, bit = e & 31;
     const int s = ((bit & 3) << 3) | (bit >> 2);
     const int K = (g << 5) | s;
     const int gp = (K & 63) >> 4;
     const int sp = (K & 15) | ((K >> 6) << 4);
-    return ((c + (gp << 4)) << 5) + sp;
+    return (gp << 5) + sp;
 }
 
-// The NL limbs of v (element e of a K-group) into operand `op` at activation
-// rows c0 .. c0+NL-1.  Called by whole waves: each 32-lane half handles one
-// 32-element block (one plane word), whose largest magnitude sets the scales
-// 2^(E-7-4q).  Lanes with ok == false take part in the reduction with v = 0
-// and store nothing.
+// The NL limbs of v into a compact record set: data points at (element, row
+// c0) and row c0+q is kRec bytes further; scale points at the K-block scale of
+// row c0; first = the lane holds element 0 of its 32-element block.  Called by
+// whole waves: each 32-lane half handles one 32-element block, whose largest
+// magnitude sets the scales 2^(E-7-4q).  Lanes with ok == false take part in
+// the reduction with v = 0 and store nothing.
 template <int NL>
-__device__ __forceinline__ void emit_limbs(float v, int e, int c0, bool ok, uint8_t *op) {
+__device__ __forceinline__ void emit_limbs(float v, uint8_t *data, uint8_t *scale, bool ok, bool first) {
     float m = fabsf(v);
 #pragma unroll
     for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
     const int E = (int)((__float_as_uint(m) >> 23) & 0xff) - 127;   // floor(log2 m); m == 0 -> -127
-    const int off = op_offset(e, c0);
     float r = v;
 #pragma unroll
     for (int q = 0; q < NL; ++q) {
@@ -142,23 +155,28 @@ __device__ __forceinline__ void emit_limbs(float v, int e, int c0, bool ok, uint
         const uint32_t b = to_fp8(ldexp2(r, -eq));
         r -= ldexp2(from_fp8(b), eq);
         if (ok) {
-            op[off + 32 * q] = (uint8_t)b;              // row c0+q is 32 bytes on
-            if ((e & 31) == 0) {
-                int sc = eq + 127;
-                sc = sc < 0 ? 0 : (sc > 254 ? 254 : sc);
-                op[kOp + c0 + q + ((e >> 5) << 4)] = (uint8_t)sc;
-            }
+            data[kRec * q] = (uint8_t)b;
+            if (first) scale[kRec * q] = (uint8_t)(eq < -127 ? 0 : (eq > 127 ? 254 : eq + 127));
         }
     }
 }
 
-// Zero the fp8 bytes and set scales to 1.0 for `count` operands at ops (LDS).
-__device__ __forceinline__ void clear_ops(uint8_t *ops, int count) {
-    uint32_t *w = (uint32_t *)ops;
-    const int words = count * kOpS / 4;
-    for (int i = threadIdx.x; i < words; i += kThreads) {
-        const int off = (i * 4) % kOpS;
-        w[i] = off >= kOp ? 0x7f7f7f7fu : 0u;
+// Compact operands -> LDS operand layout.  Each operand holds R records of
+// kRec bytes; record r goes to rows r of lane groups 0..3 and its four scales
+// to lanes r + 16g.  One 16-byte vector per call; vector i of the source.
+__device__ __forceinline__ void expand_vec(uint8_t *dst_ops, int i, int R, const v4u v) {
+    const int o = i * 16;
+    const int opi = o / (R * kRec);
+    const int w = o - opi * R * kRec;
+    const int r = w / kRec;
+    const int b = w - r * kRec;
+    uint8_t *op = dst_ops + opi * kOpS;
+    if (b < 128) {
+        *(v4u *)(op + ((r + ((b >> 5) << 4)) << 5) + (b & 31)) = v;
+    } else if (b == 128) {
+        const uint32_t sc = v[0];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) op[kOp + r + 16 * g] = (uint8_t)(sc >> (8 * g));
     }
 }
 
@@ -175,17 +193,6 @@ __device__ __forceinline__ uint32_t sign_nibbles(uint32_t x, const Nib &k) {
     return r;
 }
 
-// fp4 sign operand of one plane word: slot 8q+i <- bit 4i+q, as +-1.0.
-__device__ __forceinline__ v8i unpack_word(uint32_t w, const Nib &one) {
-    v8i a;
-    a[0] = (int)sign_nibbles(w << 3, one);
-    a[1] = (int)sign_nibbles(w << 2, one);
-    a[2] = (int)sign_nibbles(w << 1, one);
-    a[3] = (int)sign_nibbles(w, one);
-    a[4] = a[5] = a[6] = a[7] = 0;
-    return a;
-}
-
 // The two constants of sign_nibbles in registers, opaque to constant folding.
 __device__ __forceinline__ Nib nibble_constants() {
     Nib k;
@@ -193,6 +200,18 @@ __device__ __forceinline__ Nib nibble_constants() {
     asm volatile("v_mov_b32 %0, 0x22222222" : "=v"(k.one));
     return k;
 }
+
+// fp4 sign operand of one plane word: slot 8q+i <- bit 4i+q, as +-1.0.
+__device__ __forceinline__ v8i unpack_word(uint32_t w, const Nib &k) {
+    v8i a;
+    a[0] = (int)sign_nibbles(w << 3, k);
+    a[1] = (int)sign_nibbles(w << 2, k);
+    a[2] = (int)sign_nibbles(w << 1, k);
+    a[3] = (int)sign_nibbles(w, k);
+    a[4] = a[5] = a[6] = a[7] = 0;
+    return a;
+}
+
 __device__ __forceinline__ v8i load_op(const uint8_t *op) {
     const int4 *p = (const int4 *)(op + (threadIdx.x & 63) * 32);
     const int4 lo = p[0], hi = p[1];
@@ -261,6 +280,88 @@ __device__ __forceinline__ void store4(void *y, int dtype, int64_t e0, int64_t r
         if (row + q < d_out) store_act(y, dtype, e0 + q, v[q]);
 }
 
+// Compact operands [nops][R records] of src -> LDS operands at dst.  The first
+// kPreVec vectors of each thread were loaded into pre[] before the caller's
+// plane loads; any remainder is copied here.
+__device__ __forceinline__ void expand_ops(uint8_t *dst, const uint8_t *src, int nops, int R,
+                                           const v4u (&pre)[kPreVec]) {
+    const int vecs = nops * R * kRec / 16;
+#pragma unroll
+    for (int j = 0; j < kPreVec; ++j) {
+        const int i = j * kThreads + (int)threadIdx.x;
+        if (i < vecs) expand_vec(dst, i, R, pre[j]);
+    }
+    for (int i = kPreVec * kThreads + (int)threadIdx.x; i < vecs; i += kThreads)
+        expand_vec(dst, i, R, ((const v4u *)src)[i]);
+}
+
+__device__ __forceinline__ void preload_ops(const uint8_t *src, int nops, int R, v4u (&pre)[kPreVec]) {
+    const int vecs = nops * R * kRec / 16;
+#pragma unroll
+    for (int j = 0; j < kPreVec; ++j) {
+        const int i = j * kThreads + (int)threadIdx.x;
+        pre[j] = i < vecs ? ((const v4u *)src)[i] : v4u{0u, 0u, 0u, 0u};
+    }
+}
+
+// ---------------------------------------------------------------------------
+// prep: fp8 limbs of g_p (.) x as compact stage-1 operands
+// ---------------------------------------------------------------------------
+
+template <int NL, int NB1>
+__global__ __launch_bounds__(kThreads) void k_prep(MRun run, MLin single) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    using R = Rows<NL>;
+    const MLin L = pick(run, single, run.lin0);
+    const int64_t local = (int64_t)blockIdx.x - L.item0;
+    const int c = (int)(local % L.nprep);
+    const int p = (int)(local / L.nprep);
+    const int T = run.T;
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int kg0 = c * L.kcp;
+    const int nkg = (int)imin(L.kcp, L.kgv - kg0);
+    const int opb = L.R1 * kRec;                          // bytes of one compact operand
+
+    // half h of wave w takes 32-element blocks 2w+h, 2w+h+8, ...: its block
+    // within a K-group, and so its byte offset in a record, never change
+    const int h = lane >> 5, el = lane & 31;
+    const int bq = (2 * wave + h) & 3;
+    const int off_e = rec_offset(bq * 32 + el);
+    const int blocks = nkg * 4;
+    const int64_t i0 = (int64_t)kg0 * 128;
+    const uint16_t *gp = L.g + (int64_t)p * L.d_in;
+    constexpr int kPre = 8;
+    for (int n = 0; n < T; ++n) {
+        const int c0 = (n % R::TPM1) * R::S1;
+        uint8_t *opn = smem + (n / R::TPM1) * opb + c0 * kRec;
+        for (int b0 = 2 * wave; b0 < blocks; b0 += 8 * kPre) {
+            float v[kPre];
+#pragma unroll
+            for (int j = 0; j < kPre; ++j) {
+                const int blk = b0 + 8 * j + h;
+                const int64_t i = i0 + blk * 32 + el;
+                v[j] = (blk < blocks && i < L.d_in)
+                           ? f16_to_f32(gp[i]) * load_act(L.x, run.x_dtype, (int64_t)n * L.d_in + i)
+                           : 0.0f;
+            }
+#pragma unroll
+            for (int j = 0; j < kPre; ++j) {
+                const int bw = b0 + 8 * j;                          // wave-uniform
+                if (bw >= blocks) break;
+                const int blk = bw + h;
+                uint8_t *op = opn + (blk >> 2) * NB1 * opb;
+                emit_limbs<NL>(v[j], op + off_e, op + 128 + bq, blk < blocks, el == 0);
+            }
+        }
+    }
+    __syncthreads();
+    // operands of tokens < T only; records of unused rows are never read
+    const int4 *src = (const int4 *)smem;
+    int4 *dst = (int4 *)(L.pa + ((int64_t)p * L.kgv + kg0) * NB1 * opb);
+    const int vecs = nkg * NB1 * opb / 16;
+    for (int i = threadIdx.x; i < vecs; i += kThreads) dst[i] = src[i];
+}
+
 // ---------------------------------------------------------------------------
 // stage 1: partial latent sums u = sign(V_p)^T (g_p (.) x) over one chunk
 // ---------------------------------------------------------------------------
@@ -277,43 +378,33 @@ __global__ __launch_bounds__(kThreads) void k_stage1(MRun run, MLin single) {
     const int T = run.T;
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int r16 = lane & 15, gq = lane >> 4;
-    const Nib one = nibble_constants();
+    const Nib nib = nibble_constants();
 
-    // ---- the V-plane loads go out first; the limb work below hides them ----
+    // operands first: loads complete in issue order, so the LDS fill below
+    // then waits for these only, not for the plane loads
+    const int kg0 = c * L.kcg;
+    const int nkg = (int)imin(L.kcg, L.kgv - kg0);
+    const uint8_t *opsrc = L.pa + ((int64_t)p * L.kgv + kg0) * NB1 * L.R1 * kRec;
+    v4u pre[kPreVec];
+    preload_ops(opsrc, nkg * NB1, L.R1, pre);
+
+    // ---- V-plane loads of this wave's 64-latent tile ------------------------
     const int row0 = rg * kRG + wave * kTile;
     const int row = row0 + 4 * r16;
     const bool active = row0 < L.r_p;                            // wave-uniform
     // planes of this path only: planes past d_in read as zeros (their inputs are zero too)
     const __amdgpu_buffer_rsrc_t rv =
         make_rsrc(L.v_bits + (int64_t)p * L.kw_v * L.ld_v, (int64_t)L.kw_v * L.ld_v * 4);
-    const int plane0 = c * L.kcg * 4;
-    const uint32_t vo = (uint32_t)(((int64_t)(plane0 + gq) * L.ld_v + row) * 4);
+    const uint32_t vo = (uint32_t)(((int64_t)(kg0 * 4 + gq) * L.ld_v + row) * 4);
     const uint32_t vstep = (uint32_t)(4 * L.ld_v * 4);                 // one K-group of planes
     v4u w[kMaxKcg];
 #pragma unroll
     for (int j = 0; j < kMaxKcg; ++j)
-        w[j] = (active && j < L.kcg) ? load_rows(rv, vo + j * vstep) : v4u{0u, 0u, 0u, 0u};
+        w[j] = (active && j < nkg) ? load_rows(rv, vo + j * vstep) : v4u{0u, 0u, 0u, 0u};
 
-    // ---- A operands: fp8 limbs of g_p (.) x over this chunk -----------------
-    clear_ops(smem, L.kcg * NB1);
-    __syncthreads();
-    {
-        const int blocks = L.kcg * 4;                       // 32-element blocks
-        const int units = T * blocks;
-        const int64_t i0 = (int64_t)c * L.kcg * 128;
-        const uint16_t *gp = L.g + (int64_t)p * L.d_in;
-        for (int u0 = 2 * wave; u0 < units; u0 += 2 * kWaves) {
-            const int u = u0 + (lane >> 5);
-            const bool ok = u < units;
-            const int n = ok ? u / blocks : 0;
-            const int e = ok ? (u % blocks) * 32 + (lane & 31) : 0;   // element in chunk
-            const int64_t i = i0 + e;
-            float v = 0.0f;
-            if (ok && i < L.d_in) v = f16_to_f32(gp[i]) * load_act(L.x, run.x_dtype, (int64_t)n * L.d_in + i);
-            uint8_t *op = smem + ((e >> 7) * NB1 + n / R::TPM1) * kOpS;
-            emit_limbs<NL>(v, e & 127, (n % R::TPM1) * R::S1, ok, op);
-        }
-    }
+    // Rows of tokens >= T stay unwritten: an MFMA row only feeds its own
+    // accumulator row, which the epilogue never reads.
+    expand_ops(smem, opsrc, nkg * NB1, L.R1, pre);
     __syncthreads();
     if (!active) return;
 
@@ -324,7 +415,7 @@ __global__ __launch_bounds__(kThreads) void k_stage1(MRun run, MLin single) {
         for (int b = 0; b < NB1; ++b) acc[m][b] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < kMaxKcg; ++j) {
-        if (j >= L.kcg) continue;                               // uniform; keeps w[] in registers
+        if (j >= nkg) continue;                                 // uniform; keeps w[] in registers
         const uint8_t *ops = smem + j * NB1 * kOpS;
         v8i ao[NB1];
         int sa[NB1];
@@ -336,7 +427,7 @@ __global__ __launch_bounds__(kThreads) void k_stage1(MRun run, MLin single) {
         const uint32_t ws[4] = {w[j][0], w[j][1], w[j][2], w[j][3]};
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const v8i sg = unpack_word(ws[m], one);
+            const v8i sg = unpack_word(ws[m], nib);
 #pragma unroll
             for (int b = 0; b < NB1; ++b) acc[m][b] = mfma(ao[b], sg, acc[m][b], sa[b]);
         }
@@ -344,7 +435,6 @@ __global__ __launch_bounds__(kThreads) void k_stage1(MRun run, MLin single) {
 
     // ---- partial latent sums: lane (gq, r16) holds latents row0+4*r16+m -------
     const int64_t Rtot = (int64_t)L.P * L.r_p;
-    const int k0 = row0 + 4 * r16;
 #pragma unroll
     for (int b = 0; b < NB1; ++b) {
 #pragma unroll
@@ -358,15 +448,15 @@ __global__ __launch_bounds__(kThreads) void k_stage1(MRun run, MLin single) {
                 for (int q = 0; q < NL; ++q) sum += acc[m][b][s * R::S1 + q];
                 u[m] = sum;
             }
-            if (n < T && k0 < L.r_p)
-                store4(L.part, LB_F32, ((int64_t)c * T + n) * Rtot + (int64_t)p * L.r_p + k0, k0,
+            if (n < T && row < L.r_p)
+                store4(L.part, LB_F32, ((int64_t)c * T + n) * Rtot + (int64_t)p * L.r_p + row, row,
                        L.r_p, u);
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// latents: t = l (.) sum over chunks, as the stage-2 A operands
+// latents: t = l (.) sum over chunks, as compact stage-2 operands
 // ---------------------------------------------------------------------------
 
 template <int NL, int NB2>
@@ -381,12 +471,19 @@ __global__ __launch_bounds__(kThreads) void k_latent(MRun run, MLin single) {
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int kg_first = rg * 2;                                  // 256 latents = 2 K-groups
     const int kg_count = (int)imin(2, L.kg2 - kg_first);
-    clear_ops(smem, kg_count * NB2);
+    const int opb = L.R2 * kRec;
+    // the other path's rows of these operands must read as zero
+    {
+        uint32_t *w = (uint32_t *)smem;
+        const int words = kg_count * NB2 * opb / 4;
+        for (int i = threadIdx.x; i < words; i += kThreads) w[i] = 0u;
+    }
     __syncthreads();
     const int64_t Rtot = (int64_t)L.P * L.r_p;
     const int blocks = kg_count * 4;
     const int units = T * blocks;
     const uint16_t *lp = L.l + (int64_t)p * L.r_p;
+    const int64_t cs = (int64_t)T * Rtot;
     for (int u0 = 2 * wave; u0 < units; u0 += 2 * kWaves) {
         const int u = u0 + (lane >> 5);
         const bool ok = u < units;
@@ -395,18 +492,29 @@ __global__ __launch_bounds__(kThreads) void k_latent(MRun run, MLin single) {
         const int k = rg * kRG + e;
         float v = 0.0f;
         if (ok && k < L.r_p) {
+            // chunk order fixed; loads of four chunks in flight at once
             float sum = 0.0f;
-            for (int cc = 0; cc < L.nchunks; ++cc)
-                sum += L.part[((int64_t)cc * T + n) * Rtot + (int64_t)p * L.r_p + k];
+            const float *pk = L.part + (int64_t)n * Rtot + (int64_t)p * L.r_p + k;
+            int cc = 0;
+            for (; cc + 4 <= L.nchunks; cc += 4) {
+                const float a0 = pk[cc * cs], a1 = pk[(cc + 1) * cs], a2 = pk[(cc + 2) * cs],
+                            a3 = pk[(cc + 3) * cs];
+                sum += a0;
+                sum += a1;
+                sum += a2;
+                sum += a3;
+            }
+            for (; cc < L.nchunks; ++cc) sum += pk[cc * cs];
             v = f16_to_f32(lp[k]) * sum;
         }
-        uint8_t *op = smem + ((e >> 7) * NB2 + n / R::TPM2) * kOpS;
-        emit_limbs<NL>(v, e & 127, (n % R::TPM2) * R::S2 + p * NL, ok, op);
+        const int row = (n % R::TPM2) * R::S2 + p * NL;
+        uint8_t *op = smem + ((e >> 7) * NB2 + n / R::TPM2) * opb + row * kRec;
+        emit_limbs<NL>(v, op + rec_offset(e & 127), op + 128 + ((e & 127) >> 5), ok, (e & 31) == 0);
     }
     __syncthreads();
     const int4 *src = (const int4 *)smem;
-    int4 *dst = (int4 *)(L.tb + ((int64_t)p * L.kg2 + kg_first) * NB2 * kOpS);
-    const int vecs = kg_count * NB2 * kOpS / 16;
+    int4 *dst = (int4 *)(L.tb + ((int64_t)p * L.kg2 + kg_first) * NB2 * opb);
+    const int vecs = kg_count * NB2 * opb / 16;
     for (int i = threadIdx.x; i < vecs; i += kThreads) dst[i] = src[i];
 }
 
@@ -426,7 +534,7 @@ __global__ __launch_bounds__(kThreads) void k_stage2(MRun run, MLin single) {
     const int T = run.T;
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int r16 = lane & 15, gq = lane >> 4;
-    const Nib one = nibble_constants();
+    const Nib nib = nibble_constants();
 
     const int steps = L.P * L.kg2;                 // (path, K-group) pairs, path-major
     const int ops = run.ops2;                      // steps the LDS holds (a multiple of kBatch when < steps)
@@ -435,28 +543,31 @@ __global__ __launch_bounds__(kThreads) void k_stage2(MRun run, MLin single) {
     const int64_t row_begin = local * L.rows2;
     const int tiles = (int)imin(L.rows2 / kRG, cdiv(L.d_out - row_begin, kRG));
     const int units = tiles * nbat;
+    const int opb = L.R2 * kRec;
 
-    if (fits) {
-        const int4 *src = (const int4 *)L.tb;
-        int4 *dst = (int4 *)smem;
-        const int vecs = steps * NB2 * kOpS / 16;
-        for (int i = threadIdx.x; i < vecs; i += kThreads) dst[i] = src[i];
-    }
+    // operands first (loads complete in issue order)
+    v4u pre[kPreVec];
+    if (fits) preload_ops(L.tb, steps * NB2, L.R2, pre);
 
     // all U planes of the linear; rows and planes past the end read as zeros
     const __amdgpu_buffer_rsrc_t ru = make_rsrc(L.u_bits, (int64_t)L.P * L.kw_u * L.ld_u * 4);
     const uint32_t uo = (uint32_t)(((int64_t)gq * L.ld_u + wave * kTile + 4 * r16) * 4);
-    auto issue = [&](v4u (&w)[kBatch], int u) {
-        const int t = u / nbat, b = u % nbat;
-        const int64_t rowt = row_begin + (int64_t)t * kRG;                 // uniform
+    // (path, K-group) of a batch's first step, advanced without division
+    auto advance = [&](int &pp, int &kg, int n) {
+        for (int i = 0; i < n; ++i)
+            if (++kg == L.kg2) { kg = 0; ++pp; }
+    };
+    auto issue = [&](v4u (&w)[kBatch], int t, int b, int pp, int kg) {
+        const uint32_t rowt4 = (uint32_t)((row_begin + (int64_t)t * kRG) * 4);      // uniform
+        const uint32_t plane4 = (uint32_t)(L.ld_u * 4);
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
             const int st = b * kBatch + j;
-            const int pp = st / L.kg2, kg = st % L.kg2;
-            const uint32_t so = (uint32_t)((((int64_t)pp * L.kw_u + 4 * kg) * L.ld_u + rowt) * 4);
+            const uint32_t so = ((uint32_t)pp * (uint32_t)L.kw_u + 4u * (uint32_t)kg) * plane4 + rowt4;
             // a path's last K-group may reach into the next path's planes: those
             // pair with zero activations
             w[j] = st < steps ? load_rows(ru, uo + so) : v4u{0u, 0u, 0u, 0u};
+            if (++kg == L.kg2) { kg = 0; ++pp; }
         }
     };
 
@@ -467,9 +578,11 @@ __global__ __launch_bounds__(kThreads) void k_stage2(MRun run, MLin single) {
         for (int b = 0; b < NB2; ++b) acc[m][b] = v4f{0.f, 0.f, 0.f, 0.f};
 
     v4u wc[kBatch];
-    issue(wc, 0);
+    issue(wc, 0, 0, 0, 0);
+    if (fits) expand_ops(smem, L.tb, steps * NB2, L.R2, pre);
+    int t = 0, bt = 0, npp = 0, nkg = 0;            // unit in flight; next batch's first step
+    advance(npp, nkg, kBatch);
     for (int u = 0; u < units; ++u) {
-        const int t = u / nbat, bt = u % nbat;
         const int64_t row = row_begin + (int64_t)t * kRG + wave * kTile + 4 * r16;   // this lane's 4 rows
         const bool last = bt == nbat - 1;
         // h of this lane's 4 rows, both paths, before the last batch of the tile
@@ -492,15 +605,18 @@ __global__ __launch_bounds__(kThreads) void k_stage2(MRun run, MLin single) {
             }
         }
         v4u wn[kBatch];
-        if (u + 1 < units) issue(wn, u + 1);
-        if (!fits && (bt * kBatch) % ops == 0) {   // next chunk of A operands
+        const int tn = last ? t + 1 : t, bn = last ? 0 : bt + 1;
+        if (last) npp = nkg = 0;
+        if (u + 1 < units) issue(wn, tn, bn, npp, nkg);
+        advance(npp, nkg, kBatch);
+        if (!fits && (bt * kBatch) % ops == 0) {   // next chunk of operands
             const int s0 = bt * kBatch;
             const int ns = (int)imin(ops, steps - s0);
             __syncthreads();
-            const int4 *src = (const int4 *)(L.tb + (int64_t)s0 * NB2 * kOpS);
-            int4 *dst = (int4 *)smem;
-            const int vecs = ns * NB2 * kOpS / 16;
-            for (int i = threadIdx.x; i < vecs; i += kThreads) dst[i] = src[i];
+            const uint8_t *src = L.tb + (int64_t)s0 * NB2 * opb;
+            const int vecs = ns * NB2 * opb / 16;
+            for (int i = threadIdx.x; i < vecs; i += kThreads)
+                expand_vec(smem, i, L.R2, ((const v4u *)src)[i]);
         }
         if (u == 0 || !fits) __syncthreads();
         const int lds0 = fits ? 0 : ((bt * kBatch) / ops) * ops;    // first step held in LDS
@@ -519,7 +635,7 @@ __global__ __launch_bounds__(kThreads) void k_stage2(MRun run, MLin single) {
             const uint32_t ws[4] = {wc[j][0], wc[j][1], wc[j][2], wc[j][3]};
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                const v8i sg = unpack_word(ws[m], one);
+                const v8i sg = unpack_word(ws[m], nib);
 #pragma unroll
                 for (int b = 0; b < NB2; ++b) acc[m][b] = mfma(ao[b], sg, acc[m][b], sa[b]);
             }
@@ -527,14 +643,14 @@ __global__ __launch_bounds__(kThreads) void k_stage2(MRun run, MLin single) {
         if (last) {
             // y = sum_p h_p z_p: lane (gq, r16) holds activation rows 4gq..4gq+3
             // of weight rows row+m; S2 = 4 puts one token's p0/p1 limbs there,
-            // S2 = 8 splits them over lane groups gq and gq^1.
+            // S2 = 8 splits them over lane groups gq and gq^1.  Both paths add
+            // their limbs in the same order (limb 0 first).
 #pragma unroll
             for (int b = 0; b < NB2; ++b) {
                 float y4[4];
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const v4f a = acc[m][b];
-                    // both paths add their limbs in the same order (limb 0 first)
                     if (NL == 2) {
                         y4[m] = hv[0][m] * (a[0] + a[1]) + hv[1][m] * (a[2] + a[3]);
                     } else {
@@ -556,6 +672,8 @@ __global__ __launch_bounds__(kThreads) void k_stage2(MRun run, MLin single) {
         }
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) wc[j] = wn[j];
+        t = tn;
+        bt = bn;
     }
 }
 
@@ -584,6 +702,8 @@ bool shape_for(int64_t T, int y_dtype, Shape *s) {
 
 size_t rup256(size_t n) { return (n + 255) & ~(size_t)255; }
 
+int rows1(const Shape &s, int64_t T) { return (int)imin(16, T * (s.NL == 2 ? 2 : 4)); }
+int rows2(const Shape &s, int64_t T) { return (int)imin(16, T * (s.NL == 2 ? 4 : 8)); }
 int kcg_cap(const Shape &s) { return (int)imin(kMaxKcg, kLdsBudget / (s.NB1 * kOpS)); }
 
 // Steps the stage-2 LDS holds: all steps of the largest linear when they fit,
@@ -612,14 +732,22 @@ size_t plan_linear(const Linear &a, const Shape &s, bool many, MLin *m) {
     m->P = a.P;
     m->kw_v = (int32_t)a.kw_v();
     m->kw_u = (int32_t)a.kw_u();
+    m->kgv = (int32_t)cdiv(m->kw_v, 4);
     m->nrg = (int32_t)cdiv(a.r_p, kRG);
+    m->R1 = rows1(s, a.T);
+    m->R2 = rows2(s, a.T);
     int kcg = kcg_cap(s);
-    const int64_t kgv = cdiv(m->kw_v, 4);
     if (!many)   // a lone linear: smaller chunks until the chip has work
-        while (kcg > 1 && a.P * m->nrg * cdiv(kgv, kcg) < 512) kcg = (kcg + 1) / 2;
-    if (kcg > kgv) kcg = (int)kgv;
+        while (kcg > 1 && a.P * m->nrg * cdiv(m->kgv, kcg) < 512) kcg = (kcg + 1) / 2;
+    if (kcg > m->kgv) kcg = m->kgv;
     m->kcg = kcg;
-    m->nchunks = (int32_t)cdiv(kgv, kcg);
+    m->nchunks = (int32_t)cdiv(m->kgv, kcg);
+    // prep items: up to 16 K-groups, LDS-bounded
+    int kcp = (int)imin(16, kLdsBudget / (s.NB1 * m->R1 * kRec));
+    if (kcp < 1) kcp = 1;
+    if (kcp > m->kgv) kcp = m->kgv;
+    m->kcp = kcp;
+    m->nprep = (int32_t)cdiv(m->kgv, kcp);
     m->kg2 = (int32_t)cdiv(m->kw_u, 4);
     int tiles = kTilesPerItem2;
     if (!many)   // a lone linear: fewer tiles per item until the chip has work
@@ -627,31 +755,41 @@ size_t plan_linear(const Linear &a, const Shape &s, bool many, MLin *m) {
     m->rows2 = kRG * tiles;
     m->n2 = (int32_t)cdiv(a.d_out, m->rows2);
     const size_t part = rup256((size_t)m->nchunks * a.T * a.P * a.r_p * 4);
-    const size_t tb = rup256((size_t)a.P * m->kg2 * s.NB2 * kOpS);
-    return part + tb;
+    const size_t pa = rup256((size_t)a.P * m->kgv * s.NB1 * m->R1 * kRec);
+    const size_t tb = rup256((size_t)a.P * m->kg2 * s.NB2 * m->R2 * kRec);
+    return part + pa + tb;
 }
 
-void bind_ws(MLin *m, const Linear &a, uint8_t *ws) {
+void bind_ws(MLin *m, const Linear &a, const Shape &s, uint8_t *ws) {
     const size_t part = rup256((size_t)m->nchunks * a.T * a.P * a.r_p * 4);
+    const size_t pa = rup256((size_t)a.P * m->kgv * s.NB1 * m->R1 * kRec);
     m->part = (float *)ws;
-    m->tb = ws + part;
+    m->pa = ws + part;
+    m->tb = ws + part + pa;
 }
 
+int64_t items0_of(const MLin &m) { return (int64_t)m.P * m.nprep; }
 int64_t items1_of(const MLin &m) { return (int64_t)m.P * m.nchunks * m.nrg; }
 int64_t itemsF_of(const MLin &m) { return (int64_t)m.P * m.nrg; }
 
-// stage_mask: bit 0 = stage 1 and the latent pass, bit 1 = stage 2.
+// LDS of each kernel, given the largest per-linear figures of a launch.
+struct Lds {
+    size_t prep, s1, lat, s2;
+};
+
+// stage_mask: bit 0 = prep, stage 1 and the latent pass; bit 1 = stage 2.
 template <int NL, int NB1, int NB2>
-int launch_all(const MRun &run, const MLin &single, int kcg_max, hipStream_t st, int stage_mask) {
+int launch_all(const MRun &run, const MLin &single, const Lds &lds, hipStream_t st, int stage_mask) {
     if (stage_mask & 1) {
-        const size_t l1 = (size_t)kcg_max * NB1 * kOpS;
-        k_stage1<NL, NB1><<<(unsigned)run.items1, kThreads, l1, st>>>(run, single);
+        k_prep<NL, NB1><<<(unsigned)run.items0, kThreads, lds.prep, st>>>(run, single);
         if (int rc = last_launch_status()) return rc;
-        k_latent<NL, NB2><<<(unsigned)run.itemsF, kThreads, (size_t)2 * NB2 * kOpS, st>>>(run, single);
+        k_stage1<NL, NB1><<<(unsigned)run.items1, kThreads, lds.s1, st>>>(run, single);
+        if (int rc = last_launch_status()) return rc;
+        k_latent<NL, NB2><<<(unsigned)run.itemsF, kThreads, lds.lat, st>>>(run, single);
         if (int rc = last_launch_status()) return rc;
     }
     if (stage_mask & 2) {
-        const size_t l2 = (size_t)run.ops2 * NB2 * kOpS;
+        const size_t l2 = lds.s2;
         if (run.ops2 < 1 || l2 > 160 * 1024) return LB_EUNSUPPORTED;
         if (l2 > 64 * 1024) {
             static bool raised = false;    // once per instantiation (idempotent if raced)
@@ -670,20 +808,31 @@ int launch_all(const MRun &run, const MLin &single, int kcg_max, hipStream_t st,
     return LB_OK;
 }
 
-int launch_shape(const Shape &s, const MRun &run, const MLin &single, int kcg_max, hipStream_t st,
+int launch_shape(const Shape &s, const MRun &run, const MLin &single, const Lds &lds, hipStream_t st,
                  int stage_mask = 3) {
     const int key = s.NL * 1000 + s.NB1 * 10 + s.NB2;
     switch (key) {
-        case 2011: return launch_all<2, 1, 1>(run, single, kcg_max, st, stage_mask);
-        case 2012: return launch_all<2, 1, 2>(run, single, kcg_max, st, stage_mask);
-        case 2024: return launch_all<2, 2, 4>(run, single, kcg_max, st, stage_mask);
-        case 2048: return launch_all<2, 4, 8>(run, single, kcg_max, st, stage_mask);
-        case 3011: return launch_all<3, 1, 1>(run, single, kcg_max, st, stage_mask);
-        case 3012: return launch_all<3, 1, 2>(run, single, kcg_max, st, stage_mask);
-        case 3024: return launch_all<3, 2, 4>(run, single, kcg_max, st, stage_mask);
-        case 3048: return launch_all<3, 4, 8>(run, single, kcg_max, st, stage_mask);
+        case 2011: return launch_all<2, 1, 1>(run, single, lds, st, stage_mask);
+        case 2012: return launch_all<2, 1, 2>(run, single, lds, st, stage_mask);
+        case 2024: return launch_all<2, 2, 4>(run, single, lds, st, stage_mask);
+        case 2048: return launch_all<2, 4, 8>(run, single, lds, st, stage_mask);
+        case 3011: return launch_all<3, 1, 1>(run, single, lds, st, stage_mask);
+        case 3012: return launch_all<3, 1, 2>(run, single, lds, st, stage_mask);
+        case 3024: return launch_all<3, 2, 4>(run, single, lds, st, stage_mask);
+        case 3048: return launch_all<3, 4, 8>(run, single, lds, st, stage_mask);
     }
     return LB_EUNSUPPORTED;
+}
+
+void lds_add(Lds *l, const MLin &m, const Shape &s, int ops2) {
+    const size_t prep = (size_t)m.kcp * s.NB1 * m.R1 * kRec;
+    const size_t s1 = (size_t)m.kcg * s.NB1 * kOpS;
+    const size_t lat = (size_t)2 * s.NB2 * m.R2 * kRec;
+    const size_t s2 = (size_t)ops2 * s.NB2 * kOpS;
+    if (prep > l->prep) l->prep = prep;
+    if (s1 > l->s1) l->s1 = s1;
+    if (lat > l->lat) l->lat = lat;
+    if (s2 > l->s2) l->s2 = s2;
 }
 
 }  // namespace
@@ -711,17 +860,20 @@ int mfma_decode_forward(const Linear &a, void *ws, hipStream_t st) {
     if (!shape_for(a.T, a.y_dtype, &s)) return LB_EUNSUPPORTED;
     MLin m;
     plan_linear(a, s, false, &m);
-    bind_ws(&m, a, (uint8_t *)ws);
+    bind_ws(&m, a, s, (uint8_t *)ws);
     MRun run{};
     run.T = (int)a.T;
     run.x_dtype = a.x_dtype;
     run.y_dtype = a.y_dtype;
     run.ops2 = ops2_for(s, a.P * m.kg2);
+    run.items0 = items0_of(m);
     run.items1 = items1_of(m);
     run.itemsF = itemsF_of(m);
     run.items2 = m.n2;
     run.table = nullptr;
-    return launch_shape(s, run, m, m.kcg, st);
+    Lds lds{};
+    lds_add(&lds, m, s, run.ops2);
+    return launch_shape(s, run, m, lds, st);
 }
 
 // ---- groups ------------------------------------------------------------------
@@ -729,22 +881,24 @@ int mfma_decode_forward(const Linear &a, void *ws, hipStream_t st) {
 struct MGroupHost {
     Shape s;
     MRun run;
-    int kcg_max;
+    Lds lds;
 };
 
 size_t mfma_group_workspace_bytes(const Linear *ls, int n, int64_t T, int y_dtype) {
     Shape s;
     if (!shape_for(T, y_dtype, &s)) return 0;
     size_t need = 256 + rup256(sizeof(MLin) * n);
-    int64_t i1 = 0, iF = 0, i2 = 0;
+    int64_t i0 = 0, i1 = 0, iF = 0, i2 = 0;
     for (int j = 0; j < n; ++j) {
         MLin m;
         need += plan_linear(ls[j], s, true, &m);
+        i0 += items0_of(m);
         i1 += items1_of(m);
         iF += itemsF_of(m);
         i2 += m.n2;
     }
-    need += rup256((size_t)i1 * 4) + rup256((size_t)iF * 4) + rup256((size_t)i2 * 4);
+    need += rup256((size_t)i0 * 4) + rup256((size_t)i1 * 4) + rup256((size_t)iF * 4) +
+            rup256((size_t)i2 * 4);
     return need;
 }
 
@@ -758,51 +912,58 @@ int mfma_group_prepare(const Linear *ls, int n, int64_t T, int y_dtype, void *ws
     MLin *table_dev = (MLin *)(w + 256);
     uint8_t *cur = w + 256 + rup256(sizeof(MLin) * n);
     std::vector<MLin> tab((size_t)n);
-    int64_t i1 = 0, iF = 0, i2 = 0;
-    int kcg_max = 1, steps_max = 1;
+    int64_t i0 = 0, i1 = 0, iF = 0, i2 = 0;
+    int steps_max = 1;
     for (int j = 0; j < n; ++j) {
         MLin &m = tab[(size_t)j];
         const size_t b = plan_linear(ls[j], hs->s, true, &m);
-        bind_ws(&m, ls[j], cur);
+        bind_ws(&m, ls[j], hs->s, cur);
         cur += b;
+        m.item0 = i0;
         m.item1 = i1;
         m.itemF = iF;
         m.item2 = i2;
+        i0 += items0_of(m);
         i1 += items1_of(m);
         iF += itemsF_of(m);
         i2 += m.n2;
-        if (m.kcg > kcg_max) kcg_max = m.kcg;
         if (m.P * m.kg2 > steps_max) steps_max = m.P * m.kg2;
     }
-    int32_t *lin1 = (int32_t *)cur;
-    int32_t *linF = (int32_t *)(cur + rup256((size_t)i1 * 4));
-    int32_t *lin2 = (int32_t *)(cur + rup256((size_t)i1 * 4) + rup256((size_t)iF * 4));
-    std::vector<int32_t> h1((size_t)i1), hF((size_t)iF), h2((size_t)i2);
+    MRun &run = hs->run;
+    run = MRun{};
+    run.ops2 = ops2_for(hs->s, steps_max);
+    hs->lds = Lds{};
+    for (int j = 0; j < n; ++j) lds_add(&hs->lds, tab[(size_t)j], hs->s, run.ops2);
+    int32_t *lin0 = (int32_t *)cur;
+    int32_t *lin1 = (int32_t *)((uint8_t *)lin0 + rup256((size_t)i0 * 4));
+    int32_t *linF = (int32_t *)((uint8_t *)lin1 + rup256((size_t)i1 * 4));
+    int32_t *lin2 = (int32_t *)((uint8_t *)linF + rup256((size_t)iF * 4));
+    std::vector<int32_t> h0((size_t)i0), h1((size_t)i1), hF((size_t)iF), h2((size_t)i2);
     for (int j = 0; j < n; ++j) {
         const MLin &m = tab[(size_t)j];
+        for (int64_t k = 0; k < items0_of(m); ++k) h0[(size_t)(m.item0 + k)] = j;
         for (int64_t k = 0; k < items1_of(m); ++k) h1[(size_t)(m.item1 + k)] = j;
         for (int64_t k = 0; k < itemsF_of(m); ++k) hF[(size_t)(m.itemF + k)] = j;
         for (int64_t k = 0; k < m.n2; ++k) h2[(size_t)(m.item2 + k)] = j;
     }
     if (hipMemcpy(table_dev, tab.data(), sizeof(MLin) * n, hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(lin0, h0.data(), (size_t)i0 * 4, hipMemcpyHostToDevice) != hipSuccess ||
         hipMemcpy(lin1, h1.data(), (size_t)i1 * 4, hipMemcpyHostToDevice) != hipSuccess ||
         hipMemcpy(linF, hF.data(), (size_t)iF * 4, hipMemcpyHostToDevice) != hipSuccess ||
         hipMemcpy(lin2, h2.data(), (size_t)i2 * 4, hipMemcpyHostToDevice) != hipSuccess)
         return hip_status(hipGetLastError());
-    MRun &run = hs->run;
-    run = MRun{};
     run.T = (int)T;
     run.x_dtype = ls[0].x_dtype;
     run.y_dtype = y_dtype;
-    run.ops2 = ops2_for(hs->s, steps_max);
+    run.items0 = i0;
     run.items1 = i1;
     run.itemsF = iF;
     run.items2 = i2;
     run.table = table_dev;
+    run.lin0 = lin0;
     run.lin1 = lin1;
     run.linF = linF;
     run.lin2 = lin2;
-    hs->kcg_max = kcg_max;
     return LB_OK;
 }
 
@@ -811,7 +972,7 @@ size_t mfma_group_state_bytes() { return sizeof(MGroupHost); }
 int mfma_group_run(const void *host_state, hipStream_t st, int stage_mask) {
     const MGroupHost *hs = (const MGroupHost *)host_state;
     MLin dummy{};
-    return launch_shape(hs->s, hs->run, dummy, hs->kcg_max, st, stage_mask);
+    return launch_shape(hs->s, hs->run, dummy, hs->lds, st, stage_mask);
 }
 
 }  // namespace lb
