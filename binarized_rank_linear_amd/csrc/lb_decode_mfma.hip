@@ -33,9 +33,10 @@
 //   stage 1: item = (linear, path, chunk of d_in, group of 256 latents): loads
 //            its operands (before the plane loads, since loads complete in
 //            order), streams the V planes and writes partial latent sums.
-//   latent:  item = (linear, path, group of 256 latents): adds the chunk
-//            partials in chunk order, scales by l and writes the stage-2
-//            operands (limbs of t).
+//   latent:  item = (linear, two stage-2 K-groups): adds the chunk partials
+//            in chunk order, scales by l and writes the stage-2 operands
+//            (limbs of t).  Stage-2 K-groups run over the U planes of both
+//            paths back to back, so no plane is read twice.
 //   stage 2: item = (linear, block of output rows): each wave walks 64-row
 //            tiles, streaming the U planes of both paths into one accumulator set.
 #include <vector>
@@ -91,7 +92,7 @@ struct MLin {
     int32_t kcp;          // K-groups per prep item
     int32_t nprep;        // prep items per path
     int32_t nrg;          // 256-latent groups per path
-    int32_t kg2;          // stage-2 K-groups per path
+    int32_t kgs;          // stage-2 K-groups over the planes of all paths (path-major)
     int32_t rows2;        // output rows per stage-2 item
     int32_t n2;           // stage-2 items
     int32_t R1, R2;       // activation rows in use (compact records per operand)
@@ -99,7 +100,7 @@ struct MLin {
     int64_t item0, item1, itemF, item2;   // first item of this linear in each launch
     float *part;          // [nchunks][T][P*r_p]
     uint8_t *pa;          // stage-1 operands, compact: [P][kgv][NB1][R1][kRec]
-    uint8_t *tb;          // stage-2 operands, compact: [P][kg2][NB2][R2][kRec]
+    uint8_t *tb;          // stage-2 operands, compact: [kgs][NB2][R2][kRec]
 };
 
 struct MRun {
@@ -465,14 +466,12 @@ __global__ __launch_bounds__(kThreads) void k_latent(MRun run, MLin single) {
     using R = Rows<NL>;
     const MLin L = pick(run, single, run.linF);
     const int64_t local = (int64_t)blockIdx.x - L.itemF;
-    const int rg = (int)(local % L.nrg);
-    const int p = (int)(local / L.nrg);
     const int T = run.T;
     const int lane = threadIdx.x & 63, wave = wave_id();
-    const int kg_first = rg * 2;                                  // 256 latents = 2 K-groups
-    const int kg_count = (int)imin(2, L.kg2 - kg_first);
+    const int kg_first = (int)local * 2;                          // 2 K-groups = 8 planes
+    const int kg_count = (int)imin(2, L.kgs - kg_first);
     const int opb = L.R2 * kRec;
-    // the other path's rows of these operands must read as zero
+    // every row of these operands that no (token, path, limb) fills reads as zero
     {
         uint32_t *w = (uint32_t *)smem;
         const int words = kg_count * NB2 * opb / 4;
@@ -480,18 +479,20 @@ __global__ __launch_bounds__(kThreads) void k_latent(MRun run, MLin single) {
     }
     __syncthreads();
     const int64_t Rtot = (int64_t)L.P * L.r_p;
-    const int blocks = kg_count * 4;
+    const int blocks = kg_count * 4;                              // planes, one path each
     const int units = T * blocks;
-    const uint16_t *lp = L.l + (int64_t)p * L.r_p;
     const int64_t cs = (int64_t)T * Rtot;
     for (int u0 = 2 * wave; u0 < units; u0 += 2 * kWaves) {
         const int u = u0 + (lane >> 5);
         const bool ok = u < units;
         const int n = ok ? u / blocks : 0;
-        const int e = ok ? (u % blocks) * 32 + (lane & 31) : 0;   // latent in group
-        const int k = rg * kRG + e;
+        const int blk = ok ? u % blocks : 0;
+        const int e = blk * 32 + (lane & 31);                     // element in the two K-groups
+        const int pl = kg_first * 4 + blk;                        // plane over both paths
+        const int p = pl / L.kw_u;                                // uniform per wave half
+        const int k = (pl - p * L.kw_u) * 32 + (lane & 31);       // latent of path p
         float v = 0.0f;
-        if (ok && k < L.r_p) {
+        if (ok && p < L.P && k < L.r_p) {
             // chunk order fixed; loads of four chunks in flight at once
             float sum = 0.0f;
             const float *pk = L.part + (int64_t)n * Rtot + (int64_t)p * L.r_p + k;
@@ -505,15 +506,16 @@ __global__ __launch_bounds__(kThreads) void k_latent(MRun run, MLin single) {
                 sum += a3;
             }
             for (; cc < L.nchunks; ++cc) sum += pk[cc * cs];
-            v = f16_to_f32(lp[k]) * sum;
+            v = f16_to_f32(L.l[(int64_t)p * L.r_p + k]) * sum;
         }
-        const int row = (n % R::TPM2) * R::S2 + p * NL;
+        const int row = (n % R::TPM2) * R::S2 + (p < L.P ? p : 0) * NL;
         uint8_t *op = smem + ((e >> 7) * NB2 + n / R::TPM2) * opb + row * kRec;
-        emit_limbs<NL>(v, op + rec_offset(e & 127), op + 128 + ((e & 127) >> 5), ok, (e & 31) == 0);
+        emit_limbs<NL>(v, op + rec_offset(e & 127), op + 128 + ((e & 127) >> 5), ok && p < L.P,
+                       (e & 31) == 0);
     }
     __syncthreads();
     const int4 *src = (const int4 *)smem;
-    int4 *dst = (int4 *)(L.tb + ((int64_t)p * L.kg2 + kg_first) * NB2 * opb);
+    int4 *dst = (int4 *)(L.tb + (int64_t)kg_first * NB2 * opb);
     const int vecs = kg_count * NB2 * opb / 16;
     for (int i = threadIdx.x; i < vecs; i += kThreads) dst[i] = src[i];
 }
@@ -536,7 +538,10 @@ __global__ __launch_bounds__(kThreads) void k_stage2(MRun run, MLin single) {
     const int r16 = lane & 15, gq = lane >> 4;
     const Nib nib = nibble_constants();
 
-    const int steps = L.P * L.kg2;                 // (path, K-group) pairs, path-major
+    // K-groups run over the U planes of all paths back to back, so a group may
+    // hold the last planes of path 0 and the first of path 1: each path's
+    // activation rows are zero outside its own planes
+    const int steps = L.kgs;
     const int ops = run.ops2;                      // steps the LDS holds (a multiple of kBatch when < steps)
     const bool fits = steps <= ops;
     const int nbat = (int)cdiv(steps, kBatch);     // batches per tile
@@ -552,23 +557,13 @@ __global__ __launch_bounds__(kThreads) void k_stage2(MRun run, MLin single) {
     // all U planes of the linear; rows and planes past the end read as zeros
     const __amdgpu_buffer_rsrc_t ru = make_rsrc(L.u_bits, (int64_t)L.P * L.kw_u * L.ld_u * 4);
     const uint32_t uo = (uint32_t)(((int64_t)gq * L.ld_u + wave * kTile + 4 * r16) * 4);
-    // (path, K-group) of a batch's first step, advanced without division
-    auto advance = [&](int &pp, int &kg, int n) {
-        for (int i = 0; i < n; ++i)
-            if (++kg == L.kg2) { kg = 0; ++pp; }
-    };
-    auto issue = [&](v4u (&w)[kBatch], int t, int b, int pp, int kg) {
-        const uint32_t rowt4 = (uint32_t)((row_begin + (int64_t)t * kRG) * 4);      // uniform
-        const uint32_t plane4 = (uint32_t)(L.ld_u * 4);
+    const uint32_t group4 = (uint32_t)(4 * L.ld_u * 4);            // bytes of one K-group of planes
+    auto issue = [&](v4u (&w)[kBatch], int t, int b) {
+        const uint32_t base = uo + (uint32_t)((row_begin + (int64_t)t * kRG) * 4) +
+                              (uint32_t)(b * kBatch) * group4;
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-            const int st = b * kBatch + j;
-            const uint32_t so = ((uint32_t)pp * (uint32_t)L.kw_u + 4u * (uint32_t)kg) * plane4 + rowt4;
-            // a path's last K-group may reach into the next path's planes: those
-            // pair with zero activations
-            w[j] = st < steps ? load_rows(ru, uo + so) : v4u{0u, 0u, 0u, 0u};
-            if (++kg == L.kg2) { kg = 0; ++pp; }
-        }
+        for (int j = 0; j < kBatch; ++j)
+            w[j] = b * kBatch + j < steps ? load_rows(ru, base + j * group4) : v4u{0u, 0u, 0u, 0u};
     };
 
     v4f acc[4][NB2];
@@ -578,10 +573,9 @@ __global__ __launch_bounds__(kThreads) void k_stage2(MRun run, MLin single) {
         for (int b = 0; b < NB2; ++b) acc[m][b] = v4f{0.f, 0.f, 0.f, 0.f};
 
     v4u wc[kBatch];
-    issue(wc, 0, 0, 0, 0);
+    issue(wc, 0, 0);
     if (fits) expand_ops(smem, L.tb, steps * NB2, L.R2, pre);
-    int t = 0, bt = 0, npp = 0, nkg = 0;            // unit in flight; next batch's first step
-    advance(npp, nkg, kBatch);
+    int t = 0, bt = 0;                              // unit in flight
     for (int u = 0; u < units; ++u) {
         const int64_t row = row_begin + (int64_t)t * kRG + wave * kTile + 4 * r16;   // this lane's 4 rows
         const bool last = bt == nbat - 1;
@@ -606,9 +600,7 @@ __global__ __launch_bounds__(kThreads) void k_stage2(MRun run, MLin single) {
         }
         v4u wn[kBatch];
         const int tn = last ? t + 1 : t, bn = last ? 0 : bt + 1;
-        if (last) npp = nkg = 0;
-        if (u + 1 < units) issue(wn, tn, bn, npp, nkg);
-        advance(npp, nkg, kBatch);
+        if (u + 1 < units) issue(wn, tn, bn);
         if (!fits && (bt * kBatch) % ops == 0) {   // next chunk of operands
             const int s0 = bt * kBatch;
             const int ns = (int)imin(ops, steps - s0);
@@ -748,7 +740,7 @@ size_t plan_linear(const Linear &a, const Shape &s, bool many, MLin *m) {
     if (kcp > m->kgv) kcp = m->kgv;
     m->kcp = kcp;
     m->nprep = (int32_t)cdiv(m->kgv, kcp);
-    m->kg2 = (int32_t)cdiv(m->kw_u, 4);
+    m->kgs = (int32_t)cdiv((int64_t)a.P * m->kw_u, 4);
     int tiles = kTilesPerItem2;
     if (!many)   // a lone linear: fewer tiles per item until the chip has work
         while (tiles > 1 && cdiv(a.d_out, (int64_t)kRG * tiles) < 512) tiles /= 2;
@@ -756,7 +748,7 @@ size_t plan_linear(const Linear &a, const Shape &s, bool many, MLin *m) {
     m->n2 = (int32_t)cdiv(a.d_out, m->rows2);
     const size_t part = rup256((size_t)m->nchunks * a.T * a.P * a.r_p * 4);
     const size_t pa = rup256((size_t)a.P * m->kgv * s.NB1 * m->R1 * kRec);
-    const size_t tb = rup256((size_t)a.P * m->kg2 * s.NB2 * m->R2 * kRec);
+    const size_t tb = rup256((size_t)m->kgs * s.NB2 * m->R2 * kRec);
     return part + pa + tb;
 }
 
@@ -770,7 +762,7 @@ void bind_ws(MLin *m, const Linear &a, const Shape &s, uint8_t *ws) {
 
 int64_t items0_of(const MLin &m) { return (int64_t)m.P * m.nprep; }
 int64_t items1_of(const MLin &m) { return (int64_t)m.P * m.nchunks * m.nrg; }
-int64_t itemsF_of(const MLin &m) { return (int64_t)m.P * m.nrg; }
+int64_t itemsF_of(const MLin &m) { return cdiv(m.kgs, 2); }
 
 // LDS of each kernel, given the largest per-linear figures of a launch.
 struct Lds {
@@ -865,7 +857,7 @@ int mfma_decode_forward(const Linear &a, void *ws, hipStream_t st) {
     run.T = (int)a.T;
     run.x_dtype = a.x_dtype;
     run.y_dtype = a.y_dtype;
-    run.ops2 = ops2_for(s, a.P * m.kg2);
+    run.ops2 = ops2_for(s, m.kgs);
     run.items0 = items0_of(m);
     run.items1 = items1_of(m);
     run.itemsF = itemsF_of(m);
@@ -927,7 +919,7 @@ int mfma_group_prepare(const Linear *ls, int n, int64_t T, int y_dtype, void *ws
         i1 += items1_of(m);
         iF += itemsF_of(m);
         i2 += m.n2;
-        if (m.P * m.kg2 > steps_max) steps_max = m.P * m.kg2;
+        if (m.kgs > steps_max) steps_max = m.kgs;
     }
     MRun &run = hs->run;
     run = MRun{};
