@@ -109,7 +109,9 @@ def cpu_baseline(w, T, layers):
 
 
 def prefill_leg(w, T, steps):
-    """One layer of the workload's linears at T tokens through the GEMM path."""
+    """One layer of the workload's linears at T tokens as one GEMM-path group:
+    stage 1 (and the d_in-piece reduce) for all linears in one launch, then
+    stage 2 in one launch; HIP events bracket each on the launch stream."""
     import torch
     import synth
     import binarized_rank_linear_amd as lb
@@ -120,27 +122,35 @@ def prefill_leg(w, T, steps):
                                            2 if w.residual else 1)
         layer.append(lb.PackedLinear.from_factors(U, V, h, g, l))
         del U, V
-    xs = {d: synth.device_activations(7 + d, T, d, "bf16") for d in {s.d_in for s in w.linears}}
+    xs = {d: synth.device_activations(synth.activation_seed(d), T, d, "bf16")
+          for d in {s.d_in for s in w.linears}}
     ys = [torch.empty((T, lin.d_out), dtype=torch.bfloat16, device="cuda") for lin in layer]
-    wss = [lb.workspace(lb.linear_workspace_bytes(lin, T, lb.LB_PATH_PREFILL)) for lin in layer]
-
-    def run():
-        for lin, y, ws in zip(layer, ys, wss):
-            lb.linear_forward(xs[lin.d_in], lin, torch.bfloat16, lb.LB_PATH_PREFILL, ws=ws, out=y)
-
-    run()
+    grp = lb.Group([(xs[lin.d_in], y, lin) for lin, y in zip(layer, ys)], T, torch.bfloat16,
+                   torch.bfloat16)
+    s = torch.cuda.current_stream()
+    for _ in range(2):
+        grp.run_stage(1)
+        grp.run_stage(2)
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        run()
-    e1.record()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for k in range(steps):
+        ev[k][0].record(s)
+        grp.run_stage(1)
+        ev[k][1].record(s)
+        grp.run_stage(2)
+        ev[k][2].record(s)
     torch.cuda.synchronize()
-    t = e0.elapsed_time(e1) * 1e-3 / steps
-    flops = sum(2 * T * lin.r * (lin.d_in + lin.d_out) for lin in layer)
-    return {"workload": "one layer of the same linears, T=%d (GEMM path)" % T, "T": T,
+    t1 = sum(e[0].elapsed_time(e[1]) for e in ev) / steps * 1e-3
+    t2 = sum(e[1].elapsed_time(e[2]) for e in ev) / steps * 1e-3
+    t = t1 + t2
+    f1 = sum(2 * T * lin.r * lin.d_in for lin in layer)
+    f2 = sum(2 * T * lin.r * lin.d_out for lin in layer)
+    flops = f1 + f2
+    return {"workload": "%s, one layer (%d linears) as one group, T=%d (GEMM path)"
+                        % (w.title, len(layer), T), "T": T,
             "tok_per_s": T / t, "ms_per_layer": t * 1e3,
+            "stage1_us": t1 * 1e6, "stage2_us": t2 * 1e6,
+            "stage1_TFLOPs": f1 / t1 / 1e12, "stage2_TFLOPs": f2 / t2 / 1e12,
             "roofline": {"bound": "mfma", "achieved": flops / t / 1e12, "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": flops / t / 1e12 / BF16_PEAK_TFLOPS}}
 

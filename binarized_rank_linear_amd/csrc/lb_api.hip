@@ -288,20 +288,18 @@ int lb_mlp_forward(const void *x, int x_dtype, void *y, int y_dtype, const lb_fa
 // ---- layer groups ----------------------------------------------------------
 
 namespace {
+enum class GroupKind { Loop, Decode, Gemm };
+
 struct GroupRecord {
     std::vector<lb_linear_desc> descs;
     int64_t T;
     int x_dtype, y_dtype;
     unsigned flags;
     size_t ws_bytes;
-    bool fused;                       // matrix-core group kernels (two launches per run)
+    GroupKind kind;                   // Decode / Gemm: whole-group kernels
     std::vector<uint8_t> state;       // their host-side launch state
 };
 
-bool group_fused(unsigned flags, int64_t T, int y_dtype) {
-    const unsigned p = flags & LB_PATH_MASK;
-    return (p == LB_PATH_AUTO || p == LB_PATH_DECODE) && mfma_decode_supported(T, y_dtype);
-}
 std::mutex g_groups_mu;
 std::unordered_map<void *, GroupRecord> g_groups;
 
@@ -312,33 +310,44 @@ int group_linear(const lb_linear_desc &d, int64_t T, int x_dtype, int y_dtype, L
     if ((rc = check_io(d.x, x_dtype, d.y, y_dtype, a))) return rc;
     return LB_OK;
 }
+
+// Shapes only (pointers unset): enough for sizing and path choice.
+bool group_shapes(const lb_linear_desc *descs, int n, int64_t T, std::vector<Linear> *ls) {
+    ls->assign((size_t)n, Linear{});
+    for (int i = 0; i < n; ++i) {
+        Linear &a = (*ls)[(size_t)i];
+        if (check_shape(descs[i].d_in, descs[i].d_out, descs[i].r, T, descs[i].residual, &a)) return false;
+        a.x_dtype = a.y_dtype = LB_BF16;
+    }
+    return true;
+}
+
+GroupKind group_kind(unsigned flags, int64_t T, int y_dtype, const std::vector<Linear> &ls) {
+    Path p;
+    if (choose_path(flags, T, y_dtype, &p)) return GroupKind::Loop;
+    if (p == Path::MfmaDecode) return GroupKind::Decode;
+    if (p == Path::Gemm && gemm_group_supported(ls.data(), (int)ls.size())) return GroupKind::Gemm;
+    return GroupKind::Loop;
+}
 }  // namespace
 
 size_t lb_grouped_workspace_bytes(const lb_linear_desc *descs, int n, int64_t T, unsigned flags) {
-    if (!descs || n <= 0 || T <= 0 || T > kDecodeMaxT) return 0;
+    if (!descs || n <= 0 || T <= 0) return 0;
+    std::vector<Linear> ls;
+    if (!group_shapes(descs, n, T, &ls)) return 0;
     size_t need = 0;
-    // the fused kernels' table and per-linear scratch (sized for bf16 outputs,
-    // the larger of fp32 when that needs more)
-    {
-        std::vector<Linear> ls((size_t)n);
-        bool ok = true;
-        for (int i = 0; i < n && ok; ++i) {
-            Linear &a = ls[(size_t)i];
-            a = Linear{};
-            ok = check_shape(descs[i].d_in, descs[i].d_out, descs[i].r, T, descs[i].residual, &a) == LB_OK;
-            a.x_dtype = a.y_dtype = LB_BF16;
-        }
-        if (ok)
-            for (int yd : {LB_BF16, LB_F32})
-                if (group_fused(flags, T, yd)) {
-                    const size_t b = mfma_group_workspace_bytes(ls.data(), n, T, yd);
-                    if (b > need) need = b;
-                }
+    // whole-group kernels' tables and per-linear scratch, for either output dtype
+    for (int yd : {LB_BF16, LB_F32}) {
+        const GroupKind k = group_kind(flags, T, yd, ls);
+        size_t b = 0;
+        if (k == GroupKind::Decode) b = mfma_group_workspace_bytes(ls.data(), n, T, yd);
+        if (k == GroupKind::Gemm) b = gemm_group_workspace_bytes(ls.data(), n);
+        if (b > need) need = b;
     }
+    // the linear-by-linear loop
     for (int i = 0; i < n; ++i) {
         const size_t b = lb_linear_workspace_bytes(descs[i].d_in, descs[i].d_out, descs[i].r, T,
                                                    descs[i].residual, flags);
-        if (b == 0 && descs[i].d_in > 0) continue;
         if (b > need) need = b;
     }
     return rup256(need) + 256;
@@ -346,14 +355,13 @@ size_t lb_grouped_workspace_bytes(const lb_linear_desc *descs, int n, int64_t T,
 
 int lb_grouped_prepare(const lb_linear_desc *descs, int n, int64_t T, int x_dtype, int y_dtype,
                        void *ws, size_t ws_bytes, unsigned flags, void *stream) {
-    if (!descs || n <= 0 || T <= 0 || T > kDecodeMaxT) return LB_EINVAL;
+    if (!descs || n <= 0 || T <= 0) return LB_EINVAL;
     Path p;
     int rc;
     if ((rc = choose_path(flags, T, y_dtype, &p))) return rc;
-    for (int i = 0; i < n; ++i) {
-        Linear a{};
-        if ((rc = group_linear(descs[i], T, x_dtype, y_dtype, &a))) return rc;
-    }
+    std::vector<Linear> ls((size_t)n);
+    for (int i = 0; i < n; ++i)
+        if ((rc = group_linear(descs[i], T, x_dtype, y_dtype, &ls[(size_t)i]))) return rc;
     const size_t need = lb_grouped_workspace_bytes(descs, n, T, flags);
     if (!ws || ws_bytes < need) return LB_EWORKSPACE;
     if (!aligned(ws, 256)) return LB_EALIGN;
@@ -364,14 +372,15 @@ int lb_grouped_prepare(const lb_linear_desc *descs, int n, int64_t T, int x_dtyp
     rec.y_dtype = y_dtype;
     rec.flags = flags;
     rec.ws_bytes = ws_bytes;
-    rec.fused = group_fused(flags, T, y_dtype);
-    if (rec.fused) {
-        std::vector<Linear> ls((size_t)n);
-        for (int i = 0; i < n; ++i) group_linear(descs[i], T, x_dtype, y_dtype, &ls[(size_t)i]);
+    rec.kind = group_kind(flags, T, y_dtype, ls);
+    if (rec.kind == GroupKind::Decode) {
         rec.state.assign(mfma_group_state_bytes(), 0);
         if ((rc = mfma_group_prepare(ls.data(), n, T, y_dtype, ws, ws_bytes, rec.state.data(),
                                      (hipStream_t)stream)))
             return rc;
+    } else if (rec.kind == GroupKind::Gemm) {
+        rec.state.assign(gemm_group_state_bytes(), 0);
+        if ((rc = gemm_group_prepare(ls.data(), n, ws, ws_bytes, rec.state.data()))) return rc;
     }
     std::lock_guard<std::mutex> lk(g_groups_mu);
     g_groups[ws] = std::move(rec);
@@ -386,7 +395,8 @@ int lb_grouped_run(void *ws, void *stream) {
         if (it == g_groups.end()) return LB_EINVAL;
         g = it->second;
     }
-    if (g.fused) return mfma_group_run(g.state.data(), (hipStream_t)stream);
+    if (g.kind == GroupKind::Decode) return mfma_group_run(g.state.data(), (hipStream_t)stream);
+    if (g.kind == GroupKind::Gemm) return gemm_group_run(g.state.data(), (hipStream_t)stream);
     void *lws = (char *)ws + 256;
     for (const lb_linear_desc &d : g.descs) {
         const int rc = lb_linear_forward(d.x, g.x_dtype, d.y, g.y_dtype, &d.w, d.d_in, d.d_out, d.r,
@@ -403,9 +413,11 @@ int lb_grouped_run_stage(void *ws, int stage, void *stream) {
         std::lock_guard<std::mutex> lk(g_groups_mu);
         auto it = g_groups.find(ws);
         if (it == g_groups.end()) return LB_EINVAL;
-        if (!it->second.fused) return LB_EUNSUPPORTED;
+        if (it->second.kind == GroupKind::Loop) return LB_EUNSUPPORTED;
+        g.kind = it->second.kind;
         g.state = it->second.state;
     }
+    if (g.kind == GroupKind::Gemm) return gemm_group_run(g.state.data(), (hipStream_t)stream, stage);
     return mfma_group_run(g.state.data(), (hipStream_t)stream, stage);
 }
 

@@ -1,10 +1,620 @@
-// lb_gemm.hip -- MFMA GEMM (prefill) path (placeholder: plain decode kernels).
+// lb_gemm.hip -- prefill path (many tokens) of the LittleBit forward on bf16 matrix cores.
+//
+// Proposition 1 (sesamedisk page, "What the method actually computes") over a
+// block of T tokens is two skinny GEMMs with diagonal scalings between them:
+//   stage 1:  u = X . (diag(g_p) sign(V_p))        M = T, N = latents of all paths, K = d_in
+//             t = l (.) u, rounded to bf16         (the rank-r intermediate, workspace)
+//   stage 2:  y = t . (sign(U_p)^T diag(h_p))      M = T, N = d_out, K = latents of all paths
+// Both run as v_mfma_f32_32x32x16_bf16 with fp32 accumulation ("two smaller
+// binary matmuls with FP16 element-wise scaling between them", same page, the
+// compute paragraph; the scales enter rounded to bf16 here).
+//
+// Sign operand: multiplying by -1 is a sign flip (same page, the note after
+// the proposition), so each operand pair is a bf16 scale pair (g per
+// contraction element in stage 1, h per output column in stage 2) whose sign
+// bits are flipped where the packed bit is 1.  While a K-tile is staged, each
+// packed word is "unzipped" once (even bits to the low half, odd bits to the
+// high half); a pair of adjacent elements is then one shift, one AND and one
+// XOR away: ((X << c) & 0x80008000) ^ scale_pair.
+//
+// The product is computed transposed, D = S . A^T (signs as the first
+// operand), so the accumulator quad of a lane holds 4 consecutive output
+// columns of one token: one 8-byte store of bf16.
+//
+// Tiles: 256 tokens x 128 columns, K-tiles of 64 elements double-buffered in
+// LDS (activations with a 16-byte XOR swizzle, unzipped sign words, scales),
+// 4 waves of 128 x 64.  Stage 1 splits d_in into pieces of at most 8192 when
+// it is longer; a reduce pass then adds the pieces in order.  A launch covers
+// every linear of a group (a table maps work items to linears), and work items
+// are renumbered so that each of the 8 XCDs (own L2) gets a contiguous range:
+// neighbouring tiles share their activation rows.
+#include <vector>
+
 #include "lb_internal.h"
 
 namespace lb {
 
-size_t gemm_workspace_bytes(const Linear &a) { return valu_workspace_bytes(a); }
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-int gemm_forward(const Linear &a, void *ws, hipStream_t s) { return valu_forward(a, ws, s); }
+namespace {
+
+constexpr int kBM = 256;                     // tokens per tile
+constexpr int kBN = 128;                     // output columns per tile
+constexpr int kBK = 64;                      // contraction elements per K-tile (two packed words)
+constexpr int kThreads = 256;
+constexpr int kRowBytes = kBK * 2;           // one activation row of a K-tile (bf16)
+constexpr int kABytes = kBM * kRowBytes;     // 32 KB
+constexpr int kXBytes = 2 * kBN * 4;         // unzipped sign words [2][kBN]
+constexpr int kGBytes = 2 * kBK * 2;         // stage-1 scales, bf16 [path][kBK]
+constexpr int kBuf = kABytes + kXBytes + kGBytes;
+constexpr int kLds = 2 * kBuf;
+constexpr int kMaxKtPerSplit = 128;          // stage-1 K-tiles per piece (8192 inputs)
+
+// One linear of a prefill launch.
+struct GLin {
+    const void *x;
+    void *y;
+    const uint32_t *v_bits, *u_bits;
+    const uint16_t *g, *l, *h;
+    uint16_t *t;          // [T][ldt] bf16 latents; zero outside the P*r_p real ones
+    float *part;          // [nsplit][T][ldt] fp32 stage-1 pieces (nsplit > 1)
+    int64_t ld_v, ld_u, d_in, d_out;
+    int32_t r_p, P;
+    int32_t kw;           // packed words per path along r_p (= U planes per path)
+    int32_t kw_v;         // packed words along d_in (= V planes per path)
+    int32_t ldt;          // latent row stride: P*kw*32 rounded up to kBK
+    int32_t nsplit, ktps; // stage-1 pieces and K-tiles per piece
+    int32_t nkt1, nkt2;   // K-tiles of stage 1 (d_in) and stage 2 (ldt)
+    int32_t mt, nt1, nt2; // token tiles; column tiles of stage 1 (ldt) and stage 2 (d_out)
+    int32_t nred;         // reduce items (nsplit > 1), 0 otherwise
+    int64_t item1, itemR, item2;
+};
+
+struct GRun {
+    int T, x_dtype, y_dtype, pad_;
+    int64_t items1, itemsR, items2;
+    const GLin *table;                       // null: the single linear passed by value
+    const int32_t *lin1, *linR, *lin2;       // item -> linear, per launch
+};
+
+// Work item v of n for block b: each XCD (blocks b % 8) takes a contiguous range.
+__device__ __forceinline__ int64_t xcd_order(int64_t b, int64_t n) {
+    const int64_t x = b & 7, j = b >> 3;
+    const int64_t per = n >> 3, rem = n & 7;
+    return x * per + (x < rem ? x : rem) + j;
+}
+
+// The linear of work item v as a wave-uniform value (matrix instructions ignore
+// the exec mask, so every branch around them must be uniform).
+__device__ __forceinline__ GLin pick(const GRun &run, const GLin &single, const int32_t *map,
+                                     int64_t v) {
+    GLin m = run.table ? run.table[map[v]] : single;
+    static_assert(sizeof(GLin) % 4 == 0, "GLin is copied as 32-bit words");
+    int w[sizeof(GLin) / 4];
+    __builtin_memcpy(w, &m, sizeof(GLin));
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(GLin) / 4); ++i) w[i] = __builtin_amdgcn_readfirstlane(w[i]);
+    __builtin_memcpy(&m, w, sizeof(GLin));
+    return m;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int64_t bytes) {
+    const int n = bytes > 0x7fffffff ? 0x7fffffff : (int)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, n, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+
+// Even bits of x to the low half, odd bits to the high half (inverse perfect
+// shuffle by four delta swaps).
+__device__ __forceinline__ uint32_t unzip_bits(uint32_t x) {
+    uint32_t t;
+    t = (x ^ (x >> 1)) & 0x22222222u; x ^= t ^ (t << 1);
+    t = (x ^ (x >> 2)) & 0x0C0C0C0Cu; x ^= t ^ (t << 2);
+    t = (x ^ (x >> 4)) & 0x00F000F0u; x ^= t ^ (t << 4);
+    t = (x ^ (x >> 8)) & 0x0000FF00u; x ^= t ^ (t << 8);
+    return x;
+}
+
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
+    return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+}
+
+__device__ __forceinline__ f32x16 mfma(const u32x4 &s, const u32x4 &a, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, s),
+                                                   __builtin_bit_cast(bf16x8, a), c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// the two GEMM stages
+// ---------------------------------------------------------------------------
+
+// STAGE 1: A = x (bf16, or fp32 rounded to bf16 when XF32), sign words of V,
+//          scales g; output t (bf16, l applied) or fp32 pieces.
+// STAGE 2: A = t (bf16), sign words of U, scales h; output y.
+template <int STAGE, bool XF32>
+__global__ __launch_bounds__(kThreads, 2) void k_gemm(GRun run, GLin single) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int64_t items = STAGE == 1 ? run.items1 : run.items2;
+    const int64_t v = xcd_order(blockIdx.x, items);
+    const GLin L = pick(run, single, STAGE == 1 ? run.lin1 : run.lin2, v);
+    const int64_t local = v - (STAGE == 1 ? L.item1 : L.item2);
+    const int nt = STAGE == 1 ? L.nt1 : L.nt2;
+    const int ni = (int)(local % nt);
+    const int mi = (int)((local / nt) % L.mt);
+    const int split = STAGE == 1 ? (int)(local / ((int64_t)nt * L.mt)) : 0;
+    const int T = run.T;
+    const int64_t m0 = (int64_t)mi * kBM;
+    const int n0 = ni * kBN;
+    const int kt0 = STAGE == 1 ? split * L.ktps : 0;
+    const int kt1 = STAGE == 1 ? (int)imin(L.nkt1, kt0 + L.ktps) : L.nkt2;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hh = lane >> 5, l32 = lane & 31;
+    const int wm = wave & 1, wn = wave >> 1;
+
+    // ---- staging roles ----
+    // activations: chunk ch (16 bytes = 8 elements) of rows rb + 32c, c = 0..7
+    const int ch = tid & 7, rb = tid >> 3;
+    const int64_t K = STAGE == 1 ? L.d_in : L.ldt;       // elements per activation row
+    constexpr int esz = (STAGE == 1 && XF32) ? 4 : 2;
+    const int rows = (int)imin(kBM, (int64_t)T - m0);
+    const uint8_t *abase = STAGE == 1 ? (const uint8_t *)L.x : (const uint8_t *)L.t;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(abase + m0 * K * esz, (int64_t)rows * K * esz);
+    const uint32_t arow = (uint32_t)(K * esz);
+    const uint32_t lds_a = (uint32_t)(rb * kRowBytes + ((ch ^ (rb & 7)) << 4));
+    // sign words: word w of the K-tile for column n0 + col
+    const int xw = tid >> 7, xcol = tid & 127;
+    const int xn = n0 + xcol;
+    const uint32_t *xsrc;
+    int64_t xstride;
+    bool xcol_ok;
+    if (STAGE == 1) {
+        const int qn = xn >> 5;
+        const int p = qn / L.kw;
+        const int k = (qn - p * L.kw) * 32 + (xn & 31);
+        xcol_ok = p < L.P && k < L.r_p;
+        xsrc = L.v_bits + (xcol_ok ? ((int64_t)p * L.kw_v * L.ld_v + k) : 0);
+        xstride = L.ld_v;
+    } else {
+        xcol_ok = xn < L.d_out;
+        xsrc = L.u_bits + (xcol_ok ? xn : 0);
+        xstride = L.ld_u;
+    }
+    const int xwords = STAGE == 1 ? L.kw_v : L.P * L.kw;   // packed words along K
+
+    u32x4 sa[esz == 4 ? 16 : 8];
+    uint32_t sx = 0, sg = 0;
+
+    auto stage_load = [&](int kt) {
+        const int kel = kt * kBK + 8 * ch;                     // first element of the chunk
+        const bool kok = kel < K;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const uint32_t off = kok ? (uint32_t)(rb + 32 * c) * arow + (uint32_t)kel * esz : 0u;
+            if (esz == 4) {
+                sa[2 * c] = load16(ra, off);
+                sa[2 * c + 1] = load16(ra, off + 16);
+                if (!kok) sa[2 * c] = sa[2 * c + 1] = u32x4{0u, 0u, 0u, 0u};
+            } else {
+                sa[c] = load16(ra, off);
+                if (!kok) sa[c] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+        const int q = kt * 2 + xw;
+        sx = (xcol_ok && q < xwords) ? xsrc[(int64_t)q * xstride] : 0u;
+        if (STAGE == 1 && tid < 64) {
+            const int p = tid >> 5;
+            const int64_t k = (int64_t)kt * kBK + 2 * (tid & 31);
+            const uint16_t *gp = L.g + (int64_t)p * L.d_in;
+            const float g0 = (p < L.P && k < L.d_in) ? f16_to_f32(gp[k]) : 0.0f;
+            const float g1 = (p < L.P && k + 1 < L.d_in) ? f16_to_f32(gp[k + 1]) : 0.0f;
+            sg = bf16_pair(g0, g1);
+        }
+    };
+    auto stage_store = [&](int buf) {
+        uint8_t *A = smem + buf * kBuf;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            u32x4 vv;
+            if (esz == 4) {
+                const u32x4 lo = sa[2 * c], hi = sa[2 * c + 1];
+                vv[0] = bf16_pair(__uint_as_float(lo[0]), __uint_as_float(lo[1]));
+                vv[1] = bf16_pair(__uint_as_float(lo[2]), __uint_as_float(lo[3]));
+                vv[2] = bf16_pair(__uint_as_float(hi[0]), __uint_as_float(hi[1]));
+                vv[3] = bf16_pair(__uint_as_float(hi[2]), __uint_as_float(hi[3]));
+            } else {
+                vv = sa[c];
+            }
+            *(u32x4 *)(A + lds_a + c * 32 * kRowBytes) = vv;
+        }
+        ((uint32_t *)(A + kABytes))[xw * kBN + xcol] = unzip_bits(sx);
+        if (STAGE == 1 && tid < 64) ((uint32_t *)(A + kABytes + kXBytes))[tid] = sg;
+    };
+
+    // ---- per-lane constants of the sign operands ----
+    // column of n-block b for this lane; its path (stage 1) or its h pair per path (stage 2)
+    int gofs[2];
+    uint32_t hpair[2][2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const int n = n0 + wn * 64 + b * 32 + l32;
+        if (STAGE == 1) {
+            const int p = (n >> 5) / L.kw;
+            gofs[b] = (p < L.P ? p : 0) * kBK * 2 + hh * 16;
+        } else {
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const float hv = (p < L.P && n < L.d_out) ? f16_to_f32(L.h[(int64_t)p * L.d_out + n]) : 0.0f;
+                hpair[b][p] = bf16_pair(hv, hv);
+            }
+        }
+    }
+    const uint32_t xshift = 4u - 4u * (uint32_t)hh;
+
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[b][mb][i] = 0.0f;
+
+    auto compute = [&](int buf, int kt) {
+        const uint8_t *A = smem + buf * kBuf;
+        const uint32_t *X = (const uint32_t *)(A + kABytes);
+        const uint8_t *G = A + kABytes + kXBytes;
+#pragma unroll
+        for (int w2 = 0; w2 < 2; ++w2) {
+            uint32_t xs[2];
+#pragma unroll
+            for (int b = 0; b < 2; ++b) xs[b] = X[w2 * kBN + wn * 64 + b * 32 + l32] << xshift;
+            int pq = 0;
+            if (STAGE == 2) pq = (kt * 2 + w2) >= L.kw ? 1 : 0;       // path of this word (uniform)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                u32x4 act[4];
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb) {
+                    const int row = wm * 128 + mb * 32 + l32;
+                    const int chunk = 4 * w2 + 2 * s + hh;
+                    act[mb] = *(const u32x4 *)(A + row * kRowBytes + ((chunk ^ (row & 7)) << 4));
+                }
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    u32x4 sc;
+                    if (STAGE == 1) {
+                        sc = *(const u32x4 *)(G + gofs[b] + (32 * w2 + 16 * s) * 2);
+                    } else {
+                        const uint32_t hp = pq ? hpair[b][1] : hpair[b][0];
+                        sc = u32x4{hp, hp, hp, hp};
+                    }
+                    u32x4 sg4;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        sg4[j] = sc[j] ^ ((xs[b] << (11 - 8 * s - j)) & 0x80008000u);
+#pragma unroll
+                    for (int mb = 0; mb < 4; ++mb) acc[b][mb] = mfma(sg4, act[mb], acc[b][mb]);
+                }
+            }
+        }
+    };
+
+    stage_load(kt0);
+    stage_store(0);
+    __syncthreads();
+    for (int kt = kt0; kt < kt1; ++kt) {
+        const int cur = (kt - kt0) & 1;
+        const bool more = kt + 1 < kt1;                 // uniform
+        if (more) stage_load(kt + 1);
+        compute(cur, kt);
+        if (more) stage_store(cur ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: lane holds columns n .. n+3 of token m per accumulator quad ----
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+        const int64_t m = m0 + wm * 128 + mb * 32 + l32;
+        if (m >= T) continue;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int n = n0 + wn * 64 + b * 32 + 8 * q4 + 4 * hh;
+                float o[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = acc[b][mb][4 * q4 + e];
+                if (STAGE == 1) {
+                    if (n >= L.ldt) continue;
+                    if (L.nsplit > 1) {
+                        float *dst = L.part + ((int64_t)split * T + m) * L.ldt + n;
+                        *(f32x4 *)dst = f32x4{o[0], o[1], o[2], o[3]};
+                    } else {
+                        const int qn = n >> 5;
+                        const int p = qn / L.kw;
+                        const int k = (qn - p * L.kw) * 32 + (n & 31);
+                        float tv[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            tv[e] = (p < L.P && k + e < L.r_p)
+                                        ? f16_to_f32(L.l[(int64_t)p * L.r_p + k + e]) * o[e]
+                                        : 0.0f;
+                        *(u32x2 *)(L.t + m * L.ldt + n) = u32x2{bf16_pair(tv[0], tv[1]), bf16_pair(tv[2], tv[3])};
+                    }
+                } else {
+                    if (n >= L.d_out) continue;
+                    const int64_t e0 = m * L.d_out + n;
+                    if (run.y_dtype == LB_BF16) {
+                        uint16_t *py = (uint16_t *)L.y + e0;
+                        if (n + 4 <= L.d_out && ((uintptr_t)py & 7) == 0) {
+                            *(u32x2 *)py = u32x2{bf16_pair(o[0], o[1]), bf16_pair(o[2], o[3])};
+                            continue;
+                        }
+                    } else {
+                        float *py = (float *)L.y + e0;
+                        if (n + 4 <= L.d_out && ((uintptr_t)py & 15) == 0) {
+                            *(f32x4 *)py = f32x4{o[0], o[1], o[2], o[3]};
+                            continue;
+                        }
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < L.d_out) store_act(L.y, run.y_dtype, e0 + e, o[e]);
+                }
+            }
+        }
+    }
+}
+
+// Stage-1 pieces -> t: the pieces are added in order, then scaled by l.
+// Item = kRedGroups groups of 4 latents (one token row segment each).
+constexpr int kRedGroups = 1024;
+
+__global__ __launch_bounds__(kThreads) void k_reduce(GRun run, GLin single) {
+    const int64_t v = blockIdx.x;
+    const GLin L = pick(run, single, run.linR, v);
+    const int64_t local = v - L.itemR;
+    const int T = run.T;
+    const int64_t groups = (int64_t)T * (L.ldt / 4);
+    const int64_t stride = (int64_t)T * L.ldt;
+    for (int i = threadIdx.x; i < kRedGroups; i += kThreads) {
+        const int64_t gi = local * kRedGroups + i;
+        if (gi >= groups) break;
+        const int64_t m = gi / (L.ldt / 4);
+        const int n = (int)(gi - m * (L.ldt / 4)) * 4;
+        f32x4 s = *(const f32x4 *)(L.part + m * L.ldt + n);
+        for (int sp = 1; sp < L.nsplit; ++sp) {
+            const f32x4 a = *(const f32x4 *)(L.part + sp * stride + m * L.ldt + n);
+            s[0] += a[0];
+            s[1] += a[1];
+            s[2] += a[2];
+            s[3] += a[3];
+        }
+        const int qn = n >> 5;
+        const int p = qn / L.kw;
+        const int k = (qn - p * L.kw) * 32 + (n & 31);
+        float tv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            tv[e] = (p < L.P && k + e < L.r_p) ? f16_to_f32(L.l[(int64_t)p * L.r_p + k + e]) * s[e] : 0.0f;
+        *(u32x2 *)(L.t + m * L.ldt + n) = u32x2{bf16_pair(tv[0], tv[1]), bf16_pair(tv[2], tv[3])};
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+
+size_t rup256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Shapes the GEMM kernels take: 16-byte activation rows (d_in % 8 == 0) and a
+// 16-byte aligned x.  Others run on the vector-ALU kernels.
+bool gemm_shape_ok(const Linear &a) {
+    if (a.d_in % 8 != 0) return false;
+    if (a.x && ((uintptr_t)a.x % 16) != 0) return false;
+    if (a.T > (1ll << 24)) return false;
+    // 32-bit buffer offsets over one 256-token tile of activations or latents
+    if (a.d_in >= (1ll << 21) || a.r_p >= (1ll << 20)) return false;
+    return true;
+}
+
+// Schedule fields of one linear; returns the workspace bytes it needs.
+size_t plan(const Linear &a, GLin *m) {
+    *m = GLin{};
+    m->x = a.x;
+    m->y = a.y;
+    m->v_bits = a.v_bits;
+    m->u_bits = a.u_bits;
+    m->g = a.g;
+    m->l = a.l;
+    m->h = a.h;
+    m->ld_v = a.ld_v;
+    m->ld_u = a.ld_u;
+    m->d_in = a.d_in;
+    m->d_out = a.d_out;
+    m->r_p = (int32_t)a.r_p;
+    m->P = a.P;
+    m->kw = (int32_t)cdiv(a.r_p, 32);
+    m->kw_v = (int32_t)cdiv(a.d_in, 32);
+    m->ldt = (int32_t)rup((int64_t)a.P * m->kw * 32, kBK);
+    m->nkt1 = (int32_t)cdiv(a.d_in, kBK);
+    m->nsplit = (int32_t)cdiv(m->nkt1, kMaxKtPerSplit);
+    m->ktps = (int32_t)cdiv(m->nkt1, m->nsplit);
+    m->nsplit = (int32_t)cdiv(m->nkt1, m->ktps);
+    m->nkt2 = m->ldt / kBK;
+    m->mt = (int32_t)cdiv(a.T, kBM);
+    m->nt1 = (int32_t)cdiv(m->ldt, kBN);
+    m->nt2 = (int32_t)cdiv(a.d_out, kBN);
+    m->nred = m->nsplit > 1 ? (int32_t)cdiv(a.T * (m->ldt / 4), kRedGroups) : 0;
+    const size_t tb = rup256((size_t)a.T * m->ldt * 2);
+    const size_t pb = m->nsplit > 1 ? rup256((size_t)m->nsplit * a.T * m->ldt * 4) : 0;
+    return tb + pb;
+}
+
+void bind(GLin *m, const Linear &a, uint8_t *ws) {
+    m->t = (uint16_t *)ws;
+    m->part = m->nsplit > 1 ? (float *)(ws + rup256((size_t)a.T * m->ldt * 2)) : nullptr;
+}
+
+int64_t items1_of(const GLin &m) { return (int64_t)m.nsplit * m.nt1 * m.mt; }
+int64_t items2_of(const GLin &m) { return (int64_t)m.nt2 * m.mt; }
+
+template <typename K>
+int raise_lds(K kern) {
+    // > 64 KB of dynamic LDS needs an explicit opt-in (once per kernel; idempotent)
+    static bool done = false;
+    if (!done) {
+        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLds) !=
+            hipSuccess)
+            return hip_status(hipGetLastError());
+        done = true;
+    }
+    return LB_OK;
+}
+
+int launch_gemms(const GRun &run, const GLin &single, hipStream_t st) {
+    int rc;
+    if (run.items1 > 0) {
+        if (run.x_dtype == LB_F32) {
+            if ((rc = raise_lds(k_gemm<1, true>))) return rc;
+            k_gemm<1, true><<<(unsigned)run.items1, kThreads, kLds, st>>>(run, single);
+        } else {
+            if ((rc = raise_lds(k_gemm<1, false>))) return rc;
+            k_gemm<1, false><<<(unsigned)run.items1, kThreads, kLds, st>>>(run, single);
+        }
+        if ((rc = last_launch_status())) return rc;
+    }
+    if (run.itemsR > 0) {
+        k_reduce<<<(unsigned)run.itemsR, kThreads, 0, st>>>(run, single);
+        if ((rc = last_launch_status())) return rc;
+    }
+    if (run.items2 > 0) {
+        if ((rc = raise_lds(k_gemm<2, false>))) return rc;
+        k_gemm<2, false><<<(unsigned)run.items2, kThreads, kLds, st>>>(run, single);
+        if ((rc = last_launch_status())) return rc;
+    }
+    return LB_OK;
+}
+
+}  // namespace
+
+size_t gemm_workspace_bytes(const Linear &a) {
+    const size_t v = valu_workspace_bytes(a);
+    if (!gemm_shape_ok(a)) return v;
+    GLin m;
+    const size_t g = plan(a, &m);
+    return g > v ? g : v;     // a misaligned x at run time takes the vector-ALU kernels
+}
+
+int gemm_forward(const Linear &a, void *ws, hipStream_t st) {
+    if (!gemm_shape_ok(a)) return valu_forward(a, ws, st);
+    GLin m;
+    plan(a, &m);
+    bind(&m, a, (uint8_t *)ws);
+    GRun run{};
+    run.T = (int)a.T;
+    run.x_dtype = a.x_dtype;
+    run.y_dtype = a.y_dtype;
+    run.items1 = items1_of(m);
+    run.itemsR = m.nred;
+    run.items2 = items2_of(m);
+    run.table = nullptr;
+    return launch_gemms(run, m, st);
+}
+
+// ---- groups ------------------------------------------------------------------
+
+struct GGroupHost {
+    GRun run;
+};
+
+bool gemm_group_supported(const Linear *ls, int n) {
+    for (int j = 0; j < n; ++j)
+        if (!gemm_shape_ok(ls[j])) return false;
+    return n > 0 && ls[0].T > 0;
+}
+
+size_t gemm_group_workspace_bytes(const Linear *ls, int n) {
+    size_t need = 256 + rup256(sizeof(GLin) * n);
+    int64_t i1 = 0, iR = 0, i2 = 0;
+    for (int j = 0; j < n; ++j) {
+        GLin m;
+        need += plan(ls[j], &m);
+        i1 += items1_of(m);
+        iR += m.nred;
+        i2 += items2_of(m);
+    }
+    return need + rup256((size_t)i1 * 4) + rup256((size_t)iR * 4) + rup256((size_t)i2 * 4);
+}
+
+size_t gemm_group_state_bytes() { return sizeof(GGroupHost); }
+
+int gemm_group_prepare(const Linear *ls, int n, void *ws, size_t ws_bytes, void *host_state) {
+    GGroupHost *hs = (GGroupHost *)host_state;
+    if (!gemm_group_supported(ls, n)) return LB_EUNSUPPORTED;
+    if (ws_bytes < gemm_group_workspace_bytes(ls, n)) return LB_EWORKSPACE;
+    uint8_t *w = (uint8_t *)ws;
+    GLin *table_dev = (GLin *)(w + 256);
+    uint8_t *cur = w + 256 + rup256(sizeof(GLin) * n);
+    std::vector<GLin> tab((size_t)n);
+    int64_t i1 = 0, iR = 0, i2 = 0;
+    for (int j = 0; j < n; ++j) {
+        GLin &m = tab[(size_t)j];
+        const size_t b = plan(ls[j], &m);
+        bind(&m, ls[j], cur);
+        cur += b;
+        m.item1 = i1;
+        m.itemR = iR;
+        m.item2 = i2;
+        i1 += items1_of(m);
+        iR += m.nred;
+        i2 += items2_of(m);
+    }
+    int32_t *lin1 = (int32_t *)cur;
+    int32_t *linR = (int32_t *)((uint8_t *)lin1 + rup256((size_t)i1 * 4));
+    int32_t *lin2 = (int32_t *)((uint8_t *)linR + rup256((size_t)iR * 4));
+    std::vector<int32_t> h1((size_t)i1), hR((size_t)iR), h2((size_t)i2);
+    for (int j = 0; j < n; ++j) {
+        const GLin &m = tab[(size_t)j];
+        for (int64_t k = 0; k < items1_of(m); ++k) h1[(size_t)(m.item1 + k)] = j;
+        for (int64_t k = 0; k < m.nred; ++k) hR[(size_t)(m.itemR + k)] = j;
+        for (int64_t k = 0; k < items2_of(m); ++k) h2[(size_t)(m.item2 + k)] = j;
+    }
+    if (hipMemcpy(table_dev, tab.data(), sizeof(GLin) * n, hipMemcpyHostToDevice) != hipSuccess ||
+        (i1 && hipMemcpy(lin1, h1.data(), (size_t)i1 * 4, hipMemcpyHostToDevice) != hipSuccess) ||
+        (iR && hipMemcpy(linR, hR.data(), (size_t)iR * 4, hipMemcpyHostToDevice) != hipSuccess) ||
+        (i2 && hipMemcpy(lin2, h2.data(), (size_t)i2 * 4, hipMemcpyHostToDevice) != hipSuccess))
+        return hip_status(hipGetLastError());
+    GRun &run = hs->run;
+    run = GRun{};
+    run.T = (int)ls[0].T;
+    run.x_dtype = ls[0].x_dtype;
+    run.y_dtype = ls[0].y_dtype;
+    run.items1 = i1;
+    run.itemsR = iR;
+    run.items2 = i2;
+    run.table = table_dev;
+    run.lin1 = lin1;
+    run.linR = linR;
+    run.lin2 = lin2;
+    return LB_OK;
+}
+
+int gemm_group_run(const void *host_state, hipStream_t st, int stage_mask) {
+    const GGroupHost *hs = (const GGroupHost *)host_state;
+    GRun run = hs->run;
+    if (!(stage_mask & 1)) run.items1 = run.itemsR = 0;
+    if (!(stage_mask & 2)) run.items2 = 0;
+    GLin dummy{};
+    return launch_gemms(run, dummy, st);
+}
 
 }  // namespace lb

@@ -86,9 +86,16 @@ int mfma_group_prepare(const Linear *ls, int n, int64_t T, int y_dtype, void *ws
                        void *host_state, hipStream_t s);
 int mfma_group_run(const void *host_state, hipStream_t s, int stage_mask = 3);
 
-// GEMM (prefill) path.
+// GEMM (prefill) path: bf16 matrix cores; shapes it does not take (d_in % 8,
+// misaligned x) run on the vector-ALU kernels.
 size_t gemm_workspace_bytes(const Linear &a);
 int gemm_forward(const Linear &a, void *ws, hipStream_t s);
+// Groups of independent linears on the GEMM path: stage 1 (+ reduce), stage 2.
+bool gemm_group_supported(const Linear *ls, int n);
+size_t gemm_group_workspace_bytes(const Linear *ls, int n);
+size_t gemm_group_state_bytes();
+int gemm_group_prepare(const Linear *ls, int n, void *ws, size_t ws_bytes, void *host_state);
+int gemm_group_run(const void *host_state, hipStream_t s, int stage_mask = 3);
 
 // SwiGLU gate: a = silu(gate) * up, elementwise over n values (fp32 in place).
 int launch_swiglu_f32(float *gate_io, const float *up, int64_t n, hipStream_t s);

@@ -130,6 +130,8 @@ def test_mlp_and_group_argument_errors():
     assert L.lb_mlp_workspace_bytes(1024, 3072, 415, 416, 16, 1, 0) == 0   # odd rank, residual
     arr = (lb.lb_linear_desc * 1)()
     arr[0] = lb.lb_linear_desc(FAKE + 0x5000000, FAKE + 0x6000000, _factors(), 1024, 1024, 512, 0, 0)
-    assert L.lb_grouped_workspace_bytes(arr, 1, 64, 0) == 0                # groups are decode-only
+    assert L.lb_grouped_workspace_bytes(arr, 1, 64, 0) > 0                 # GEMM-path group
+    assert L.lb_grouped_workspace_bytes(arr, 1, 0, 0) == 0                 # no tokens
+    assert L.lb_grouped_workspace_bytes(arr, 0, 4, 0) == 0                 # no linears
     assert L.lb_grouped_prepare(arr, 1, 1, lb.LB_F32, lb.LB_F32, None, 0, 0, None) == lb.LB_EWORKSPACE
     assert L.lb_grouped_run(FAKE, None) == lb.LB_EINVAL                   # never prepared

@@ -78,6 +78,21 @@ def test_more_tokens_than_decode_width_fp32(T):
     _check(inp, x, "f32", "auto")
 
 
+@pytest.mark.parametrize("d_in,d_out,r_p,P", [(1000, 700, 48, 2), (520, 130, 16, 1),
+                                              (9000, 300, 96, 2), (100, 70, 16, 2),
+                                              (2048, 1100, 304, 2)])
+@pytest.mark.parametrize("T", [33, 257])
+@pytest.mark.parametrize("xdt", ["bf16", "f32"])
+def test_prefill_ragged(d_in, d_out, r_p, P, T, xdt):
+    """GEMM path over ragged tiles: token and column tails, a K tail (d_in % 64),
+    two d_in pieces (9000 > 8192), a path boundary inside a packed word
+    (r_p = 304), fp32 inputs rounded to bf16 on staging; d_in = 100 is not a
+    multiple of 8 and runs on the vector-ALU kernels."""
+    inp = synth.layer_inputs(d_in + 3 * d_out, d_in, d_out, r_p, P)
+    x = synth.activations(T + 7 * d_in, T, d_in, xdt)
+    _check(inp, x, "bf16", "prefill")
+
+
 # ---- the configurations' linears at full size ----
 
 def _cfg_linear(key, name):

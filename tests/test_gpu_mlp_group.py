@@ -49,7 +49,7 @@ def test_mlp_prefill_sampled():
     assert err <= TOL["bf16"], err
 
 
-def _stack_check(key, layers, T, check_layers, rows_per=512):
+def _stack_check(key, layers, T, check_layers, rows_per=512, tokens=None):
     torch = torch_or_skip()
     import binarized_rank_linear_amd as lb
     from binarized_rank_linear_amd.stack import LayerStack
@@ -74,9 +74,10 @@ def _stack_check(key, layers, T, check_layers, rows_per=512):
         for i, sh in enumerate(w.linears):
             inp = kept[(L, i)]
             x = xs[sh.d_in].float().cpu().numpy()
+            tok = np.arange(T) if tokens is None else np.asarray(tokens)
             rows = np.unique(np.linspace(0, sh.d_out - 1, rows_per).astype(np.int64))
-            ref = oracle.linear_forward_rows(x, inp.U, inp.V, inp.h, inp.g, inp.l, rows)
-            got = y_to_np(st.outputs[L][i])[:, rows]
+            ref = oracle.linear_forward_rows(x[tok], inp.U, inp.V, inp.h, inp.g, inp.l, rows)
+            got = y_to_np(st.outputs[L][i])[tok][:, rows]
             err = oracle.rel_l2(got, ref)
             assert err <= TOL["bf16"], (L, sh.name, err)
 
@@ -84,6 +85,13 @@ def _stack_check(key, layers, T, check_layers, rows_per=512):
 @pytest.mark.parametrize("key,T", [("c3", 4), ("c4", 1), ("c5", 1), ("c3", 32)])
 def test_small_stack_all_layers(key, T):
     _stack_check(key, 2, T, {0, 1})
+
+
+@pytest.mark.parametrize("key,T", [("c5", 100), ("c4", 300), ("c3", 64)])
+def test_prefill_layer_group(key, T):
+    """One decoder layer's linears as one GEMM-path group (one launch per
+    stage for all seven), sampled tokens and rows."""
+    _stack_check(key, 1, T, {0}, rows_per=256, tokens=[0, 1, T // 2, T - 2, T - 1])
 
 
 def test_full_c5_stack_sampled_layers():
