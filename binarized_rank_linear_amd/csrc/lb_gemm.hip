@@ -39,6 +39,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 namespace {
 
@@ -46,23 +48,29 @@ constexpr int kBM = 256;                     // tokens per tile
 constexpr int kBN = 128;                     // output columns per tile
 constexpr int kBK = 64;                      // contraction elements per K-tile (two packed words)
 constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kStages = 2;                   // LDS ring depth: two workgroups fit one CU
 constexpr int kRowBytes = kBK * 2;           // one activation row of a K-tile (bf16)
 constexpr int kABytes = kBM * kRowBytes;     // 32 KB
-constexpr int kXBytes = 2 * kBN * 4;         // unzipped sign words [2][kBN]
-constexpr int kGBytes = 2 * kBK * 2;         // stage-1 scales, bf16 [path][kBK]
-constexpr int kBuf = kABytes + kXBytes + kGBytes;
-constexpr int kLds = 2 * kBuf;
+constexpr int kXWave = 2 * 64 * 4;           // a wave's sign words: [2 words][64 columns]
+constexpr int kGWave = 2 * kBK * 2;          // a wave's bf16 g: [2 paths][kBK]
+constexpr int kSlot = kABytes + kWaves * (kXWave + kGWave);
+constexpr int kLds = kStages * kSlot;        // 70 KB: two workgroups per CU
 constexpr int kMaxKtPerSplit = 128;          // stage-1 K-tiles per piece (8192 inputs)
+constexpr uint32_t kOOB = 0x7ffffff0u;       // a buffer offset past every range: reads as zero
 
 // One linear of a prefill launch.
 struct GLin {
-    const void *x;
+    const void *x;        // [T][d_in] bf16 (fp32 inputs are converted first)
     void *y;
     const uint32_t *v_bits, *u_bits;
     const uint16_t *g, *l, *h;
     uint16_t *t;          // [T][ldt] bf16 latents; zero outside the P*r_p real ones
+    uint16_t *gb;         // [P][d_in] g rounded to bf16          (written by k_prep)
+    uint32_t *vz, *uz;    // V and U sign words, unzipped, planes of zld_v / zld_u words
     float *part;          // [nsplit][T][ldt] fp32 stage-1 pieces (nsplit > 1)
     int64_t ld_v, ld_u, d_in, d_out;
+    int64_t zld_v, zld_u; // plane strides of vz / uz: r_p and d_out rounded up to 4
     int32_t r_p, P;
     int32_t kw;           // packed words per path along r_p (= U planes per path)
     int32_t kw_v;         // packed words along d_in (= V planes per path)
@@ -71,14 +79,15 @@ struct GLin {
     int32_t nkt1, nkt2;   // K-tiles of stage 1 (d_in) and stage 2 (ldt)
     int32_t mt, nt1, nt2; // token tiles; column tiles of stage 1 (ldt) and stage 2 (d_out)
     int32_t nred;         // reduce items (nsplit > 1), 0 otherwise
-    int64_t item1, itemR, item2;
+    int32_t ngp;          // prep items
+    int64_t itemG, item1, itemR, item2;
 };
 
 struct GRun {
-    int T, x_dtype, y_dtype, pad_;
-    int64_t items1, itemsR, items2;
+    int T, y_dtype, pad0_, pad1_;
+    int64_t itemsG, items1, itemsR, items2;
     const GLin *table;                       // null: the single linear passed by value
-    const int32_t *lin1, *linR, *lin2;       // item -> linear, per launch
+    const int32_t *linG, *lin1, *linR, *lin2;   // item -> linear, per launch
 };
 
 // Work item v of n for block b: each XCD (blocks b % 8) takes a contiguous range.
@@ -107,8 +116,28 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int64
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, n, 0x00020000);
 }
 
-__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Global -> LDS without registers: lane i's `size` bytes land at dst + size*i
+// (dst wave-uniform); offsets past the descriptor's range read as zero.
+template <int SIZE>
+__device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t r, uint8_t *dst, uint32_t voff) {
+    static_assert(SIZE == 4 || SIZE == 16, "LDS load size");
+    if constexpr (SIZE == 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 16, (int)voff, 0, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 4, (int)voff, 0, 0, 0);
+}
+
+// Wait until at most n vector-memory operations of this wave are outstanding,
+// then meet the other waves: their loads before the wait are in LDS too.
+template <int N>
+__device__ __forceinline__ void wait_and_meet() {
+    static_assert(N >= 0 && N < 64, "vmcnt field");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 // Even bits of x to the low half, odd bits to the high half (inverse perfect
@@ -122,8 +151,14 @@ __device__ __forceinline__ uint32_t unzip_bits(uint32_t x) {
     return x;
 }
 
+// two fp32 -> two bf16 in one word (v_cvt_pk_bf16_f32: round to nearest even)
+// 16-byte chunk position of chunk c in activation row r of a K-tile: rows
+// 0..7 and rows 0..15 of one parity all use different positions, so an 8- or
+// 16-lane phase of a 16-byte LDS read touches every bank once (32 or 64 banks).
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
 __device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
-    return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
 __device__ __forceinline__ f32x16 mfma(const u32x4 &s, const u32x4 &a, f32x16 c) {
@@ -135,10 +170,10 @@ __device__ __forceinline__ f32x16 mfma(const u32x4 &s, const u32x4 &a, f32x16 c)
 // the two GEMM stages
 // ---------------------------------------------------------------------------
 
-// STAGE 1: A = x (bf16, or fp32 rounded to bf16 when XF32), sign words of V,
-//          scales g; output t (bf16, l applied) or fp32 pieces.
+// STAGE 1: A = x (bf16), sign words of V, scales g; output t (bf16, l applied)
+//          or fp32 pieces.
 // STAGE 2: A = t (bf16), sign words of U, scales h; output y.
-template <int STAGE, bool XF32>
+template <int STAGE>
 __global__ __launch_bounds__(kThreads, 2) void k_gemm(GRun run, GLin single) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int64_t items = STAGE == 1 ? run.items1 : run.items2;
@@ -160,89 +195,69 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(GRun run, GLin single) {
     const int hh = lane >> 5, l32 = lane & 31;
     const int wm = wave & 1, wn = wave >> 1;
 
-    // ---- staging roles ----
-    // activations: chunk ch (16 bytes = 8 elements) of rows rb + 32c, c = 0..7
-    const int ch = tid & 7, rb = tid >> 3;
-    const int64_t K = STAGE == 1 ? L.d_in : L.ldt;       // elements per activation row
-    constexpr int esz = (STAGE == 1 && XF32) ? 4 : 2;
+    // ---- loads of one K-tile (per wave: 8 activation DMAs, 2 sign-word DMAs, 1 g DMA) ----
+    // activations: wave w fills rows 64w .. 64w+63, 8 rows (1 KB) per DMA; lane i
+    // lands in row r0 + i/8 at swizzled position i%8, which holds chunk (i%8)^(r%8)
+    const int64_t K = STAGE == 1 ? L.d_in : L.ldt;
     const int rows = (int)imin(kBM, (int64_t)T - m0);
     const uint8_t *abase = STAGE == 1 ? (const uint8_t *)L.x : (const uint8_t *)L.t;
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(abase + m0 * K * esz, (int64_t)rows * K * esz);
-    const uint32_t arow = (uint32_t)(K * esz);
-    const uint32_t lds_a = (uint32_t)(rb * kRowBytes + ((ch ^ (rb & 7)) << 4));
-    // sign words: word w of the K-tile for column n0 + col
-    const int xw = tid >> 7, xcol = tid & 127;
-    const int xn = n0 + xcol;
-    const uint32_t *xsrc;
-    int64_t xstride;
-    bool xcol_ok;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(abase + m0 * K * 2, (int64_t)rows * K * 2);
+    // (rows r0 .. r0+7 with r0 = 64w + 8i: swz(r) = (i/8 % 8) ^ (i & 1))
+    const int arow0 = wave * 64 + (lane >> 3);               // + 8i
+    const int ach0 = (lane & 7) ^ ((lane >> 3) & 7);          // chunk for even i
+    const int ach1 = ach0 ^ 1;                                // chunk for odd i
+    const uint32_t aoffe = (uint32_t)(arow0 * K * 2) + (uint32_t)(ach0 * 16);
+    const uint32_t aoffo = (uint32_t)(arow0 * K * 2) + (uint32_t)(ach1 * 16);
+    const uint32_t astep = (uint32_t)(8 * K * 2);            // 8 rows
+    // sign words: this wave's 64 columns n0 + 64*wn + lane, both words of the K-tile
+    const int xn = n0 + wn * 64 + lane;
+    __amdgpu_buffer_rsrc_t rx;
+    uint32_t xoff = kOOB, xstep;
+    int xwords;
     if (STAGE == 1) {
+        rx = make_rsrc(L.vz, (int64_t)L.P * L.kw_v * L.zld_v * 4);
         const int qn = xn >> 5;
         const int p = qn / L.kw;
         const int k = (qn - p * L.kw) * 32 + (xn & 31);
-        xcol_ok = p < L.P && k < L.r_p;
-        xsrc = L.v_bits + (xcol_ok ? ((int64_t)p * L.kw_v * L.ld_v + k) : 0);
-        xstride = L.ld_v;
+        if (p < L.P && k < L.r_p) xoff = (uint32_t)(((int64_t)p * L.kw_v * L.zld_v + k) * 4);
+        xstep = (uint32_t)(L.zld_v * 4);
+        xwords = L.kw_v;
     } else {
-        xcol_ok = xn < L.d_out;
-        xsrc = L.u_bits + (xcol_ok ? xn : 0);
-        xstride = L.ld_u;
+        rx = make_rsrc(L.uz, (int64_t)L.P * L.kw * L.zld_u * 4);
+        if (xn < L.d_out) xoff = (uint32_t)(xn * 4);
+        xstep = (uint32_t)(L.zld_u * 4);
+        xwords = L.P * L.kw;
     }
-    const int xwords = STAGE == 1 ? L.kw_v : L.P * L.kw;   // packed words along K
+    // g (stage 1, bf16): lane i -> path i/32, elements 2(i%32), +1 of the K-tile
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(L.gb, (int64_t)L.P * L.d_in * 2);
+    const int gpath = lane >> 5, gel = 2 * (lane & 31);
 
-    u32x4 sa[esz == 4 ? 16 : 8];
-    uint32_t sx = 0, sg = 0;
-
-    auto stage_load = [&](int kt) {
-        const int kel = kt * kBK + 8 * ch;                     // first element of the chunk
-        const bool kok = kel < K;
+    auto issue = [&](int kt, int slot) {
+        uint8_t *S = smem + slot * kSlot;
+        const bool kine = kt * kBK + 8 * ach0 < K;            // chunk inside the row
+        const bool kino = kt * kBK + 8 * ach1 < K;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const uint32_t off = kok ? (uint32_t)(rb + 32 * c) * arow + (uint32_t)kel * esz : 0u;
-            if (esz == 4) {
-                sa[2 * c] = load16(ra, off);
-                sa[2 * c + 1] = load16(ra, off + 16);
-                if (!kok) sa[2 * c] = sa[2 * c + 1] = u32x4{0u, 0u, 0u, 0u};
-            } else {
-                sa[c] = load16(ra, off);
-                if (!kok) sa[c] = u32x4{0u, 0u, 0u, 0u};
-            }
+        for (int i = 0; i < 8; ++i) {
+            const bool kin = (i & 1) ? kino : kine;
+            const uint32_t off = ((i & 1) ? aoffo : aoffe) + i * astep + (uint32_t)(kt * kBK * 2);
+            dma<16>(ra, S + (wave * 64 + 8 * i) * kRowBytes, kin ? off : kOOB);
         }
-        const int q = kt * 2 + xw;
-        sx = (xcol_ok && q < xwords) ? xsrc[(int64_t)q * xstride] : 0u;
-        if (STAGE == 1 && tid < 64) {
-            const int p = tid >> 5;
-            const int64_t k = (int64_t)kt * kBK + 2 * (tid & 31);
-            const uint16_t *gp = L.g + (int64_t)p * L.d_in;
-            const float g0 = (p < L.P && k < L.d_in) ? f16_to_f32(gp[k]) : 0.0f;
-            const float g1 = (p < L.P && k + 1 < L.d_in) ? f16_to_f32(gp[k + 1]) : 0.0f;
-            sg = bf16_pair(g0, g1);
+        uint8_t *X = S + kABytes + wave * (kXWave + kGWave);
+#pragma unroll
+        for (int wd = 0; wd < 2; ++wd) {
+            const int q = kt * 2 + wd;
+            dma<4>(rx, X + wd * 256, (xoff != kOOB && q < xwords) ? xoff + (uint32_t)q * xstep : kOOB);
+        }
+        if (STAGE == 1) {
+            const int64_t e = (int64_t)kt * kBK + gel;
+            dma<4>(rg, X + kXWave, e < L.d_in ? (uint32_t)((gpath * L.d_in + e) * 2) : kOOB);
         }
     };
-    auto stage_store = [&](int buf) {
-        uint8_t *A = smem + buf * kBuf;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            u32x4 vv;
-            if (esz == 4) {
-                const u32x4 lo = sa[2 * c], hi = sa[2 * c + 1];
-                vv[0] = bf16_pair(__uint_as_float(lo[0]), __uint_as_float(lo[1]));
-                vv[1] = bf16_pair(__uint_as_float(lo[2]), __uint_as_float(lo[3]));
-                vv[2] = bf16_pair(__uint_as_float(hi[0]), __uint_as_float(hi[1]));
-                vv[3] = bf16_pair(__uint_as_float(hi[2]), __uint_as_float(hi[3]));
-            } else {
-                vv = sa[c];
-            }
-            *(u32x4 *)(A + lds_a + c * 32 * kRowBytes) = vv;
-        }
-        ((uint32_t *)(A + kABytes))[xw * kBN + xcol] = unzip_bits(sx);
-        if (STAGE == 1 && tid < 64) ((uint32_t *)(A + kABytes + kXBytes))[tid] = sg;
-    };
+    constexpr int kIssued = STAGE == 1 ? 11 : 10;            // DMAs per K-tile per wave
 
     // ---- per-lane constants of the sign operands ----
-    // column of n-block b for this lane; its path (stage 1) or its h pair per path (stage 2)
-    int gofs[2];
-    uint32_t hpair[2][2];
+    int gofs[2];          // stage 1: byte offset of this lane's g run (path of the column)
+    uint32_t hpair[2][2]; // stage 2: bf16 h pair per n-block and path
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
         const int n = n0 + wn * 64 + b * 32 + l32;
@@ -259,6 +274,42 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(GRun run, GLin single) {
     }
     const uint32_t xshift = 4u - 4u * (uint32_t)hh;
 
+    // stage 1 without pieces: l for this lane's output columns (4 per accumulator
+    // quad), loaded before the K loop.  r_p is a multiple of 16, so a run of 4
+    // columns is all real latents or all padding.
+    u32x2 lsc[2][4];
+    uint32_t lok = 0;                                  // bit 4b+q4: run of real latents
+    if (STAGE == 1 && L.nsplit == 1) {
+        const uint16_t *lp[2][4];
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int n = n0 + wn * 64 + b * 32 + 8 * q4 + 4 * hh;
+                const int qn = n >> 5;
+                const int p = qn / L.kw;
+                const int k = (qn - p * L.kw) * 32 + (n & 31);
+                const bool ok = n < L.ldt && p < L.P && k < L.r_p;
+                lok |= (ok ? 1u : 0u) << (4 * b + q4);
+                lp[b][q4] = L.l + (ok ? (int64_t)p * L.r_p + k : 0);
+            }
+        if (((uintptr_t)L.l & 7) == 0) {
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) lsc[b][q4] = *(const u32x2 *)lp[b][q4];
+        } else {
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const uint16_t *q = lp[b][q4];
+                    lsc[b][q4] = u32x2{(uint32_t)q[0] | ((uint32_t)q[1] << 16),
+                                       (uint32_t)q[2] | ((uint32_t)q[3] << 16)};
+                }
+        }
+    }
+
     f32x16 acc[2][4];
 #pragma unroll
     for (int b = 0; b < 2; ++b)
@@ -267,15 +318,16 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(GRun run, GLin single) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[b][mb][i] = 0.0f;
 
-    auto compute = [&](int buf, int kt) {
-        const uint8_t *A = smem + buf * kBuf;
-        const uint32_t *X = (const uint32_t *)(A + kABytes);
-        const uint8_t *G = A + kABytes + kXBytes;
+    auto compute = [&](int slot, int kt) {
+        const uint8_t *A = smem + slot * kSlot;
+        const uint8_t *Xw = A + kABytes + wave * (kXWave + kGWave);
+        const uint8_t *G = Xw + kXWave;
 #pragma unroll
         for (int w2 = 0; w2 < 2; ++w2) {
             uint32_t xs[2];
 #pragma unroll
-            for (int b = 0; b < 2; ++b) xs[b] = X[w2 * kBN + wn * 64 + b * 32 + l32] << xshift;
+            for (int b = 0; b < 2; ++b)
+                xs[b] = ((const uint32_t *)Xw)[w2 * 64 + b * 32 + l32] << xshift;
             int pq = 0;
             if (STAGE == 2) pq = (kt * 2 + w2) >= L.kw ? 1 : 0;       // path of this word (uniform)
 #pragma unroll
@@ -285,7 +337,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(GRun run, GLin single) {
                 for (int mb = 0; mb < 4; ++mb) {
                     const int row = wm * 128 + mb * 32 + l32;
                     const int chunk = 4 * w2 + 2 * s + hh;
-                    act[mb] = *(const u32x4 *)(A + row * kRowBytes + ((chunk ^ (row & 7)) << 4));
+                    act[mb] = *(const u32x4 *)(A + row * kRowBytes + ((chunk ^ swz(row)) << 4));
                 }
 #pragma unroll
                 for (int b = 0; b < 2; ++b) {
@@ -307,16 +359,19 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(GRun run, GLin single) {
         }
     };
 
-    stage_load(kt0);
-    stage_store(0);
-    __syncthreads();
+    // ---- K loop over a ring of kStages slots ----
+    // At the top of iteration kt the tiles kt .. kt+kStages-2 have been issued;
+    // after the wait and the barrier tile kt is in LDS for every wave and the
+    // slot of tile kt-1 is free again, so tile kt+kStages-1 is issued into it.
+#pragma unroll
+    for (int j = 0; j < kStages - 1; ++j)
+        if (kt0 + j < kt1) issue(kt0 + j, j);
     for (int kt = kt0; kt < kt1; ++kt) {
-        const int cur = (kt - kt0) & 1;
-        const bool more = kt + 1 < kt1;                 // uniform
-        if (more) stage_load(kt + 1);
-        compute(cur, kt);
-        if (more) stage_store(cur ^ 1);
-        __syncthreads();
+        const int slot = (kt - kt0) % kStages;
+        if (kt + kStages - 2 < kt1) wait_and_meet<(kStages - 2) * kIssued>();
+        else wait_and_meet<0>();
+        if (kt + kStages - 1 < kt1) issue(kt + kStages - 1, (slot + kStages - 1) % kStages);
+        compute(slot, kt);
     }
 
     // ---- epilogue: lane holds columns n .. n+3 of token m per accumulator quad ----
@@ -338,16 +393,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(GRun run, GLin single) {
                         float *dst = L.part + ((int64_t)split * T + m) * L.ldt + n;
                         *(f32x4 *)dst = f32x4{o[0], o[1], o[2], o[3]};
                     } else {
-                        const int qn = n >> 5;
-                        const int p = qn / L.kw;
-                        const int k = (qn - p * L.kw) * 32 + (n & 31);
-                        float tv[4];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            tv[e] = (p < L.P && k + e < L.r_p)
-                                        ? f16_to_f32(L.l[(int64_t)p * L.r_p + k + e]) * o[e]
-                                        : 0.0f;
-                        *(u32x2 *)(L.t + m * L.ldt + n) = u32x2{bf16_pair(tv[0], tv[1]), bf16_pair(tv[2], tv[3])};
+                        const u32x2 w = lsc[b][q4];
+                        const bool ok = (lok >> (4 * b + q4)) & 1u;   // padding columns stay zero
+                        const float t0 = ok ? f16_to_f32((uint16_t)(w[0] & 0xffffu)) * o[0] : 0.0f;
+                        const float t1 = ok ? f16_to_f32((uint16_t)(w[0] >> 16)) * o[1] : 0.0f;
+                        const float t2 = ok ? f16_to_f32((uint16_t)(w[1] & 0xffffu)) * o[2] : 0.0f;
+                        const float t3 = ok ? f16_to_f32((uint16_t)(w[1] >> 16)) * o[3] : 0.0f;
+                        *(u32x2 *)(L.t + m * L.ldt + n) = u32x2{bf16_pair(t0, t1), bf16_pair(t2, t3)};
                     }
                 } else {
                     if (n >= L.d_out) continue;
@@ -370,6 +422,39 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(GRun run, GLin single) {
                         if (n + e < L.d_out) store_act(L.y, run.y_dtype, e0 + e, o[e]);
                 }
             }
+        }
+    }
+}
+
+// Per-call operand preparation: g -> bf16 (round to nearest even) for the
+// stage-1 sign operands, and every packed sign word of V and U unzipped (even
+// bits to the low half, odd bits to the high half) for both stages.
+constexpr int kPrep = 1024;       // words per item
+
+__global__ __launch_bounds__(kThreads) void k_prep(GRun run, GLin single) {
+    const int64_t v = blockIdx.x;
+    const GLin L = pick(run, single, run.linG, v);
+    const int64_t local = v - L.itemG;
+    const int64_t ng = (int64_t)L.P * L.d_in / 2;                 // g pairs
+    const int64_t nv = (int64_t)L.P * L.kw_v * L.zld_v;           // V words (compact)
+    const int64_t nu = (int64_t)L.P * L.kw * L.zld_u;             // U words (compact)
+    for (int i = threadIdx.x; i < kPrep; i += kThreads) {
+        int64_t e = local * kPrep + i;
+        if (e < ng) {
+            const uint32_t w = ((const uint32_t *)L.g)[e];
+            ((uint32_t *)L.gb)[e] = bf16_pair(f16_to_f32((uint16_t)(w & 0xffffu)), f16_to_f32((uint16_t)(w >> 16)));
+            continue;
+        }
+        e -= ng;
+        if (e < nv) {
+            const int64_t pl = e / L.zld_v;
+            L.vz[e] = unzip_bits(L.v_bits[pl * L.ld_v + (e - pl * L.zld_v)]);
+            continue;
+        }
+        e -= nv;
+        if (e < nu) {
+            const int64_t pl = e / L.zld_u;
+            L.uz[e] = unzip_bits(L.u_bits[pl * L.ld_u + (e - pl * L.zld_u)]);
         }
     }
 }
@@ -409,24 +494,39 @@ __global__ __launch_bounds__(kThreads) void k_reduce(GRun run, GLin single) {
     }
 }
 
+// fp32 activations -> bf16 (round to nearest even), 4 per thread.
+__global__ __launch_bounds__(kThreads) void k_to_bf16(const float *__restrict__ x, uint16_t *__restrict__ xb,
+                                                      int64_t n4) {
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= n4) return;
+    const f32x4 v = ((const f32x4 *)x)[i];
+    ((u32x2 *)xb)[i] = u32x2{bf16_pair(v[0], v[1]), bf16_pair(v[2], v[3])};
+}
+
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 
 size_t rup256(size_t n) { return (n + 255) & ~(size_t)255; }
 
-// Shapes the GEMM kernels take: 16-byte activation rows (d_in % 8 == 0) and a
-// 16-byte aligned x.  Others run on the vector-ALU kernels.
+// Shapes the GEMM kernels take: 16-byte activation rows (d_in % 8 == 0), a
+// 16-byte aligned x and a 4-byte aligned g (both are read by 16- and 4-byte
+// LDS loads).  Others run on the vector-ALU kernels.
 bool gemm_shape_ok(const Linear &a) {
     if (a.d_in % 8 != 0) return false;
     if (a.x && ((uintptr_t)a.x % 16) != 0) return false;
+    if (a.g && ((uintptr_t)a.g % 4) != 0) return false;
     if (a.T > (1ll << 24)) return false;
-    // 32-bit buffer offsets over one 256-token tile of activations or latents
+    // 32-bit buffer offsets over one 256-token tile of activations or latents,
+    // and over the packed words of one linear
     if (a.d_in >= (1ll << 21) || a.r_p >= (1ll << 20)) return false;
+    if ((int64_t)a.P * cdiv(a.d_in, 32) * rup(a.r_p, 4) * 4 >= (1ll << 31)) return false;
+    if ((int64_t)a.P * cdiv(a.r_p, 32) * rup(a.d_out, 4) * 4 >= (1ll << 31)) return false;
     return true;
 }
 
-// Schedule fields of one linear; returns the workspace bytes it needs.
+// Schedule fields of one linear; returns the workspace bytes it needs (the
+// latents, the stage-1 pieces and, for fp32 inputs, their bf16 copy).
 size_t plan(const Linear &a, GLin *m) {
     *m = GLin{};
     m->x = a.x;
@@ -442,6 +542,8 @@ size_t plan(const Linear &a, GLin *m) {
     m->d_out = a.d_out;
     m->r_p = (int32_t)a.r_p;
     m->P = a.P;
+    m->zld_v = rup(a.r_p, 4);
+    m->zld_u = rup(a.d_out, 4);
     m->kw = (int32_t)cdiv(a.r_p, 32);
     m->kw_v = (int32_t)cdiv(a.d_in, 32);
     m->ldt = (int32_t)rup((int64_t)a.P * m->kw * 32, kBK);
@@ -454,14 +556,29 @@ size_t plan(const Linear &a, GLin *m) {
     m->nt1 = (int32_t)cdiv(m->ldt, kBN);
     m->nt2 = (int32_t)cdiv(a.d_out, kBN);
     m->nred = m->nsplit > 1 ? (int32_t)cdiv(a.T * (m->ldt / 4), kRedGroups) : 0;
+    const int64_t nv = (int64_t)a.P * m->kw_v * m->zld_v, nu = (int64_t)a.P * m->kw * m->zld_u;
+    m->ngp = (int32_t)cdiv((int64_t)a.P * a.d_in / 2 + nv + nu, kPrep);
     const size_t tb = rup256((size_t)a.T * m->ldt * 2);
     const size_t pb = m->nsplit > 1 ? rup256((size_t)m->nsplit * a.T * m->ldt * 4) : 0;
-    return tb + pb;
+    const size_t gbb = rup256((size_t)a.P * a.d_in * 2);
+    const size_t vzb = rup256((size_t)nv * 4), uzb = rup256((size_t)nu * 4);
+    const size_t xb = rup256((size_t)a.T * a.d_in * 2);
+    return tb + pb + gbb + vzb + uzb + xb;
 }
 
-void bind(GLin *m, const Linear &a, uint8_t *ws) {
+// Workspace pointers; returns the bf16 copy of x (used when x is fp32).
+uint16_t *bind(GLin *m, const Linear &a, uint8_t *ws) {
+    const size_t tb = rup256((size_t)a.T * m->ldt * 2);
+    const size_t pb = m->nsplit > 1 ? rup256((size_t)m->nsplit * a.T * m->ldt * 4) : 0;
+    const size_t gbb = rup256((size_t)a.P * a.d_in * 2);
+    const int64_t nv = (int64_t)a.P * m->kw_v * m->zld_v, nu = (int64_t)a.P * m->kw * m->zld_u;
+    const size_t vzb = rup256((size_t)nv * 4), uzb = rup256((size_t)nu * 4);
     m->t = (uint16_t *)ws;
-    m->part = m->nsplit > 1 ? (float *)(ws + rup256((size_t)a.T * m->ldt * 2)) : nullptr;
+    m->part = m->nsplit > 1 ? (float *)(ws + tb) : nullptr;
+    m->gb = (uint16_t *)(ws + tb + pb);
+    m->vz = (uint32_t *)(ws + tb + pb + gbb);
+    m->uz = (uint32_t *)(ws + tb + pb + gbb + vzb);
+    return (uint16_t *)(ws + tb + pb + gbb + vzb + uzb);
 }
 
 int64_t items1_of(const GLin &m) { return (int64_t)m.nsplit * m.nt1 * m.mt; }
@@ -482,14 +599,13 @@ int raise_lds(K kern) {
 
 int launch_gemms(const GRun &run, const GLin &single, hipStream_t st) {
     int rc;
+    if (run.itemsG > 0) {
+        k_prep<<<(unsigned)run.itemsG, kThreads, 0, st>>>(run, single);
+        if ((rc = last_launch_status())) return rc;
+    }
     if (run.items1 > 0) {
-        if (run.x_dtype == LB_F32) {
-            if ((rc = raise_lds(k_gemm<1, true>))) return rc;
-            k_gemm<1, true><<<(unsigned)run.items1, kThreads, kLds, st>>>(run, single);
-        } else {
-            if ((rc = raise_lds(k_gemm<1, false>))) return rc;
-            k_gemm<1, false><<<(unsigned)run.items1, kThreads, kLds, st>>>(run, single);
-        }
+        if ((rc = raise_lds(k_gemm<1>))) return rc;
+        k_gemm<1><<<(unsigned)run.items1, kThreads, kLds, st>>>(run, single);
         if ((rc = last_launch_status())) return rc;
     }
     if (run.itemsR > 0) {
@@ -497,8 +613,8 @@ int launch_gemms(const GRun &run, const GLin &single, hipStream_t st) {
         if ((rc = last_launch_status())) return rc;
     }
     if (run.items2 > 0) {
-        if ((rc = raise_lds(k_gemm<2, false>))) return rc;
-        k_gemm<2, false><<<(unsigned)run.items2, kThreads, kLds, st>>>(run, single);
+        if ((rc = raise_lds(k_gemm<2>))) return rc;
+        k_gemm<2><<<(unsigned)run.items2, kThreads, kLds, st>>>(run, single);
         if ((rc = last_launch_status())) return rc;
     }
     return LB_OK;
@@ -518,11 +634,17 @@ int gemm_forward(const Linear &a, void *ws, hipStream_t st) {
     if (!gemm_shape_ok(a)) return valu_forward(a, ws, st);
     GLin m;
     plan(a, &m);
-    bind(&m, a, (uint8_t *)ws);
+    uint16_t *xb = bind(&m, a, (uint8_t *)ws);
+    if (a.x_dtype == LB_F32) {
+        const int64_t n4 = a.T * a.d_in / 4;
+        k_to_bf16<<<(unsigned)cdiv(n4, kThreads), kThreads, 0, st>>>((const float *)a.x, xb, n4);
+        if (int rc = last_launch_status()) return rc;
+        m.x = xb;
+    }
     GRun run{};
     run.T = (int)a.T;
-    run.x_dtype = a.x_dtype;
     run.y_dtype = a.y_dtype;
+    run.itemsG = m.ngp;
     run.items1 = items1_of(m);
     run.itemsR = m.nred;
     run.items2 = items2_of(m);
@@ -536,23 +658,26 @@ struct GGroupHost {
     GRun run;
 };
 
+// bf16 inputs only (fp32 groups run linear by linear)
 bool gemm_group_supported(const Linear *ls, int n) {
     for (int j = 0; j < n; ++j)
-        if (!gemm_shape_ok(ls[j])) return false;
+        if (!gemm_shape_ok(ls[j]) || ls[j].x_dtype != LB_BF16) return false;
     return n > 0 && ls[0].T > 0;
 }
 
 size_t gemm_group_workspace_bytes(const Linear *ls, int n) {
     size_t need = 256 + rup256(sizeof(GLin) * n);
-    int64_t i1 = 0, iR = 0, i2 = 0;
+    int64_t iG = 0, i1 = 0, iR = 0, i2 = 0;
     for (int j = 0; j < n; ++j) {
         GLin m;
         need += plan(ls[j], &m);
+        iG += m.ngp;
         i1 += items1_of(m);
         iR += m.nred;
         i2 += items2_of(m);
     }
-    return need + rup256((size_t)i1 * 4) + rup256((size_t)iR * 4) + rup256((size_t)i2 * 4);
+    return need + rup256((size_t)iG * 4) + rup256((size_t)i1 * 4) + rup256((size_t)iR * 4) +
+           rup256((size_t)i2 * 4);
 }
 
 size_t gemm_group_state_bytes() { return sizeof(GGroupHost); }
@@ -565,30 +690,35 @@ int gemm_group_prepare(const Linear *ls, int n, void *ws, size_t ws_bytes, void 
     GLin *table_dev = (GLin *)(w + 256);
     uint8_t *cur = w + 256 + rup256(sizeof(GLin) * n);
     std::vector<GLin> tab((size_t)n);
-    int64_t i1 = 0, iR = 0, i2 = 0;
+    int64_t iG = 0, i1 = 0, iR = 0, i2 = 0;
     for (int j = 0; j < n; ++j) {
         GLin &m = tab[(size_t)j];
         const size_t b = plan(ls[j], &m);
         bind(&m, ls[j], cur);
         cur += b;
+        m.itemG = iG;
         m.item1 = i1;
         m.itemR = iR;
         m.item2 = i2;
+        iG += m.ngp;
         i1 += items1_of(m);
         iR += m.nred;
         i2 += items2_of(m);
     }
-    int32_t *lin1 = (int32_t *)cur;
+    int32_t *linG = (int32_t *)cur;
+    int32_t *lin1 = (int32_t *)((uint8_t *)linG + rup256((size_t)iG * 4));
     int32_t *linR = (int32_t *)((uint8_t *)lin1 + rup256((size_t)i1 * 4));
     int32_t *lin2 = (int32_t *)((uint8_t *)linR + rup256((size_t)iR * 4));
-    std::vector<int32_t> h1((size_t)i1), hR((size_t)iR), h2((size_t)i2);
+    std::vector<int32_t> hG((size_t)iG), h1((size_t)i1), hR((size_t)iR), h2((size_t)i2);
     for (int j = 0; j < n; ++j) {
         const GLin &m = tab[(size_t)j];
+        for (int64_t k = 0; k < m.ngp; ++k) hG[(size_t)(m.itemG + k)] = j;
         for (int64_t k = 0; k < items1_of(m); ++k) h1[(size_t)(m.item1 + k)] = j;
         for (int64_t k = 0; k < m.nred; ++k) hR[(size_t)(m.itemR + k)] = j;
         for (int64_t k = 0; k < items2_of(m); ++k) h2[(size_t)(m.item2 + k)] = j;
     }
     if (hipMemcpy(table_dev, tab.data(), sizeof(GLin) * n, hipMemcpyHostToDevice) != hipSuccess ||
+        (iG && hipMemcpy(linG, hG.data(), (size_t)iG * 4, hipMemcpyHostToDevice) != hipSuccess) ||
         (i1 && hipMemcpy(lin1, h1.data(), (size_t)i1 * 4, hipMemcpyHostToDevice) != hipSuccess) ||
         (iR && hipMemcpy(linR, hR.data(), (size_t)iR * 4, hipMemcpyHostToDevice) != hipSuccess) ||
         (i2 && hipMemcpy(lin2, h2.data(), (size_t)i2 * 4, hipMemcpyHostToDevice) != hipSuccess))
@@ -596,12 +726,13 @@ int gemm_group_prepare(const Linear *ls, int n, void *ws, size_t ws_bytes, void 
     GRun &run = hs->run;
     run = GRun{};
     run.T = (int)ls[0].T;
-    run.x_dtype = ls[0].x_dtype;
     run.y_dtype = ls[0].y_dtype;
+    run.itemsG = iG;
     run.items1 = i1;
     run.itemsR = iR;
     run.items2 = i2;
     run.table = table_dev;
+    run.linG = linG;
     run.lin1 = lin1;
     run.linR = linR;
     run.lin2 = lin2;
@@ -611,7 +742,7 @@ int gemm_group_prepare(const Linear *ls, int n, void *ws, size_t ws_bytes, void 
 int gemm_group_run(const void *host_state, hipStream_t st, int stage_mask) {
     const GGroupHost *hs = (const GGroupHost *)host_state;
     GRun run = hs->run;
-    if (!(stage_mask & 1)) run.items1 = run.itemsR = 0;
+    if (!(stage_mask & 1)) run.itemsG = run.items1 = run.itemsR = 0;
     if (!(stage_mask & 2)) run.items2 = 0;
     GLin dummy{};
     return launch_gemms(run, dummy, st);
