@@ -27,14 +27,17 @@ HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 
 CFLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-I" + INCLUDE, "-I" + CSRC,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          # matrix-instruction accumulators stay in VGPRs (no copies through AGPRs)
-          "-mllvm", "-amdgpu-mfma-vgpr-form",
           "-Wall", "-Wno-unused-function", "-Wno-unused-result"]
+# matrix-instruction accumulators stay in VGPRs (no copies through AGPRs) in
+# the decode kernels; the GEMM kernels keep their 256 accumulators in AGPRs
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+AGPR_ACC = {"lb_gemm.hip"}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + CFLAGS + ["-c", src, "-o", obj]
+    extra = [] if os.path.basename(src) in AGPR_ACC else VGPR_FORM
+    cmd = [HIPCC] + CFLAGS + extra + ["-c", src, "-o", obj]
     p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     # hipcc's host pass does not know the packed-fp32 feature; that note is harmless.
     out = "\n".join(l for l in p.stdout.splitlines()

@@ -380,7 +380,9 @@ int lb_grouped_prepare(const lb_linear_desc *descs, int n, int64_t T, int x_dtyp
             return rc;
     } else if (rec.kind == GroupKind::Gemm) {
         rec.state.assign(gemm_group_state_bytes(), 0);
-        if ((rc = gemm_group_prepare(ls.data(), n, ws, ws_bytes, rec.state.data()))) return rc;
+        if ((rc = gemm_group_prepare(ls.data(), n, ws, ws_bytes, rec.state.data(),
+                                     (hipStream_t)stream)))
+            return rc;
     }
     std::lock_guard<std::mutex> lk(g_groups_mu);
     g_groups[ws] = std::move(rec);

@@ -45,18 +45,29 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 namespace {
 
 constexpr int kBM = 256;                     // tokens per tile
-constexpr int kBN = 128;                     // output columns per tile
 constexpr int kBK = 64;                      // contraction elements per K-tile (two packed words)
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
-constexpr int kStages = 2;                   // LDS ring depth: two workgroups fit one CU
 constexpr int kRowBytes = kBK * 2;           // one activation row of a K-tile (bf16)
 constexpr int kABytes = kBM * kRowBytes;     // 32 KB
-constexpr int kXWave = 2 * 64 * 4;           // a wave's sign words: [2 words][64 columns]
 constexpr int kGWave = 2 * kBK * 2;          // a wave's bf16 g: [2 paths][kBK]
-constexpr int kSlot = kABytes + kWaves * (kXWave + kGWave);
-constexpr int kLds = kStages * kSlot;        // 70 KB: two workgroups per CU
-constexpr int kMaxKtPerSplit = 128;          // stage-1 K-tiles per piece (8192 inputs)
+
+// Two tile shapes, by n-blocks (32 columns) per wave NBW; waves are 2 x 2:
+//   NBW = 2: 256 x 128 tiles, 128 x 64 per wave, 2-slot ring (70 KB): two
+//            workgroups per CU (stage 1: few, long tiles)
+//   NBW = 4: 256 x 256 tiles, 128 x 128 per wave (accumulators in AGPRs),
+//            4-slot ring (148 KB): one workgroup per CU, three K-tiles in flight
+template <int NBW> struct Shape {
+    static constexpr int BN = 64 * NBW;
+    static constexpr int XWave = 2 * NBW * 32 * 4;     // a wave's sign words: [2 words][NBW*32]
+    static constexpr int Slot = kABytes + kWaves * (XWave + kGWave);
+    static constexpr int Stages = NBW == 4 ? 4 : 2;
+    static constexpr int Lds = Stages * Slot;
+};
+constexpr int kNBW1 = 2, kNBW2 = 2;          // stage 1, stage 2
+constexpr int kBN1 = Shape<kNBW1>::BN, kBN2 = Shape<kNBW2>::BN;
+constexpr int kWG1 = 512;                    // stage-1 workgroups a launch aims for: two per
+                                             // CU on 256 CUs, so no CU runs a second round
 constexpr uint32_t kOOB = 0x7ffffff0u;       // a buffer offset past every range: reads as zero
 
 // One linear of a prefill launch.
@@ -173,20 +184,23 @@ __device__ __forceinline__ f32x16 mfma(const u32x4 &s, const u32x4 &a, f32x16 c)
 // STAGE 1: A = x (bf16), sign words of V, scales g; output t (bf16, l applied)
 //          or fp32 pieces.
 // STAGE 2: A = t (bf16), sign words of U, scales h; output y.
-template <int STAGE>
-__global__ __launch_bounds__(kThreads, 2) void k_gemm(GRun run, GLin single) {
+template <int STAGE, int NBW>
+__global__ __launch_bounds__(kThreads, NBW == 4 ? 1 : 2) void k_gemm(GRun run, GLin single) {
+    using SH = Shape<NBW>;
+    constexpr int BN = SH::BN, XWave = SH::XWave, Slot = SH::Slot, Stages = SH::Stages;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int64_t items = STAGE == 1 ? run.items1 : run.items2;
     const int64_t v = xcd_order(blockIdx.x, items);
     const GLin L = pick(run, single, STAGE == 1 ? run.lin1 : run.lin2, v);
     const int64_t local = v - (STAGE == 1 ? L.item1 : L.item2);
+    // item = (piece of d_in [stage 1], token tile, column tile)
     const int nt = STAGE == 1 ? L.nt1 : L.nt2;
     const int ni = (int)(local % nt);
     const int mi = (int)((local / nt) % L.mt);
     const int split = STAGE == 1 ? (int)(local / ((int64_t)nt * L.mt)) : 0;
     const int T = run.T;
     const int64_t m0 = (int64_t)mi * kBM;
-    const int n0 = ni * kBN;
+    const int n0 = ni * BN;
     const int kt0 = STAGE == 1 ? split * L.ktps : 0;
     const int kt1 = STAGE == 1 ? (int)imin(L.nkt1, kt0 + L.ktps) : L.nkt2;
 
@@ -194,10 +208,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(GRun run, GLin single) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hh = lane >> 5, l32 = lane & 31;
     const int wm = wave & 1, wn = wave >> 1;
+    const int nw0 = n0 + wn * NBW * 32;                       // this wave's first column
 
-    // ---- loads of one K-tile (per wave: 8 activation DMAs, 2 sign-word DMAs, 1 g DMA) ----
+    // ---- loads of one K-tile (per wave: 8 activation DMAs, NBW sign-word DMAs, 1 g DMA) ----
     // activations: wave w fills rows 64w .. 64w+63, 8 rows (1 KB) per DMA; lane i
-    // lands in row r0 + i/8 at swizzled position i%8, which holds chunk (i%8)^(r%8)
+    // lands in row r = r0 + i/8 at position i%8, which holds chunk (i%8) ^ swz(r)
     const int64_t K = STAGE == 1 ? L.d_in : L.ldt;
     const int rows = (int)imin(kBM, (int64_t)T - m0);
     const uint8_t *abase = STAGE == 1 ? (const uint8_t *)L.x : (const uint8_t *)L.t;
@@ -209,22 +224,29 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(GRun run, GLin single) {
     const uint32_t aoffe = (uint32_t)(arow0 * K * 2) + (uint32_t)(ach0 * 16);
     const uint32_t aoffo = (uint32_t)(arow0 * K * 2) + (uint32_t)(ach1 * 16);
     const uint32_t astep = (uint32_t)(8 * K * 2);            // 8 rows
-    // sign words: this wave's 64 columns n0 + 64*wn + lane, both words of the K-tile
-    const int xn = n0 + wn * 64 + lane;
+    // sign words: this wave's columns nw0 + 64c + lane, c < NBW/2, both words of the K-tile
     __amdgpu_buffer_rsrc_t rx;
-    uint32_t xoff = kOOB, xstep;
+    uint32_t xoff[NBW / 2], xstep;
     int xwords;
     if (STAGE == 1) {
         rx = make_rsrc(L.vz, (int64_t)L.P * L.kw_v * L.zld_v * 4);
-        const int qn = xn >> 5;
-        const int p = qn / L.kw;
-        const int k = (qn - p * L.kw) * 32 + (xn & 31);
-        if (p < L.P && k < L.r_p) xoff = (uint32_t)(((int64_t)p * L.kw_v * L.zld_v + k) * 4);
+#pragma unroll
+        for (int c = 0; c < NBW / 2; ++c) {
+            const int xn = nw0 + 64 * c + lane;
+            const int qn = xn >> 5;
+            const int p = qn / L.kw;
+            const int k = (qn - p * L.kw) * 32 + (xn & 31);
+            xoff[c] = (p < L.P && k < L.r_p) ? (uint32_t)(((int64_t)p * L.kw_v * L.zld_v + k) * 4) : kOOB;
+        }
         xstep = (uint32_t)(L.zld_v * 4);
         xwords = L.kw_v;
     } else {
         rx = make_rsrc(L.uz, (int64_t)L.P * L.kw * L.zld_u * 4);
-        if (xn < L.d_out) xoff = (uint32_t)(xn * 4);
+#pragma unroll
+        for (int c = 0; c < NBW / 2; ++c) {
+            const int xn = nw0 + 64 * c + lane;
+            xoff[c] = xn < L.d_out ? (uint32_t)(xn * 4) : kOOB;
+        }
         xstep = (uint32_t)(L.zld_u * 4);
         xwords = L.P * L.kw;
     }
@@ -233,7 +255,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(GRun run, GLin single) {
     const int gpath = lane >> 5, gel = 2 * (lane & 31);
 
     auto issue = [&](int kt, int slot) {
-        uint8_t *S = smem + slot * kSlot;
+        uint8_t *S = smem + slot * Slot;
         const bool kine = kt * kBK + 8 * ach0 < K;            // chunk inside the row
         const bool kino = kt * kBK + 8 * ach1 < K;
 #pragma unroll
@@ -242,25 +264,28 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(GRun run, GLin single) {
             const uint32_t off = ((i & 1) ? aoffo : aoffe) + i * astep + (uint32_t)(kt * kBK * 2);
             dma<16>(ra, S + (wave * 64 + 8 * i) * kRowBytes, kin ? off : kOOB);
         }
-        uint8_t *X = S + kABytes + wave * (kXWave + kGWave);
+        uint8_t *X = S + kABytes + wave * (XWave + kGWave);
 #pragma unroll
         for (int wd = 0; wd < 2; ++wd) {
             const int q = kt * 2 + wd;
-            dma<4>(rx, X + wd * 256, (xoff != kOOB && q < xwords) ? xoff + (uint32_t)q * xstep : kOOB);
+#pragma unroll
+            for (int c = 0; c < NBW / 2; ++c)
+                dma<4>(rx, X + (wd * NBW * 32 + 64 * c) * 4,
+                       (xoff[c] != kOOB && q < xwords) ? xoff[c] + (uint32_t)q * xstep : kOOB);
         }
         if (STAGE == 1) {
             const int64_t e = (int64_t)kt * kBK + gel;
-            dma<4>(rg, X + kXWave, e < L.d_in ? (uint32_t)((gpath * L.d_in + e) * 2) : kOOB);
+            dma<4>(rg, X + XWave, e < L.d_in ? (uint32_t)((gpath * L.d_in + e) * 2) : kOOB);
         }
     };
-    constexpr int kIssued = STAGE == 1 ? 11 : 10;            // DMAs per K-tile per wave
+    constexpr int kIssued = 8 + NBW + (STAGE == 1 ? 1 : 0);   // DMAs per K-tile per wave
 
     // ---- per-lane constants of the sign operands ----
-    int gofs[2];          // stage 1: byte offset of this lane's g run (path of the column)
-    uint32_t hpair[2][2]; // stage 2: bf16 h pair per n-block and path
+    int gofs[NBW];           // stage 1: byte offset of this lane's g run (path of the column)
+    uint32_t hpair[NBW][2];  // stage 2: bf16 h pair per n-block and path
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        const int n = n0 + wn * 64 + b * 32 + l32;
+    for (int b = 0; b < NBW; ++b) {
+        const int n = nw0 + b * 32 + l32;
         if (STAGE == 1) {
             const int p = (n >> 5) / L.kw;
             gofs[b] = (p < L.P ? p : 0) * kBK * 2 + hh * 16;
@@ -277,15 +302,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(GRun run, GLin single) {
     // stage 1 without pieces: l for this lane's output columns (4 per accumulator
     // quad), loaded before the K loop.  r_p is a multiple of 16, so a run of 4
     // columns is all real latents or all padding.
-    u32x2 lsc[2][4];
+    u32x2 lsc[NBW][4];
     uint32_t lok = 0;                                  // bit 4b+q4: run of real latents
     if (STAGE == 1 && L.nsplit == 1) {
-        const uint16_t *lp[2][4];
+        const uint16_t *lp[NBW][4];
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < NBW; ++b)
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
-                const int n = n0 + wn * 64 + b * 32 + 8 * q4 + 4 * hh;
+                const int n = nw0 + b * 32 + 8 * q4 + 4 * hh;
                 const int qn = n >> 5;
                 const int p = qn / L.kw;
                 const int k = (qn - p * L.kw) * 32 + (n & 31);
@@ -295,12 +320,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(GRun run, GLin single) {
             }
         if (((uintptr_t)L.l & 7) == 0) {
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+            for (int b = 0; b < NBW; ++b)
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) lsc[b][q4] = *(const u32x2 *)lp[b][q4];
         } else {
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+            for (int b = 0; b < NBW; ++b)
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     const uint16_t *q = lp[b][q4];
@@ -310,119 +335,138 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(GRun run, GLin single) {
         }
     }
 
-    f32x16 acc[2][4];
+    f32x16 acc[NBW][4];
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < NBW; ++b)
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[b][mb][i] = 0.0f;
 
+    // One K-tile = 4 steps of 16 elements (step st: word st/2, half st%2).
     auto compute = [&](int slot, int kt) {
-        const uint8_t *A = smem + slot * kSlot;
-        const uint8_t *Xw = A + kABytes + wave * (kXWave + kGWave);
-        const uint8_t *G = Xw + kXWave;
+        const uint8_t *A = smem + slot * Slot;
+        const uint8_t *Xw = A + kABytes + wave * (XWave + kGWave);
+        const uint8_t *G = Xw + XWave;
 #pragma unroll
-        for (int w2 = 0; w2 < 2; ++w2) {
-            uint32_t xs[2];
+        for (int st = 0; st < 4; ++st) {
+            const int w2 = st >> 1, s = st & 1;
+            u32x4 act[4];
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
-                xs[b] = ((const uint32_t *)Xw)[w2 * 64 + b * 32 + l32] << xshift;
-            int pq = 0;
-            if (STAGE == 2) pq = (kt * 2 + w2) >= L.kw ? 1 : 0;       // path of this word (uniform)
+            for (int mb = 0; mb < 4; ++mb) {
+                const int row = wm * 128 + mb * 32 + l32;
+                const int chunk = 2 * st + hh;
+                act[mb] = *(const u32x4 *)(A + row * kRowBytes + ((chunk ^ swz(row)) << 4));
+            }
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                u32x4 act[4];
-#pragma unroll
-                for (int mb = 0; mb < 4; ++mb) {
-                    const int row = wm * 128 + mb * 32 + l32;
-                    const int chunk = 4 * w2 + 2 * s + hh;
-                    act[mb] = *(const u32x4 *)(A + row * kRowBytes + ((chunk ^ swz(row)) << 4));
+            for (int b = 0; b < NBW; ++b) {
+                const uint32_t xs = ((const uint32_t *)Xw)[w2 * NBW * 32 + b * 32 + l32] << xshift;
+                u32x4 sc;
+                if (STAGE == 1) {
+                    sc = *(const u32x4 *)(G + gofs[b] + (32 * w2 + 16 * s) * 2);
+                } else {
+                    const uint32_t hp = (kt * 2 + w2) >= L.kw ? hpair[b][1] : hpair[b][0];
+                    sc = u32x4{hp, hp, hp, hp};
                 }
+                u32x4 sg;
 #pragma unroll
-                for (int b = 0; b < 2; ++b) {
-                    u32x4 sc;
-                    if (STAGE == 1) {
-                        sc = *(const u32x4 *)(G + gofs[b] + (32 * w2 + 16 * s) * 2);
-                    } else {
-                        const uint32_t hp = pq ? hpair[b][1] : hpair[b][0];
-                        sc = u32x4{hp, hp, hp, hp};
-                    }
-                    u32x4 sg4;
+                for (int jj = 0; jj < 4; ++jj)
+                    sg[jj] = sc[jj] ^ ((xs << (11 - 8 * s - jj)) & 0x80008000u);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        sg4[j] = sc[j] ^ ((xs[b] << (11 - 8 * s - j)) & 0x80008000u);
-#pragma unroll
-                    for (int mb = 0; mb < 4; ++mb) acc[b][mb] = mfma(sg4, act[mb], acc[b][mb]);
-                }
+                for (int mb = 0; mb < 4; ++mb) acc[b][mb] = mfma(sg, act[mb], acc[b][mb]);
             }
         }
     };
 
-    // ---- K loop over a ring of kStages slots ----
-    // At the top of iteration kt the tiles kt .. kt+kStages-2 have been issued;
+    // ---- K loop over a ring of Stages slots ----
+    // At the top of iteration kt the tiles kt .. kt+Stages-2 have been issued;
     // after the wait and the barrier tile kt is in LDS for every wave and the
-    // slot of tile kt-1 is free again, so tile kt+kStages-1 is issued into it.
+    // slot of tile kt-1 is free again, so tile kt+Stages-1 is issued into it.
 #pragma unroll
-    for (int j = 0; j < kStages - 1; ++j)
+    for (int j = 0; j < Stages - 1; ++j)
         if (kt0 + j < kt1) issue(kt0 + j, j);
     for (int kt = kt0; kt < kt1; ++kt) {
-        const int slot = (kt - kt0) % kStages;
-        if (kt + kStages - 2 < kt1) wait_and_meet<(kStages - 2) * kIssued>();
+        const int slot = (kt - kt0) % Stages;
+        if (kt + Stages - 2 < kt1) wait_and_meet<(Stages - 2) * kIssued>();
         else wait_and_meet<0>();
-        if (kt + kStages - 1 < kt1) issue(kt + kStages - 1, (slot + kStages - 1) % kStages);
+        if (kt + Stages - 1 < kt1) issue(kt + Stages - 1, (slot + Stages - 1) % Stages);
         compute(slot, kt);
     }
 
-    // ---- epilogue: lane holds columns n .. n+3 of token m per accumulator quad ----
+    // ---- epilogue ----
+    // The lane holds columns n .. n+3 of token m per accumulator quad.  Each
+    // wave stages 64 rows of its tile at a time in its own part of the (now
+    // idle) ring and writes them back as whole 16-byte chunks of rows, through
+    // a buffer descriptor over this token tile's rows: rows past T fall outside
+    // the range and are dropped.
+    const int64_t ld_out = STAGE == 1 ? L.ldt : L.d_out;
+    const int64_t n_lim = STAGE == 1 ? L.ldt : L.d_out;       // columns that exist
+    const int osz = STAGE == 1 ? (L.nsplit > 1 ? 4 : 2) : (run.y_dtype == LB_BF16 ? 2 : 4);
+    const uint8_t *obase = STAGE == 1
+        ? (L.nsplit > 1 ? (const uint8_t *)(L.part + (int64_t)split * T * L.ldt) : (const uint8_t *)L.t)
+        : (const uint8_t *)L.y;
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(obase + m0 * ld_out * osz, (int64_t)rows * ld_out * osz);
+    constexpr int WC = NBW * 32;                               // columns of a wave
+    const int rbytes = WC * osz + 16;                          // staged row (padded)
+    uint8_t *stage = smem + wave * 64 * (WC * 4 + 16);         // room for the fp32 case
+    // whole 16-byte chunks only when every row starts 16-byte aligned
+    const bool chunky = ((ld_out * osz) % 16) == 0 && ((uintptr_t)obase % 16) == 0;
+    wait_and_meet<0>();                                        // every wave is done with the ring
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-        const int64_t m = m0 + wm * 128 + mb * 32 + l32;
-        if (m >= T) continue;
+    for (int half = 0; half < 2; ++half) {
+        // accumulators -> LDS (l applied for stage-1 latents)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
+        for (int mh = 0; mh < 2; ++mh) {
+            const int mb = 2 * half + mh;
+            uint8_t *rowp = stage + (mh * 32 + l32) * rbytes;
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int n = n0 + wn * 64 + b * 32 + 8 * q4 + 4 * hh;
-                float o[4];
+            for (int b = 0; b < NBW; ++b)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) o[e] = acc[b][mb][4 * q4 + e];
-                if (STAGE == 1) {
-                    if (n >= L.ldt) continue;
-                    if (L.nsplit > 1) {
-                        float *dst = L.part + ((int64_t)split * T + m) * L.ldt + n;
-                        *(f32x4 *)dst = f32x4{o[0], o[1], o[2], o[3]};
-                    } else {
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const f32x16 &a = acc[b][mb];
+                    float o0 = a[4 * q4], o1 = a[4 * q4 + 1], o2 = a[4 * q4 + 2], o3 = a[4 * q4 + 3];
+                    const int c = b * 32 + 8 * q4 + 4 * hh;          // column within the wave
+                    if (STAGE == 1 && L.nsplit == 1) {
                         const u32x2 w = lsc[b][q4];
                         const bool ok = (lok >> (4 * b + q4)) & 1u;   // padding columns stay zero
-                        const float t0 = ok ? f16_to_f32((uint16_t)(w[0] & 0xffffu)) * o[0] : 0.0f;
-                        const float t1 = ok ? f16_to_f32((uint16_t)(w[0] >> 16)) * o[1] : 0.0f;
-                        const float t2 = ok ? f16_to_f32((uint16_t)(w[1] & 0xffffu)) * o[2] : 0.0f;
-                        const float t3 = ok ? f16_to_f32((uint16_t)(w[1] >> 16)) * o[3] : 0.0f;
-                        *(u32x2 *)(L.t + m * L.ldt + n) = u32x2{bf16_pair(t0, t1), bf16_pair(t2, t3)};
+                        o0 = ok ? f16_to_f32((uint16_t)(w[0] & 0xffffu)) * o0 : 0.0f;
+                        o1 = ok ? f16_to_f32((uint16_t)(w[0] >> 16)) * o1 : 0.0f;
+                        o2 = ok ? f16_to_f32((uint16_t)(w[1] & 0xffffu)) * o2 : 0.0f;
+                        o3 = ok ? f16_to_f32((uint16_t)(w[1] >> 16)) * o3 : 0.0f;
                     }
-                } else {
-                    if (n >= L.d_out) continue;
-                    const int64_t e0 = m * L.d_out + n;
-                    if (run.y_dtype == LB_BF16) {
-                        uint16_t *py = (uint16_t *)L.y + e0;
-                        if (n + 4 <= L.d_out && ((uintptr_t)py & 7) == 0) {
-                            *(u32x2 *)py = u32x2{bf16_pair(o[0], o[1]), bf16_pair(o[2], o[3])};
-                            continue;
-                        }
-                    } else {
-                        float *py = (float *)L.y + e0;
-                        if (n + 4 <= L.d_out && ((uintptr_t)py & 15) == 0) {
-                            *(f32x4 *)py = f32x4{o[0], o[1], o[2], o[3]};
-                            continue;
-                        }
-                    }
+                    if (osz == 2)
+                        *(u32x2 *)(rowp + c * 2) = u32x2{bf16_pair(o0, o1), bf16_pair(o2, o3)};
+                    else
+                        *(f32x4 *)(rowp + c * 4) = f32x4{o0, o1, o2, o3};
+                }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave's LDS writes land
+        // LDS -> global: 64 rows x WC columns in 16-byte chunks, lane order row-major
+        const int cpr = WC * osz / 16;                         // chunks per row
+        const int nchunks = 64 * cpr;
+        for (int ci = lane; ci < nchunks; ci += 64) {
+            const int r = ci / cpr, ch = ci - r * cpr;
+            const int col = ch * (16 / osz);                   // first column of the chunk
+            const int n = nw0 + col;
+            const u32x4 val = *(const u32x4 *)(stage + r * rbytes + ch * 16);
+            const uint32_t off =
+                (uint32_t)(((wm * 128 + half * 64 + r) * ld_out + n) * osz);
+            const int per = 16 / osz;
+            if (chunky && n + per <= n_lim) {
+                __builtin_amdgcn_raw_buffer_store_b128(val, ro, (int)off, 0, 0);
+            } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (n + e < L.d_out) store_act(L.y, run.y_dtype, e0 + e, o[e]);
+                for (int e = 0; e < 8; ++e) {
+                    if (e >= per || n + e >= n_lim) break;
+                    if (osz == 2)
+                        __builtin_amdgcn_raw_buffer_store_b16(
+                            (unsigned short)((val[e >> 1] >> (16 * (e & 1))) & 0xffffu), ro, (int)(off + 2 * e), 0, 0);
+                    else
+                        __builtin_amdgcn_raw_buffer_store_b32(val[e], ro, (int)(off + 4 * e), 0, 0);
                 }
             }
         }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the next half
     }
 }
 
@@ -519,7 +563,7 @@ bool gemm_shape_ok(const Linear &a) {
     if (a.T > (1ll << 24)) return false;
     // 32-bit buffer offsets over one 256-token tile of activations or latents,
     // and over the packed words of one linear
-    if (a.d_in >= (1ll << 21) || a.r_p >= (1ll << 20)) return false;
+    if (a.d_in >= (1ll << 21) || a.r_p >= (1ll << 19) || a.d_out >= (1ll << 20)) return false;
     if ((int64_t)a.P * cdiv(a.d_in, 32) * rup(a.r_p, 4) * 4 >= (1ll << 31)) return false;
     if ((int64_t)a.P * cdiv(a.r_p, 32) * rup(a.d_out, 4) * 4 >= (1ll << 31)) return false;
     return true;
@@ -527,7 +571,35 @@ bool gemm_shape_ok(const Linear &a) {
 
 // Schedule fields of one linear; returns the workspace bytes it needs (the
 // latents, the stage-1 pieces and, for fp32 inputs, their bf16 copy).
-size_t plan(const Linear &a, GLin *m) {
+// Stage-1 pieces (d_in splits) per linear for a launch over ls[0..n): start
+// at one piece per tile and, while the launch stays within kWG1 workgroups,
+// split further the linear whose pieces are longest (every tile of a linear
+// takes one more piece).  Writes splits[j].
+void stage1_splits(const Linear *ls, int n, std::vector<int> &splits) {
+    std::vector<int64_t> nkt((size_t)n), tiles((size_t)n);
+    int64_t used = 0;
+    for (int j = 0; j < n; ++j) {
+        const Linear &a = ls[j];
+        const int64_t ldt = rup((int64_t)a.P * cdiv(a.r_p, 32) * 32, kBK);
+        nkt[(size_t)j] = cdiv(a.d_in, kBK);
+        tiles[(size_t)j] = cdiv(ldt, kBN1) * cdiv(a.T, kBM);
+        used += tiles[(size_t)j];
+    }
+    splits.assign((size_t)n, 1);
+    for (;;) {
+        int best = -1;
+        int64_t len = 0;
+        for (int j = 0; j < n; ++j) {
+            const int64_t l = cdiv(nkt[(size_t)j], splits[(size_t)j]);
+            if (l > len && splits[(size_t)j] < nkt[(size_t)j]) { len = l; best = j; }
+        }
+        if (best < 0 || len <= 8 || used + tiles[(size_t)best] > kWG1) break;
+        used += tiles[(size_t)best];
+        ++splits[(size_t)best];
+    }
+}
+
+size_t plan(const Linear &a, GLin *m, int nsplit) {
     *m = GLin{};
     m->x = a.x;
     m->y = a.y;
@@ -548,13 +620,13 @@ size_t plan(const Linear &a, GLin *m) {
     m->kw_v = (int32_t)cdiv(a.d_in, 32);
     m->ldt = (int32_t)rup((int64_t)a.P * m->kw * 32, kBK);
     m->nkt1 = (int32_t)cdiv(a.d_in, kBK);
-    m->nsplit = (int32_t)cdiv(m->nkt1, kMaxKtPerSplit);
+    m->nsplit = (int32_t)imax(1, nsplit);
     m->ktps = (int32_t)cdiv(m->nkt1, m->nsplit);
     m->nsplit = (int32_t)cdiv(m->nkt1, m->ktps);
     m->nkt2 = m->ldt / kBK;
     m->mt = (int32_t)cdiv(a.T, kBM);
-    m->nt1 = (int32_t)cdiv(m->ldt, kBN);
-    m->nt2 = (int32_t)cdiv(a.d_out, kBN);
+    m->nt1 = (int32_t)cdiv(m->ldt, kBN1);
+    m->nt2 = (int32_t)cdiv(a.d_out, kBN2);
     m->nred = m->nsplit > 1 ? (int32_t)cdiv(a.T * (m->ldt / 4), kRedGroups) : 0;
     const int64_t nv = (int64_t)a.P * m->kw_v * m->zld_v, nu = (int64_t)a.P * m->kw * m->zld_u;
     m->ngp = (int32_t)cdiv((int64_t)a.P * a.d_in / 2 + nv + nu, kPrep);
@@ -585,11 +657,11 @@ int64_t items1_of(const GLin &m) { return (int64_t)m.nsplit * m.nt1 * m.mt; }
 int64_t items2_of(const GLin &m) { return (int64_t)m.nt2 * m.mt; }
 
 template <typename K>
-int raise_lds(K kern) {
+int raise_lds(K kern, int bytes) {
     // > 64 KB of dynamic LDS needs an explicit opt-in (once per kernel; idempotent)
     static bool done = false;
     if (!done) {
-        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLds) !=
+        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) !=
             hipSuccess)
             return hip_status(hipGetLastError());
         done = true;
@@ -604,8 +676,8 @@ int launch_gemms(const GRun &run, const GLin &single, hipStream_t st) {
         if ((rc = last_launch_status())) return rc;
     }
     if (run.items1 > 0) {
-        if ((rc = raise_lds(k_gemm<1>))) return rc;
-        k_gemm<1><<<(unsigned)run.items1, kThreads, kLds, st>>>(run, single);
+        if ((rc = raise_lds(k_gemm<1, kNBW1>, Shape<kNBW1>::Lds))) return rc;
+        k_gemm<1, kNBW1><<<(unsigned)run.items1, kThreads, Shape<kNBW1>::Lds, st>>>(run, single);
         if ((rc = last_launch_status())) return rc;
     }
     if (run.itemsR > 0) {
@@ -613,8 +685,8 @@ int launch_gemms(const GRun &run, const GLin &single, hipStream_t st) {
         if ((rc = last_launch_status())) return rc;
     }
     if (run.items2 > 0) {
-        if ((rc = raise_lds(k_gemm<2>))) return rc;
-        k_gemm<2><<<(unsigned)run.items2, kThreads, kLds, st>>>(run, single);
+        if ((rc = raise_lds(k_gemm<2, kNBW2>, Shape<kNBW2>::Lds))) return rc;
+        k_gemm<2, kNBW2><<<(unsigned)run.items2, kThreads, Shape<kNBW2>::Lds, st>>>(run, single);
         if ((rc = last_launch_status())) return rc;
     }
     return LB_OK;
@@ -626,14 +698,18 @@ size_t gemm_workspace_bytes(const Linear &a) {
     const size_t v = valu_workspace_bytes(a);
     if (!gemm_shape_ok(a)) return v;
     GLin m;
-    const size_t g = plan(a, &m);
+    std::vector<int> sp;
+    stage1_splits(&a, 1, sp);
+    const size_t g = plan(a, &m, sp[0]);
     return g > v ? g : v;     // a misaligned x at run time takes the vector-ALU kernels
 }
 
 int gemm_forward(const Linear &a, void *ws, hipStream_t st) {
     if (!gemm_shape_ok(a)) return valu_forward(a, ws, st);
     GLin m;
-    plan(a, &m);
+    std::vector<int> sp;
+    stage1_splits(&a, 1, sp);
+    plan(a, &m, sp[0]);
     uint16_t *xb = bind(&m, a, (uint8_t *)ws);
     if (a.x_dtype == LB_F32) {
         const int64_t n4 = a.T * a.d_in / 4;
@@ -655,7 +731,7 @@ int gemm_forward(const Linear &a, void *ws, hipStream_t st) {
 // ---- groups ------------------------------------------------------------------
 
 struct GGroupHost {
-    GRun run;
+    GRun run;      // the weight preparation (k_prep) ran at prepare time
 };
 
 // bf16 inputs only (fp32 groups run linear by linear)
@@ -666,11 +742,13 @@ bool gemm_group_supported(const Linear *ls, int n) {
 }
 
 size_t gemm_group_workspace_bytes(const Linear *ls, int n) {
+    std::vector<int> sp;
+    stage1_splits(ls, n, sp);
     size_t need = 256 + rup256(sizeof(GLin) * n);
     int64_t iG = 0, i1 = 0, iR = 0, i2 = 0;
     for (int j = 0; j < n; ++j) {
         GLin m;
-        need += plan(ls[j], &m);
+        need += plan(ls[j], &m, sp[(size_t)j]);
         iG += m.ngp;
         i1 += items1_of(m);
         iR += m.nred;
@@ -682,18 +760,21 @@ size_t gemm_group_workspace_bytes(const Linear *ls, int n) {
 
 size_t gemm_group_state_bytes() { return sizeof(GGroupHost); }
 
-int gemm_group_prepare(const Linear *ls, int n, void *ws, size_t ws_bytes, void *host_state) {
+int gemm_group_prepare(const Linear *ls, int n, void *ws, size_t ws_bytes, void *host_state,
+                       hipStream_t st) {
     GGroupHost *hs = (GGroupHost *)host_state;
     if (!gemm_group_supported(ls, n)) return LB_EUNSUPPORTED;
     if (ws_bytes < gemm_group_workspace_bytes(ls, n)) return LB_EWORKSPACE;
     uint8_t *w = (uint8_t *)ws;
+    std::vector<int> sp;
+    stage1_splits(ls, n, sp);
     GLin *table_dev = (GLin *)(w + 256);
     uint8_t *cur = w + 256 + rup256(sizeof(GLin) * n);
     std::vector<GLin> tab((size_t)n);
     int64_t iG = 0, i1 = 0, iR = 0, i2 = 0;
     for (int j = 0; j < n; ++j) {
         GLin &m = tab[(size_t)j];
-        const size_t b = plan(ls[j], &m);
+        const size_t b = plan(ls[j], &m, sp[(size_t)j]);
         bind(&m, ls[j], cur);
         cur += b;
         m.itemG = iG;
@@ -736,13 +817,20 @@ int gemm_group_prepare(const Linear *ls, int n, void *ws, size_t ws_bytes, void 
     run.lin1 = lin1;
     run.linR = linR;
     run.lin2 = lin2;
-    return LB_OK;
+    // the factors are captured with the group: convert g and unzip the sign
+    // words once here (runs read the converted copies)
+    GRun prep = run;
+    prep.items1 = prep.itemsR = prep.items2 = 0;
+    GLin dummy{};
+    if (int rc = launch_gemms(prep, dummy, st)) return rc;
+    run.itemsG = 0;
+    return hip_status(hipStreamSynchronize(st));
 }
 
 int gemm_group_run(const void *host_state, hipStream_t st, int stage_mask) {
     const GGroupHost *hs = (const GGroupHost *)host_state;
     GRun run = hs->run;
-    if (!(stage_mask & 1)) run.itemsG = run.items1 = run.itemsR = 0;
+    if (!(stage_mask & 1)) run.items1 = run.itemsR = 0;
     if (!(stage_mask & 2)) run.items2 = 0;
     GLin dummy{};
     return launch_gemms(run, dummy, st);

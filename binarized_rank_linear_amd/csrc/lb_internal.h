@@ -94,7 +94,10 @@ int gemm_forward(const Linear &a, void *ws, hipStream_t s);
 bool gemm_group_supported(const Linear *ls, int n);
 size_t gemm_group_workspace_bytes(const Linear *ls, int n);
 size_t gemm_group_state_bytes();
-int gemm_group_prepare(const Linear *ls, int n, void *ws, size_t ws_bytes, void *host_state);
+// Also prepares the captured factors (bf16 g, unzipped sign words) on stream s
+// and waits for it.
+int gemm_group_prepare(const Linear *ls, int n, void *ws, size_t ws_bytes, void *host_state,
+                       hipStream_t s);
 int gemm_group_run(const void *host_state, hipStream_t s, int stage_mask = 3);
 
 // SwiGLU gate: a = silu(gate) * up, elementwise over n values (fp32 in place).
