@@ -16,6 +16,7 @@ oracle on one layer of the same stack and scales to the stack.
     python bench.py [--steps K] [--warmup W] [--workload c5] [--tokens 1]
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -89,23 +90,63 @@ def time_decode(st, steps, warmup):
     return wall / steps, s1, s2
 
 
-def cpu_baseline(w, T, layers):
-    """fp64 oracle on one layer of the stack (all its linears), scaled to L layers."""
-    import numpy as np
+def cpu_baseline(w, T, layers, budget_s=10.0):
+    """The fp64 oracle on one layer of the stack (all its linears, seeded
+    inputs of the same shapes), run repeatedly until about budget_s seconds of
+    CPU time, scaled to the L-layer stack (the layers cost the same)."""
     import oracle
     import synth
-    t_layer = 0.0
+    inputs = []
     for i, sh in enumerate(w.linears):
         r, rp = oracle.rank_for_budget(sh.d_in, sh.d_out, w.b_num, w.b_den, w.residual)
         inp = synth.layer_inputs(i, sh.d_in, sh.d_out, rp, 2 if w.residual else 1)
         x = synth.activations(synth.activation_seed(T), T, sh.d_in, w.dtype)
+        inputs.append((x, inp))
+    passes, t_total = 0, 0.0
+    while t_total < budget_s and passes < 1000:
         t0 = time.perf_counter()
-        oracle.linear_forward(x, inp.U, inp.V, inp.h, inp.g, inp.l)
-        t_layer += time.perf_counter() - t0
+        for x, inp in inputs:
+            oracle.linear_forward(x, inp.U, inp.V, inp.h, inp.g, inp.l)
+        t_total += time.perf_counter() - t0
+        passes += 1
+    t_layer = t_total / passes
     cores = oracle.max_threads()
     return {"value": T / (t_layer * layers), "unit": "tok/s", "cores": cores, "kind": "oracle",
-            "sample": "one layer (%d linears) at T=%d timed once, scaled to the %d-layer stack"
-                      % (len(w.linears), T, layers)}
+            "sample": "one layer (%d linears, seeded inputs) at T=%d, %d passes in %.1f s, scaled "
+                      "to the %d-layer stack" % (len(w.linears), T, passes, t_total, layers)}
+
+
+def measured_traffic(kernel, workload, T):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when there is
+    none or the kernel source changed since the counters were taken."""
+    f = os.path.join(ROOT, "profiles", "traffic_%s_%s_T%d.txt" % (kernel, workload, T))
+    if not os.path.exists(f):
+        return None
+    kv = {}
+    for line in open(f):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    src = os.path.join(ROOT, "binarized_rank_linear_amd", "csrc", kv.get("source", ""))
+    if not os.path.exists(src):
+        return None
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != kv.get("source_sha256"):
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
+def calibrate_copy(mib, reps):
+    """A plain device-to-device copy of `mib` MiB, `reps` times: the reference
+    kernel whose FETCH_SIZE / WRITE_SIZE calibrate the traffic counters."""
+    import torch
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n * 4, "reps": reps}), flush=True)
 
 
 def prefill_leg(w, T, steps):
@@ -166,6 +207,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-prefill", action="store_true", help="skip the T=2048 prefill leg")
     ap.add_argument("--prefill-tokens", type=int, default=2048)
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only run the T=2048 prefill leg and print its JSON")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain MIB-MiB device copy (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the LittleBit stack fits one MI355X and this build "
@@ -175,6 +220,13 @@ def main():
     import torch
     import synth
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy, max(1, args.steps))
+        return
+    if args.prefill_only:
+        w = synth.WORKLOADS[args.workload]
+        print(json.dumps(prefill_leg(w, args.prefill_tokens, max(1, args.steps))), flush=True)
+        return
     w = synth.WORKLOADS[args.workload]
     layers = args.layers or w.layers
     T = args.tokens
@@ -215,7 +267,9 @@ def main():
             "packed_bytes_per_pass": st.packed_bytes() + st.scale_bytes(),
         },
         "roofline": {"bound": "hbm", "achieved": dominant[3], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": dominant[3] / HBM_PEAK_GBS, "traffic": None,
+                     "frac": dominant[3] / HBM_PEAK_GBS,
+                     "traffic": measured_traffic("k_stage%d" % dominant[0], args.workload, T),
+                     "algorithmic_bytes": dominant[1],
                      "kernel": "k_stage%d" % dominant[0],
                      "pass_GBs": (b1 + b2) / step_s / 1e9,
                      "pass_frac": (b1 + b2) / step_s / 1e9 / HBM_PEAK_GBS,

@@ -137,7 +137,9 @@ size_t lb_linear_workspace_bytes(int64_t d_in, int64_t d_out, int64_t r, int64_t
  * x and y must not overlap each other or ws (LB_EINVAL).
  * Path choice (flags): AUTO uses the decode kernels for T <= 32 and the MFMA
  * GEMM kernels above; PREFILL with y_dtype LB_F32 is LB_EUNSUPPORTED (the
- * GEMM path rounds its operands to bf16, outside the fp32 tolerance).
+ * GEMM path rounds its operands, including g and h, to bf16, outside the fp32
+ * tolerance).  Shapes the GEMM kernels do not take (d_in % 8 != 0, x not
+ * 16-byte or g not 4-byte aligned) run on the vector-ALU decode kernels.
  * Calls that overlap on the same workspace race. */
 int lb_linear_forward(const void *x, int x_dtype, void *y, int y_dtype,
                       const lb_factors *w, int64_t d_in, int64_t d_out, int64_t r,
@@ -180,14 +182,22 @@ size_t lb_grouped_workspace_bytes(const lb_linear_desc *descs, int n, int64_t T,
 /* Build the device work table of a group into ws.  BLOCKS until the table is
  * on the device (a setup call, not for the timed loop).  descs is a host array
  * of n descriptors; it is copied and may be freed afterwards.  All linears use
- * x_dtype / y_dtype and T tokens (1 <= T <= 32: the group runs the decode
- * kernels).  The pointers in descs are captured: later runs read and write the
- * same buffers. */
+ * x_dtype / y_dtype and T tokens.  The pointers in descs are captured: later
+ * runs read and write the same buffers.  The kernels a group runs:
+ *  - 1 <= T <= 32: the matrix-core decode kernels (stage 1 = activation
+ *    operands, first contractions and latents; stage 2 = second contractions);
+ *  - T > 32, bf16 output, bf16 input and shapes the GEMM kernels take
+ *    (d_in % 8 == 0, x 16-byte and g 4-byte aligned): the GEMM kernels
+ *    (stage 1 = first contractions and the d_in-piece reduction; stage 2 =
+ *    second contractions).  For these, prepare also derives a bf16 copy of g
+ *    and a re-ordered copy of the sign words into ws, so a caller that changes
+ *    the CONTENTS of the factor buffers must prepare the group again;
+ *  - otherwise the linears run one after the other through lb_linear_forward. */
 int lb_grouped_prepare(const lb_linear_desc *descs, int n, int64_t T, int x_dtype, int y_dtype,
                        void *ws, size_t ws_bytes, unsigned flags, void *stream);
 
-/* Run a prepared group: every linear's y = layer(x).  Two kernel launches for
- * the whole group (all first contractions, then all second contractions).
+/* Run a prepared group: every linear's y = layer(x), in a few launches for the
+ * whole group (all first contractions, then all second contractions).
  * Runs on the same workspace race. */
 int lb_grouped_run(void *ws, void *stream);
 
@@ -195,9 +205,9 @@ int lb_grouped_run(void *ws, void *stream);
  * applied to g (.) x, and the rank-r latents) or stage 2 (all second
  * contractions and the outputs).  Running stage 1 then stage 2 on one stream
  * equals lb_grouped_run; stage 2 reads what the preceding stage 1 wrote.
- * For timing and scheduling the two kernels separately.  LB_EINVAL for a
- * stage other than 1 or 2; LB_EUNSUPPORTED for a group prepared for a path
- * that does not run as two group kernels. */
+ * For timing and scheduling the two halves separately.  LB_EINVAL for a
+ * stage other than 1 or 2; LB_EUNSUPPORTED for a group that runs linear by
+ * linear. */
 int lb_grouped_run_stage(void *ws, int stage, void *stream);
 
 #ifdef __cplusplus
