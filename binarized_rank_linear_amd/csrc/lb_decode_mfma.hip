@@ -64,6 +64,9 @@ constexpr int kMaxKcg = 16;               // K-groups per stage-1 chunk (loads i
 constexpr int kBatch = 8;                 // stage-2 steps per load batch
 constexpr int kTilesPerItem2 = 8;         // 64-row tiles per wave in one stage-2 item
 constexpr int kPreVec = 8;                // operand vectors a thread loads before the plane loads
+constexpr int kWin2 = 8;                  // stage 2 (streaming form): plane loads in flight per wave
+constexpr uint32_t kOOB = 0x7ffffff0u;    // a buffer offset past every range: reads as zero
+constexpr int kHRows = kRG * kTilesPerItem2;   // output rows of one stage-2 item, at most
 
 // Activation-row layout of the A operands.  Stage 1 (one path): token n uses
 // rows (n % TPM1)*S1 + q, S1 = 2 (two limbs) or 4 (three limbs).  Stage 2 (both
@@ -106,6 +109,8 @@ struct MLin {
 struct MRun {
     int T, x_dtype, y_dtype;
     int ops2;                  // stage-2 operands (steps) the LDS holds at once
+    int dma2;                  // stage 2 runs k_stage2r (all operands and h fit the LDS)
+    int pad_;
     int64_t items0, items1, itemsF, items2;
     const MLin *table;         // null: the single linear passed by value
     const int32_t *lin0, *lin1, *linF, *lin2;   // item -> linear, per launch
@@ -669,6 +674,128 @@ __global__ __launch_bounds__(kThreads) void k_stage2(MRun run, MLin single) {
     }
 }
 
+// Stage 2, streaming form: each wave walks its (tile, K-group) sequence with
+// kWin2 plane loads in flight in a rotating set of registers: slot k is
+// consumed and immediately reloaded with the element kWin2 further on, so no
+// register is copied and no wait other than the one for the oldest load is
+// needed.  Loads are unconditional (offsets past the range read zeros).  The
+// operands of all steps and h of the item's rows sit in LDS for the whole item.
+template <int NL, int NB2>
+__global__ __launch_bounds__(kThreads) void k_stage2r(MRun run, MLin single) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    using R = Rows<NL>;
+    const MLin L = pick(run, single, run.lin2);
+    const int64_t local = (int64_t)blockIdx.x - L.item2;
+    const int T = run.T;
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int r16 = lane & 15, gq = lane >> 4;
+    const Nib nib = nibble_constants();
+
+    const int steps = L.kgs;                       // K-groups over both paths' planes
+    const int64_t row_begin = local * L.rows2;
+    const int tiles = (int)imin(L.rows2 / kRG, cdiv(L.d_out - row_begin, kRG));
+    const int total = tiles * steps;               // this wave's stream (uniform)
+    const int opb = L.R2 * kRec;
+    uint8_t *ops = smem;                                          // [steps][NB2] operands
+    uint16_t *hs = (uint16_t *)(smem + run.ops2 * NB2 * kOpS);   // [2][kHRows] fp16 h
+
+    // lane (gq, r16) loads rows row+4r16 .. +3 of plane 4s + gq of tile i
+    const __amdgpu_buffer_rsrc_t ru = make_rsrc(L.u_bits, (int64_t)L.P * L.kw_u * L.ld_u * 4);
+    const uint32_t uo = (uint32_t)(((int64_t)gq * L.ld_u + row_begin + wave * kTile + 4 * r16) * 4);
+    const uint32_t group4 = (uint32_t)(4 * L.ld_u * 4);
+    auto off_of = [&](int e) -> uint32_t {
+        const int i = e / steps, st = e - i * steps;
+        return e < total ? uo + (uint32_t)(i * kRG * 4) + (uint32_t)st * group4 : kOOB;
+    };
+    v4u slot[kWin2];
+#pragma unroll
+    for (int k = 0; k < kWin2; ++k) slot[k] = load_rows(ru, off_of(k));
+
+    // operands of every step and h of the item's rows, shared by the 4 waves
+    {
+        const int vecs = steps * NB2 * opb / 16;
+        for (int i = threadIdx.x; i < vecs; i += kThreads)
+            expand_vec(ops, i, L.R2, ((const v4u *)L.tb)[i]);
+        const int hn = 2 * L.rows2;
+        for (int i = threadIdx.x; i < hn; i += kThreads) {
+            const int pp = i >= L.rows2 ? 1 : 0;
+            const int64_t row = row_begin + (i - pp * L.rows2);
+            hs[pp * kHRows + (i - pp * L.rows2)] =
+                (pp < L.P && row < L.d_out) ? L.h[(int64_t)pp * L.d_out + row] : (uint16_t)0;
+        }
+    }
+    __syncthreads();
+
+    v4f acc[4][NB2];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int b = 0; b < NB2; ++b) acc[m][b] = v4f{0.f, 0.f, 0.f, 0.f};
+    int i = 0, st = 0;
+    auto process = [&](const v4u &w) {
+        const uint8_t *opp = ops + st * NB2 * kOpS;
+        v8i ao[NB2];
+        int sa[NB2];
+#pragma unroll
+        for (int b = 0; b < NB2; ++b) {
+            ao[b] = load_op(opp + b * kOpS);
+            sa[b] = opp[b * kOpS + kOp + lane];
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const v8i sg = unpack_word(w[m], nib);
+#pragma unroll
+            for (int b = 0; b < NB2; ++b) acc[m][b] = mfma(ao[b], sg, acc[m][b], sa[b]);
+        }
+        if (++st == steps) {
+            // y = sum_p h_p z_p for this lane's 4 rows of tile i (as k_stage2)
+            const int rl = i * kRG + wave * kTile + 4 * r16;      // row within the item
+            const int64_t row = row_begin + rl;
+            float hv[2][4];
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+                const v2u hw = *(const v2u *)(hs + pp * kHRows + rl);
+                hv[pp][0] = f16_to_f32((uint16_t)(hw[0] & 0xffffu));
+                hv[pp][1] = f16_to_f32((uint16_t)(hw[0] >> 16));
+                hv[pp][2] = f16_to_f32((uint16_t)(hw[1] & 0xffffu));
+                hv[pp][3] = f16_to_f32((uint16_t)(hw[1] >> 16));
+            }
+#pragma unroll
+            for (int b = 0; b < NB2; ++b) {
+                float y4[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const v4f a = acc[m][b];
+                    if (NL == 2) {
+                        y4[m] = hv[0][m] * (a[0] + a[1]) + hv[1][m] * (a[2] + a[3]);
+                    } else {
+                        const float o0 = __shfl_xor(a[0], 16, 64), o1 = __shfl_xor(a[1], 16, 64);
+                        const float z0 = (a[0] + a[1]) + a[2];
+                        const float z1 = (a[3] + o0) + o1;
+                        y4[m] = hv[0][m] * z0 + hv[1][m] * z1;
+                    }
+                }
+                const int n = b * R::TPM2 + (NL == 2 ? gq : gq / 2);
+                const bool writer = n < T && (NL == 2 || (gq & 1) == 0);
+                if (writer) store4(L.y, run.y_dtype, (int64_t)n * L.d_out + row, row, L.d_out, y4);
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int b = 0; b < NB2; ++b) acc[m][b] = v4f{0.f, 0.f, 0.f, 0.f};
+            st = 0;
+            ++i;
+        }
+    };
+    for (int e0 = 0; e0 < total; e0 += kWin2) {
+#pragma unroll
+        for (int k = 0; k < kWin2; ++k) {
+            if (e0 + k < total) process(slot[k]);                 // uniform
+            slot[k] = load_rows(ru, off_of(e0 + k + kWin2));
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
@@ -700,6 +827,12 @@ int kcg_cap(const Shape &s) { return (int)imin(kMaxKcg, kLdsBudget / (s.NB1 * kO
 
 // Steps the stage-2 LDS holds: all steps of the largest linear when they fit,
 // else a multiple of the batch (at least one batch, which may exceed 64 KB).
+// Whether stage 2 can run k_stage2r: every step's operands and h of an item
+// fit the LDS of one CU (two workgroups' worth when possible).
+bool dma2_for(const Shape &s, int steps_max) {
+    return (size_t)steps_max * s.NB2 * kOpS + 2 * kHRows * 2 <= 80 * 1024;
+}
+
 int ops2_for(const Shape &s, int steps_max) {
     int cap = kLdsBudget / (s.NB2 * kOpS);
     if (cap < kBatch) cap = kBatch;
@@ -780,7 +913,19 @@ int launch_all(const MRun &run, const MLin &single, const Lds &lds, hipStream_t 
         k_latent<NL, NB2><<<(unsigned)run.itemsF, kThreads, lds.lat, st>>>(run, single);
         if (int rc = last_launch_status()) return rc;
     }
-    if (stage_mask & 2) {
+    if ((stage_mask & 2) && run.dma2) {
+        const size_t l2 = (size_t)run.ops2 * NB2 * kOpS + 2 * kHRows * 2;
+        if (l2 > 160 * 1024) return LB_EUNSUPPORTED;
+        static bool raised = false;        // once per instantiation (idempotent if raced)
+        if (!raised) {
+            if (hipFuncSetAttribute((const void *)k_stage2r<NL, NB2>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    160 * 1024) != hipSuccess)
+                return hip_status(hipGetLastError());
+            raised = true;
+        }
+        k_stage2r<NL, NB2><<<(unsigned)run.items2, kThreads, l2, st>>>(run, single);
+        if (int rc = last_launch_status()) return rc;
+    } else if (stage_mask & 2) {
         const size_t l2 = lds.s2;
         if (run.ops2 < 1 || l2 > 160 * 1024) return LB_EUNSUPPORTED;
         if (l2 > 64 * 1024) {
@@ -857,7 +1002,8 @@ int mfma_decode_forward(const Linear &a, void *ws, hipStream_t st) {
     run.T = (int)a.T;
     run.x_dtype = a.x_dtype;
     run.y_dtype = a.y_dtype;
-    run.ops2 = ops2_for(s, m.kgs);
+    run.dma2 = dma2_for(s, m.kgs);
+    run.ops2 = run.dma2 ? m.kgs : ops2_for(s, m.kgs);
     run.items0 = items0_of(m);
     run.items1 = items1_of(m);
     run.itemsF = itemsF_of(m);
@@ -923,7 +1069,8 @@ int mfma_group_prepare(const Linear *ls, int n, int64_t T, int y_dtype, void *ws
     }
     MRun &run = hs->run;
     run = MRun{};
-    run.ops2 = ops2_for(hs->s, steps_max);
+    run.dma2 = dma2_for(hs->s, steps_max);
+    run.ops2 = run.dma2 ? steps_max : ops2_for(hs->s, steps_max);
     hs->lds = Lds{};
     for (int j = 0; j < n; ++j) lds_add(&hs->lds, tab[(size_t)j], hs->s, run.ops2);
     int32_t *lin0 = (int32_t *)cur;
