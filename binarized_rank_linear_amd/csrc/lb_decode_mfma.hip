@@ -301,13 +301,15 @@ __device__ __forceinline__ void expand_ops(uint8_t *dst, const uint8_t *src, int
         expand_vec(dst, i, R, ((const v4u *)src)[i]);
 }
 
+// Buffer loads (not flat ones: the compiler cannot count flat loads among the
+// vector-memory operations in flight and would wait for all of them), issued
+// unconditionally; vectors past the end read as zeros.
 __device__ __forceinline__ void preload_ops(const uint8_t *src, int nops, int R, v4u (&pre)[kPreVec]) {
     const int vecs = nops * R * kRec / 16;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(src, (int64_t)vecs * 16);
 #pragma unroll
-    for (int j = 0; j < kPreVec; ++j) {
-        const int i = j * kThreads + (int)threadIdx.x;
-        pre[j] = i < vecs ? ((const v4u *)src)[i] : v4u{0u, 0u, 0u, 0u};
-    }
+    for (int j = 0; j < kPreVec; ++j)
+        pre[j] = __builtin_amdgcn_raw_buffer_load_b128(r, (j * kThreads + (int)threadIdx.x) * 16, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -341,14 +343,36 @@ __global__ __launch_bounds__(kThreads) void k_prep(MRun run, MLin single) {
         const int c0 = (n % R::TPM1) * R::S1;
         uint8_t *opn = smem + (n / R::TPM1) * opb + c0 * kRec;
         for (int b0 = 2 * wave; b0 < blocks; b0 += 8 * kPre) {
+            // all loads first, from clamped (always valid) indices; the
+            // products of elements past the chunk or past d_in are masked after
             float v[kPre];
+            uint16_t gv[kPre];
+            float xv[kPre];
+            if (run.x_dtype == LB_BF16) {                        // uniform: one branch for all loads
+                const uint16_t *xp = (const uint16_t *)L.x + (int64_t)n * L.d_in;
+                uint16_t xb[kPre];
+#pragma unroll
+                for (int j = 0; j < kPre; ++j) {
+                    const int64_t i = imin(i0 + (b0 + 8 * j + h) * 32 + el, L.d_in - 1);
+                    gv[j] = gp[i];
+                    xb[j] = xp[i];
+                }
+#pragma unroll
+                for (int j = 0; j < kPre; ++j) xv[j] = bf16_to_f32(xb[j]);
+            } else {
+                const float *xp = (const float *)L.x + (int64_t)n * L.d_in;
+#pragma unroll
+                for (int j = 0; j < kPre; ++j) {
+                    const int64_t i = imin(i0 + (b0 + 8 * j + h) * 32 + el, L.d_in - 1);
+                    gv[j] = gp[i];
+                    xv[j] = xp[i];
+                }
+            }
 #pragma unroll
             for (int j = 0; j < kPre; ++j) {
                 const int blk = b0 + 8 * j + h;
                 const int64_t i = i0 + blk * 32 + el;
-                v[j] = (blk < blocks && i < L.d_in)
-                           ? f16_to_f32(gp[i]) * load_act(L.x, run.x_dtype, (int64_t)n * L.d_in + i)
-                           : 0.0f;
+                v[j] = (blk < blocks && i < L.d_in) ? f16_to_f32(gv[j]) * xv[j] : 0.0f;
             }
 #pragma unroll
             for (int j = 0; j < kPre; ++j) {
@@ -699,6 +723,23 @@ __global__ __launch_bounds__(kThreads) void k_stage2r(MRun run, MLin single) {
     uint8_t *ops = smem;                                          // [steps][NB2] operands
     uint16_t *hs = (uint16_t *)(smem + run.ops2 * NB2 * kOpS);   // [2][kHRows] fp16 h
 
+    // operands and h first, as buffer loads (counted precisely, so the LDS
+    // fill below waits for these only, not for the plane loads behind them)
+    v4u pre[kPreVec];
+    preload_ops(L.tb, steps * NB2, L.R2, pre);
+    // h of the item's rows: thread t holds 8 consecutive fp16 of path t / (kThreads/2)
+    const int hp = (int)threadIdx.x / (kThreads / 2), hr = ((int)threadIdx.x % (kThreads / 2)) * 8;
+    const __amdgpu_buffer_rsrc_t rh = make_rsrc(L.h, (int64_t)L.P * L.d_out * 2);
+    // 16-byte pieces when every row group of 8 starts 16-byte aligned and none straddles d_out
+    const bool hvec = (L.d_out & 7) == 0 && ((uintptr_t)L.h & 15) == 0;
+    v4u hq[kHRows / (kThreads / 2) / 8];
+#pragma unroll
+    for (int k = 0; k < kHRows / (kThreads / 2) / 8; ++k) {
+        const int64_t row = row_begin + hr + k * (kThreads / 2) * 8;
+        const bool ok = hvec && hp < L.P && row + 8 <= L.d_out;
+        hq[k] = __builtin_amdgcn_raw_buffer_load_b128(rh, ok ? (uint32_t)(((int64_t)hp * L.d_out + row) * 2) : kOOB, 0, 0);
+    }
+
     // lane (gq, r16) loads rows row+4r16 .. +3 of plane 4s + gq of tile i
     const __amdgpu_buffer_rsrc_t ru = make_rsrc(L.u_bits, (int64_t)L.P * L.kw_u * L.ld_u * 4);
     const uint32_t uo = (uint32_t)(((int64_t)gq * L.ld_u + row_begin + wave * kTile + 4 * r16) * 4);
@@ -711,17 +752,19 @@ __global__ __launch_bounds__(kThreads) void k_stage2r(MRun run, MLin single) {
 #pragma unroll
     for (int k = 0; k < kWin2; ++k) slot[k] = load_rows(ru, off_of(k));
 
-    // operands of every step and h of the item's rows, shared by the 4 waves
-    {
-        const int vecs = steps * NB2 * opb / 16;
-        for (int i = threadIdx.x; i < vecs; i += kThreads)
-            expand_vec(ops, i, L.R2, ((const v4u *)L.tb)[i]);
-        const int hn = 2 * L.rows2;
-        for (int i = threadIdx.x; i < hn; i += kThreads) {
-            const int pp = i >= L.rows2 ? 1 : 0;
-            const int64_t row = row_begin + (i - pp * L.rows2);
-            hs[pp * kHRows + (i - pp * L.rows2)] =
-                (pp < L.P && row < L.d_out) ? L.h[(int64_t)pp * L.d_out + row] : (uint16_t)0;
+    // operands of every step and h of the item's rows into LDS, shared by the 4 waves
+    expand_ops(ops, L.tb, steps * NB2, L.R2, pre);
+#pragma unroll
+    for (int k = 0; k < kHRows / (kThreads / 2) / 8; ++k) {
+        const int rl = hr + k * (kThreads / 2) * 8;
+        *(v4u *)(hs + hp * kHRows + rl) = hq[k];
+    }
+    if (!hvec) {                  // rows the 16-byte loads did not cover: one by one
+        __syncthreads();
+        for (int i = threadIdx.x; i < 2 * kHRows; i += kThreads) {
+            const int pp = i / kHRows, rl = i - pp * kHRows;
+            const int64_t row = row_begin + rl;
+            hs[i] = (pp < L.P && row < L.d_out) ? L.h[(int64_t)pp * L.d_out + row] : (uint16_t)0;
         }
     }
     __syncthreads();
