@@ -65,6 +65,8 @@ constexpr int kBatch = 8;                 // stage-2 steps per load batch
 constexpr int kTilesPerItem2 = 8;         // 64-row tiles per wave in one stage-2 item
 constexpr int kPreVec = 8;                // operand vectors a thread loads before the plane loads
 constexpr int kWin2 = 8;                  // stage 2 (streaming form): plane loads in flight per wave
+constexpr int kWin1 = 8;                  // stage 1 (fused form): plane loads in flight per wave
+constexpr int kMaxKcf = 32;               // K-groups per fused stage-1 chunk (two 8-input pieces per thread)
 constexpr uint32_t kOOB = 0x7ffffff0u;    // a buffer offset past every range: reads as zero
 constexpr int kHRows = kRG * kTilesPerItem2;   // output rows of one stage-2 item, at most
 
@@ -90,19 +92,19 @@ struct MLin {
     int32_t r_p, P;
     int32_t kw_v, kw_u;   // planes of V (per path) and of U (per path)
     int32_t kgv;          // K-groups of V per path
-    int32_t kcg;          // K-groups (128 inputs) per stage-1 chunk, <= kMaxKcg
+    int32_t kcg;          // K-groups (128 inputs) per stage-1 chunk, <= kMaxKcg (fused: <= kMaxKcf)
     int32_t nchunks;      // stage-1 chunks along d_in
     int32_t kcp;          // K-groups per prep item
     int32_t nprep;        // prep items per path
-    int32_t nrg;          // 256-latent groups per path
+    int32_t nrg;          // 256-latent groups per path (unfused stage 1)
     int32_t kgs;          // stage-2 K-groups over the planes of all paths (path-major)
     int32_t rows2;        // output rows per stage-2 item
     int32_t n2;           // stage-2 items
     int32_t R1, R2;       // activation rows in use (compact records per operand)
-    int32_t pad_;
+    int32_t xvec;         // fused stage 1: x and g read as 16-byte pieces (d_in % 8 == 0, aligned)
     int64_t item0, item1, itemF, item2;   // first item of this linear in each launch
     float *part;          // [nchunks][T][P*r_p]
-    uint8_t *pa;          // stage-1 operands, compact: [P][kgv][NB1][R1][kRec]
+    uint8_t *pa;          // stage-1 operands, compact: [P][kgv][NB1][R1][kRec] (unused by the fused form)
     uint8_t *tb;          // stage-2 operands, compact: [kgs][NB2][R2][kRec]
 };
 
@@ -224,6 +226,15 @@ __device__ __forceinline__ v8i load_op(const uint8_t *op) {
     v8i b;
     b[0] = lo.x; b[1] = lo.y; b[2] = lo.z; b[3] = lo.w;
     b[4] = hi.x; b[5] = hi.y; b[6] = hi.z; b[7] = hi.w;
+    return b;
+}
+
+// 32 bytes at p (16-byte aligned) as an fp8 operand
+__device__ __forceinline__ v8i load_op_at(const uint8_t *p) {
+    const v4u lo = *(const v4u *)p, hi = *(const v4u *)(p + 16);
+    v8i b;
+    b[0] = (int)lo[0]; b[1] = (int)lo[1]; b[2] = (int)lo[2]; b[3] = (int)lo[3];
+    b[4] = (int)hi[0]; b[5] = (int)hi[1]; b[6] = (int)hi[2]; b[7] = (int)hi[3];
     return b;
 }
 
@@ -483,6 +494,261 @@ __global__ __launch_bounds__(kThreads) void k_stage1(MRun run, MLin single) {
                        L.r_p, u);
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// stage 1, fused form: all tokens in one activation-row block (T <= TPM1)
+// ---------------------------------------------------------------------------
+
+// LDS writes of this wave done, then every wave of the workgroup meets; loads
+// in flight stay in flight (no vmcnt wait, unlike __syncthreads).
+__device__ __forceinline__ void lds_meet() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));   // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// max over the four lanes of a quad (DPP quad permutations xor 1, xor 2)
+__device__ __forceinline__ float quad_max(float m) {
+    m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0xB1, 0xF, 0xF, false)));
+    m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x4E, 0xF, 0xF, false)));
+    return m;
+}
+
+// fp32 products g (.) x of 8 consecutive inputs from their 16-byte pieces
+__device__ __forceinline__ void gx8_bf16(const v4u &g, const v4u &x, float (&v)[8]) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const uint32_t gw = g[t >> 1], xw = x[t >> 1];
+        const float gf = f16_to_f32((uint16_t)((t & 1) ? gw >> 16 : gw & 0xffffu));
+        v[t] = gf * __uint_as_float((t & 1) ? xw & 0xffff0000u : xw << 16);
+    }
+}
+__device__ __forceinline__ void gx8_f32(const v4u &g, const v4u &x0, const v4u &x1, float (&v)[8]) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const uint32_t gw = g[t >> 1];
+        const float gf = f16_to_f32((uint16_t)((t & 1) ? gw >> 16 : gw & 0xffffu));
+        v[t] = gf * __uint_as_float(t < 4 ? x0[t] : x1[t - 4]);
+    }
+}
+
+// The NL limbs of one 8-input piece into compact records (same arithmetic as
+// emit_limbs; the 32-input block is the lane's quad).  Piece a (0..3) of block
+// gb (0..3) of a K-group: inputs t and t + 4 land in adjacent record bytes, at
+// 64(gb&1) + 16(gb>>1) + 2a + {0, 8, 32, 40}[t] (rec_offset for 8a+t, 8a+t+4).
+// rec0 points at the record of limb 0; limb q is q*kRec further.
+template <int NL>
+__device__ __forceinline__ void emit_piece(const float (&v)[8], uint8_t *rec0, int gb, int a, bool ok) {
+    float m = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) m = fmaxf(m, fabsf(v[t]));
+    m = quad_max(m);
+    const int E = (int)((__float_as_uint(m) >> 23) & 0xff) - 127;
+    float r[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) r[t] = v[t];
+    const int base = ((gb & 1) << 6) + ((gb >> 1) << 4) + 2 * a;
+#pragma unroll
+    for (int q = 0; q < NL; ++q) {
+        const int eq = E - 7 - 4 * q;
+        uint8_t *d = rec0 + q * kRec;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint32_t b = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ldexp2(r[t], -eq), ldexp2(r[t + 4], -eq), 0, false);
+            if (ok) *(uint16_t *)(d + base + ((t >> 1) << 5) + ((t & 1) << 3)) = (uint16_t)b;
+            if (q + 1 < NL) {
+                r[t] -= ldexp2(__builtin_amdgcn_cvt_f32_fp8((int)b, 0), eq);
+                r[t + 4] -= ldexp2(__builtin_amdgcn_cvt_f32_fp8((int)b, 1), eq);
+            }
+        }
+        if (ok && a == 0) d[128 + gb] = (uint8_t)(eq < -127 ? 0 : (eq > 127 ? 254 : eq + 127));
+    }
+}
+
+// Item = (linear, path, chunk of up to kMaxKcf K-groups of d_in).  The
+// workgroup turns g_p (.) x over its chunk into compact limb records in LDS
+// (loads of g and of token 0 go out before the first plane loads, so only
+// their own latency is waited for), then wave w streams K-groups
+// [w*sub, (w+1)*sub) of the chunk across every 64-latent tile with kWin1
+// plane loads in flight (rotating register slots, as k_stage2r).  At each tile
+// end the four waves' partial sums meet in LDS and are added in wave order:
+// one partial per (chunk, token, latent), in a fixed summation order.
+template <int NL>
+__global__ __launch_bounds__(kThreads) void k_stage1f(MRun run, MLin single) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    using R = Rows<NL>;
+    const MLin L = pick(run, single, run.lin1);
+    const int64_t local = (int64_t)blockIdx.x - L.item1;
+    const int c = (int)(local % L.nchunks);
+    const int p = (int)(local / L.nchunks);
+    const int T = run.T;
+    const int tid = (int)threadIdx.x;
+    const int lane = tid & 63, wave = wave_id();
+    const int r16 = lane & 15, gq = lane >> 4;
+    const Nib nib = nibble_constants();
+    const int kg0 = c * L.kcg;
+    const int nkg = (int)imin(L.kcg, L.kgv - kg0);
+    const int R1 = L.R1;
+    uint8_t *recs = smem;                                               // [nkg][R1] records
+    float *red = (float *)(smem + (size_t)L.kcg * R1 * kRec);          // [2][kWaves][T][64]
+
+    // ---- g and token-0 x of this thread's pieces (8 inputs each) -------------
+    constexpr int kPPT = kMaxKcf * 16 / kThreads;                      // pieces per thread
+    const int npc = nkg * 16;
+    const int64_t i_chunk = (int64_t)kg0 * 128;
+    const bool xf32 = run.x_dtype == LB_F32;
+    const int xb = xf32 ? 4 : 2;
+    const bool vec = L.xvec != 0;
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(L.g + (int64_t)p * L.d_in, L.d_in * 2);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(L.x, (int64_t)T * L.d_in * xb);
+    v4u gr[kPPT], xr[kPPT][2];
+#pragma unroll
+    for (int j = 0; j < kPPT; ++j) {
+        const int pc = tid + j * kThreads;
+        const int64_t i = i_chunk + (int64_t)pc * 8;
+        const bool ok = vec && pc < npc && i < L.d_in;
+        gr[j] = __builtin_amdgcn_raw_buffer_load_b128(rg, ok ? (uint32_t)(i * 2) : kOOB, 0, 0);
+        xr[j][0] = __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? (uint32_t)(i * xb) : kOOB, 0, 0);
+        xr[j][1] = __builtin_amdgcn_raw_buffer_load_b128(rx, ok && xf32 ? (uint32_t)(i * 4 + 16) : kOOB, 0, 0);
+    }
+
+    // ---- first plane loads ----------------------------------------------------
+    const int sub = (L.kcg + kWaves - 1) / kWaves;
+    const int ka = wave * sub;                                         // chunk-local K-group
+    const int nk = (int)imax(0, imin(sub, nkg - ka));
+    const int ntile = (int)cdiv(L.r_p, kTile);
+    const int total = ntile * nk;
+    const __amdgpu_buffer_rsrc_t rv =
+        make_rsrc(L.v_bits + (int64_t)p * L.kw_v * L.ld_v, (int64_t)L.kw_v * L.ld_v * 4);
+    const uint32_t vo = (uint32_t)(((int64_t)((kg0 + ka) * 4 + gq) * L.ld_v + 4 * r16) * 4);
+    const uint32_t group4 = (uint32_t)(4 * L.ld_v * 4);
+    // next (tile, K-group) to load; selects only, so every load is issued
+    // on every path and the compiler can count them
+    const int ltiles = nk > 0 ? ntile : 0;
+    int lt = 0, lk = 0;
+    auto next_off = [&]() -> uint32_t {
+        const bool live = lt < ltiles && lt * kTile + 4 * r16 < L.r_p;
+        const uint32_t o = live ? vo + (uint32_t)(lt * kTile * 4) + (uint32_t)lk * group4 : kOOB;
+        const bool wrap = lk + 1 == nk;
+        lt = wrap ? lt + 1 : lt;
+        lk = wrap ? 0 : lk + 1;
+        return o;
+    };
+    v4u slot[kWin1];
+#pragma unroll
+    for (int k = 0; k < kWin1; ++k) slot[k] = load_rows(rv, next_off());
+
+    // ---- limbs of g (.) x into the records ------------------------------------
+    // piece pc: K-group pc/16 of the chunk, block (pc/4)%4, quarter pc%4; a
+    // quad of lanes holds one 32-input block
+    auto rec_of = [&](int pc, int n) { return recs + ((size_t)(pc >> 4) * R1 + n * R::S1) * kRec; };
+    if (vec) {
+#pragma unroll
+        for (int j = 0; j < kPPT; ++j) {                        // token 0 from the preloads
+            const int pc = tid + j * kThreads;
+            float v[8];
+            if (xf32) gx8_f32(gr[j], xr[j][0], xr[j][1], v);
+            else gx8_bf16(gr[j], xr[j][0], v);
+            emit_piece<NL>(v, rec_of(pc, 0), (pc >> 2) & 3, pc & 3, pc < npc);
+        }
+        for (int n = 1; n < T; ++n) {
+#pragma unroll
+            for (int j = 0; j < kPPT; ++j) {
+                const int pc = tid + j * kThreads;
+                const int64_t i = i_chunk + (int64_t)pc * 8;
+                const bool in = pc < npc && i < L.d_in;
+                const int64_t xo = ((int64_t)n * L.d_in + i) * xb;
+                const v4u x0 = __builtin_amdgcn_raw_buffer_load_b128(rx, in ? (uint32_t)xo : kOOB, 0, 0);
+                const v4u x1 = __builtin_amdgcn_raw_buffer_load_b128(rx, in && xf32 ? (uint32_t)(xo + 16) : kOOB, 0, 0);
+                float v[8];
+                if (xf32) gx8_f32(gr[j], x0, x1, v);
+                else gx8_bf16(gr[j], x0, v);
+                emit_piece<NL>(v, rec_of(pc, n), (pc >> 2) & 3, pc & 3, pc < npc);
+            }
+        }
+    } else {                                                    // ragged or unaligned: input by input
+        for (int n = 0; n < T; ++n) {
+#pragma unroll
+            for (int j = 0; j < kPPT; ++j) {
+                const int pc = tid + j * kThreads;
+                const int64_t i = i_chunk + (int64_t)pc * 8;
+                float v[8];
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const bool in = pc < npc && i + t < L.d_in;
+                    const uint32_t go = in ? (uint32_t)((i + t) * 2) : kOOB;
+                    const uint32_t xo = in ? (uint32_t)(((int64_t)n * L.d_in + i + t) * xb) : kOOB;
+                    const float gf = f16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rg, go, 0, 0));
+                    const float xf = xf32 ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rx, xo, 0, 0))
+                                          : bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rx, xo, 0, 0));
+                    v[t] = gf * xf;
+                }
+                emit_piece<NL>(v, rec_of(pc, n), (pc >> 2) & 3, pc & 3, pc < npc);
+            }
+        }
+    }
+    lds_meet();
+
+    // ---- stream ------------------------------------------------------------
+    v4f acc[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[m] = v4f{0.f, 0.f, 0.f, 0.f};
+    const int rr = r16 < R1 ? r16 : R1 - 1;       // rows past R1 repeat the last one (never read out)
+    const int64_t Rtot = (int64_t)L.P * L.r_p;
+    // partial sums through a buffer descriptor: a flat store would be counted
+    // with the LDS operations too, and every later wait would become a full one
+    const __amdgpu_buffer_rsrc_t rpart = make_rsrc(L.part, (int64_t)L.nchunks * T * Rtot * 4);
+    // tile t done: this wave's partials to LDS, meet, the fixed-order sum to part
+    auto tile_end = [&](int t) {
+        float *mine = red + ((t & 1) * kWaves + wave) * T * 64;
+#pragma unroll
+        for (int s = 0; s < 4 / R::S1; ++s) {
+            const int n = gq * (4 / R::S1) + s;
+            v4f u;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                float sum = 0.0f;
+#pragma unroll
+                for (int q = 0; q < NL; ++q) sum += acc[m][s * R::S1 + q];
+                u[m] = sum;
+            }
+            if (n < T) *(v4f *)(mine + n * 64 + 4 * r16) = u;
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) acc[m] = v4f{0.f, 0.f, 0.f, 0.f};
+        lds_meet();
+        const float *both = red + (t & 1) * kWaves * T * 64;
+        for (int f = tid; f < T * 64; f += kThreads) {
+            const float s = ((both[f] + both[T * 64 + f]) + both[2 * T * 64 + f]) + both[3 * T * 64 + f];
+            const int n = f >> 6, row = t * kTile + (f & 63);
+            const uint32_t po = (uint32_t)((((int64_t)c * T + n) * Rtot + (int64_t)p * L.r_p + row) * 4);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s), rpart, row < L.r_p ? po : kOOB, 0, 0);
+        }
+    };
+    int pk = 0, pt = 0;
+    auto process = [&](const v4u &w) {
+        const uint8_t *rec = recs + ((size_t)(ka + pk) * R1 + rr) * kRec;
+        const v8i ao = load_op_at(rec + gq * 32);
+        const int sa = rec[128 + gq];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) acc[m] = mfma(ao, unpack_word(w[m], nib), acc[m], sa);
+        if (++pk == nk) {
+            tile_end(pt);
+            pk = 0;
+            ++pt;
+        }
+    };
+    for (int e0 = 0; e0 < total; e0 += kWin1) {
+#pragma unroll
+        for (int k = 0; k < kWin1; ++k) {
+            if (e0 + k < total) process(slot[k]);                 // uniform
+            slot[k] = load_rows(rv, next_off());
+        }
+    }
+    if (nk == 0)
+        for (int t = 0; t < ntile; ++t) tile_end(t);
 }
 
 // ---------------------------------------------------------------------------
@@ -868,6 +1134,12 @@ int rows1(const Shape &s, int64_t T) { return (int)imin(16, T * (s.NL == 2 ? 2 :
 int rows2(const Shape &s, int64_t T) { return (int)imin(16, T * (s.NL == 2 ? 4 : 8)); }
 int kcg_cap(const Shape &s) { return (int)imin(kMaxKcg, kLdsBudget / (s.NB1 * kOpS)); }
 
+// Stage 1 runs fused (k_stage1f) when the tokens fill one activation-row block.
+bool fused1(const Shape &s) { return s.NB1 == 1; }
+constexpr int64_t kFusedBytes = 96 * 1024;     // V-plane bytes per fused stage-1 item, about
+// LDS of the fused form's cross-wave reduction: [2][kWaves][T][64] floats
+size_t red1_bytes(int64_t T) { return (size_t)2 * kWaves * T * 64 * 4; }
+
 // Steps the stage-2 LDS holds: all steps of the largest linear when they fit,
 // else a multiple of the batch (at least one batch, which may exceed 64 KB).
 // Whether stage 2 can run k_stage2r: every step's operands and h of an item
@@ -904,18 +1176,35 @@ size_t plan_linear(const Linear &a, const Shape &s, bool many, MLin *m) {
     m->nrg = (int32_t)cdiv(a.r_p, kRG);
     m->R1 = rows1(s, a.T);
     m->R2 = rows2(s, a.T);
-    int kcg = kcg_cap(s);
-    if (!many)   // a lone linear: smaller chunks until the chip has work
-        while (kcg > 1 && a.P * m->nrg * cdiv(m->kgv, kcg) < 512) kcg = (kcg + 1) / 2;
-    if (kcg > m->kgv) kcg = m->kgv;
-    m->kcg = kcg;
-    m->nchunks = (int32_t)cdiv(m->kgv, kcg);
-    // prep items: up to 16 K-groups, LDS-bounded
-    int kcp = (int)imin(16, kLdsBudget / (s.NB1 * m->R1 * kRec));
-    if (kcp < 1) kcp = 1;
-    if (kcp > m->kgv) kcp = m->kgv;
-    m->kcp = kcp;
-    m->nprep = (int32_t)cdiv(m->kgv, kcp);
+    if (fused1(s)) {
+        // chunks of about kFusedBytes of V planes (all latents of the path),
+        // LDS-bounded, spread evenly over d_in
+        const int64_t per_kg = (int64_t)a.r_p * 16;
+        int64_t kc = imax(1, imin(kMaxKcf, kFusedBytes / per_kg));
+        kc = imin(kc, (int64_t)((kLdsBudget - red1_bytes(a.T)) / (m->R1 * kRec)));
+        if (!many)   // a lone linear: smaller chunks until the chip has work
+            while (kc > 4 && a.P * cdiv(m->kgv, kc) < 256) kc = (kc + 1) / 2;
+        const int64_t nch = cdiv(m->kgv, kc);
+        m->kcg = (int32_t)cdiv(m->kgv, nch);
+        m->nchunks = (int32_t)cdiv(m->kgv, m->kcg);
+        m->nrg = 1;
+        m->kcp = 0;
+        m->nprep = 0;
+        m->xvec = (a.d_in % 8 == 0 && ((uintptr_t)a.x & 15) == 0 && ((uintptr_t)a.g & 15) == 0) ? 1 : 0;
+    } else {
+        int kcg = kcg_cap(s);
+        if (!many)   // a lone linear: smaller chunks until the chip has work
+            while (kcg > 1 && a.P * m->nrg * cdiv(m->kgv, kcg) < 512) kcg = (kcg + 1) / 2;
+        if (kcg > m->kgv) kcg = m->kgv;
+        m->kcg = kcg;
+        m->nchunks = (int32_t)cdiv(m->kgv, kcg);
+        // prep items: up to 16 K-groups, LDS-bounded
+        int kcp = (int)imin(16, kLdsBudget / (s.NB1 * m->R1 * kRec));
+        if (kcp < 1) kcp = 1;
+        if (kcp > m->kgv) kcp = m->kgv;
+        m->kcp = kcp;
+        m->nprep = (int32_t)cdiv(m->kgv, kcp);
+    }
     m->kgs = (int32_t)cdiv((int64_t)a.P * m->kw_u, 4);
     int tiles = kTilesPerItem2;
     if (!many)   // a lone linear: fewer tiles per item until the chip has work
@@ -923,16 +1212,16 @@ size_t plan_linear(const Linear &a, const Shape &s, bool many, MLin *m) {
     m->rows2 = kRG * tiles;
     m->n2 = (int32_t)cdiv(a.d_out, m->rows2);
     const size_t part = rup256((size_t)m->nchunks * a.T * a.P * a.r_p * 4);
-    const size_t pa = rup256((size_t)a.P * m->kgv * s.NB1 * m->R1 * kRec);
+    const size_t pa = fused1(s) ? 0 : rup256((size_t)a.P * m->kgv * s.NB1 * m->R1 * kRec);
     const size_t tb = rup256((size_t)m->kgs * s.NB2 * m->R2 * kRec);
     return part + pa + tb;
 }
 
 void bind_ws(MLin *m, const Linear &a, const Shape &s, uint8_t *ws) {
     const size_t part = rup256((size_t)m->nchunks * a.T * a.P * a.r_p * 4);
-    const size_t pa = rup256((size_t)a.P * m->kgv * s.NB1 * m->R1 * kRec);
+    const size_t pa = fused1(s) ? 0 : rup256((size_t)a.P * m->kgv * s.NB1 * m->R1 * kRec);
     m->part = (float *)ws;
-    m->pa = ws + part;
+    m->pa = fused1(s) ? nullptr : ws + part;
     m->tb = ws + part + pa;
 }
 
@@ -948,11 +1237,16 @@ struct Lds {
 // stage_mask: bit 0 = prep, stage 1 and the latent pass; bit 1 = stage 2.
 template <int NL, int NB1, int NB2>
 int launch_all(const MRun &run, const MLin &single, const Lds &lds, hipStream_t st, int stage_mask) {
-    if (stage_mask & 1) {
+    if ((stage_mask & 1) && NB1 == 1) {
+        k_stage1f<NL><<<(unsigned)run.items1, kThreads, lds.s1, st>>>(run, single);
+        if (int rc = last_launch_status()) return rc;
+    } else if (stage_mask & 1) {
         k_prep<NL, NB1><<<(unsigned)run.items0, kThreads, lds.prep, st>>>(run, single);
         if (int rc = last_launch_status()) return rc;
         k_stage1<NL, NB1><<<(unsigned)run.items1, kThreads, lds.s1, st>>>(run, single);
         if (int rc = last_launch_status()) return rc;
+    }
+    if (stage_mask & 1) {
         k_latent<NL, NB2><<<(unsigned)run.itemsF, kThreads, lds.lat, st>>>(run, single);
         if (int rc = last_launch_status()) return rc;
     }
@@ -1004,9 +1298,9 @@ int launch_shape(const Shape &s, const MRun &run, const MLin &single, const Lds 
     return LB_EUNSUPPORTED;
 }
 
-void lds_add(Lds *l, const MLin &m, const Shape &s, int ops2) {
+void lds_add(Lds *l, const MLin &m, const Shape &s, int ops2, int64_t T) {
     const size_t prep = (size_t)m.kcp * s.NB1 * m.R1 * kRec;
-    const size_t s1 = (size_t)m.kcg * s.NB1 * kOpS;
+    const size_t s1 = fused1(s) ? (size_t)m.kcg * m.R1 * kRec + red1_bytes(T) : (size_t)m.kcg * s.NB1 * kOpS;
     const size_t lat = (size_t)2 * s.NB2 * m.R2 * kRec;
     const size_t s2 = (size_t)ops2 * s.NB2 * kOpS;
     if (prep > l->prep) l->prep = prep;
@@ -1053,7 +1347,7 @@ int mfma_decode_forward(const Linear &a, void *ws, hipStream_t st) {
     run.items2 = m.n2;
     run.table = nullptr;
     Lds lds{};
-    lds_add(&lds, m, s, run.ops2);
+    lds_add(&lds, m, s, run.ops2, a.T);
     return launch_shape(s, run, m, lds, st);
 }
 
@@ -1115,7 +1409,7 @@ int mfma_group_prepare(const Linear *ls, int n, int64_t T, int y_dtype, void *ws
     run.dma2 = dma2_for(hs->s, steps_max);
     run.ops2 = run.dma2 ? steps_max : ops2_for(hs->s, steps_max);
     hs->lds = Lds{};
-    for (int j = 0; j < n; ++j) lds_add(&hs->lds, tab[(size_t)j], hs->s, run.ops2);
+    for (int j = 0; j < n; ++j) lds_add(&hs->lds, tab[(size_t)j], hs->s, run.ops2, T);
     int32_t *lin0 = (int32_t *)cur;
     int32_t *lin1 = (int32_t *)((uint8_t *)lin0 + rup256((size_t)i0 * 4));
     int32_t *linF = (int32_t *)((uint8_t *)lin1 + rup256((size_t)i1 * 4));
