@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
         L.lb_rank_for_budget.restype = ctypes.c_int
         L.lb_packed_ld.argtypes = [_i64]
         L.lb_packed_ld.restype = _i64
+        L.lb_packed_ld_aligned.argtypes = [_i64]
+        L.lb_packed_ld_aligned.restype = _i64
         L.lb_packed_words.argtypes = [_i64, _i64, ctypes.c_int, _i64]
         L.lb_packed_words.restype = _i64
         L.lb_pack_signs.argtypes = [_vp, _i64, _i64, ctypes.c_int, _vp, _i64, _vp]
@@ -131,6 +133,10 @@ def rank_for_budget(d_in: int, d_out: int, b_num: int, b_den: int, residual: boo
 
 def packed_ld(n_other: int) -> int:
     return lib().lb_packed_ld(n_other)
+
+
+def packed_ld_aligned(n_other: int) -> int:
+    return lib().lb_packed_ld_aligned(n_other)
 
 
 def packed_words(rows: int, cols: int, axis: int, ld: int) -> int:
@@ -218,7 +224,7 @@ class PackedLinear:
         d_in = V.shape[1]
         if V.shape != (P, d_in, r_p):
             raise ValueError("U and V shapes disagree")
-        ld_v, ld_u = packed_ld(r_p), packed_ld(d_out)
+        ld_v, ld_u = packed_ld_aligned(r_p), packed_ld_aligned(d_out)
         kw_v, kw_u = (d_in + 31) // 32, (r_p + 31) // 32
         v_bits = torch.empty((P, kw_v, ld_v), dtype=torch.int32, device=U.device)
         u_bits = torch.empty((P, kw_u, ld_u), dtype=torch.int32, device=U.device)

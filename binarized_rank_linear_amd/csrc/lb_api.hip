@@ -159,6 +159,8 @@ int lb_rank_for_budget(int64_t d_in, int64_t d_out, int64_t b_num, int64_t b_den
 
 int64_t lb_packed_ld(int64_t n_other) { return n_other <= 0 ? 0 : rup(n_other, 4); }
 
+int64_t lb_packed_ld_aligned(int64_t n_other) { return n_other <= 0 ? 0 : rup(n_other, 32); }
+
 int64_t lb_packed_words(int64_t rows, int64_t cols, int axis, int64_t ld) {
     if (rows <= 0 || cols <= 0 || (axis != 0 && axis != 1)) return 0;
     const int64_t n_pack = axis == 0 ? rows : cols;

@@ -96,7 +96,7 @@ struct MLin {
     int32_t nchunks;      // stage-1 chunks along d_in
     int32_t kcp;          // K-groups per prep item
     int32_t nprep;        // prep items per path
-    int32_t nrg;          // 256-latent groups per path (unfused stage 1)
+    int32_t nrg;          // latent groups per path: 256 latents (unfused), F tiles (fused)
     int32_t kgs;          // stage-2 K-groups over the planes of all paths (path-major)
     int32_t rows2;        // output rows per stage-2 item
     int32_t n2;           // stage-2 items
@@ -112,7 +112,7 @@ struct MRun {
     int T, x_dtype, y_dtype;
     int ops2;                  // stage-2 operands (steps) the LDS holds at once
     int dma2;                  // stage 2 runs k_stage2r (all operands and h fit the LDS)
-    int pad_;
+    int flush1;                // fused stage 1: latent tiles per item (F)
     int64_t items0, items1, itemsF, items2;
     const MLin *table;         // null: the single linear passed by value
     const int32_t *lin0, *lin1, *linF, *lin2;   // item -> linear, per launch
@@ -271,30 +271,62 @@ __device__ __forceinline__ MLin pick(const MRun &run, const MLin &single, const 
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
-// Store 4 consecutive outputs y[e0 .. e0+4) (only those with row < d_out).
-__device__ __forceinline__ void store4(void *y, int dtype, int64_t e0, int64_t row, int64_t d_out,
-                                      const float (&v)[4]) {
-    if (row + 4 <= d_out) {
-        if (dtype == LB_BF16) {
-            uint16_t *p = (uint16_t *)y + e0;
-            if (((uintptr_t)p & 7) == 0) {
-                v2u w;
-                w[0] = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-                w[1] = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-                *(v2u *)p = w;
-                return;
-            }
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values as a bf16 pair (hardware conversion, round to nearest even).
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+
+// Outputs through a buffer descriptor.  A flat store is counted with the LDS
+// operations as well, and after one the compiler can only wait for every load
+// in flight; buffer stores keep the plane-load window counted precisely.
+struct OutBuf {
+    __amdgpu_buffer_rsrc_t r;
+    int dtype;
+    bool vec;       // rows come in whole, aligned groups of four: one vector store per lane
+};
+
+__device__ __forceinline__ OutBuf out_buf(void *y, int dtype, int64_t elems, int64_t d_out) {
+    OutBuf o;
+    const int eb = dtype == LB_BF16 ? 2 : 4;
+    o.r = make_rsrc(y, elems * eb);
+    o.dtype = dtype;
+    o.vec = (d_out & 3) == 0 && ((uintptr_t)y & 15) == 0;
+    return o;
+}
+
+// y[e0 .. e0+4) = v for the rows row .. row+3 that are < d_out (ok: this lane writes).
+__device__ __forceinline__ void store4(const OutBuf &o, int64_t e0, int64_t row, int64_t d_out,
+                                      const float (&v)[4], bool ok) {
+    if (o.dtype == LB_BF16) {
+        if (o.vec) {
+            v2u w;
+            w[0] = bf16_pair(v[0], v[1]);
+            w[1] = bf16_pair(v[2], v[3]);
+            __builtin_amdgcn_raw_buffer_store_b64(w, o.r, ok && row < d_out ? (uint32_t)(e0 * 2) : kOOB, 0, 0);
         } else {
-            float *p = (float *)y + e0;
-            if (((uintptr_t)p & 15) == 0) {
-                *(v4f *)p = v4f{v[0], v[1], v[2], v[3]};
-                return;
+#pragma unroll
+            for (int q = 0; q < 4; q += 2) {
+                const uint32_t w = bf16_pair(v[q], v[q + 1]);
+                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(w & 0xffffu), o.r,
+                                                      ok && row + q < d_out ? (uint32_t)((e0 + q) * 2) : kOOB, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(w >> 16), o.r,
+                                                      ok && row + q + 1 < d_out ? (uint32_t)((e0 + q + 1) * 2) : kOOB, 0, 0);
             }
         }
-    }
+    } else {
+        if (o.vec) {
+            const v4u w = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+            __builtin_amdgcn_raw_buffer_store_b128(w, o.r, ok && row < d_out ? (uint32_t)(e0 * 4) : kOOB, 0, 0);
+        } else {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-        if (row + q < d_out) store_act(y, dtype, e0 + q, v[q]);
+            for (int q = 0; q < 4; ++q)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[q]), o.r,
+                                                      ok && row + q < d_out ? (uint32_t)((e0 + q) * 4) : kOOB, 0, 0);
+        }
+    }
 }
 
 // Compact operands [nops][R records] of src -> LDS operands at dst.  The first
@@ -476,6 +508,7 @@ __global__ __launch_bounds__(kThreads) void k_stage1(MRun run, MLin single) {
 
     // ---- partial latent sums: lane (gq, r16) holds latents row0+4*r16+m -------
     const int64_t Rtot = (int64_t)L.P * L.r_p;
+    const OutBuf ob = out_buf(L.part, LB_F32, (int64_t)L.nchunks * T * Rtot, 4);
 #pragma unroll
     for (int b = 0; b < NB1; ++b) {
 #pragma unroll
@@ -489,9 +522,7 @@ __global__ __launch_bounds__(kThreads) void k_stage1(MRun run, MLin single) {
                 for (int q = 0; q < NL; ++q) sum += acc[m][b][s * R::S1 + q];
                 u[m] = sum;
             }
-            if (n < T && row < L.r_p)
-                store4(L.part, LB_F32, ((int64_t)c * T + n) * Rtot + (int64_t)p * L.r_p + row, row,
-                       L.r_p, u);
+            store4(ob, ((int64_t)c * T + n) * Rtot + (int64_t)p * L.r_p + row, row, L.r_p, u, n < T);
         }
     }
 }
@@ -582,7 +613,8 @@ __global__ __launch_bounds__(kThreads) void k_stage1f(MRun run, MLin single) {
     const MLin L = pick(run, single, run.lin1);
     const int64_t local = (int64_t)blockIdx.x - L.item1;
     const int c = (int)(local % L.nchunks);
-    const int p = (int)(local / L.nchunks);
+    const int rg = (int)((local / L.nchunks) % L.nrg);
+    const int p = (int)(local / ((int64_t)L.nchunks * L.nrg));
     const int T = run.T;
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63, wave = wave_id();
@@ -592,7 +624,7 @@ __global__ __launch_bounds__(kThreads) void k_stage1f(MRun run, MLin single) {
     const int nkg = (int)imin(L.kcg, L.kgv - kg0);
     const int R1 = L.R1;
     uint8_t *recs = smem;                                               // [nkg][R1] records
-    float *red = (float *)(smem + (size_t)L.kcg * R1 * kRec);          // [2][kWaves][T][64]
+    float *red = (float *)(smem + (size_t)L.kcg * R1 * kRec);          // [F][kWaves][T][64]
 
     // ---- g and token-0 x of this thread's pieces (8 inputs each) -------------
     constexpr int kPPT = kMaxKcf * 16 / kThreads;                      // pieces per thread
@@ -601,7 +633,7 @@ __global__ __launch_bounds__(kThreads) void k_stage1f(MRun run, MLin single) {
     const bool xf32 = run.x_dtype == LB_F32;
     const int xb = xf32 ? 4 : 2;
     const bool vec = L.xvec != 0;
-    const __amdgpu_buffer_rsrc_t rg = make_rsrc(L.g + (int64_t)p * L.d_in, L.d_in * 2);
+    const __amdgpu_buffer_rsrc_t rgs = make_rsrc(L.g + (int64_t)p * L.d_in, L.d_in * 2);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(L.x, (int64_t)T * L.d_in * xb);
     v4u gr[kPPT], xr[kPPT][2];
 #pragma unroll
@@ -609,7 +641,7 @@ __global__ __launch_bounds__(kThreads) void k_stage1f(MRun run, MLin single) {
         const int pc = tid + j * kThreads;
         const int64_t i = i_chunk + (int64_t)pc * 8;
         const bool ok = vec && pc < npc && i < L.d_in;
-        gr[j] = __builtin_amdgcn_raw_buffer_load_b128(rg, ok ? (uint32_t)(i * 2) : kOOB, 0, 0);
+        gr[j] = __builtin_amdgcn_raw_buffer_load_b128(rgs, ok ? (uint32_t)(i * 2) : kOOB, 0, 0);
         xr[j][0] = __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? (uint32_t)(i * xb) : kOOB, 0, 0);
         xr[j][1] = __builtin_amdgcn_raw_buffer_load_b128(rx, ok && xf32 ? (uint32_t)(i * 4 + 16) : kOOB, 0, 0);
     }
@@ -618,18 +650,19 @@ __global__ __launch_bounds__(kThreads) void k_stage1f(MRun run, MLin single) {
     const int sub = (L.kcg + kWaves - 1) / kWaves;
     const int ka = wave * sub;                                         // chunk-local K-group
     const int nk = (int)imax(0, imin(sub, nkg - ka));
-    const int ntile = (int)cdiv(L.r_p, kTile);
+    const int tile0 = rg * run.flush1;                                 // first 64-latent tile of the item
+    const int ntile = (int)imin(run.flush1, cdiv(L.r_p, kTile) - tile0);
     const int total = ntile * nk;
     const __amdgpu_buffer_rsrc_t rv =
         make_rsrc(L.v_bits + (int64_t)p * L.kw_v * L.ld_v, (int64_t)L.kw_v * L.ld_v * 4);
-    const uint32_t vo = (uint32_t)(((int64_t)((kg0 + ka) * 4 + gq) * L.ld_v + 4 * r16) * 4);
+    const uint32_t vo = (uint32_t)(((int64_t)((kg0 + ka) * 4 + gq) * L.ld_v + tile0 * kTile + 4 * r16) * 4);
     const uint32_t group4 = (uint32_t)(4 * L.ld_v * 4);
     // next (tile, K-group) to load; selects only, so every load is issued
     // on every path and the compiler can count them
     const int ltiles = nk > 0 ? ntile : 0;
     int lt = 0, lk = 0;
     auto next_off = [&]() -> uint32_t {
-        const bool live = lt < ltiles && lt * kTile + 4 * r16 < L.r_p;
+        const bool live = lt < ltiles && (tile0 + lt) * kTile + 4 * r16 < L.r_p;
         const uint32_t o = live ? vo + (uint32_t)(lt * kTile * 4) + (uint32_t)lk * group4 : kOOB;
         const bool wrap = lk + 1 == nk;
         lt = wrap ? lt + 1 : lt;
@@ -680,7 +713,7 @@ __global__ __launch_bounds__(kThreads) void k_stage1f(MRun run, MLin single) {
                     const bool in = pc < npc && i + t < L.d_in;
                     const uint32_t go = in ? (uint32_t)((i + t) * 2) : kOOB;
                     const uint32_t xo = in ? (uint32_t)(((int64_t)n * L.d_in + i + t) * xb) : kOOB;
-                    const float gf = f16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rg, go, 0, 0));
+                    const float gf = f16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rgs, go, 0, 0));
                     const float xf = xf32 ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rx, xo, 0, 0))
                                           : bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rx, xo, 0, 0));
                     v[t] = gf * xf;
@@ -700,9 +733,9 @@ __global__ __launch_bounds__(kThreads) void k_stage1f(MRun run, MLin single) {
     // partial sums through a buffer descriptor: a flat store would be counted
     // with the LDS operations too, and every later wait would become a full one
     const __amdgpu_buffer_rsrc_t rpart = make_rsrc(L.part, (int64_t)L.nchunks * T * Rtot * 4);
-    // tile t done: this wave's partials to LDS, meet, the fixed-order sum to part
+    // Tile t done: this wave's partials go to its LDS slot, with no wait.
     auto tile_end = [&](int t) {
-        float *mine = red + ((t & 1) * kWaves + wave) * T * 64;
+        float *mine = red + ((size_t)(t * kWaves + wave) * T) * 64;
 #pragma unroll
         for (int s = 0; s < 4 / R::S1; ++s) {
             const int n = gq * (4 / R::S1) + s;
@@ -718,14 +751,6 @@ __global__ __launch_bounds__(kThreads) void k_stage1f(MRun run, MLin single) {
         }
 #pragma unroll
         for (int m = 0; m < 4; ++m) acc[m] = v4f{0.f, 0.f, 0.f, 0.f};
-        lds_meet();
-        const float *both = red + (t & 1) * kWaves * T * 64;
-        for (int f = tid; f < T * 64; f += kThreads) {
-            const float s = ((both[f] + both[T * 64 + f]) + both[2 * T * 64 + f]) + both[3 * T * 64 + f];
-            const int n = f >> 6, row = t * kTile + (f & 63);
-            const uint32_t po = (uint32_t)((((int64_t)c * T + n) * Rtot + (int64_t)p * L.r_p + row) * 4);
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s), rpart, row < L.r_p ? po : kOOB, 0, 0);
-        }
     };
     int pk = 0, pt = 0;
     auto process = [&](const v4u &w) {
@@ -748,7 +773,19 @@ __global__ __launch_bounds__(kThreads) void k_stage1f(MRun run, MLin single) {
         }
     }
     if (nk == 0)
-        for (int t = 0; t < ntile; ++t) tile_end(t);
+        for (int t = 0; t < ntile; ++t) tile_end(t);                  // zeros
+
+    // every wave's partials in LDS: add them in wave order, write row-contiguous
+    lds_meet();
+    const int per = T * 64;                                           // floats of one wave's tile
+    for (int f = tid; f < ntile * per; f += kThreads) {
+        const int k = f / per, rem = f - k * per;
+        const int n = rem >> 6, row = (tile0 + k) * kTile + (rem & 63);
+        const float *q = red + (size_t)k * kWaves * per + rem;
+        const float sum = ((q[0] + q[per]) + q[2 * per]) + q[3 * per];
+        const uint32_t po = (uint32_t)((((int64_t)c * T + n) * Rtot + (int64_t)p * L.r_p + row) * 4);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sum), rpart, row < L.r_p ? po : kOOB, 0, 0);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -844,6 +881,7 @@ __global__ __launch_bounds__(kThreads) void k_stage2(MRun run, MLin single) {
     const int tiles = (int)imin(L.rows2 / kRG, cdiv(L.d_out - row_begin, kRG));
     const int units = tiles * nbat;
     const int opb = L.R2 * kRec;
+    const OutBuf ob = out_buf(L.y, run.y_dtype, (int64_t)T * L.d_out, L.d_out);
 
     // operands first (loads complete in issue order)
     v4u pre[kPreVec];
@@ -950,7 +988,7 @@ __global__ __launch_bounds__(kThreads) void k_stage2(MRun run, MLin single) {
                 }
                 const int n = b * R::TPM2 + (NL == 2 ? gq : gq / 2);
                 const bool writer = n < T && (NL == 2 || (gq & 1) == 0);
-                if (writer) store4(L.y, run.y_dtype, (int64_t)n * L.d_out + row, row, L.d_out, y4);
+                store4(ob, (int64_t)n * L.d_out + row, row, L.d_out, y4, writer);
             }
 #pragma unroll
             for (int m = 0; m < 4; ++m)
@@ -986,6 +1024,7 @@ __global__ __launch_bounds__(kThreads) void k_stage2r(MRun run, MLin single) {
     const int tiles = (int)imin(L.rows2 / kRG, cdiv(L.d_out - row_begin, kRG));
     const int total = tiles * steps;               // this wave's stream (uniform)
     const int opb = L.R2 * kRec;
+    const OutBuf ob = out_buf(L.y, run.y_dtype, (int64_t)T * L.d_out, L.d_out);
     uint8_t *ops = smem;                                          // [steps][NB2] operands
     uint16_t *hs = (uint16_t *)(smem + run.ops2 * NB2 * kOpS);   // [2][kHRows] fp16 h
 
@@ -1010,9 +1049,12 @@ __global__ __launch_bounds__(kThreads) void k_stage2r(MRun run, MLin single) {
     const __amdgpu_buffer_rsrc_t ru = make_rsrc(L.u_bits, (int64_t)L.P * L.kw_u * L.ld_u * 4);
     const uint32_t uo = (uint32_t)(((int64_t)gq * L.ld_u + row_begin + wave * kTile + 4 * r16) * 4);
     const uint32_t group4 = (uint32_t)(4 * L.ld_u * 4);
+    // rows past d_out are not loaded (padding words of the planes)
+    const int64_t lane_row = row_begin + wave * kTile + 4 * r16;
     auto off_of = [&](int e) -> uint32_t {
         const int i = e / steps, st = e - i * steps;
-        return e < total ? uo + (uint32_t)(i * kRG * 4) + (uint32_t)st * group4 : kOOB;
+        return e < total && lane_row + (int64_t)i * kRG < L.d_out ? uo + (uint32_t)(i * kRG * 4) + (uint32_t)st * group4
+                                                                 : kOOB;
     };
     v4u slot[kWin2];
 #pragma unroll
@@ -1086,7 +1128,7 @@ __global__ __launch_bounds__(kThreads) void k_stage2r(MRun run, MLin single) {
                 }
                 const int n = b * R::TPM2 + (NL == 2 ? gq : gq / 2);
                 const bool writer = n < T && (NL == 2 || (gq & 1) == 0);
-                if (writer) store4(L.y, run.y_dtype, (int64_t)n * L.d_out + row, row, L.d_out, y4);
+                store4(ob, (int64_t)n * L.d_out + row, row, L.d_out, y4, writer);
             }
 #pragma unroll
             for (int m = 0; m < 4; ++m)
@@ -1137,8 +1179,11 @@ int kcg_cap(const Shape &s) { return (int)imin(kMaxKcg, kLdsBudget / (s.NB1 * kO
 // Stage 1 runs fused (k_stage1f) when the tokens fill one activation-row block.
 bool fused1(const Shape &s) { return s.NB1 == 1; }
 constexpr int64_t kFusedBytes = 96 * 1024;     // V-plane bytes per fused stage-1 item, about
-// LDS of the fused form's cross-wave reduction: [2][kWaves][T][64] floats
-size_t red1_bytes(int64_t T) { return (size_t)2 * kWaves * T * 64 * 4; }
+// Fused form: an item covers at most F latent tiles, as many as the LDS of its
+// cross-wave sums ([F][kWaves][T][64] floats) holds within kRedBudget.
+constexpr size_t kRedBudget = 24 * 1024;
+int flush1_for(int64_t T) { return (int)imax(1, (int64_t)kRedBudget / ((int64_t)kWaves * T * 64 * 4)); }
+size_t red1_bytes(int64_t T, int F) { return (size_t)F * kWaves * T * 64 * 4; }
 
 // Steps the stage-2 LDS holds: all steps of the largest linear when they fit,
 // else a multiple of the batch (at least one batch, which may exceed 64 KB).
@@ -1181,13 +1226,13 @@ size_t plan_linear(const Linear &a, const Shape &s, bool many, MLin *m) {
         // LDS-bounded, spread evenly over d_in
         const int64_t per_kg = (int64_t)a.r_p * 16;
         int64_t kc = imax(1, imin(kMaxKcf, kFusedBytes / per_kg));
-        kc = imin(kc, (int64_t)((kLdsBudget - red1_bytes(a.T)) / (m->R1 * kRec)));
+        kc = imin(kc, (int64_t)((kLdsBudget - kRedBudget) / (m->R1 * kRec)));
         if (!many)   // a lone linear: smaller chunks until the chip has work
             while (kc > 4 && a.P * cdiv(m->kgv, kc) < 256) kc = (kc + 1) / 2;
         const int64_t nch = cdiv(m->kgv, kc);
         m->kcg = (int32_t)cdiv(m->kgv, nch);
         m->nchunks = (int32_t)cdiv(m->kgv, m->kcg);
-        m->nrg = 1;
+        m->nrg = (int32_t)cdiv(cdiv(a.r_p, kTile), flush1_for(a.T));
         m->kcp = 0;
         m->nprep = 0;
         m->xvec = (a.d_in % 8 == 0 && ((uintptr_t)a.x & 15) == 0 && ((uintptr_t)a.g & 15) == 0) ? 1 : 0;
@@ -1298,9 +1343,9 @@ int launch_shape(const Shape &s, const MRun &run, const MLin &single, const Lds 
     return LB_EUNSUPPORTED;
 }
 
-void lds_add(Lds *l, const MLin &m, const Shape &s, int ops2, int64_t T) {
+void lds_add(Lds *l, const MLin &m, const Shape &s, int ops2, int64_t T, int F) {
     const size_t prep = (size_t)m.kcp * s.NB1 * m.R1 * kRec;
-    const size_t s1 = fused1(s) ? (size_t)m.kcg * m.R1 * kRec + red1_bytes(T) : (size_t)m.kcg * s.NB1 * kOpS;
+    const size_t s1 = fused1(s) ? (size_t)m.kcg * m.R1 * kRec + red1_bytes(T, F) : (size_t)m.kcg * s.NB1 * kOpS;
     const size_t lat = (size_t)2 * s.NB2 * m.R2 * kRec;
     const size_t s2 = (size_t)ops2 * s.NB2 * kOpS;
     if (prep > l->prep) l->prep = prep;
@@ -1347,7 +1392,8 @@ int mfma_decode_forward(const Linear &a, void *ws, hipStream_t st) {
     run.items2 = m.n2;
     run.table = nullptr;
     Lds lds{};
-    lds_add(&lds, m, s, run.ops2, a.T);
+    run.flush1 = (int)imin(flush1_for(a.T), cdiv(m.r_p, kTile));
+    lds_add(&lds, m, s, run.ops2, a.T, run.flush1);
     return launch_shape(s, run, m, lds, st);
 }
 
@@ -1409,7 +1455,10 @@ int mfma_group_prepare(const Linear *ls, int n, int64_t T, int y_dtype, void *ws
     run.dma2 = dma2_for(hs->s, steps_max);
     run.ops2 = run.dma2 ? steps_max : ops2_for(hs->s, steps_max);
     hs->lds = Lds{};
-    for (int j = 0; j < n; ++j) lds_add(&hs->lds, tab[(size_t)j], hs->s, run.ops2, T);
+    int64_t ntile_max = 1;
+    for (int j = 0; j < n; ++j) ntile_max = imax(ntile_max, cdiv(tab[(size_t)j].r_p, kTile));
+    run.flush1 = (int)imin(flush1_for(T), ntile_max);
+    for (int j = 0; j < n; ++j) lds_add(&hs->lds, tab[(size_t)j], hs->s, run.ops2, T, run.flush1);
     int32_t *lin0 = (int32_t *)cur;
     int32_t *lin1 = (int32_t *)((uint8_t *)lin0 + rup256((size_t)i0 * 4));
     int32_t *linF = (int32_t *)((uint8_t *)lin1 + rup256((size_t)i1 * 4));

@@ -89,6 +89,12 @@ int lb_rank_for_budget(int64_t d_in, int64_t d_out, int64_t b_num, int64_t b_den
 /* Smallest valid plane stride for an other-axis length n (n rounded up to 4). */
 int64_t lb_packed_ld(int64_t n_other);
 
+/* The plane stride the decode kernels stream fastest: n rounded up to 32
+ * words, so every plane starts on a 128-byte line and a 64-row piece of a
+ * plane is two whole lines.  The padding words are never read by the forward
+ * kernels; they cost memory only (at most 31 words per plane). */
+int64_t lb_packed_ld_aligned(int64_t n_other);
+
 /* Number of uint32 words a packed factor occupies: ceil(n_pack/32) * ld, where
  * n_pack is rows (axis 0) or cols (axis 1).  0 for bad arguments. */
 int64_t lb_packed_words(int64_t rows, int64_t cols, int axis, int64_t ld);

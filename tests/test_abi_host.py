@@ -56,6 +56,8 @@ def test_rank_rule_errors():
 
 def test_packed_sizes():
     assert lb.packed_ld(1) == 4 and lb.packed_ld(304) == 304 and lb.packed_ld(305) == 308
+    assert lb.packed_ld_aligned(1) == 32 and lb.packed_ld_aligned(304) == 320 and lb.packed_ld_aligned(320) == 320
+    assert lb.packed_ld_aligned(0) == 0
     assert lb.packed_words(100, 7, 0, 8) == 4 * 8
     assert lb.packed_words(7, 100, 1, 8) == 4 * 8
     assert lb.packed_words(7, 100, 1, 6) == 0        # ld below the other axis
