@@ -64,11 +64,13 @@ def build_stack(w, layers, T):
     return st, xs
 
 
-def time_decode(st, steps, warmup):
-    """Times `steps` passes back to back (the timed region: nothing between
-    the passes, synchronised on both sides), then `steps` more with HIP events
-    on the launch stream around each stage for the per-stage durations (events
-    between kernels add a little time, so these run outside the timed region).
+def time_decode(st, steps, warmup, settle_s=0.3):
+    """Runs `warmup` untimed passes, then more untimed passes until `settle_s`
+    seconds have gone by (the GPU clocks take some tens of milliseconds to
+    leave their idle state; a decode service runs in the steady state), then
+    `steps` passes with HIP events on the launch stream around each stage
+    (per-stage durations; events between kernels add a little time), then the
+    timed region: `steps` passes back to back, synchronised on both sides.
     Returns (seconds per pass, stage-1 seconds, stage-2 seconds)."""
     import torch
     s = torch.cuda.current_stream()
@@ -78,11 +80,11 @@ def time_decode(st, steps, warmup):
         g.run_stage(2)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
-        g.run_stage(1)
-        g.run_stage(2)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    while time.perf_counter() - t0 < settle_s:
+        for _ in range(20):
+            g.run_stage(1)
+            g.run_stage(2)
+        torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     for k in range(steps):
         ev[k][0].record(s)
@@ -93,6 +95,12 @@ def time_decode(st, steps, warmup):
     torch.cuda.synchronize()
     s1 = sum(e[0].elapsed_time(e[1]) for e in ev) / steps * 1e-3
     s2 = sum(e[1].elapsed_time(e[2]) for e in ev) / steps * 1e-3
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.run_stage(1)
+        g.run_stage(2)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
     return wall / steps, s1, s2
 
 

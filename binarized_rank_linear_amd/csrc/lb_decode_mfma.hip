@@ -1178,7 +1178,7 @@ int kcg_cap(const Shape &s) { return (int)imin(kMaxKcg, kLdsBudget / (s.NB1 * kO
 
 // Stage 1 runs fused (k_stage1f) when the tokens fill one activation-row block.
 bool fused1(const Shape &s) { return s.NB1 == 1; }
-constexpr int64_t kFusedBytes = 96 * 1024;     // V-plane bytes per fused stage-1 item, about
+constexpr int64_t kFusedBytes = 192 * 1024;    // V-plane bytes per fused stage-1 item, about
 // Fused form: an item covers at most F latent tiles, as many as the LDS of its
 // cross-wave sums ([F][kWaves][T][64] floats) holds within kRedBudget.
 constexpr size_t kRedBudget = 24 * 1024;
