@@ -29,6 +29,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 METRIC = "LittleBit layer tok/s at T=1 and T=2048; % HBM BW / % MFMA peak"
+# the kernels a decode group at T <= 8 (bf16 out) runs: stage 1 = k_stage1f then
+# k_latent, stage 2 = k_stage2r alone (so the stage-2 events time that kernel)
+STAGE_KERNEL = {1: "k_stage1f", 2: "k_stage2r"}
 
 
 def _log(*a):
@@ -64,28 +67,28 @@ def build_stack(w, layers, T):
     return st, xs
 
 
-def time_decode(st, steps, warmup, settle_s=0.3):
+def time_decode(st, steps, warmup, settle_s):
     """Runs `warmup` untimed passes, then more untimed passes until `settle_s`
     seconds have gone by (the GPU clocks take some tens of milliseconds to
     leave their idle state; a decode service runs in the steady state), then
-    `steps` passes with HIP events on the launch stream around each stage
-    (per-stage durations; events between kernels add a little time), then the
-    timed region: `steps` passes back to back, synchronised on both sides.
-    Returns (seconds per pass, stage-1 seconds, stage-2 seconds)."""
+    the timed region: `steps` passes, each as stage 1 then stage 2 on the
+    launch stream with HIP events around each stage, synchronised on both
+    sides.  Returns (seconds per pass by the host clock, mean stage-1 seconds,
+    mean stage-2 seconds by the events)."""
     import torch
     s = torch.cuda.current_stream()
     g = st.group
     for _ in range(warmup):
-        g.run_stage(1)
-        g.run_stage(2)
+        g.run()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < settle_s:
         for _ in range(20):
-            g.run_stage(1)
-            g.run_stage(2)
+            g.run()
         torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
     for k in range(steps):
         ev[k][0].record(s)
         g.run_stage(1)
@@ -93,14 +96,9 @@ def time_decode(st, steps, warmup, settle_s=0.3):
         g.run_stage(2)
         ev[k][2].record(s)
     torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
     s1 = sum(e[0].elapsed_time(e[1]) for e in ev) / steps * 1e-3
     s2 = sum(e[1].elapsed_time(e[2]) for e in ev) / steps * 1e-3
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        g.run_stage(1)
-        g.run_stage(2)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     return wall / steps, s1, s2
 
 
@@ -215,6 +213,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle", type=float, default=0.3,
+                    help="seconds of untimed passes after the warmup (clocks leave idle); 0 under a profiler")
     ap.add_argument("--workload", default="c5", choices=["c3", "c4", "c5"])
     ap.add_argument("--tokens", type=int, default=1)
     ap.add_argument("--layers", type=int, default=0, help="stack depth (default: the workload's)")
@@ -253,7 +253,7 @@ def main():
             s1, s2 = linear_bytes(lin.d_in, lin.d_out, lin.r, P, T)
             b1 += s1
             b2 += s2
-    step_s, s1_s, s2_s = time_decode(st, args.steps, args.warmup)
+    step_s, s1_s, s2_s = time_decode(st, args.steps, args.warmup, args.settle)
     bw1 = b1 / s1_s / 1e9
     bw2 = b2 / s2_s / 1e9
     dominant = (2, b2, s2_s, bw2) if b2 >= b1 else (1, b1, s1_s, bw1)
@@ -282,9 +282,9 @@ def main():
         },
         "roofline": {"bound": "hbm", "achieved": dominant[3], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": dominant[3] / HBM_PEAK_GBS,
-                     "traffic": measured_traffic("k_stage%d" % dominant[0], args.workload, T),
+                     "traffic": measured_traffic(STAGE_KERNEL[dominant[0]], args.workload, T),
                      "algorithmic_bytes": dominant[1],
-                     "kernel": "k_stage%d" % dominant[0],
+                     "kernel": STAGE_KERNEL[dominant[0]],
                      "pass_GBs": (b1 + b2) / step_s / 1e9,
                      "pass_frac": (b1 + b2) / step_s / 1e9 / HBM_PEAK_GBS,
                      "stage1_us": s1_s * 1e6, "stage2_us": s2_s * 1e6},

@@ -104,6 +104,8 @@ def lib() -> ctypes.CDLL:
         L.lb_grouped_run.restype = ctypes.c_int
         L.lb_grouped_run_stage.argtypes = [_vp, ctypes.c_int, _vp]
         L.lb_grouped_run_stage.restype = ctypes.c_int
+        L.lb_grouped_release.argtypes = [_vp]
+        L.lb_grouped_release.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -332,3 +334,16 @@ class Group:
     def run_stage(self, stage: int, stream=None):
         _check(lib().lb_grouped_run_stage(self.ws.data_ptr(), stage, _stream_ptr(stream)),
                "lb_grouped_run_stage")
+
+    def release(self):
+        """Forget the group's host-side record (lb_grouped_release); idempotent."""
+        ws = getattr(self, "ws", None)
+        if ws is not None:
+            lib().lb_grouped_release(ws.data_ptr())
+            self.ws = None
+
+    def __del__(self):
+        try:
+            self.release()
+        except Exception:
+            pass

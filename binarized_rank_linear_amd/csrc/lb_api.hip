@@ -391,6 +391,14 @@ int lb_grouped_prepare(const lb_linear_desc *descs, int n, int64_t T, int x_dtyp
     return LB_OK;
 }
 
+int lb_grouped_release(void *ws) {
+    std::lock_guard<std::mutex> lk(g_groups_mu);
+    auto it = g_groups.find(ws);
+    if (it == g_groups.end()) return LB_EINVAL;
+    g_groups.erase(it);
+    return LB_OK;
+}
+
 int lb_grouped_run(void *ws, void *stream) {
     GroupRecord g;
     {

@@ -114,6 +114,7 @@ struct MRun {
     int dma2;                  // stage 2 runs k_stage2r (all operands and h fit the LDS)
     int flush1;                // fused stage 1: latent tiles per item (F)
     int64_t items0, items1, itemsF, items2;
+    int64_t base0, base1, baseF, base2;   // item of workgroup 0 in each launch (0: all items)
     const MLin *table;         // null: the single linear passed by value
     const int32_t *lin0, *lin1, *linF, *lin2;   // item -> linear, per launch
 };
@@ -258,8 +259,8 @@ __device__ __forceinline__ v4u load_rows(__amdgpu_buffer_rsrc_t r, uint32_t voff
 
 // The linear of a work item, as a wave-uniform value (matrix instructions
 // ignore the exec mask, so every branch around them must be uniform).
-__device__ __forceinline__ MLin pick(const MRun &run, const MLin &single, const int32_t *map) {
-    MLin m = run.table ? run.table[map[blockIdx.x]] : single;
+__device__ __forceinline__ MLin pick(const MRun &run, const MLin &single, const int32_t *map, int64_t item) {
+    MLin m = run.table ? run.table[map[item]] : single;
     static_assert(sizeof(MLin) % 4 == 0, "MLin is copied as 32-bit words");
     int w[sizeof(MLin) / 4];
     __builtin_memcpy(w, &m, sizeof(MLin));
@@ -363,8 +364,9 @@ template <int NL, int NB1>
 __global__ __launch_bounds__(kThreads) void k_prep(MRun run, MLin single) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     using R = Rows<NL>;
-    const MLin L = pick(run, single, run.lin0);
-    const int64_t local = (int64_t)blockIdx.x - L.item0;
+    const int64_t item = (int64_t)blockIdx.x + run.base0;
+    const MLin L = pick(run, single, run.lin0, item);
+    const int64_t local = item - L.item0;
     const int c = (int)(local % L.nprep);
     const int p = (int)(local / L.nprep);
     const int T = run.T;
@@ -443,8 +445,9 @@ template <int NL, int NB1>
 __global__ __launch_bounds__(kThreads) void k_stage1(MRun run, MLin single) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     using R = Rows<NL>;
-    const MLin L = pick(run, single, run.lin1);
-    const int64_t local = (int64_t)blockIdx.x - L.item1;
+    const int64_t item = (int64_t)blockIdx.x + run.base1;
+    const MLin L = pick(run, single, run.lin1, item);
+    const int64_t local = item - L.item1;
     const int rg = (int)(local % L.nrg);
     const int c = (int)((local / L.nrg) % L.nchunks);
     const int p = (int)(local / ((int64_t)L.nrg * L.nchunks));
@@ -610,8 +613,9 @@ template <int NL>
 __global__ __launch_bounds__(kThreads) void k_stage1f(MRun run, MLin single) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     using R = Rows<NL>;
-    const MLin L = pick(run, single, run.lin1);
-    const int64_t local = (int64_t)blockIdx.x - L.item1;
+    const int64_t item = (int64_t)blockIdx.x + run.base1;
+    const MLin L = pick(run, single, run.lin1, item);
+    const int64_t local = item - L.item1;
     const int c = (int)(local % L.nchunks);
     const int rg = (int)((local / L.nchunks) % L.nrg);
     const int p = (int)(local / ((int64_t)L.nchunks * L.nrg));
@@ -796,8 +800,9 @@ template <int NL, int NB2>
 __global__ __launch_bounds__(kThreads) void k_latent(MRun run, MLin single) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     using R = Rows<NL>;
-    const MLin L = pick(run, single, run.linF);
-    const int64_t local = (int64_t)blockIdx.x - L.itemF;
+    const int64_t item = (int64_t)blockIdx.x + run.baseF;
+    const MLin L = pick(run, single, run.linF, item);
+    const int64_t local = item - L.itemF;
     const int T = run.T;
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int kg_first = (int)local * 2;                          // 2 K-groups = 8 planes
@@ -863,8 +868,9 @@ template <int NL, int NB2>
 __global__ __launch_bounds__(kThreads) void k_stage2(MRun run, MLin single) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     using R = Rows<NL>;
-    const MLin L = pick(run, single, run.lin2);
-    const int64_t local = (int64_t)blockIdx.x - L.item2;
+    const int64_t item = (int64_t)blockIdx.x + run.base2;
+    const MLin L = pick(run, single, run.lin2, item);
+    const int64_t local = item - L.item2;
     const int T = run.T;
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int r16 = lane & 15, gq = lane >> 4;
@@ -1012,8 +1018,9 @@ template <int NL, int NB2>
 __global__ __launch_bounds__(kThreads) void k_stage2r(MRun run, MLin single) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     using R = Rows<NL>;
-    const MLin L = pick(run, single, run.lin2);
-    const int64_t local = (int64_t)blockIdx.x - L.item2;
+    const int64_t item = (int64_t)blockIdx.x + run.base2;
+    const MLin L = pick(run, single, run.lin2, item);
+    const int64_t local = item - L.item2;
     const int T = run.T;
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int r16 = lane & 15, gq = lane >> 4;
@@ -1282,19 +1289,27 @@ struct Lds {
 // stage_mask: bit 0 = prep, stage 1 and the latent pass; bit 1 = stage 2.
 template <int NL, int NB1, int NB2>
 int launch_all(const MRun &run, const MLin &single, const Lds &lds, hipStream_t st, int stage_mask) {
+    // launches with no items (a chunk of a group may have none of a kind) are skipped
     if ((stage_mask & 1) && NB1 == 1) {
-        k_stage1f<NL><<<(unsigned)run.items1, kThreads, lds.s1, st>>>(run, single);
-        if (int rc = last_launch_status()) return rc;
+        if (run.items1 > 0) {
+            k_stage1f<NL><<<(unsigned)run.items1, kThreads, lds.s1, st>>>(run, single);
+            if (int rc = last_launch_status()) return rc;
+        }
     } else if (stage_mask & 1) {
-        k_prep<NL, NB1><<<(unsigned)run.items0, kThreads, lds.prep, st>>>(run, single);
-        if (int rc = last_launch_status()) return rc;
-        k_stage1<NL, NB1><<<(unsigned)run.items1, kThreads, lds.s1, st>>>(run, single);
-        if (int rc = last_launch_status()) return rc;
+        if (run.items0 > 0) {
+            k_prep<NL, NB1><<<(unsigned)run.items0, kThreads, lds.prep, st>>>(run, single);
+            if (int rc = last_launch_status()) return rc;
+        }
+        if (run.items1 > 0) {
+            k_stage1<NL, NB1><<<(unsigned)run.items1, kThreads, lds.s1, st>>>(run, single);
+            if (int rc = last_launch_status()) return rc;
+        }
     }
-    if (stage_mask & 1) {
+    if ((stage_mask & 1) && run.itemsF > 0) {
         k_latent<NL, NB2><<<(unsigned)run.itemsF, kThreads, lds.lat, st>>>(run, single);
         if (int rc = last_launch_status()) return rc;
     }
+    if ((stage_mask & 2) && run.items2 <= 0) return LB_OK;
     if ((stage_mask & 2) && run.dma2) {
         const size_t l2 = (size_t)run.ops2 * NB2 * kOpS + 2 * kHRows * 2;
         if (l2 > 160 * 1024) return LB_EUNSUPPORTED;
@@ -1496,6 +1511,11 @@ size_t mfma_group_state_bytes() { return sizeof(MGroupHost); }
 
 int mfma_group_run(const void *host_state, hipStream_t st, int stage_mask) {
     const MGroupHost *hs = (const MGroupHost *)host_state;
+    const MRun &r = hs->run;
+    // every launch of a group looks its items up in these tables
+    if (!r.table || (r.items0 > 0 && !r.lin0) || (r.items1 > 0 && !r.lin1) || (r.itemsF > 0 && !r.linF) ||
+        (r.items2 > 0 && !r.lin2))
+        return LB_EINVAL;
     MLin dummy{};
     return launch_shape(hs->s, hs->run, dummy, hs->lds, st, stage_mask);
 }

@@ -207,6 +207,13 @@ int lb_grouped_prepare(const lb_linear_desc *descs, int n, int64_t T, int x_dtyp
  * Runs on the same workspace race. */
 int lb_grouped_run(void *ws, void *stream);
 
+/* Forget a prepared group (its host-side record; ws itself stays the
+ * caller's).  Not while a run of the group may be enqueued from another
+ * thread; work already enqueued completes normally.  Preparing a group again
+ * on the same ws replaces the previous record.  LB_EINVAL for a ws with no
+ * group. */
+int lb_grouped_release(void *ws);
+
 /* One half of lb_grouped_run: stage 1 (all first contractions, sign(V)^T
  * applied to g (.) x, and the rank-r latents) or stage 2 (all second
  * contractions and the outputs).  Running stage 1 then stage 2 on one stream

@@ -137,3 +137,4 @@ def test_mlp_and_group_argument_errors():
     assert L.lb_grouped_workspace_bytes(arr, 0, 4, 0) == 0                 # no linears
     assert L.lb_grouped_prepare(arr, 1, 1, lb.LB_F32, lb.LB_F32, None, 0, 0, None) == lb.LB_EWORKSPACE
     assert L.lb_grouped_run(FAKE, None) == lb.LB_EINVAL                   # never prepared
+    assert L.lb_grouped_release(FAKE) == lb.LB_EINVAL                     # never prepared

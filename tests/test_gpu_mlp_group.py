@@ -98,3 +98,38 @@ def test_full_c5_stack_sampled_layers():
     """The 80-layer Llama2-70B-shaped stack as the benchmark runs it (one
     group, T = 1); layers 0, 40 and 79 are checked on sampled rows."""
     _stack_check("c5", 80, 1, {0, 40, 79})
+
+
+@pytest.mark.parametrize("key,T,out", [("c3", 3, "bf16"), ("c4", 9, "f32"), ("c3", 1, "f32")])
+def test_group_run_matches_staged_run(key, T, out):
+    """A whole-group run equals stage 1 then stage 2 bit for bit (the same
+    kernels and summation order), also for runs enqueued back to back."""
+    torch = torch_or_skip()
+    from binarized_rank_linear_amd.stack import LayerStack
+    w = synth.WORKLOADS[key]
+    say("chunked group", key, "T", T, out)
+
+    def make(L, i, di, do, rp, P):
+        return synth.device_layer(synth.layer_seed(L, i) + 1000, di, do, rp, P)
+
+    st = LayerStack([(s.name, s.d_in, s.d_out) for s in w.linears], 3, w.b_num, w.b_den, w.residual, make)
+    widths = sorted({s.d_in for s in w.linears})
+    xs = {d: synth.device_activations(synth.activation_seed(d) + 7, T, d, w.dtype) for d in widths}
+    odt = torch.bfloat16 if out == "bf16" else torch.float32
+    st.bind(T, xs, odt)
+    st.group.run_stage(1)
+    st.group.run_stage(2)
+    torch.cuda.synchronize()
+    staged = [[y.clone() for y in row] for row in st.outputs]
+    for row in st.outputs:
+        for y in row:
+            y.fill_(float("nan"))
+    for _ in range(3):
+        st.group.run()
+    torch.cuda.synchronize()
+    for L, row in enumerate(st.outputs):
+        for i, y in enumerate(row):
+            assert torch.equal(y.view(torch.int16) if odt == torch.bfloat16 else y.view(torch.int32),
+                               staged[L][i].view(torch.int16) if odt == torch.bfloat16
+                               else staged[L][i].view(torch.int32)), (L, i)
+    st.group.release()
