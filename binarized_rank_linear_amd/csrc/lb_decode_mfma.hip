@@ -69,6 +69,7 @@ constexpr int kWin1 = 8;                  // stage 1 (fused form): plane loads i
 constexpr int kMaxKcf = 32;               // K-groups per fused stage-1 chunk (two 8-input pieces per thread)
 constexpr uint32_t kOOB = 0x7ffffff0u;    // a buffer offset past every range: reads as zero
 constexpr int kHRows = kRG * kTilesPerItem2;   // output rows of one stage-2 item, at most
+constexpr int kYStage = 16 * 1024;        // LDS for k_stage2r's collected outputs, at most
 
 // Activation-row layout of the A operands.  Stage 1 (one path): token n uses
 // rows (n % TPM1)*S1 + q, S1 = 2 (two limbs) or 4 (three limbs).  Stage 2 (both
@@ -113,6 +114,7 @@ struct MRun {
     int ops2;                  // stage-2 operands (steps) the LDS holds at once
     int dma2;                  // stage 2 runs k_stage2r (all operands and h fit the LDS)
     int flush1;                // fused stage 1: latent tiles per item (F)
+    int ystage;                // k_stage2r collects the item's outputs in LDS, stored after its stream
     int64_t items0, items1, itemsF, items2;
     int64_t base0, base1, baseF, base2;   // item of workgroup 0 in each launch (0: all items)
     const MLin *table;         // null: the single linear passed by value
@@ -1034,6 +1036,11 @@ __global__ __launch_bounds__(kThreads) void k_stage2r(MRun run, MLin single) {
     const OutBuf ob = out_buf(L.y, run.y_dtype, (int64_t)T * L.d_out, L.d_out);
     uint8_t *ops = smem;                                          // [steps][NB2] operands
     uint16_t *hs = (uint16_t *)(smem + run.ops2 * NB2 * kOpS);   // [2][kHRows] fp16 h
+    // [T][kHRows] outputs of the item (bf16 or fp32): stores inside the stream
+    // would share the in-order counter with the plane loads, so every later
+    // wait would also wait for their acknowledgements
+    uint8_t *ys = (uint8_t *)(hs + 2 * kHRows);
+    const int yb = run.y_dtype == LB_BF16 ? 2 : 4;
 
     // operands and h first, as buffer loads (counted precisely, so the LDS
     // fill below waits for these only, not for the plane loads behind them)
@@ -1135,7 +1142,17 @@ __global__ __launch_bounds__(kThreads) void k_stage2r(MRun run, MLin single) {
                 }
                 const int n = b * R::TPM2 + (NL == 2 ? gq : gq / 2);
                 const bool writer = n < T && (NL == 2 || (gq & 1) == 0);
-                store4(ob, (int64_t)n * L.d_out + row, row, L.d_out, y4, writer);
+                if (run.ystage) {                               // uniform
+                    if (writer) {
+                        uint8_t *yp = ys + ((size_t)n * kHRows + rl) * yb;
+                        if (yb == 2)
+                            *(v2u *)yp = v2u{bf16_pair(y4[0], y4[1]), bf16_pair(y4[2], y4[3])};
+                        else
+                            *(v4f *)yp = v4f{y4[0], y4[1], y4[2], y4[3]};
+                    }
+                } else {
+                    store4(ob, (int64_t)n * L.d_out + row, row, L.d_out, y4, writer);
+                }
             }
 #pragma unroll
             for (int m = 0; m < 4; ++m)
@@ -1150,6 +1167,36 @@ __global__ __launch_bounds__(kThreads) void k_stage2r(MRun run, MLin single) {
         for (int k = 0; k < kWin2; ++k) {
             if (e0 + k < total) process(slot[k]);                 // uniform
             slot[k] = load_rows(ru, off_of(e0 + k + kWin2));
+        }
+    }
+    if (run.ystage) {
+        // the item's outputs leave as one contiguous burst per token row
+        // (16-byte chunks, all threads together), not as scattered pieces
+        // between other workgroups' plane reads
+        __syncthreads();
+        const int64_t rows = imin((int64_t)L.rows2, L.d_out - row_begin);
+        const int per = 16 / yb;                                   // outputs per chunk
+        const bool chunky = ob.vec && (L.d_out % per) == 0 && ((uintptr_t)L.y & 15) == 0;
+        const int cpr = (int)cdiv(rows, per);                      // chunks per token row
+        for (int c = threadIdx.x; c < T * cpr; c += kThreads) {
+            const int n = c / cpr, k = c - n * cpr;
+            const int64_t r0 = (int64_t)k * per;                   // row within the item
+            const v4u w = *(const v4u *)(ys + ((size_t)n * kHRows + r0) * yb);
+            const int64_t e0 = (int64_t)n * L.d_out + row_begin + r0;
+            if (chunky) {
+                __builtin_amdgcn_raw_buffer_store_b128(w, ob.r, r0 + per <= rows ? (uint32_t)(e0 * yb) : kOOB, 0, 0);
+            } else {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    if (q >= per) break;
+                    const bool ok = r0 + q < rows;
+                    if (yb == 2)
+                        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(w[q >> 1] >> (16 * (q & 1))), ob.r,
+                                                              ok ? (uint32_t)((e0 + q) * 2) : kOOB, 0, 0);
+                    else
+                        __builtin_amdgcn_raw_buffer_store_b32(w[q], ob.r, ok ? (uint32_t)((e0 + q) * 4) : kOOB, 0, 0);
+                }
+            }
         }
     }
 }
@@ -1196,6 +1243,11 @@ size_t red1_bytes(int64_t T, int F) { return (size_t)F * kWaves * T * 64 * 4; }
 // else a multiple of the batch (at least one batch, which may exceed 64 KB).
 // Whether stage 2 can run k_stage2r: every step's operands and h of an item
 // fit the LDS of one CU (two workgroups' worth when possible).
+// k_stage2r collects an item's outputs in LDS when they fit kYStage.
+int ystage_for(int64_t T, int y_dtype) {
+    return (size_t)T * kHRows * (y_dtype == LB_BF16 ? 2 : 4) <= (size_t)kYStage ? 1 : 0;
+}
+
 bool dma2_for(const Shape &s, int steps_max) {
     return (size_t)steps_max * s.NB2 * kOpS + 2 * kHRows * 2 <= 80 * 1024;
 }
@@ -1311,7 +1363,8 @@ int launch_all(const MRun &run, const MLin &single, const Lds &lds, hipStream_t 
     }
     if ((stage_mask & 2) && run.items2 <= 0) return LB_OK;
     if ((stage_mask & 2) && run.dma2) {
-        const size_t l2 = (size_t)run.ops2 * NB2 * kOpS + 2 * kHRows * 2;
+        const size_t l2 = (size_t)run.ops2 * NB2 * kOpS + 2 * kHRows * 2 +
+                          (run.ystage ? (size_t)run.T * kHRows * (run.y_dtype == LB_BF16 ? 2 : 4) : 0);
         if (l2 > 160 * 1024) return LB_EUNSUPPORTED;
         static bool raised = false;        // once per instantiation (idempotent if raced)
         if (!raised) {
@@ -1400,6 +1453,7 @@ int mfma_decode_forward(const Linear &a, void *ws, hipStream_t st) {
     run.x_dtype = a.x_dtype;
     run.y_dtype = a.y_dtype;
     run.dma2 = dma2_for(s, m.kgs);
+    run.ystage = ystage_for(a.T, a.y_dtype);
     run.ops2 = run.dma2 ? m.kgs : ops2_for(s, m.kgs);
     run.items0 = items0_of(m);
     run.items1 = items1_of(m);
@@ -1468,6 +1522,7 @@ int mfma_group_prepare(const Linear *ls, int n, int64_t T, int y_dtype, void *ws
     MRun &run = hs->run;
     run = MRun{};
     run.dma2 = dma2_for(hs->s, steps_max);
+    run.ystage = ystage_for(T, y_dtype);
     run.ops2 = run.dma2 ? steps_max : ops2_for(hs->s, steps_max);
     hs->lds = Lds{};
     int64_t ntile_max = 1;
