@@ -1259,7 +1259,14 @@ int ops2_for(const Shape &s, int steps_max) {
 }
 
 // Fill the schedule fields of m and return the workspace bytes it needs.
-size_t plan_linear(const Linear &a, const Shape &s, bool many, MLin *m) {
+// Grain of a group's items: the fused stage-1 chunk target (bytes of V planes)
+// and the 256-row tiles of a stage-2 item.
+struct Grain {
+    int64_t fused_bytes = kFusedBytes;
+    int tiles2 = kTilesPerItem2;
+};
+
+size_t plan_linear(const Linear &a, const Shape &s, bool many, MLin *m, Grain gr = Grain{}) {
     *m = MLin{};
     m->x = a.x;
     m->y = a.y;
@@ -1284,7 +1291,7 @@ size_t plan_linear(const Linear &a, const Shape &s, bool many, MLin *m) {
         // chunks of about kFusedBytes of V planes (all latents of the path),
         // LDS-bounded, spread evenly over d_in
         const int64_t per_kg = (int64_t)a.r_p * 16;
-        int64_t kc = imax(1, imin(kMaxKcf, kFusedBytes / per_kg));
+        int64_t kc = imax(1, imin(kMaxKcf, gr.fused_bytes / per_kg));
         kc = imin(kc, (int64_t)((kLdsBudget - kRedBudget) / (m->R1 * kRec)));
         if (!many)   // a lone linear: smaller chunks until the chip has work
             while (kc > 4 && a.P * cdiv(m->kgv, kc) < 256) kc = (kc + 1) / 2;
@@ -1310,7 +1317,7 @@ size_t plan_linear(const Linear &a, const Shape &s, bool many, MLin *m) {
         m->nprep = (int32_t)cdiv(m->kgv, kcp);
     }
     m->kgs = (int32_t)cdiv((int64_t)a.P * m->kw_u, 4);
-    int tiles = kTilesPerItem2;
+    int tiles = gr.tiles2;
     if (!many)   // a lone linear: fewer tiles per item until the chip has work
         while (tiles > 1 && cdiv(a.d_out, (int64_t)kRG * tiles) < 512) tiles /= 2;
     m->rows2 = kRG * tiles;
@@ -1474,14 +1481,46 @@ struct MGroupHost {
     Lds lds;
 };
 
+// Items sized for large stacks leave a small group (one layer) with a few
+// dozen workgroups; halve the grain while a launch has fewer than
+// kMinGroupItems items (the stage-1 chunk down to 4 K-groups, the stage-2
+// item down to one 256-row tile).
+constexpr int64_t kMinGroupItems = 1024;
+
+Grain group_grain(const Linear *ls, int n, const Shape &s) {
+    Grain g;
+    for (int pass = 0; pass < 8; ++pass) {
+        int64_t i1 = 0, i2 = 0, kc_min = kMaxKcf;
+        for (int j = 0; j < n; ++j) {
+            MLin m;
+            plan_linear(ls[j], s, true, &m, g);
+            i1 += items1_of(m);
+            i2 += m.n2;
+            kc_min = imin(kc_min, m.kcg);
+        }
+        bool changed = false;
+        if (fused1(s) && i1 < kMinGroupItems && kc_min > 4 && g.fused_bytes > 4096) {
+            g.fused_bytes /= 2;
+            changed = true;
+        }
+        if (i2 < kMinGroupItems && g.tiles2 > 1) {
+            g.tiles2 /= 2;
+            changed = true;
+        }
+        if (!changed) break;
+    }
+    return g;
+}
+
 size_t mfma_group_workspace_bytes(const Linear *ls, int n, int64_t T, int y_dtype) {
     Shape s;
     if (!shape_for(T, y_dtype, &s)) return 0;
     size_t need = 256 + rup256(sizeof(MLin) * n);
+    const Grain gr = group_grain(ls, n, s);
     int64_t i0 = 0, i1 = 0, iF = 0, i2 = 0;
     for (int j = 0; j < n; ++j) {
         MLin m;
-        need += plan_linear(ls[j], s, true, &m);
+        need += plan_linear(ls[j], s, true, &m, gr);
         i0 += items0_of(m);
         i1 += items1_of(m);
         iF += itemsF_of(m);
@@ -1502,11 +1541,12 @@ int mfma_group_prepare(const Linear *ls, int n, int64_t T, int y_dtype, void *ws
     MLin *table_dev = (MLin *)(w + 256);
     uint8_t *cur = w + 256 + rup256(sizeof(MLin) * n);
     std::vector<MLin> tab((size_t)n);
+    const Grain gr = group_grain(ls, n, hs->s);
     int64_t i0 = 0, i1 = 0, iF = 0, i2 = 0;
     int steps_max = 1;
     for (int j = 0; j < n; ++j) {
         MLin &m = tab[(size_t)j];
-        const size_t b = plan_linear(ls[j], hs->s, true, &m);
+        const size_t b = plan_linear(ls[j], hs->s, true, &m, gr);
         bind_ws(&m, ls[j], hs->s, cur);
         cur += b;
         m.item0 = i0;
