@@ -39,6 +39,7 @@
 //            paths back to back, so no plane is read twice.
 //   stage 2: item = (linear, block of output rows): each wave walks 64-row
 //            tiles, streaming the U planes of both paths into one accumulator set.
+#include <algorithm>
 #include <vector>
 
 #include "lb_internal.h"
@@ -119,6 +120,7 @@ struct MRun {
     int64_t base0, base1, baseF, base2;   // item of workgroup 0 in each launch (0: all items)
     const MLin *table;         // null: the single linear passed by value
     const int32_t *lin0, *lin1, *linF, *lin2;   // item -> linear, per launch
+    const int32_t *ord1, *ord2;  // workgroup -> item for stage 1 / stage 2 (largest first; null: identity)
 };
 
 __device__ __forceinline__ float ldexp2(float v, int e) { return __builtin_amdgcn_ldexpf(v, e); }
@@ -273,6 +275,13 @@ __device__ __forceinline__ MLin pick(const MRun &run, const MLin &single, const 
 }
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// The item a workgroup runs: launches of a group start their largest items
+// first (ord), so the last workgroups to start are short ones.
+__device__ __forceinline__ int64_t item_of(const int32_t *ord, int64_t base) {
+    const int64_t w = (int64_t)blockIdx.x + base;
+    return ord ? (int64_t)__builtin_amdgcn_readfirstlane(ord[w]) : w;
+}
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -447,7 +456,7 @@ template <int NL, int NB1>
 __global__ __launch_bounds__(kThreads) void k_stage1(MRun run, MLin single) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     using R = Rows<NL>;
-    const int64_t item = (int64_t)blockIdx.x + run.base1;
+    const int64_t item = item_of(run.ord1, run.base1);
     const MLin L = pick(run, single, run.lin1, item);
     const int64_t local = item - L.item1;
     const int rg = (int)(local % L.nrg);
@@ -615,7 +624,7 @@ template <int NL>
 __global__ __launch_bounds__(kThreads) void k_stage1f(MRun run, MLin single) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     using R = Rows<NL>;
-    const int64_t item = (int64_t)blockIdx.x + run.base1;
+    const int64_t item = item_of(run.ord1, run.base1);
     const MLin L = pick(run, single, run.lin1, item);
     const int64_t local = item - L.item1;
     const int c = (int)(local % L.nchunks);
@@ -870,7 +879,7 @@ template <int NL, int NB2>
 __global__ __launch_bounds__(kThreads) void k_stage2(MRun run, MLin single) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     using R = Rows<NL>;
-    const int64_t item = (int64_t)blockIdx.x + run.base2;
+    const int64_t item = item_of(run.ord2, run.base2);
     const MLin L = pick(run, single, run.lin2, item);
     const int64_t local = item - L.item2;
     const int T = run.T;
@@ -1020,7 +1029,7 @@ template <int NL, int NB2>
 __global__ __launch_bounds__(kThreads) void k_stage2r(MRun run, MLin single) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     using R = Rows<NL>;
-    const int64_t item = (int64_t)blockIdx.x + run.base2;
+    const int64_t item = item_of(run.ord2, run.base2);
     const MLin L = pick(run, single, run.lin2, item);
     const int64_t local = item - L.item2;
     const int T = run.T;
@@ -1528,6 +1537,7 @@ size_t mfma_group_workspace_bytes(const Linear *ls, int n, int64_t T, int y_dtyp
     }
     need += rup256((size_t)i0 * 4) + rup256((size_t)i1 * 4) + rup256((size_t)iF * 4) +
             rup256((size_t)i2 * 4);
+    need += rup256((size_t)i1 * 4) + rup256((size_t)i2 * 4);   // dispatch orders
     return need;
 }
 
@@ -1573,6 +1583,8 @@ int mfma_group_prepare(const Linear *ls, int n, int64_t T, int y_dtype, void *ws
     int32_t *lin1 = (int32_t *)((uint8_t *)lin0 + rup256((size_t)i0 * 4));
     int32_t *linF = (int32_t *)((uint8_t *)lin1 + rup256((size_t)i1 * 4));
     int32_t *lin2 = (int32_t *)((uint8_t *)linF + rup256((size_t)iF * 4));
+    int32_t *ord1 = (int32_t *)((uint8_t *)lin2 + rup256((size_t)i2 * 4));
+    int32_t *ord2 = (int32_t *)((uint8_t *)ord1 + rup256((size_t)i1 * 4));
     std::vector<int32_t> h0((size_t)i0), h1((size_t)i1), hF((size_t)iF), h2((size_t)i2);
     for (int j = 0; j < n; ++j) {
         const MLin &m = tab[(size_t)j];
@@ -1587,6 +1599,38 @@ int mfma_group_prepare(const Linear *ls, int n, int64_t T, int y_dtype, void *ws
         hipMemcpy(linF, hF.data(), (size_t)iF * 4, hipMemcpyHostToDevice) != hipSuccess ||
         hipMemcpy(lin2, h2.data(), (size_t)i2 * 4, hipMemcpyHostToDevice) != hipSuccess)
         return hip_status(hipGetLastError());
+    // dispatch orders: largest items first (bytes of sign planes each streams;
+    // ties keep item order), so a launch ends on short workgroups
+    {
+        const bool fz = fused1(hs->s);
+        std::vector<int64_t> c1((size_t)i1), c2((size_t)i2);
+        for (int j = 0; j < n; ++j) {
+            const MLin &m = tab[(size_t)j];
+            for (int64_t k = 0; k < items1_of(m); ++k) {
+                const int64_t c = k % m.nchunks;
+                const int64_t rg = fz ? (k / m.nchunks) % m.nrg : k % m.nrg;
+                const int64_t cc = fz ? c : (k / m.nrg) % m.nchunks;
+                const int64_t nkg = imin(m.kcg, m.kgv - cc * m.kcg);
+                const int64_t span = fz ? (int64_t)run.flush1 * kTile : kRG;
+                const int64_t rows = imin(span, m.r_p - rg * span);
+                c1[(size_t)(m.item1 + k)] = nkg * rows;
+            }
+            for (int64_t k = 0; k < m.n2; ++k) {
+                const int64_t tiles = imin(m.rows2 / kRG, cdiv(m.d_out - k * m.rows2, kRG));
+                c2[(size_t)(m.item2 + k)] = tiles * m.kgs;
+            }
+        }
+        auto order = [](const std::vector<int64_t> &cost) {
+            std::vector<int32_t> o(cost.size());
+            for (size_t i = 0; i < o.size(); ++i) o[i] = (int32_t)i;
+            std::stable_sort(o.begin(), o.end(), [&](int32_t a, int32_t b) { return cost[(size_t)a] > cost[(size_t)b]; });
+            return o;
+        };
+        const std::vector<int32_t> o1 = order(c1), o2 = order(c2);
+        if (hipMemcpy(ord1, o1.data(), (size_t)i1 * 4, hipMemcpyHostToDevice) != hipSuccess ||
+            hipMemcpy(ord2, o2.data(), (size_t)i2 * 4, hipMemcpyHostToDevice) != hipSuccess)
+            return hip_status(hipGetLastError());
+    }
     run.T = (int)T;
     run.x_dtype = ls[0].x_dtype;
     run.y_dtype = y_dtype;
@@ -1599,6 +1643,8 @@ int mfma_group_prepare(const Linear *ls, int n, int64_t T, int y_dtype, void *ws
     run.lin1 = lin1;
     run.linF = linF;
     run.lin2 = lin2;
+    run.ord1 = ord1;
+    run.ord2 = ord2;
     return LB_OK;
 }
 
