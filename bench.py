@@ -252,6 +252,8 @@ def main():
     ap.add_argument("--layers", type=int, default=0, help="stack depth (default: the workload's)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-prefill", action="store_true", help="skip the T=2048 prefill leg")
+    ap.add_argument("--no-single-layer", action="store_true",
+                    help="skip the cache-resident single-layer decode figure (e.g. under a profiler)")
     ap.add_argument("--prefill-tokens", type=int, default=2048)
     ap.add_argument("--prefill-only", action="store_true",
                     help="only run the T=2048 prefill leg and print its JSON")
@@ -323,7 +325,8 @@ def main():
     }
     del st
     torch.cuda.empty_cache()
-    out["decode_single_layer"] = single_layer_leg(w, T)
+    if not args.no_single_layer:
+        out["decode_single_layer"] = single_layer_leg(w, T)
     if not args.no_prefill and args.prefill_tokens > 32:
         try:
             out["prefill"] = prefill_leg(w, args.prefill_tokens, max(3, args.steps // 50))
