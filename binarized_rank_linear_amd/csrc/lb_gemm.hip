@@ -453,7 +453,9 @@ __global__ __launch_bounds__(kThreads, NBW == 4 ? 1 : 2) void k_gemm(GRun run, G
                 (uint32_t)(((wm * 128 + half * 64 + r) * ld_out + n) * osz);
             const int per = 16 / osz;
             if (chunky && n + per <= n_lim) {
-                __builtin_amdgcn_raw_buffer_store_b128(val, ro, (int)off, 0, 0);
+                // non-temporal: the outputs stream out instead of filling the L2
+                // that holds the activation rows other tiles still read
+                __builtin_amdgcn_raw_buffer_store_b128(val, ro, (int)off, 0, 2);
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
