@@ -405,10 +405,14 @@ int lb_grouped_run(void *ws, void *stream) {
         std::lock_guard<std::mutex> lk(g_groups_mu);
         auto it = g_groups.find(ws);
         if (it == g_groups.end()) return LB_EINVAL;
-        g = it->second;
+        GroupRecord &rec = it->second;
+        // whole-group kernels launch from the record itself, under the lock:
+        // their host state advances with every run (the decode pass numbers
+        // its runs)
+        if (rec.kind == GroupKind::Decode) return mfma_group_run(rec.state.data(), (hipStream_t)stream);
+        if (rec.kind == GroupKind::Gemm) return gemm_group_run(rec.state.data(), (hipStream_t)stream);
+        g = rec;
     }
-    if (g.kind == GroupKind::Decode) return mfma_group_run(g.state.data(), (hipStream_t)stream);
-    if (g.kind == GroupKind::Gemm) return gemm_group_run(g.state.data(), (hipStream_t)stream);
     void *lws = (char *)ws + 256;
     for (const lb_linear_desc &d : g.descs) {
         const int rc = lb_linear_forward(d.x, g.x_dtype, d.y, g.y_dtype, &d.w, d.d_in, d.d_out, d.r,
@@ -420,17 +424,13 @@ int lb_grouped_run(void *ws, void *stream) {
 
 int lb_grouped_run_stage(void *ws, int stage, void *stream) {
     if (stage != 1 && stage != 2) return LB_EINVAL;
-    GroupRecord g;
-    {
-        std::lock_guard<std::mutex> lk(g_groups_mu);
-        auto it = g_groups.find(ws);
-        if (it == g_groups.end()) return LB_EINVAL;
-        if (it->second.kind == GroupKind::Loop) return LB_EUNSUPPORTED;
-        g.kind = it->second.kind;
-        g.state = it->second.state;
-    }
-    if (g.kind == GroupKind::Gemm) return gemm_group_run(g.state.data(), (hipStream_t)stream, stage);
-    return mfma_group_run(g.state.data(), (hipStream_t)stream, stage);
+    std::lock_guard<std::mutex> lk(g_groups_mu);
+    auto it = g_groups.find(ws);
+    if (it == g_groups.end()) return LB_EINVAL;
+    GroupRecord &rec = it->second;
+    if (rec.kind == GroupKind::Loop) return LB_EUNSUPPORTED;
+    if (rec.kind == GroupKind::Gemm) return gemm_group_run(rec.state.data(), (hipStream_t)stream, stage);
+    return mfma_group_run(rec.state.data(), (hipStream_t)stream, stage);
 }
 
 }  // extern "C"

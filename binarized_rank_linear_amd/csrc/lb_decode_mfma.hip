@@ -69,6 +69,9 @@ constexpr int kWin2 = 8;                  // stage 2 (streaming form): plane loa
 constexpr int kWin1 = 8;                  // stage 1 (fused form): plane loads in flight per wave
 constexpr int kMaxKcf = 32;               // K-groups per fused stage-1 chunk (two 8-input pieces per thread)
 constexpr uint32_t kOOB = 0x7ffffff0u;    // a buffer offset past every range: reads as zero
+// Cache policy of a buffer access at device scope (sc1): coherent across the
+// XCDs' L2 caches, as agent-scope atomics are.
+constexpr int kDeviceScope = 16;
 constexpr int kHRows = kRG * kTilesPerItem2;   // output rows of one stage-2 item, at most
 constexpr int kYStage = 16 * 1024;        // LDS for k_stage2r's collected outputs, at most
 
@@ -110,6 +113,11 @@ struct MLin {
     uint8_t *tb;          // stage-2 operands, compact: [kgs][NB2][R2][kRec]
 };
 
+// items of a linear in each launch
+__host__ __device__ inline int64_t items0_of(const MLin &m) { return (int64_t)m.P * m.nprep; }
+__host__ __device__ inline int64_t items1_of(const MLin &m) { return (int64_t)m.P * m.nchunks * m.nrg; }
+__host__ __device__ inline int64_t itemsF_of(const MLin &m) { return ((int64_t)m.kgs + 1) / 2; }
+
 struct MRun {
     int T, x_dtype, y_dtype;
     int ops2;                  // stage-2 operands (steps) the LDS holds at once
@@ -121,6 +129,11 @@ struct MRun {
     const MLin *table;         // null: the single linear passed by value
     const int32_t *lin0, *lin1, *linF, *lin2;   // item -> linear, per launch
     const int32_t *ord1, *ord2;  // workgroup -> item for stage 1 / stage 2 (largest first; null: identity)
+    // the one-launch pass (k_pass)
+    const int32_t *ordP1, *ordP2;  // workgroup -> stage-1 item, (workgroup - items1) -> stage-2 item
+    uint32_t *arrive, *ready;      // per linear: stage-1 items counted in, run number of its operands
+    uint32_t epoch;                // this run's number (from 0)
+    int pass;                      // 1: a full run is one k_pass launch
 };
 
 __device__ __forceinline__ float ldexp2(float v, int e) { return __builtin_amdgcn_ldexpf(v, e); }
@@ -344,6 +357,7 @@ __device__ __forceinline__ void store4(const OutBuf &o, int64_t e0, int64_t row,
 // Compact operands [nops][R records] of src -> LDS operands at dst.  The first
 // kPreVec vectors of each thread were loaded into pre[] before the caller's
 // plane loads; any remainder is copied here.
+template <int AUX = 0>
 __device__ __forceinline__ void expand_ops(uint8_t *dst, const uint8_t *src, int nops, int R,
                                            const v4u (&pre)[kPreVec]) {
     const int vecs = nops * R * kRec / 16;
@@ -352,19 +366,36 @@ __device__ __forceinline__ void expand_ops(uint8_t *dst, const uint8_t *src, int
         const int i = j * kThreads + (int)threadIdx.x;
         if (i < vecs) expand_vec(dst, i, R, pre[j]);
     }
+    if (vecs <= kPreVec * kThreads) return;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(src, (int64_t)vecs * 16);
     for (int i = kPreVec * kThreads + (int)threadIdx.x; i < vecs; i += kThreads)
-        expand_vec(dst, i, R, ((const v4u *)src)[i]);
+        expand_vec(dst, i, R, __builtin_amdgcn_raw_buffer_load_b128(r, i * 16, 0, AUX));
 }
 
 // Buffer loads (not flat ones: the compiler cannot count flat loads among the
 // vector-memory operations in flight and would wait for all of them), issued
 // unconditionally; vectors past the end read as zeros.
+template <int AUX = 0>
 __device__ __forceinline__ void preload_ops(const uint8_t *src, int nops, int R, v4u (&pre)[kPreVec]) {
     const int vecs = nops * R * kRec / 16;
     const __amdgpu_buffer_rsrc_t r = make_rsrc(src, (int64_t)vecs * 16);
 #pragma unroll
     for (int j = 0; j < kPreVec; ++j)
-        pre[j] = __builtin_amdgcn_raw_buffer_load_b128(r, (j * kThreads + (int)threadIdx.x) * 16, 0, 0);
+        pre[j] = __builtin_amdgcn_raw_buffer_load_b128(r, (j * kThreads + (int)threadIdx.x) * 16, 0, AUX);
+}
+
+constexpr uint32_t kSpinLimit = 1u << 20;
+constexpr int kFlagStride = 64;           // words between two linears' counters (own 256-byte lines)
+
+// Thread 0 polls *flag (device scope) until it reads `want` or kSpinLimit
+// polls have gone by; the workgroup waits at a barrier meanwhile.
+__device__ __forceinline__ void wait_ready(const uint32_t *flag, uint32_t want) {
+    if (threadIdx.x == 0) {
+        uint32_t n = 0;
+        while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != want && ++n < kSpinLimit)
+            __builtin_amdgcn_s_sleep(2);
+    }
+    __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
@@ -614,18 +645,16 @@ __device__ __forceinline__ void emit_piece(const float (&v)[8], uint8_t *rec0, i
 
 // Item = (linear, path, chunk of up to kMaxKcf K-groups of d_in).  The
 // workgroup turns g_p (.) x over its chunk into compact limb records in LDS
-// (loads of g and of token 0 go out before the first plane loads, so only
-// their own latency is waited for), then wave w streams K-groups
+// (g and token 0 of x are loaded first), then wave w streams K-groups
 // [w*sub, (w+1)*sub) of the chunk across every 64-latent tile with kWin1
 // plane loads in flight (rotating register slots, as k_stage2r).  At each tile
 // end the four waves' partial sums meet in LDS and are added in wave order:
 // one partial per (chunk, token, latent), in a fixed summation order.
-template <int NL>
-__global__ __launch_bounds__(kThreads) void k_stage1f(MRun run, MLin single) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+// COHERENT: the partial sums are read back inside the same launch by another
+// workgroup (the one-launch pass), so they are stored at device scope.
+template <int NL, bool COHERENT>
+__device__ __forceinline__ void stage1f_item(const MRun &run, const MLin &L, int64_t item, uint8_t *smem) {
     using R = Rows<NL>;
-    const int64_t item = item_of(run.ord1, run.base1);
-    const MLin L = pick(run, single, run.lin1, item);
     const int64_t local = item - L.item1;
     const int c = (int)(local % L.nchunks);
     const int rg = (int)((local / L.nchunks) % L.nrg);
@@ -684,9 +713,16 @@ __global__ __launch_bounds__(kThreads) void k_stage1f(MRun run, MLin single) {
         lk = wrap ? 0 : lk + 1;
         return o;
     };
+    // The standalone kernel issues its first plane loads now, so their latency
+    // overlaps the limb work below.  Inside the one-launch pass they go out
+    // after it: held through the limb work they would take 32 more registers,
+    // and the pass, which holds stage 2 as well, would fit one workgroup less
+    // per CU.
     v4u slot[kWin1];
+    if constexpr (!COHERENT) {
 #pragma unroll
-    for (int k = 0; k < kWin1; ++k) slot[k] = load_rows(rv, next_off());
+        for (int k = 0; k < kWin1; ++k) slot[k] = load_rows(rv, next_off());
+    }
 
     // ---- limbs of g (.) x into the records ------------------------------------
     // piece pc: K-group pc/16 of the chunk, block (pc/4)%4, quarter pc%4; a
@@ -740,6 +776,10 @@ __global__ __launch_bounds__(kThreads) void k_stage1f(MRun run, MLin single) {
     lds_meet();
 
     // ---- stream ------------------------------------------------------------
+    if constexpr (COHERENT) {
+#pragma unroll
+        for (int k = 0; k < kWin1; ++k) slot[k] = load_rows(rv, next_off());
+    }
     v4f acc[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc[m] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -799,73 +839,121 @@ __global__ __launch_bounds__(kThreads) void k_stage1f(MRun run, MLin single) {
         const float *q = red + (size_t)k * kWaves * per + rem;
         const float sum = ((q[0] + q[per]) + q[2 * per]) + q[3 * per];
         const uint32_t po = (uint32_t)((((int64_t)c * T + n) * Rtot + (int64_t)p * L.r_p + row) * 4);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sum), rpart, row < L.r_p ? po : kOOB, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sum), rpart, row < L.r_p ? po : kOOB, 0,
+                                              COHERENT ? kDeviceScope : 0);
     }
+}
+
+template <int NL>
+__global__ __launch_bounds__(kThreads) void k_stage1f(MRun run, MLin single) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int64_t item = item_of(run.ord1, run.base1);
+    stage1f_item<NL, false>(run, pick(run, single, run.lin1, item), item, smem);
 }
 
 // ---------------------------------------------------------------------------
 // latents: t = l (.) sum over chunks, as compact stage-2 operands
 // ---------------------------------------------------------------------------
 
-template <int NL, int NB2>
-__global__ __launch_bounds__(kThreads) void k_latent(MRun run, MLin single) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+// K-groups kg_first .. kg_first+kg_count-1 of a linear's stage-2 operands.
+// Lanes map to (unit = token x plane of 32 latents, latent); each lane
+// gathers the chunk partials of up to kLU units at once.  A latent sums its
+// partials slice by slice: the kLC chunks of a slice are loaded together (all
+// in flight: unconditional buffer loads, chunks past the end read as zeros)
+// and added in chunk order from zero, and the slice sums in slice order from
+// zero.  COHERENT: the partial sums were written by other workgroups of the
+// same launch and the operands are read by others, so both go at device
+// scope.
+constexpr int kLU = 4, kLC = 8;   // units per lane, chunks per slice
+template <int NL, int NB2, bool COHERENT>
+__device__ __forceinline__ void latent_item(const MRun &run, const MLin &L, int kg_first, int kg_count,
+                                            uint8_t *smem) {
     using R = Rows<NL>;
-    const int64_t item = (int64_t)blockIdx.x + run.baseF;
-    const MLin L = pick(run, single, run.linF, item);
-    const int64_t local = item - L.itemF;
+    constexpr int AUX = COHERENT ? kDeviceScope : 0;
     const int T = run.T;
     const int lane = threadIdx.x & 63, wave = wave_id();
-    const int kg_first = (int)local * 2;                          // 2 K-groups = 8 planes
-    const int kg_count = (int)imin(2, L.kgs - kg_first);
     const int opb = L.R2 * kRec;
+    const int opsz = kg_count * NB2 * opb;                        // bytes of the staged operands
     // every row of these operands that no (token, path, limb) fills reads as zero
     {
         uint32_t *w = (uint32_t *)smem;
-        const int words = kg_count * NB2 * opb / 4;
-        for (int i = threadIdx.x; i < words; i += kThreads) w[i] = 0u;
+        for (int i = threadIdx.x; i < opsz / 4; i += kThreads) w[i] = 0u;
     }
     __syncthreads();
     const int64_t Rtot = (int64_t)L.P * L.r_p;
     const int blocks = kg_count * 4;                              // planes, one path each
     const int units = T * blocks;
-    const int64_t cs = (int64_t)T * Rtot;
-    for (int u0 = 2 * wave; u0 < units; u0 += 2 * kWaves) {
-        const int u = u0 + (lane >> 5);
-        const bool ok = u < units;
-        const int n = ok ? u / blocks : 0;
-        const int blk = ok ? u % blocks : 0;
-        const int e = blk * 32 + (lane & 31);                     // element in the two K-groups
-        const int pl = kg_first * 4 + blk;                        // plane over both paths
-        const int p = pl / L.kw_u;                                // uniform per wave half
-        const int k = (pl - p * L.kw_u) * 32 + (lane & 31);       // latent of path p
-        float v = 0.0f;
-        if (ok && p < L.P && k < L.r_p) {
-            // chunk order fixed; loads of four chunks in flight at once
-            float sum = 0.0f;
-            const float *pk = L.part + (int64_t)n * Rtot + (int64_t)p * L.r_p + k;
-            int cc = 0;
-            for (; cc + 4 <= L.nchunks; cc += 4) {
-                const float a0 = pk[cc * cs], a1 = pk[(cc + 1) * cs], a2 = pk[(cc + 2) * cs],
-                            a3 = pk[(cc + 3) * cs];
-                sum += a0;
-                sum += a1;
-                sum += a2;
-                sum += a3;
-            }
-            for (; cc < L.nchunks; ++cc) sum += pk[cc * cs];
-            v = f16_to_f32(L.l[(int64_t)p * L.r_p + k]) * sum;
+    const int64_t cs = (int64_t)T * Rtot;                         // floats per chunk
+    const int ns = (int)cdiv(L.nchunks, kLC);                     // slices
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(L.part, (int64_t)L.nchunks * cs * 4);
+    constexpr int step = 2 * kWaves;                              // wave halves of the workgroup
+    for (int ub = 2 * wave; ub < units; ub += step * kLU) {      // uniform per wave
+        uint32_t base[kLU];
+        bool live[kLU];
+#pragma unroll
+        for (int q = 0; q < kLU; ++q) {
+            const int u = ub + q * step + (lane >> 5);
+            const bool ok = u < units;
+            const int n = ok ? u / blocks : 0;
+            const int pl = kg_first * 4 + (ok ? u % blocks : 0);  // plane over both paths
+            const int p = pl / L.kw_u;                            // uniform per wave half
+            const int k = (pl - p * L.kw_u) * 32 + (lane & 31);   // latent of path p
+            live[q] = ok && p < L.P && k < L.r_p;
+            base[q] = live[q] ? (uint32_t)(((int64_t)n * Rtot + (int64_t)p * L.r_p + k) * 4) : 0u;
         }
-        const int row = (n % R::TPM2) * R::S2 + (p < L.P ? p : 0) * NL;
-        uint8_t *op = smem + ((e >> 7) * NB2 + n / R::TPM2) * opb + row * kRec;
-        emit_limbs<NL>(v, op + rec_offset(e & 127), op + 128 + ((e & 127) >> 5), ok && p < L.P,
-                       (e & 31) == 0);
+        float sum[kLU];
+#pragma unroll
+        for (int q = 0; q < kLU; ++q) sum[q] = 0.0f;
+        for (int sl = 0; sl < ns; ++sl) {                         // uniform
+            float a[kLU][kLC];
+#pragma unroll
+            for (int q = 0; q < kLU; ++q)
+#pragma unroll
+                for (int t = 0; t < kLC; ++t) {
+                    const int c = sl * kLC + t;
+                    a[q][t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                        rp, live[q] && c < L.nchunks ? base[q] + (uint32_t)((int64_t)c * cs * 4) : kOOB, 0, AUX));
+                }
+#pragma unroll
+            for (int q = 0; q < kLU; ++q) {
+                float x = 0.0f;
+#pragma unroll
+                for (int t = 0; t < kLC; ++t) x += a[q][t];
+                sum[q] += x;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < kLU; ++q) {
+            const int u = ub + q * step + (lane >> 5);
+            const bool ok = u < units;
+            const int n = ok ? u / blocks : 0;
+            const int blk = ok ? u % blocks : 0;
+            const int e = blk * 32 + (lane & 31);                 // element in the K-group range
+            const int pl = kg_first * 4 + blk;
+            const int p = pl / L.kw_u;
+            const int k = (pl - p * L.kw_u) * 32 + (lane & 31);
+            const float v = live[q] ? f16_to_f32(L.l[(int64_t)p * L.r_p + k]) * sum[q] : 0.0f;
+            const int row = (n % R::TPM2) * R::S2 + (p < L.P ? p : 0) * NL;
+            uint8_t *op = smem + ((e >> 7) * NB2 + n / R::TPM2) * opb + row * kRec;
+            emit_limbs<NL>(v, op + rec_offset(e & 127), op + 128 + ((e & 127) >> 5), ok && p < L.P,
+                           (e & 31) == 0);
+        }
     }
     __syncthreads();
-    const int4 *src = (const int4 *)smem;
-    int4 *dst = (int4 *)(L.tb + (int64_t)kg_first * NB2 * opb);
-    const int vecs = kg_count * NB2 * opb / 16;
-    for (int i = threadIdx.x; i < vecs; i += kThreads) dst[i] = src[i];
+    const v4u *src = (const v4u *)smem;
+    const int vecs = opsz / 16;
+    const __amdgpu_buffer_rsrc_t rt = make_rsrc(L.tb + (int64_t)kg_first * NB2 * opb, (int64_t)vecs * 16);
+    for (int i = threadIdx.x; i < vecs; i += kThreads)
+        __builtin_amdgcn_raw_buffer_store_b128(src[i], rt, i * 16, 0, AUX);
+}
+
+template <int NL, int NB2>
+__global__ __launch_bounds__(kThreads) void k_latent(MRun run, MLin single) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int64_t item = (int64_t)blockIdx.x + run.baseF;
+    const MLin L = pick(run, single, run.linF, item);
+    const int kg_first = (int)(item - L.itemF) * 2;               // 2 K-groups = 8 planes per item
+    latent_item<NL, NB2, false>(run, L, kg_first, (int)imin(2, L.kgs - kg_first), smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -1025,12 +1113,13 @@ __global__ __launch_bounds__(kThreads) void k_stage2(MRun run, MLin single) {
 // register is copied and no wait other than the one for the oldest load is
 // needed.  Loads are unconditional (offsets past the range read zeros).  The
 // operands of all steps and h of the item's rows sit in LDS for the whole item.
-template <int NL, int NB2>
-__global__ __launch_bounds__(kThreads) void k_stage2r(MRun run, MLin single) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+// COHERENT: the operands were written earlier in the same launch (the
+// one-launch pass); `ready` is the linear's flag, and the workgroup waits for
+// it to read the run's number before it loads them, at device scope.
+template <int NL, int NB2, bool COHERENT>
+__device__ __forceinline__ void stage2r_item(const MRun &run, const MLin &L, int64_t item, uint8_t *smem,
+                                             const uint32_t *ready) {
     using R = Rows<NL>;
-    const int64_t item = item_of(run.ord2, run.base2);
-    const MLin L = pick(run, single, run.lin2, item);
     const int64_t local = item - L.item2;
     const int T = run.T;
     const int lane = threadIdx.x & 63, wave = wave_id();
@@ -1041,7 +1130,6 @@ __global__ __launch_bounds__(kThreads) void k_stage2r(MRun run, MLin single) {
     const int64_t row_begin = local * L.rows2;
     const int tiles = (int)imin(L.rows2 / kRG, cdiv(L.d_out - row_begin, kRG));
     const int total = tiles * steps;               // this wave's stream (uniform)
-    const int opb = L.R2 * kRec;
     const OutBuf ob = out_buf(L.y, run.y_dtype, (int64_t)T * L.d_out, L.d_out);
     uint8_t *ops = smem;                                          // [steps][NB2] operands
     uint16_t *hs = (uint16_t *)(smem + run.ops2 * NB2 * kOpS);   // [2][kHRows] fp16 h
@@ -1053,8 +1141,9 @@ __global__ __launch_bounds__(kThreads) void k_stage2r(MRun run, MLin single) {
 
     // operands and h first, as buffer loads (counted precisely, so the LDS
     // fill below waits for these only, not for the plane loads behind them)
+    if (COHERENT) wait_ready(ready, run.epoch + 1u);
     v4u pre[kPreVec];
-    preload_ops(L.tb, steps * NB2, L.R2, pre);
+    preload_ops<COHERENT ? kDeviceScope : 0>(L.tb, steps * NB2, L.R2, pre);
     // h of the item's rows: thread t holds 8 consecutive fp16 of path t / (kThreads/2)
     const int hp = (int)threadIdx.x / (kThreads / 2), hr = ((int)threadIdx.x % (kThreads / 2)) * 8;
     const __amdgpu_buffer_rsrc_t rh = make_rsrc(L.h, (int64_t)L.P * L.d_out * 2);
@@ -1084,7 +1173,7 @@ __global__ __launch_bounds__(kThreads) void k_stage2r(MRun run, MLin single) {
     for (int k = 0; k < kWin2; ++k) slot[k] = load_rows(ru, off_of(k));
 
     // operands of every step and h of the item's rows into LDS, shared by the 4 waves
-    expand_ops(ops, L.tb, steps * NB2, L.R2, pre);
+    expand_ops<COHERENT ? kDeviceScope : 0>(ops, L.tb, steps * NB2, L.R2, pre);
 #pragma unroll
     for (int k = 0; k < kHRows / (kThreads / 2) / 8; ++k) {
         const int rl = hr + k * (kThreads / 2) * 8;
@@ -1207,6 +1296,69 @@ __global__ __launch_bounds__(kThreads) void k_stage2r(MRun run, MLin single) {
                 }
             }
         }
+    }
+}
+
+template <int NL, int NB2>
+__global__ __launch_bounds__(kThreads) void k_stage2r(MRun run, MLin single) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int64_t item = item_of(run.ord2, run.base2);
+    stage2r_item<NL, NB2, false>(run, pick(run, single, run.lin2, item), item, smem, nullptr);
+}
+
+// ---------------------------------------------------------------------------
+// the one-launch pass: stage 1, latents and stage 2 of a group in one grid
+// ---------------------------------------------------------------------------
+
+// Workgroups [0, items1) run stage-1 items, the rest stage-2 items.  A linear's
+// stage-2 items need its latents, so the hand-off is per linear, inside the
+// launch:
+//   - a stage-1 workgroup stores its partial sums at device scope, waits until
+//     they are complete, and counts itself in arrive[linear];
+//   - the workgroup that completes the count (the last of the linear's stage-1
+//     items in this run) sums the partials into the stage-2 operands (the
+//     latent step), stores them at device scope and sets ready[linear] to the
+//     run's number;
+//   - a stage-2 workgroup waits for that number before it loads the operands.
+// Device-scope accesses bypass the non-coherent caches of the other XCDs, so
+// no cache-wide write-back or invalidation is needed.  Workgroups start in
+// index order, so when a stage-2 workgroup runs, every stage-1 workgroup has
+// started already; those never wait, so every wait ends.  The wait is also
+// bounded (kSpinLimit polls); past it the workgroup goes on and its outputs
+// are wrong, but the launch still ends.
+// The counters keep counting across runs: after run e (from 0) arrive[j] is
+// (e + 1) * items1(j), so the completing workgroup is the one that reads
+// (e + 1) * items1(j) - 1 before its increment.
+template <int NL, int NB2>
+__global__ __launch_bounds__(kThreads) void k_pass(MRun run, MLin single) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    __shared__ uint32_t s_count;
+    const int64_t b = blockIdx.x;
+    if (b < run.items1) {
+        const int64_t item = __builtin_amdgcn_readfirstlane(run.ordP1[b]);
+        const int j = run.table ? __builtin_amdgcn_readfirstlane(run.lin1[item]) : 0;
+        const MLin L = pick(run, single, run.lin1, item);
+        stage1f_item<NL, true>(run, L, item, smem);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // this wave's partial sums are stored
+        __syncthreads();
+        if (threadIdx.x == 0)
+            s_count = __hip_atomic_fetch_add(run.arrive + j * kFlagStride, 1u, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        const uint32_t n1 = (uint32_t)items1_of(L);
+        if (s_count + 1u == (run.epoch + 1u) * n1) {                // uniform
+            latent_item<NL, NB2, true>(run, L, 0, L.kgs, smem);    // all of the linear's K-groups
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's operands are stored
+            __syncthreads();
+            if (threadIdx.x == 0)
+                __hip_atomic_store(run.ready + j * kFlagStride, run.epoch + 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+    } else {
+        const int64_t item = __builtin_amdgcn_readfirstlane(run.ordP2[b - run.items1]);
+        const int j = run.table ? __builtin_amdgcn_readfirstlane(run.lin2[item]) : 0;
+        stage2r_item<NL, NB2, true>(run, pick(run, single, run.lin2, item), item, smem,
+                                    run.ready + j * kFlagStride);
     }
 }
 
@@ -1345,9 +1497,6 @@ void bind_ws(MLin *m, const Linear &a, const Shape &s, uint8_t *ws) {
     m->tb = ws + part + pa;
 }
 
-int64_t items0_of(const MLin &m) { return (int64_t)m.P * m.nprep; }
-int64_t items1_of(const MLin &m) { return (int64_t)m.P * m.nchunks * m.nrg; }
-int64_t itemsF_of(const MLin &m) { return cdiv(m.kgs, 2); }
 
 // LDS of each kernel, given the largest per-linear figures of a launch.
 struct Lds {
@@ -1488,16 +1637,46 @@ struct MGroupHost {
     Shape s;
     MRun run;
     Lds lds;
+    size_t lds_pass;     // dynamic LDS of k_pass
+    uint32_t epoch;      // number of the next one-launch run
+    int64_t n1_max;      // most stage-1 items of one linear
+    int n;               // linears
 };
+
+// k_pass: stage-2 items of the linears whose stage-1 items start among the last
+// kLateItems of the launch's stage-1 order go after all other stage-2 items
+// (those are ready by the time they start), so few workgroups wait.
+constexpr int64_t kLateItems = 1024;
 
 // Items sized for large stacks leave a small group (one layer) with a few
 // dozen workgroups; halve the grain while a launch has fewer than
-// kMinGroupItems items (the stage-1 chunk down to 4 K-groups, the stage-2
-// item down to one 256-row tile).
+// kMinGroupItems items (the stage-1 chunk down to a floor of K-groups, the
+// stage-2 item down to one 256-row tile).
 constexpr int64_t kMinGroupItems = 1024;
+
+// The one-launch pass sums each linear's chunk partials in one workgroup (the
+// last of its stage-1 items), a few loads per chunk in sequence: small groups
+// keep chunks of at least kPassMinKcg K-groups there, where the three-launch
+// form (which spreads that sum over many workgroups) goes down to 4.
+constexpr int kPassMinKcg = 16;
+
+// Whether a group runs as one launch (k_pass): the fused stage 1 and a stage 2
+// whose operands fit the LDS (the K-groups, and so that test, do not depend on
+// the grain).
+bool pass_form(const Linear *ls, int n, const Shape &s) {
+    if (!fused1(s)) return false;
+    int steps_max = 1;
+    for (int j = 0; j < n; ++j) {
+        MLin m;
+        plan_linear(ls[j], s, true, &m);
+        steps_max = (int)imax(steps_max, m.kgs);
+    }
+    return dma2_for(s, steps_max);
+}
 
 Grain group_grain(const Linear *ls, int n, const Shape &s) {
     Grain g;
+    const int kc_floor = pass_form(ls, n, s) ? kPassMinKcg : 4;
     for (int pass = 0; pass < 8; ++pass) {
         int64_t i1 = 0, i2 = 0, kc_min = kMaxKcf;
         for (int j = 0; j < n; ++j) {
@@ -1508,7 +1687,7 @@ Grain group_grain(const Linear *ls, int n, const Shape &s) {
             kc_min = imin(kc_min, m.kcg);
         }
         bool changed = false;
-        if (fused1(s) && i1 < kMinGroupItems && kc_min > 4 && g.fused_bytes > 4096) {
+        if (fused1(s) && i1 < kMinGroupItems && kc_min > kc_floor && g.fused_bytes > 4096) {
             g.fused_bytes /= 2;
             changed = true;
         }
@@ -1538,6 +1717,8 @@ size_t mfma_group_workspace_bytes(const Linear *ls, int n, int64_t T, int y_dtyp
     need += rup256((size_t)i0 * 4) + rup256((size_t)i1 * 4) + rup256((size_t)iF * 4) +
             rup256((size_t)i2 * 4);
     need += rup256((size_t)i1 * 4) + rup256((size_t)i2 * 4);   // dispatch orders
+    need += rup256((size_t)i1 * 4) + rup256((size_t)i2 * 4);   // dispatch orders of k_pass
+    need += 2 * (size_t)n * kFlagStride * 4;                   // arrive, ready
     return need;
 }
 
@@ -1585,6 +1766,10 @@ int mfma_group_prepare(const Linear *ls, int n, int64_t T, int y_dtype, void *ws
     int32_t *lin2 = (int32_t *)((uint8_t *)linF + rup256((size_t)iF * 4));
     int32_t *ord1 = (int32_t *)((uint8_t *)lin2 + rup256((size_t)i2 * 4));
     int32_t *ord2 = (int32_t *)((uint8_t *)ord1 + rup256((size_t)i1 * 4));
+    int32_t *ordP1 = (int32_t *)((uint8_t *)ord2 + rup256((size_t)i2 * 4));
+    int32_t *ordP2 = (int32_t *)((uint8_t *)ordP1 + rup256((size_t)i1 * 4));
+    uint32_t *arrive = (uint32_t *)((uint8_t *)ordP2 + rup256((size_t)i2 * 4));
+    uint32_t *ready = arrive + (size_t)n * kFlagStride;
     std::vector<int32_t> h0((size_t)i0), h1((size_t)i1), hF((size_t)iF), h2((size_t)i2);
     for (int j = 0; j < n; ++j) {
         const MLin &m = tab[(size_t)j];
@@ -1630,7 +1815,27 @@ int mfma_group_prepare(const Linear *ls, int n, int64_t T, int y_dtype, void *ws
         if (hipMemcpy(ord1, o1.data(), (size_t)i1 * 4, hipMemcpyHostToDevice) != hipSuccess ||
             hipMemcpy(ord2, o2.data(), (size_t)i2 * 4, hipMemcpyHostToDevice) != hipSuccess)
             return hip_status(hipGetLastError());
+        // k_pass: stage-1 items linear by linear (a linear's latents are ready
+        // early); stage-2 items of the early linears largest first, then those
+        // of the late ones, largest first
+        std::vector<int32_t> p1((size_t)i1), p2;
+        for (size_t i = 0; i < p1.size(); ++i) p1[i] = (int32_t)i;
+        std::vector<int32_t> early, late;
+        for (size_t i = 0; i < o2.size(); ++i) {
+            const MLin &m = tab[(size_t)h2[(size_t)o2[i]]];
+            (m.item1 + items1_of(m) > i1 - kLateItems ? late : early).push_back(o2[i]);
+        }
+        p2 = early;
+        p2.insert(p2.end(), late.begin(), late.end());
+        if (hipMemcpy(ordP1, p1.data(), (size_t)i1 * 4, hipMemcpyHostToDevice) != hipSuccess ||
+            hipMemcpy(ordP2, p2.data(), (size_t)i2 * 4, hipMemcpyHostToDevice) != hipSuccess ||
+            hipMemset(arrive, 0, (size_t)n * kFlagStride * 4 * 2) != hipSuccess)
+            return hip_status(hipGetLastError());
     }
+    hs->n1_max = 1;
+    for (int j = 0; j < n; ++j) hs->n1_max = imax(hs->n1_max, items1_of(tab[(size_t)j]));
+    hs->epoch = 0;
+    hs->n = n;
     run.T = (int)T;
     run.x_dtype = ls[0].x_dtype;
     run.y_dtype = y_dtype;
@@ -1645,18 +1850,77 @@ int mfma_group_prepare(const Linear *ls, int n, int64_t T, int y_dtype, void *ws
     run.lin2 = lin2;
     run.ord1 = ord1;
     run.ord2 = ord2;
+    run.ordP1 = ordP1;
+    run.ordP2 = ordP2;
+    run.arrive = arrive;
+    run.ready = ready;
+    // one launch per run when stage 1 is the fused form and stage 2 k_stage2r
+    run.pass = fused1(hs->s) && run.dma2 && i1 > 0 && i2 > 0 ? 1 : 0;
+    hs->lds_pass = 0;
+    if (run.pass) {
+        const size_t l2 = (size_t)run.ops2 * hs->s.NB2 * kOpS + 2 * kHRows * 2 +
+                          (run.ystage ? (size_t)T * kHRows * (y_dtype == LB_BF16 ? 2 : 4) : 0);
+        size_t lat_all = 0;                 // the completing workgroup builds all K-groups at once
+        for (int j = 0; j < n; ++j)
+            lat_all = std::max(lat_all, (size_t)tab[(size_t)j].kgs * hs->s.NB2 * tab[(size_t)j].R2 * kRec);
+        hs->lds_pass = std::max(std::max(hs->lds.s1, lat_all), l2);
+        if (hs->lds_pass > 160 * 1024 - 64) run.pass = 0;
+    }
     return LB_OK;
 }
 
 size_t mfma_group_state_bytes() { return sizeof(MGroupHost); }
 
+__global__ void k_zero_words(uint32_t *a, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        a[i] = 0u;
+}
+
+template <int NL, int NB2>
+int launch_pass(const MRun &run, size_t lds, hipStream_t st) {
+    static bool raised = false;        // once per instantiation (idempotent if raced)
+    if (!raised) {
+        if (hipFuncSetAttribute((const void *)k_pass<NL, NB2>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                160 * 1024 - 64) != hipSuccess)
+            return hip_status(hipGetLastError());
+        raised = true;
+    }
+    MLin dummy{};
+    k_pass<NL, NB2><<<(unsigned)(run.items1 + run.items2), kThreads, lds, st>>>(run, dummy);
+    return last_launch_status();
+}
+
 int mfma_group_run(const void *host_state, hipStream_t st, int stage_mask) {
-    const MGroupHost *hs = (const MGroupHost *)host_state;
-    const MRun &r = hs->run;
+    // the run number advances with every one-launch run (the state is the
+    // group's own; runs of one group are issued one at a time)
+    MGroupHost *hs = (MGroupHost *)const_cast<void *>(host_state);
+    MRun &r = hs->run;
     // every launch of a group looks its items up in these tables
     if (!r.table || (r.items0 > 0 && !r.lin0) || (r.items1 > 0 && !r.lin1) || (r.itemsF > 0 && !r.linF) ||
         (r.items2 > 0 && !r.lin2))
         return LB_EINVAL;
+    if (stage_mask == 3 && r.pass) {
+        if (!r.ordP1 || !r.ordP2 || !r.arrive || !r.ready) return LB_EINVAL;
+        // the counters reach (epoch + 1) * items1 of a linear: start over
+        // before that leaves 31 bits (arrive and ready are contiguous)
+        if ((uint64_t)(hs->epoch + 1) * (uint64_t)hs->n1_max >= (1ull << 31)) {
+            const int64_t words = (int64_t)hs->n * kFlagStride * 2;
+            k_zero_words<<<(unsigned)imin(1024, cdiv(words, 256)), 256, 0, st>>>(r.arrive, words);
+            if (int rc = last_launch_status()) return rc;
+            hs->epoch = 0;
+        }
+        r.epoch = hs->epoch;
+        int rc = LB_EUNSUPPORTED;
+        const int key = hs->s.NL * 10 + hs->s.NB2;
+        switch (key) {
+            case 21: rc = launch_pass<2, 1>(r, hs->lds_pass, st); break;
+            case 22: rc = launch_pass<2, 2>(r, hs->lds_pass, st); break;
+            case 31: rc = launch_pass<3, 1>(r, hs->lds_pass, st); break;
+            case 32: rc = launch_pass<3, 2>(r, hs->lds_pass, st); break;
+        }
+        if (rc == LB_OK) ++hs->epoch;
+        return rc;
+    }
     MLin dummy{};
     return launch_shape(hs->s, hs->run, dummy, hs->lds, st, stage_mask);
 }

@@ -133,3 +133,51 @@ def test_group_run_matches_staged_run(key, T, out):
                                staged[L][i].view(torch.int16) if odt == torch.bfloat16
                                else staged[L][i].view(torch.int32)), (L, i)
     st.group.release()
+
+
+@pytest.mark.parametrize("key,T,out", [("c3", 3, "bf16"), ("c5", 6, "bf16"), ("c5", 4, "f32"), ("c5", 1, "f32")])
+def test_pass_reads_each_runs_inputs(key, T, out):
+    """The one-launch pass hands each run's latents to that run's stage 2:
+    with other activations between runs, every run equals the staged run of
+    its own inputs bit for bit (a stale hand-off would repeat the previous
+    run's outputs)."""
+    torch = torch_or_skip()
+    from binarized_rank_linear_amd.stack import LayerStack
+    w = synth.WORKLOADS[key]
+    say("pass inputs", key, "T", T, out)
+
+    def make(L, i, di, do, rp, P):
+        return synth.device_layer(synth.layer_seed(L, i) + 2000, di, do, rp, P)
+
+    st = LayerStack([(s.name, s.d_in, s.d_out) for s in w.linears], 2, w.b_num, w.b_den, w.residual, make)
+    widths = sorted({s.d_in for s in w.linears})
+    src = [{d: synth.device_activations(synth.activation_seed(d) + 31 * k, T, d, w.dtype) for d in widths}
+           for k in range(2)]
+    xs = {d: src[0][d].clone() for d in widths}
+    odt = torch.bfloat16 if out == "bf16" else torch.float32
+    st.bind(T, xs, odt)
+    bits = (lambda y: y.view(torch.int16)) if odt == torch.bfloat16 else (lambda y: y.view(torch.int32))
+
+    def load(k):
+        for d in widths:
+            xs[d].copy_(src[k][d])
+        for row in st.outputs:
+            for y in row:
+                y.fill_(float("nan"))
+
+    refs = []
+    for k in range(2):
+        load(k)
+        st.group.run_stage(1)
+        st.group.run_stage(2)
+        torch.cuda.synchronize()
+        refs.append([[y.clone() for y in row] for row in st.outputs])
+    assert not torch.equal(bits(refs[0][0][0]), bits(refs[1][0][0]))
+    for k in (0, 1, 1, 0, 1):
+        load(k)
+        st.group.run()
+        torch.cuda.synchronize()
+        for L, row in enumerate(st.outputs):
+            for i, y in enumerate(row):
+                assert torch.equal(bits(y), bits(refs[k][L][i])), (k, L, i)
+    st.group.release()
