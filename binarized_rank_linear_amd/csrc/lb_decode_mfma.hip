@@ -67,6 +67,7 @@ constexpr int kTilesPerItem2 = 8;         // 64-row tiles per wave in one stage-
 constexpr int kPreVec = 8;                // operand vectors a thread loads before the plane loads
 constexpr int kWin2 = 8;                  // stage 2 (streaming form): plane loads in flight per wave
 constexpr int kWin1 = 8;                  // stage 1 (fused form): plane loads in flight per wave
+constexpr int kEarly1 = 2;                // of which issued before the limb work inside the one-launch pass
 constexpr int kMaxKcf = 32;               // K-groups per fused stage-1 chunk (two 8-input pieces per thread)
 constexpr uint32_t kOOB = 0x7ffffff0u;    // a buffer offset past every range: reads as zero
 // Cache policy of a buffer access at device scope (sc1): coherent across the
@@ -130,7 +131,9 @@ struct MRun {
     const int32_t *lin0, *lin1, *linF, *lin2;   // item -> linear, per launch
     const int32_t *ord1, *ord2;  // workgroup -> item for stage 1 / stage 2 (largest first; null: identity)
     // the one-launch pass (k_pass)
-    const int32_t *ordP1, *ordP2;  // workgroup -> stage-1 item, (workgroup - items1) -> stage-2 item
+    const int32_t *ordP1;          // workgroup -> stage-1 item
+    const int32_t *tabP2;          // (workgroup - items1) -> (linear, first 256-row tile << 8 | tiles)
+    int64_t items2P;               // stage-2 workgroups of k_pass
     uint32_t *arrive, *ready;      // per linear: stage-1 items counted in, run number of its operands
     uint32_t epoch;                // this run's number (from 0)
     int pass;                      // 1: a full run is one k_pass launch
@@ -287,6 +290,17 @@ __device__ __forceinline__ MLin pick(const MRun &run, const MLin &single, const 
     return m;
 }
 
+// Linear j of the run as a wave-uniform value.
+__device__ __forceinline__ MLin pick_linear(const MRun &run, const MLin &single, int j) {
+    MLin m = run.table ? run.table[j] : single;
+    int w[sizeof(MLin) / 4];
+    __builtin_memcpy(w, &m, sizeof(MLin));
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(MLin) / 4); ++i) w[i] = __builtin_amdgcn_readfirstlane(w[i]);
+    __builtin_memcpy(&m, w, sizeof(MLin));
+    return m;
+}
+
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // The item a workgroup runs: launches of a group start their largest items
@@ -387,15 +401,14 @@ __device__ __forceinline__ void preload_ops(const uint8_t *src, int nops, int R,
 constexpr uint32_t kSpinLimit = 1u << 20;
 constexpr int kFlagStride = 64;           // words between two linears' counters (own 256-byte lines)
 
-// Thread 0 polls *flag (device scope) until it reads `want` or kSpinLimit
-// polls have gone by; the workgroup waits at a barrier meanwhile.
-__device__ __forceinline__ void wait_ready(const uint32_t *flag, uint32_t want) {
-    if (threadIdx.x == 0) {
-        uint32_t n = 0;
-        while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != want && ++n < kSpinLimit)
-            __builtin_amdgcn_s_sleep(2);
-    }
-    __syncthreads();
+// The wave polls *flag (device scope) until it reads `want` or kSpinLimit
+// polls have gone by.
+__device__ __forceinline__ void wait_flag(const uint32_t *flag, uint32_t want) {
+    uint32_t n = 0;
+    while ((uint32_t)__builtin_amdgcn_readfirstlane(
+               __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != want &&
+           ++n < kSpinLimit)
+        __builtin_amdgcn_s_sleep(2);
 }
 
 // ---------------------------------------------------------------------------
@@ -714,15 +727,14 @@ __device__ __forceinline__ void stage1f_item(const MRun &run, const MLin &L, int
         return o;
     };
     // The standalone kernel issues its first plane loads now, so their latency
-    // overlaps the limb work below.  Inside the one-launch pass they go out
-    // after it: held through the limb work they would take 32 more registers,
-    // and the pass, which holds stage 2 as well, would fit one workgroup less
-    // per CU.
+    // overlaps the limb work below.  Inside the one-launch pass only kEarly1
+    // go out now and the rest after it: all of them held through the limb work
+    // would take 32 more registers, and the pass, which holds stage 2 as well,
+    // would fit one workgroup less per CU.
+    constexpr int early = COHERENT ? kEarly1 : kWin1;
     v4u slot[kWin1];
-    if constexpr (!COHERENT) {
 #pragma unroll
-        for (int k = 0; k < kWin1; ++k) slot[k] = load_rows(rv, next_off());
-    }
+    for (int k = 0; k < early; ++k) slot[k] = load_rows(rv, next_off());
 
     // ---- limbs of g (.) x into the records ------------------------------------
     // piece pc: K-group pc/16 of the chunk, block (pc/4)%4, quarter pc%4; a
@@ -776,10 +788,8 @@ __device__ __forceinline__ void stage1f_item(const MRun &run, const MLin &L, int
     lds_meet();
 
     // ---- stream ------------------------------------------------------------
-    if constexpr (COHERENT) {
 #pragma unroll
-        for (int k = 0; k < kWin1; ++k) slot[k] = load_rows(rv, next_off());
-    }
+    for (int k = early; k < kWin1; ++k) slot[k] = load_rows(rv, next_off());
     v4f acc[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc[m] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -1114,21 +1124,20 @@ __global__ __launch_bounds__(kThreads) void k_stage2(MRun run, MLin single) {
 // needed.  Loads are unconditional (offsets past the range read zeros).  The
 // operands of all steps and h of the item's rows sit in LDS for the whole item.
 // COHERENT: the operands were written earlier in the same launch (the
-// one-launch pass); `ready` is the linear's flag, and the workgroup waits for
-// it to read the run's number before it loads them, at device scope.
+// one-launch pass); `ready` is the linear's flag.  Each wave loads it (device
+// scope) as its first load, then h and its first plane loads; the check waits
+// for the flag load alone (loads complete in issue order for the counter), and
+// only then do the operand loads go out, at device scope.
 template <int NL, int NB2, bool COHERENT>
-__device__ __forceinline__ void stage2r_item(const MRun &run, const MLin &L, int64_t item, uint8_t *smem,
-                                             const uint32_t *ready) {
+__device__ __forceinline__ void stage2r_item(const MRun &run, const MLin &L, int64_t row_begin, int tiles,
+                                             uint8_t *smem, const uint32_t *ready) {
     using R = Rows<NL>;
-    const int64_t local = item - L.item2;
     const int T = run.T;
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int r16 = lane & 15, gq = lane >> 4;
     const Nib nib = nibble_constants();
 
     const int steps = L.kgs;                       // K-groups over both paths' planes
-    const int64_t row_begin = local * L.rows2;
-    const int tiles = (int)imin(L.rows2 / kRG, cdiv(L.d_out - row_begin, kRG));
     const int total = tiles * steps;               // this wave's stream (uniform)
     const OutBuf ob = out_buf(L.y, run.y_dtype, (int64_t)T * L.d_out, L.d_out);
     uint8_t *ops = smem;                                          // [steps][NB2] operands
@@ -1141,9 +1150,11 @@ __device__ __forceinline__ void stage2r_item(const MRun &run, const MLin &L, int
 
     // operands and h first, as buffer loads (counted precisely, so the LDS
     // fill below waits for these only, not for the plane loads behind them)
-    if (COHERENT) wait_ready(ready, run.epoch + 1u);
+    uint32_t flag = 0;
+    if constexpr (COHERENT)
+        flag = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(ready, 4), 0, 0, kDeviceScope);
     v4u pre[kPreVec];
-    preload_ops<COHERENT ? kDeviceScope : 0>(L.tb, steps * NB2, L.R2, pre);
+    if constexpr (!COHERENT) preload_ops(L.tb, steps * NB2, L.R2, pre);
     // h of the item's rows: thread t holds 8 consecutive fp16 of path t / (kThreads/2)
     const int hp = (int)threadIdx.x / (kThreads / 2), hr = ((int)threadIdx.x % (kThreads / 2)) * 8;
     const __amdgpu_buffer_rsrc_t rh = make_rsrc(L.h, (int64_t)L.P * L.d_out * 2);
@@ -1171,6 +1182,10 @@ __device__ __forceinline__ void stage2r_item(const MRun &run, const MLin &L, int
     v4u slot[kWin2];
 #pragma unroll
     for (int k = 0; k < kWin2; ++k) slot[k] = load_rows(ru, off_of(k));
+    if constexpr (COHERENT) {
+        if ((uint32_t)__builtin_amdgcn_readfirstlane(flag) != run.epoch + 1u) wait_flag(ready, run.epoch + 1u);
+        preload_ops<kDeviceScope>(L.tb, steps * NB2, L.R2, pre);
+    }
 
     // operands of every step and h of the item's rows into LDS, shared by the 4 waves
     expand_ops<COHERENT ? kDeviceScope : 0>(ops, L.tb, steps * NB2, L.R2, pre);
@@ -1272,7 +1287,7 @@ __device__ __forceinline__ void stage2r_item(const MRun &run, const MLin &L, int
         // (16-byte chunks, all threads together), not as scattered pieces
         // between other workgroups' plane reads
         __syncthreads();
-        const int64_t rows = imin((int64_t)L.rows2, L.d_out - row_begin);
+        const int64_t rows = imin((int64_t)tiles * kRG, L.d_out - row_begin);
         const int per = 16 / yb;                                   // outputs per chunk
         const bool chunky = ob.vec && (L.d_out % per) == 0 && ((uintptr_t)L.y & 15) == 0;
         const int cpr = (int)cdiv(rows, per);                      // chunks per token row
@@ -1303,7 +1318,10 @@ template <int NL, int NB2>
 __global__ __launch_bounds__(kThreads) void k_stage2r(MRun run, MLin single) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int64_t item = item_of(run.ord2, run.base2);
-    stage2r_item<NL, NB2, false>(run, pick(run, single, run.lin2, item), item, smem, nullptr);
+    const MLin L = pick(run, single, run.lin2, item);
+    const int64_t row_begin = (item - L.item2) * L.rows2;
+    const int tiles = (int)imin(L.rows2 / kRG, cdiv(L.d_out - row_begin, kRG));
+    stage2r_item<NL, NB2, false>(run, L, row_begin, tiles, smem, nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -1355,9 +1373,11 @@ __global__ __launch_bounds__(kThreads) void k_pass(MRun run, MLin single) {
                                    __HIP_MEMORY_SCOPE_AGENT);
         }
     } else {
-        const int64_t item = __builtin_amdgcn_readfirstlane(run.ordP2[b - run.items1]);
-        const int j = run.table ? __builtin_amdgcn_readfirstlane(run.lin2[item]) : 0;
-        stage2r_item<NL, NB2, true>(run, pick(run, single, run.lin2, item), item, smem,
+        // (linear, first 256-row tile << 8 | tiles) of this workgroup
+        const int32_t *e = run.tabP2 + 2 * (b - run.items1);
+        const int j = __builtin_amdgcn_readfirstlane(e[0]);
+        const int g = __builtin_amdgcn_readfirstlane(e[1]);
+        stage2r_item<NL, NB2, true>(run, pick_linear(run, single, j), (int64_t)(g >> 8) * kRG, g & 255, smem,
                                     run.ready + j * kFlagStride);
     }
 }
@@ -1717,7 +1737,7 @@ size_t mfma_group_workspace_bytes(const Linear *ls, int n, int64_t T, int y_dtyp
     need += rup256((size_t)i0 * 4) + rup256((size_t)i1 * 4) + rup256((size_t)iF * 4) +
             rup256((size_t)i2 * 4);
     need += rup256((size_t)i1 * 4) + rup256((size_t)i2 * 4);   // dispatch orders
-    need += rup256((size_t)i1 * 4) + rup256((size_t)i2 * 4);   // dispatch orders of k_pass
+    need += rup256((size_t)i1 * 4) + rup256((size_t)i2 * 8);   // k_pass: stage-1 order, stage-2 table
     need += 2 * (size_t)n * kFlagStride * 4;                   // arrive, ready
     return need;
 }
@@ -1767,8 +1787,8 @@ int mfma_group_prepare(const Linear *ls, int n, int64_t T, int y_dtype, void *ws
     int32_t *ord1 = (int32_t *)((uint8_t *)lin2 + rup256((size_t)i2 * 4));
     int32_t *ord2 = (int32_t *)((uint8_t *)ord1 + rup256((size_t)i1 * 4));
     int32_t *ordP1 = (int32_t *)((uint8_t *)ord2 + rup256((size_t)i2 * 4));
-    int32_t *ordP2 = (int32_t *)((uint8_t *)ordP1 + rup256((size_t)i1 * 4));
-    uint32_t *arrive = (uint32_t *)((uint8_t *)ordP2 + rup256((size_t)i2 * 4));
+    int32_t *tabP2 = (int32_t *)((uint8_t *)ordP1 + rup256((size_t)i1 * 4));
+    uint32_t *arrive = (uint32_t *)((uint8_t *)tabP2 + rup256((size_t)i2 * 8));
     uint32_t *ready = arrive + (size_t)n * kFlagStride;
     std::vector<int32_t> h0((size_t)i0), h1((size_t)i1), hF((size_t)iF), h2((size_t)i2);
     for (int j = 0; j < n; ++j) {
@@ -1827,8 +1847,23 @@ int mfma_group_prepare(const Linear *ls, int n, int64_t T, int y_dtype, void *ws
         }
         p2 = early;
         p2.insert(p2.end(), late.begin(), late.end());
+        // one entry per stage-2 workgroup: (linear, first 256-row tile << 8 |
+        // tiles).  (Cutting the last items into smaller pieces, so that the
+        // launch drains sooner, was slower: every piece pays the operand and
+        // flag round trips of an item.)
+        std::vector<int32_t> e2;
+        e2.reserve((size_t)i2 * 2);
+        for (size_t i = 0; i < p2.size(); ++i) {
+            const int j = h2[(size_t)p2[i]];
+            const MLin &m = tab[(size_t)j];
+            const int64_t local = p2[i] - m.item2;
+            const int tiles = (int)imin(m.rows2 / kRG, cdiv(m.d_out - local * m.rows2, kRG));
+            e2.push_back(j);
+            e2.push_back((int32_t)(((local * (m.rows2 / kRG)) << 8) | tiles));
+        }
+        run.items2P = (int64_t)e2.size() / 2;
         if (hipMemcpy(ordP1, p1.data(), (size_t)i1 * 4, hipMemcpyHostToDevice) != hipSuccess ||
-            hipMemcpy(ordP2, p2.data(), (size_t)i2 * 4, hipMemcpyHostToDevice) != hipSuccess ||
+            hipMemcpy(tabP2, e2.data(), e2.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
             hipMemset(arrive, 0, (size_t)n * kFlagStride * 4 * 2) != hipSuccess)
             return hip_status(hipGetLastError());
     }
@@ -1851,7 +1886,7 @@ int mfma_group_prepare(const Linear *ls, int n, int64_t T, int y_dtype, void *ws
     run.ord1 = ord1;
     run.ord2 = ord2;
     run.ordP1 = ordP1;
-    run.ordP2 = ordP2;
+    run.tabP2 = tabP2;
     run.arrive = arrive;
     run.ready = ready;
     // one launch per run when stage 1 is the fused form and stage 2 k_stage2r
@@ -1886,7 +1921,7 @@ int launch_pass(const MRun &run, size_t lds, hipStream_t st) {
         raised = true;
     }
     MLin dummy{};
-    k_pass<NL, NB2><<<(unsigned)(run.items1 + run.items2), kThreads, lds, st>>>(run, dummy);
+    k_pass<NL, NB2><<<(unsigned)(run.items1 + run.items2P), kThreads, lds, st>>>(run, dummy);
     return last_launch_status();
 }
 
@@ -1900,7 +1935,7 @@ int mfma_group_run(const void *host_state, hipStream_t st, int stage_mask) {
         (r.items2 > 0 && !r.lin2))
         return LB_EINVAL;
     if (stage_mask == 3 && r.pass) {
-        if (!r.ordP1 || !r.ordP2 || !r.arrive || !r.ready) return LB_EINVAL;
+        if (!r.ordP1 || !r.tabP2 || !r.arrive || !r.ready || r.items2P != r.items2) return LB_EINVAL;
         // the counters reach (epoch + 1) * items1 of a linear: start over
         // before that leaves 31 bits (arrive and ready are contiguous)
         if ((uint64_t)(hs->epoch + 1) * (uint64_t)hs->n1_max >= (1ull << 31)) {
