@@ -181,3 +181,44 @@ def test_pass_reads_each_runs_inputs(key, T, out):
             for i, y in enumerate(row):
                 assert torch.equal(bits(y), bits(refs[k][L][i])), (k, L, i)
     st.group.release()
+
+
+@pytest.mark.parametrize("T,out", [(1, "bf16"), (5, "bf16"), (8, "bf16"), (1, "f32"), (3, "f32")])
+def test_pass_ragged_mixed_group(T, out):
+    """A decode group of ragged linears, with and without the residual path
+    (d_in, d_out and r_p off every tile size), runs as one launch per pass:
+    every run equals the staged run bit for bit, and the oracle within the
+    tolerance."""
+    torch = torch_or_skip()
+    import binarized_rank_linear_amd as lb
+    say("pass ragged group T", T, out)
+    shapes = [(1000, 700, 48, 2), (520, 130, 16, 1), (2048, 1536, 160, 2), (96, 1100, 32, 1),
+              (1024, 333, 64, 2), (4096, 257, 304, 2)]
+    odt = torch.bfloat16 if out == "bf16" else torch.float32
+    items, inps, xs = [], [], []
+    for i, (d_in, d_out, r_p, P) in enumerate(shapes):
+        inp = synth.layer_inputs(500 + i, d_in, d_out, r_p, P)
+        x = synth.activations(600 + i, T, d_in, "bf16")
+        y = torch.empty((T, d_out), dtype=odt, device="cuda")
+        items.append((x_to_dev(x), y, dev_layer(inp)))
+        inps.append(inp)
+        xs.append(x)
+    g = lb.Group(items, T, torch.bfloat16, odt)
+    bits = (lambda y: y.view(torch.int16)) if odt == torch.bfloat16 else (lambda y: y.view(torch.int32))
+    g.run_stage(1)
+    g.run_stage(2)
+    torch.cuda.synchronize()
+    staged = [it[1].clone() for it in items]
+    for _ in range(3):
+        for it in items:
+            it[1].fill_(float("nan"))
+        g.run()
+        torch.cuda.synchronize()
+        for i, it in enumerate(items):
+            assert torch.equal(bits(it[1]), bits(staged[i])), i
+    for i, inp in enumerate(inps):
+        xf = synth.bf16_bits_to_f32(xs[i]) if xs[i].dtype == np.uint16 else xs[i]
+        ref = oracle.linear_forward(xf, inp.U, inp.V, inp.h, inp.g, inp.l)
+        err = oracle.rel_l2(y_to_np(items[i][1]), ref)
+        assert err <= TOL[out], (i, err)
+    g.release()
