@@ -285,8 +285,8 @@ def main():
                     help="only run a plain MIB-MiB device copy (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: the LittleBit stack fits one MI355X and this build "
-              "has no multi-GPU path (see the sharding notes in DESIGN.md).", file=sys.stderr)
+        print("bench.py runs on one GPU only: the LittleBit stack fits one MI355X, and the "
+              "library has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
     import torch
