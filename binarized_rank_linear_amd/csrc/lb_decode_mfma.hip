@@ -105,6 +105,7 @@ struct MLin {
     int32_t R1, R2;       // activation rows in use (compact records per operand)
     int32_t xvec;         // fused stage 1: x and g read as 16-byte pieces (d_in % 8 == 0, aligned)
     int64_t item0, item1, itemF, item2;   // first item of this linear in each launch
+    int64_t fin0;         // the one-launch pass: first (path, latent group) counter of this linear
     float *part;          // [nchunks][T][P*r_p]
     uint8_t *pa;          // stage-1 operands, compact: [P][kgv][NB1][R1][kRec] (unused by the fused form)
     uint8_t *tb;          // stage-2 operands, compact: [kgs][NB2][R2][kRec]
@@ -114,6 +115,8 @@ struct MLin {
 __host__ __device__ inline int64_t items0_of(const MLin &m) { return (int64_t)m.P * m.nprep; }
 __host__ __device__ inline int64_t items1_of(const MLin &m) { return (int64_t)m.P * m.nchunks * m.nrg; }
 __host__ __device__ inline int64_t itemsF_of(const MLin &m) { return ((int64_t)m.kgs + 1) / 2; }
+// latent groups of a linear (the one-launch pass counts each one's chunks)
+__host__ __device__ inline int64_t groups_of(const MLin &m) { return (int64_t)m.P * m.nrg; }
 
 struct MRun {
     int T, x_dtype, y_dtype;
@@ -130,7 +133,8 @@ struct MRun {
     const int32_t *ordP1;          // workgroup -> stage-1 item
     const int32_t *tabP2;          // (workgroup - items1) -> (linear, first 256-row tile << 8 | tiles)
     int64_t items2P;               // stage-2 workgroups of k_pass
-    uint32_t *arrive, *ready;      // per linear: stage-1 items counted in, run number of its operands
+    uint32_t *arrive;              // per (linear, path, latent group): its stage-1 items counted in
+    uint32_t *ready;               // per linear: its latent groups whose operands are stored
     uint32_t epoch;                // this run's number (from 0)
     int pass;                      // 1: a full run is one k_pass launch
 };
@@ -297,6 +301,31 @@ __device__ __forceinline__ void preload_ops(const uint8_t *src, int nops, int R,
 #pragma unroll
     for (int j = 0; j < kPreVec; ++j)
         pre[j] = __builtin_amdgcn_raw_buffer_load_b128(r, (j * kThreads + (int)threadIdx.x) * 16, 0, AUX);
+}
+
+// Compact operands [nops][R records] of src -> the same bytes at dst (k_stage2r
+// keeps the records as they are).  The first kPreVec vectors of each thread
+// were loaded into pre[] before the caller's plane loads; any remainder is
+// copied here.
+template <int AUX = 0>
+__device__ __forceinline__ void copy_ops(uint8_t *dst, const uint8_t *src, int nops, int R,
+                                         const v4u (&pre)[kPreVec]) {
+    const int vecs = nops * R * kRec / 16;
+#pragma unroll
+    for (int j = 0; j < kPreVec; ++j) {
+        const int i = j * kThreads + (int)threadIdx.x;
+        if (i < vecs) *(v4u *)(dst + i * 16) = pre[j];
+    }
+    if (vecs <= kPreVec * kThreads) return;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(src, (int64_t)vecs * 16);
+    for (int i = kPreVec * kThreads + (int)threadIdx.x; i < vecs; i += kThreads)
+        *(v4u *)(dst + i * 16) = __builtin_amdgcn_raw_buffer_load_b128(r, i * 16, 0, AUX);
+}
+
+// LDS of k_stage2r's operands: `steps` K-groups of NB2 compact operands of R2
+// records, then one zero record (read by the lanes of rows no token fills).
+__host__ __device__ inline size_t ops2r_bytes(int steps, int NB2, int R2) {
+    return ((size_t)steps * NB2 * R2 + 1) * kRec;
 }
 
 constexpr uint32_t kSpinLimit = 1u << 20;
@@ -772,15 +801,12 @@ __global__ __launch_bounds__(kThreads) void k_stage1f(MRun run, MLin single) {
 // partials slice by slice: the kLC chunks of a slice are loaded together (all
 // in flight: unconditional buffer loads, chunks past the end read as zeros)
 // and added in chunk order from zero, and the slice sums in slice order from
-// zero.  COHERENT: the partial sums were written by other workgroups of the
-// same launch and the operands are read by others, so both go at device
-// scope.
+// zero.
 constexpr int kLU = 4, kLC = 8;   // units per lane, chunks per slice
-template <int NL, int NB2, bool COHERENT>
+template <int NL, int NB2>
 __device__ __forceinline__ void latent_item(const MRun &run, const MLin &L, int kg_first, int kg_count,
                                             uint8_t *smem) {
     using R = Rows<NL>;
-    constexpr int AUX = COHERENT ? kDeviceScope : 0;
     const int T = run.T;
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int opb = L.R2 * kRec;
@@ -823,7 +849,7 @@ __device__ __forceinline__ void latent_item(const MRun &run, const MLin &L, int 
                 for (int t = 0; t < kLC; ++t) {
                     const int c = sl * kLC + t;
                     a[q][t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                        rp, live[q] && c < L.nchunks ? base[q] + (uint32_t)((int64_t)c * cs * 4) : kOOB, 0, AUX));
+                        rp, live[q] && c < L.nchunks ? base[q] + (uint32_t)((int64_t)c * cs * 4) : kOOB, 0, 0));
                 }
 #pragma unroll
             for (int q = 0; q < kLU; ++q) {
@@ -855,7 +881,98 @@ __device__ __forceinline__ void latent_item(const MRun &run, const MLin &L, int 
     const int vecs = opsz / 16;
     const __amdgpu_buffer_rsrc_t rt = make_rsrc(L.tb + (int64_t)kg_first * NB2 * opb, (int64_t)vecs * 16);
     for (int i = threadIdx.x; i < vecs; i += kThreads)
-        __builtin_amdgcn_raw_buffer_store_b128(src[i], rt, i * 16, 0, AUX);
+        __builtin_amdgcn_raw_buffer_store_b128(src[i], rt, i * 16, 0, 0);
+}
+
+// The one-launch pass: the latents of one stage-1 latent group (path p,
+// 64-latent tiles [rg*F, (rg+1)*F), F = run.flush1) for every token, summed
+// as latent_item sums them.  Each (token, 32-latent plane) is staged in LDS as
+// NL records, of which only the plane's 32 bytes and its scale byte are
+// stored: the stage-2 records' other planes belong to other groups, and rows
+// no (token, path, limb) fills stay as the workspace set-up left them (zero).
+// The partial sums come from other workgroups of the launch and the operands
+// go to others, so both are accessed at device scope.
+template <int NL, int NB2>
+__device__ __forceinline__ void latent_rows(const MRun &run, const MLin &L, int p, int rg, uint8_t *smem) {
+    using R = Rows<NL>;
+    const int T = run.T;
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int pl0 = rg * run.flush1 * 2;                          // first plane of the group (path p)
+    const int npl = (int)imin(run.flush1 * 2, L.kw_u - pl0);
+    const int units = T * npl;                                    // (token, plane), token-major
+    const int64_t Rtot = (int64_t)L.P * L.r_p;
+    const int64_t cs = (int64_t)T * Rtot;                         // floats per chunk
+    const int ns = (int)cdiv(L.nchunks, kLC);                     // slices
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(L.part, (int64_t)L.nchunks * cs * 4);
+    constexpr int step = 2 * kWaves;                              // wave halves of the workgroup
+    for (int ub = 2 * wave; ub < units; ub += step * kLU) {      // uniform per wave
+        uint32_t base[kLU];
+        bool live[kLU];
+#pragma unroll
+        for (int q = 0; q < kLU; ++q) {
+            const int u = ub + q * step + (lane >> 5);
+            const bool ok = u < units;
+            const int n = ok ? u / npl : 0;
+            const int k = (pl0 + (ok ? u % npl : 0)) * 32 + (lane & 31);   // latent of path p
+            live[q] = ok && k < L.r_p;
+            base[q] = live[q] ? (uint32_t)(((int64_t)n * Rtot + (int64_t)p * L.r_p + k) * 4) : 0u;
+        }
+        float sum[kLU];
+#pragma unroll
+        for (int q = 0; q < kLU; ++q) sum[q] = 0.0f;
+        for (int sl = 0; sl < ns; ++sl) {                         // uniform
+            float a[kLU][kLC];
+#pragma unroll
+            for (int q = 0; q < kLU; ++q)
+#pragma unroll
+                for (int t = 0; t < kLC; ++t) {
+                    const int c = sl * kLC + t;
+                    a[q][t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                        rp, live[q] && c < L.nchunks ? base[q] + (uint32_t)((int64_t)c * cs * 4) : kOOB, 0,
+                        kDeviceScope));
+                }
+#pragma unroll
+            for (int q = 0; q < kLU; ++q) {
+                float x = 0.0f;
+#pragma unroll
+                for (int t = 0; t < kLC; ++t) x += a[q][t];
+                sum[q] += x;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < kLU; ++q) {
+            const int u = ub + q * step + (lane >> 5);
+            const bool ok = u < units;
+            const int pl = pl0 + (ok ? u % npl : 0);
+            const int k = pl * 32 + (lane & 31);
+            const float v = live[q] ? f16_to_f32(L.l[(int64_t)p * L.r_p + k]) * sum[q] : 0.0f;
+            const int e = ((p * L.kw_u + pl) & 3) * 32 + (lane & 31);   // element in the K-group
+            uint8_t *rec = smem + (size_t)(ok ? u : 0) * NL * kRec;
+            emit_limbs<NL>(v, rec + rec_offset(e), rec + 128 + (e >> 5), ok, (e & 31) == 0);
+        }
+    }
+    __syncthreads();
+    // (unit, limb, 16-byte half) -> its place in the stage-2 records
+    const int opb = L.R2 * kRec;
+    const __amdgpu_buffer_rsrc_t rt = make_rsrc(L.tb, (int64_t)L.kgs * NB2 * opb);
+    for (int i = threadIdx.x; i < units * NL * 2; i += kThreads) {
+        const int u = i / (NL * 2), q = (i >> 1) % NL, h = i & 1;
+        const int n = u / npl, gp = p * L.kw_u + pl0 + u % npl;  // plane over both paths
+        const int row = (n % R::TPM2) * R::S2 + p * NL + q;
+        // block b of a record: bytes [16 * (b >> 1) + 64 * (b & 1), +16) and 32 further (rec_offset)
+        const int blk = ((gp & 3) >> 1) * 16 + ((gp & 3) & 1) * 64 + h * 32;
+        const uint32_t dst = (uint32_t)((((gp >> 2) * NB2 + n / R::TPM2) * L.R2 + row) * kRec + blk);
+        const v4u w = *(const v4u *)(smem + (size_t)(u * NL + q) * kRec + blk);
+        __builtin_amdgcn_raw_buffer_store_b128(w, rt, dst, 0, kDeviceScope);
+    }
+    for (int i = threadIdx.x; i < units * NL; i += kThreads) {
+        const int u = i / NL, q = i % NL;
+        const int n = u / npl, gp = p * L.kw_u + pl0 + u % npl;
+        const int row = (n % R::TPM2) * R::S2 + p * NL + q;
+        const uint32_t dst = (uint32_t)((((gp >> 2) * NB2 + n / R::TPM2) * L.R2 + row) * kRec + 128 + (gp & 3));
+        __builtin_amdgcn_raw_buffer_store_b8(smem[(size_t)(u * NL + q) * kRec + 128 + (gp & 3)], rt, dst, 0,
+                                             kDeviceScope);
+    }
 }
 
 template <int NL, int NB2>
@@ -864,7 +981,7 @@ __global__ __launch_bounds__(kThreads) void k_latent(MRun run, MLin single) {
     const int64_t item = (int64_t)blockIdx.x + run.baseF;
     const MLin L = pick(run, single, run.linF, item);
     const int kg_first = (int)(item - L.itemF) * 2;               // 2 K-groups = 8 planes per item
-    latent_item<NL, NB2, false>(run, L, kg_first, (int)imin(2, L.kgs - kg_first), smem);
+    latent_item<NL, NB2>(run, L, kg_first, (int)imin(2, L.kgs - kg_first), smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -1023,12 +1140,15 @@ __global__ __launch_bounds__(kThreads) void k_stage2(MRun run, MLin single) {
 // consumed and immediately reloaded with the element kWin2 further on, so no
 // register is copied and no wait other than the one for the oldest load is
 // needed.  Loads are unconditional (offsets past the range read zeros).  The
-// operands of all steps and h of the item's rows sit in LDS for the whole item.
+// operands of all steps (the compact records as the workspace holds them, plus
+// a zero record for the rows no token fills) and h of the item's rows sit in
+// LDS for the whole item.
 // COHERENT: the operands were written earlier in the same launch (the
-// one-launch pass); `ready` is the linear's flag.  Each wave loads it (device
-// scope) as its first load, then h and its first plane loads; the check waits
-// for the flag load alone (loads complete in issue order for the counter), and
-// only then do the operand loads go out, at device scope.
+// one-launch pass); `ready` counts the linear's latent groups whose operands
+// are stored.  Each wave loads it (device scope) as its first load, then h and
+// its first plane loads; the check waits for the counter load alone (loads
+// complete in issue order for the counter), and only then do the operand loads
+// go out, at device scope.
 template <int NL, int NB2, bool COHERENT>
 __device__ __forceinline__ void stage2r_item(const MRun &run, const MLin &L, int64_t row_begin, int tiles,
                                              uint8_t *smem, const uint32_t *ready) {
@@ -1041,8 +1161,10 @@ __device__ __forceinline__ void stage2r_item(const MRun &run, const MLin &L, int
     const int steps = L.kgs;                       // K-groups over both paths' planes
     const int total = tiles * steps;               // this wave's stream (uniform)
     const OutBuf ob = out_buf(L.y, run.y_dtype, (int64_t)T * L.d_out, L.d_out);
-    uint8_t *ops = smem;                                          // [steps][NB2] operands
-    uint16_t *hs = (uint16_t *)(smem + run.ops2 * NB2 * kOpS);   // [2][kHRows] fp16 h
+    const int R2 = L.R2;
+    uint8_t *ops = smem;                                          // [steps][NB2][R2] records
+    uint8_t *zrec = ops + (size_t)steps * NB2 * R2 * kRec;        // the zero record
+    uint16_t *hs = (uint16_t *)(smem + ops2r_bytes(run.ops2, NB2, R2));   // [2][kHRows] fp16 h
     // [T][kHRows] outputs of the item (bf16 or fp32): stores inside the stream
     // would share the in-order counter with the plane loads, so every later
     // wait would also wait for their acknowledgements
@@ -1084,12 +1206,14 @@ __device__ __forceinline__ void stage2r_item(const MRun &run, const MLin &L, int
 #pragma unroll
     for (int k = 0; k < kWin2; ++k) slot[k] = load_rows(ru, off_of(k));
     if constexpr (COHERENT) {
-        if ((uint32_t)__builtin_amdgcn_readfirstlane(flag) != run.epoch + 1u) wait_flag(ready, run.epoch + 1u);
+        const uint32_t want = (run.epoch + 1u) * (uint32_t)(L.P * L.nrg);   // every latent group of the linear
+        if ((uint32_t)__builtin_amdgcn_readfirstlane(flag) != want) wait_flag(ready, want);
         preload_ops<kDeviceScope>(L.tb, steps * NB2, L.R2, pre);
     }
 
     // operands of every step and h of the item's rows into LDS, shared by the 4 waves
-    expand_ops<COHERENT ? kDeviceScope : 0>(ops, L.tb, steps * NB2, L.R2, pre);
+    copy_ops<COHERENT ? kDeviceScope : 0>(ops, L.tb, steps * NB2, R2, pre);
+    if (threadIdx.x < kRec / 16) *(v4u *)(zrec + threadIdx.x * 16) = v4u{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int k = 0; k < kHRows / (kThreads / 2) / 8; ++k) {
         const int rl = hr + k * (kThreads / 2) * 8;
@@ -1110,16 +1234,23 @@ __device__ __forceinline__ void stage2r_item(const MRun &run, const MLin &L, int
     for (int m = 0; m < 4; ++m)
 #pragma unroll
         for (int b = 0; b < NB2; ++b) acc[m][b] = v4f{0.f, 0.f, 0.f, 0.f};
-    int i = 0, st = 0;
+    // lane (gq, r16) reads quarter gq of record r16 of each operand and its
+    // scale; rows no token fills read the zero record
+    const bool rlive = r16 < R2;
+    const uint8_t *dl = (rlive ? ops + r16 * kRec : zrec) + gq * 32;
+    const uint8_t *sl = (rlive ? ops + r16 * kRec : zrec) + 128 + gq;
+    const int sb = rlive ? R2 * kRec : 0;                         // next token block
+    const int ss = sb * NB2;                                      // next step
+    int i = 0, st = 0, so = 0;
     auto process = [&](const v4u &w) {
-        const uint8_t *opp = ops + st * NB2 * kOpS;
         v8i ao[NB2];
         int sa[NB2];
 #pragma unroll
         for (int b = 0; b < NB2; ++b) {
-            ao[b] = load_op(opp + b * kOpS);
-            sa[b] = opp[b * kOpS + kOp + lane];
+            ao[b] = load_op_at(dl + so + b * sb);
+            sa[b] = sl[so + b * sb];
         }
+        so += ss;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const v8i sg = unpack_word(w[m], nib);
@@ -1173,6 +1304,7 @@ __device__ __forceinline__ void stage2r_item(const MRun &run, const MLin &L, int
 #pragma unroll
                 for (int b = 0; b < NB2; ++b) acc[m][b] = v4f{0.f, 0.f, 0.f, 0.f};
             st = 0;
+            so = 0;
             ++i;
         }
     };
@@ -1230,24 +1362,28 @@ __global__ __launch_bounds__(kThreads) void k_stage2r(MRun run, MLin single) {
 // ---------------------------------------------------------------------------
 
 // Workgroups [0, items1) run stage-1 items, the rest stage-2 items.  A linear's
-// stage-2 items need its latents, so the hand-off is per linear, inside the
-// launch:
+// stage-2 items need its latents, so the hand-off goes through counters,
+// inside the launch:
 //   - a stage-1 workgroup stores its partial sums at device scope, waits until
-//     they are complete, and counts itself in arrive[linear];
-//   - the workgroup that completes the count (the last of the linear's stage-1
-//     items in this run) sums the partials into the stage-2 operands (the
-//     latent step), stores them at device scope and sets ready[linear] to the
-//     run's number;
-//   - a stage-2 workgroup waits for that number before it loads the operands.
+//     they are complete, and counts itself in the counter of its latent group
+//     (linear, path, tiles [rg*F, (rg+1)*F)), whose chunks are its nchunks
+//     items;
+//   - the workgroup that completes that count (the group's last chunk in this
+//     run) sums the group's partials into its planes of the stage-2 operands
+//     (the latent step, spread over the linear's P * nrg groups), stores them
+//     at device scope and counts the group in ready[linear];
+//   - a stage-2 workgroup waits until every group of its linear is counted in
+//     before it loads the operands.
 // Device-scope accesses bypass the non-coherent caches of the other XCDs, so
 // no cache-wide write-back or invalidation is needed.  Workgroups start in
 // index order, so when a stage-2 workgroup runs, every stage-1 workgroup has
 // started already; those never wait, so every wait ends.  The wait is also
 // bounded (kSpinLimit polls); past it the workgroup goes on and its outputs
 // are wrong, but the launch still ends.
-// The counters keep counting across runs: after run e (from 0) arrive[j] is
-// (e + 1) * items1(j), so the completing workgroup is the one that reads
-// (e + 1) * items1(j) - 1 before its increment.
+// The counters keep counting across runs: after run e (from 0) a group's
+// counter is (e + 1) * nchunks, so the completing workgroup is the one that
+// reads (e + 1) * nchunks - 1 before its increment, and ready[j] is
+// (e + 1) * P * nrg.
 template <int NL, int NB2>
 __global__ __launch_bounds__(kThreads) void k_pass(MRun run, MLin single) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -1260,18 +1396,17 @@ __global__ __launch_bounds__(kThreads) void k_pass(MRun run, MLin single) {
         stage1f_item<NL, true>(run, L, item, smem);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // this wave's partial sums are stored
         __syncthreads();
+        const int f = (int)((item - L.item1) / L.nchunks);          // latent group: path * nrg + rg
         if (threadIdx.x == 0)
-            s_count = __hip_atomic_fetch_add(run.arrive + j * kFlagStride, 1u, __ATOMIC_RELAXED,
+            s_count = __hip_atomic_fetch_add(run.arrive + (L.fin0 + f) * kFlagStride, 1u, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
-        const uint32_t n1 = (uint32_t)items1_of(L);
-        if (s_count + 1u == (run.epoch + 1u) * n1) {                // uniform
-            latent_item<NL, NB2, true>(run, L, 0, L.kgs, smem);    // all of the linear's K-groups
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's operands are stored
+        if (s_count + 1u == (run.epoch + 1u) * (uint32_t)L.nchunks) {   // uniform
+            latent_rows<NL, NB2>(run, L, f / L.nrg, f % L.nrg, smem);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's operand bytes are stored
             __syncthreads();
             if (threadIdx.x == 0)
-                __hip_atomic_store(run.ready + j * kFlagStride, run.epoch + 1u, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_fetch_add(run.ready + j * kFlagStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     } else {
         // (linear, first 256-row tile << 8 | tiles) of this workgroup
@@ -1330,8 +1465,8 @@ int ystage_for(int64_t T, int y_dtype) {
     return (size_t)T * kHRows * (y_dtype == LB_BF16 ? 2 : 4) <= (size_t)kYStage ? 1 : 0;
 }
 
-bool dma2_for(const Shape &s, int steps_max) {
-    return (size_t)steps_max * s.NB2 * kOpS + 2 * kHRows * 2 <= 80 * 1024;
+bool dma2_for(const Shape &s, int64_t T, int steps_max) {
+    return ops2r_bytes(steps_max, s.NB2, rows2(s, T)) + 2 * kHRows * 2 <= 88 * 1024;
 }
 
 int ops2_for(const Shape &s, int steps_max) {
@@ -1449,7 +1584,7 @@ int launch_all(const MRun &run, const MLin &single, const Lds &lds, hipStream_t 
     }
     if ((stage_mask & 2) && run.items2 <= 0) return LB_OK;
     if ((stage_mask & 2) && run.dma2) {
-        const size_t l2 = (size_t)run.ops2 * NB2 * kOpS + 2 * kHRows * 2 +
+        const size_t l2 = ops2r_bytes(run.ops2, NB2, rows2(Shape{NL, NB1, NB2}, run.T)) + 2 * kHRows * 2 +
                           (run.ystage ? (size_t)run.T * kHRows * (run.y_dtype == LB_BF16 ? 2 : 4) : 0);
         if (l2 > 160 * 1024) return LB_EUNSUPPORTED;
         static bool raised = false;        // once per instantiation (idempotent if raced)
@@ -1538,7 +1673,7 @@ int mfma_decode_forward(const Linear &a, void *ws, hipStream_t st) {
     run.T = (int)a.T;
     run.x_dtype = a.x_dtype;
     run.y_dtype = a.y_dtype;
-    run.dma2 = dma2_for(s, m.kgs);
+    run.dma2 = dma2_for(s, a.T, m.kgs);
     run.ystage = ystage_for(a.T, a.y_dtype);
     run.ops2 = run.dma2 ? m.kgs : ops2_for(s, m.kgs);
     run.items0 = items0_of(m);
@@ -1561,6 +1696,7 @@ struct MGroupHost {
     size_t lds_pass;     // dynamic LDS of k_pass
     uint32_t epoch;      // number of the next one-launch run
     int64_t n1_max;      // most stage-1 items of one linear
+    int64_t nf;          // latent groups of all linears (counters in arrive)
     int n;               // linears
 };
 
@@ -1581,18 +1717,24 @@ constexpr int64_t kMinGroupItems = 1024;
 // form (which spreads that sum over many workgroups) goes down to 4.
 constexpr int kPassMinKcg = 16;
 
-// Whether a group runs as one launch (k_pass): the fused stage 1 and a stage 2
-// whose operands fit the LDS (the K-groups, and so that test, do not depend on
-// the grain).
+// Token counts the one-launch pass serves: one token (either output dtype).
+// On the 32-, 40- and 80-layer stacks it measured 3 to 7 percent faster than
+// the three launches there, but slower from T = 4 on (by 10 to 50 percent) and
+// at T = 2 on two of the three stacks.
+bool pass_tokens(const Shape &s, int64_t T) { return fused1(s) && T == 1; }
+
+// Whether a group runs as one launch (k_pass): such a token count and a stage
+// 2 whose operands fit the LDS (the K-groups, and so that test, do not depend
+// on the grain).
 bool pass_form(const Linear *ls, int n, const Shape &s) {
-    if (!fused1(s)) return false;
+    if (!pass_tokens(s, ls[0].T)) return false;
     int steps_max = 1;
     for (int j = 0; j < n; ++j) {
         MLin m;
         plan_linear(ls[j], s, true, &m);
         steps_max = (int)imax(steps_max, m.kgs);
     }
-    return dma2_for(s, steps_max);
+    return dma2_for(s, ls[0].T, steps_max);
 }
 
 Grain group_grain(const Linear *ls, int n, const Shape &s) {
@@ -1626,7 +1768,7 @@ size_t mfma_group_workspace_bytes(const Linear *ls, int n, int64_t T, int y_dtyp
     if (!shape_for(T, y_dtype, &s)) return 0;
     size_t need = 256 + rup256(sizeof(MLin) * n);
     const Grain gr = group_grain(ls, n, s);
-    int64_t i0 = 0, i1 = 0, iF = 0, i2 = 0;
+    int64_t i0 = 0, i1 = 0, iF = 0, i2 = 0, nf = 0;
     for (int j = 0; j < n; ++j) {
         MLin m;
         need += plan_linear(ls[j], s, true, &m, gr);
@@ -1634,12 +1776,13 @@ size_t mfma_group_workspace_bytes(const Linear *ls, int n, int64_t T, int y_dtyp
         i1 += items1_of(m);
         iF += itemsF_of(m);
         i2 += m.n2;
+        nf += groups_of(m);
     }
     need += rup256((size_t)i0 * 4) + rup256((size_t)i1 * 4) + rup256((size_t)iF * 4) +
             rup256((size_t)i2 * 4);
     need += rup256((size_t)i1 * 4) + rup256((size_t)i2 * 4);   // dispatch orders
     need += rup256((size_t)i1 * 4) + rup256((size_t)i2 * 8);   // k_pass: stage-1 order, stage-2 table
-    need += 2 * (size_t)n * kFlagStride * 4;                   // arrive, ready
+    need += (size_t)(nf + n) * kFlagStride * 4;                // arrive (per latent group), ready (per linear)
     return need;
 }
 
@@ -1654,8 +1797,9 @@ int mfma_group_prepare(const Linear *ls, int n, int64_t T, int y_dtype, void *ws
     uint8_t *cur = w + 256 + rup256(sizeof(MLin) * n);
     std::vector<MLin> tab((size_t)n);
     const Grain gr = group_grain(ls, n, hs->s);
-    int64_t i0 = 0, i1 = 0, iF = 0, i2 = 0;
+    int64_t i0 = 0, i1 = 0, iF = 0, i2 = 0, nf = 0;
     int steps_max = 1;
+    uint8_t *const lin_area = cur;
     for (int j = 0; j < n; ++j) {
         MLin &m = tab[(size_t)j];
         const size_t b = plan_linear(ls[j], hs->s, true, &m, gr);
@@ -1665,15 +1809,17 @@ int mfma_group_prepare(const Linear *ls, int n, int64_t T, int y_dtype, void *ws
         m.item1 = i1;
         m.itemF = iF;
         m.item2 = i2;
+        m.fin0 = nf;
         i0 += items0_of(m);
         i1 += items1_of(m);
         iF += itemsF_of(m);
         i2 += m.n2;
+        nf += groups_of(m);
         if (m.kgs > steps_max) steps_max = m.kgs;
     }
     MRun &run = hs->run;
     run = MRun{};
-    run.dma2 = dma2_for(hs->s, steps_max);
+    run.dma2 = dma2_for(hs->s, T, steps_max);
     run.ystage = ystage_for(T, y_dtype);
     run.ops2 = run.dma2 ? steps_max : ops2_for(hs->s, steps_max);
     hs->lds = Lds{};
@@ -1690,7 +1836,7 @@ int mfma_group_prepare(const Linear *ls, int n, int64_t T, int y_dtype, void *ws
     int32_t *ordP1 = (int32_t *)((uint8_t *)ord2 + rup256((size_t)i2 * 4));
     int32_t *tabP2 = (int32_t *)((uint8_t *)ordP1 + rup256((size_t)i1 * 4));
     uint32_t *arrive = (uint32_t *)((uint8_t *)tabP2 + rup256((size_t)i2 * 8));
-    uint32_t *ready = arrive + (size_t)n * kFlagStride;
+    uint32_t *ready = arrive + (size_t)nf * kFlagStride;
     std::vector<int32_t> h0((size_t)i0), h1((size_t)i1), hF((size_t)iF), h2((size_t)i2);
     for (int j = 0; j < n; ++j) {
         const MLin &m = tab[(size_t)j];
@@ -1765,13 +1911,17 @@ int mfma_group_prepare(const Linear *ls, int n, int64_t T, int y_dtype, void *ws
         run.items2P = (int64_t)e2.size() / 2;
         if (hipMemcpy(ordP1, p1.data(), (size_t)i1 * 4, hipMemcpyHostToDevice) != hipSuccess ||
             hipMemcpy(tabP2, e2.data(), e2.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
-            hipMemset(arrive, 0, (size_t)n * kFlagStride * 4 * 2) != hipSuccess)
+            hipMemset(arrive, 0, (size_t)(nf + n) * kFlagStride * 4) != hipSuccess ||
+            // the one-launch pass stores only the operand bytes that tokens
+            // fill: the rest of the stage-2 records starts (and stays) zero
+            hipMemset(lin_area, 0, (size_t)(cur - lin_area)) != hipSuccess)
             return hip_status(hipGetLastError());
     }
     hs->n1_max = 1;
     for (int j = 0; j < n; ++j) hs->n1_max = imax(hs->n1_max, items1_of(tab[(size_t)j]));
     hs->epoch = 0;
     hs->n = n;
+    hs->nf = nf;
     run.T = (int)T;
     run.x_dtype = ls[0].x_dtype;
     run.y_dtype = y_dtype;
@@ -1791,15 +1941,14 @@ int mfma_group_prepare(const Linear *ls, int n, int64_t T, int y_dtype, void *ws
     run.arrive = arrive;
     run.ready = ready;
     // one launch per run when stage 1 is the fused form and stage 2 k_stage2r
-    run.pass = fused1(hs->s) && run.dma2 && i1 > 0 && i2 > 0 ? 1 : 0;
+    run.pass = pass_tokens(hs->s, T) && run.dma2 && i1 > 0 && i2 > 0 ? 1 : 0;
     hs->lds_pass = 0;
     if (run.pass) {
-        const size_t l2 = (size_t)run.ops2 * hs->s.NB2 * kOpS + 2 * kHRows * 2 +
+        const size_t l2 = ops2r_bytes(run.ops2, hs->s.NB2, rows2(hs->s, T)) + 2 * kHRows * 2 +
                           (run.ystage ? (size_t)T * kHRows * (y_dtype == LB_BF16 ? 2 : 4) : 0);
-        size_t lat_all = 0;                 // the completing workgroup builds all K-groups at once
-        for (int j = 0; j < n; ++j)
-            lat_all = std::max(lat_all, (size_t)tab[(size_t)j].kgs * hs->s.NB2 * tab[(size_t)j].R2 * kRec);
-        hs->lds_pass = std::max(std::max(hs->lds.s1, lat_all), l2);
+        // a latent group's (token, plane) units staged as NL records each
+        const size_t lat = (size_t)T * run.flush1 * 2 * hs->s.NL * kRec;
+        hs->lds_pass = std::max(std::max(hs->lds.s1, lat), l2);
         if (hs->lds_pass > 160 * 1024 - 64) run.pass = 0;
     }
     return LB_OK;
@@ -1837,10 +1986,11 @@ int mfma_group_run(const void *host_state, hipStream_t st, int stage_mask) {
         return LB_EINVAL;
     if (stage_mask == 3 && r.pass) {
         if (!r.ordP1 || !r.tabP2 || !r.arrive || !r.ready || r.items2P != r.items2) return LB_EINVAL;
-        // the counters reach (epoch + 1) * items1 of a linear: start over
-        // before that leaves 31 bits (arrive and ready are contiguous)
+        // the counters reach (epoch + 1) * nchunks or (epoch + 1) * P * nrg,
+        // at most (epoch + 1) * items1 of a linear: start over before that
+        // leaves 31 bits (arrive and ready are contiguous)
         if ((uint64_t)(hs->epoch + 1) * (uint64_t)hs->n1_max >= (1ull << 31)) {
-            const int64_t words = (int64_t)hs->n * kFlagStride * 2;
+            const int64_t words = (hs->nf + hs->n) * kFlagStride;
             k_zero_words<<<(unsigned)imin(1024, cdiv(words, 256)), 256, 0, st>>>(r.arrive, words);
             if (int rc = last_launch_status()) return rc;
             hs->epoch = 0;

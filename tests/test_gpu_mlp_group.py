@@ -135,12 +135,14 @@ def test_group_run_matches_staged_run(key, T, out):
     st.group.release()
 
 
-@pytest.mark.parametrize("key,T,out", [("c3", 3, "bf16"), ("c5", 6, "bf16"), ("c5", 4, "f32"), ("c5", 1, "f32")])
+@pytest.mark.parametrize("key,T,out", [("c3", 1, "bf16"), ("c4", 1, "bf16"), ("c5", 1, "f32"), ("c3", 2, "bf16"),
+                                       ("c5", 6, "bf16"), ("c5", 4, "f32")])
 def test_pass_reads_each_runs_inputs(key, T, out):
-    """The one-launch pass hands each run's latents to that run's stage 2:
-    with other activations between runs, every run equals the staged run of
-    its own inputs bit for bit (a stale hand-off would repeat the previous
-    run's outputs)."""
+    """The one-launch pass (T = 1) hands each run's latents to that run's
+    stage 2: with other activations between runs, every run equals the staged
+    run of its own inputs bit for bit (a stale hand-off would repeat the
+    previous run's outputs).  Larger T runs three launches per run, checked
+    the same way."""
     torch = torch_or_skip()
     from binarized_rank_linear_amd.stack import LayerStack
     w = synth.WORKLOADS[key]
@@ -183,12 +185,12 @@ def test_pass_reads_each_runs_inputs(key, T, out):
     st.group.release()
 
 
-@pytest.mark.parametrize("T,out", [(1, "bf16"), (5, "bf16"), (8, "bf16"), (1, "f32"), (3, "f32")])
+@pytest.mark.parametrize("T,out", [(1, "bf16"), (2, "bf16"), (5, "bf16"), (8, "bf16"), (1, "f32"), (3, "f32")])
 def test_pass_ragged_mixed_group(T, out):
     """A decode group of ragged linears, with and without the residual path
-    (d_in, d_out and r_p off every tile size), runs as one launch per pass:
-    every run equals the staged run bit for bit, and the oracle within the
-    tolerance."""
+    (d_in, d_out and r_p off every tile size), runs as one launch per pass
+    (T = 1; three launches beyond): every run equals the staged run bit for
+    bit, and the oracle within the tolerance."""
     torch = torch_or_skip()
     import binarized_rank_linear_amd as lb
     say("pass ragged group T", T, out)
