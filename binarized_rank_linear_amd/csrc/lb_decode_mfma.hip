@@ -1711,8 +1711,8 @@ constexpr int64_t kLateItems = 1024;
 // stage-2 item down to one 256-row tile).
 constexpr int64_t kMinGroupItems = 1024;
 
-// The one-launch pass sums each linear's chunk partials in one workgroup (the
-// last of its stage-1 items), a few loads per chunk in sequence: small groups
+// The one-launch pass sums a latent group's chunk partials in one workgroup
+// (the group's last chunk), a few loads per chunk in sequence: small groups
 // keep chunks of at least kPassMinKcg K-groups there, where the three-launch
 // form (which spreads that sum over many workgroups) goes down to 4.
 constexpr int kPassMinKcg = 16;

@@ -204,13 +204,13 @@ int lb_grouped_prepare(const lb_linear_desc *descs, int n, int64_t T, int x_dtyp
 
 /* Run a prepared group: every linear's y = layer(x), in a few launches for the
  * whole group (all first contractions, then all second contractions).  A
- * decode group whose tokens fill one activation block (T <= 8 with bf16
- * output, T <= 4 with fp32) and whose operands fit the LDS runs as ONE launch:
- * each linear's stage 2 starts as soon as its own stage 1 is done.  That
- * launch numbers its runs in ws (per-linear counters that keep counting), so
- * runs of one group must be issued one after the other, from one thread at a
+ * decode group at T = 1 whose operands fit the LDS runs as ONE launch: each
+ * linear's stage 2 starts as soon as its own stage 1 and latents are done.
+ * That launch numbers its runs in ws (counters that keep counting), so runs
+ * of one group must be issued one after the other, from one thread at a
  * time, each on a stream ordered after the previous run; runs on the same
- * workspace that overlap race. */
+ * workspace that overlap race, and the workspace must not be written between
+ * runs. */
 int lb_grouped_run(void *ws, void *stream);
 
 /* Forget a prepared group (its host-side record; ws itself stays the
