@@ -190,12 +190,14 @@ def test_pass_ragged_mixed_group(T, out):
     """A decode group of ragged linears, with and without the residual path
     (d_in, d_out and r_p off every tile size), runs as one launch per pass
     (T = 1; three launches beyond): every run equals the staged run bit for
-    bit, and the oracle within the tolerance."""
+    bit, and the oracle within the tolerance.  The last two ranks span two
+    stage-1 latent groups per path at T = 1 (more than 24 tiles of 64
+    latents), the second one ragged."""
     torch = torch_or_skip()
     import binarized_rank_linear_amd as lb
     say("pass ragged group T", T, out)
     shapes = [(1000, 700, 48, 2), (520, 130, 16, 1), (2048, 1536, 160, 2), (96, 1100, 32, 1),
-              (1024, 333, 64, 2), (4096, 257, 304, 2)]
+              (1024, 333, 64, 2), (4096, 257, 304, 2), (1024, 512, 1696, 2), (640, 384, 2000, 1)]
     odt = torch.bfloat16 if out == "bf16" else torch.float32
     items, inps, xs = [], [], []
     for i, (d_in, d_out, r_p, P) in enumerate(shapes):
