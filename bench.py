@@ -217,6 +217,41 @@ def single_layer_leg(w, T, reps=2000):
                     % (nbytes / 1e6)}
 
 
+def library_gemm_reference(layer, xs, T, steps):
+    """A reference point for the prefill roofline fraction, not part of the
+    path: torch.nn.functional.linear in bf16 (the vendor GEMM library) on the
+    prefill shapes of the layer with dense random weights (no signs, no
+    scales): stage 1 = x [T][d_in] times a [r][d_in] weight, stage 2 =
+    t [T][r] times a [d_out][r] weight, for every linear.  HIP events bracket
+    `steps` repetitions of each stage."""
+    import torch
+    F = torch.nn.functional
+    w1 = [torch.randn((lin.r, lin.d_in), device="cuda", dtype=torch.bfloat16) for lin in layer]
+    w2 = [torch.randn((lin.d_out, lin.r), device="cuda", dtype=torch.bfloat16) for lin in layer]
+    ts = [torch.randn((T, lin.r), device="cuda", dtype=torch.bfloat16) for lin in layer]
+    stages = [lambda: [F.linear(xs[lin.d_in], w1[i]) for i, lin in enumerate(layer)],
+              lambda: [F.linear(ts[i], w2[i]) for i in range(len(layer))]]
+    s = torch.cuda.current_stream()
+    out = []
+    for run in stages:
+        for _ in range(3):
+            run()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(s)
+        for _ in range(steps):
+            run()
+        e1.record(s)
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / steps * 1e-3)
+    f = sum(2 * T * lin.r * (lin.d_in + lin.d_out) for lin in layer)
+    t = out[0] + out[1]
+    return {"what": "torch bf16 F.linear (vendor GEMM library) on the same shapes, dense weights",
+            "stage1_us": out[0] * 1e6, "stage2_us": out[1] * 1e6, "ms_per_layer": t * 1e3,
+            "TFLOPs": f / t / 1e12, "frac": f / t / 1e12 / BF16_PEAK_TFLOPS}
+
+
 def prefill_leg(w, T, steps):
     """One layer of the workload's linears at T tokens as one GEMM-path group:
     stage 1 (and the d_in-piece reduce) for all linears in one launch, then
@@ -261,7 +296,8 @@ def prefill_leg(w, T, steps):
             "stage1_us": t1 * 1e6, "stage2_us": t2 * 1e6,
             "stage1_TFLOPs": f1 / t1 / 1e12, "stage2_TFLOPs": f2 / t2 / 1e12,
             "roofline": {"bound": "mfma", "achieved": flops / t / 1e12, "peak": BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": flops / t / 1e12 / BF16_PEAK_TFLOPS}}
+                         "unit": "TFLOP/s", "frac": flops / t / 1e12 / BF16_PEAK_TFLOPS},
+            "library_bf16_gemm": library_gemm_reference(layer, xs, T, steps)}
 
 
 def main():
