@@ -123,6 +123,7 @@ struct MRun {
     int ops2;                  // stage-2 operands (steps) the LDS holds at once
     int dma2;                  // stage 2 runs k_stage2r (all operands and h fit the LDS)
     int flush1;                // fused stage 1: latent tiles per item (F)
+    int tsplit;                // fused stage 1: waves split the item's tiles (1) or its K-groups (0)
     int ystage;                // k_stage2r collects the item's outputs in LDS, stored after its stream
     int64_t items0, items1, itemsF, items2;
     int64_t base0, base1, baseF, base2;   // item of workgroup 0 in each launch (0: all items)
@@ -588,11 +589,18 @@ __device__ __forceinline__ void emit_piece(const float (&v)[8], uint8_t *rec0, i
 
 // Item = (linear, path, chunk of up to kMaxKcf K-groups of d_in).  The
 // workgroup turns g_p (.) x over its chunk into compact limb records in LDS
-// (g and token 0 of x are loaded first), then wave w streams K-groups
-// [w*sub, (w+1)*sub) of the chunk across every 64-latent tile with kWin1
-// plane loads in flight (rotating register slots, as k_stage2r).  At each tile
-// end the four waves' partial sums meet in LDS and are added in wave order:
-// one partial per (chunk, token, latent), in a fixed summation order.
+// (g and token 0 of x are loaded first), then each wave streams its share of
+// the item's (tile, K-group) pairs with kWin1 plane loads in flight (rotating
+// register slots, as k_stage2r).  Two ways to share them (run.tsplit):
+//   - K split: wave w takes K-groups [w*sub, (w+1)*sub) of the chunk across
+//     every 64-latent tile of the item; at the end the four waves' partial
+//     sums meet in LDS and are added in wave order.  Needs no more tiles than
+//     one, but the LDS of the partials is [F][kWaves][T][64] floats.
+//   - tile split: wave w takes tiles w, w+4, ... of the item across every
+//     K-group of the chunk, so each latent has one wave and the partials need
+//     [F][T][64] floats: with more tokens an item still covers many tiles.
+// Either way one partial per (chunk, token, latent), in a fixed summation
+// order.
 // COHERENT: the partial sums are read back inside the same launch by another
 // workgroup (the one-launch pass), so they are stored at device scope.
 template <int NL, bool COHERENT>
@@ -634,23 +642,28 @@ __device__ __forceinline__ void stage1f_item(const MRun &run, const MLin &L, int
     }
 
     // ---- first plane loads ----------------------------------------------------
+    const bool ts = run.tsplit != 0;
     const int sub = (L.kcg + kWaves - 1) / kWaves;
-    const int ka = wave * sub;                                         // chunk-local K-group
-    const int nk = (int)imax(0, imin(sub, nkg - ka));
+    const int ka = ts ? 0 : wave * sub;                                // chunk-local K-group
+    const int nk = ts ? nkg : (int)imax(0, imin(sub, nkg - ka));
     const int tile0 = rg * run.flush1;                                 // first 64-latent tile of the item
     const int ntile = (int)imin(run.flush1, cdiv(L.r_p, kTile) - tile0);
-    const int total = ntile * nk;
+    // this wave's tiles of the item: tf, tf + tstep, ... (wt of them)
+    const int tf = ts ? wave : 0, tstep = ts ? kWaves : 1;
+    const int wt = ts ? (ntile > wave ? (int)cdiv(ntile - wave, kWaves) : 0) : ntile;
+    const int total = wt * nk;
     const __amdgpu_buffer_rsrc_t rv =
         make_rsrc(L.v_bits + (int64_t)p * L.kw_v * L.ld_v, (int64_t)L.kw_v * L.ld_v * 4);
-    const uint32_t vo = (uint32_t)(((int64_t)((kg0 + ka) * 4 + gq) * L.ld_v + tile0 * kTile + 4 * r16) * 4);
+    const uint32_t vo =
+        (uint32_t)(((int64_t)((kg0 + ka) * 4 + gq) * L.ld_v + (tile0 + tf) * kTile + 4 * r16) * 4);
     const uint32_t group4 = (uint32_t)(4 * L.ld_v * 4);
     // next (tile, K-group) to load; selects only, so every load is issued
     // on every path and the compiler can count them
-    const int ltiles = nk > 0 ? ntile : 0;
+    const int ltiles = nk > 0 ? wt : 0;
     int lt = 0, lk = 0;
     auto next_off = [&]() -> uint32_t {
-        const bool live = lt < ltiles && (tile0 + lt) * kTile + 4 * r16 < L.r_p;
-        const uint32_t o = live ? vo + (uint32_t)(lt * kTile * 4) + (uint32_t)lk * group4 : kOOB;
+        const bool live = lt < ltiles && (tile0 + tf + lt * tstep) * kTile + 4 * r16 < L.r_p;
+        const uint32_t o = live ? vo + (uint32_t)(lt * tstep * kTile * 4) + (uint32_t)lk * group4 : kOOB;
         const bool wrap = lk + 1 == nk;
         lt = wrap ? lt + 1 : lt;
         lk = wrap ? 0 : lk + 1;
@@ -728,9 +741,9 @@ __device__ __forceinline__ void stage1f_item(const MRun &run, const MLin &L, int
     // partial sums through a buffer descriptor: a flat store would be counted
     // with the LDS operations too, and every later wait would become a full one
     const __amdgpu_buffer_rsrc_t rpart = make_rsrc(L.part, (int64_t)L.nchunks * T * Rtot * 4);
-    // Tile t done: this wave's partials go to its LDS slot, with no wait.
+    // The wave's t-th tile done: its partials go to their LDS slot, with no wait.
     auto tile_end = [&](int t) {
-        float *mine = red + ((size_t)(t * kWaves + wave) * T) * 64;
+        float *mine = red + ((size_t)(ts ? tf + t * tstep : t * kWaves + wave) * T) * 64;
 #pragma unroll
         for (int s = 0; s < 4 / R::S1; ++s) {
             const int n = gq * (4 / R::S1) + s;
@@ -767,17 +780,18 @@ __device__ __forceinline__ void stage1f_item(const MRun &run, const MLin &L, int
             slot[k] = load_rows(rv, next_off());
         }
     }
-    if (nk == 0)
+    if (nk == 0 && !ts)
         for (int t = 0; t < ntile; ++t) tile_end(t);                  // zeros
 
-    // every wave's partials in LDS: add them in wave order, write row-contiguous
+    // every wave's partials in LDS: add them in wave order (K split), write
+    // row-contiguous
     lds_meet();
     const int per = T * 64;                                           // floats of one wave's tile
     for (int f = tid; f < ntile * per; f += kThreads) {
         const int k = f / per, rem = f - k * per;
         const int n = rem >> 6, row = (tile0 + k) * kTile + (rem & 63);
-        const float *q = red + (size_t)k * kWaves * per + rem;
-        const float sum = ((q[0] + q[per]) + q[2 * per]) + q[3 * per];
+        const float *q = red + (size_t)k * (ts ? 1 : kWaves) * per + rem;
+        const float sum = ts ? q[0] : ((q[0] + q[per]) + q[2 * per]) + q[3 * per];
         const uint32_t po = (uint32_t)((((int64_t)c * T + n) * Rtot + (int64_t)p * L.r_p + row) * 4);
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sum), rpart, row < L.r_p ? po : kOOB, 0,
                                               COHERENT ? kDeviceScope : 0);
@@ -1453,8 +1467,17 @@ constexpr int64_t kFusedBytes = 192 * 1024;    // V-plane bytes per fused stage-
 // Fused form: an item covers at most F latent tiles, as many as the LDS of its
 // cross-wave sums ([F][kWaves][T][64] floats) holds within kRedBudget.
 constexpr size_t kRedBudget = 24 * 1024;
-int flush1_for(int64_t T) { return (int)imax(1, (int64_t)kRedBudget / ((int64_t)kWaves * T * 64 * 4)); }
-size_t red1_bytes(int64_t T, int F) { return (size_t)F * kWaves * T * 64 * 4; }
+int flush1_for(int64_t T, int ts) {
+    return (int)imax(1, (int64_t)kRedBudget / ((ts ? 1 : kWaves) * T * 64 * 4));
+}
+size_t red1_bytes(int64_t T, int F, int ts) { return (size_t)F * (ts ? 1 : kWaves) * T * 64 * 4; }
+// The fused stage 1 splits an item's tiles among the waves when every linear
+// has at least one 64-latent tile per wave, else its K-groups.
+bool tsplit_for(const Linear *ls, int n) {
+    for (int j = 0; j < n; ++j)
+        if (cdiv(ls[j].r_p, kTile) < kWaves) return false;
+    return n > 0;
+}
 
 // Steps the stage-2 LDS holds: all steps of the largest linear when they fit,
 // else a multiple of the batch (at least one batch, which may exceed 64 KB).
@@ -1481,6 +1504,7 @@ int ops2_for(const Shape &s, int steps_max) {
 struct Grain {
     int64_t fused_bytes = kFusedBytes;
     int tiles2 = kTilesPerItem2;
+    int tsplit = 0;       // fused stage 1 splits tiles among the waves (tsplit_for)
 };
 
 size_t plan_linear(const Linear &a, const Shape &s, bool many, MLin *m, Grain gr = Grain{}) {
@@ -1515,7 +1539,7 @@ size_t plan_linear(const Linear &a, const Shape &s, bool many, MLin *m, Grain gr
         const int64_t nch = cdiv(m->kgv, kc);
         m->kcg = (int32_t)cdiv(m->kgv, nch);
         m->nchunks = (int32_t)cdiv(m->kgv, m->kcg);
-        m->nrg = (int32_t)cdiv(cdiv(a.r_p, kTile), flush1_for(a.T));
+        m->nrg = (int32_t)cdiv(cdiv(a.r_p, kTile), flush1_for(a.T, gr.tsplit));
         m->kcp = 0;
         m->nprep = 0;
         m->xvec = (a.d_in % 8 == 0 && ((uintptr_t)a.x & 15) == 0 && ((uintptr_t)a.g & 15) == 0) ? 1 : 0;
@@ -1632,9 +1656,9 @@ int launch_shape(const Shape &s, const MRun &run, const MLin &single, const Lds 
     return LB_EUNSUPPORTED;
 }
 
-void lds_add(Lds *l, const MLin &m, const Shape &s, int ops2, int64_t T, int F) {
+void lds_add(Lds *l, const MLin &m, const Shape &s, int ops2, int64_t T, int F, int ts) {
     const size_t prep = (size_t)m.kcp * s.NB1 * m.R1 * kRec;
-    const size_t s1 = fused1(s) ? (size_t)m.kcg * m.R1 * kRec + red1_bytes(T, F) : (size_t)m.kcg * s.NB1 * kOpS;
+    const size_t s1 = fused1(s) ? (size_t)m.kcg * m.R1 * kRec + red1_bytes(T, F, ts) : (size_t)m.kcg * s.NB1 * kOpS;
     const size_t lat = (size_t)2 * s.NB2 * m.R2 * kRec;
     const size_t s2 = (size_t)ops2 * s.NB2 * kOpS;
     if (prep > l->prep) l->prep = prep;
@@ -1667,7 +1691,9 @@ int mfma_decode_forward(const Linear &a, void *ws, hipStream_t st) {
     Shape s;
     if (!shape_for(a.T, a.y_dtype, &s)) return LB_EUNSUPPORTED;
     MLin m;
-    plan_linear(a, s, false, &m);
+    Grain gr;
+    gr.tsplit = fused1(s) && tsplit_for(&a, 1) ? 1 : 0;
+    plan_linear(a, s, false, &m, gr);
     bind_ws(&m, a, s, (uint8_t *)ws);
     MRun run{};
     run.T = (int)a.T;
@@ -1682,8 +1708,9 @@ int mfma_decode_forward(const Linear &a, void *ws, hipStream_t st) {
     run.items2 = m.n2;
     run.table = nullptr;
     Lds lds{};
-    run.flush1 = (int)imin(flush1_for(a.T), cdiv(m.r_p, kTile));
-    lds_add(&lds, m, s, run.ops2, a.T, run.flush1);
+    run.tsplit = gr.tsplit;
+    run.flush1 = (int)imin(flush1_for(a.T, run.tsplit), cdiv(m.r_p, kTile));
+    lds_add(&lds, m, s, run.ops2, a.T, run.flush1, run.tsplit);
     return launch_shape(s, run, m, lds, st);
 }
 
@@ -1739,6 +1766,7 @@ bool pass_form(const Linear *ls, int n, const Shape &s) {
 
 Grain group_grain(const Linear *ls, int n, const Shape &s) {
     Grain g;
+    g.tsplit = fused1(s) && tsplit_for(ls, n) ? 1 : 0;
     const int kc_floor = pass_form(ls, n, s) ? kPassMinKcg : 4;
     for (int pass = 0; pass < 8; ++pass) {
         int64_t i1 = 0, i2 = 0, kc_min = kMaxKcf;
@@ -1825,8 +1853,9 @@ int mfma_group_prepare(const Linear *ls, int n, int64_t T, int y_dtype, void *ws
     hs->lds = Lds{};
     int64_t ntile_max = 1;
     for (int j = 0; j < n; ++j) ntile_max = imax(ntile_max, cdiv(tab[(size_t)j].r_p, kTile));
-    run.flush1 = (int)imin(flush1_for(T), ntile_max);
-    for (int j = 0; j < n; ++j) lds_add(&hs->lds, tab[(size_t)j], hs->s, run.ops2, T, run.flush1);
+    run.tsplit = gr.tsplit;
+    run.flush1 = (int)imin(flush1_for(T, run.tsplit), ntile_max);
+    for (int j = 0; j < n; ++j) lds_add(&hs->lds, tab[(size_t)j], hs->s, run.ops2, T, run.flush1, run.tsplit);
     int32_t *lin0 = (int32_t *)cur;
     int32_t *lin1 = (int32_t *)((uint8_t *)lin0 + rup256((size_t)i0 * 4));
     int32_t *linF = (int32_t *)((uint8_t *)lin1 + rup256((size_t)i1 * 4));
