@@ -40,6 +40,7 @@
 //   stage 2: item = (linear, block of output rows): each wave walks 64-row
 //            tiles, streaming the U planes of both paths into one accumulator set.
 #include <algorithm>
+#include <cstdlib>
 #include <vector>
 
 #include "lb_internal.h"
@@ -1724,6 +1725,7 @@ struct MGroupHost {
     uint32_t epoch;      // number of the next one-launch run
     int64_t n1_max;      // most stage-1 items of one linear
     int64_t nf;          // latent groups of all linears (counters in arrive)
+    uint64_t wrap;       // the counters start over before (epoch + 1) * n1_max reaches this
     int n;               // linears
 };
 
@@ -1951,6 +1953,13 @@ int mfma_group_prepare(const Linear *ls, int n, int64_t T, int y_dtype, void *ws
     hs->epoch = 0;
     hs->n = n;
     hs->nf = nf;
+    // 2^31 keeps every counter within 31 bits; LB_PASS_EPOCH_LIMIT (a positive
+    // number below that) lowers it, so that tests can run through the reset
+    hs->wrap = 1ull << 31;
+    if (const char *e = getenv("LB_PASS_EPOCH_LIMIT")) {
+        const long long v = atoll(e);
+        if (v > 0 && v < (1ll << 31)) hs->wrap = (uint64_t)v;
+    }
     run.T = (int)T;
     run.x_dtype = ls[0].x_dtype;
     run.y_dtype = y_dtype;
@@ -2018,7 +2027,7 @@ int mfma_group_run(const void *host_state, hipStream_t st, int stage_mask) {
         // the counters reach (epoch + 1) * nchunks or (epoch + 1) * P * nrg,
         // at most (epoch + 1) * items1 of a linear: start over before that
         // leaves 31 bits (arrive and ready are contiguous)
-        if ((uint64_t)(hs->epoch + 1) * (uint64_t)hs->n1_max >= (1ull << 31)) {
+        if ((uint64_t)(hs->epoch + 1) * (uint64_t)hs->n1_max >= hs->wrap) {
             const int64_t words = (hs->nf + hs->n) * kFlagStride;
             k_zero_words<<<(unsigned)imin(1024, cdiv(words, 256)), 256, 0, st>>>(r.arrive, words);
             if (int rc = last_launch_status()) return rc;

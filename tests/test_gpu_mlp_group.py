@@ -135,18 +135,14 @@ def test_group_run_matches_staged_run(key, T, out):
     st.group.release()
 
 
-@pytest.mark.parametrize("key,T,out", [("c3", 1, "bf16"), ("c4", 1, "bf16"), ("c5", 1, "f32"), ("c3", 2, "bf16"),
-                                       ("c5", 6, "bf16"), ("c5", 4, "f32")])
-def test_pass_reads_each_runs_inputs(key, T, out):
-    """The one-launch pass (T = 1) hands each run's latents to that run's
-    stage 2: with other activations between runs, every run equals the staged
-    run of its own inputs bit for bit (a stale hand-off would repeat the
-    previous run's outputs).  Larger T runs three launches per run, checked
-    the same way."""
+def _runs_match_staged(key, T, out, order):
+    """Runs a 2-layer stack of the workload as one group with two sets of
+    activations, loaded in `order` before each run, and checks every run
+    against the staged run (stage 1 then stage 2) of its own inputs, bit for
+    bit."""
     torch = torch_or_skip()
     from binarized_rank_linear_amd.stack import LayerStack
     w = synth.WORKLOADS[key]
-    say("pass inputs", key, "T", T, out)
 
     def make(L, i, di, do, rp, P):
         return synth.device_layer(synth.layer_seed(L, i) + 2000, di, do, rp, P)
@@ -175,7 +171,7 @@ def test_pass_reads_each_runs_inputs(key, T, out):
         torch.cuda.synchronize()
         refs.append([[y.clone() for y in row] for row in st.outputs])
     assert not torch.equal(bits(refs[0][0][0]), bits(refs[1][0][0]))
-    for k in (0, 1, 1, 0, 1):
+    for k in order:
         load(k)
         st.group.run()
         torch.cuda.synchronize()
@@ -183,6 +179,30 @@ def test_pass_reads_each_runs_inputs(key, T, out):
             for i, y in enumerate(row):
                 assert torch.equal(bits(y), bits(refs[k][L][i])), (k, L, i)
     st.group.release()
+
+
+@pytest.mark.parametrize("key,T,out", [("c3", 1, "bf16"), ("c4", 1, "bf16"), ("c5", 1, "f32"), ("c3", 2, "bf16"),
+                                       ("c5", 6, "bf16"), ("c5", 4, "f32")])
+def test_pass_reads_each_runs_inputs(key, T, out):
+    """The one-launch pass (T = 1) hands each run's latents to that run's
+    stage 2: with other activations between runs, every run equals the staged
+    run of its own inputs bit for bit (a stale hand-off would repeat the
+    previous run's outputs).  Larger T runs three launches per run, checked
+    the same way."""
+    say("pass inputs", key, "T", T, out)
+    _runs_match_staged(key, T, out, (0, 1, 1, 0, 1))
+
+
+@pytest.mark.parametrize("limit", ["1", "100"])
+def test_pass_counters_start_over(limit, monkeypatch):
+    """The one-launch pass's run counters start over (a fill kernel clears
+    them) before they would leave 31 bits.  With the limit lowered for the
+    group, that happens before every run (limit 1) or every few runs (100),
+    and every run still equals the staged run of its own inputs bit for
+    bit."""
+    monkeypatch.setenv("LB_PASS_EPOCH_LIMIT", limit)
+    say("pass counter reset, limit", limit)
+    _runs_match_staged("c5", 1, "bf16", (0, 1, 1, 0, 1, 0, 0, 1, 1))
 
 
 @pytest.mark.parametrize("T,out", [(1, "bf16"), (2, "bf16"), (5, "bf16"), (8, "bf16"), (1, "f32"), (3, "f32")])
