@@ -60,7 +60,8 @@ constexpr int kOpS = kOp + 64;            // plus one scale byte per lane
 constexpr int kLdsBudget = 64 * 1024;
 constexpr int kMaxKcg = 16;               // K-groups per stage-1 chunk (loads in flight per wave)
 constexpr int kBatch = 8;                 // stage-2 steps per load batch
-constexpr int kTilesPerItem2 = 8;         // 64-row tiles per wave in one stage-2 item
+constexpr int kTilesPerItem2 = 8;         // 64-row tiles per wave in one stage-2 item, at most
+constexpr int kSteps2 = 40;               // (tile, K-group) steps a stage-2 item aims for, per 4 activation rows
 constexpr int kPreVec = 8;                // operand vectors a thread loads before the plane loads
 constexpr int kWin2 = 8;                  // stage 2 (streaming form): plane loads in flight per wave
 constexpr int kWin1 = 8;                  // stage 1 (fused form): plane loads in flight per wave
@@ -1199,10 +1200,11 @@ __device__ __forceinline__ void stage2r_item(const MRun &run, const MLin &L, int
     // 16-byte pieces when every row group of 8 starts 16-byte aligned and none straddles d_out
     const bool hvec = (L.d_out & 7) == 0 && ((uintptr_t)L.h & 15) == 0;
     v4u hq[kHRows / (kThreads / 2) / 8];
+    const int64_t row_end = imin(L.d_out, row_begin + (int64_t)tiles * kRG);   // rows of the item
 #pragma unroll
     for (int k = 0; k < kHRows / (kThreads / 2) / 8; ++k) {
         const int64_t row = row_begin + hr + k * (kThreads / 2) * 8;
-        const bool ok = hvec && hp < L.P && row + 8 <= L.d_out;
+        const bool ok = hvec && hp < L.P && row + 8 <= row_end;
         hq[k] = __builtin_amdgcn_raw_buffer_load_b128(rh, ok ? (uint32_t)(((int64_t)hp * L.d_out + row) * 2) : kOOB, 0, 0);
     }
 
@@ -1559,7 +1561,12 @@ size_t plan_linear(const Linear &a, const Shape &s, bool many, MLin *m, Grain gr
         m->nprep = (int32_t)cdiv(m->kgv, kcp);
     }
     m->kgs = (int32_t)cdiv((int64_t)a.P * m->kw_u, 4);
-    int tiles = gr.tiles2;
+    // long K (many K-groups per tile): fewer tiles per item, so that an item
+    // streams about kSteps2 (tile, K-group) steps per 4 activation rows and the
+    // last items of a launch end close together.  (Every item first loads all
+    // of its linear's operands, R2 rows per K-group, so with more rows it
+    // keeps more tiles.)
+    int tiles = (int)imax(1, imin(gr.tiles2, kSteps2 * m->R2 / (4 * m->kgs)));
     if (!many)   // a lone linear: fewer tiles per item until the chip has work
         while (tiles > 1 && cdiv(a.d_out, (int64_t)kRG * tiles) < 512) tiles /= 2;
     m->rows2 = kRG * tiles;
