@@ -1753,11 +1753,12 @@ constexpr int64_t kMinGroupItems = 1024;
 // form (which spreads that sum over many workgroups) goes down to 4.
 constexpr int kPassMinKcg = 16;
 
-// Token counts the one-launch pass serves: one token (either output dtype).
-// On the 32-, 40- and 80-layer stacks it measured 3 to 7 percent faster than
-// the three launches there, but slower from T = 4 on (by 10 to 50 percent) and
-// at T = 2 on two of the three stacks.
-bool pass_tokens(const Shape &s, int64_t T) { return fused1(s) && T == 1; }
+// Token counts the one-launch pass serves: those that fill at most 8 of the
+// 16 stage-2 activation rows (bf16 out: T <= 2, fp32 out: T = 1).  On the 32-,
+// 40- and 80-layer stacks it measured 4 to 7 percent faster than the three
+// launches at T = 1 and -1 to +6 percent at T = 2, but 12 to 26 percent
+// slower at T = 4, where its workgroups hold stage 2's 16-row operands.
+bool pass_tokens(const Shape &s, int64_t T) { return fused1(s) && rows2(s, T) <= 8; }
 
 // Whether a group runs as one launch (k_pass): such a token count and a stage
 // 2 whose operands fit the LDS (the K-groups, and so that test, do not depend

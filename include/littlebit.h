@@ -204,7 +204,8 @@ int lb_grouped_prepare(const lb_linear_desc *descs, int n, int64_t T, int x_dtyp
 
 /* Run a prepared group: every linear's y = layer(x), in a few launches for the
  * whole group (all first contractions, then all second contractions).  A
- * decode group at T = 1 whose operands fit the LDS runs as ONE launch: each
+ * decode group at T <= 2 (bf16 output) or T = 1 (fp32) whose operands fit
+ * the LDS runs as ONE launch: each
  * linear's stage 2 starts as soon as its own stage 1 and latents are done.
  * That launch numbers its runs in ws (counters that keep counting), so runs
  * of one group must be issued one after the other, from one thread at a

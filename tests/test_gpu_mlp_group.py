@@ -184,11 +184,11 @@ def _runs_match_staged(key, T, out, order):
 @pytest.mark.parametrize("key,T,out", [("c3", 1, "bf16"), ("c4", 1, "bf16"), ("c5", 1, "f32"), ("c3", 2, "bf16"),
                                        ("c5", 6, "bf16"), ("c5", 4, "f32")])
 def test_pass_reads_each_runs_inputs(key, T, out):
-    """The one-launch pass (T = 1) hands each run's latents to that run's
-    stage 2: with other activations between runs, every run equals the staged
-    run of its own inputs bit for bit (a stale hand-off would repeat the
-    previous run's outputs).  Larger T runs three launches per run, checked
-    the same way."""
+    """The one-launch pass (bf16 T <= 2, fp32 T = 1) hands each run's latents
+    to that run's stage 2: with other activations between runs, every run
+    equals the staged run of its own inputs bit for bit (a stale hand-off
+    would repeat the previous run's outputs).  Larger T runs three launches
+    per run, checked the same way."""
     say("pass inputs", key, "T", T, out)
     _runs_match_staged(key, T, out, (0, 1, 1, 0, 1))
 
@@ -209,8 +209,8 @@ def test_pass_counters_start_over(limit, monkeypatch):
 def test_pass_ragged_mixed_group(T, out):
     """A decode group of ragged linears, with and without the residual path
     (d_in, d_out and r_p off every tile size), runs as one launch per pass
-    (T = 1; three launches beyond): every run equals the staged run bit for
-    bit, and the oracle within the tolerance.  The last two ranks span two
+    (bf16 T <= 2, fp32 T = 1; three launches beyond): every run equals the
+    staged run bit for bit, and the oracle within the tolerance.  The last two ranks span two
     stage-1 latent groups per path at T = 1 (more than 24 tiles of 64
     latents), the second one ragged."""
     torch = torch_or_skip()
