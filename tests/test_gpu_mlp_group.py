@@ -193,6 +193,15 @@ def test_pass_reads_each_runs_inputs(key, T, out):
     _runs_match_staged(key, T, out, (0, 1, 1, 0, 1))
 
 
+def test_pass_many_runs():
+    """200 one-launch passes in a row (2-layer 80-layer-stack slice, T = 1),
+    the two input sets in an irregular order: every run equals the staged run
+    of its own inputs bit for bit (the hand-off between workgroups uses no
+    cache-wide fence, so a stale operand would show as a repeated output)."""
+    say("pass, 200 runs")
+    _runs_match_staged("c5", 1, "bf16", tuple((k * 7 // 3 + k // 5) % 2 for k in range(200)))
+
+
 @pytest.mark.parametrize("limit", ["1", "100"])
 def test_pass_counters_start_over(limit, monkeypatch):
     """The one-launch pass's run counters start over (a fill kernel clears
