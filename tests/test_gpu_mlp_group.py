@@ -214,19 +214,33 @@ def test_pass_counters_start_over(limit, monkeypatch):
     _runs_match_staged("c5", 1, "bf16", (0, 1, 1, 0, 1, 0, 0, 1, 1))
 
 
-@pytest.mark.parametrize("T,out", [(1, "bf16"), (2, "bf16"), (5, "bf16"), (8, "bf16"), (1, "f32"), (3, "f32")])
-def test_pass_ragged_mixed_group(T, out):
+# (d_in, d_out, r_p, P) per linear.  "mixed": ranks from 16 to 2000, some
+# under 4 latent tiles of 64 (stage 1 splits K-groups among its waves);
+# "wide": every rank at least 4 tiles (4 to 23), none a multiple of 64
+# latents (stage 1 splits tiles among its waves).
+RAGGED = {
+    "mixed": [(1000, 700, 48, 2), (520, 130, 16, 1), (2048, 1536, 160, 2), (96, 1100, 32, 1),
+              (1024, 333, 64, 2), (4096, 257, 304, 2), (1024, 512, 1696, 2), (640, 384, 2000, 1)],
+    "wide": [(1000, 700, 304, 2), (520, 130, 208, 1), (2048, 1536, 416, 2), (600, 1100, 1456, 1),
+             (1024, 333, 1040, 2)],
+}
+
+
+@pytest.mark.parametrize("T,out,kind", [(1, "bf16", "mixed"), (2, "bf16", "mixed"), (5, "bf16", "mixed"),
+                                        (8, "bf16", "mixed"), (1, "f32", "mixed"), (3, "f32", "mixed"),
+                                        (1, "bf16", "wide"), (2, "bf16", "wide"), (6, "bf16", "wide"),
+                                        (1, "f32", "wide"), (4, "f32", "wide")])
+def test_pass_ragged_mixed_group(T, out, kind):
     """A decode group of ragged linears, with and without the residual path
     (d_in, d_out and r_p off every tile size), runs as one launch per pass
     (bf16 T <= 2, fp32 T = 1; three launches beyond): every run equals the
-    staged run bit for bit, and the oracle within the tolerance.  The last two ranks span two
-    stage-1 latent groups per path at T = 1 (more than 24 tiles of 64
-    latents), the second one ragged."""
+    staged run bit for bit, and the oracle within the tolerance.  In the mixed
+    set the last two ranks span two stage-1 latent groups per path at T = 1
+    (more than 24 tiles of 64 latents), the second one ragged."""
     torch = torch_or_skip()
     import binarized_rank_linear_amd as lb
-    say("pass ragged group T", T, out)
-    shapes = [(1000, 700, 48, 2), (520, 130, 16, 1), (2048, 1536, 160, 2), (96, 1100, 32, 1),
-              (1024, 333, 64, 2), (4096, 257, 304, 2), (1024, 512, 1696, 2), (640, 384, 2000, 1)]
+    say("pass ragged group T", T, out, kind)
+    shapes = RAGGED[kind]
     odt = torch.bfloat16 if out == "bf16" else torch.float32
     items, inps, xs = [], [], []
     for i, (d_in, d_out, r_p, P) in enumerate(shapes):
