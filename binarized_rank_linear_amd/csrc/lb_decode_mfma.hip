@@ -596,8 +596,9 @@ __device__ __forceinline__ void emit_piece(const float (&v)[8], uint8_t *rec0, i
 // register slots, as k_stage2r).  Two ways to share them (run.tsplit):
 //   - K split: wave w takes K-groups [w*sub, (w+1)*sub) of the chunk across
 //     every 64-latent tile of the item; at the end the four waves' partial
-//     sums meet in LDS and are added in wave order.  Needs no more tiles than
-//     one, but the LDS of the partials is [F][kWaves][T][64] floats.
+//     sums meet in LDS and are added in wave order.  It keeps all four waves
+//     busy with any number of tiles, but the partials take [F][kWaves][T][64]
+//     floats of LDS.
 //   - tile split: wave w takes tiles w, w+4, ... of the item across every
 //     K-group of the chunk, so each latent has one wave and the partials need
 //     [F][T][64] floats: with more tokens an item still covers many tiles.
