@@ -252,6 +252,41 @@ def library_gemm_reference(layer, xs, T, steps):
             "TFLOPs": f / t / 1e12, "frac": f / t / 1e12 / BF16_PEAK_TFLOPS}
 
 
+def prefill_per_linear(layer, xs, T, steps, P):
+    """Each linear of the prefill layer as a group of its own (both stages,
+    HIP events around `steps` runs), against its own roofline: the larger of
+    its flops at the bf16 MFMA peak and its bytes at the HBM peak (signs,
+    scales, x, y and the bf16 t round trip between the stages)."""
+    import torch
+    import binarized_rank_linear_amd as lb
+    s = torch.cuda.current_stream()
+    out = []
+    for i, lin in enumerate(layer):
+        y = torch.empty((T, lin.d_out), dtype=torch.bfloat16, device="cuda")
+        g = lb.Group([(xs[lin.d_in], y, lin)], T, torch.bfloat16, torch.bfloat16)
+        for _ in range(2):
+            g.run()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(s)
+        for _ in range(steps):
+            g.run()
+        e1.record(s)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / steps * 1e-3
+        g.release()
+        flops = 2 * T * lin.r * (lin.d_in + lin.d_out)
+        s1, s2 = linear_bytes(lin.d_in, lin.d_out, lin.r, P, T)
+        nbytes = s1 + s2 + 2 * T * lin.r * 2
+        t_mfma = flops / (BF16_PEAK_TFLOPS * 1e12)
+        t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+        out.append({"linear": "%dx%d r=%d" % (lin.d_in, lin.d_out, lin.r), "us": t * 1e6,
+                    "TFLOPs": flops / t / 1e12, "bound": "mfma" if t_mfma >= t_hbm else "hbm",
+                    "roofline_us": max(t_mfma, t_hbm) * 1e6, "frac": max(t_mfma, t_hbm) / t})
+    return out
+
+
 def prefill_leg(w, T, steps):
     """One layer of the workload's linears at T tokens as one GEMM-path group:
     stage 1 (and the d_in-piece reduce) for all linears in one launch, then
@@ -297,7 +332,8 @@ def prefill_leg(w, T, steps):
             "stage1_TFLOPs": f1 / t1 / 1e12, "stage2_TFLOPs": f2 / t2 / 1e12,
             "roofline": {"bound": "mfma", "achieved": flops / t / 1e12, "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": flops / t / 1e12 / BF16_PEAK_TFLOPS},
-            "library_bf16_gemm": library_gemm_reference(layer, xs, T, steps)}
+            "library_bf16_gemm": library_gemm_reference(layer, xs, T, steps),
+            "per_linear": prefill_per_linear(layer, xs, T, steps, 2 if w.residual else 1)}
 
 
 def main():
