@@ -5,9 +5,9 @@
 //   stage 1:  u = X . (diag(g_p) sign(V_p))        M = T, N = latents of all paths, K = d_in
 //             t = l (.) u, rounded to bf16         (the rank-r intermediate, workspace)
 //   stage 2:  y = t . (sign(U_p)^T diag(h_p))      M = T, N = d_out, K = latents of all paths
-// Both run as v_mfma_f32_32x32x16_bf16 with fp32 accumulation ("two smaller
-// binary matmuls with FP16 element-wise scaling between them", same page, the
-// compute paragraph; the scales enter rounded to bf16 here).
+// Both run as v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  The same page
+// (its compute paragraph) describes the layer as two binary products joined by
+// elementwise fp16 scalings; here the scales enter rounded to bf16.
 //
 // Sign operand: multiplying by -1 is a sign flip (same page, the note after
 // the proposition), so each operand pair is a bf16 scale pair (g per

@@ -1,7 +1,7 @@
-// lb_pack.hip -- sign packing: one bit per factor entry (sesamedisk page,
-// "How low-rank binarization works": sign-only storage costs one bit per
-// factor entry).  Bit b of word (w, o) = (src element 32w+b of the packed axis
-// at other-axis index o) < 0.  Offline, once per layer.
+// lb_pack.hip -- sign packing (sesamedisk page, "How low-rank binarization
+// works": each binary factor entry is stored as a single bit).  Bit b of word
+// (w, o) = (src element 32w+b of the packed axis at other-axis index o) < 0.
+// Offline, once per layer.
 #include "lb_internal.h"
 
 namespace lb {
