@@ -20,6 +20,7 @@ LB_EUNSUPPORTED = -2
 LB_EALIGN = -3
 LB_EWORKSPACE = -4
 LB_EHIP = -5
+LB_EDEVICE = -6
 
 LB_F32 = 0
 LB_BF16 = 1
@@ -28,6 +29,10 @@ LB_PATH_AUTO = 0
 LB_PATH_DECODE = 1
 LB_PATH_PREFILL = 2
 LB_PATH_DECODE_VALU = 3
+LB_GROUP_FAULT_TEST = 1 << 8
+
+LB_FAULT_HANDOFF_TIMEOUT = 1
+LB_FAULT_STALE_WORKSPACE = 2
 
 _i64 = ctypes.c_int64
 _vp = ctypes.c_void_p
@@ -42,6 +47,12 @@ class lb_factors(ctypes.Structure):
 class lb_linear_desc(ctypes.Structure):
     _fields_ = [("x", _vp), ("y", _vp), ("w", lb_factors), ("d_in", _i64), ("d_out", _i64),
                 ("r", _i64), ("residual", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class lb_linear_call(ctypes.Structure):
+    _fields_ = [("x", _vp), ("y", _vp), ("w", lb_factors), ("d_in", _i64), ("d_out", _i64),
+                ("r", _i64), ("T", _i64), ("residual", ctypes.c_int32), ("x_dtype", ctypes.c_int32),
+                ("y_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
 
 
 class LBError(RuntimeError):
@@ -106,6 +117,15 @@ def lib() -> ctypes.CDLL:
         L.lb_grouped_run_stage.restype = ctypes.c_int
         L.lb_grouped_release.argtypes = [_vp]
         L.lb_grouped_release.restype = ctypes.c_int
+        L.lb_linear_grouped_workspace_bytes.argtypes = [ctypes.POINTER(lb_linear_call), ctypes.c_int]
+        L.lb_linear_grouped_workspace_bytes.restype = _sz
+        L.lb_linear_forward_grouped.argtypes = [ctypes.POINTER(lb_linear_call), ctypes.c_int, _vp, _sz, _vp]
+        L.lb_linear_forward_grouped.restype = ctypes.c_int
+        L.lb_device_faults.argtypes = [_vp, ctypes.POINTER(ctypes.c_uint32)]
+        L.lb_device_faults.restype = ctypes.c_int
+        L.lb_linear_path.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_uint]
+        L.lb_linear_path.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -304,6 +324,55 @@ def mlp_forward(x, gate: PackedLinear, up: PackedLinear, down: PackedLinear, out
                                 int(gate.residual), ws.data_ptr(), ws.numel(), flags,
                                 _stream_ptr(stream)), "lb_mlp_forward")
     return out
+
+
+def device_faults(stream=None) -> int:
+    """Waits for the stream, then reads and clears the device's fault bits
+    (LB_FAULT_*); 0 if no kernel reported a fault."""
+    f = ctypes.c_uint32(0)
+    rc = lib().lb_device_faults(_stream_ptr(stream), ctypes.byref(f))
+    if rc not in (LB_OK, LB_EDEVICE):
+        _check(rc, "lb_device_faults")
+    return f.value
+
+
+def linear_path(d_in: int, d_out: int, r: int, T: int, residual: bool, x_dtype, y_dtype,
+                flags: int = LB_PATH_AUTO) -> int:
+    """The kernel family (LB_PATH_DECODE / LB_PATH_PREFILL / LB_PATH_DECODE_VALU)
+    lb_linear_forward would run for these sizes (host only)."""
+    rc = lib().lb_linear_path(d_in, d_out, r, T, int(residual), _dtype_code(x_dtype),
+                              _dtype_code(y_dtype), flags)
+    if rc < 0:
+        _check(rc, "lb_linear_path")
+    return rc
+
+
+def _calls(items, flags):
+    arr = (lb_linear_call * len(items))()
+    for i, (x, y, layer) in enumerate(items):
+        _dev_check(x, y)
+        if x.shape[-1] != layer.d_in or y.shape[-1] != layer.d_out or x.shape[0] != y.shape[0]:
+            raise ValueError("item %d: x/y shapes do not match the layer" % i)
+        arr[i] = lb_linear_call(x.data_ptr(), y.data_ptr(), layer.struct(), layer.d_in, layer.d_out,
+                                layer.r, x.shape[0], int(layer.residual), _dtype_code(x.dtype),
+                                _dtype_code(y.dtype), flags)
+    return arr
+
+
+def grouped_workspace_bytes(items, flags: int = LB_PATH_AUTO) -> int:
+    return lib().lb_linear_grouped_workspace_bytes(_calls(items, flags), len(items))
+
+
+def linear_forward_grouped(items, flags: int = LB_PATH_AUTO, ws=None, stream=None):
+    """The stateless grouped call: items is a sequence of (x, y, PackedLinear);
+    every y is recomputed from its x (lb_linear_forward_grouped)."""
+    arr = _calls(items, flags)
+    need = lib().lb_linear_grouped_workspace_bytes(arr, len(items))
+    if ws is None or ws.numel() < need:
+        ws = workspace(need, items[0][0].device)
+    _check(lib().lb_linear_forward_grouped(arr, len(items), ws.data_ptr(), ws.numel(),
+                                           _stream_ptr(stream)), "lb_linear_forward_grouped")
+    return ws
 
 
 class Group:

@@ -1,6 +1,11 @@
 // lb_api.hip -- the C entry points of littlebit.h: argument checks, path
 // dispatch, workspace sizing, the SwiGLU block and layer groups.
+#include <algorithm>
+#include <atomic>
+#include <deque>
+#include <memory>
 #include <mutex>
+#include <random>
 #include <string.h>
 #include <unordered_map>
 #include <vector>
@@ -27,17 +32,24 @@ bool overlap(const void *a, size_t na, const void *b, size_t nb) {
 
 enum class Path { Valu, MfmaDecode, Gemm };
 
-// The path a request runs on.  Returns false for an invalid or unsupported flag.
-int choose_path(unsigned flags, int64_t T, int y_dtype, Path *out) {
+// Flag bits a call may carry: the path, and for groups the fault-report test.
+constexpr unsigned kLinearFlags = LB_PATH_MASK;
+constexpr unsigned kGroupFlags = LB_PATH_MASK | LB_GROUP_FAULT_TEST;
+
+// The path a request runs on (a: its sizes, and its strides when known).
+// Returns LB_EINVAL for an invalid path flag, LB_EUNSUPPORTED for a path the
+// request cannot take.
+int choose_path(unsigned flags, int64_t T, int y_dtype, Path *out, const Linear *a = nullptr) {
+    const bool mfma_ok = mfma_decode_supported(T, y_dtype) && (!a || mfma_decode_shape_ok(*a));
     switch (flags & LB_PATH_MASK) {
         case LB_PATH_AUTO:
             if (T <= kDecodeMaxT)
-                *out = mfma_decode_supported(T, y_dtype) ? Path::MfmaDecode : Path::Valu;
+                *out = mfma_ok ? Path::MfmaDecode : Path::Valu;
             else
                 *out = y_dtype == LB_BF16 ? Path::Gemm : Path::Valu;
             return LB_OK;
         case LB_PATH_DECODE:
-            *out = mfma_decode_supported(T, y_dtype) ? Path::MfmaDecode : Path::Valu;
+            *out = mfma_ok ? Path::MfmaDecode : Path::Valu;
             return LB_OK;
         case LB_PATH_PREFILL:
             if (y_dtype != LB_BF16) return LB_EUNSUPPORTED;
@@ -137,6 +149,7 @@ const char *lb_status_string(int status) {
         case LB_EALIGN: return "misaligned pointer or stride";
         case LB_EWORKSPACE: return "workspace missing or too small";
         case LB_EHIP: return "HIP runtime error";
+        case LB_EDEVICE: return "a kernel reported a fault (lb_device_faults)";
         default: return "unknown status";
     }
 }
@@ -188,13 +201,16 @@ size_t lb_linear_workspace_bytes(int64_t d_in, int64_t d_out, int64_t r, int64_t
     Linear a{};
     if (check_shape(d_in, d_out, r, T, residual, &a)) return 0;
     a.x_dtype = a.y_dtype = LB_BF16;
+    if (flags & ~kLinearFlags) return 0;
     size_t need = 0;
-    // AUTO may pick either path for T > 32 depending on the output dtype.
+    // AUTO may pick either path for T > 32 depending on the output dtype, and
+    // the vector-ALU kernels for strides the decode kernels do not address.
     const int ys[2] = {LB_BF16, LB_F32};
     for (int yi = 0; yi < 2; ++yi) {
         Path p;
         if (choose_path(flags, T, ys[yi], &p)) continue;
-        const size_t b = path_workspace(p, a);
+        size_t b = path_workspace(p, a);
+        if (p == Path::MfmaDecode) b = std::max(b, path_workspace(Path::Valu, a));
         if (b > need) need = b;
     }
     return rup256(need);
@@ -208,8 +224,9 @@ int lb_linear_forward(const void *x, int x_dtype, void *y, int y_dtype, const lb
     if ((rc = check_shape(d_in, d_out, r, T, residual, &a))) return rc;
     if ((rc = check_factors(w, &a))) return rc;
     if ((rc = check_io(x, x_dtype, y, y_dtype, &a))) return rc;
+    if (flags & ~kLinearFlags) return LB_EINVAL;
     Path p;
-    if ((rc = choose_path(flags, T, y_dtype, &p))) return rc;
+    if ((rc = choose_path(flags, T, y_dtype, &p, &a))) return rc;
     if (T == 0) return LB_OK;
     const size_t need = path_workspace(p, a);
     if (need > 0) {
@@ -257,7 +274,8 @@ int lb_mlp_forward(const void *x, int x_dtype, void *y, int y_dtype, const lb_fa
                 (size_t)(T * d_model) * act_size(y_dtype)))
         return LB_EINVAL;
     Path p;
-    if ((rc = choose_path(flags, T, y_dtype, &p))) return rc;
+    if (flags & ~kLinearFlags) return LB_EINVAL;
+    if ((rc = choose_path(flags, T, y_dtype, &p, &ad))) return rc;
     if (T == 0) return LB_OK;
     const size_t need = lb_mlp_workspace_bytes(d_model, d_ff, r_gu, r_down, T, residual, flags);
     if (!ws || ws_bytes < need) return LB_EWORKSPACE;
@@ -277,7 +295,7 @@ int lb_mlp_forward(const void *x, int x_dtype, void *y, int y_dtype, const lb_fa
     au.y = zu;
     ag.y_dtype = au.y_dtype = LB_F32;
     Path pi;
-    if ((rc = choose_path(flags, T, LB_F32, &pi))) pi = Path::Valu;
+    if ((rc = choose_path(flags, T, LB_F32, &pi, &ag))) pi = Path::Valu;
     if (p == Path::Gemm) pi = Path::Gemm;
     if ((rc = run_path(pi, ag, lws, s))) return rc;
     if ((rc = run_path(pi, au, lws, s))) return rc;
@@ -287,23 +305,38 @@ int lb_mlp_forward(const void *x, int x_dtype, void *y, int y_dtype, const lb_fa
     return run_path(p, ad, lws, s);
 }
 
+}  // extern "C"
+
 // ---- layer groups ----------------------------------------------------------
 
 namespace {
 enum class GroupKind { Loop, Decode, Gemm };
 
-struct GroupRecord {
+// Everything a run of a group needs: the linears (for the linear-by-linear
+// form), the launch state of the whole-group kernels, and the image its
+// workspace must hold (header with the stamp, tables, zeroed counters).
+struct GroupPlan {
     std::vector<lb_linear_desc> descs;
-    int64_t T;
-    int x_dtype, y_dtype;
-    unsigned flags;
-    size_t ws_bytes;
-    GroupKind kind;                   // Decode / Gemm: whole-group kernels
-    std::vector<uint8_t> state;       // their host-side launch state
+    int64_t T = 0;
+    int x_dtype = 0, y_dtype = 0;
+    unsigned flags = 0;
+    void *ws = nullptr;
+    size_t ws_bytes = 0;
+    GroupKind kind = GroupKind::Loop;
+    std::vector<uint8_t> state;
+    GroupImage img;
 };
 
-std::mutex g_groups_mu;
-std::unordered_map<void *, GroupRecord> g_groups;
+// A tag no other group set-up in this process has (and, with its random
+// half, unlikely to be any earlier contents of the memory it stamps).
+uint64_t new_tag() {
+    static std::atomic<uint64_t> counter{1};
+    static const uint64_t salt = [] {
+        std::random_device rd;
+        return ((uint64_t)rd() << 32) ^ (uint64_t)rd();
+    }();
+    return salt ^ (counter.fetch_add(1) * 0x9e3779b97f4a7c15ull);
+}
 
 int group_linear(const lb_linear_desc &d, int64_t T, int x_dtype, int y_dtype, Linear *a) {
     int rc;
@@ -320,6 +353,8 @@ bool group_shapes(const lb_linear_desc *descs, int n, int64_t T, std::vector<Lin
         Linear &a = (*ls)[(size_t)i];
         if (check_shape(descs[i].d_in, descs[i].d_out, descs[i].r, T, descs[i].residual, &a)) return false;
         a.x_dtype = a.y_dtype = LB_BF16;
+        a.ld_v = descs[i].w.ld_v;
+        a.ld_u = descs[i].w.ld_u;
     }
     return true;
 }
@@ -327,14 +362,17 @@ bool group_shapes(const lb_linear_desc *descs, int n, int64_t T, std::vector<Lin
 GroupKind group_kind(unsigned flags, int64_t T, int y_dtype, const std::vector<Linear> &ls) {
     Path p;
     if (choose_path(flags, T, y_dtype, &p)) return GroupKind::Loop;
-    if (p == Path::MfmaDecode) return GroupKind::Decode;
+    if (p == Path::MfmaDecode) {
+        for (const Linear &a : ls)
+            if (!mfma_decode_shape_ok(a)) return GroupKind::Loop;
+        return GroupKind::Decode;
+    }
     if (p == Path::Gemm && gemm_group_supported(ls.data(), (int)ls.size())) return GroupKind::Gemm;
     return GroupKind::Loop;
 }
-}  // namespace
 
-size_t lb_grouped_workspace_bytes(const lb_linear_desc *descs, int n, int64_t T, unsigned flags) {
-    if (!descs || n <= 0 || T <= 0) return 0;
+size_t group_ws_bytes(const lb_linear_desc *descs, int n, int64_t T, unsigned flags) {
+    if (!descs || n <= 0 || T <= 0 || (flags & ~kGroupFlags)) return 0;
     std::vector<Linear> ls;
     if (!group_shapes(descs, n, T, &ls)) return 0;
     size_t need = 0;
@@ -346,48 +384,235 @@ size_t lb_grouped_workspace_bytes(const lb_linear_desc *descs, int n, int64_t T,
         if (k == GroupKind::Gemm) b = gemm_group_workspace_bytes(ls.data(), n);
         if (b > need) need = b;
     }
-    // the linear-by-linear loop
+    // the linear-by-linear loop (after a 256-byte header)
     for (int i = 0; i < n; ++i) {
         const size_t b = lb_linear_workspace_bytes(descs[i].d_in, descs[i].d_out, descs[i].r, T,
-                                                   descs[i].residual, flags);
-        if (b > need) need = b;
+                                                   descs[i].residual, flags & kLinearFlags);
+        if (b + 256 > need) need = b + 256;
     }
-    return rup256(need) + 256;
+    return rup256(need);
 }
 
-int lb_grouped_prepare(const lb_linear_desc *descs, int n, int64_t T, int x_dtype, int y_dtype,
-                       void *ws, size_t ws_bytes, unsigned flags, void *stream) {
+// Checks a group and plans it on ws (nothing is enqueued).
+int build_plan(const lb_linear_desc *descs, int n, int64_t T, int x_dtype, int y_dtype, void *ws,
+               size_t ws_bytes, unsigned flags, GroupPlan *gp) {
     if (!descs || n <= 0 || T <= 0) return LB_EINVAL;
+    if (flags & ~kGroupFlags) return LB_EINVAL;
     Path p;
     int rc;
     if ((rc = choose_path(flags, T, y_dtype, &p))) return rc;
     std::vector<Linear> ls((size_t)n);
     for (int i = 0; i < n; ++i)
         if ((rc = group_linear(descs[i], T, x_dtype, y_dtype, &ls[(size_t)i]))) return rc;
-    const size_t need = lb_grouped_workspace_bytes(descs, n, T, flags);
+    const size_t need = group_ws_bytes(descs, n, T, flags);
     if (!ws || ws_bytes < need) return LB_EWORKSPACE;
     if (!aligned(ws, 256)) return LB_EALIGN;
-    GroupRecord rec;
-    rec.descs.assign(descs, descs + n);
-    rec.T = T;
-    rec.x_dtype = x_dtype;
-    rec.y_dtype = y_dtype;
-    rec.flags = flags;
-    rec.ws_bytes = ws_bytes;
-    rec.kind = group_kind(flags, T, y_dtype, ls);
-    if (rec.kind == GroupKind::Decode) {
-        rec.state.assign(mfma_group_state_bytes(), 0);
-        if ((rc = mfma_group_prepare(ls.data(), n, T, y_dtype, ws, ws_bytes, rec.state.data(),
-                                     (hipStream_t)stream)))
-            return rc;
-    } else if (rec.kind == GroupKind::Gemm) {
-        rec.state.assign(gemm_group_state_bytes(), 0);
-        if ((rc = gemm_group_prepare(ls.data(), n, ws, ws_bytes, rec.state.data(),
-                                     (hipStream_t)stream)))
-            return rc;
+    for (int i = 0; i < n; ++i) {
+        const Linear &a = ls[(size_t)i];
+        if (overlap(ws, need, a.x, (size_t)(T * a.d_in) * act_size(x_dtype)) ||
+            overlap(ws, need, a.y, (size_t)(T * a.d_out) * act_size(y_dtype)))
+            return LB_EINVAL;
     }
+    gp->descs.assign(descs, descs + n);
+    gp->T = T;
+    gp->x_dtype = x_dtype;
+    gp->y_dtype = y_dtype;
+    gp->flags = flags;
+    gp->ws = ws;
+    gp->ws_bytes = ws_bytes;
+    gp->kind = group_kind(flags, T, y_dtype, ls);
+    const uint64_t tag = new_tag();
+    if (gp->kind == GroupKind::Decode) {
+        gp->state.assign(mfma_group_state_bytes(), 0);
+        return mfma_group_plan(ls.data(), n, T, y_dtype, ws, ws_bytes, tag, (flags & LB_GROUP_FAULT_TEST) != 0,
+                               gp->state.data(), &gp->img);
+    }
+    if (gp->kind == GroupKind::Gemm) {
+        gp->state.assign(gemm_group_state_bytes(), 0);
+        return gemm_group_plan(ls.data(), n, ws, ws_bytes, tag, gp->state.data(), &gp->img);
+    }
+    return LB_OK;
+}
+
+// Enqueues the set-up of a planned group on s: its workspace image from
+// `src` (host memory that stays valid until the copy is done), the zeroed
+// scratch and, for the GEMM kernels, the factor preparation.
+int enqueue_setup(const GroupPlan &gp, const void *src, hipStream_t s) {
+    if (gp.kind == GroupKind::Loop) return LB_OK;
+    if (hipMemcpyAsync(gp.ws, src, gp.img.bytes.size(), hipMemcpyHostToDevice, s) != hipSuccess)
+        return hip_status(hipGetLastError());
+    if (int rc = fill_words((char *)gp.ws + gp.img.zero_off, gp.img.zero_bytes, 0u, s)) return rc;
+    if (gp.kind == GroupKind::Gemm) return gemm_group_run(gp.state.data(), s, 4);
+    return LB_OK;
+}
+
+int run_plan(const GroupPlan &gp, int stage_mask, hipStream_t s) {
+    if (gp.kind == GroupKind::Decode) return mfma_group_run(gp.state.data(), s, stage_mask);
+    if (gp.kind == GroupKind::Gemm) return gemm_group_run(gp.state.data(), s, stage_mask);
+    if (stage_mask != 3) return LB_EUNSUPPORTED;
+    void *lws = (char *)gp.ws + 256;
+    for (const lb_linear_desc &d : gp.descs) {
+        const int rc = lb_linear_forward(d.x, gp.x_dtype, d.y, gp.y_dtype, &d.w, d.d_in, d.d_out, d.r, gp.T,
+                                         d.residual, lws, gp.ws_bytes - 256, gp.flags & kLinearFlags, s);
+        if (rc) return rc;
+    }
+    return LB_OK;
+}
+
+// Prepared groups, by workspace address.  A record is looked up under the
+// lock and used outside it; runs read it only.
+std::mutex g_groups_mu;
+std::unordered_map<void *, std::shared_ptr<const GroupPlan>> g_groups;
+
+std::shared_ptr<const GroupPlan> find_group(void *ws) {
     std::lock_guard<std::mutex> lk(g_groups_mu);
-    g_groups[ws] = std::move(rec);
+    auto it = g_groups.find(ws);
+    return it == g_groups.end() ? nullptr : it->second;
+}
+
+// ---- the stateless grouped call: plans cached by their arguments ----------
+
+uint64_t fnv1a(const void *p, size_t n, uint64_t h = 1469598103934665603ull) {
+    const uint8_t *b = (const uint8_t *)p;
+    for (size_t i = 0; i < n; ++i) h = (h ^ b[i]) * 1099511628211ull;
+    return h;
+}
+
+// One cached plan: its key (the call's bytes), the plan, a pinned copy of its
+// workspace image and an event after the last copy out of it.
+struct CachedPlan {
+    std::vector<uint8_t> key;
+    uint64_t hash = 0;
+    std::shared_ptr<GroupPlan> plan;
+    void *pinned = nullptr;
+    hipEvent_t copied = nullptr;
+    uint64_t used = 0;
+    bool captured = false;    // a captured graph copies from `pinned`: kept until the process ends
+};
+
+constexpr size_t kPlanCache = 8;
+std::mutex g_cache_mu;
+std::deque<CachedPlan> g_cache;      // deque: slots keep their address as it grows
+uint64_t g_cache_clock = 0;
+
+void drop_cached(CachedPlan &c) {
+    if (c.copied) {
+        (void)hipEventSynchronize(c.copied);
+        (void)hipEventDestroy(c.copied);
+    }
+    if (c.pinned) (void)hipHostFree(c.pinned);
+    c = CachedPlan{};
+}
+
+// Plans a sub-group (or finds its plan) and enqueues its set-up and run.
+int run_stateless(const lb_linear_desc *descs, int n, int64_t T, int x_dtype, int y_dtype, void *ws,
+                  size_t ws_bytes, unsigned flags, hipStream_t s) {
+    std::vector<uint8_t> key(sizeof(lb_linear_desc) * n + 64);
+    memcpy(key.data(), descs, sizeof(lb_linear_desc) * n);
+    uint8_t *tail = key.data() + sizeof(lb_linear_desc) * n;
+    memcpy(tail, &T, 8);
+    memcpy(tail + 8, &x_dtype, 4);
+    memcpy(tail + 12, &y_dtype, 4);
+    memcpy(tail + 16, &flags, 4);
+    memcpy(tail + 24, &ws, sizeof(void *));
+    memcpy(tail + 32, &ws_bytes, sizeof(size_t));
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    memcpy(tail + 40, &dev, 4);
+    const uint64_t h = fnv1a(key.data(), key.size());
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    CachedPlan *hit = nullptr;
+    for (CachedPlan &c : g_cache)
+        if (c.plan && c.hash == h && c.key == key) hit = &c;
+    if (!hit) {
+        auto gp = std::make_shared<GroupPlan>();
+        if (int rc = build_plan(descs, n, T, x_dtype, y_dtype, ws, ws_bytes, flags, gp.get())) return rc;
+        // a free slot, else the least recently used one no graph copies from
+        CachedPlan *slot = nullptr;
+        size_t live = 0;
+        for (CachedPlan &c : g_cache) live += c.captured ? 0 : 1;
+        if (live < kPlanCache) {
+            for (CachedPlan &c : g_cache)
+                if (!c.plan) { slot = &c; break; }
+            if (!slot) slot = &g_cache.emplace_back();
+        } else {
+            for (CachedPlan &c : g_cache)
+                if (!c.captured && (!slot || c.used < slot->used)) slot = &c;
+        }
+        drop_cached(*slot);
+        slot->key = std::move(key);
+        slot->hash = h;
+        slot->plan = gp;
+        if (!gp->img.bytes.empty()) {
+            if (hipHostMalloc(&slot->pinned, gp->img.bytes.size(), hipHostMallocDefault) != hipSuccess ||
+                hipEventCreateWithFlags(&slot->copied, hipEventDisableTiming) != hipSuccess) {
+                const int rc = hip_status(hipGetLastError());
+                drop_cached(*slot);
+                return rc;
+            }
+            memcpy(slot->pinned, gp->img.bytes.data(), gp->img.bytes.size());
+        }
+        hit = slot;
+    }
+    hit->used = ++g_cache_clock;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess) return hip_status(hipGetLastError());
+    if (cs != hipStreamCaptureStatusNone) hit->captured = true;
+    const GroupPlan &gp = *hit->plan;
+    if (int rc = enqueue_setup(gp, hit->pinned, s)) return rc;
+    // (a captured copy is never waited for: its slot is kept)
+    if (hit->copied && cs == hipStreamCaptureStatusNone && hipEventRecord(hit->copied, s) != hipSuccess)
+        return hip_status(hipGetLastError());
+    return run_plan(gp, 3, s);
+}
+
+lb_linear_desc desc_of(const lb_linear_call &c) {
+    lb_linear_desc d{};
+    d.x = c.x;
+    d.y = c.y;
+    d.w = c.w;
+    d.d_in = c.d_in;
+    d.d_out = c.d_out;
+    d.r = c.r;
+    d.residual = c.residual;
+    return d;
+}
+
+bool same_group(const lb_linear_call &a, const lb_linear_call &b) {
+    return a.T == b.T && a.x_dtype == b.x_dtype && a.y_dtype == b.y_dtype && a.flags == b.flags;
+}
+
+// The calls' sub-groups (equal T, dtypes and flags), in order of first appearance.
+std::vector<std::vector<int>> sub_groups(const lb_linear_call *calls, int n) {
+    std::vector<std::vector<int>> gs;
+    for (int i = 0; i < n; ++i) {
+        bool placed = false;
+        for (auto &g : gs)
+            if (same_group(calls[g[0]], calls[i])) { g.push_back(i); placed = true; break; }
+        if (!placed) gs.push_back({i});
+    }
+    return gs;
+}
+}  // namespace
+
+extern "C" {
+
+size_t lb_grouped_workspace_bytes(const lb_linear_desc *descs, int n, int64_t T, unsigned flags) {
+    return group_ws_bytes(descs, n, T, flags);
+}
+
+int lb_grouped_prepare(const lb_linear_desc *descs, int n, int64_t T, int x_dtype, int y_dtype,
+                       void *ws, size_t ws_bytes, unsigned flags, void *stream) {
+    auto gp = std::make_shared<GroupPlan>();
+    if (int rc = build_plan(descs, n, T, x_dtype, y_dtype, ws, ws_bytes, flags, gp.get())) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    // blocking: the host image is copied out before this returns
+    if (int rc = enqueue_setup(*gp, gp->img.bytes.data(), s)) return rc;
+    if (int rc = hip_status(hipStreamSynchronize(s))) return rc;
+    gp->img.bytes.clear();
+    gp->img.bytes.shrink_to_fit();
+    std::lock_guard<std::mutex> lk(g_groups_mu);
+    g_groups[ws] = std::move(gp);
     return LB_OK;
 }
 
@@ -400,37 +625,85 @@ int lb_grouped_release(void *ws) {
 }
 
 int lb_grouped_run(void *ws, void *stream) {
-    GroupRecord g;
-    {
-        std::lock_guard<std::mutex> lk(g_groups_mu);
-        auto it = g_groups.find(ws);
-        if (it == g_groups.end()) return LB_EINVAL;
-        GroupRecord &rec = it->second;
-        // whole-group kernels launch from the record itself, under the lock:
-        // their host state advances with every run (the decode pass numbers
-        // its runs)
-        if (rec.kind == GroupKind::Decode) return mfma_group_run(rec.state.data(), (hipStream_t)stream);
-        if (rec.kind == GroupKind::Gemm) return gemm_group_run(rec.state.data(), (hipStream_t)stream);
-        g = rec;
-    }
-    void *lws = (char *)ws + 256;
-    for (const lb_linear_desc &d : g.descs) {
-        const int rc = lb_linear_forward(d.x, g.x_dtype, d.y, g.y_dtype, &d.w, d.d_in, d.d_out, d.r,
-                                         g.T, d.residual, lws, g.ws_bytes - 256, g.flags, stream);
-        if (rc) return rc;
-    }
-    return LB_OK;
+    const std::shared_ptr<const GroupPlan> gp = find_group(ws);
+    if (!gp) return LB_EINVAL;
+    return run_plan(*gp, 3, (hipStream_t)stream);
 }
 
 int lb_grouped_run_stage(void *ws, int stage, void *stream) {
     if (stage != 1 && stage != 2) return LB_EINVAL;
-    std::lock_guard<std::mutex> lk(g_groups_mu);
-    auto it = g_groups.find(ws);
-    if (it == g_groups.end()) return LB_EINVAL;
-    GroupRecord &rec = it->second;
-    if (rec.kind == GroupKind::Loop) return LB_EUNSUPPORTED;
-    if (rec.kind == GroupKind::Gemm) return gemm_group_run(rec.state.data(), (hipStream_t)stream, stage);
-    return mfma_group_run(rec.state.data(), (hipStream_t)stream, stage);
+    const std::shared_ptr<const GroupPlan> gp = find_group(ws);
+    if (!gp) return LB_EINVAL;
+    if (gp->kind == GroupKind::Loop) return LB_EUNSUPPORTED;
+    return run_plan(*gp, stage, (hipStream_t)stream);
+}
+
+size_t lb_linear_grouped_workspace_bytes(const lb_linear_call *calls, int n) {
+    if (!calls || n <= 0) return 0;
+    size_t need = 0;
+    for (const std::vector<int> &g : sub_groups(calls, n)) {
+        const lb_linear_call &c0 = calls[g[0]];
+        if (c0.T == 0) continue;
+        std::vector<lb_linear_desc> ds;
+        for (int i : g) ds.push_back(desc_of(calls[i]));
+        const size_t b = group_ws_bytes(ds.data(), (int)ds.size(), c0.T, c0.flags);
+        if (b == 0) return 0;
+        need = std::max(need, b);
+    }
+    return need;
+}
+
+int lb_linear_forward_grouped(const lb_linear_call *calls, int n, void *ws, size_t ws_bytes, void *stream) {
+    if (!calls || n <= 0) return LB_EINVAL;
+    const std::vector<std::vector<int>> gs = sub_groups(calls, n);
+    // every call is checked before anything is enqueued
+    for (int i = 0; i < n; ++i) {
+        const lb_linear_call &c = calls[i];
+        if (c.T < 0 || (c.flags & ~kGroupFlags)) return LB_EINVAL;
+        Linear a{};
+        int rc;
+        if ((rc = check_shape(c.d_in, c.d_out, c.r, c.T, c.residual, &a))) return rc;
+        if ((rc = check_factors(&c.w, &a))) return rc;
+        if ((rc = check_io(c.x, c.x_dtype, c.y, c.y_dtype, &a))) return rc;
+        Path p;
+        if ((rc = choose_path(c.flags & kLinearFlags, c.T, c.y_dtype, &p))) return rc;
+    }
+    const size_t need = lb_linear_grouped_workspace_bytes(calls, n);
+    if (need > 0 && (!ws || ws_bytes < need)) return LB_EWORKSPACE;
+    for (const std::vector<int> &g : gs) {
+        const lb_linear_call &c0 = calls[g[0]];
+        if (c0.T == 0) continue;
+        std::vector<lb_linear_desc> ds;
+        for (int i : g) ds.push_back(desc_of(calls[i]));
+        if (int rc = run_stateless(ds.data(), (int)ds.size(), c0.T, c0.x_dtype, c0.y_dtype, ws, ws_bytes,
+                                   c0.flags, (hipStream_t)stream))
+            return rc;
+    }
+    return LB_OK;
+}
+
+int lb_device_faults(void *stream, uint32_t *faults) {
+    uint32_t f = 0;
+    if (int rc = take_faults((hipStream_t)stream, &f)) return rc;
+    if (faults) *faults = f;
+    return f ? LB_EDEVICE : LB_OK;
+}
+
+int lb_linear_path(int64_t d_in, int64_t d_out, int64_t r, int64_t T, int residual, int x_dtype, int y_dtype,
+                   unsigned flags) {
+    Linear a{};
+    int rc;
+    if ((rc = check_shape(d_in, d_out, r, T, residual, &a))) return rc;
+    if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype) || (flags & ~kLinearFlags)) return LB_EINVAL;
+    a.x_dtype = x_dtype;
+    a.y_dtype = y_dtype;
+    a.ld_v = lb_packed_ld_aligned(a.r_p);
+    a.ld_u = lb_packed_ld_aligned(d_out);
+    Path p;
+    if ((rc = choose_path(flags, T, y_dtype, &p, &a))) return rc;
+    if (p == Path::Gemm && !gemm_linear_supported(a)) p = Path::Valu;
+    return p == Path::MfmaDecode ? (int)LB_PATH_DECODE : p == Path::Gemm ? (int)LB_PATH_PREFILL
+                                                                          : (int)LB_PATH_DECODE_VALU;
 }
 
 }  // extern "C"

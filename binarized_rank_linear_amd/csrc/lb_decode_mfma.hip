@@ -41,6 +41,7 @@
 //            tiles, streaming the U planes of both paths into one accumulator set.
 #include <algorithm>
 #include <cstdlib>
+#include <cstring>
 #include <vector>
 
 #include "lb_internal.h"
@@ -137,9 +138,14 @@ struct MRun {
     const int32_t *tabP2;          // (workgroup - items1) -> (linear, first 256-row tile << 8 | tiles)
     int64_t items2P;               // stage-2 workgroups of k_pass
     uint32_t *arrive;              // per (linear, path, latent group): its stage-1 items counted in
-    uint32_t *ready;               // per linear: its latent groups whose operands are stored
-    uint32_t epoch;                // this run's number (from 0)
+    uint32_t *sync;                // per linear: latent groups stored (low 16 bits), events (high 16 bits)
+    uint32_t spin_limit;           // polls a stage-2 wave makes before it gives up
+    uint32_t want_extra;           // 0; 1 asks for one latent group more than exists (fault-report test)
     int pass;                      // 1: a full run is one k_pass launch
+    // groups: the workspace stamp written at set-up and the tag it must equal
+    // (null for a single linear, which keeps nothing in its workspace)
+    const uint64_t *stamp;
+    uint64_t tag;
 };
 
 // Compact operands -> LDS operand layout.  Each operand holds R records of
@@ -332,16 +338,57 @@ __host__ __device__ inline size_t ops2r_bytes(int steps, int NB2, int R2) {
 }
 
 constexpr uint32_t kSpinLimit = 1u << 20;
+constexpr uint32_t kSpinLimitTest = 64;   // under LB_GROUP_FAULT_TEST
 constexpr int kFlagStride = 64;           // words between two linears' counters (own 256-byte lines)
 
-// The wave polls *flag (device scope) until it reads `want` or kSpinLimit
-// polls have gone by.
-__device__ __forceinline__ void wait_flag(const uint32_t *flag, uint32_t want) {
+}  // namespace
+
+// The fault word of each device: kernels OR LB_FAULT_* bits into it, and
+// lb_device_faults reads and clears it.  Library-owned, so a kernel can report
+// even when the workspace it was given is not (or no longer) the group's.
+__device__ uint32_t g_lb_faults;
+__device__ uint32_t g_lb_faults_out;      // where lb_device_faults exchanges it to
+
+namespace {
+
+__device__ __forceinline__ void report_fault(uint32_t bit) {
+    __hip_atomic_fetch_or(&g_lb_faults, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Whether a group's workspace no longer carries the stamp the group was set up
+// with (the memory was reused or overwritten since).  Its tables are then not
+// to be trusted: the workgroup reports it and does nothing.  Uniform.
+__device__ __forceinline__ bool stale_ws(const MRun &run) {
+    if (!run.stamp) return false;
+    if (*run.stamp == run.tag) return false;
+    if (threadIdx.x == 0) report_fault(LB_FAULT_STALE_WORKSPACE);
+    return true;
+}
+
+// The wave polls the low 16 bits of *w (device scope) until they read `want`
+// or `limit` polls have gone by; false (after reporting the fault) if it gave
+// up.  Nothing after the poll may move above it: the operand loads that follow
+// are device-scope loads issued after the poll's value has been compared.
+__device__ __forceinline__ bool wait_count(const uint32_t *w, uint32_t want, uint32_t limit) {
     uint32_t n = 0;
-    while ((uint32_t)__builtin_amdgcn_readfirstlane(
-               __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != want &&
-           ++n < kSpinLimit)
+    bool ok;
+    while (!(ok = ((uint32_t)__builtin_amdgcn_readfirstlane(
+                       __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) & 0xffffu) == want) &&
+           ++n < limit)
         __builtin_amdgcn_s_sleep(2);
+    asm volatile("" ::: "memory");
+    if (!ok && (threadIdx.x & 63) == 0) report_fault(LB_FAULT_HANDOFF_TIMEOUT);
+    return ok;
+}
+
+// One event of a linear's run in its sync word (`add` = 0x10001 for a latent
+// group whose operands are stored, 0x10000 for a stage-2 workgroup past its
+// wait).  A run has `events` of them; the one that completes the count is the
+// run's last access to the word and sets it back to zero, so every run starts
+// from zero and no run number is needed.
+__device__ __forceinline__ void sync_event(uint32_t *w, uint32_t add, uint32_t events) {
+    const uint32_t old = __hip_atomic_fetch_add(w, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((old >> 16) + 1u == events) __hip_atomic_store(w, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -351,6 +398,7 @@ __device__ __forceinline__ void wait_flag(const uint32_t *flag, uint32_t want) {
 template <int NL, int NB1>
 __global__ __launch_bounds__(kThreads) void k_prep(MRun run, MLin single) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    if (stale_ws(run)) return;
     using R = Rows<NL>;
     const int64_t item = (int64_t)blockIdx.x + run.base0;
     const MLin L = pick(run, single, run.lin0, item);
@@ -432,6 +480,7 @@ __global__ __launch_bounds__(kThreads) void k_prep(MRun run, MLin single) {
 template <int NL, int NB1>
 __global__ __launch_bounds__(kThreads) void k_stage1(MRun run, MLin single) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    if (stale_ws(run)) return;
     using R = Rows<NL>;
     const int64_t item = item_of(run.ord1, run.base1);
     const MLin L = pick(run, single, run.lin1, item);
@@ -804,6 +853,7 @@ __device__ __forceinline__ void stage1f_item(const MRun &run, const MLin &L, int
 template <int NL>
 __global__ __launch_bounds__(kThreads) void k_stage1f(MRun run, MLin single) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    if (stale_ws(run)) return;
     const int64_t item = item_of(run.ord1, run.base1);
     stage1f_item<NL, false>(run, pick(run, single, run.lin1, item), item, smem);
 }
@@ -995,6 +1045,7 @@ __device__ __forceinline__ void latent_rows(const MRun &run, const MLin &L, int 
 template <int NL, int NB2>
 __global__ __launch_bounds__(kThreads) void k_latent(MRun run, MLin single) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    if (stale_ws(run)) return;
     const int64_t item = (int64_t)blockIdx.x + run.baseF;
     const MLin L = pick(run, single, run.linF, item);
     const int kg_first = (int)(item - L.itemF) * 2;               // 2 K-groups = 8 planes per item
@@ -1011,6 +1062,7 @@ __global__ __launch_bounds__(kThreads) void k_latent(MRun run, MLin single) {
 template <int NL, int NB2>
 __global__ __launch_bounds__(kThreads) void k_stage2(MRun run, MLin single) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    if (stale_ws(run)) return;
     using R = Rows<NL>;
     const int64_t item = item_of(run.ord2, run.base2);
     const MLin L = pick(run, single, run.lin2, item);
@@ -1161,14 +1213,15 @@ __global__ __launch_bounds__(kThreads) void k_stage2(MRun run, MLin single) {
 // a zero record for the rows no token fills) and h of the item's rows sit in
 // LDS for the whole item.
 // COHERENT: the operands were written earlier in the same launch (the
-// one-launch pass); `ready` counts the linear's latent groups whose operands
-// are stored.  Each wave loads it (device scope) as its first load, then h and
-// its first plane loads; the check waits for the counter load alone (loads
-// complete in issue order for the counter), and only then do the operand loads
-// go out, at device scope.
+// one-launch pass); the low half of the linear's `sync` word counts its latent
+// groups whose operands are stored.  Each wave loads it (device scope) as its
+// first load, then h and its first plane loads; the check waits for the
+// counter load alone (loads complete in issue order for the counter), and only
+// then do the operand loads go out, at device scope.  Once all four waves are
+// past the check, the workgroup counts itself in the high half (see k_pass).
 template <int NL, int NB2, bool COHERENT>
 __device__ __forceinline__ void stage2r_item(const MRun &run, const MLin &L, int64_t row_begin, int tiles,
-                                             uint8_t *smem, const uint32_t *ready) {
+                                             uint8_t *smem, uint32_t *sync) {
     using R = Rows<NL>;
     const int T = run.T;
     const int lane = threadIdx.x & 63, wave = wave_id();
@@ -1192,7 +1245,7 @@ __device__ __forceinline__ void stage2r_item(const MRun &run, const MLin &L, int
     // fill below waits for these only, not for the plane loads behind them)
     uint32_t flag = 0;
     if constexpr (COHERENT)
-        flag = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(ready, 4), 0, 0, kDeviceScope);
+        flag = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(sync, 4), 0, 0, kDeviceScope);
     v4u pre[kPreVec];
     if constexpr (!COHERENT) preload_ops(L.tb, steps * NB2, L.R2, pre);
     // h of the item's rows: thread t holds 8 consecutive fp16 of path t / (kThreads/2)
@@ -1224,8 +1277,9 @@ __device__ __forceinline__ void stage2r_item(const MRun &run, const MLin &L, int
 #pragma unroll
     for (int k = 0; k < kWin2; ++k) slot[k] = load_rows(ru, off_of(k));
     if constexpr (COHERENT) {
-        const uint32_t want = (run.epoch + 1u) * (uint32_t)(L.P * L.nrg);   // every latent group of the linear
-        if ((uint32_t)__builtin_amdgcn_readfirstlane(flag) != want) wait_flag(ready, want);
+        const uint32_t want = (uint32_t)(L.P * L.nrg) + run.want_extra;   // every latent group of the linear
+        if (((uint32_t)__builtin_amdgcn_readfirstlane(flag) & 0xffffu) != want)
+            wait_count(sync, want, run.spin_limit);
         preload_ops<kDeviceScope>(L.tb, steps * NB2, L.R2, pre);
     }
 
@@ -1246,6 +1300,11 @@ __device__ __forceinline__ void stage2r_item(const MRun &run, const MLin &L, int
         }
     }
     __syncthreads();
+    if constexpr (COHERENT) {
+        // every wave is past its check: count this workgroup as an event of
+        // the linear; the run's last event clears the word for the next run
+        if (threadIdx.x == 0) sync_event(sync, 0x10000u, (uint32_t)(L.P * L.nrg + L.n2));
+    }
 
     v4f acc[4][NB2];
 #pragma unroll
@@ -1368,6 +1427,7 @@ __device__ __forceinline__ void stage2r_item(const MRun &run, const MLin &L, int
 template <int NL, int NB2>
 __global__ __launch_bounds__(kThreads) void k_stage2r(MRun run, MLin single) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    if (stale_ws(run)) return;
     const int64_t item = item_of(run.ord2, run.base2);
     const MLin L = pick(run, single, run.lin2, item);
     const int64_t row_begin = (item - L.item2) * L.rows2;
@@ -1387,25 +1447,29 @@ __global__ __launch_bounds__(kThreads) void k_stage2r(MRun run, MLin single) {
 //     (linear, path, tiles [rg*F, (rg+1)*F)), whose chunks are its nchunks
 //     items;
 //   - the workgroup that completes that count (the group's last chunk in this
-//     run) sums the group's partials into its planes of the stage-2 operands
-//     (the latent step, spread over the linear's P * nrg groups), stores them
-//     at device scope and counts the group in ready[linear];
+//     run) sets the counter back to zero, sums the group's partials into its
+//     planes of the stage-2 operands (the latent step, spread over the
+//     linear's P * nrg groups), stores them at device scope and counts the
+//     group in the linear's sync word;
 //   - a stage-2 workgroup waits until every group of its linear is counted in
-//     before it loads the operands.
+//     before it loads the operands, then counts itself in the same word.
+// The sync word of a linear holds the stored groups in its low half and all
+// events (groups stored, stage-2 workgroups past their wait) in its high half;
+// the run's last event sets it back to zero.  So every counter is zero when a
+// run starts and again when it has ended, and a run needs nothing from the
+// host but its tables: a captured launch replays like a fresh one.
 // Device-scope accesses bypass the non-coherent caches of the other XCDs, so
 // no cache-wide write-back or invalidation is needed.  Workgroups start in
 // index order, so when a stage-2 workgroup runs, every stage-1 workgroup has
 // started already; those never wait, so every wait ends.  The wait is also
-// bounded (kSpinLimit polls); past it the workgroup goes on and its outputs
-// are wrong, but the launch still ends.
-// The counters keep counting across runs: after run e (from 0) a group's
-// counter is (e + 1) * nchunks, so the completing workgroup is the one that
-// reads (e + 1) * nchunks - 1 before its increment, and ready[j] is
-// (e + 1) * P * nrg.
+// bounded (spin_limit polls): a wave that gives up reports
+// LB_FAULT_HANDOFF_TIMEOUT in the fault word (its outputs are wrong) and the
+// launch still ends; the counters still return to zero.
 template <int NL, int NB2>
 __global__ __launch_bounds__(kThreads) void k_pass(MRun run, MLin single) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     __shared__ uint32_t s_count;
+    if (stale_ws(run)) return;
     const int64_t b = blockIdx.x;
     if (b < run.items1) {
         const int64_t item = __builtin_amdgcn_readfirstlane(run.ordP1[b]);
@@ -1415,16 +1479,17 @@ __global__ __launch_bounds__(kThreads) void k_pass(MRun run, MLin single) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // this wave's partial sums are stored
         __syncthreads();
         const int f = (int)((item - L.item1) / L.nchunks);          // latent group: path * nrg + rg
+        uint32_t *arr = run.arrive + (L.fin0 + f) * kFlagStride;
         if (threadIdx.x == 0)
-            s_count = __hip_atomic_fetch_add(run.arrive + (L.fin0 + f) * kFlagStride, 1u, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
+            s_count = __hip_atomic_fetch_add(arr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
-        if (s_count + 1u == (run.epoch + 1u) * (uint32_t)L.nchunks) {   // uniform
+        if (s_count + 1u == (uint32_t)L.nchunks) {           // uniform: the group's last chunk
+            if (threadIdx.x == 0) __hip_atomic_store(arr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             latent_rows<NL, NB2>(run, L, f / L.nrg, f % L.nrg, smem);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's operand bytes are stored
             __syncthreads();
             if (threadIdx.x == 0)
-                __hip_atomic_fetch_add(run.ready + j * kFlagStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                sync_event(run.sync + j * kFlagStride, 0x10001u, (uint32_t)(L.P * L.nrg + L.n2));
         }
     } else {
         // (linear, first 256-row tile << 8 | tiles) of this workgroup
@@ -1432,7 +1497,7 @@ __global__ __launch_bounds__(kThreads) void k_pass(MRun run, MLin single) {
         const int j = __builtin_amdgcn_readfirstlane(e[0]);
         const int g = __builtin_amdgcn_readfirstlane(e[1]);
         stage2r_item<NL, NB2, true>(run, pick_linear(run, single, j), (int64_t)(g >> 8) * kRG, g & 255, smem,
-                                    run.ready + j * kFlagStride);
+                                    run.sync + j * kFlagStride);
     }
 }
 
@@ -1683,6 +1748,27 @@ bool mfma_decode_supported(int64_t T, int y_dtype) {
     return shape_for(T, y_dtype, &s);
 }
 
+bool mfma_decode_shape_ok(const Linear &a) {
+    // every buffer the kernels address through 32-bit offsets stays below 2 GiB
+    const int64_t lim = 1ll << 31;
+    const int64_t kgv = cdiv(a.kw_v(), 4), kgs = cdiv((int64_t)a.P * a.kw_u(), 4);
+    return (int64_t)a.P * a.kw_v() * a.ld_v * 4 < lim && (int64_t)a.P * a.kw_u() * a.ld_u * 4 < lim &&
+           a.T * a.d_in * 4 < lim && a.T * a.d_out * 4 < lim && (int64_t)a.P * a.d_out * 2 < lim &&
+           kgv * a.T * a.P * a.r_p * 4 < lim && kgs * 8 * 16 * kRec < lim;
+}
+
+uint32_t *fault_word_ptr() {
+    static uint32_t *ptr[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    if (!ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_lb_faults)) != hipSuccess) return nullptr;
+        ptr[dev] = (uint32_t *)p;
+    }
+    return ptr[dev];
+}
+
 size_t mfma_decode_workspace_bytes(const Linear &a) {
     // sized for the larger of the two output dtypes' limb counts
     size_t need = 0;
@@ -1730,10 +1816,6 @@ struct MGroupHost {
     MRun run;
     Lds lds;
     size_t lds_pass;     // dynamic LDS of k_pass
-    uint32_t epoch;      // number of the next one-launch run
-    int64_t n1_max;      // most stage-1 items of one linear
-    int64_t nf;          // latent groups of all linears (counters in arrive)
-    uint64_t wrap;       // the counters start over before (epoch + 1) * n1_max reaches this
     int n;               // linears
 };
 
@@ -1802,60 +1884,88 @@ Grain group_grain(const Linear *ls, int n, const Shape &s) {
     return g;
 }
 
+// Workspace of a group, in this order: the 256-byte header (the stamp), the
+// per-linear table, the item tables and dispatch orders, the counters (the
+// "control" part, which a run reads but never writes except the counters,
+// which it leaves at zero), then each linear's scratch (partial latents,
+// operand records), which must start zero.
+struct GroupLayout {
+    int64_t i0 = 0, i1 = 0, iF = 0, i2 = 0, nf = 0;
+    size_t table, lin0, lin1, linF, lin2, ord1, ord2, ordP1, tabP2, arrive, sync, ctrl_end, total;
+};
+
+GroupLayout group_layout(const Linear *ls, int n, const Shape &s, const Grain &gr, std::vector<MLin> *tab,
+                         std::vector<size_t> *scratch) {
+    GroupLayout g;
+    size_t lin_bytes = 0;
+    if (tab) tab->assign((size_t)n, MLin{});
+    if (scratch) scratch->assign((size_t)n, 0);
+    for (int j = 0; j < n; ++j) {
+        MLin m;
+        const size_t b = plan_linear(ls[j], s, true, &m, gr);
+        m.item0 = g.i0;
+        m.item1 = g.i1;
+        m.itemF = g.iF;
+        m.item2 = g.i2;
+        m.fin0 = g.nf;
+        g.i0 += items0_of(m);
+        g.i1 += items1_of(m);
+        g.iF += itemsF_of(m);
+        g.i2 += m.n2;
+        g.nf += groups_of(m);
+        if (tab) (*tab)[(size_t)j] = m;
+        if (scratch) (*scratch)[(size_t)j] = b;
+        lin_bytes += b;
+    }
+    size_t at = 256;
+    auto take = [&](size_t bytes) { const size_t o = at; at += rup256(bytes); return o; };
+    g.table = take(sizeof(MLin) * n);
+    g.lin0 = take((size_t)g.i0 * 4);
+    g.lin1 = take((size_t)g.i1 * 4);
+    g.linF = take((size_t)g.iF * 4);
+    g.lin2 = take((size_t)g.i2 * 4);
+    g.ord1 = take((size_t)g.i1 * 4);     // dispatch orders
+    g.ord2 = take((size_t)g.i2 * 4);
+    g.ordP1 = take((size_t)g.i1 * 4);    // k_pass: stage-1 order, stage-2 table
+    g.tabP2 = take((size_t)g.i2 * 8);
+    g.arrive = take((size_t)g.nf * kFlagStride * 4);   // per latent group
+    g.sync = take((size_t)n * kFlagStride * 4);        // per linear
+    g.ctrl_end = at;
+    g.total = at + lin_bytes;
+    return g;
+}
+
 size_t mfma_group_workspace_bytes(const Linear *ls, int n, int64_t T, int y_dtype) {
     Shape s;
     if (!shape_for(T, y_dtype, &s)) return 0;
-    size_t need = 256 + rup256(sizeof(MLin) * n);
-    const Grain gr = group_grain(ls, n, s);
-    int64_t i0 = 0, i1 = 0, iF = 0, i2 = 0, nf = 0;
-    for (int j = 0; j < n; ++j) {
-        MLin m;
-        need += plan_linear(ls[j], s, true, &m, gr);
-        i0 += items0_of(m);
-        i1 += items1_of(m);
-        iF += itemsF_of(m);
-        i2 += m.n2;
-        nf += groups_of(m);
-    }
-    need += rup256((size_t)i0 * 4) + rup256((size_t)i1 * 4) + rup256((size_t)iF * 4) +
-            rup256((size_t)i2 * 4);
-    need += rup256((size_t)i1 * 4) + rup256((size_t)i2 * 4);   // dispatch orders
-    need += rup256((size_t)i1 * 4) + rup256((size_t)i2 * 8);   // k_pass: stage-1 order, stage-2 table
-    need += (size_t)(nf + n) * kFlagStride * 4;                // arrive (per latent group), ready (per linear)
-    return need;
+    return group_layout(ls, n, s, group_grain(ls, n, s), nullptr, nullptr).total;
 }
 
-int mfma_group_prepare(const Linear *ls, int n, int64_t T, int y_dtype, void *ws, size_t ws_bytes,
-                       void *host_state, hipStream_t st) {
-    (void)st;
+int mfma_group_plan(const Linear *ls, int n, int64_t T, int y_dtype, void *ws, size_t ws_bytes, uint64_t tag,
+                    bool fault_test, void *host_state, GroupImage *img) {
     MGroupHost *hs = (MGroupHost *)host_state;
+    *hs = MGroupHost{};
     if (!shape_for(T, y_dtype, &hs->s)) return LB_EUNSUPPORTED;
-    if (ws_bytes < mfma_group_workspace_bytes(ls, n, T, y_dtype)) return LB_EWORKSPACE;
-    uint8_t *w = (uint8_t *)ws;
-    MLin *table_dev = (MLin *)(w + 256);
-    uint8_t *cur = w + 256 + rup256(sizeof(MLin) * n);
-    std::vector<MLin> tab((size_t)n);
     const Grain gr = group_grain(ls, n, hs->s);
-    int64_t i0 = 0, i1 = 0, iF = 0, i2 = 0, nf = 0;
+    std::vector<MLin> tab;
+    std::vector<size_t> scratch;
+    const GroupLayout G = group_layout(ls, n, hs->s, gr, &tab, &scratch);
+    if (ws_bytes < G.total) return LB_EWORKSPACE;
+    const int64_t i0 = G.i0, i1 = G.i1, iF = G.iF, i2 = G.i2;
+    uint8_t *w = (uint8_t *)ws;
+    std::vector<uint8_t> &im = img->bytes;
+    im.assign(G.ctrl_end, 0);
+    memcpy(im.data(), &tag, sizeof(tag));
+    uint8_t *cur = w + G.ctrl_end;
     int steps_max = 1;
-    uint8_t *const lin_area = cur;
     for (int j = 0; j < n; ++j) {
         MLin &m = tab[(size_t)j];
-        const size_t b = plan_linear(ls[j], hs->s, true, &m, gr);
         bind_ws(&m, ls[j], hs->s, cur);
-        cur += b;
-        m.item0 = i0;
-        m.item1 = i1;
-        m.itemF = iF;
-        m.item2 = i2;
-        m.fin0 = nf;
-        i0 += items0_of(m);
-        i1 += items1_of(m);
-        iF += itemsF_of(m);
-        i2 += m.n2;
-        nf += groups_of(m);
+        cur += scratch[(size_t)j];
         if (m.kgs > steps_max) steps_max = m.kgs;
     }
+    img->zero_off = G.ctrl_end;
+    img->zero_bytes = G.total - G.ctrl_end;
     MRun &run = hs->run;
     run = MRun{};
     run.dma2 = dma2_for(hs->s, T, steps_max);
@@ -1867,16 +1977,7 @@ int mfma_group_prepare(const Linear *ls, int n, int64_t T, int y_dtype, void *ws
     run.tsplit = gr.tsplit;
     run.flush1 = (int)imin(flush1_for(T, run.tsplit), ntile_max);
     for (int j = 0; j < n; ++j) lds_add(&hs->lds, tab[(size_t)j], hs->s, run.ops2, T, run.flush1, run.tsplit);
-    int32_t *lin0 = (int32_t *)cur;
-    int32_t *lin1 = (int32_t *)((uint8_t *)lin0 + rup256((size_t)i0 * 4));
-    int32_t *linF = (int32_t *)((uint8_t *)lin1 + rup256((size_t)i1 * 4));
-    int32_t *lin2 = (int32_t *)((uint8_t *)linF + rup256((size_t)iF * 4));
-    int32_t *ord1 = (int32_t *)((uint8_t *)lin2 + rup256((size_t)i2 * 4));
-    int32_t *ord2 = (int32_t *)((uint8_t *)ord1 + rup256((size_t)i1 * 4));
-    int32_t *ordP1 = (int32_t *)((uint8_t *)ord2 + rup256((size_t)i2 * 4));
-    int32_t *tabP2 = (int32_t *)((uint8_t *)ordP1 + rup256((size_t)i1 * 4));
-    uint32_t *arrive = (uint32_t *)((uint8_t *)tabP2 + rup256((size_t)i2 * 8));
-    uint32_t *ready = arrive + (size_t)nf * kFlagStride;
+    auto put = [&](size_t off, const void *src, size_t bytes) { if (bytes) memcpy(im.data() + off, src, bytes); };
     std::vector<int32_t> h0((size_t)i0), h1((size_t)i1), hF((size_t)iF), h2((size_t)i2);
     for (int j = 0; j < n; ++j) {
         const MLin &m = tab[(size_t)j];
@@ -1885,90 +1986,70 @@ int mfma_group_prepare(const Linear *ls, int n, int64_t T, int y_dtype, void *ws
         for (int64_t k = 0; k < itemsF_of(m); ++k) hF[(size_t)(m.itemF + k)] = j;
         for (int64_t k = 0; k < m.n2; ++k) h2[(size_t)(m.item2 + k)] = j;
     }
-    if (hipMemcpy(table_dev, tab.data(), sizeof(MLin) * n, hipMemcpyHostToDevice) != hipSuccess ||
-        hipMemcpy(lin0, h0.data(), (size_t)i0 * 4, hipMemcpyHostToDevice) != hipSuccess ||
-        hipMemcpy(lin1, h1.data(), (size_t)i1 * 4, hipMemcpyHostToDevice) != hipSuccess ||
-        hipMemcpy(linF, hF.data(), (size_t)iF * 4, hipMemcpyHostToDevice) != hipSuccess ||
-        hipMemcpy(lin2, h2.data(), (size_t)i2 * 4, hipMemcpyHostToDevice) != hipSuccess)
-        return hip_status(hipGetLastError());
+    put(G.table, tab.data(), sizeof(MLin) * n);
+    put(G.lin0, h0.data(), (size_t)i0 * 4);
+    put(G.lin1, h1.data(), (size_t)i1 * 4);
+    put(G.linF, hF.data(), (size_t)iF * 4);
+    put(G.lin2, h2.data(), (size_t)i2 * 4);
     // dispatch orders: largest items first (bytes of sign planes each streams;
     // ties keep item order), so a launch ends on short workgroups
-    {
-        const bool fz = fused1(hs->s);
-        std::vector<int64_t> c1((size_t)i1), c2((size_t)i2);
-        for (int j = 0; j < n; ++j) {
-            const MLin &m = tab[(size_t)j];
-            for (int64_t k = 0; k < items1_of(m); ++k) {
-                const int64_t c = k % m.nchunks;
-                const int64_t rg = fz ? (k / m.nchunks) % m.nrg : k % m.nrg;
-                const int64_t cc = fz ? c : (k / m.nrg) % m.nchunks;
-                const int64_t nkg = imin(m.kcg, m.kgv - cc * m.kcg);
-                const int64_t span = fz ? (int64_t)run.flush1 * kTile : kRG;
-                const int64_t rows = imin(span, m.r_p - rg * span);
-                c1[(size_t)(m.item1 + k)] = nkg * rows;
-            }
-            for (int64_t k = 0; k < m.n2; ++k) {
-                const int64_t tiles = imin(m.rows2 / kRG, cdiv(m.d_out - k * m.rows2, kRG));
-                c2[(size_t)(m.item2 + k)] = tiles * m.kgs;
-            }
+    const bool fz = fused1(hs->s);
+    std::vector<int64_t> c1((size_t)i1), c2((size_t)i2);
+    for (int j = 0; j < n; ++j) {
+        const MLin &m = tab[(size_t)j];
+        for (int64_t k = 0; k < items1_of(m); ++k) {
+            const int64_t c = k % m.nchunks;
+            const int64_t rg = fz ? (k / m.nchunks) % m.nrg : k % m.nrg;
+            const int64_t cc = fz ? c : (k / m.nrg) % m.nchunks;
+            const int64_t nkg = imin(m.kcg, m.kgv - cc * m.kcg);
+            const int64_t span = fz ? (int64_t)run.flush1 * kTile : kRG;
+            const int64_t rows = imin(span, m.r_p - rg * span);
+            c1[(size_t)(m.item1 + k)] = nkg * rows;
         }
-        auto order = [](const std::vector<int64_t> &cost) {
-            std::vector<int32_t> o(cost.size());
-            for (size_t i = 0; i < o.size(); ++i) o[i] = (int32_t)i;
-            std::stable_sort(o.begin(), o.end(), [&](int32_t a, int32_t b) { return cost[(size_t)a] > cost[(size_t)b]; });
-            return o;
-        };
-        const std::vector<int32_t> o1 = order(c1), o2 = order(c2);
-        if (hipMemcpy(ord1, o1.data(), (size_t)i1 * 4, hipMemcpyHostToDevice) != hipSuccess ||
-            hipMemcpy(ord2, o2.data(), (size_t)i2 * 4, hipMemcpyHostToDevice) != hipSuccess)
-            return hip_status(hipGetLastError());
-        // k_pass: stage-1 items linear by linear (a linear's latents are ready
-        // early); stage-2 items of the early linears largest first, then those
-        // of the late ones, largest first
-        std::vector<int32_t> p1((size_t)i1), p2;
-        for (size_t i = 0; i < p1.size(); ++i) p1[i] = (int32_t)i;
-        std::vector<int32_t> early, late;
-        for (size_t i = 0; i < o2.size(); ++i) {
-            const MLin &m = tab[(size_t)h2[(size_t)o2[i]]];
-            (m.item1 + items1_of(m) > i1 - kLateItems ? late : early).push_back(o2[i]);
+        for (int64_t k = 0; k < m.n2; ++k) {
+            const int64_t tiles = imin(m.rows2 / kRG, cdiv(m.d_out - k * m.rows2, kRG));
+            c2[(size_t)(m.item2 + k)] = tiles * m.kgs;
         }
-        p2 = early;
-        p2.insert(p2.end(), late.begin(), late.end());
-        // one entry per stage-2 workgroup: (linear, first 256-row tile << 8 |
-        // tiles).  (Cutting the last items into smaller pieces, so that the
-        // launch drains sooner, was slower: every piece pays the operand and
-        // flag round trips of an item.)
-        std::vector<int32_t> e2;
-        e2.reserve((size_t)i2 * 2);
-        for (size_t i = 0; i < p2.size(); ++i) {
-            const int j = h2[(size_t)p2[i]];
-            const MLin &m = tab[(size_t)j];
-            const int64_t local = p2[i] - m.item2;
-            const int tiles = (int)imin(m.rows2 / kRG, cdiv(m.d_out - local * m.rows2, kRG));
-            e2.push_back(j);
-            e2.push_back((int32_t)(((local * (m.rows2 / kRG)) << 8) | tiles));
-        }
-        run.items2P = (int64_t)e2.size() / 2;
-        if (hipMemcpy(ordP1, p1.data(), (size_t)i1 * 4, hipMemcpyHostToDevice) != hipSuccess ||
-            hipMemcpy(tabP2, e2.data(), e2.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
-            hipMemset(arrive, 0, (size_t)(nf + n) * kFlagStride * 4) != hipSuccess ||
-            // the one-launch pass stores only the operand bytes that tokens
-            // fill: the rest of the stage-2 records starts (and stays) zero
-            hipMemset(lin_area, 0, (size_t)(cur - lin_area)) != hipSuccess)
-            return hip_status(hipGetLastError());
     }
-    hs->n1_max = 1;
-    for (int j = 0; j < n; ++j) hs->n1_max = imax(hs->n1_max, items1_of(tab[(size_t)j]));
-    hs->epoch = 0;
+    auto order = [](const std::vector<int64_t> &cost) {
+        std::vector<int32_t> o(cost.size());
+        for (size_t i = 0; i < o.size(); ++i) o[i] = (int32_t)i;
+        std::stable_sort(o.begin(), o.end(), [&](int32_t a, int32_t b) { return cost[(size_t)a] > cost[(size_t)b]; });
+        return o;
+    };
+    const std::vector<int32_t> o1 = order(c1), o2 = order(c2);
+    put(G.ord1, o1.data(), (size_t)i1 * 4);
+    put(G.ord2, o2.data(), (size_t)i2 * 4);
+    // k_pass: stage-1 items linear by linear (a linear's latents are ready
+    // early); stage-2 items of the early linears largest first, then those of
+    // the late ones, largest first
+    std::vector<int32_t> p1((size_t)i1), p2;
+    for (size_t i = 0; i < p1.size(); ++i) p1[i] = (int32_t)i;
+    std::vector<int32_t> early, late;
+    for (size_t i = 0; i < o2.size(); ++i) {
+        const MLin &m = tab[(size_t)h2[(size_t)o2[i]]];
+        (m.item1 + items1_of(m) > i1 - kLateItems ? late : early).push_back(o2[i]);
+    }
+    p2 = early;
+    p2.insert(p2.end(), late.begin(), late.end());
+    // one entry per stage-2 workgroup: (linear, first 256-row tile << 8 |
+    // tiles).  (Cutting the last items into smaller pieces, so that the
+    // launch drains sooner, was slower: every piece pays the operand and flag
+    // round trips of an item.)
+    std::vector<int32_t> e2;
+    e2.reserve((size_t)i2 * 2);
+    for (size_t i = 0; i < p2.size(); ++i) {
+        const int j = h2[(size_t)p2[i]];
+        const MLin &m = tab[(size_t)j];
+        const int64_t local = p2[i] - m.item2;
+        const int tiles = (int)imin(m.rows2 / kRG, cdiv(m.d_out - local * m.rows2, kRG));
+        e2.push_back(j);
+        e2.push_back((int32_t)(((local * (m.rows2 / kRG)) << 8) | tiles));
+    }
+    run.items2P = (int64_t)e2.size() / 2;
+    put(G.ordP1, p1.data(), (size_t)i1 * 4);
+    put(G.tabP2, e2.data(), e2.size() * 4);
     hs->n = n;
-    hs->nf = nf;
-    // 2^31 keeps every counter within 31 bits; LB_PASS_EPOCH_LIMIT (a positive
-    // number below that) lowers it, so that tests can run through the reset
-    hs->wrap = 1ull << 31;
-    if (const char *e = getenv("LB_PASS_EPOCH_LIMIT")) {
-        const long long v = atoll(e);
-        if (v > 0 && v < (1ll << 31)) hs->wrap = (uint64_t)v;
-    }
     run.T = (int)T;
     run.x_dtype = ls[0].x_dtype;
     run.y_dtype = y_dtype;
@@ -1976,19 +2057,28 @@ int mfma_group_prepare(const Linear *ls, int n, int64_t T, int y_dtype, void *ws
     run.items1 = i1;
     run.itemsF = iF;
     run.items2 = i2;
-    run.table = table_dev;
-    run.lin0 = lin0;
-    run.lin1 = lin1;
-    run.linF = linF;
-    run.lin2 = lin2;
-    run.ord1 = ord1;
-    run.ord2 = ord2;
-    run.ordP1 = ordP1;
-    run.tabP2 = tabP2;
-    run.arrive = arrive;
-    run.ready = ready;
-    // one launch per run when stage 1 is the fused form and stage 2 k_stage2r
+    run.table = (const MLin *)(w + G.table);
+    run.lin0 = (const int32_t *)(w + G.lin0);
+    run.lin1 = (const int32_t *)(w + G.lin1);
+    run.linF = (const int32_t *)(w + G.linF);
+    run.lin2 = (const int32_t *)(w + G.lin2);
+    run.ord1 = (const int32_t *)(w + G.ord1);
+    run.ord2 = (const int32_t *)(w + G.ord2);
+    run.ordP1 = (const int32_t *)(w + G.ordP1);
+    run.tabP2 = (const int32_t *)(w + G.tabP2);
+    run.arrive = (uint32_t *)(w + G.arrive);
+    run.sync = (uint32_t *)(w + G.sync);
+    run.stamp = (const uint64_t *)w;
+    run.tag = tag;
+    run.spin_limit = fault_test ? kSpinLimitTest : kSpinLimit;
+    run.want_extra = fault_test ? 1u : 0u;
+    // one launch per run when stage 1 is the fused form and stage 2 k_stage2r,
+    // and each linear's events fit the 16-bit halves of its sync word
     run.pass = pass_tokens(hs->s, T) && run.dma2 && i1 > 0 && i2 > 0 ? 1 : 0;
+    for (int j = 0; j < n; ++j) {
+        const MLin &m = tab[(size_t)j];
+        if ((int64_t)m.P * m.nrg + m.n2 >= 0xffff) run.pass = 0;
+    }
     hs->lds_pass = 0;
     if (run.pass) {
         const size_t l2 = ops2r_bytes(run.ops2, hs->s.NB2, rows2(hs->s, T)) + 2 * kHRows * 2 +
@@ -2002,11 +2092,6 @@ int mfma_group_prepare(const Linear *ls, int n, int64_t T, int y_dtype, void *ws
 }
 
 size_t mfma_group_state_bytes() { return sizeof(MGroupHost); }
-
-__global__ void k_zero_words(uint32_t *a, int64_t n) {
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-        a[i] = 0u;
-}
 
 template <int NL, int NB2>
 int launch_pass(const MRun &run, size_t lds, hipStream_t st) {
@@ -2023,39 +2108,64 @@ int launch_pass(const MRun &run, size_t lds, hipStream_t st) {
 }
 
 int mfma_group_run(const void *host_state, hipStream_t st, int stage_mask) {
-    // the run number advances with every one-launch run (the state is the
-    // group's own; runs of one group are issued one at a time)
-    MGroupHost *hs = (MGroupHost *)const_cast<void *>(host_state);
-    MRun &r = hs->run;
+    const MGroupHost *hs = (const MGroupHost *)host_state;
+    const MRun &r = hs->run;
     // every launch of a group looks its items up in these tables
     if (!r.table || (r.items0 > 0 && !r.lin0) || (r.items1 > 0 && !r.lin1) || (r.itemsF > 0 && !r.linF) ||
         (r.items2 > 0 && !r.lin2))
         return LB_EINVAL;
     if (stage_mask == 3 && r.pass) {
-        if (!r.ordP1 || !r.tabP2 || !r.arrive || !r.ready || r.items2P != r.items2) return LB_EINVAL;
-        // the counters reach (epoch + 1) * nchunks or (epoch + 1) * P * nrg,
-        // at most (epoch + 1) * items1 of a linear: start over before that
-        // leaves 31 bits (arrive and ready are contiguous)
-        if ((uint64_t)(hs->epoch + 1) * (uint64_t)hs->n1_max >= hs->wrap) {
-            const int64_t words = (hs->nf + hs->n) * kFlagStride;
-            k_zero_words<<<(unsigned)imin(1024, cdiv(words, 256)), 256, 0, st>>>(r.arrive, words);
-            if (int rc = last_launch_status()) return rc;
-            hs->epoch = 0;
-        }
-        r.epoch = hs->epoch;
-        int rc = LB_EUNSUPPORTED;
+        if (!r.ordP1 || !r.tabP2 || !r.arrive || !r.sync || r.items2P != r.items2) return LB_EINVAL;
         const int key = hs->s.NL * 10 + hs->s.NB2;
         switch (key) {
-            case 21: rc = launch_pass<2, 1>(r, hs->lds_pass, st); break;
-            case 22: rc = launch_pass<2, 2>(r, hs->lds_pass, st); break;
-            case 31: rc = launch_pass<3, 1>(r, hs->lds_pass, st); break;
-            case 32: rc = launch_pass<3, 2>(r, hs->lds_pass, st); break;
+            case 21: return launch_pass<2, 1>(r, hs->lds_pass, st);
+            case 22: return launch_pass<2, 2>(r, hs->lds_pass, st);
+            case 31: return launch_pass<3, 1>(r, hs->lds_pass, st);
+            case 32: return launch_pass<3, 2>(r, hs->lds_pass, st);
         }
-        if (rc == LB_OK) ++hs->epoch;
-        return rc;
+        return LB_EUNSUPPORTED;
     }
     MLin dummy{};
     return launch_shape(hs->s, hs->run, dummy, hs->lds, st, stage_mask);
+}
+
+// ---- the fault word ----------------------------------------------------------
+
+namespace {
+__global__ void k_take_faults(uint32_t *out) {
+    *out = __hip_atomic_exchange(&g_lb_faults, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__global__ void k_fill_words(uint32_t *a, int64_t n, uint32_t v) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        a[i] = v;
+}
+}  // namespace
+
+int take_faults(hipStream_t st, uint32_t *faults) {
+    // one word per device for the exchanged value, found once per device
+    static uint32_t *out_dev[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hip_status(hipGetLastError());
+    if (!out_dev[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_lb_faults_out)) != hipSuccess) return hip_status(hipGetLastError());
+        out_dev[dev] = (uint32_t *)p;
+    }
+    k_take_faults<<<1, 1, 0, st>>>(out_dev[dev]);
+    if (int rc = last_launch_status()) return rc;
+    uint32_t v = 0;
+    if (hipMemcpyAsync(&v, out_dev[dev], 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+        return hip_status(hipGetLastError());
+    *faults = v;
+    return LB_OK;
+}
+
+int fill_words(void *p, size_t bytes, uint32_t v, hipStream_t st) {
+    const int64_t n = (int64_t)(bytes / 4);
+    if (n <= 0) return LB_OK;
+    k_fill_words<<<(unsigned)imin(2048, cdiv(n, 256)), 256, 0, st>>>((uint32_t *)p, n, v);
+    return last_launch_status();
 }
 
 }  // namespace lb

@@ -28,6 +28,7 @@
 // every linear of a group (a table maps work items to linears), and work items
 // are renumbered so that each of the 8 XCDs (own L2) gets a contiguous range:
 // neighbouring tiles share their activation rows.
+#include <cstring>
 #include <vector>
 
 #include "lb_internal.h"
@@ -99,7 +100,23 @@ struct GRun {
     int64_t itemsG, items1, itemsR, items2;
     const GLin *table;                       // null: the single linear passed by value
     const int32_t *linG, *lin1, *linR, *lin2;   // item -> linear, per launch
+    // groups: the workspace stamp written at set-up, the tag it must equal and
+    // the device's fault word (stamp null for a single linear)
+    const uint64_t *stamp;
+    uint64_t tag;
+    uint32_t *faults;
 };
+
+// Whether a group's workspace no longer carries the stamp the group was set up
+// with: its tables are then not to be trusted, so the workgroup reports
+// LB_FAULT_STALE_WORKSPACE and does nothing.  Uniform.
+__device__ __forceinline__ bool stale_ws(const GRun &run) {
+    if (!run.stamp || *run.stamp == run.tag) return false;
+    if (threadIdx.x == 0 && run.faults)
+        __hip_atomic_fetch_or(run.faults, (uint32_t)LB_FAULT_STALE_WORKSPACE, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
+    return true;
+}
 
 // Work item v of n for block b: each XCD (blocks b % 8) takes a contiguous range.
 __device__ __forceinline__ int64_t xcd_order(int64_t b, int64_t n) {
@@ -189,6 +206,7 @@ __global__ __launch_bounds__(kThreads, NBW == 4 ? 1 : 2) void k_gemm(GRun run, G
     using SH = Shape<NBW>;
     constexpr int BN = SH::BN, XWave = SH::XWave, Slot = SH::Slot, Stages = SH::Stages;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    if (stale_ws(run)) return;
     const int64_t items = STAGE == 1 ? run.items1 : run.items2;
     const int64_t v = xcd_order(blockIdx.x, items);
     const GLin L = pick(run, single, STAGE == 1 ? run.lin1 : run.lin2, v);
@@ -478,6 +496,7 @@ __global__ __launch_bounds__(kThreads, NBW == 4 ? 1 : 2) void k_gemm(GRun run, G
 constexpr int kPrep = 1024;       // words per item
 
 __global__ __launch_bounds__(kThreads) void k_prep(GRun run, GLin single) {
+    if (stale_ws(run)) return;
     const int64_t v = blockIdx.x;
     const GLin L = pick(run, single, run.linG, v);
     const int64_t local = v - L.itemG;
@@ -510,6 +529,7 @@ __global__ __launch_bounds__(kThreads) void k_prep(GRun run, GLin single) {
 constexpr int kRedGroups = 1024;
 
 __global__ __launch_bounds__(kThreads) void k_reduce(GRun run, GLin single) {
+    if (stale_ws(run)) return;
     const int64_t v = blockIdx.x;
     const GLin L = pick(run, single, run.linR, v);
     const int64_t local = v - L.itemR;
@@ -696,6 +716,8 @@ int launch_gemms(const GRun &run, const GLin &single, hipStream_t st) {
 
 }  // namespace
 
+bool gemm_linear_supported(const Linear &a) { return gemm_shape_ok(a); }
+
 size_t gemm_workspace_bytes(const Linear &a) {
     const size_t v = valu_workspace_bytes(a);
     if (!gemm_shape_ok(a)) return v;
@@ -733,7 +755,7 @@ int gemm_forward(const Linear &a, void *ws, hipStream_t st) {
 // ---- groups ------------------------------------------------------------------
 
 struct GGroupHost {
-    GRun run;      // the weight preparation (k_prep) ran at prepare time
+    GRun run;
 };
 
 // bf16 inputs only (fp32 groups run linear by linear)
@@ -743,56 +765,67 @@ bool gemm_group_supported(const Linear *ls, int n) {
     return n > 0 && ls[0].T > 0;
 }
 
-size_t gemm_group_workspace_bytes(const Linear *ls, int n) {
+// Workspace of a group: the 256-byte header (the stamp), the per-linear table
+// and the item tables (the "control" part), then each linear's scratch.
+struct GLayout {
+    int64_t iG = 0, i1 = 0, iR = 0, i2 = 0;
+    size_t table, linG, lin1, linR, lin2, ctrl_end, total;
+};
+
+GLayout glayout(const Linear *ls, int n, std::vector<GLin> *tab, std::vector<size_t> *scratch) {
     std::vector<int> sp;
     stage1_splits(ls, n, sp);
-    size_t need = 256 + rup256(sizeof(GLin) * n);
-    int64_t iG = 0, i1 = 0, iR = 0, i2 = 0;
+    GLayout g;
+    size_t lin_bytes = 0;
+    if (tab) tab->assign((size_t)n, GLin{});
+    if (scratch) scratch->assign((size_t)n, 0);
     for (int j = 0; j < n; ++j) {
         GLin m;
-        need += plan(ls[j], &m, sp[(size_t)j]);
-        iG += m.ngp;
-        i1 += items1_of(m);
-        iR += m.nred;
-        i2 += items2_of(m);
+        const size_t b = plan(ls[j], &m, sp[(size_t)j]);
+        m.itemG = g.iG;
+        m.item1 = g.i1;
+        m.itemR = g.iR;
+        m.item2 = g.i2;
+        g.iG += m.ngp;
+        g.i1 += items1_of(m);
+        g.iR += m.nred;
+        g.i2 += items2_of(m);
+        if (tab) (*tab)[(size_t)j] = m;
+        if (scratch) (*scratch)[(size_t)j] = b;
+        lin_bytes += b;
     }
-    return need + rup256((size_t)iG * 4) + rup256((size_t)i1 * 4) + rup256((size_t)iR * 4) +
-           rup256((size_t)i2 * 4);
+    size_t at = 256;
+    auto take = [&](size_t bytes) { const size_t o = at; at += rup256(bytes); return o; };
+    g.table = take(sizeof(GLin) * n);
+    g.linG = take((size_t)g.iG * 4);
+    g.lin1 = take((size_t)g.i1 * 4);
+    g.linR = take((size_t)g.iR * 4);
+    g.lin2 = take((size_t)g.i2 * 4);
+    g.ctrl_end = at;
+    g.total = at + lin_bytes;
+    return g;
 }
+
+size_t gemm_group_workspace_bytes(const Linear *ls, int n) { return glayout(ls, n, nullptr, nullptr).total; }
 
 size_t gemm_group_state_bytes() { return sizeof(GGroupHost); }
 
-int gemm_group_prepare(const Linear *ls, int n, void *ws, size_t ws_bytes, void *host_state,
-                       hipStream_t st) {
+int gemm_group_plan(const Linear *ls, int n, void *ws, size_t ws_bytes, uint64_t tag, void *host_state,
+                    GroupImage *img) {
     GGroupHost *hs = (GGroupHost *)host_state;
+    *hs = GGroupHost{};
     if (!gemm_group_supported(ls, n)) return LB_EUNSUPPORTED;
-    if (ws_bytes < gemm_group_workspace_bytes(ls, n)) return LB_EWORKSPACE;
+    std::vector<GLin> tab;
+    std::vector<size_t> scratch;
+    const GLayout G = glayout(ls, n, &tab, &scratch);
+    if (ws_bytes < G.total) return LB_EWORKSPACE;
     uint8_t *w = (uint8_t *)ws;
-    std::vector<int> sp;
-    stage1_splits(ls, n, sp);
-    GLin *table_dev = (GLin *)(w + 256);
-    uint8_t *cur = w + 256 + rup256(sizeof(GLin) * n);
-    std::vector<GLin> tab((size_t)n);
-    int64_t iG = 0, i1 = 0, iR = 0, i2 = 0;
+    uint8_t *cur = w + G.ctrl_end;
     for (int j = 0; j < n; ++j) {
-        GLin &m = tab[(size_t)j];
-        const size_t b = plan(ls[j], &m, sp[(size_t)j]);
-        bind(&m, ls[j], cur);
-        cur += b;
-        m.itemG = iG;
-        m.item1 = i1;
-        m.itemR = iR;
-        m.item2 = i2;
-        iG += m.ngp;
-        i1 += items1_of(m);
-        iR += m.nred;
-        i2 += items2_of(m);
+        bind(&tab[(size_t)j], ls[j], cur);
+        cur += scratch[(size_t)j];
     }
-    int32_t *linG = (int32_t *)cur;
-    int32_t *lin1 = (int32_t *)((uint8_t *)linG + rup256((size_t)iG * 4));
-    int32_t *linR = (int32_t *)((uint8_t *)lin1 + rup256((size_t)i1 * 4));
-    int32_t *lin2 = (int32_t *)((uint8_t *)linR + rup256((size_t)iR * 4));
-    std::vector<int32_t> hG((size_t)iG), h1((size_t)i1), hR((size_t)iR), h2((size_t)i2);
+    std::vector<int32_t> hG((size_t)G.iG), h1((size_t)G.i1), hR((size_t)G.iR), h2((size_t)G.i2);
     for (int j = 0; j < n; ++j) {
         const GLin &m = tab[(size_t)j];
         for (int64_t k = 0; k < m.ngp; ++k) hG[(size_t)(m.itemG + k)] = j;
@@ -800,38 +833,41 @@ int gemm_group_prepare(const Linear *ls, int n, void *ws, size_t ws_bytes, void 
         for (int64_t k = 0; k < m.nred; ++k) hR[(size_t)(m.itemR + k)] = j;
         for (int64_t k = 0; k < items2_of(m); ++k) h2[(size_t)(m.item2 + k)] = j;
     }
-    if (hipMemcpy(table_dev, tab.data(), sizeof(GLin) * n, hipMemcpyHostToDevice) != hipSuccess ||
-        (iG && hipMemcpy(linG, hG.data(), (size_t)iG * 4, hipMemcpyHostToDevice) != hipSuccess) ||
-        (i1 && hipMemcpy(lin1, h1.data(), (size_t)i1 * 4, hipMemcpyHostToDevice) != hipSuccess) ||
-        (iR && hipMemcpy(linR, hR.data(), (size_t)iR * 4, hipMemcpyHostToDevice) != hipSuccess) ||
-        (i2 && hipMemcpy(lin2, h2.data(), (size_t)i2 * 4, hipMemcpyHostToDevice) != hipSuccess))
-        return hip_status(hipGetLastError());
+    std::vector<uint8_t> &im = img->bytes;
+    im.assign(G.ctrl_end, 0);
+    memcpy(im.data(), &tag, sizeof(tag));
+    auto put = [&](size_t off, const void *src, size_t bytes) { if (bytes) memcpy(im.data() + off, src, bytes); };
+    put(G.table, tab.data(), sizeof(GLin) * n);
+    put(G.linG, hG.data(), (size_t)G.iG * 4);
+    put(G.lin1, h1.data(), (size_t)G.i1 * 4);
+    put(G.linR, hR.data(), (size_t)G.iR * 4);
+    put(G.lin2, h2.data(), (size_t)G.i2 * 4);
+    // the scratch needs no initial contents (every byte a run reads it writes first)
+    img->zero_off = G.ctrl_end;
+    img->zero_bytes = 0;
     GRun &run = hs->run;
     run = GRun{};
     run.T = (int)ls[0].T;
     run.y_dtype = ls[0].y_dtype;
-    run.itemsG = iG;
-    run.items1 = i1;
-    run.itemsR = iR;
-    run.items2 = i2;
-    run.table = table_dev;
-    run.linG = linG;
-    run.lin1 = lin1;
-    run.linR = linR;
-    run.lin2 = lin2;
-    // the factors are captured with the group: convert g and unzip the sign
-    // words once here (runs read the converted copies)
-    GRun prep = run;
-    prep.items1 = prep.itemsR = prep.items2 = 0;
-    GLin dummy{};
-    if (int rc = launch_gemms(prep, dummy, st)) return rc;
-    run.itemsG = 0;
-    return hip_status(hipStreamSynchronize(st));
+    run.itemsG = G.iG;
+    run.items1 = G.i1;
+    run.itemsR = G.iR;
+    run.items2 = G.i2;
+    run.table = (const GLin *)(w + G.table);
+    run.linG = (const int32_t *)(w + G.linG);
+    run.lin1 = (const int32_t *)(w + G.lin1);
+    run.linR = (const int32_t *)(w + G.linR);
+    run.lin2 = (const int32_t *)(w + G.lin2);
+    run.stamp = (const uint64_t *)w;
+    run.tag = tag;
+    run.faults = fault_word_ptr();
+    return LB_OK;
 }
 
 int gemm_group_run(const void *host_state, hipStream_t st, int stage_mask) {
     const GGroupHost *hs = (const GGroupHost *)host_state;
     GRun run = hs->run;
+    if (!(stage_mask & 4)) run.itemsG = 0;
     if (!(stage_mask & 1)) run.items1 = run.itemsR = 0;
     if (!(stage_mask & 2)) run.items2 = 0;
     GLin dummy{};

@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stddef.h>
+#include <vector>
 
 #include "littlebit.h"
 
@@ -75,30 +76,53 @@ int launch_pack(const float *src, int64_t rows, int64_t cols, int axis, uint32_t
 size_t valu_workspace_bytes(const Linear &a);
 int valu_forward(const Linear &a, void *ws, hipStream_t s);
 
+// The set-up of a group of linears: what its workspace must hold before a
+// run.  Bytes [0, bytes.size()) of the workspace are `bytes` (header with the
+// stamp, tables, zeroed counters); [zero_off, zero_off + zero_bytes) are zero.
+struct GroupImage {
+    std::vector<uint8_t> bytes;
+    size_t zero_off = 0, zero_bytes = 0;
+};
+
 // Matrix-core decode path (fp4 signs x fp8 activation limbs).
 bool mfma_decode_supported(int64_t T, int y_dtype);
+// Whether the decode kernels' 32-bit buffer offsets cover this linear.
+bool mfma_decode_shape_ok(const Linear &a);
 size_t mfma_decode_workspace_bytes(const Linear &a);
 int mfma_decode_forward(const Linear &a, void *ws, hipStream_t s);
-// Groups of independent linears on the matrix-core decode path: two launches per run.
+// Groups of independent linears on the matrix-core decode path.
 size_t mfma_group_workspace_bytes(const Linear *ls, int n, int64_t T, int y_dtype);
 size_t mfma_group_state_bytes();
-int mfma_group_prepare(const Linear *ls, int n, int64_t T, int y_dtype, void *ws, size_t ws_bytes,
-                       void *host_state, hipStream_t s);
+// Plans a group on workspace ws: fills the host state and the image.
+// fault_test: the one-launch pass's waits ask for one latent group more than
+// exists and give up after a few polls (LB_GROUP_FAULT_TEST).
+int mfma_group_plan(const Linear *ls, int n, int64_t T, int y_dtype, void *ws, size_t ws_bytes, uint64_t tag,
+                    bool fault_test, void *host_state, GroupImage *img);
 int mfma_group_run(const void *host_state, hipStream_t s, int stage_mask = 3);
+
+// Reads and clears this device's fault word (after the work on s is done).
+int take_faults(hipStream_t s, uint32_t *faults);
+// Sets bytes / 4 words at p to v (a kernel, so it may be captured in a graph).
+int fill_words(void *p, size_t bytes, uint32_t v, hipStream_t s);
 
 // GEMM (prefill) path: bf16 matrix cores; shapes it does not take (d_in % 8,
 // misaligned x) run on the vector-ALU kernels.
+bool gemm_linear_supported(const Linear &a);
 size_t gemm_workspace_bytes(const Linear &a);
 int gemm_forward(const Linear &a, void *ws, hipStream_t s);
-// Groups of independent linears on the GEMM path: stage 1 (+ reduce), stage 2.
+// Groups of independent linears on the GEMM path: the factor preparation
+// (bf16 g, unzipped sign words), stage 1 (+ reduce), stage 2.
 bool gemm_group_supported(const Linear *ls, int n);
 size_t gemm_group_workspace_bytes(const Linear *ls, int n);
 size_t gemm_group_state_bytes();
-// Also prepares the captured factors (bf16 g, unzipped sign words) on stream s
-// and waits for it.
-int gemm_group_prepare(const Linear *ls, int n, void *ws, size_t ws_bytes, void *host_state,
-                       hipStream_t s);
+int gemm_group_plan(const Linear *ls, int n, void *ws, size_t ws_bytes, uint64_t tag, void *host_state,
+                    GroupImage *img);
+// stage_mask: bit 0 stage 1, bit 1 stage 2, bit 2 the factor preparation
+// (before stage 1), which a prepared group runs once at set-up.
 int gemm_group_run(const void *host_state, hipStream_t s, int stage_mask = 3);
+// The fault word of the current device (kernels of other sources report
+// through this pointer).
+uint32_t *fault_word_ptr();
 
 // SwiGLU gate: a = silu(gate) * up, elementwise over n values (fp32 in place).
 int launch_swiglu_f32(float *gate_io, const float *up, int64_t n, hipStream_t s);

@@ -35,6 +35,12 @@
  *    bits past the end of the packed axis and words past the other axis are 0.
  *    The pages store one bit per factor entry (sesamedisk, "How low-rank
  *    binarization works"); the bit order and plane layout are this library's.
+ *    Deliberately plane-major, i.e. the TRANSPOSE of the row-major word layout
+ *    [other axis][ld_words] a reader might expect (V as [r_p][d_in/32]):
+ *    here V is [d_in/32][ld_v] and U is [r_p/32][ld_u].  A 16-byte load then
+ *    gives a lane four consecutive latents (stage 1) or output rows (stage 2)
+ *    of one plane, so a wave's loads are contiguous.  Words in the other
+ *    layout give wrong outputs without an error: pack with lb_pack_signs.
  */
 #ifndef LITTLEBIT_H
 #define LITTLEBIT_H
@@ -53,6 +59,7 @@ extern "C" {
 #define LB_EALIGN       -3   /* pointer or ld misaligned */
 #define LB_EWORKSPACE   -4   /* workspace missing or too small */
 #define LB_EHIP         -5   /* the HIP runtime reported an error */
+#define LB_EDEVICE      -6   /* a kernel reported a fault (lb_device_faults) */
 
 /* activation dtypes */
 #define LB_F32  0
@@ -65,6 +72,22 @@ extern "C" {
 #define LB_PATH_DECODE_VALU 3u  /* force the plain vector-ALU decode kernels */
 #define LB_PATH_MASK        15u
 
+/* flags: for groups only (lb_grouped_prepare, lb_linear_forward_grouped).
+ * LB_GROUP_FAULT_TEST exists to test the fault report: in a group that runs
+ * as one launch per pass (see lb_grouped_run), every stage-2 workgroup waits
+ * for one latent group more than the linear has and gives up after a few
+ * polls, so every run reports LB_FAULT_HANDOFF_TIMEOUT and its outputs are
+ * wrong.  Every kernel still ends normally and the group's counters return to
+ * zero.  Never set it outside such a test. */
+#define LB_GROUP_FAULT_TEST (1u << 8)
+
+/* Fault bits a kernel can report (lb_device_faults). */
+#define LB_FAULT_HANDOFF_TIMEOUT 1u  /* a stage-2 workgroup of a one-launch pass gave up waiting for
+                                        its linear's latents: that run's outputs are wrong */
+#define LB_FAULT_STALE_WORKSPACE 2u  /* a prepared group's workspace no longer carried the stamp the
+                                        group was prepared with (the memory was reused or written
+                                        since): the launch did nothing and its outputs are unset */
+
 /* Library version, (major << 16) | minor. */
 int lb_version(void);
 
@@ -74,6 +97,22 @@ const char *lb_status_string(int status);
 /* Text of the last HIP runtime error this thread saw inside the library (the
  * cause behind an LB_EHIP status); static storage. */
 const char *lb_last_hip_error(void);
+
+/* Faults the kernels reported on the current device since the last call.
+ * BLOCKS until the work enqueued on `stream` is done, then reads and clears
+ * the device's fault word (one per device, owned by the library, shared by
+ * every stream and caller on that device).  Writes the LB_FAULT_* bits to
+ * *faults (host pointer; may be NULL).  Returns LB_OK if none was set,
+ * LB_EDEVICE if any was, LB_EHIP if the runtime failed. */
+int lb_device_faults(void *stream, uint32_t *faults);
+
+/* The kernel family lb_linear_forward would use for these sizes and flags,
+ * with packed strides from lb_packed_ld_aligned and aligned pointers:
+ * LB_PATH_DECODE (matrix-core decode), LB_PATH_PREFILL (bf16 GEMM) or
+ * LB_PATH_DECODE_VALU (vector ALU), or a negative status for a request
+ * lb_linear_forward would reject.  Host only; enqueues nothing. */
+int lb_linear_path(int64_t d_in, int64_t d_out, int64_t r, int64_t T, int residual,
+                   int x_dtype, int y_dtype, unsigned flags);
 
 /* Rank from the bit budget (littlebitllm page, "Pipeline" step 01 and "How
  * small": the rank is sized to the target bits per weight, counting factor bits
@@ -182,11 +221,50 @@ typedef struct lb_linear_desc {
     int32_t reserved;
 } lb_linear_desc;
 
+/* One independent linear of lb_linear_forward_grouped: the arguments of
+ * lb_linear_forward (x [T][d_in], y [T][d_out], device pointers). */
+typedef struct lb_linear_call {
+    const void *x;
+    void *y;
+    lb_factors w;
+    int64_t d_in, d_out, r, T;
+    int32_t residual;
+    int32_t x_dtype, y_dtype;
+    uint32_t flags;     /* path flags, and LB_GROUP_FAULT_TEST */
+} lb_linear_call;
+
+/* Workspace bytes lb_linear_forward_grouped needs for these calls.  0 on bad
+ * arguments. */
+size_t lb_linear_grouped_workspace_bytes(const lb_linear_call *calls, int n);
+
+/* n independent linears in few launches (q/k/v, a layer, a layer stack):
+ * every calls[i].y = layer_i(calls[i].x), as n calls of lb_linear_forward
+ * would give.  Stateless: nothing carries over from earlier calls, ws
+ * (device, 256-byte aligned, >= lb_linear_grouped_workspace_bytes) needs no
+ * contents and is clobbered, and the call may be captured in a graph.  Calls
+ * with equal (T, x_dtype, y_dtype, flags) run together as one group, in the
+ * order of their first appearance; groups run one after another on `stream`.
+ * Each group run first copies its work tables into ws (host to device, about
+ * 100 bytes per linear plus 12-20 bytes per work item) and clears its
+ * counters; the tables are planned on the host on first use of an argument set
+ * and cached (the last 8 sets: key = the calls' bytes, ws, ws_bytes and the
+ * device; the cache holds pinned host copies of the tables; a set whose call
+ * was captured in a graph keeps its copy, which the graph's copy node reads,
+ * until the process ends).  For a group that runs many times,
+ * lb_grouped_prepare / lb_grouped_run skip the copy.
+ * Errors as lb_linear_forward; every call is checked before anything is
+ * enqueued.  No output may overlap an input, another output or ws. */
+int lb_linear_forward_grouped(const lb_linear_call *calls, int n, void *ws, size_t ws_bytes,
+                              void *stream);
+
 /* Workspace bytes for a group of n linears at T tokens. 0 on bad arguments. */
 size_t lb_grouped_workspace_bytes(const lb_linear_desc *descs, int n, int64_t T, unsigned flags);
 
-/* Build the device work table of a group into ws.  BLOCKS until the table is
- * on the device (a setup call, not for the timed loop).  descs is a host array
+/* Build the device work table of a group into ws and keep a host record of
+ * the group, keyed by ws (lb_grouped_release forgets it; preparing another
+ * group on the same ws replaces it).  BLOCKS until the table is on the device
+ * (a setup call, not for the timed loop); ws must not be written until the
+ * group is released, except by the group's own runs.  descs is a host array
  * of n descriptors; it is copied and may be freed afterwards.  All linears use
  * x_dtype / y_dtype and T tokens.  The pointers in descs are captured: later
  * runs read and write the same buffers.  The kernels a group runs:
@@ -205,13 +283,16 @@ int lb_grouped_prepare(const lb_linear_desc *descs, int n, int64_t T, int x_dtyp
 /* Run a prepared group: every linear's y = layer(x), in a few launches for the
  * whole group (all first contractions, then all second contractions).  A
  * decode group at T <= 2 (bf16 output) or T = 1 (fp32) whose operands fit
- * the LDS runs as ONE launch: each
- * linear's stage 2 starts as soon as its own stage 1 and latents are done.
- * That launch numbers its runs in ws (counters that keep counting), so runs
- * of one group must be issued one after the other, from one thread at a
- * time, each on a stream ordered after the previous run; runs on the same
- * workspace that overlap race, and the workspace must not be written between
- * runs. */
+ * the LDS runs as ONE launch: each linear's stage 2 starts as soon as its own
+ * stage 1 and latents are done.  Its workgroups hand the latents over through
+ * counters in ws, which every run leaves at zero, so a run needs no state from
+ * the host: a run may be captured in a graph and replayed.  Runs that overlap
+ * on the same workspace race.  Every launch first checks the stamp
+ * lb_grouped_prepare wrote into ws: if ws was reused or overwritten since,
+ * the launch does nothing and reports LB_FAULT_STALE_WORKSPACE.  A stage-2
+ * wait that gives up reports LB_FAULT_HANDOFF_TIMEOUT.  Either is read with
+ * lb_device_faults; after one, prepare the group again.  LB_EINVAL for a ws
+ * with no prepared group. */
 int lb_grouped_run(void *ws, void *stream);
 
 /* Forget a prepared group (its host-side record; ws itself stays the

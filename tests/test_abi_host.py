@@ -31,7 +31,8 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for rc in (lb.LB_OK, lb.LB_EINVAL, lb.LB_EUNSUPPORTED, lb.LB_EALIGN, lb.LB_EWORKSPACE, lb.LB_EHIP):
+    for rc in (lb.LB_OK, lb.LB_EINVAL, lb.LB_EUNSUPPORTED, lb.LB_EALIGN, lb.LB_EWORKSPACE, lb.LB_EHIP,
+               lb.LB_EDEVICE):
         assert lb.status_string(rc) and lb.status_string(rc) != "unknown status"
 
 
@@ -138,3 +139,66 @@ def test_mlp_and_group_argument_errors():
     assert L.lb_grouped_prepare(arr, 1, 1, lb.LB_F32, lb.LB_F32, None, 0, 0, None) == lb.LB_EWORKSPACE
     assert L.lb_grouped_run(FAKE, None) == lb.LB_EINVAL                   # never prepared
     assert L.lb_grouped_release(FAKE) == lb.LB_EINVAL                     # never prepared
+
+
+def test_linear_path_choice():
+    """Which kernel family a request takes (host only): the decode kernels up
+    to 32 tokens, the bf16 GEMM kernels above for bf16 outputs, the vector-ALU
+    kernels for fp32 outputs above 32 tokens, for shapes the GEMM kernels do not
+    take, and for buffers the decode kernels' 32-bit offsets cannot address."""
+    import torch
+    bf, f32 = torch.bfloat16, torch.float32
+    D, G, V = lb.LB_PATH_DECODE, lb.LB_PATH_PREFILL, lb.LB_PATH_DECODE_VALU
+    assert lb.linear_path(8192, 28672, 608, 1, True, bf, bf) == D
+    assert lb.linear_path(8192, 28672, 608, 32, True, bf, bf) == D
+    assert lb.linear_path(8192, 28672, 608, 33, True, bf, bf) == G
+    assert lb.linear_path(8192, 28672, 608, 2048, True, bf, bf) == G
+    assert lb.linear_path(1024, 1024, 512, 64, False, f32, f32) == V
+    assert lb.linear_path(100, 70, 32, 64, True, bf, bf) == V            # d_in % 8 != 0
+    assert lb.linear_path(1024, 1024, 512, 1, False, f32, f32, lb.LB_PATH_DECODE_VALU) == V
+    # x of 32 tokens x 2^25 fp32 inputs is 4 GiB: past the decode kernels' offsets
+    assert lb.linear_path(1 << 25, 64, 64, 32, False, f32, f32) == V
+    assert lb.linear_path(1 << 25, 64, 64, 1, False, f32, f32) == D
+    with pytest.raises(lb.LBError) as e:
+        lb.linear_path(1024, 1024, 512, 64, False, f32, f32, lb.LB_PATH_PREFILL)
+    assert e.value.status == lb.LB_EUNSUPPORTED
+    with pytest.raises(lb.LBError):
+        lb.linear_path(1024, 1024, 512, 1, False, f32, f32, 1 << 8)     # a group-only flag
+
+
+def _call(**kw):
+    c = lb.lb_linear_call(FAKE + 0x5000000, FAKE + 0x6000000, _factors(), 1024, 1024, 512, 1, 0,
+                          lb.LB_BF16, lb.LB_BF16, 0)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_grouped_call_argument_errors():
+    L = lb.lib()
+    arr = (lb.lb_linear_call * 2)(_call(), _call(x=FAKE + 0x8000000, y=FAKE + 0x9000000, T=64))
+    need = L.lb_linear_grouped_workspace_bytes(arr, 2)
+    assert need > 0
+    # two sub-groups (T = 1 and T = 64) share the workspace: the larger one sizes it
+    one = (lb.lb_linear_call * 1)(arr[0])
+    two = (lb.lb_linear_call * 1)(arr[1])
+    assert need == max(L.lb_linear_grouped_workspace_bytes(one, 1), L.lb_linear_grouped_workspace_bytes(two, 1))
+    assert L.lb_linear_forward_grouped(None, 1, FAKE, need, None) == lb.LB_EINVAL
+    assert L.lb_linear_forward_grouped(arr, 0, FAKE, need, None) == lb.LB_EINVAL
+    assert L.lb_linear_forward_grouped(arr, 2, None, 0, None) == lb.LB_EWORKSPACE
+    assert L.lb_linear_forward_grouped(arr, 2, FAKE + 0xa000000, need - 1, None) == lb.LB_EWORKSPACE
+    bad = (lb.lb_linear_call * 1)(_call(flags=1 << 9))                  # unknown flag bit
+    assert L.lb_linear_forward_grouped(bad, 1, FAKE + 0xa000000, need, None) == lb.LB_EINVAL
+    bad = (lb.lb_linear_call * 1)(_call(r=511, residual=1))             # odd total rank
+    assert L.lb_linear_forward_grouped(bad, 1, FAKE + 0xa000000, need, None) == lb.LB_EINVAL
+    bad = (lb.lb_linear_call * 1)(_call(y=FAKE + 0x5000000))            # y overlaps x
+    assert L.lb_linear_forward_grouped(bad, 1, FAKE + 0xa000000, need, None) == lb.LB_EINVAL
+    bad = (lb.lb_linear_call * 1)(_call(x_dtype=5))
+    assert L.lb_linear_forward_grouped(bad, 1, FAKE + 0xa000000, need, None) == lb.LB_EINVAL
+    assert L.lb_linear_grouped_workspace_bytes(None, 1) == 0
+    descs = (lb.lb_linear_desc * 1)()
+    descs[0] = lb.lb_linear_desc(FAKE + 0x5000000, FAKE + 0x6000000, _factors(), 1024, 1024, 512, 0, 0)
+    assert L.lb_grouped_workspace_bytes(descs, 1, 1, 1 << 9) == 0       # unknown flag bit
+    assert L.lb_grouped_workspace_bytes(descs, 1, 1, lb.LB_GROUP_FAULT_TEST) > 0
+    assert L.lb_grouped_prepare(descs, 1, 1, lb.LB_BF16, lb.LB_BF16, FAKE, 1 << 30, 1 << 9,
+                                None) == lb.LB_EINVAL
