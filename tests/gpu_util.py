@@ -4,6 +4,7 @@ import sys
 import numpy as np
 import pytest
 
+import oracle
 import synth
 
 TOL = {"f32": 1e-3, "bf16": 8e-3}    # relative L2 bound against the fp64 oracle
@@ -47,3 +48,22 @@ def host_layer_from_dev(U, V, h, g, l):
     P, d_out, r_p = U.shape
     return synth.LayerInputs(V.shape[1], d_out, r_p, P, d(U), d(V),
                              d(h).view(np.uint16), d(g).view(np.uint16), d(l).view(np.uint16))
+
+
+def assert_close(got, ref, tol, what=""):
+    """Relative L2 over the whole tensor within tol, and every element within
+    8 * tol * rms(ref): a single wrong element (a lane, a tail row) can hide
+    inside the L2 of a wide output but not under the per-element bound.  The
+    worst element is named on failure."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    err = oracle.rel_l2(got, ref)
+    assert err <= tol, (what, "rel-L2", err, tol)
+    d = np.abs(got - ref)
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    if d.size:
+        i = int(np.argmax(d))
+        bound = 8.0 * tol * rms
+        assert d.flat[i] <= bound, (what, "worst element", np.unravel_index(i, d.shape), float(d.flat[i]),
+                                    "bound", bound, "got", float(got.flat[i]), "want", float(ref.flat[i]))
+    return err

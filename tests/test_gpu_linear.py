@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import TOL, dev_layer, say, torch_or_skip, x_to_dev, y_to_np
+from gpu_util import TOL, assert_close, dev_layer, say, torch_or_skip, x_to_dev, y_to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -40,9 +40,7 @@ def _check(inp, x, out_dtype, path, rows=None, tokens=None):
     else:
         ref = oracle.linear_forward_rows(xs, inp.U, inp.V, inp.h, inp.g, inp.l, rows)
         got = (y if tokens is None else y[tokens])[:, rows]
-    err = oracle.rel_l2(got, ref)
-    assert err <= TOL[out_dtype], err
-    return err
+    return assert_close(got, ref, TOL[out_dtype], (inp.d_in, inp.d_out, inp.r_path, T, out_dtype, path))
 
 
 # ---- configuration 1: 1024 x 1024, 1.0 bpw -> r = 512, no residual, fp32 ----
@@ -225,3 +223,60 @@ def test_decode_and_prefill_agree(path):
     inp = synth.layer_inputs(40, 2048, 1536, 160, 2)
     x = synth.activations(41, 32, 2048, "bf16")
     _check(inp, x, "bf16", path)
+
+
+def _integer_layer(seed, d_in, d_out, r_p, P):
+    """Random signs with integer-friendly scales: g, l in {1, 2}, h in {1/2, 1, 2}."""
+    rng = np.random.default_rng(seed)
+    base = synth.layer_inputs(seed, d_in, d_out, r_p, P)
+    return synth.LayerInputs(d_in, d_out, r_p, P, base.U, base.V, _pow2(rng, (P, d_out), -1, 1),
+                             _pow2(rng, (P, d_in), 0, 1), _pow2(rng, (P, r_p), 0, 1))
+
+
+def _sparse_x(seed, T, d_in, nnz=16):
+    """x in {-2..2}, at most nnz non-zeros per token: |g x| <= 4, |t| <= 2 * 4 * nnz = 128."""
+    rng = np.random.default_rng(seed)
+    x = np.zeros((T, d_in), np.float32)
+    for n in range(T):
+        idx = rng.choice(d_in, size=min(nnz, d_in), replace=False)
+        x[n, idx] = rng.integers(-2, 3, idx.size)
+    return x
+
+
+@pytest.mark.parametrize("d_in,d_out,r_p,P", [(1024, 700, 96, 2), (2080, 515, 200, 2), (96, 1100, 32, 1),
+                                              (4096, 4096, 1024, 2)])
+@pytest.mark.parametrize("T", [1, 2, 5])
+def test_two_limb_decode_exact_regime_bit_exact(d_in, d_out, r_p, P, T):
+    """The bf16-output decode path (two fp8 limbs per activation) in a regime
+    where two limbs are exact: g x integers with |g x| <= 4 (one limb), t an
+    integer with |t| <= 128 (an integer below 256 is the sum of its nearest
+    e4m3 value and an e4m3 remainder, with the block's power-of-two scale), so
+    every partial sum is exact and the bf16 output equals the oracle rounded
+    to bf16 (nearest even) bit for bit."""
+    inp = _integer_layer(50 + T + d_in, d_in, d_out, r_p, P)
+    x = _sparse_x(60 + T, T, d_in)
+    ref = oracle.linear_forward(x, inp.U, inp.V, inp.h, inp.g, inp.l)
+    xb = synth.f32_to_bf16_bits(x)
+    y = _run(inp, xb, "bf16", "decode", T).cpu().view(__import__("torch").int16).numpy().view(np.uint16)
+    want = synth.f32_to_bf16_bits(ref.astype(np.float32))
+    bad = np.argwhere(y != want)
+    assert bad.size == 0, (bad[:4], y[tuple(bad[0])], want[tuple(bad[0])])
+
+
+@pytest.mark.parametrize("path,T,dt", [("decode", 1, "bf16"), ("decode", 4, "bf16"), ("decode", 1, "f32"),
+                                       ("decode", 3, "f32"), ("valu", 2, "bf16"), ("prefill", 64, "bf16")])
+def test_outlier_activations(path, T, dt):
+    """A few input channels 100x larger than the rest (the activation outliers
+    of real models): each 32-input block shares one power-of-two limb scale
+    on the decode path, and the limbs are floating point, so the small inputs
+    beside an outlier keep their own precision.  Within tolerance, and every
+    element within the per-element bound."""
+    d_in, d_out, r_p, P = 4096, 1536, 160, 2
+    inp = synth.layer_inputs(71, d_in, d_out, r_p, P)
+    x = synth.activations(72, T, d_in, "f32")
+    rng = np.random.default_rng(73)
+    ch = rng.choice(d_in, size=12, replace=False)
+    x[:, ch] *= 100.0
+    if dt == "bf16":
+        x = synth.f32_to_bf16_bits(x)
+    _check(inp, x, dt, path)

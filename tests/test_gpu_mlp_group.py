@@ -4,7 +4,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import TOL, dev_layer, host_layer_from_dev, say, torch_or_skip, x_to_dev, y_to_np
+from gpu_util import TOL, assert_close, dev_layer, host_layer_from_dev, say, torch_or_skip, x_to_dev, y_to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -30,8 +30,7 @@ def test_config2_mlp_block(T, path):
                        flags=path)
     torch.cuda.synchronize()
     ref = oracle.mlp_forward(x, g, u, d)
-    err = oracle.rel_l2(y_to_np(y), ref)
-    assert err <= TOL["bf16"], err
+    assert_close(y_to_np(y), ref, TOL["bf16"], ("mlp", T, path))
 
 
 def test_mlp_prefill_sampled():
@@ -45,8 +44,7 @@ def test_mlp_prefill_sampled():
     torch.cuda.synchronize()
     tok = np.array([0, 31, 32, 63, 95])
     ref = oracle.mlp_forward(x[tok], g, u, d)
-    err = oracle.rel_l2(y_to_np(y)[tok], ref)
-    assert err <= TOL["bf16"], err
+    assert_close(y_to_np(y)[tok], ref, TOL["bf16"], "mlp prefill")
 
 
 def _stack_check(key, layers, T, check_layers, rows_per=512, tokens=None):
@@ -78,8 +76,7 @@ def _stack_check(key, layers, T, check_layers, rows_per=512, tokens=None):
             rows = np.unique(np.linspace(0, sh.d_out - 1, rows_per).astype(np.int64))
             ref = oracle.linear_forward_rows(x[tok], inp.U, inp.V, inp.h, inp.g, inp.l, rows)
             got = y_to_np(st.outputs[L][i])[tok][:, rows]
-            err = oracle.rel_l2(got, ref)
-            assert err <= TOL["bf16"], (L, sh.name, err)
+            assert_close(got, ref, TOL["bf16"], (key, L, sh.name))
 
 
 @pytest.mark.parametrize("key,T", [("c3", 4), ("c4", 1), ("c5", 1), ("c3", 32)])
@@ -92,6 +89,14 @@ def test_prefill_layer_group(key, T):
     """One decoder layer's linears as one GEMM-path group (one launch per
     stage for all seven), sampled tokens and rows."""
     _stack_check(key, 1, T, {0}, rows_per=256, tokens=[0, 1, T // 2, T - 2, T - 1])
+
+
+@pytest.mark.parametrize("key,layers", [("c3", 32), ("c4", 40)])
+def test_full_stack_sampled_layers(key, layers):
+    """The 32-layer Llama2-7B-shaped and 40-layer Qwen3-14B-shaped stacks as
+    the benchmark runs them (one group, T = 1, one launch per pass); layers 0,
+    L/2 and L - 1 are checked against the oracle on sampled rows."""
+    _stack_check(key, layers, 1, {0, layers // 2, layers - 1})
 
 
 def test_full_c5_stack_sampled_layers():
@@ -202,18 +207,6 @@ def test_pass_many_runs():
     _runs_match_staged("c5", 1, "bf16", tuple((k * 7 // 3 + k // 5) % 2 for k in range(200)))
 
 
-@pytest.mark.parametrize("limit", ["1", "100"])
-def test_pass_counters_start_over(limit, monkeypatch):
-    """The one-launch pass's run counters start over (a fill kernel clears
-    them) before they would leave 31 bits.  With the limit lowered for the
-    group, that happens before every run (limit 1) or every few runs (100),
-    and every run still equals the staged run of its own inputs bit for
-    bit."""
-    monkeypatch.setenv("LB_PASS_EPOCH_LIMIT", limit)
-    say("pass counter reset, limit", limit)
-    _runs_match_staged("c5", 1, "bf16", (0, 1, 1, 0, 1, 0, 0, 1, 1))
-
-
 # (d_in, d_out, r_p, P) per linear.  "mixed": ranks from 16 to 2000, some
 # under 4 latent tiles of 64 (stage 1 splits K-groups among its waves);
 # "wide": every rank at least 4 tiles (4 to 23), none a multiple of 64
@@ -266,6 +259,38 @@ def test_pass_ragged_mixed_group(T, out, kind):
     for i, inp in enumerate(inps):
         xf = synth.bf16_bits_to_f32(xs[i]) if xs[i].dtype == np.uint16 else xs[i]
         ref = oracle.linear_forward(xf, inp.U, inp.V, inp.h, inp.g, inp.l)
-        err = oracle.rel_l2(y_to_np(items[i][1]), ref)
-        assert err <= TOL[out], (i, err)
+        assert_close(y_to_np(items[i][1]), ref, TOL[out], ("ragged group", kind, T, i))
+    g.release()
+
+
+@pytest.mark.parametrize("T,kind", [(1, "mixed"), (2, "mixed"), (4, "mixed"), (1, "wide"), (2, "wide"),
+                                    (6, "wide")])
+def test_group_two_limb_exact_regime(T, kind):
+    """Decode groups with bf16 outputs (two fp8 limbs) in the regime where two
+    limbs are exact (integer g x with |g x| <= 4, integer |t| <= 128): every
+    output of the one-launch pass (T <= 2) and of the three-launch form (T >= 4)
+    equals the oracle rounded to bf16, bit for bit."""
+    torch = torch_or_skip()
+    import binarized_rank_linear_amd as lb
+    from test_gpu_linear import _integer_layer, _sparse_x
+    say("group exact two-limb T", T, kind)
+    items, refs = [], []
+    for i, (d_in, d_out, r_p, P) in enumerate(RAGGED[kind]):
+        inp = _integer_layer(800 + i, d_in, d_out, r_p, P)
+        x = _sparse_x(900 + i + T, T, d_in)
+        refs.append(synth.f32_to_bf16_bits(oracle.linear_forward(x, inp.U, inp.V, inp.h, inp.g, inp.l)
+                                           .astype(np.float32)))
+        y = torch.empty((T, d_out), dtype=torch.bfloat16, device="cuda")
+        items.append((x_to_dev(synth.f32_to_bf16_bits(x)), y, dev_layer(inp)))
+    g = lb.Group(items, T, torch.bfloat16, torch.bfloat16)
+    for _ in range(2):
+        for it in items:
+            it[1].fill_(float("nan"))
+        g.run()
+        torch.cuda.synchronize()
+        for i, it in enumerate(items):
+            y = it[1].cpu().view(torch.int16).numpy().view(np.uint16)
+            bad = np.argwhere(y != refs[i])
+            assert bad.size == 0, (i, bad[:4])
+    assert lb.device_faults() == 0
     g.release()

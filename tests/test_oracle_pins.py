@@ -364,3 +364,12 @@ def test_mlp_matches_composed_linears():
     a = zg / (1.0 + np.exp(-zg)) * zu
     yd = oracle.dense_forward(a, down.U, down.V, down.h, down.g, down.l)
     assert oracle.rel_l2(y, yd) < 1e-12
+
+
+def test_rel_l2_hand_values():
+    """The parity checker itself: ||got - ref|| / ||ref|| on hand-computed
+    cases (3-4-5 and 1-2-2-3 triangles), and the absolute norm when ref is 0."""
+    assert oracle.rel_l2([3.3, 4.4], [3.0, 4.0]) == pytest.approx(0.1, abs=1e-15)
+    assert oracle.rel_l2([[1.0, 2.0], [2.0, 0.3]], [[1.0, 2.0], [2.0, 0.0]]) == pytest.approx(0.1, abs=1e-15)
+    assert oracle.rel_l2([1.0, -2.0, 2.0], [0.0, 0.0, 0.0]) == pytest.approx(3.0, abs=1e-15)
+    assert oracle.rel_l2([5.0, 6.0], [5.0, 6.0]) == 0.0
