@@ -8,6 +8,9 @@
 //
 //   stage 1: part[z][n][p*r_p + k] = sum_{i in chunk z} sign(V_p[i][k]) g_p[i] x[n][i]
 //   stage 2: y[n][j] = sum_p h_p[j] sum_k sign(U_p[j][k]) (l_p[k] sum_z part[z][n][p*r_p+k])
+// for the tokens n of one launch pair (at most 32); the pairs run one after
+// the other on the stream and reuse part, so the workspace does not grow
+// with the token count.
 //
 // One thread per latent row (stage 1) or output row (stage 2); the packed
 // word planes make the 64 lanes of a wave read 256 consecutive bytes.
@@ -81,7 +84,7 @@ __global__ __launch_bounds__(kBlock) void k_s1_valu(Linear a, int64_t n0, int nt
     if (k < a.r_p) {
         const int64_t R = a.P * a.r_p;
         for (int n = 0; n < ntok; ++n)
-            part[((int64_t)blockIdx.z * a.T + n0 + n) * R + p * a.r_p + k] = acc[n];
+            part[((int64_t)blockIdx.z * NT + n) * R + p * a.r_p + k] = acc[n];
     }
 }
 
@@ -109,7 +112,7 @@ __global__ __launch_bounds__(kBlock) void k_s2_valu(Linear a, int64_t n0, int nt
                 if (n < ntok && kx < a.r_p) {
                     float s = 0.0f;
                     for (int z = 0; z < nsplit; ++z)
-                        s += part[((int64_t)z * a.T + n0 + n) * R + p * a.r_p + kx];
+                        s += part[((int64_t)z * NT + n) * R + p * a.r_p + kx];
                     v = f16_to_f32(a.l[p * a.r_p + kx]) * s;
                 }
                 st[n][kk] = v;
@@ -155,7 +158,7 @@ int run_valu(const Linear &a, const ValuPlan &pl, float *part, hipStream_t s) {
 
 size_t valu_workspace_bytes(const Linear &a) {
     const ValuPlan pl = plan_valu(a);
-    return (size_t)pl.nsplit * (size_t)a.T * (size_t)(a.P * a.r_p) * sizeof(float);
+    return (size_t)pl.nsplit * (size_t)pl.nt * (size_t)(a.P * a.r_p) * sizeof(float);
 }
 
 int valu_forward(const Linear &a, void *ws, hipStream_t s) {
