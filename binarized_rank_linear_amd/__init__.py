@@ -126,6 +126,10 @@ def lib() -> ctypes.CDLL:
         L.lb_linear_path.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_uint]
         L.lb_linear_path.restype = ctypes.c_int
+        L.lb_linear_forward_noalloc.argtypes = [_vp, ctypes.c_int, _vp, ctypes.c_int,
+                                                ctypes.POINTER(lb_factors), _i64, _i64, _i64, _i64,
+                                                ctypes.c_int, ctypes.c_uint, _vp]
+        L.lb_linear_forward_noalloc.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -297,6 +301,30 @@ def linear_forward(x, layer: PackedLinear, out_dtype=None, flags: int = LB_PATH_
                                    _dtype_code(out.dtype), ctypes.byref(f), layer.d_in,
                                    layer.d_out, layer.r, T, int(layer.residual), ws.data_ptr(),
                                    ws.numel(), flags, _stream_ptr(stream)), "lb_linear_forward")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def linear_forward_noalloc(x, layer: PackedLinear, out_dtype=None, flags: int = LB_PATH_AUTO,
+                           out=None, stream=None):
+    """lb_linear_forward_noalloc: the library's own fixed workspace (no
+    allocation by the library; `out` may be passed to avoid torch's)."""
+    torch = _torch()
+    _dev_check(x)
+    T, d_in = x.shape
+    if d_in != layer.d_in:
+        raise ValueError("x has %d features, layer expects %d" % (d_in, layer.d_in))
+    out_dtype = out_dtype or x.dtype
+    if out is None:
+        out = torch.empty((T, layer.d_out), dtype=out_dtype, device=x.device)
+    _dev_check(out)
+    f = layer.struct()
+    _check(lib().lb_linear_forward_noalloc(x.data_ptr(), _dtype_code(x.dtype), out.data_ptr(),
+                                           _dtype_code(out.dtype), ctypes.byref(f), layer.d_in,
+                                           layer.d_out, layer.r, T, int(layer.residual), flags,
+                                           _stream_ptr(stream)), "lb_linear_forward_noalloc")
     return out
 
 

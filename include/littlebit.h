@@ -191,6 +191,23 @@ int lb_linear_forward(const void *x, int x_dtype, void *y, int y_dtype,
                       int64_t T, int residual, void *ws, size_t ws_bytes,
                       unsigned flags, void *stream);
 
+/* For callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid allocation): lb_linear_forward
+ * with the library's own workspace, a fixed device array of
+ * LB_NOALLOC_SCRATCH_BYTES per GPU (allocated with the code object, held
+ * until the process ends).  Allocates nothing.  Same arguments, results and
+ * errors as lb_linear_forward, except that a request whose kernels need more
+ * workspace than the array holds returns LB_EWORKSPACE (every configuration
+ * linear fits at T <= 32 on the decode kernels; compare
+ * lb_linear_workspace_bytes with LB_NOALLOC_SCRATCH_BYTES).  Every call on a
+ * GPU shares that GPU's array: calls that overlap on one GPU (on different
+ * streams, or from different threads without ordering) race.  The array keeps
+ * the last call's contents; the kernels need none. */
+#define LB_NOALLOC_SCRATCH_BYTES (32u << 20)
+int lb_linear_forward_noalloc(const void *x, int x_dtype, void *y, int y_dtype,
+                              const lb_factors *w, int64_t d_in, int64_t d_out, int64_t r,
+                              int64_t T, int residual, unsigned flags, void *stream);
+
 /* Workspace bytes lb_mlp_forward needs.  0 on bad arguments. */
 size_t lb_mlp_workspace_bytes(int64_t d_model, int64_t d_ff, int64_t r_gu, int64_t r_down,
                               int64_t T, int residual, unsigned flags);
