@@ -66,6 +66,12 @@ def lib():
                                                  _fp, _fp, _dp, _dp, _dp, _i64p, _i64, _dp,
                                                  ctypes.c_int]
         L.oracle_linear_forward_rows.restype = None
+        L.oracle_linear_latents.argtypes = [_dp, _i64, _i64, _i64, ctypes.c_int, _fp, _dp, _dp, _dp,
+                                            ctypes.c_int]
+        L.oracle_linear_latents.restype = None
+        L.oracle_linear_from_latents.argtypes = [_dp, _i64, _i64, _i64, ctypes.c_int, _fp, _dp, _dp,
+                                                 ctypes.c_int]
+        L.oracle_linear_from_latents.restype = None
         L.oracle_mlp_forward.argtypes = ([_dp, _i64, _i64, _i64, ctypes.c_int, _i64, _i64]
                                          + [_fp, _fp, _dp, _dp, _dp] * 3 + [_dp, ctypes.c_int])
         L.oracle_mlp_forward.restype = None
@@ -174,6 +180,34 @@ def linear_forward_rows(x: np.ndarray, U, V, h, g, l, rows: Sequence[int],
                                      _ptr(U, _fp), _ptr(V, _fp), _ptr(hd, _dp), _ptr(gd, _dp),
                                      _ptr(ldd, _dp), _ptr(idx, _i64p), len(idx), _ptr(y, _dp),
                                      nthreads)
+    return y
+
+
+def linear_latents(x: np.ndarray, V: np.ndarray, g, l, nthreads: int = 0) -> np.ndarray:
+    """The rank-r intermediate t [T][P*r_p] (path p in columns p*r_p..):
+    t = l_p * (sign(V_p)^T (g_p * x)) per path (C)."""
+    xd = widen_x(x)
+    T, d_in = xd.shape
+    P, _, r_p = V.shape
+    V = np.ascontiguousarray(V, dtype=np.float32)
+    gd, ldd = _scale64(g), _scale64(l)
+    t = np.empty((T, P * r_p), np.float64)
+    lib().oracle_linear_latents(_ptr(xd, _dp), T, d_in, r_p, P, _ptr(V, _fp), _ptr(gd, _dp),
+                                _ptr(ldd, _dp), _ptr(t, _dp), nthreads)
+    return t
+
+
+def linear_from_latents(t: np.ndarray, U: np.ndarray, h, nthreads: int = 0) -> np.ndarray:
+    """y [T][d_out] = sum_p h_p * (sign(U_p) t_p) from latents t [T][P*r_p] (C)."""
+    td = np.ascontiguousarray(t, dtype=np.float64)
+    P, d_out, r_p = U.shape
+    T = td.shape[0]
+    assert td.shape == (T, P * r_p)
+    U = np.ascontiguousarray(U, dtype=np.float32)
+    hd = _scale64(h)
+    y = np.empty((T, d_out), np.float64)
+    lib().oracle_linear_from_latents(_ptr(td, _dp), T, d_out, r_p, P, _ptr(U, _fp), _ptr(hd, _dp),
+                                     _ptr(y, _dp), nthreads)
     return y
 
 

@@ -48,9 +48,9 @@
  * vectors are not counted).  One path of rank r stores r*(d_in + d_out) sign
  * bits against d_in*d_out weights, so the largest r within b bits per weight is
  * floor(b*d_in*d_out/(d_in+d_out)) (sesamedisk, "How low-rank binarization
- * works": the rank sets the bit budget).  The residual path shares the same
- * budget (same page: "without raising the total bit budget"), so the two
- * paths split r.  Exact integer arithmetic: b = b_num / b_den.
+ * works": the rank sets the bit budget).  The residual path fits inside the
+ * same budget (same page and section), so the two paths split r.  Exact
+ * integer arithmetic: b = b_num / b_den.
  * Returns 0 on success, -1 if the rank rounds to zero or inputs are bad. */
 int oracle_rank_for_budget(int64_t d_in, int64_t d_out, int64_t b_num, int64_t b_den,
                            int residual, int64_t *r_total, int64_t *r_path)
@@ -207,6 +207,54 @@ void oracle_linear_forward_rows(const double *x, int64_t T, int64_t d_in, int64_
         }
     }
     free(t);
+}
+
+/* The two halves of the layer around the rank-r intermediate, which the
+ * sesamedisk page ("The real result") names as what a k/v projection can
+ * cache instead of its d_out-wide output.
+ * Latents: t [T][P*r_p], path p in columns p*r_p .. p*r_p + r_p - 1,
+ *   t[n][p*r_p + k] = l_p[k] * sum_i sign(V_p[i][k]) * (g_p[i] * x[n][i]),
+ * the same loop as the first half of path_forward. */
+void oracle_linear_latents(const double *x, int64_t T, int64_t d_in, int64_t r_p, int P,
+                           const float *V, const double *g, const double *l, double *t, int nthreads)
+{
+    set_threads(nthreads);
+    int64_t R = (int64_t)P * r_p;
+    for (int p = 0; p < P; ++p) {
+        const float *Vp = V + (size_t)p * d_in * r_p;
+        const double *gp = g + (size_t)p * d_in, *lp = l + (size_t)p * r_p;
+        #pragma omp parallel for schedule(static)
+        for (int64_t nk = 0; nk < T * r_p; ++nk) {
+            int64_t n = nk / r_p, k = nk % r_p;
+            double u = 0.0;
+            for (int64_t i = 0; i < d_in; ++i)
+                u += sgn(Vp[i * r_p + k]) * (gp[i] * x[n * d_in + i]);
+            t[n * R + (int64_t)p * r_p + k] = lp[k] * u;
+        }
+    }
+}
+
+/* Output from given latents t [T][P*r_p] (layout as above):
+ *   y[n][j] = sum_p h_p[j] * sum_k sign(U_p[j][k]) * t[n][p*r_p + k],
+ * the paths added in order, as path_forward adds them. */
+void oracle_linear_from_latents(const double *t, int64_t T, int64_t d_out, int64_t r_p, int P,
+                                const float *U, const double *h, double *y, int nthreads)
+{
+    set_threads(nthreads);
+    int64_t R = (int64_t)P * r_p;
+    memset(y, 0, sizeof(double) * (size_t)(T * d_out));
+    for (int p = 0; p < P; ++p) {
+        const float *Up = U + (size_t)p * d_out * r_p;
+        const double *hp = h + (size_t)p * d_out;
+        #pragma omp parallel for schedule(static)
+        for (int64_t nj = 0; nj < T * d_out; ++nj) {
+            int64_t n = nj / d_out, j = nj % d_out;
+            double z = 0.0;
+            for (int64_t k = 0; k < r_p; ++k)
+                z += sgn(Up[j * r_p + k]) * t[n * R + (int64_t)p * r_p + k];
+            y[n * d_out + j] += hp[j] * z;
+        }
+    }
 }
 
 /* ------------------------------------------------------------------------ */

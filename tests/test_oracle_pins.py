@@ -373,3 +373,30 @@ def test_rel_l2_hand_values():
     assert oracle.rel_l2([[1.0, 2.0], [2.0, 0.3]], [[1.0, 2.0], [2.0, 0.0]]) == pytest.approx(0.1, abs=1e-15)
     assert oracle.rel_l2([1.0, -2.0, 2.0], [0.0, 0.0, 0.0]) == pytest.approx(3.0, abs=1e-15)
     assert oracle.rel_l2([5.0, 6.0], [5.0, 6.0]) == 0.0
+
+
+def test_latents_against_dense_and_composition():
+    """The two halves around the rank-r intermediate (the latent a k/v cache
+    would hold; sesamedisk, "The real result"): t against the plain matrix
+    product diag(l) S_V^T diag(g) x per path (numpy), and stage 2 of the
+    oracle's t equal to the whole forward bit for bit (the same fp64
+    operations in the same order)."""
+    inp = synth.layer_inputs(5, 70, 45, 24, 2)
+    x = synth.activations(6, 3, 70, "f32")
+    t = oracle.linear_latents(x, inp.V, inp.g, inp.l)
+    xd = oracle.widen_x(x)
+    for p in range(2):
+        SV = np.where(inp.V[p] < 0, -1.0, 1.0)
+        want = (oracle.widen_f16(inp.l[p])[None, :] * ((xd * oracle.widen_f16(inp.g[p])[None, :]) @ SV))
+        assert np.allclose(t[:, p * 24:(p + 1) * 24], want, rtol=1e-13, atol=1e-13)
+    y = oracle.linear_from_latents(t, inp.U, inp.h)
+    assert np.array_equal(y, oracle.linear_forward(x, inp.U, inp.V, inp.h, inp.g, inp.l))
+
+
+def test_latent_cache_ratio_pin():
+    """A k projection of Llama2-7B's shape (4096 -> 4096) at 0.1 bits per weight
+    has rank 192: a latent per token instead of the 4096-wide output is the
+    pages' 21.3x smaller cache (sesamedisk, "The real result")."""
+    r, rp = oracle.rank_for_budget(4096, 4096, 1, 10, True)
+    assert r == 192 and rp == 96
+    assert round(4096 / r, 1) == 21.3
