@@ -130,6 +130,13 @@ def lib() -> ctypes.CDLL:
                                                 ctypes.POINTER(lb_factors), _i64, _i64, _i64, _i64,
                                                 ctypes.c_int, ctypes.c_uint, _vp]
         L.lb_linear_forward_noalloc.restype = ctypes.c_int
+        L.lb_linear_stage1.argtypes = [_vp, ctypes.c_int, _vp, ctypes.c_int, ctypes.c_int,
+                                       ctypes.POINTER(lb_factors), _i64, _i64, _i64, _i64, ctypes.c_int,
+                                       _vp, _sz, ctypes.c_uint, _vp]
+        L.lb_linear_stage1.restype = ctypes.c_int
+        L.lb_linear_stage2.argtypes = [_vp, ctypes.c_int, _vp, ctypes.c_int, ctypes.POINTER(lb_factors),
+                                       _i64, _i64, _i64, _i64, ctypes.c_int, _vp, _sz, ctypes.c_uint, _vp]
+        L.lb_linear_stage2.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -325,6 +332,52 @@ def linear_forward_noalloc(x, layer: PackedLinear, out_dtype=None, flags: int = 
                                            _dtype_code(out.dtype), ctypes.byref(f), layer.d_in,
                                            layer.d_out, layer.r, T, int(layer.residual), flags,
                                            _stream_ptr(stream)), "lb_linear_forward_noalloc")
+    return out
+
+
+def linear_stage1(x, layer: PackedLinear, t_dtype=None, out_dtype=None, flags: int = LB_PATH_AUTO,
+                  ws=None, out=None, stream=None):
+    """The latents t [T][r] = l (.) sign(V)^T (g (.) x) per path (lb_linear_stage1).
+    out_dtype: the dtype of the layer's output, which selects the kernels."""
+    torch = _torch()
+    _dev_check(x)
+    T, d_in = x.shape
+    if d_in != layer.d_in:
+        raise ValueError("x has %d features, layer expects %d" % (d_in, layer.d_in))
+    t_dtype = t_dtype or torch.float32
+    out_dtype = out_dtype or x.dtype
+    if out is None:
+        out = torch.empty((T, layer.r), dtype=t_dtype, device=x.device)
+    _dev_check(out)
+    need = linear_workspace_bytes(layer, T, flags)
+    if ws is None or ws.numel() < need:
+        ws = workspace(need, x.device)
+    f = layer.struct()
+    _check(lib().lb_linear_stage1(x.data_ptr(), _dtype_code(x.dtype), out.data_ptr(), _dtype_code(out.dtype),
+                                  _dtype_code(out_dtype), ctypes.byref(f), layer.d_in, layer.d_out, layer.r, T,
+                                  int(layer.residual), ws.data_ptr(), ws.numel(), flags, _stream_ptr(stream)),
+           "lb_linear_stage1")
+    return out
+
+
+def linear_stage2(t, layer: PackedLinear, out_dtype, flags: int = LB_PATH_AUTO, ws=None, out=None,
+                  stream=None):
+    """y [T][d_out] from the latents t [T][r] (lb_linear_stage2)."""
+    torch = _torch()
+    _dev_check(t)
+    T, r = t.shape
+    if r != layer.r:
+        raise ValueError("t has %d latents, layer has %d" % (r, layer.r))
+    if out is None:
+        out = torch.empty((T, layer.d_out), dtype=out_dtype, device=t.device)
+    _dev_check(out)
+    need = linear_workspace_bytes(layer, T, flags)
+    if ws is None or ws.numel() < need:
+        ws = workspace(need, t.device)
+    f = layer.struct()
+    _check(lib().lb_linear_stage2(t.data_ptr(), _dtype_code(t.dtype), out.data_ptr(), _dtype_code(out.dtype),
+                                  ctypes.byref(f), layer.d_in, layer.d_out, layer.r, T, int(layer.residual),
+                                  ws.data_ptr(), ws.numel(), flags, _stream_ptr(stream)), "lb_linear_stage2")
     return out
 
 

@@ -239,6 +239,79 @@ int lb_linear_forward(const void *x, int x_dtype, void *y, int y_dtype, const lb
     return run_path(p, a, ws, (hipStream_t)stream);
 }
 
+// ---- the latent API ----------------------------------------------------------
+
+namespace {
+int run_stage(Path p, const Linear &a, void *ws, int stage, void *t, int t_dtype, hipStream_t s) {
+    switch (p) {
+        case Path::Valu: return valu_stage_forward(a, ws, stage, t, t_dtype, s);
+        case Path::MfmaDecode: return mfma_decode_stage(a, ws, stage, t, t_dtype, s);
+        case Path::Gemm: return gemm_stage_forward(a, ws, stage, t, t_dtype, s);
+    }
+    return LB_EINVAL;
+}
+
+// Checks shared by both halves: sizes, factors, the latents buffer, the
+// workspace and the path.  act/act_bytes: the activation (x or y) the half
+// reads or writes besides t.
+int stage_common(const lb_factors *w, int64_t d_in, int64_t d_out, int64_t r, int64_t T, int residual,
+                 const void *t, int t_dtype, const void *act, size_t act_bytes, int y_dtype, void *ws,
+                 size_t ws_bytes, unsigned flags, Linear *a, Path *p) {
+    int rc;
+    if ((rc = check_shape(d_in, d_out, r, T, residual, a))) return rc;
+    if ((rc = check_factors(w, a))) return rc;
+    if (!valid_dtype(t_dtype) || !valid_dtype(y_dtype) || (flags & ~kLinearFlags)) return LB_EINVAL;
+    if (T > 0 && (!t || !act)) return LB_EINVAL;
+    if (!aligned(t, act_size(t_dtype))) return LB_EALIGN;
+    const size_t t_bytes = (size_t)(T * r) * act_size(t_dtype);
+    if (overlap(t, t_bytes, act, act_bytes)) return LB_EINVAL;
+    a->y_dtype = y_dtype;
+    if ((rc = choose_path(flags, T, y_dtype, p, a))) return rc;
+    if (T == 0) return LB_OK;
+    const size_t need = path_workspace(*p, *a);
+    if (need > 0) {
+        if (!ws || ws_bytes < need) return LB_EWORKSPACE;
+        if (!aligned(ws, 256)) return LB_EALIGN;
+        if (overlap(ws, need, t, t_bytes) || overlap(ws, need, act, act_bytes)) return LB_EINVAL;
+    }
+    return LB_OK;
+}
+}  // namespace
+
+int lb_linear_stage1(const void *x, int x_dtype, void *t, int t_dtype, int y_dtype, const lb_factors *w,
+                     int64_t d_in, int64_t d_out, int64_t r, int64_t T, int residual, void *ws, size_t ws_bytes,
+                     unsigned flags, void *stream) {
+    Linear a{};
+    Path p;
+    if (!valid_dtype(x_dtype)) return LB_EINVAL;
+    if (!aligned(x, act_size(x_dtype))) return LB_EALIGN;
+    const size_t x_bytes = (size_t)(T > 0 ? T * d_in : 0) * act_size(x_dtype);
+    if (int rc = stage_common(w, d_in, d_out, r, T, residual, t, t_dtype, x, x_bytes, y_dtype, ws, ws_bytes,
+                              flags, &a, &p))
+        return rc;
+    if (T == 0) return LB_OK;
+    a.x = x;
+    a.x_dtype = x_dtype;
+    return run_stage(p, a, ws, 1, t, t_dtype, (hipStream_t)stream);
+}
+
+int lb_linear_stage2(const void *t, int t_dtype, void *y, int y_dtype, const lb_factors *w, int64_t d_in,
+                     int64_t d_out, int64_t r, int64_t T, int residual, void *ws, size_t ws_bytes, unsigned flags,
+                     void *stream) {
+    Linear a{};
+    Path p;
+    if (!valid_dtype(y_dtype)) return LB_EINVAL;
+    if (!aligned(y, act_size(y_dtype))) return LB_EALIGN;
+    const size_t y_bytes = (size_t)(T > 0 ? T * d_out : 0) * act_size(y_dtype);
+    if (int rc = stage_common(w, d_in, d_out, r, T, residual, t, t_dtype, y, y_bytes, y_dtype, ws, ws_bytes,
+                              flags, &a, &p))
+        return rc;
+    if (T == 0) return LB_OK;
+    a.y = y;
+    a.x_dtype = LB_BF16;
+    return run_stage(p, a, ws, 2, const_cast<void *>(t), t_dtype, (hipStream_t)stream);
+}
+
 // ---- SwiGLU block ----------------------------------------------------------
 
 static size_t mlp_linear_ws(int64_t d_model, int64_t d_ff, int64_t r_gu, int64_t r_down, int64_t T,

@@ -146,6 +146,12 @@ struct MRun {
     // (null for a single linear, which keeps nothing in its workspace)
     const uint64_t *stamp;
     uint64_t tag;
+    // the latent API (single linears): k_latent also writes the latents t
+    // [T][P*r_p] (t_mode 1), or takes them from t instead of the partial sums
+    // (t_mode 2); t_dtype LB_F32 or LB_BF16
+    void *t_io;
+    int t_dtype;
+    int t_mode;
 };
 
 // Compact operands -> LDS operand layout.  Each operand holds R records of
@@ -908,7 +914,7 @@ __device__ __forceinline__ void latent_item(const MRun &run, const MLin &L, int 
         float sum[kLU];
 #pragma unroll
         for (int q = 0; q < kLU; ++q) sum[q] = 0.0f;
-        for (int sl = 0; sl < ns; ++sl) {                         // uniform
+        for (int sl = 0; sl < (run.t_mode == 2 ? 0 : ns); ++sl) {   // uniform
             float a[kLU][kLC];
 #pragma unroll
             for (int q = 0; q < kLU; ++q)
@@ -936,7 +942,20 @@ __device__ __forceinline__ void latent_item(const MRun &run, const MLin &L, int 
             const int pl = kg_first * 4 + blk;
             const int p = pl / L.kw_u;
             const int k = (pl - p * L.kw_u) * 32 + (lane & 31);
-            const float v = live[q] ? f16_to_f32(L.l[(int64_t)p * L.r_p + k]) * sum[q] : 0.0f;
+            float v;
+            if (run.t_mode == 2) {                                // latents given (uniform)
+                const int64_t ti = (int64_t)n * Rtot + (int64_t)p * L.r_p + k;
+                v = !live[q] ? 0.0f
+                    : run.t_dtype == LB_F32 ? ((const float *)run.t_io)[ti]
+                                            : bf16_to_f32(((const uint16_t *)run.t_io)[ti]);
+            } else {
+                v = live[q] ? f16_to_f32(L.l[(int64_t)p * L.r_p + k]) * sum[q] : 0.0f;
+                if (run.t_mode == 1 && live[q]) {                 // latents out, as computed
+                    const int64_t ti = (int64_t)n * Rtot + (int64_t)p * L.r_p + k;
+                    if (run.t_dtype == LB_F32) ((float *)run.t_io)[ti] = v;
+                    else ((uint16_t *)run.t_io)[ti] = f32_to_bf16(v);
+                }
+            }
             const int row = (n % R::TPM2) * R::S2 + (p < L.P ? p : 0) * NL;
             uint8_t *op = smem + ((e >> 7) * NB2 + n / R::TPM2) * opb + row * kRec;
             emit_limbs<NL>(v, op + rec_offset(e & 127), op + 128 + ((e & 127) >> 5), ok && p < L.P,
@@ -1657,7 +1676,8 @@ struct Lds {
     size_t prep, s1, lat, s2;
 };
 
-// stage_mask: bit 0 = prep, stage 1 and the latent pass; bit 1 = stage 2.
+// stage_mask: bit 0 = prep, stage 1 and the latent pass; bit 1 = stage 2;
+// bit 2 = the latent pass alone (from given latents).
 template <int NL, int NB1, int NB2>
 int launch_all(const MRun &run, const MLin &single, const Lds &lds, hipStream_t st, int stage_mask) {
     // launches with no items (a chunk of a group may have none of a kind) are skipped
@@ -1676,7 +1696,7 @@ int launch_all(const MRun &run, const MLin &single, const Lds &lds, hipStream_t 
             if (int rc = last_launch_status()) return rc;
         }
     }
-    if ((stage_mask & 1) && run.itemsF > 0) {
+    if ((stage_mask & 5) && run.itemsF > 0) {
         k_latent<NL, NB2><<<(unsigned)run.itemsF, kThreads, lds.lat, st>>>(run, single);
         if (int rc = last_launch_status()) return rc;
     }
@@ -1782,31 +1802,55 @@ size_t mfma_decode_workspace_bytes(const Linear &a) {
     return need;
 }
 
+namespace {
+// A single linear's launch state on the decode kernels.
+int single_setup(const Linear &a, void *ws, Shape *s, MLin *m, MRun *run, Lds *lds) {
+    if (!shape_for(a.T, a.y_dtype, s)) return LB_EUNSUPPORTED;
+    Grain gr;
+    gr.tsplit = fused1(*s) && tsplit_for(&a, 1) ? 1 : 0;
+    plan_linear(a, *s, false, m, gr);
+    bind_ws(m, a, *s, (uint8_t *)ws);
+    *run = MRun{};
+    run->T = (int)a.T;
+    run->x_dtype = a.x_dtype;
+    run->y_dtype = a.y_dtype;
+    run->dma2 = dma2_for(*s, a.T, m->kgs);
+    run->ystage = ystage_for(a.T, a.y_dtype);
+    run->ops2 = run->dma2 ? m->kgs : ops2_for(*s, m->kgs);
+    run->items0 = items0_of(*m);
+    run->items1 = items1_of(*m);
+    run->itemsF = itemsF_of(*m);
+    run->items2 = m->n2;
+    run->table = nullptr;
+    *lds = Lds{};
+    run->tsplit = gr.tsplit;
+    run->flush1 = (int)imin(flush1_for(a.T, run->tsplit), cdiv(m->r_p, kTile));
+    lds_add(lds, *m, *s, run->ops2, a.T, run->flush1, run->tsplit);
+    return LB_OK;
+}
+}  // namespace
+
 int mfma_decode_forward(const Linear &a, void *ws, hipStream_t st) {
     Shape s;
-    if (!shape_for(a.T, a.y_dtype, &s)) return LB_EUNSUPPORTED;
     MLin m;
-    Grain gr;
-    gr.tsplit = fused1(s) && tsplit_for(&a, 1) ? 1 : 0;
-    plan_linear(a, s, false, &m, gr);
-    bind_ws(&m, a, s, (uint8_t *)ws);
-    MRun run{};
-    run.T = (int)a.T;
-    run.x_dtype = a.x_dtype;
-    run.y_dtype = a.y_dtype;
-    run.dma2 = dma2_for(s, a.T, m.kgs);
-    run.ystage = ystage_for(a.T, a.y_dtype);
-    run.ops2 = run.dma2 ? m.kgs : ops2_for(s, m.kgs);
-    run.items0 = items0_of(m);
-    run.items1 = items1_of(m);
-    run.itemsF = itemsF_of(m);
-    run.items2 = m.n2;
-    run.table = nullptr;
-    Lds lds{};
-    run.tsplit = gr.tsplit;
-    run.flush1 = (int)imin(flush1_for(a.T, run.tsplit), cdiv(m.r_p, kTile));
-    lds_add(&lds, m, s, run.ops2, a.T, run.flush1, run.tsplit);
+    MRun run;
+    Lds lds;
+    if (int rc = single_setup(a, ws, &s, &m, &run, &lds)) return rc;
     return launch_shape(s, run, m, lds, st);
+}
+
+int mfma_decode_stage(const Linear &a, void *ws, int stage, void *t, int t_dtype, hipStream_t st) {
+    Shape s;
+    MLin m;
+    MRun run;
+    Lds lds;
+    if (int rc = single_setup(a, ws, &s, &m, &run, &lds)) return rc;
+    run.t_io = t;
+    run.t_dtype = t_dtype;
+    run.t_mode = stage == 1 ? 1 : 2;
+    // stage 1: activation operands, first contractions, latents (also to t);
+    // stage 2: the latent step from t, second contractions
+    return launch_shape(s, run, m, lds, st, stage == 1 ? 1 : 6);
 }
 
 // ---- groups ------------------------------------------------------------------

@@ -88,9 +88,32 @@ __global__ __launch_bounds__(kBlock) void k_s1_valu(Linear a, int64_t n0, int nt
     }
 }
 
+// The latents of one launch pair's tokens, t [T][P*r_p] (t_dtype), summed as
+// k_s2_valu sums them: l * (sum of the pieces in order).  One thread per
+// (token, latent).
+template <int NT>
+__global__ __launch_bounds__(kBlock) void k_t_valu(Linear a, int64_t n0, int ntok, int nsplit,
+                                                   const float *__restrict__ part, void *t, int t_dtype) {
+    const int64_t R = a.P * a.r_p;
+    const int64_t e = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (e >= ntok * R) return;
+    const int n = (int)(e / R);
+    const int64_t pk = e - n * R;
+    const int p = (int)(pk / a.r_p);
+    const int64_t kx = pk - (int64_t)p * a.r_p;
+    float s = 0.0f;
+    for (int z = 0; z < nsplit; ++z) s += part[((int64_t)z * NT + n) * R + pk];
+    const float v = f16_to_f32(a.l[p * a.r_p + kx]) * s;
+    const int64_t o = (n0 + n) * R + pk;
+    if (t_dtype == LB_F32) ((float *)t)[o] = v;
+    else ((uint16_t *)t)[o] = f32_to_bf16(v);
+}
+
+// t_in (null: the latents come from part): the latents t [T][P*r_p] given.
 template <int NT>
 __global__ __launch_bounds__(kBlock) void k_s2_valu(Linear a, int64_t n0, int ntok, int nsplit,
-                                                    const float *__restrict__ part) {
+                                                    const float *__restrict__ part, const void *t_in,
+                                                    int t_dtype) {
     __shared__ float st[NT][kSpan];
     const int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x;
     const int64_t R = a.P * a.r_p;
@@ -110,10 +133,16 @@ __global__ __launch_bounds__(kBlock) void k_s2_valu(Linear a, int64_t n0, int nt
                 const int64_t kx = k0 + kk;
                 float v = 0.0f;
                 if (n < ntok && kx < a.r_p) {
-                    float s = 0.0f;
-                    for (int z = 0; z < nsplit; ++z)
-                        s += part[((int64_t)z * NT + n) * R + p * a.r_p + kx];
-                    v = f16_to_f32(a.l[p * a.r_p + kx]) * s;
+                    if (t_in) {
+                        const int64_t o = (n0 + n) * R + p * a.r_p + kx;
+                        v = t_dtype == LB_F32 ? ((const float *)t_in)[o]
+                                              : bf16_to_f32(((const uint16_t *)t_in)[o]);
+                    } else {
+                        float s = 0.0f;
+                        for (int z = 0; z < nsplit; ++z)
+                            s += part[((int64_t)z * NT + n) * R + p * a.r_p + kx];
+                        v = f16_to_f32(a.l[p * a.r_p + kx]) * s;
+                    }
                 }
                 st[n][kk] = v;
             }
@@ -140,16 +169,27 @@ __global__ __launch_bounds__(kBlock) void k_s2_valu(Linear a, int64_t n0, int nt
         for (int n = 0; n < ntok; ++n) store_act(a.y, a.y_dtype, (n0 + n) * a.d_out + j, yacc[n]);
 }
 
+// stage: 3 = the whole layer; 1 = the latents to t; 2 = the output from t.
 template <int NT>
-int run_valu(const Linear &a, const ValuPlan &pl, float *part, hipStream_t s) {
+int run_valu(const Linear &a, const ValuPlan &pl, float *part, hipStream_t s, int stage = 3,
+             void *t = nullptr, int t_dtype = LB_F32) {
     for (int64_t n0 = 0; n0 < a.T; n0 += NT) {
         const int ntok = (int)imin(NT, a.T - n0);
-        dim3 g1((unsigned)cdiv(a.r_p, kBlock), (unsigned)a.P, (unsigned)pl.nsplit);
-        k_s1_valu<NT><<<g1, kBlock, 0, s>>>(a, n0, ntok, pl.kchunk, part);
-        if (int rc = last_launch_status()) return rc;
-        dim3 g2((unsigned)cdiv(a.d_out, kBlock));
-        k_s2_valu<NT><<<g2, kBlock, 0, s>>>(a, n0, ntok, pl.nsplit, part);
-        if (int rc = last_launch_status()) return rc;
+        if (stage & 1) {
+            dim3 g1((unsigned)cdiv(a.r_p, kBlock), (unsigned)a.P, (unsigned)pl.nsplit);
+            k_s1_valu<NT><<<g1, kBlock, 0, s>>>(a, n0, ntok, pl.kchunk, part);
+            if (int rc = last_launch_status()) return rc;
+        }
+        if (stage == 1) {
+            k_t_valu<NT><<<(unsigned)cdiv(ntok * a.P * a.r_p, kBlock), kBlock, 0, s>>>(a, n0, ntok, pl.nsplit,
+                                                                                   part, t, t_dtype);
+            if (int rc = last_launch_status()) return rc;
+        }
+        if (stage & 2) {
+            dim3 g2((unsigned)cdiv(a.d_out, kBlock));
+            k_s2_valu<NT><<<g2, kBlock, 0, s>>>(a, n0, ntok, pl.nsplit, part, stage == 2 ? t : nullptr, t_dtype);
+            if (int rc = last_launch_status()) return rc;
+        }
     }
     return LB_OK;
 }
@@ -171,6 +211,19 @@ int valu_forward(const Linear &a, void *ws, hipStream_t s) {
         case 8: return run_valu<8>(a, pl, part, s);
         case 16: return run_valu<16>(a, pl, part, s);
         default: return run_valu<32>(a, pl, part, s);
+    }
+}
+
+int valu_stage_forward(const Linear &a, void *ws, int stage, void *t, int t_dtype, hipStream_t s) {
+    const ValuPlan pl = plan_valu(a);
+    float *part = (float *)ws;
+    switch (pl.nt) {
+        case 1: return run_valu<1>(a, pl, part, s, stage, t, t_dtype);
+        case 2: return run_valu<2>(a, pl, part, s, stage, t, t_dtype);
+        case 4: return run_valu<4>(a, pl, part, s, stage, t, t_dtype);
+        case 8: return run_valu<8>(a, pl, part, s, stage, t, t_dtype);
+        case 16: return run_valu<16>(a, pl, part, s, stage, t, t_dtype);
+        default: return run_valu<32>(a, pl, part, s, stage, t, t_dtype);
     }
 }
 

@@ -569,6 +569,39 @@ __global__ __launch_bounds__(kThreads) void k_to_bf16(const float *__restrict__ 
     ((u32x2 *)xb)[i] = u32x2{bf16_pair(v[0], v[1]), bf16_pair(v[2], v[3])};
 }
 
+// The latent API: the GEMM kernels keep t as bf16 [T][ldt] with path p in
+// columns p*kw*32 .. (zero padding between the paths); the caller's t is
+// [T][P*r_p] with path p in columns p*r_p ...  One thread per (token, column
+// of ldt).  Out: t_dst = the kernels' latents (widened for fp32, exact).
+__global__ __launch_bounds__(kThreads) void k_t_out(GLin L, int64_t T, void *t_dst, int t_dtype) {
+    const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (e >= T * L.ldt) return;
+    const int64_t n = e / L.ldt;
+    const int c = (int)(e - n * L.ldt);
+    const int p = c / (L.kw * 32), k = c - p * L.kw * 32;
+    if (p >= L.P || k >= L.r_p) return;
+    const uint16_t b = L.t[e];
+    const int64_t o = n * (int64_t)L.P * L.r_p + (int64_t)p * L.r_p + k;
+    if (t_dtype == LB_F32) ((float *)t_dst)[o] = bf16_to_f32(b);
+    else ((uint16_t *)t_dst)[o] = b;
+}
+
+// In: the kernels' latents from the caller's t (rounded to bf16, nearest
+// even), padding columns zero.
+__global__ __launch_bounds__(kThreads) void k_t_in(GLin L, int64_t T, const void *t_src, int t_dtype) {
+    const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (e >= T * L.ldt) return;
+    const int64_t n = e / L.ldt;
+    const int c = (int)(e - n * L.ldt);
+    const int p = c / (L.kw * 32), k = c - p * L.kw * 32;
+    uint16_t b = 0;
+    if (p < L.P && k < L.r_p) {
+        const int64_t o = n * (int64_t)L.P * L.r_p + (int64_t)p * L.r_p + k;
+        b = t_dtype == LB_F32 ? f32_to_bf16(((const float *)t_src)[o]) : ((const uint16_t *)t_src)[o];
+    }
+    L.t[e] = b;
+}
+
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
@@ -749,6 +782,38 @@ int gemm_forward(const Linear &a, void *ws, hipStream_t st) {
     run.itemsR = m.nred;
     run.items2 = items2_of(m);
     run.table = nullptr;
+    return launch_gemms(run, m, st);
+}
+
+int gemm_stage_forward(const Linear &a, void *ws, int stage, void *t, int t_dtype, hipStream_t st) {
+    if (!gemm_shape_ok(a)) return valu_stage_forward(a, ws, stage, t, t_dtype, st);
+    GLin m;
+    std::vector<int> sp;
+    stage1_splits(&a, 1, sp);
+    plan(a, &m, sp[0]);
+    uint16_t *xb = bind(&m, a, (uint8_t *)ws);
+    if (stage == 1 && a.x_dtype == LB_F32) {
+        const int64_t n4 = a.T * a.d_in / 4;
+        k_to_bf16<<<(unsigned)cdiv(n4, kThreads), kThreads, 0, st>>>((const float *)a.x, xb, n4);
+        if (int rc = last_launch_status()) return rc;
+        m.x = xb;
+    }
+    GRun run{};
+    run.T = (int)a.T;
+    run.y_dtype = a.y_dtype;
+    run.itemsG = m.ngp;
+    run.table = nullptr;
+    const unsigned nt = (unsigned)cdiv(a.T * m.ldt, kThreads);
+    if (stage == 1) {
+        run.items1 = items1_of(m);
+        run.itemsR = m.nred;
+        if (int rc = launch_gemms(run, m, st)) return rc;
+        k_t_out<<<nt, kThreads, 0, st>>>(m, a.T, t, t_dtype);
+        return last_launch_status();
+    }
+    k_t_in<<<nt, kThreads, 0, st>>>(m, a.T, t, t_dtype);
+    if (int rc = last_launch_status()) return rc;
+    run.items2 = items2_of(m);
     return launch_gemms(run, m, st);
 }
 

@@ -75,6 +75,14 @@ int launch_pack(const float *src, int64_t rows, int64_t cols, int axis, uint32_t
 // Plain vector-ALU decode path.
 size_t valu_workspace_bytes(const Linear &a);
 int valu_forward(const Linear &a, void *ws, hipStream_t s);
+// The latent API on each kernel family: stage 1 writes the latents t
+// [T][P*r_p] (t_dtype) as the layer computes them; stage 2 computes the output
+// from given latents.  Stage 1 then stage 2 equals the whole layer bit for bit
+// when t_dtype holds the family's own latent precision (fp32 on the decode
+// kernels, bf16 or fp32 on the GEMM kernels, fp32 on the vector-ALU kernels).
+int valu_stage_forward(const Linear &a, void *ws, int stage, void *t, int t_dtype, hipStream_t s);
+int mfma_decode_stage(const Linear &a, void *ws, int stage, void *t, int t_dtype, hipStream_t s);
+int gemm_stage_forward(const Linear &a, void *ws, int stage, void *t, int t_dtype, hipStream_t s);
 
 // The set-up of a group of linears: what its workspace must hold before a
 // run.  Bytes [0, bytes.size()) of the workspace are `bytes` (header with the

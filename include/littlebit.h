@@ -208,6 +208,29 @@ int lb_linear_forward_noalloc(const void *x, int x_dtype, void *y, int y_dtype,
                               const lb_factors *w, int64_t d_in, int64_t d_out, int64_t r,
                               int64_t T, int residual, unsigned flags, void *stream);
 
+/* The two halves of lb_linear_forward around the rank-r intermediate, the
+ * latents t [T][r] (row-major, token-major; with the residual, path p in
+ * columns p*r/2 .. (p+1)*r/2 - 1): t = l_p (.) (sign(V_p)^T (g_p (.) x)).
+ * A k or v projection can keep t per token instead of its d_out-wide output
+ * (sesamedisk page, "The real result": up to 21.3x smaller for Llama2-7B,
+ * 4096 / 192) and expand any number of cached tokens later with stage 2.
+ *   stage 1: x [T][d_in] (x_dtype) -> t (t_dtype, LB_F32 or LB_BF16)
+ *   stage 2: t (t_dtype) -> y [T][d_out] (y_dtype) = sum_p h_p (.) (sign(U_p) t_p)
+ * Both take the layer's full sizes and factors, the workspace of
+ * lb_linear_workspace_bytes and the flags of lb_linear_forward; stage 1 also
+ * takes the y_dtype of the layer's output, which selects the kernels (and so
+ * the precision) as lb_linear_forward does.  Stage 1 then stage 2 gives the
+ * bits of lb_linear_forward when t holds the kernels' own latent precision:
+ * LB_F32 always, LB_BF16 on the GEMM (prefill) kernels.  A bf16 t on the other
+ * kernels rounds the latents once more (within the bf16 tolerance).  t must
+ * not overlap x, y or ws.  Errors as lb_linear_forward. */
+int lb_linear_stage1(const void *x, int x_dtype, void *t, int t_dtype, int y_dtype,
+                     const lb_factors *w, int64_t d_in, int64_t d_out, int64_t r, int64_t T,
+                     int residual, void *ws, size_t ws_bytes, unsigned flags, void *stream);
+int lb_linear_stage2(const void *t, int t_dtype, void *y, int y_dtype, const lb_factors *w,
+                     int64_t d_in, int64_t d_out, int64_t r, int64_t T, int residual,
+                     void *ws, size_t ws_bytes, unsigned flags, void *stream);
+
 /* Workspace bytes lb_mlp_forward needs.  0 on bad arguments. */
 size_t lb_mlp_workspace_bytes(int64_t d_model, int64_t d_ff, int64_t r_gu, int64_t r_down,
                               int64_t T, int residual, unsigned flags);

@@ -202,3 +202,30 @@ def test_grouped_call_argument_errors():
     assert L.lb_grouped_workspace_bytes(descs, 1, 1, lb.LB_GROUP_FAULT_TEST) > 0
     assert L.lb_grouped_prepare(descs, 1, 1, lb.LB_BF16, lb.LB_BF16, FAKE, 1 << 30, 1 << 9,
                                 None) == lb.LB_EINVAL
+
+
+def test_latent_api_argument_errors():
+    L = lb.lib()
+    f = _factors()
+    X, TT, Y, WS = FAKE + 0x5000000, FAKE + 0x6000000, FAKE + 0x8000000, FAKE + 0xa000000
+    need = L.lb_linear_workspace_bytes(1024, 1024, 512, 4, 0, 0)
+    s1 = lambda **k: L.lb_linear_stage1(k.get("x", X), k.get("xd", lb.LB_BF16), k.get("t", TT),
+                                        k.get("td", lb.LB_F32), k.get("yd", lb.LB_BF16), ctypes.byref(f),
+                                        1024, 1024, k.get("r", 512), k.get("T", 4), k.get("res", 0),
+                                        k.get("ws", WS), need, k.get("flags", 0), None)
+    s2 = lambda **k: L.lb_linear_stage2(k.get("t", TT), k.get("td", lb.LB_F32), k.get("y", Y),
+                                        k.get("yd", lb.LB_BF16), ctypes.byref(f), 1024, 1024, k.get("r", 512),
+                                        k.get("T", 4), 0, k.get("ws", WS), need, 0, None)
+    assert s1(td=7) == lb.LB_EINVAL
+    assert s1(yd=7) == lb.LB_EINVAL
+    assert s1(t=0) == lb.LB_EINVAL
+    assert s1(t=TT + 2) == lb.LB_EALIGN                      # fp32 t misaligned
+    assert s1(t=X + 64) == lb.LB_EINVAL                      # t overlaps x
+    assert s1(ws=None) == lb.LB_EWORKSPACE
+    assert s1(ws=TT) == lb.LB_EINVAL                         # ws overlaps t
+    assert s1(flags=1 << 8) == lb.LB_EINVAL                  # a group-only flag
+    assert s1(r=511, res=1) == lb.LB_EINVAL
+    assert s1(T=0, x=0, t=0) == lb.LB_OK                     # empty: a no-op
+    assert s2(y=0) == lb.LB_EINVAL
+    assert s2(y=TT) == lb.LB_EINVAL                          # y overlaps t
+    assert s2(td=lb.LB_BF16, t=TT + 1) == lb.LB_EALIGN
