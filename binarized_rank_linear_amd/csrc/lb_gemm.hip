@@ -28,7 +28,10 @@
 // every linear of a group (a table maps work items to linears), and work items
 // are renumbered so that each of the 8 XCDs (own L2) gets a contiguous range:
 // neighbouring tiles share their activation rows.
+#include <algorithm>
 #include <cstring>
+#include <functional>
+#include <map>
 #include <vector>
 
 #include "lb_internal.h"
@@ -105,6 +108,9 @@ struct GRun {
     const uint64_t *stamp;
     uint64_t tag;
     uint32_t *faults;
+    // groups: workgroup -> item for stage 1 / stage 2, longest items first in
+    // blocks spread over the XCDs (null: xcd_order)
+    const int32_t *ord1, *ord2;
 };
 
 // Whether a group's workspace no longer carries the stamp the group was set up
@@ -168,6 +174,8 @@ __device__ __forceinline__ void wait_and_meet() {
     asm volatile("" ::: "memory");
 }
 
+
+
 // Even bits of x to the low half, odd bits to the high half (inverse perfect
 // shuffle by four delta swaps).
 __device__ __forceinline__ uint32_t unzip_bits(uint32_t x) {
@@ -208,7 +216,8 @@ __global__ __launch_bounds__(kThreads, NBW == 4 ? 1 : 2) void k_gemm(GRun run, G
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     if (stale_ws(run)) return;
     const int64_t items = STAGE == 1 ? run.items1 : run.items2;
-    const int64_t v = xcd_order(blockIdx.x, items);
+    const int32_t *ord = STAGE == 1 ? run.ord1 : run.ord2;
+    const int64_t v = ord ? (int64_t)__builtin_amdgcn_readfirstlane(ord[blockIdx.x]) : xcd_order(blockIdx.x, items);
     const GLin L = pick(run, single, STAGE == 1 ? run.lin1 : run.lin2, v);
     const int64_t local = v - (STAGE == 1 ? L.item1 : L.item2);
     // item = (piece of d_in [stage 1], token tile, column tile)
@@ -525,39 +534,44 @@ __global__ __launch_bounds__(kThreads) void k_prep(GRun run, GLin single) {
 }
 
 // Stage-1 pieces -> t: the pieces are added in order, then scaled by l.
-// Item = kRedGroups groups of 4 latents (one token row segment each).
-constexpr int kRedGroups = 1024;
-
+// One thread per group of 4 latents of one token; its pieces' loads go out
+// together (8 at a time, unconditional buffer loads: pieces past the last
+// read as zeros and are not added), so a thread waits about once per 8 pieces.
 __global__ __launch_bounds__(kThreads) void k_reduce(GRun run, GLin single) {
     if (stale_ws(run)) return;
     const int64_t v = blockIdx.x;
     const GLin L = pick(run, single, run.linR, v);
-    const int64_t local = v - L.itemR;
     const int T = run.T;
     const int64_t groups = (int64_t)T * (L.ldt / 4);
-    const int64_t stride = (int64_t)T * L.ldt;
-    for (int i = threadIdx.x; i < kRedGroups; i += kThreads) {
-        const int64_t gi = local * kRedGroups + i;
-        if (gi >= groups) break;
-        const int64_t m = gi / (L.ldt / 4);
-        const int n = (int)(gi - m * (L.ldt / 4)) * 4;
-        f32x4 s = *(const f32x4 *)(L.part + m * L.ldt + n);
-        for (int sp = 1; sp < L.nsplit; ++sp) {
-            const f32x4 a = *(const f32x4 *)(L.part + sp * stride + m * L.ldt + n);
-            s[0] += a[0];
-            s[1] += a[1];
-            s[2] += a[2];
-            s[3] += a[3];
-        }
-        const int qn = n >> 5;
-        const int p = qn / L.kw;
-        const int k = (qn - p * L.kw) * 32 + (n & 31);
-        float tv[4];
+    const int64_t gi = (v - L.itemR) * kThreads + threadIdx.x;
+    if (gi >= groups) return;
+    const int64_t m = gi / (L.ldt / 4);
+    const int n = (int)(gi - m * (L.ldt / 4)) * 4;
+    const int64_t stride = (int64_t)T * L.ldt * 4;                 // bytes between pieces
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(L.part, stride * L.nsplit);
+    const uint32_t base = (uint32_t)((m * L.ldt + n) * 4);
+    f32x4 s;
+    for (int sp0 = 0; sp0 < L.nsplit; sp0 += 8) {
+        u32x4 a[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            tv[e] = (p < L.P && k + e < L.r_p) ? f16_to_f32(L.l[(int64_t)p * L.r_p + k + e]) * s[e] : 0.0f;
-        *(u32x2 *)(L.t + m * L.ldt + n) = u32x2{bf16_pair(tv[0], tv[1]), bf16_pair(tv[2], tv[3])};
+        for (int q = 0; q < 8; ++q)
+            a[q] = __builtin_amdgcn_raw_buffer_load_b128(
+                rp, sp0 + q < L.nsplit ? base + (uint32_t)((int64_t)(sp0 + q) * stride) : kOOB, 0, 0);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const f32x4 x = __builtin_bit_cast(f32x4, a[q]);
+            if (sp0 + q == 0) s = x;
+            else if (sp0 + q < L.nsplit) s += x;
+        }
     }
+    const int qn = n >> 5;
+    const int p = qn / L.kw;
+    const int k = (qn - p * L.kw) * 32 + (n & 31);
+    float tv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        tv[e] = (p < L.P && k + e < L.r_p) ? f16_to_f32(L.l[(int64_t)p * L.r_p + k + e]) * s[e] : 0.0f;
+    *(u32x2 *)(L.t + m * L.ldt + n) = u32x2{bf16_pair(tv[0], tv[1]), bf16_pair(tv[2], tv[3])};
 }
 
 // fp32 activations -> bf16 (round to nearest even), 4 per thread.
@@ -630,27 +644,87 @@ bool gemm_shape_ok(const Linear &a) {
 // at one piece per tile and, while the launch stays within kWG1 workgroups,
 // split further the linear whose pieces are longest (every tile of a linear
 // takes one more piece).  Writes splits[j].
+// Stage-1 pieces (d_in splits) per linear for a launch over ls[0..n).  The
+// launch's workgroups run on kWG1 slots (two per CU), longest pieces first;
+// its time is about the makespan of that schedule (in K-tiles of 64 per
+// slot) plus the reduce pass that adds the pieces.  The pieces are cut to a
+// common target length, the one (among the lengths the linears' K-tiles
+// split into) that gives the least such estimate.  Without it one long
+// linear (a down projection, d_in 17408 or 28672, beside 5120- or
+// 8192-wide ones) sets the launch's length alone.  Writes splits[j].
+namespace {
+struct SplitModel {
+    std::vector<int64_t> nkt, tiles, red_bytes;    // per linear: K-tiles, tiles, reduce bytes per piece
+};
+
+// Longest-first makespan of pieces grouped as (length, count), on kWG1
+// identical slots; the slots' end times are kept as a multiset.
+int64_t lpt_span(std::vector<std::pair<int64_t, int64_t>> pieces) {
+    std::sort(pieces.begin(), pieces.end(), [](const std::pair<int64_t, int64_t> &x,
+                                               const std::pair<int64_t, int64_t> &y) { return x.first > y.first; });
+    std::map<int64_t, int64_t> ends;
+    ends[0] = kWG1;
+    for (const auto &pc : pieces) {
+        if (pc.first <= 0) continue;
+        int64_t c = pc.second;
+        while (c > 0) {                 // the earliest free slots take the next pieces
+            auto it = ends.begin();
+            const int64_t e = it->first, m = std::min(c, it->second);
+            it->second -= m;
+            if (it->second == 0) ends.erase(it);
+            ends[e + pc.first] += m;
+            c -= m;
+        }
+    }
+    return ends.rbegin()->first;
+}
+
+double split_cost(const SplitModel &m, const std::vector<int> &sp) {
+    std::vector<std::pair<int64_t, int64_t>> pieces;
+    double red = 0;
+    for (size_t j = 0; j < sp.size(); ++j) {
+        const int64_t ktps = cdiv(m.nkt[j], sp[j]);
+        const int64_t np = cdiv(m.nkt[j], ktps);
+        const int64_t last = m.nkt[j] - (np - 1) * ktps;
+        if (np > 1) pieces.push_back({ktps, (np - 1) * m.tiles[j]});
+        pieces.push_back({last, m.tiles[j]});
+        if (np > 1) red += (double)np * m.red_bytes[j];
+    }
+    // in us: a K-tile of 64 on a slot takes about 2 us at the measured rates
+    // (two workgroups share a CU); the reduce reads the pieces and writes t
+    // at about 5 TB/s
+    return 2.0 * (double)lpt_span(pieces) + red / 5e6;
+}
+}  // namespace
+
 void stage1_splits(const Linear *ls, int n, std::vector<int> &splits) {
-    std::vector<int64_t> nkt((size_t)n), tiles((size_t)n);
-    int64_t used = 0;
+    SplitModel m;
+    std::vector<int64_t> cand;
     for (int j = 0; j < n; ++j) {
         const Linear &a = ls[j];
         const int64_t ldt = rup((int64_t)a.P * cdiv(a.r_p, 32) * 32, kBK);
-        nkt[(size_t)j] = cdiv(a.d_in, kBK);
-        tiles[(size_t)j] = cdiv(ldt, kBN1) * cdiv(a.T, kBM);
-        used += tiles[(size_t)j];
-    }
-    splits.assign((size_t)n, 1);
-    for (;;) {
-        int best = -1;
-        int64_t len = 0;
-        for (int j = 0; j < n; ++j) {
-            const int64_t l = cdiv(nkt[(size_t)j], splits[(size_t)j]);
-            if (l > len && splits[(size_t)j] < nkt[(size_t)j]) { len = l; best = j; }
+        const int64_t nkt = cdiv(a.d_in, kBK);
+        m.nkt.push_back(nkt);
+        m.tiles.push_back(cdiv(ldt, kBN1) * cdiv(a.T, kBM));
+        m.red_bytes.push_back(a.T * ldt * 4);
+        for (int64_t sp = 1; sp <= 64; ++sp) {
+            const int64_t l = cdiv(nkt, sp);
+            if (l < 8 && sp > 1) break;                 // pieces of at least 8 K-tiles
+            cand.push_back(l);
         }
-        if (best < 0 || len <= 8 || used + tiles[(size_t)best] > kWG1) break;
-        used += tiles[(size_t)best];
-        ++splits[(size_t)best];
+    }
+    std::sort(cand.begin(), cand.end());
+    cand.erase(std::unique(cand.begin(), cand.end()), cand.end());
+    splits.assign((size_t)n, 1);
+    double best = split_cost(m, splits);
+    std::vector<int> sp((size_t)n);
+    for (int64_t target : cand) {
+        for (int j = 0; j < n; ++j) sp[(size_t)j] = (int)std::max<int64_t>(1, cdiv(m.nkt[(size_t)j], target));
+        const double c = split_cost(m, sp);
+        if (c < best - 1e-9) {
+            best = c;
+            splits = sp;
+        }
     }
 }
 
@@ -682,7 +756,7 @@ size_t plan(const Linear &a, GLin *m, int nsplit) {
     m->mt = (int32_t)cdiv(a.T, kBM);
     m->nt1 = (int32_t)cdiv(m->ldt, kBN1);
     m->nt2 = (int32_t)cdiv(a.d_out, kBN2);
-    m->nred = m->nsplit > 1 ? (int32_t)cdiv(a.T * (m->ldt / 4), kRedGroups) : 0;
+    m->nred = m->nsplit > 1 ? (int32_t)cdiv(a.T * (m->ldt / 4), kThreads) : 0;
     const int64_t nv = (int64_t)a.P * m->kw_v * m->zld_v, nu = (int64_t)a.P * m->kw * m->zld_u;
     m->ngp = (int32_t)cdiv((int64_t)a.P * a.d_in / 2 + nv + nu, kPrep);
     const size_t tb = rup256((size_t)a.T * m->ldt * 2);
@@ -834,8 +908,28 @@ bool gemm_group_supported(const Linear *ls, int n) {
 // and the item tables (the "control" part), then each linear's scratch.
 struct GLayout {
     int64_t iG = 0, i1 = 0, iR = 0, i2 = 0;
-    size_t table, linG, lin1, linR, lin2, ctrl_end, total;
+    size_t table, linG, lin1, linR, lin2, ord1, ord2, ctrl_end, total;
 };
+
+// Dispatch order of a launch's items from their lengths (K-tiles): longest
+// first, so the launch ends on short items; workgroups go to the 8 XCDs in
+// turn, so each block of 8 * kRun items in that order is dealt out as kRun
+// consecutive items per XCD (consecutive items share activation rows in the
+// XCD's L2).
+std::vector<int32_t> dispatch_order(const std::vector<int64_t> &len) {
+    constexpr int kRun = 4;
+    const int64_t n = (int64_t)len.size();
+    std::vector<int32_t> L((size_t)n);
+    for (int64_t i = 0; i < n; ++i) L[(size_t)i] = (int32_t)i;
+    std::stable_sort(L.begin(), L.end(), [&](int32_t a, int32_t b) { return len[(size_t)a] > len[(size_t)b]; });
+    std::vector<int32_t> D((size_t)n);
+    for (int64_t c0 = 0; c0 < n; c0 += 8 * kRun) {
+        const int64_t cnt = std::min<int64_t>(8 * kRun, n - c0);
+        for (int64_t b = 0; b < cnt; ++b)
+            D[(size_t)(c0 + b)] = cnt == 8 * kRun ? L[(size_t)(c0 + (b % 8) * kRun + b / 8)] : L[(size_t)(c0 + b)];
+    }
+    return D;
+}
 
 GLayout glayout(const Linear *ls, int n, std::vector<GLin> *tab, std::vector<size_t> *scratch) {
     std::vector<int> sp;
@@ -866,6 +960,8 @@ GLayout glayout(const Linear *ls, int n, std::vector<GLin> *tab, std::vector<siz
     g.lin1 = take((size_t)g.i1 * 4);
     g.linR = take((size_t)g.iR * 4);
     g.lin2 = take((size_t)g.i2 * 4);
+    g.ord1 = take((size_t)g.i1 * 4);
+    g.ord2 = take((size_t)g.i2 * 4);
     g.ctrl_end = at;
     g.total = at + lin_bytes;
     return g;
@@ -907,6 +1003,19 @@ int gemm_group_plan(const Linear *ls, int n, void *ws, size_t ws_bytes, uint64_t
     put(G.lin1, h1.data(), (size_t)G.i1 * 4);
     put(G.linR, hR.data(), (size_t)G.iR * 4);
     put(G.lin2, h2.data(), (size_t)G.i2 * 4);
+    // item lengths in K-tiles of 64: stage 1 the item's piece of d_in, stage 2 the latents
+    std::vector<int64_t> len1((size_t)G.i1), len2((size_t)G.i2);
+    for (int j = 0; j < n; ++j) {
+        const GLin &m = tab[(size_t)j];
+        for (int64_t k = 0; k < items1_of(m); ++k) {
+            const int64_t split = k / ((int64_t)m.nt1 * m.mt);
+            len1[(size_t)(m.item1 + k)] = split + 1 < m.nsplit ? m.ktps : m.nkt1 - (int64_t)(m.nsplit - 1) * m.ktps;
+        }
+        for (int64_t k = 0; k < items2_of(m); ++k) len2[(size_t)(m.item2 + k)] = m.nkt2;
+    }
+    const std::vector<int32_t> o1 = dispatch_order(len1), o2 = dispatch_order(len2);
+    put(G.ord1, o1.data(), (size_t)G.i1 * 4);
+    put(G.ord2, o2.data(), (size_t)G.i2 * 4);
     // the scratch needs no initial contents (every byte a run reads it writes first)
     img->zero_off = G.ctrl_end;
     img->zero_bytes = 0;
@@ -923,6 +1032,8 @@ int gemm_group_plan(const Linear *ls, int n, void *ws, size_t ws_bytes, uint64_t
     run.lin1 = (const int32_t *)(w + G.lin1);
     run.linR = (const int32_t *)(w + G.linR);
     run.lin2 = (const int32_t *)(w + G.lin2);
+    run.ord1 = (const int32_t *)(w + G.ord1);
+    run.ord2 = (const int32_t *)(w + G.ord2);
     run.stamp = (const uint64_t *)w;
     run.tag = tag;
     run.faults = fault_word_ptr();
