@@ -5,13 +5,16 @@ One step is one forward pass of the token batch through a stack of seeded
 synthetic LittleBit linears: by default the Llama2-70B-shaped decoder-layer
 linears (q/o 8192x8192, k/v 8192x1024, gate/up 8192x28672, down 28672x8192) at
 0.1 bits per weight with the residual path, 80 independent layers, decode T=1,
-run as one group (two kernel launches per pass).  The stack holds ~0.8 GB of
+run as one group (one kernel launch per pass).  The stack holds ~0.8 GB of
 packed signs, more than three times the 256 MB Infinity Cache, so every pass
 streams from HBM.  Prints ONE JSON line.
 
-The prefill leg times the same shapes at T=2048 (one layer, the GEMM path)
-and reports it beside the decode figure.  The CPU baseline times the fp64
-oracle on one layer of the same stack and scales to the stack.
+Beside it: the prefill leg (the same shapes at T=2048, one layer, the GEMM
+path), the Llama2-7B-shaped 32-layer stack at T=4 and T=32, the two small
+cache-resident configurations, and the measured ceilings (a streaming read,
+back-to-back bf16 matrix instructions).  The CPU baseline times the fp64
+oracle on one layer of the same stack and scales to the stack (and on a
+token subset of the prefill layer).
 
     python bench.py [--steps K] [--warmup W] [--workload c5] [--tokens 1]
 """
@@ -126,6 +129,19 @@ def time_staged(st, steps):
     return s1, s2
 
 
+def cpu_info():
+    """The host CPU's model name and logical core count (os.cpu_count)."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return model, os.cpu_count()
+
+
 def cpu_baseline(w, T, layers, budget_s=10.0):
     """The fp64 oracle on one layer of the stack (all its linears, seeded
     inputs of the same shapes), run repeatedly until about budget_s seconds of
@@ -147,9 +163,79 @@ def cpu_baseline(w, T, layers, budget_s=10.0):
         passes += 1
     t_layer = t_total / passes
     cores = oracle.max_threads()
+    model, nproc = cpu_info()
     return {"value": T / (t_layer * layers), "unit": "tok/s", "cores": cores, "kind": "oracle",
+            "cpu_model": model, "nproc": nproc,
             "sample": "one layer (%d linears, seeded inputs) at T=%d, %d passes in %.1f s, scaled "
                       "to the %d-layer stack" % (len(w.linears), T, passes, t_total, layers)}
+
+
+def oracle_prefill(w, tokens=16):
+    """The fp64 oracle on one layer of the workload at `tokens` tokens (seeded
+    inputs of the layer's shapes), scaled linearly to tokens per second (the
+    tokens are independent)."""
+    import oracle
+    import synth
+    t_total = 0.0
+    for i, sh in enumerate(w.linears):
+        r, rp = oracle.rank_for_budget(sh.d_in, sh.d_out, w.b_num, w.b_den, w.residual)
+        inp = synth.layer_inputs(i, sh.d_in, sh.d_out, rp, 2 if w.residual else 1)
+        x = synth.activations(synth.activation_seed(2048), tokens, sh.d_in, w.dtype)
+        t0 = time.perf_counter()
+        oracle.linear_forward(x, inp.U, inp.V, inp.h, inp.g, inp.l)
+        t_total += time.perf_counter() - t0
+    model, nproc = cpu_info()
+    return {"value": tokens / t_total, "unit": "tok/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "cpu_model": model, "nproc": nproc,
+            "sample": "one layer (%d linears) on %d of the 2048 tokens in %.2f s, scaled linearly"
+                      % (len(w.linears), tokens, t_total)}
+
+
+def ceilings():
+    """The measured ceilings beside the published peaks: a streaming read of
+    2 GiB (eight times the Infinity Cache) and back-to-back bf16 matrix
+    instructions on register operands (lb_ceiling_stream_read,
+    lb_ceiling_mfma_bf16), each timed with HIP events on the launch stream."""
+    import torch
+    import binarized_rank_linear_amd as lb
+    L = lb.lib()
+    s = torch.cuda.current_stream()
+    nbytes = 2 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    blocks = 256 * 8
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+
+    def timed(fn, reps):
+        for _ in range(3):
+            fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(s)
+        for _ in range(reps):
+            fn()
+        e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    def read():
+        assert L.lb_ceiling_stream_read(buf.data_ptr(), nbytes, out.data_ptr(), blocks, s.cuda_stream) == 0
+
+    iters, mblocks = 4000, 256 * 4
+
+    def mfma():
+        assert L.lb_ceiling_mfma_bf16(iters, out.data_ptr(), mblocks, s.cuda_stream) == 0
+
+    t_read = timed(read, 20)
+    t_mfma = timed(mfma, 5)
+    gbs = nbytes / t_read / 1e9
+    tfl = mblocks * 4 * iters * 8 * 32768 / t_mfma / 1e12
+    del buf
+    torch.cuda.empty_cache()
+    return {"stream_read_GBs": gbs, "stream_read_frac": gbs / HBM_PEAK_GBS,
+            "mfma_bf16_TFLOPs": tfl, "mfma_bf16_frac": tfl / BF16_PEAK_TFLOPS,
+            "how": "2 GiB read by 2048 workgroups, 16-byte non-temporal loads, 8 in flight; "
+                   "1024 workgroups x 4 waves x %d x 8 independent v_mfma_f32_32x32x16_bf16" % iters}
 
 
 def measured_traffic(kernel, workload, T):
@@ -215,6 +301,89 @@ def single_layer_leg(w, T, reps=2000):
             "effective_GBs": nbytes / t / 1e9,
             "note": "the layer's %.1f MB stay in the Infinity Cache, so this can exceed the HBM peak"
                     % (nbytes / 1e6)}
+
+
+def decode_stack_leg(key, T, steps, layers=0):
+    """A second decode figure: the workload's stack at T tokens as one group,
+    HIP events around `steps` passes after a settle period.  Below 20 tokens
+    HBM bounds the pass (fraction of 8 TB/s over the algorithmic bytes); at
+    more tokens the dense-equivalent matrix work 2 T r (d_in + d_out) is
+    also reported against the bf16 peak."""
+    import torch
+    import synth
+    w = synth.WORKLOADS[key]
+    L = layers or w.layers
+    st, _ = build_stack(w, L, T)
+    P = 2 if w.residual else 1
+    nbytes = sum(sum(linear_bytes(lin.d_in, lin.d_out, lin.r, P, T)) for row in st.linears for lin in row)
+    flops = sum(2 * T * lin.r * (lin.d_in + lin.d_out) for row in st.linears for lin in row)
+    step_s, kern_s = time_decode(st, steps, 5, 0.2)
+    del st
+    torch.cuda.empty_cache()
+    out = {"workload": "%s, decode T=%d, %d-layer stack as one group" % (w.title, T, L),
+           "us_per_pass": kern_s * 1e6, "tok_per_s": T / step_s, "algorithmic_bytes": nbytes,
+           "GBs": nbytes / kern_s / 1e9, "hbm_frac": nbytes / kern_s / 1e9 / HBM_PEAK_GBS,
+           "dense_equivalent_TFLOPs": flops / kern_s / 1e12,
+           "mfma_frac": flops / kern_s / 1e12 / BF16_PEAK_TFLOPS}
+    out["bound"] = "hbm" if nbytes / (HBM_PEAK_GBS * 1e9) >= flops / (BF16_PEAK_TFLOPS * 1e12) else "mfma"
+    return out
+
+
+def cache_resident_legs(reps=2000):
+    """The two small configurations, whose factors stay in the caches: the
+    1024 x 1024 linear at 1.0 bit per weight (fp32, T = 1 and 8) and the
+    Qwen3-0.6B-shaped SwiGLU block at 0.55 bits per weight with the residual
+    (bf16, T = 1 and 16); microseconds per call, HIP events around `reps`
+    calls with preallocated outputs and workspace."""
+    import torch
+    import synth
+    import binarized_rank_linear_amd as lb
+    s = torch.cuda.current_stream()
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.1:
+            for _ in range(50):
+                fn()
+            torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(reps):
+            fn()
+        e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    res = []
+    r, rp = lb.rank_for_budget(1024, 1024, 1, 1, False)
+    U, V, h, g, l = synth.device_layer(0, 1024, 1024, rp, 1)
+    lin = lb.PackedLinear.from_factors(U, V, h, g, l)
+    for T in (1, 8):
+        x = synth.device_activations(synth.activation_seed(T), T, 1024, "f32")
+        y = torch.empty((T, 1024), dtype=torch.float32, device="cuda")
+        ws = lb.workspace(lb.linear_workspace_bytes(lin, T))
+        t = timed(lambda: lb.linear_forward(x, lin, torch.float32, ws=ws, out=y))
+        nb = sum(linear_bytes(1024, 1024, r, 1, T, 4))
+        res.append({"workload": "1024 x 1024 linear, 1.0 bpw (r = 512), fp32, T=%d, cache-resident" % T,
+                    "us_per_call": t * 1e6, "tok_per_s": T / t, "effective_GBs": nb / t / 1e9})
+    w = synth.WORKLOADS["c2"]
+    mats = []
+    for i, sh in enumerate(w.linears):
+        r, rp = lb.rank_for_budget(sh.d_in, sh.d_out, w.b_num, w.b_den, w.residual)
+        U, V, h, g, l = synth.device_layer(i, sh.d_in, sh.d_out, rp, 2)
+        mats.append(lb.PackedLinear.from_factors(U, V, h, g, l))
+    gate, up, down = mats
+    for T in (1, 16):
+        x = synth.device_activations(synth.activation_seed(T), T, 1024, "bf16")
+        y = torch.empty((T, 1024), dtype=torch.bfloat16, device="cuda")
+        ws = lb.workspace(lb.mlp_workspace_bytes(gate, down, T))
+        t = timed(lambda: lb.mlp_forward(x, gate, up, down, torch.bfloat16, ws=ws, out=y))
+        nb = sum(sum(linear_bytes(m.d_in, m.d_out, m.r, 2, T)) for m in mats)
+        res.append({"workload": "Qwen3-0.6B-shaped SwiGLU block (1024 -> 3072 -> 1024), 0.55 bpw with the "
+                                "residual, bf16, T=%d, cache-resident" % T,
+                    "us_per_call": t * 1e6, "tok_per_s": T / t, "effective_GBs": nb / t / 1e9})
+    return res
 
 
 def library_gemm_reference(layer, xs, T, steps):
@@ -357,6 +526,9 @@ def main():
                     help="only run the T=2048 prefill leg and print its JSON")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain MIB-MiB device copy (counter calibration) and exit")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other decode legs (32-layer stack at T=4 and T=32), the "
+                         "cache-resident configurations and the measured ceilings")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the LittleBit stack fits one MI355X, and the "
@@ -431,11 +603,23 @@ def main():
         out["decode_single_layer"] = single_layer_leg(w, T)
     if not args.no_prefill and args.prefill_tokens > 32:
         try:
-            out["prefill"] = prefill_leg(w, args.prefill_tokens, max(3, args.steps // 50))
+            out["prefill"] = prefill_leg(w, args.prefill_tokens, max(10, args.steps // 10))
         except Exception as e:  # report, do not hide
             out["prefill"] = {"error": repr(e)}
+    if not args.no_extra:
+        out["decode_more"] = [decode_stack_leg("c3", 4, max(20, args.steps // 2)),
+                              decode_stack_leg("c3", 32, max(10, args.steps // 10))]
+        out["cache_resident"] = cache_resident_legs()
+        c = ceilings()
+        out["ceilings"] = c
+        out["roofline"]["frac_of_measured_ceiling"] = bw / c["stream_read_GBs"]
+        if isinstance(out.get("prefill"), dict) and "roofline" in out["prefill"]:
+            out["prefill"]["roofline"]["frac_of_measured_ceiling"] = \
+                out["prefill"]["roofline"]["achieved"] / c["mfma_bf16_TFLOPs"]
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, T, layers)
+        if isinstance(out.get("prefill"), dict) and "roofline" in out["prefill"]:
+            out["prefill"]["cpu_baseline"] = oracle_prefill(w)
     print(json.dumps(out), flush=True)
 
 

@@ -137,6 +137,10 @@ def lib() -> ctypes.CDLL:
         L.lb_linear_stage2.argtypes = [_vp, ctypes.c_int, _vp, ctypes.c_int, ctypes.POINTER(lb_factors),
                                        _i64, _i64, _i64, _i64, ctypes.c_int, _vp, _sz, ctypes.c_uint, _vp]
         L.lb_linear_stage2.restype = ctypes.c_int
+        L.lb_ceiling_stream_read.argtypes = [_vp, _sz, _vp, ctypes.c_int, _vp]
+        L.lb_ceiling_stream_read.restype = ctypes.c_int
+        L.lb_ceiling_mfma_bf16.argtypes = [ctypes.c_int, _vp, ctypes.c_int, _vp]
+        L.lb_ceiling_mfma_bf16.restype = ctypes.c_int
         _lib = L
     return _lib
 

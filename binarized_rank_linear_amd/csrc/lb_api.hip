@@ -321,13 +321,31 @@ static size_t mlp_linear_ws(int64_t d_model, int64_t d_ff, int64_t r_gu, int64_t
     return a > b ? a : b;
 }
 
+// The fused decode form of the block (bf16 output, decode kernels): gate and
+// up as one three-launch group writing bf16, then down reading silu(gate) (.)
+// up as its input (computed while its stage 1 stages the activations).
+// Workspace: gate and up outputs, then the larger of the two runs' scratch.
+static size_t mlp_fused_ws(const Linear &ag, const Linear &au, const Linear &ad) {
+    const size_t inter = rup256((size_t)(ag.T * ag.d_out) * 2);
+    const Linear gu[2] = {ag, au};
+    const size_t a = mfma_inline_workspace_bytes(gu, 2), b = mfma_decode_workspace_bytes(ad);
+    return 2 * inter + rup256(a > b ? a : b);
+}
+
 size_t lb_mlp_workspace_bytes(int64_t d_model, int64_t d_ff, int64_t r_gu, int64_t r_down,
                               int64_t T, int residual, unsigned flags) {
-    Linear a{};
-    if (check_shape(d_model, d_ff, r_gu, T, residual, &a)) return 0;
-    if (check_shape(d_ff, d_model, r_down, T, residual, &a)) return 0;
+    Linear ag{}, ad{};
+    if (check_shape(d_model, d_ff, r_gu, T, residual, &ag)) return 0;
+    if (check_shape(d_ff, d_model, r_down, T, residual, &ad)) return 0;
+    if (flags & ~kLinearFlags) return 0;
     const size_t inter = rup256((size_t)(T * d_ff) * sizeof(float));
-    return 2 * inter + mlp_linear_ws(d_model, d_ff, r_gu, r_down, T, residual, flags);
+    size_t need = 2 * inter + mlp_linear_ws(d_model, d_ff, r_gu, r_down, T, residual, flags);
+    Path p;
+    if (T > 0 && !choose_path(flags, T, LB_BF16, &p) && p == Path::MfmaDecode) {
+        ag.y_dtype = ag.x_dtype = ad.y_dtype = ad.x_dtype = LB_BF16;
+        need = std::max(need, mlp_fused_ws(ag, ag, ad));
+    }
+    return need;
 }
 
 int lb_mlp_forward(const void *x, int x_dtype, void *y, int y_dtype, const lb_factors *gate,
@@ -356,11 +374,28 @@ int lb_mlp_forward(const void *x, int x_dtype, void *y, int y_dtype, const lb_fa
     if (overlap(ws, need, x, (size_t)(T * d_model) * act_size(x_dtype)) ||
         overlap(ws, need, y, (size_t)(T * d_model) * act_size(y_dtype)))
         return LB_EINVAL;
+    hipStream_t s = (hipStream_t)stream;
+    if (p == Path::MfmaDecode && y_dtype == LB_BF16 && mfma_decode_shape_ok(ag) && mfma_decode_shape_ok(au)) {
+        // the fused form: gate and up (bf16) as one group, down reads the SwiGLU
+        const size_t inter = rup256((size_t)(T * d_ff) * 2);
+        uint16_t *yg = (uint16_t *)ws, *yu = (uint16_t *)((char *)ws + inter);
+        void *lws = (char *)ws + 2 * inter;
+        ag.x = au.x = x;
+        ag.x_dtype = au.x_dtype = x_dtype;
+        ag.y = yg;
+        au.y = yu;
+        ag.y_dtype = au.y_dtype = LB_BF16;
+        ad.x = yg;
+        ad.x2 = yu;
+        ad.x_dtype = LB_BF16;
+        const Linear gu[2] = {ag, au};
+        if ((rc = mfma_inline_forward(gu, 2, lws, s))) return rc;
+        return mfma_decode_forward(ad, lws, s);
+    }
     const size_t inter = rup256((size_t)(T * d_ff) * sizeof(float));
     float *zg = (float *)ws;
     float *zu = (float *)((char *)ws + inter);
     void *lws = (char *)ws + 2 * inter;
-    hipStream_t s = (hipStream_t)stream;
     // gate and up read the same x; the intermediate stays fp32.
     ag.x = au.x = x;
     ag.x_dtype = au.x_dtype = x_dtype;

@@ -1,0 +1,81 @@
+// lb_ceiling.hip -- the two measured ceilings the layer's figures are compared
+// against, besides the published peaks: a streaming read of device memory
+// (what the decode kernels' sign streams can reach) and back-to-back bf16
+// matrix instructions on register operands (what the prefill GEMMs can reach).
+// Measurement helpers only; no part of the layer runs here.
+#include "lb_internal.h"
+
+namespace lb {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Every workgroup reads 16-byte pieces i = blockIdx.x * 256 + threadIdx.x,
+// stepping by the grid, 8 loads in flight per thread; the XOR of everything
+// read goes to out[blockIdx.x] so no load can be dropped.
+__global__ __launch_bounds__(256) void k_stream_read(const u32x4 *__restrict__ p, int64_t n16, uint32_t *out) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    for (; i + 7 * stride < n16; i += 8 * stride) {
+        u32x4 v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = __builtin_nontemporal_load(p + i + k * stride);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc ^= v[k];
+    }
+    for (; i < n16; i += stride) acc ^= p[i];
+    const uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+    __shared__ uint32_t s[256];
+    s[threadIdx.x] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t r = 0;
+        for (int k = 0; k < 256; ++k) r ^= s[k];
+        out[blockIdx.x] = r;
+    }
+}
+
+// Each wave runs `iters` rounds of 8 independent v_mfma_f32_32x32x16_bf16 on
+// register operands (8 accumulators, so the instructions never wait for each
+// other's results); the accumulators' sum goes to out so none is dropped.
+__global__ __launch_bounds__(256) void k_mfma_bf16(int iters, float *out) {
+    const uint32_t l = threadIdx.x;
+    u32x4 a = {l * 0x00010001u, l ^ 0x3f803f80u, 0x3f803f80u, l};
+    u32x4 b = {0x3c003c00u ^ l, 0x3f80bf80u, l << 3, 0x40004000u};
+    f32x16 c[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) c[j][e] = 0.0f;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            c[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                          c[j], 0, 0, 0);
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s += c[j][e];
+    out[(int64_t)blockIdx.x * 256 + l] = s;
+}
+
+}  // namespace
+}  // namespace lb
+
+extern "C" int lb_ceiling_stream_read(const void *buf, size_t bytes, void *out, int blocks, void *stream) {
+    if (!buf || !out || bytes < 16 || blocks <= 0 || ((uintptr_t)buf & 15) || ((uintptr_t)out & 3)) return LB_EINVAL;
+    lb::k_stream_read<<<blocks, 256, 0, (hipStream_t)stream>>>((const lb::u32x4 *)buf, (int64_t)(bytes / 16),
+                                                                (uint32_t *)out);
+    return lb::last_launch_status();
+}
+
+extern "C" int lb_ceiling_mfma_bf16(int iters, void *out, int blocks, void *stream) {
+    if (!out || iters <= 0 || blocks <= 0 || ((uintptr_t)out & 3)) return LB_EINVAL;
+    lb::k_mfma_bf16<<<blocks, 256, 0, (hipStream_t)stream>>>(iters, (float *)out);
+    return lb::last_launch_status();
+}

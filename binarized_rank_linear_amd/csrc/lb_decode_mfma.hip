@@ -90,6 +90,7 @@ template <int NL> struct Rows {
 // Per-linear schedule and workspace pointers (device-resident for groups).
 struct MLin {
     const void *x;
+    const void *x2;       // SwiGLU input: the linear reads silu(x) (.) x2 (both bf16), or null
     void *y;
     const uint32_t *v_bits, *u_bits;
     const uint16_t *g, *l, *h;
@@ -152,6 +153,9 @@ struct MRun {
     void *t_io;
     int t_dtype;
     int t_mode;
+    // inline groups: the linears themselves (no device tables; table null)
+    int ninl;
+    MLin inl[kMaxInline];
 };
 
 // Compact operands -> LDS operand layout.  Each operand holds R records of
@@ -199,8 +203,29 @@ __device__ __forceinline__ v4u load_rows(__amdgpu_buffer_rsrc_t r, uint32_t voff
 
 // The linear of a work item, as a wave-uniform value (matrix instructions
 // ignore the exec mask, so every branch around them must be uniform).
+// Launch kinds, for the inline lookup: which item offset of MLin numbers them.
+enum { kKindPrep = 0, kKindStage1 = 1, kKindLatent = 2, kKindStage2 = 3 };
+
+__device__ __forceinline__ int64_t item_start(const MLin &m, int kind) {
+    return kind == kKindPrep ? m.item0 : kind == kKindStage1 ? m.item1 : kind == kKindLatent ? m.itemF : m.item2;
+}
+
+template <int KIND>
 __device__ __forceinline__ MLin pick(const MRun &run, const MLin &single, const int32_t *map, int64_t item) {
-    MLin m = run.table ? run.table[map[item]] : single;
+    MLin m;
+    if (run.table) {
+        m = run.table[map[item]];
+    } else if (run.ninl) {
+        // inline groups: the last linear starting at or before item (constant
+        // indices only: a variable index into the kernel arguments would copy
+        // them to scratch memory)
+        m = run.inl[0];
+        static_assert(kMaxInline == 3, "inline lookup");
+        if (run.ninl > 1 && item >= item_start(run.inl[1], KIND)) m = run.inl[1];
+        if (run.ninl > 2 && item >= item_start(run.inl[2], KIND)) m = run.inl[2];
+    } else {
+        m = single;
+    }
     static_assert(sizeof(MLin) % 4 == 0, "MLin is copied as 32-bit words");
     int w[sizeof(MLin) / 4];
     __builtin_memcpy(w, &m, sizeof(MLin));
@@ -229,6 +254,9 @@ __device__ __forceinline__ int64_t item_of(const int32_t *ord, int64_t base) {
     const int64_t w = (int64_t)blockIdx.x + base;
     return ord ? (int64_t)__builtin_amdgcn_readfirstlane(ord[w]) : w;
 }
+
+// silu(z) = z / (1 + exp(-z)); -0 for very negative z, no NaN for finite z
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -407,7 +435,7 @@ __global__ __launch_bounds__(kThreads) void k_prep(MRun run, MLin single) {
     if (stale_ws(run)) return;
     using R = Rows<NL>;
     const int64_t item = (int64_t)blockIdx.x + run.base0;
-    const MLin L = pick(run, single, run.lin0, item);
+    const MLin L = pick<kKindPrep>(run, single, run.lin0, item);
     const int64_t local = item - L.item0;
     const int c = (int)(local % L.nprep);
     const int p = (int)(local / L.nprep);
@@ -437,15 +465,22 @@ __global__ __launch_bounds__(kThreads) void k_prep(MRun run, MLin single) {
             float xv[kPre];
             if (run.x_dtype == LB_BF16) {                        // uniform: one branch for all loads
                 const uint16_t *xp = (const uint16_t *)L.x + (int64_t)n * L.d_in;
-                uint16_t xb[kPre];
+                const uint16_t *x2p = L.x2 ? (const uint16_t *)L.x2 + (int64_t)n * L.d_in : xp;
+                uint16_t xb[kPre], x2b[kPre];
 #pragma unroll
                 for (int j = 0; j < kPre; ++j) {
                     const int64_t i = imin(i0 + (b0 + 8 * j + h) * 32 + el, L.d_in - 1);
                     gv[j] = gp[i];
                     xb[j] = xp[i];
+                    x2b[j] = x2p[i];
                 }
+                if (L.x2) {                                       // SwiGLU input (uniform)
 #pragma unroll
-                for (int j = 0; j < kPre; ++j) xv[j] = bf16_to_f32(xb[j]);
+                    for (int j = 0; j < kPre; ++j) xv[j] = silu(bf16_to_f32(xb[j])) * bf16_to_f32(x2b[j]);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < kPre; ++j) xv[j] = bf16_to_f32(xb[j]);
+                }
             } else {
                 const float *xp = (const float *)L.x + (int64_t)n * L.d_in;
 #pragma unroll
@@ -489,7 +524,7 @@ __global__ __launch_bounds__(kThreads) void k_stage1(MRun run, MLin single) {
     if (stale_ws(run)) return;
     using R = Rows<NL>;
     const int64_t item = item_of(run.ord1, run.base1);
-    const MLin L = pick(run, single, run.lin1, item);
+    const MLin L = pick<kKindStage1>(run, single, run.lin1, item);
     const int64_t local = item - L.item1;
     const int rg = (int)(local % L.nrg);
     const int c = (int)((local / L.nrg) % L.nchunks);
@@ -602,6 +637,17 @@ __device__ __forceinline__ void gx8_bf16(const v4u &g, const v4u &x, float (&v)[
         v[t] = gf * __uint_as_float((t & 1) ? xw & 0xffff0000u : xw << 16);
     }
 }
+// The SwiGLU input: g (.) silu(xg) (.) xu of 8 consecutive inputs (bf16 xg, xu)
+__device__ __forceinline__ void gx8_glu(const v4u &g, const v4u &xg, const v4u &xu, float (&v)[8]) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const uint32_t gw = g[t >> 1], aw = xg[t >> 1], bw = xu[t >> 1];
+        const float gf = f16_to_f32((uint16_t)((t & 1) ? gw >> 16 : gw & 0xffffu));
+        const float a = __uint_as_float((t & 1) ? aw & 0xffff0000u : aw << 16);
+        const float b = __uint_as_float((t & 1) ? bw & 0xffff0000u : bw << 16);
+        v[t] = gf * (silu(a) * b);
+    }
+}
 __device__ __forceinline__ void gx8_f32(const v4u &g, const v4u &x0, const v4u &x1, float (&v)[8]) {
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
@@ -686,8 +732,14 @@ __device__ __forceinline__ void stage1f_item(const MRun &run, const MLin &L, int
     const bool xf32 = run.x_dtype == LB_F32;
     const int xb = xf32 ? 4 : 2;
     const bool vec = L.xvec != 0;
+    const bool glu = L.x2 != nullptr;                                  // SwiGLU input (bf16 x only)
     const __amdgpu_buffer_rsrc_t rgs = make_rsrc(L.g + (int64_t)p * L.d_in, L.d_in * 2);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(L.x, (int64_t)T * L.d_in * xb);
+    // second piece of each input: the high half of fp32 x, or the up input x2
+    const __amdgpu_buffer_rsrc_t rx2 = make_rsrc(glu ? L.x2 : L.x, (int64_t)T * L.d_in * xb);
+    auto second = [&](bool ok, int64_t e) -> uint32_t {         // byte offset of element e's second piece
+        return ok && (xf32 || glu) ? (uint32_t)(xf32 ? e * 4 + 16 : e * 2) : kOOB;
+    };
     v4u gr[kPPT], xr[kPPT][2];
 #pragma unroll
     for (int j = 0; j < kPPT; ++j) {
@@ -696,7 +748,7 @@ __device__ __forceinline__ void stage1f_item(const MRun &run, const MLin &L, int
         const bool ok = vec && pc < npc && i < L.d_in;
         gr[j] = __builtin_amdgcn_raw_buffer_load_b128(rgs, ok ? (uint32_t)(i * 2) : kOOB, 0, 0);
         xr[j][0] = __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? (uint32_t)(i * xb) : kOOB, 0, 0);
-        xr[j][1] = __builtin_amdgcn_raw_buffer_load_b128(rx, ok && xf32 ? (uint32_t)(i * 4 + 16) : kOOB, 0, 0);
+        xr[j][1] = __builtin_amdgcn_raw_buffer_load_b128(rx2, second(ok, i), 0, 0);
     }
 
     // ---- first plane loads ----------------------------------------------------
@@ -747,6 +799,7 @@ __device__ __forceinline__ void stage1f_item(const MRun &run, const MLin &L, int
             const int pc = tid + j * kThreads;
             float v[8];
             if (xf32) gx8_f32(gr[j], xr[j][0], xr[j][1], v);
+            else if (glu) gx8_glu(gr[j], xr[j][0], xr[j][1], v);
             else gx8_bf16(gr[j], xr[j][0], v);
             emit_piece<NL>(v, rec_of(pc, 0), (pc >> 2) & 3, pc & 3, pc < npc);
         }
@@ -756,11 +809,12 @@ __device__ __forceinline__ void stage1f_item(const MRun &run, const MLin &L, int
                 const int pc = tid + j * kThreads;
                 const int64_t i = i_chunk + (int64_t)pc * 8;
                 const bool in = pc < npc && i < L.d_in;
-                const int64_t xo = ((int64_t)n * L.d_in + i) * xb;
-                const v4u x0 = __builtin_amdgcn_raw_buffer_load_b128(rx, in ? (uint32_t)xo : kOOB, 0, 0);
-                const v4u x1 = __builtin_amdgcn_raw_buffer_load_b128(rx, in && xf32 ? (uint32_t)(xo + 16) : kOOB, 0, 0);
+                const int64_t e = (int64_t)n * L.d_in + i;
+                const v4u x0 = __builtin_amdgcn_raw_buffer_load_b128(rx, in ? (uint32_t)(e * xb) : kOOB, 0, 0);
+                const v4u x1 = __builtin_amdgcn_raw_buffer_load_b128(rx2, second(in, e), 0, 0);
                 float v[8];
                 if (xf32) gx8_f32(gr[j], x0, x1, v);
+                else if (glu) gx8_glu(gr[j], x0, x1, v);
                 else gx8_bf16(gr[j], x0, v);
                 emit_piece<NL>(v, rec_of(pc, n), (pc >> 2) & 3, pc & 3, pc < npc);
             }
@@ -778,8 +832,9 @@ __device__ __forceinline__ void stage1f_item(const MRun &run, const MLin &L, int
                     const uint32_t go = in ? (uint32_t)((i + t) * 2) : kOOB;
                     const uint32_t xo = in ? (uint32_t)(((int64_t)n * L.d_in + i + t) * xb) : kOOB;
                     const float gf = f16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rgs, go, 0, 0));
-                    const float xf = xf32 ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rx, xo, 0, 0))
-                                          : bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rx, xo, 0, 0));
+                    float xf = xf32 ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rx, xo, 0, 0))
+                                    : bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rx, xo, 0, 0));
+                    if (glu) xf = silu(xf) * bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rx2, xo, 0, 0));
                     v[t] = gf * xf;
                 }
                 emit_piece<NL>(v, rec_of(pc, n), (pc >> 2) & 3, pc & 3, pc < npc);
@@ -861,7 +916,7 @@ __global__ __launch_bounds__(kThreads) void k_stage1f(MRun run, MLin single) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     if (stale_ws(run)) return;
     const int64_t item = item_of(run.ord1, run.base1);
-    stage1f_item<NL, false>(run, pick(run, single, run.lin1, item), item, smem);
+    stage1f_item<NL, false>(run, pick<kKindStage1>(run, single, run.lin1, item), item, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -1066,7 +1121,7 @@ __global__ __launch_bounds__(kThreads) void k_latent(MRun run, MLin single) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     if (stale_ws(run)) return;
     const int64_t item = (int64_t)blockIdx.x + run.baseF;
-    const MLin L = pick(run, single, run.linF, item);
+    const MLin L = pick<kKindLatent>(run, single, run.linF, item);
     const int kg_first = (int)(item - L.itemF) * 2;               // 2 K-groups = 8 planes per item
     latent_item<NL, NB2>(run, L, kg_first, (int)imin(2, L.kgs - kg_first), smem);
 }
@@ -1084,7 +1139,7 @@ __global__ __launch_bounds__(kThreads) void k_stage2(MRun run, MLin single) {
     if (stale_ws(run)) return;
     using R = Rows<NL>;
     const int64_t item = item_of(run.ord2, run.base2);
-    const MLin L = pick(run, single, run.lin2, item);
+    const MLin L = pick<kKindStage2>(run, single, run.lin2, item);
     const int64_t local = item - L.item2;
     const int T = run.T;
     const int lane = threadIdx.x & 63, wave = wave_id();
@@ -1448,7 +1503,7 @@ __global__ __launch_bounds__(kThreads) void k_stage2r(MRun run, MLin single) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     if (stale_ws(run)) return;
     const int64_t item = item_of(run.ord2, run.base2);
-    const MLin L = pick(run, single, run.lin2, item);
+    const MLin L = pick<kKindStage2>(run, single, run.lin2, item);
     const int64_t row_begin = (item - L.item2) * L.rows2;
     const int tiles = (int)imin(L.rows2 / kRG, cdiv(L.d_out - row_begin, kRG));
     stage2r_item<NL, NB2, false>(run, L, row_begin, tiles, smem, nullptr);
@@ -1493,7 +1548,7 @@ __global__ __launch_bounds__(kThreads) void k_pass(MRun run, MLin single) {
     if (b < run.items1) {
         const int64_t item = __builtin_amdgcn_readfirstlane(run.ordP1[b]);
         const int j = run.table ? __builtin_amdgcn_readfirstlane(run.lin1[item]) : 0;
-        const MLin L = pick(run, single, run.lin1, item);
+        const MLin L = pick<kKindStage1>(run, single, run.lin1, item);
         stage1f_item<NL, true>(run, L, item, smem);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // this wave's partial sums are stored
         __syncthreads();
@@ -1598,6 +1653,7 @@ struct Grain {
 size_t plan_linear(const Linear &a, const Shape &s, bool many, MLin *m, Grain gr = Grain{}) {
     *m = MLin{};
     m->x = a.x;
+    m->x2 = a.x2;
     m->y = a.y;
     m->v_bits = a.v_bits;
     m->u_bits = a.u_bits;
@@ -1630,7 +1686,8 @@ size_t plan_linear(const Linear &a, const Shape &s, bool many, MLin *m, Grain gr
         m->nrg = (int32_t)cdiv(cdiv(a.r_p, kTile), flush1_for(a.T, gr.tsplit));
         m->kcp = 0;
         m->nprep = 0;
-        m->xvec = (a.d_in % 8 == 0 && ((uintptr_t)a.x & 15) == 0 && ((uintptr_t)a.g & 15) == 0) ? 1 : 0;
+        m->xvec = (a.d_in % 8 == 0 && ((uintptr_t)a.x & 15) == 0 && ((uintptr_t)a.x2 & 15) == 0 &&
+                   ((uintptr_t)a.g & 15) == 0) ? 1 : 0;
     } else {
         int kcg = kcg_cap(s);
         if (!many)   // a lone linear: smaller chunks until the chip has work
@@ -2171,6 +2228,70 @@ int mfma_group_run(const void *host_state, hipStream_t st, int stage_mask) {
     }
     MLin dummy{};
     return launch_shape(hs->s, hs->run, dummy, hs->lds, st, stage_mask);
+}
+
+// ---- inline groups -----------------------------------------------------------
+
+namespace {
+// The schedule of up to kMaxInline linears in the kernel arguments; returns
+// the workspace bytes (each linear's scratch, back to back).
+size_t inline_setup(const Linear *ls, int n, uint8_t *ws, Shape *s, MRun *run, Lds *lds) {
+    *run = MRun{};
+    *lds = Lds{};
+    if (n < 1 || n > kMaxInline || !shape_for(ls[0].T, ls[0].y_dtype, s)) return 0;
+    const Grain gr = group_grain(ls, n, *s);
+    size_t off = 0;
+    int64_t i0 = 0, i1 = 0, iF = 0, i2 = 0;
+    int steps_max = 1;
+    int64_t ntile_max = 1;
+    for (int j = 0; j < n; ++j) {
+        MLin &m = run->inl[j];
+        const size_t b = plan_linear(ls[j], *s, true, &m, gr);
+        if (ws) bind_ws(&m, ls[j], *s, ws + off);
+        off += b;
+        m.item0 = i0;
+        m.item1 = i1;
+        m.itemF = iF;
+        m.item2 = i2;
+        i0 += items0_of(m);
+        i1 += items1_of(m);
+        iF += itemsF_of(m);
+        i2 += m.n2;
+        steps_max = (int)imax(steps_max, m.kgs);
+        ntile_max = imax(ntile_max, cdiv(m.r_p, kTile));
+    }
+    run->ninl = n;
+    run->T = (int)ls[0].T;
+    run->x_dtype = ls[0].x_dtype;
+    run->y_dtype = ls[0].y_dtype;
+    run->dma2 = dma2_for(*s, ls[0].T, steps_max);
+    run->ystage = ystage_for(ls[0].T, ls[0].y_dtype);
+    run->ops2 = run->dma2 ? steps_max : ops2_for(*s, steps_max);
+    run->items0 = i0;
+    run->items1 = i1;
+    run->itemsF = iF;
+    run->items2 = i2;
+    run->tsplit = gr.tsplit;
+    run->flush1 = (int)imin(flush1_for(ls[0].T, run->tsplit), ntile_max);
+    for (int j = 0; j < n; ++j) lds_add(lds, run->inl[j], *s, run->ops2, ls[0].T, run->flush1, run->tsplit);
+    return off;
+}
+}  // namespace
+
+size_t mfma_inline_workspace_bytes(const Linear *ls, int n) {
+    Shape s;
+    MRun run;
+    Lds lds;
+    return inline_setup(ls, n, nullptr, &s, &run, &lds);
+}
+
+int mfma_inline_forward(const Linear *ls, int n, void *ws, hipStream_t st) {
+    Shape s;
+    MRun run;
+    Lds lds;
+    if (inline_setup(ls, n, (uint8_t *)ws, &s, &run, &lds) == 0) return LB_EUNSUPPORTED;
+    MLin dummy{};
+    return launch_shape(s, run, dummy, lds, st);
 }
 
 // ---- the fault word ----------------------------------------------------------

@@ -17,6 +17,9 @@ namespace lb {
 struct Linear {
     const void *x;
     void *y;
+    // SwiGLU input (decode kernels, bf16 x only): when set, the linear's input
+    // is silu(x) (.) x2 elementwise, x2 [T][d_in] bf16
+    const void *x2 = nullptr;
     int x_dtype, y_dtype;
     const uint32_t *v_bits;   // [P][kw_v][ld_v]
     const uint32_t *u_bits;   // [P][kw_u][ld_u]
@@ -98,6 +101,12 @@ bool mfma_decode_supported(int64_t T, int y_dtype);
 bool mfma_decode_shape_ok(const Linear &a);
 size_t mfma_decode_workspace_bytes(const Linear &a);
 int mfma_decode_forward(const Linear &a, void *ws, hipStream_t s);
+// Up to kMaxInline linears (same T and dtypes) in one three-launch run, with
+// their schedule in the kernel arguments instead of device tables: nothing to
+// set up, so a stateless call can use it.
+constexpr int kMaxInline = 3;
+size_t mfma_inline_workspace_bytes(const Linear *ls, int n);
+int mfma_inline_forward(const Linear *ls, int n, void *ws, hipStream_t s);
 // Groups of independent linears on the matrix-core decode path.
 size_t mfma_group_workspace_bytes(const Linear *ls, int n, int64_t T, int y_dtype);
 size_t mfma_group_state_bytes();

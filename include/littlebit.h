@@ -351,6 +351,21 @@ int lb_grouped_release(void *ws);
  * linear. */
 int lb_grouped_run_stage(void *ws, int stage, void *stream);
 
+/* ---- measured ceilings (measurement helpers; no part of the layer) ---- */
+
+/* A streaming read of bytes (>= 16; buf 16-byte aligned, device) by `blocks`
+ * workgroups of 256 threads, 16-byte non-temporal loads with 8 in flight per
+ * thread: the HBM read rate a decode sign stream can reach.  out (device)
+ * receives one uint32_t per workgroup (the XOR of what it read).  Enqueued
+ * on stream; time it with events.  LB_EINVAL on bad arguments. */
+int lb_ceiling_stream_read(const void *buf, size_t bytes, void *out, int blocks, void *stream);
+
+/* `blocks` workgroups of 4 waves, each wave issuing iters x 8 independent
+ * v_mfma_f32_32x32x16_bf16 (32768 flops each) on register operands: the
+ * bf16 matrix rate the prefill GEMMs can reach.  out (device) receives
+ * blocks * 256 floats.  Enqueued on stream.  LB_EINVAL on bad arguments. */
+int lb_ceiling_mfma_bf16(int iters, void *out, int blocks, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

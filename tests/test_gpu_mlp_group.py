@@ -33,6 +33,25 @@ def test_config2_mlp_block(T, path):
     assert_close(y_to_np(y), ref, TOL["bf16"], ("mlp", T, path))
 
 
+@pytest.mark.parametrize("d_model,d_ff,T", [(520, 1100, 1), (520, 1100, 7), (520, 1100, 12), (1024, 2048, 2),
+                                             (1024, 2048, 30), (96, 40, 5)])
+def test_mlp_fused_swiglu_ragged(d_model, d_ff, T):
+    """The fused decode form of the block (bf16 out): gate and up as one
+    group writing bf16, down reading silu(gate) * up as it stages its input,
+    on widths that are not multiples of 8 (input by input) and on aligned
+    ones, through the fused (T <= 8) and the separate (T > 8) stage-1 forms."""
+    torch = torch_or_skip()
+    import binarized_rank_linear_amd as lb
+    g = synth.layer_inputs(700 + d_ff, d_model, d_ff, 48, 2)
+    u = synth.layer_inputs(701 + d_ff, d_model, d_ff, 48, 2)
+    d = synth.layer_inputs(702 + d_ff, d_ff, d_model, 32, 2)
+    x = synth.activations(703 + T, T, d_model, "bf16")
+    say("mlp fused", d_model, d_ff, "T", T)
+    y = lb.mlp_forward(x_to_dev(x), dev_layer(g), dev_layer(u), dev_layer(d), torch.bfloat16)
+    torch.cuda.synchronize()
+    assert_close(y_to_np(y), oracle.mlp_forward(x, g, u, d), TOL["bf16"], ("mlp fused", d_model, d_ff, T))
+
+
 def test_mlp_prefill_sampled():
     torch = torch_or_skip()
     import binarized_rank_linear_amd as lb
