@@ -234,7 +234,8 @@ def ceilings():
     torch.cuda.empty_cache()
     return {"stream_read_GBs": gbs, "stream_read_frac": gbs / HBM_PEAK_GBS,
             "mfma_bf16_TFLOPs": tfl, "mfma_bf16_frac": tfl / BF16_PEAK_TFLOPS,
-            "how": "2 GiB read by 2048 workgroups, 16-byte non-temporal loads, 8 in flight; "
+            "how": "2 GiB read by 2048 workgroups (a contiguous share each), 16-byte non-temporal loads, "
+                   "8 in flight per thread; "
                    "1024 workgroups x 4 waves x %d x 8 independent v_mfma_f32_32x32x16_bf16" % iters}
 
 

@@ -55,6 +55,14 @@ class lb_linear_call(ctypes.Structure):
                 ("y_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
 
 
+class lb_decoder_layer(ctypes.Structure):
+    _fields_ = [("q", lb_factors), ("k", lb_factors), ("v", lb_factors), ("o", lb_factors),
+                ("gate", lb_factors), ("up", lb_factors), ("down", lb_factors),
+                ("d_model", _i64), ("d_ff", _i64), ("n_heads", _i64), ("n_kv_heads", _i64),
+                ("r_qo", _i64), ("r_kv", _i64), ("r_gu", _i64), ("r_down", _i64),
+                ("residual", ctypes.c_int32), ("eps", ctypes.c_float)]
+
+
 class LBError(RuntimeError):
     def __init__(self, status: int, what: str):
         super().__init__("%s failed: %s (%d)" % (what, status_string(status), status))
@@ -137,6 +145,10 @@ def lib() -> ctypes.CDLL:
         L.lb_linear_stage2.argtypes = [_vp, ctypes.c_int, _vp, ctypes.c_int, ctypes.POINTER(lb_factors),
                                        _i64, _i64, _i64, _i64, ctypes.c_int, _vp, _sz, ctypes.c_uint, _vp]
         L.lb_linear_stage2.restype = ctypes.c_int
+        L.lb_decoder_layer_workspace_bytes.argtypes = [ctypes.POINTER(lb_decoder_layer), _i64]
+        L.lb_decoder_layer_workspace_bytes.restype = _sz
+        L.lb_decoder_layer_forward.argtypes = [ctypes.POINTER(lb_decoder_layer), _vp, _vp, _i64, _vp, _sz, _vp]
+        L.lb_decoder_layer_forward.restype = ctypes.c_int
         L.lb_ceiling_stream_read.argtypes = [_vp, _sz, _vp, ctypes.c_int, _vp]
         L.lb_ceiling_stream_read.restype = ctypes.c_int
         L.lb_ceiling_mfma_bf16.argtypes = [ctypes.c_int, _vp, ctypes.c_int, _vp]
@@ -409,6 +421,39 @@ def mlp_forward(x, gate: PackedLinear, up: PackedLinear, down: PackedLinear, out
                                 int(gate.residual), ws.data_ptr(), ws.numel(), flags,
                                 _stream_ptr(stream)), "lb_mlp_forward")
     return out
+
+
+class DecoderLayer:
+    """One decoder layer at decode time (lb_decoder_layer_forward): pre-norm
+    attention over a one-token context with q, k, v, o LittleBit linears, then
+    a LittleBit SwiGLU MLP, both with residuals.  bf16 in and out."""
+
+    def __init__(self, q, k, v, o, gate, up, down, n_heads: int, n_kv_heads: int, eps: float = 1e-6):
+        self.lin = dict(q=q, k=k, v=v, o=o, gate=gate, up=up, down=down)
+        self.d_model, self.d_ff = q.d_in, gate.d_out
+        self.n_heads, self.n_kv_heads, self.eps = n_heads, n_kv_heads, eps
+        self.desc = lb_decoder_layer(q.struct(), k.struct(), v.struct(), o.struct(), gate.struct(),
+                                     up.struct(), down.struct(), q.d_in, gate.d_out, n_heads, n_kv_heads,
+                                     q.r, k.r, gate.r, down.r, int(q.residual), eps)
+
+    def workspace_bytes(self, T: int) -> int:
+        return lib().lb_decoder_layer_workspace_bytes(ctypes.byref(self.desc), T)
+
+    def forward(self, x, out=None, ws=None, stream=None):
+        torch = _torch()
+        _dev_check(x)
+        T = x.shape[0]
+        if x.dtype != torch.bfloat16 or x.shape != (T, self.d_model):
+            raise ValueError("x must be bf16 [T][d_model]")
+        if out is None:
+            out = torch.empty_like(x)
+        need = self.workspace_bytes(T)
+        if ws is None or ws.numel() < need:
+            ws = workspace(max(need, 1), x.device)
+        _check(lib().lb_decoder_layer_forward(ctypes.byref(self.desc), x.data_ptr(), out.data_ptr(), T,
+                                              ws.data_ptr(), ws.numel(), _stream_ptr(stream)),
+               "lb_decoder_layer_forward")
+        return out
 
 
 def device_faults(stream=None) -> int:

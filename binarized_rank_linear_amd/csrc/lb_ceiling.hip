@@ -12,21 +12,23 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// Every workgroup reads 16-byte pieces i = blockIdx.x * 256 + threadIdx.x,
-// stepping by the grid, 8 loads in flight per thread; the XOR of everything
-// read goes to out[blockIdx.x] so no load can be dropped.
+// Workgroup b reads its own contiguous 1/gridDim share of the buffer, 4 KB
+// per step (256 threads x 16 bytes), 8 steps in flight per thread; the XOR of
+// everything read goes to out[b] so no load can be dropped.
 __global__ __launch_bounds__(256) void k_stream_read(const u32x4 *__restrict__ p, int64_t n16, uint32_t *out) {
-    const int64_t stride = (int64_t)gridDim.x * 256;
+    const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+    const int64_t b0 = (int64_t)blockIdx.x * per;
+    const int64_t b1 = b0 + per < n16 ? b0 + per : n16;
     u32x4 acc = {0u, 0u, 0u, 0u};
-    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    for (; i + 7 * stride < n16; i += 8 * stride) {
+    int64_t i = b0 + threadIdx.x;
+    for (; i + 7 * 256 < b1; i += 8 * 256) {
         u32x4 v[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = __builtin_nontemporal_load(p + i + k * stride);
+        for (int k = 0; k < 8; ++k) v[k] = __builtin_nontemporal_load(p + i + k * 256);
 #pragma unroll
         for (int k = 0; k < 8; ++k) acc ^= v[k];
     }
-    for (; i < n16; i += stride) acc ^= p[i];
+    for (; i < b1; i += 256) acc ^= p[i];
     const uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
     __shared__ uint32_t s[256];
     s[threadIdx.x] = x;

@@ -91,6 +91,8 @@ template <int NL> struct Rows {
 struct MLin {
     const void *x;
     const void *x2;       // SwiGLU input: the linear reads silu(x) (.) x2 (both bf16), or null
+    const float *xs;      // per-token input scale [T] (an RMSNorm's 1/rms), or null
+    const void *resid;    // residual [T][d_out] in y's dtype, added to the output, or null
     void *y;
     const uint32_t *v_bits, *u_bits;
     const uint16_t *g, *l, *h;
@@ -129,6 +131,7 @@ struct MRun {
     int flush1;                // fused stage 1: latent tiles per item (F)
     int tsplit;                // fused stage 1: waves split the item's tiles (1) or its K-groups (0)
     int ystage;                // k_stage2r collects the item's outputs in LDS, stored after its stream
+    int yst;                   // bytes per collected output: y's size, or 4 when a residual is added
     int64_t items0, items1, itemsF, items2;
     int64_t base0, base1, baseF, base2;   // item of workgroup 0 in each launch (0: all items)
     const MLin *table;         // null: the single linear passed by value
@@ -490,6 +493,11 @@ __global__ __launch_bounds__(kThreads) void k_prep(MRun run, MLin single) {
                     xv[j] = xp[i];
                 }
             }
+            if (L.xs) {                                           // uniform
+                const float sc = L.xs[n];
+#pragma unroll
+                for (int j = 0; j < kPre; ++j) xv[j] *= sc;
+            }
 #pragma unroll
             for (int j = 0; j < kPre; ++j) {
                 const int blk = b0 + 8 * j + h;
@@ -801,6 +809,11 @@ __device__ __forceinline__ void stage1f_item(const MRun &run, const MLin &L, int
             if (xf32) gx8_f32(gr[j], xr[j][0], xr[j][1], v);
             else if (glu) gx8_glu(gr[j], xr[j][0], xr[j][1], v);
             else gx8_bf16(gr[j], xr[j][0], v);
+            if (L.xs) {                                         // uniform
+                const float sc = L.xs[0];
+#pragma unroll
+                for (int t = 0; t < 8; ++t) v[t] *= sc;
+            }
             emit_piece<NL>(v, rec_of(pc, 0), (pc >> 2) & 3, pc & 3, pc < npc);
         }
         for (int n = 1; n < T; ++n) {
@@ -816,6 +829,11 @@ __device__ __forceinline__ void stage1f_item(const MRun &run, const MLin &L, int
                 if (xf32) gx8_f32(gr[j], x0, x1, v);
                 else if (glu) gx8_glu(gr[j], x0, x1, v);
                 else gx8_bf16(gr[j], x0, v);
+                if (L.xs) {                                     // uniform
+                    const float sc = L.xs[n];
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) v[t] *= sc;
+                }
                 emit_piece<NL>(v, rec_of(pc, n), (pc >> 2) & 3, pc & 3, pc < npc);
             }
         }
@@ -836,6 +854,7 @@ __device__ __forceinline__ void stage1f_item(const MRun &run, const MLin &L, int
                                     : bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rx, xo, 0, 0));
                     if (glu) xf = silu(xf) * bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rx2, xo, 0, 0));
                     v[t] = gf * xf;
+                    if (L.xs) v[t] *= L.xs[n];
                 }
                 emit_piece<NL>(v, rec_of(pc, n), (pc >> 2) & 3, pc & 3, pc < npc);
             }
@@ -1264,6 +1283,11 @@ __global__ __launch_bounds__(kThreads) void k_stage2(MRun run, MLin single) {
                 }
                 const int n = b * R::TPM2 + (NL == 2 ? gq : gq / 2);
                 const bool writer = n < T && (NL == 2 || (gq & 1) == 0);
+                if (L.resid && writer) {                        // (uniform pointer) the residual
+#pragma unroll
+                    for (int m = 0; m < 4; ++m)
+                        if (row + m < L.d_out) y4[m] += load_act(L.resid, run.y_dtype, (int64_t)n * L.d_out + row + m);
+                }
                 store4(ob, (int64_t)n * L.d_out + row, row, L.d_out, y4, writer);
             }
 #pragma unroll
@@ -1314,6 +1338,7 @@ __device__ __forceinline__ void stage2r_item(const MRun &run, const MLin &L, int
     // wait would also wait for their acknowledgements
     uint8_t *ys = (uint8_t *)(hs + 2 * kHRows);
     const int yb = run.y_dtype == LB_BF16 ? 2 : 4;
+    const int ysb = run.yst;                                      // bytes per collected output
 
     // operands and h first, as buffer loads (counted precisely, so the LDS
     // fill below waits for these only, not for the plane loads behind them)
@@ -1440,13 +1465,18 @@ __device__ __forceinline__ void stage2r_item(const MRun &run, const MLin &L, int
                 const bool writer = n < T && (NL == 2 || (gq & 1) == 0);
                 if (run.ystage) {                               // uniform
                     if (writer) {
-                        uint8_t *yp = ys + ((size_t)n * kHRows + rl) * yb;
-                        if (yb == 2)
+                        uint8_t *yp = ys + ((size_t)n * kHRows + rl) * ysb;
+                        if (ysb == 2)
                             *(v2u *)yp = v2u{bf16_pair(y4[0], y4[1]), bf16_pair(y4[2], y4[3])};
                         else
                             *(v4f *)yp = v4f{y4[0], y4[1], y4[2], y4[3]};
                     }
                 } else {
+                    if (L.resid && writer) {                    // (uniform pointer) the residual, unrounded sum
+#pragma unroll
+                        for (int m = 0; m < 4; ++m)
+                            if (row + m < L.d_out) y4[m] += load_act(L.resid, run.y_dtype, (int64_t)n * L.d_out + row + m);
+                    }
                     store4(ob, (int64_t)n * L.d_out + row, row, L.d_out, y4, writer);
                 }
             }
@@ -1475,11 +1505,43 @@ __device__ __forceinline__ void stage2r_item(const MRun &run, const MLin &L, int
         const int per = 16 / yb;                                   // outputs per chunk
         const bool chunky = ob.vec && (L.d_out % per) == 0 && ((uintptr_t)L.y & 15) == 0;
         const int cpr = (int)cdiv(rows, per);                      // chunks per token row
+        // a residual (same dtype and layout as y) is added to the unrounded
+        // fp32 outputs, which are then collected at 4 bytes each
+        const __amdgpu_buffer_rsrc_t rres = make_rsrc(L.resid, (int64_t)T * L.d_out * yb);
         for (int c = threadIdx.x; c < T * cpr; c += kThreads) {
             const int n = c / cpr, k = c - n * cpr;
             const int64_t r0 = (int64_t)k * per;                   // row within the item
-            const v4u w = *(const v4u *)(ys + ((size_t)n * kHRows + r0) * yb);
             const int64_t e0 = (int64_t)n * L.d_out + row_begin + r0;
+            v4u w;
+            if (ysb == yb && !L.resid) {                           // uniform
+                w = *(const v4u *)(ys + ((size_t)n * kHRows + r0) * yb);
+            } else {
+                // fp32 collected; add the residual, then y's dtype
+                float f[8];
+#pragma unroll
+                for (int q = 0; q < 8; q += 4) {
+                    if (q >= per) break;
+                    const v4f a = *(const v4f *)(ys + ((size_t)n * kHRows + r0 + q) * 4);
+                    f[q] = a[0];
+                    f[q + 1] = a[1];
+                    f[q + 2] = a[2];
+                    f[q + 3] = a[3];
+                }
+                if (L.resid) {
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        if (q >= per) break;
+                        const bool ok = r0 + q < rows;
+                        const uint32_t ro = ok ? (uint32_t)((e0 + q) * yb) : kOOB;
+                        f[q] += yb == 2 ? bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rres, ro, 0, 0))
+                                        : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rres, ro, 0, 0));
+                    }
+                }
+                if (yb == 2)
+                    w = v4u{bf16_pair(f[0], f[1]), bf16_pair(f[2], f[3]), bf16_pair(f[4], f[5]), bf16_pair(f[6], f[7])};
+                else
+                    w = v4u{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3])};
+            }
             if (chunky) {
                 __builtin_amdgcn_raw_buffer_store_b128(w, ob.r, r0 + per <= rows ? (uint32_t)(e0 * yb) : kOOB, 0, 0);
             } else {
@@ -1627,8 +1689,14 @@ bool tsplit_for(const Linear *ls, int n) {
 // Whether stage 2 can run k_stage2r: every step's operands and h of an item
 // fit the LDS of one CU (two workgroups' worth when possible).
 // k_stage2r collects an item's outputs in LDS when they fit kYStage.
-int ystage_for(int64_t T, int y_dtype) {
-    return (size_t)T * kHRows * (y_dtype == LB_BF16 ? 2 : 4) <= (size_t)kYStage ? 1 : 0;
+int ystage_for(int64_t T, int yst) { return (size_t)T * kHRows * yst <= (size_t)kYStage ? 1 : 0; }
+
+// Bytes per collected stage-2 output: y's size, or 4 when any linear of the
+// launch adds a residual (it is added to the unrounded sum).
+int yst_for(const Linear *ls, int n, int y_dtype) {
+    for (int j = 0; j < n; ++j)
+        if (ls[j].resid) return 4;
+    return y_dtype == LB_BF16 ? 2 : 4;
 }
 
 bool dma2_for(const Shape &s, int64_t T, int steps_max) {
@@ -1654,6 +1722,8 @@ size_t plan_linear(const Linear &a, const Shape &s, bool many, MLin *m, Grain gr
     *m = MLin{};
     m->x = a.x;
     m->x2 = a.x2;
+    m->xs = a.xs;
+    m->resid = a.resid;
     m->y = a.y;
     m->v_bits = a.v_bits;
     m->u_bits = a.u_bits;
@@ -1760,7 +1830,7 @@ int launch_all(const MRun &run, const MLin &single, const Lds &lds, hipStream_t 
     if ((stage_mask & 2) && run.items2 <= 0) return LB_OK;
     if ((stage_mask & 2) && run.dma2) {
         const size_t l2 = ops2r_bytes(run.ops2, NB2, rows2(Shape{NL, NB1, NB2}, run.T)) + 2 * kHRows * 2 +
-                          (run.ystage ? (size_t)run.T * kHRows * (run.y_dtype == LB_BF16 ? 2 : 4) : 0);
+                          (run.ystage ? (size_t)run.T * kHRows * run.yst : 0);
         if (l2 > 160 * 1024) return LB_EUNSUPPORTED;
         static bool raised = false;        // once per instantiation (idempotent if raced)
         if (!raised) {
@@ -1872,7 +1942,8 @@ int single_setup(const Linear &a, void *ws, Shape *s, MLin *m, MRun *run, Lds *l
     run->x_dtype = a.x_dtype;
     run->y_dtype = a.y_dtype;
     run->dma2 = dma2_for(*s, a.T, m->kgs);
-    run->ystage = ystage_for(a.T, a.y_dtype);
+    run->yst = yst_for(&a, 1, a.y_dtype);
+    run->ystage = ystage_for(a.T, run->yst);
     run->ops2 = run->dma2 ? m->kgs : ops2_for(*s, m->kgs);
     run->items0 = items0_of(*m);
     run->items1 = items1_of(*m);
@@ -2070,7 +2141,8 @@ int mfma_group_plan(const Linear *ls, int n, int64_t T, int y_dtype, void *ws, s
     MRun &run = hs->run;
     run = MRun{};
     run.dma2 = dma2_for(hs->s, T, steps_max);
-    run.ystage = ystage_for(T, y_dtype);
+    run.yst = yst_for(ls, n, y_dtype);
+    run.ystage = ystage_for(T, run.yst);
     run.ops2 = run.dma2 ? steps_max : ops2_for(hs->s, steps_max);
     hs->lds = Lds{};
     int64_t ntile_max = 1;
@@ -2183,7 +2255,7 @@ int mfma_group_plan(const Linear *ls, int n, int64_t T, int y_dtype, void *ws, s
     hs->lds_pass = 0;
     if (run.pass) {
         const size_t l2 = ops2r_bytes(run.ops2, hs->s.NB2, rows2(hs->s, T)) + 2 * kHRows * 2 +
-                          (run.ystage ? (size_t)T * kHRows * (y_dtype == LB_BF16 ? 2 : 4) : 0);
+                          (run.ystage ? (size_t)T * kHRows * run.yst : 0);
         // a latent group's (token, plane) units staged as NL records each
         const size_t lat = (size_t)T * run.flush1 * 2 * hs->s.NL * kRec;
         hs->lds_pass = std::max(std::max(hs->lds.s1, lat), l2);
@@ -2265,7 +2337,8 @@ size_t inline_setup(const Linear *ls, int n, uint8_t *ws, Shape *s, MRun *run, L
     run->x_dtype = ls[0].x_dtype;
     run->y_dtype = ls[0].y_dtype;
     run->dma2 = dma2_for(*s, ls[0].T, steps_max);
-    run->ystage = ystage_for(ls[0].T, ls[0].y_dtype);
+    run->yst = yst_for(ls, n, ls[0].y_dtype);
+    run->ystage = ystage_for(ls[0].T, run->yst);
     run->ops2 = run->dma2 ? steps_max : ops2_for(*s, steps_max);
     run->items0 = i0;
     run->items1 = i1;

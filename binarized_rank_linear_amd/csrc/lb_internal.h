@@ -20,6 +20,10 @@ struct Linear {
     // SwiGLU input (decode kernels, bf16 x only): when set, the linear's input
     // is silu(x) (.) x2 elementwise, x2 [T][d_in] bf16
     const void *x2 = nullptr;
+    // decode kernels only: a per-token scale of the input ([T] fp32: an
+    // RMSNorm's 1/rms), and a residual [T][d_out] (y's dtype) added to y
+    const float *xs = nullptr;
+    const void *resid = nullptr;
     int x_dtype, y_dtype;
     const uint32_t *v_bits;   // [P][kw_v][ld_v]
     const uint32_t *u_bits;   // [P][kw_u][ld_u]

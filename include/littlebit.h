@@ -231,6 +231,40 @@ int lb_linear_stage2(const void *t, int t_dtype, void *y, int y_dtype, const lb_
                      int64_t d_in, int64_t d_out, int64_t r, int64_t T, int residual,
                      void *ws, size_t ws_bytes, unsigned flags, void *stream);
 
+/* One decoder layer of a model whose seven linears are LittleBit linears
+ * (the model architecture is otherwise unchanged: littlebitllm page, hero;
+ * deniz.in, "Factorize first, then binarize"), at decode time, minus
+ * attention over a KV cache.  Pre-norm (the Llama / Qwen layout):
+ *     a = x / rms(x);  q, k, v = Q(a), K(a), V(a)
+ *     o_in = v with each kv head serving its group of n_heads / n_kv_heads
+ *            query heads (attention over a context of one token)
+ *     x1 = x + O(o_in);  b = x1 / rms(x1)
+ *     y = x1 + Down(silu(Gate(b)) (.) Up(b))
+ * rms(x) = sqrt(mean(x^2) + eps) per token; the RMSNorms' per-channel weights
+ * are folded into the g of the linears they feed (g scales the same input
+ * channels).  q and k are computed (they cost what they cost) but, with one
+ * token of context, do not change o_in.  Shapes: q, o d_model x d_model (total
+ * rank r_qo); k, v d_model -> d_model / n_heads * n_kv_heads (r_kv); gate, up
+ * d_model -> d_ff (r_gu); down d_ff -> d_model (r_down); `residual` gives
+ * every linear the residual path.  x, y: bf16 [T][d_model] device, 16-byte
+ * aligned, not overlapping; 0 <= T <= 32 (the decode kernels;
+ * LB_EUNSUPPORTED beyond; T = 0 checks the layer and does nothing; the
+ * workspace query returns 0 for it and for bad arguments).  Runs 15 launches on `stream` (2 norms, q/k/v as
+ * one group, the head expansion, o, gate/up as one group, down), with every
+ * intermediate in ws (>= lb_decoder_layer_workspace_bytes, 256-byte aligned,
+ * no contents needed).  Layers chain by passing one's y as the next one's x. */
+typedef struct lb_decoder_layer {
+    lb_factors q, k, v, o, gate, up, down;
+    int64_t d_model, d_ff, n_heads, n_kv_heads;
+    int64_t r_qo, r_kv, r_gu, r_down;
+    int32_t residual;
+    float eps;
+} lb_decoder_layer;
+
+size_t lb_decoder_layer_workspace_bytes(const lb_decoder_layer *layer, int64_t T);
+int lb_decoder_layer_forward(const lb_decoder_layer *layer, const void *x, void *y, int64_t T,
+                             void *ws, size_t ws_bytes, void *stream);
+
 /* Workspace bytes lb_mlp_forward needs.  0 on bad arguments. */
 size_t lb_mlp_workspace_bytes(int64_t d_model, int64_t d_ff, int64_t r_gu, int64_t r_down,
                               int64_t T, int residual, unsigned flags);
@@ -354,8 +388,9 @@ int lb_grouped_run_stage(void *ws, int stage, void *stream);
 /* ---- measured ceilings (measurement helpers; no part of the layer) ---- */
 
 /* A streaming read of bytes (>= 16; buf 16-byte aligned, device) by `blocks`
- * workgroups of 256 threads, 16-byte non-temporal loads with 8 in flight per
- * thread: the HBM read rate a decode sign stream can reach.  out (device)
+ * workgroups of 256 threads, each reading a contiguous share with 16-byte
+ * non-temporal loads, 8 in flight per thread: the HBM read rate a decode sign
+ * stream can reach.  out (device)
  * receives one uint32_t per workgroup (the XOR of what it read).  Enqueued
  * on stream; time it with events.  LB_EINVAL on bad arguments. */
 int lb_ceiling_stream_read(const void *buf, size_t bytes, void *out, int blocks, void *stream);

@@ -229,6 +229,69 @@ def mlp_forward(x: np.ndarray, gate, up, down, nthreads: int = 0) -> np.ndarray:
     return y
 
 
+# ----------------------------------------------------------------------------
+# one decoder layer at decode time (numpy composition of the C linears)
+# ----------------------------------------------------------------------------
+# The pages keep the model architecture as it is and replace its dense linears
+# by LittleBit linears (trove.briskstack page, overview; deniz.in, "Factorize
+# first, then binarize"; the mlsanity page lists Llama 2 and GQA as the models
+# it builds on).  The layer here is the Llama form: pre-RMSNorm, attention
+# with grouped kv heads, SwiGLU MLP, residual adds.  Attention is over a
+# context of one token, whose softmax weight is 1.
+
+def round_bf16(a: np.ndarray) -> np.ndarray:
+    """fp64 values rounded to the nearest bf16 (8 significant bits, ties to
+    even), kept in fp64.  With a = m * 2^e, 0.5 <= |m| < 1, the bf16 step is
+    2^(e-8); below the smallest normal the step stays 2^-133."""
+    a = np.asarray(a, dtype=np.float64)
+    out = a.copy()
+    nz = np.isfinite(a) & (a != 0)
+    _, e = np.frexp(a[nz])
+    step = np.ldexp(1.0, np.maximum(e, -125) - 8)
+    out[nz] = np.round(a[nz] / step) * step        # numpy rounds halves to even
+    return out
+
+
+def rms_inverse(x: np.ndarray, eps: float) -> np.ndarray:
+    """1 / sqrt(mean over channels of x^2 + eps), one value per token."""
+    xd = widen_x(x)
+    return 1.0 / np.sqrt(np.mean(xd * xd, axis=1) + eps)
+
+
+def attend_one_token(v: np.ndarray, n_heads: int, n_kv_heads: int) -> np.ndarray:
+    """Attention output [T][n_heads * d_head] over a context of one token:
+    query head h reads value head h // (n_heads / n_kv_heads)."""
+    T, d_kv = v.shape
+    dh = d_kv // n_kv_heads
+    grp = n_heads // n_kv_heads
+    out = np.empty((T, n_heads * dh), np.float64)
+    for h in range(n_heads):
+        kv = h // grp
+        out[:, h * dh:(h + 1) * dh] = v[:, kv * dh:(kv + 1) * dh]
+    return out
+
+
+def decoder_layer_forward(x: np.ndarray, lin: dict, n_heads: int, n_kv_heads: int, eps: float,
+                          store=None, nthreads: int = 0) -> np.ndarray:
+    """One decoder layer: a = x / rms(x); v = V(a);
+    x1 = x + O(attend(v)); b = x1 / rms(x1); y = x1 + Down(silu(Gate(b)) * Up(b)).
+    lin maps q, k, v, o, gate, up, down to objects with U, V, h, g, l.  The
+    RMSNorm weights are taken as folded into the linears' g.  `store` (None or
+    round_bf16) is applied to every tensor handed from one step to the next,
+    to model an implementation that keeps them in a narrower type."""
+    keep = store or (lambda a: a)
+    f = lambda name, a: linear_forward(a, lin[name].U, lin[name].V, lin[name].h, lin[name].g,
+                                       lin[name].l, nthreads)
+    xd = widen_x(x)
+    a = xd * rms_inverse(xd, eps)[:, None]
+    v = keep(f("v", a))                  # q and k do not change a one-token attention
+    x1 = keep(xd + f("o", attend_one_token(v, n_heads, n_kv_heads)))
+    b = x1 * rms_inverse(x1, eps)[:, None]
+    zg, zu = keep(f("gate", b)), keep(f("up", b))
+    m = zg / (1.0 + np.exp(-zg)) * zu
+    return x1 + f("down", m)
+
+
 def _scale64(s: np.ndarray) -> np.ndarray:
     if s.dtype == np.uint16:
         return widen_f16(s)

@@ -87,6 +87,14 @@ def layer_inputs(seed: int, d_in: int, d_out: int, r_path: int, paths: int,
     return LayerInputs(d_in, d_out, r_path, paths, U, V, h, g, l)
 
 
+def unit_gain_l(d_in: int, r_path: int, paths: int) -> float:
+    """Factor on the l draw that gives a linear an output RMS near its input's
+    (signs are +-1, so each contraction grows a norm by about the square root
+    of its length).  Used for layers chained one into the next, whose
+    activations would otherwise grow layer by layer."""
+    return 1.0 / float(np.sqrt(d_in * r_path * paths))
+
+
 def activations(seed: int, T: int, d: int, dtype: str) -> np.ndarray:
     """x [T][d]: float32 array for dtype 'f32', uint16 bf16 bits for 'bf16'."""
     rng = np.random.Generator(np.random.PCG64(seed))

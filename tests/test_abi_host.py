@@ -229,3 +229,35 @@ def test_latent_api_argument_errors():
     assert s2(y=0) == lb.LB_EINVAL
     assert s2(y=TT) == lb.LB_EINVAL                          # y overlaps t
     assert s2(td=lb.LB_BF16, t=TT + 1) == lb.LB_EALIGN
+
+
+def test_decoder_layer_argument_errors():
+    """lb_decoder_layer_forward's checks, before any launch (fake device
+    addresses; a call that got past them would fault, so each one must not)."""
+    L = lb.lib()
+    f = _factors(ld_v=512, ld_u=2048)
+    mk = lambda **k: lb.lb_decoder_layer(f, f, f, f, f, f, f, k.get("d", 1024), k.get("ff", 2048),
+                                         k.get("nh", 8), k.get("nkv", 2), 256, 128, 256, 256, 1,
+                                         k.get("eps", 1e-6))
+    good = mk()
+    need = L.lb_decoder_layer_workspace_bytes(ctypes.byref(good), 4)
+    assert need > 0
+    assert L.lb_decoder_layer_workspace_bytes(ctypes.byref(good), 33) == 0
+    assert L.lb_decoder_layer_workspace_bytes(ctypes.byref(good), 0) == 0
+    assert L.lb_decoder_layer_workspace_bytes(ctypes.byref(mk(nh=3)), 4) == 0
+    X, Y, WS = FAKE + 0x5000000, FAKE + 0x6000000, FAKE + 0xa000000
+    run = lambda lay=good, **k: L.lb_decoder_layer_forward(ctypes.byref(lay), k.get("x", X), k.get("y", Y),
+                                                           k.get("T", 4), k.get("ws", WS), k.get("n", need), None)
+    assert run(T=33) == lb.LB_EUNSUPPORTED
+    assert run(T=-1) == lb.LB_EINVAL
+    assert run(T=0, x=0, y=0) == lb.LB_OK                    # empty: a no-op
+    assert run(mk(nh=3)) == lb.LB_EINVAL                     # heads do not divide d_model
+    assert run(mk(nh=8, nkv=3)) == lb.LB_EINVAL              # kv heads do not divide heads
+    assert run(mk(eps=float("nan"))) == lb.LB_EINVAL
+    assert run(x=0) == lb.LB_EINVAL
+    assert run(x=X + 2) == lb.LB_EALIGN
+    assert run(y=X + 256) == lb.LB_EINVAL                    # y overlaps x
+    assert run(ws=None) == lb.LB_EWORKSPACE
+    assert run(n=need - 1) == lb.LB_EWORKSPACE
+    assert run(ws=WS + 16) == lb.LB_EALIGN
+    assert run(ws=X - 256) == lb.LB_EINVAL                   # ws overlaps x

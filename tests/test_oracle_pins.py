@@ -400,3 +400,77 @@ def test_latent_cache_ratio_pin():
     r, rp = oracle.rank_for_budget(4096, 4096, 1, 10, True)
     assert r == 192 and rp == 96
     assert round(4096 / r, 1) == 21.3
+
+
+def test_round_bf16_against_storage_rounding():
+    """The oracle's fp64 -> bf16 rounding against torch's conversion and the
+    input generator's bit-level one, on fp32 values (no double rounding) that
+    include exact ties, subnormals and powers of two."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(11)
+    a = rng.standard_normal(4000).astype(np.float32) * np.float32(2.0) ** rng.integers(-20, 20, 4000)
+    ties = (np.arange(1, 200, dtype=np.uint32) << 16 | 0x8000).view(np.float32)     # halfway cases
+    tiny = np.array([1e-39, -3e-40, 2.0 ** -133, 2.0 ** -126, 1.0, -0.5, 3.0 * 2.0 ** -134], np.float32)
+    v = np.concatenate([a, ties, tiny])
+    got = oracle.round_bf16(v.astype(np.float64))
+    want = torch.from_numpy(v).to(torch.bfloat16).float().numpy().astype(np.float64)
+    assert np.array_equal(got, want)
+    assert np.array_equal(got, synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(v)).astype(np.float64))
+
+
+def _layer_set(seed, d, ff, dkv, ranks, P=2):
+    rng = np.random.default_rng(seed)
+    shapes = dict(q=(d, d, ranks[0]), k=(d, dkv, ranks[1]), v=(d, dkv, ranks[1]), o=(d, d, ranks[0]),
+                  gate=(d, ff, ranks[2]), up=(d, ff, ranks[2]), down=(ff, d, ranks[3]))
+    lin = {}
+    for name, (din, dout, rp) in shapes.items():
+        U, V, h, g, l = _rand_layer(rng, din, dout, rp, P)
+        lin[name] = synth.LayerInputs(din, dout, rp, P, U, V, h, g, l / np.sqrt(din * rp * P))
+    return lin
+
+
+@pytest.mark.parametrize("n_heads,n_kv", [(4, 4), (4, 2), (6, 1)])
+def test_decoder_layer_against_library_attention(n_heads, n_kv):
+    """The decoder-layer composition against torch's own routines on the CPU:
+    RMSNorm (F.rms_norm), scaled-dot-product attention with grouped kv heads
+    (enable_gqa; q and k really computed, each token a one-token context),
+    SiLU, and the dense reconstructed weights in place of the factorised C
+    forward.  A dropped norm, a wrong kv-head mapping, a missing residual or a
+    swapped gate and up fails here."""
+    torch = pytest.importorskip("torch")
+    F = torch.nn.functional
+    d, ff, dh = 48, 80, 48 // n_heads
+    dkv = dh * n_kv
+    lin = _layer_set(20 + n_kv, d, ff, dkv, (16, 8, 24, 16))
+    x = np.random.default_rng(3).standard_normal((5, d)) * 1.7
+    eps = 1e-5
+    y = oracle.decoder_layer_forward(x, lin, n_heads, n_kv, eps)
+
+    W = {k: torch.from_numpy(oracle.dense_weight(v.U, v.V, v.h, v.g, v.l)) for k, v in lin.items()}
+    xt = torch.from_numpy(x)
+    T = x.shape[0]
+    a = F.rms_norm(xt, (d,), eps=eps)
+    q = (a @ W["q"].T).view(T, 1, n_heads, dh).transpose(1, 2)
+    k = (a @ W["k"].T).view(T, 1, n_kv, dh).transpose(1, 2)
+    v = (a @ W["v"].T).view(T, 1, n_kv, dh).transpose(1, 2)
+    att = F.scaled_dot_product_attention(q, k, v, enable_gqa=True).transpose(1, 2).reshape(T, d)
+    x1 = xt + att @ W["o"].T
+    b = F.rms_norm(x1, (d,), eps=eps)
+    want = x1 + (F.silu(b @ W["gate"].T) * (b @ W["up"].T)) @ W["down"].T
+    assert oracle.rel_l2(y, want.numpy()) < 1e-12
+
+
+def test_decoder_layer_norm_scale_invariance():
+    """With eps = 0 the attention and MLP branches see x only through x/rms(x):
+    scaling x by c changes x1 - x and the output's branch by nothing, so
+    y(c x) - c x equals, for c = 1, y(x) - x only through x1; checked as
+    x1(c x) - c x = x1(x) - x on the attention half via a zero MLP."""
+    lin = _layer_set(7, 32, 40, 32, (8, 8, 8, 8))
+    zero = lin["down"]
+    lin["down"] = synth.LayerInputs(zero.d_in, zero.d_out, zero.r_path, zero.paths, zero.U, zero.V,
+                                    zero.h * 0.0, zero.g, zero.l)
+    x = np.random.default_rng(9).standard_normal((3, 32))
+    for c in (0.25, 3.0):
+        y1 = oracle.decoder_layer_forward(x, lin, 4, 4, 0.0)
+        yc = oracle.decoder_layer_forward(c * x, lin, 4, 4, 0.0)
+        assert np.allclose(yc - c * x, y1 - x, rtol=1e-12, atol=1e-12)
