@@ -330,6 +330,65 @@ def decode_stack_leg(key, T, steps, layers=0):
     return out
 
 
+def decoder_stack_leg(key, T, steps, layers=0):
+    """The workload's layers as a model runs them at decode time: each
+    decoder layer (two RMSNorms, q/k/v, a one-token attention, o, the SwiGLU
+    block, two residual adds) feeds the next, so the layers run one after
+    another.  The whole stack is captured as one HIP graph; HIP events
+    around `steps` replays.  Factors are drawn with l scaled for unit gain so
+    the activations stay in range through the chain."""
+    import torch
+    import synth
+    from binarized_rank_linear_amd.stack import DecoderStack
+    w = synth.WORKLOADS[key]
+    L = layers or w.layers
+    sh = {s.name: s for s in w.linears}
+    P = 2 if w.residual else 1
+
+    def make(layer, i, di, do, rp, paths):
+        U, V, h, g, l = synth.device_layer(synth.layer_seed(layer, i), di, do, rp, paths)
+        return U, V, h, g, (l.float() * synth.unit_gain_l(di, rp, paths)).half()
+
+    t0 = time.time()
+    st = DecoderStack(sh["q"].d_in, sh["gate"].d_out, w.heads[0], w.heads[1], L, w.b_num, w.b_den,
+                      w.residual, make)
+    x = synth.device_activations(synth.activation_seed(T), T, sh["q"].d_in, "bf16")
+    bufs = [torch.empty_like(x), torch.empty_like(x)]
+    ws = torch.empty(st.workspace_bytes(T), dtype=torch.uint8, device="cuda")
+    _log("decoder stack of %d layers built in %.1f s" % (L, time.time() - t0))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        st.forward(x, bufs, ws, stream=s)              # eager once (the graph needs no warm state)
+        s.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            st.forward(x, bufs, ws, stream=s)
+        for _ in range(5):
+            g.replay()
+        s.synchronize()
+        t1 = time.perf_counter()
+        while time.perf_counter() - t1 < 0.2:
+            g.replay()
+            s.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(steps):
+            g.replay()
+        e1.record(s)
+        s.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / steps
+    nbytes = sum(sum(linear_bytes(lin.d_in, lin.d_out, lin.r, P, T)) for lin in st.linears())
+    finite = bool(torch.isfinite(bufs[(L - 1) & 1].float()).all())
+    del st, g
+    torch.cuda.empty_cache()
+    return {"workload": "%s, %d decoder layers chained at decode T=%d (one HIP graph)" % (w.title, L, T),
+            "us_per_pass": t * 1e6, "us_per_layer": t * 1e6 / L, "tok_per_s": T / t,
+            "launches_per_layer": 15, "algorithmic_bytes": nbytes, "GBs": nbytes / t / 1e9,
+            "hbm_frac": nbytes / t / 1e9 / HBM_PEAK_GBS, "output_finite": finite}
+
+
 def cache_resident_legs(reps=2000):
     """The two small configurations, whose factors stay in the caches: the
     1024 x 1024 linear at 1.0 bit per weight (fp32, T = 1 and 8) and the
@@ -610,6 +669,8 @@ def main():
     if not args.no_extra:
         out["decode_more"] = [decode_stack_leg("c3", 4, max(20, args.steps // 2)),
                               decode_stack_leg("c3", 32, max(10, args.steps // 10))]
+        out["decoder_chain"] = [decoder_stack_leg(args.workload, T, max(10, args.steps // 10)),
+                                decoder_stack_leg("c3", 1, max(10, args.steps // 10))]
         out["cache_resident"] = cache_resident_legs()
         c = ceilings()
         out["ceilings"] = c

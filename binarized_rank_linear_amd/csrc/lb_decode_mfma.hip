@@ -67,6 +67,7 @@ constexpr int kPreVec = 8;                // operand vectors a thread loads befo
 constexpr int kWin2 = 8;                  // stage 2 (streaming form): plane loads in flight per wave
 constexpr int kWin1 = 8;                  // stage 1 (fused form): plane loads in flight per wave
 constexpr int kEarly1 = 2;                // of which issued before the limb work inside the one-launch pass
+constexpr int kTB = 3;                   // stage 1 (fused form): tokens whose inputs load together
 constexpr int kMaxKcf = 32;               // K-groups per fused stage-1 chunk (two 8-input pieces per thread)
 constexpr uint32_t kOOB = 0x7ffffff0u;    // a buffer offset past every range: reads as zero
 // Cache policy of a buffer access at device scope (sc1): coherent across the
@@ -238,9 +239,25 @@ __device__ __forceinline__ MLin pick(const MRun &run, const MLin &single, const 
     return m;
 }
 
+// Index of the inline linear whose KIND items hold `item` (constant indices).
+template <int KIND>
+__device__ __forceinline__ int inline_index(const MRun &run, int64_t item) {
+    int j = 0;
+    if (run.ninl > 1 && item >= item_start(run.inl[1], KIND)) j = 1;
+    if (run.ninl > 2 && item >= item_start(run.inl[2], KIND)) j = 2;
+    return j;
+}
+
 // Linear j of the run as a wave-uniform value.
 __device__ __forceinline__ MLin pick_linear(const MRun &run, const MLin &single, int j) {
-    MLin m = run.table ? run.table[j] : single;
+    MLin m = single;
+    if (run.table) {
+        m = run.table[j];
+    } else if (run.ninl) {                 // constant indices, as in pick
+        m = run.inl[0];
+        if (j == 1) m = run.inl[1];
+        if (j == 2) m = run.inl[2];
+    }
     int w[sizeof(MLin) / 4];
     __builtin_memcpy(w, &m, sizeof(MLin));
 #pragma unroll
@@ -816,25 +833,40 @@ __device__ __forceinline__ void stage1f_item(const MRun &run, const MLin &L, int
             }
             emit_piece<NL>(v, rec_of(pc, 0), (pc >> 2) & 3, pc & 3, pc < npc);
         }
-        for (int n = 1; n < T; ++n) {
+        // the other tokens kTB at a time, all of a round's loads in flight
+        // together (one load latency per round, not one per token)
+        constexpr int TB = COHERENT ? 1 : kTB;   // the pass: T <= 2, registers kept for stage 2
+        for (int n0 = 1; n0 < T; n0 += TB) {
+            v4u xa[TB][kPPT][2];
 #pragma unroll
-            for (int j = 0; j < kPPT; ++j) {
-                const int pc = tid + j * kThreads;
-                const int64_t i = i_chunk + (int64_t)pc * 8;
-                const bool in = pc < npc && i < L.d_in;
-                const int64_t e = (int64_t)n * L.d_in + i;
-                const v4u x0 = __builtin_amdgcn_raw_buffer_load_b128(rx, in ? (uint32_t)(e * xb) : kOOB, 0, 0);
-                const v4u x1 = __builtin_amdgcn_raw_buffer_load_b128(rx2, second(in, e), 0, 0);
-                float v[8];
-                if (xf32) gx8_f32(gr[j], x0, x1, v);
-                else if (glu) gx8_glu(gr[j], x0, x1, v);
-                else gx8_bf16(gr[j], x0, v);
-                if (L.xs) {                                     // uniform
-                    const float sc = L.xs[n];
+            for (int u = 0; u < TB; ++u)
 #pragma unroll
-                    for (int t = 0; t < 8; ++t) v[t] *= sc;
+                for (int j = 0; j < kPPT; ++j) {
+                    const int pc = tid + j * kThreads;
+                    const int64_t i = i_chunk + (int64_t)pc * 8;
+                    const bool in = n0 + u < T && pc < npc && i < L.d_in;
+                    const int64_t e = (int64_t)(n0 + u) * L.d_in + i;
+                    xa[u][j][0] = __builtin_amdgcn_raw_buffer_load_b128(rx, in ? (uint32_t)(e * xb) : kOOB, 0, 0);
+                    xa[u][j][1] = __builtin_amdgcn_raw_buffer_load_b128(rx2, second(in, e), 0, 0);
                 }
-                emit_piece<NL>(v, rec_of(pc, n), (pc >> 2) & 3, pc & 3, pc < npc);
+#pragma unroll
+            for (int u = 0; u < TB; ++u) {
+                const int n = n0 + u;
+                if (n >= T) break;                                  // uniform
+#pragma unroll
+                for (int j = 0; j < kPPT; ++j) {
+                    const int pc = tid + j * kThreads;
+                    float v[8];
+                    if (xf32) gx8_f32(gr[j], xa[u][j][0], xa[u][j][1], v);
+                    else if (glu) gx8_glu(gr[j], xa[u][j][0], xa[u][j][1], v);
+                    else gx8_bf16(gr[j], xa[u][j][0], v);
+                    if (L.xs) {                                     // uniform
+                        const float sc = L.xs[n];
+#pragma unroll
+                        for (int t = 0; t < 8; ++t) v[t] *= sc;
+                    }
+                    emit_piece<NL>(v, rec_of(pc, n), (pc >> 2) & 3, pc & 3, pc < npc);
+                }
             }
         }
     } else {                                                    // ragged or unaligned: input by input
@@ -1608,8 +1640,10 @@ __global__ __launch_bounds__(kThreads) void k_pass(MRun run, MLin single) {
     if (stale_ws(run)) return;
     const int64_t b = blockIdx.x;
     if (b < run.items1) {
-        const int64_t item = __builtin_amdgcn_readfirstlane(run.ordP1[b]);
-        const int j = run.table ? __builtin_amdgcn_readfirstlane(run.lin1[item]) : 0;
+        // groups: the stage-1 order from the workspace; inline runs: item order
+        const int64_t item = run.ordP1 ? (int64_t)__builtin_amdgcn_readfirstlane(run.ordP1[b]) : b;
+        const int j = run.table ? __builtin_amdgcn_readfirstlane(run.lin1[item])
+                                : run.ninl ? inline_index<kKindStage1>(run, item) : 0;
         const MLin L = pick<kKindStage1>(run, single, run.lin1, item);
         stage1f_item<NL, true>(run, L, item, smem);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // this wave's partial sums are stored
@@ -1628,10 +1662,22 @@ __global__ __launch_bounds__(kThreads) void k_pass(MRun run, MLin single) {
                 sync_event(run.sync + j * kFlagStride, 0x10001u, (uint32_t)(L.P * L.nrg + L.n2));
         }
     } else {
-        // (linear, first 256-row tile << 8 | tiles) of this workgroup
-        const int32_t *e = run.tabP2 + 2 * (b - run.items1);
-        const int j = __builtin_amdgcn_readfirstlane(e[0]);
-        const int g = __builtin_amdgcn_readfirstlane(e[1]);
+        // (linear, first 256-row tile << 8 | tiles) of this workgroup: from the
+        // workspace table (groups), or the inline linears' stage-2 items in order
+        int j, g;
+        if (run.tabP2) {
+            const int32_t *e = run.tabP2 + 2 * (b - run.items1);
+            j = __builtin_amdgcn_readfirstlane(e[0]);
+            g = __builtin_amdgcn_readfirstlane(e[1]);
+        } else {
+            const int64_t e = b - run.items1;
+            j = run.ninl ? inline_index<kKindStage2>(run, e) : 0;
+            const MLin m = pick_linear(run, single, j);
+            const int64_t local = e - m.item2;
+            const int per = (int)(m.rows2 / kRG);
+            const int tiles = (int)imin(per, cdiv(m.d_out - local * m.rows2, kRG));
+            g = (int)((local * per) << 8) | tiles;
+        }
         stage2r_item<NL, NB2, true>(run, pick_linear(run, single, j), (int64_t)(g >> 8) * kRG, g & 255, smem,
                                     run.sync + j * kFlagStride);
     }
@@ -1716,6 +1762,7 @@ struct Grain {
     int64_t fused_bytes = kFusedBytes;
     int tiles2 = kTilesPerItem2;
     int tsplit = 0;       // fused stage 1 splits tiles among the waves (tsplit_for)
+    int f_cap = 1 << 20;  // fused stage 1: 64-latent tiles per item, at most
 };
 
 size_t plan_linear(const Linear &a, const Shape &s, bool many, MLin *m, Grain gr = Grain{}) {
@@ -1753,7 +1800,7 @@ size_t plan_linear(const Linear &a, const Shape &s, bool many, MLin *m, Grain gr
         const int64_t nch = cdiv(m->kgv, kc);
         m->kcg = (int32_t)cdiv(m->kgv, nch);
         m->nchunks = (int32_t)cdiv(m->kgv, m->kcg);
-        m->nrg = (int32_t)cdiv(cdiv(a.r_p, kTile), flush1_for(a.T, gr.tsplit));
+        m->nrg = (int32_t)cdiv(cdiv(a.r_p, kTile), imin(flush1_for(a.T, gr.tsplit), gr.f_cap));
         m->kcp = 0;
         m->nprep = 0;
         m->xvec = (a.d_in % 8 == 0 && ((uintptr_t)a.x & 15) == 0 && ((uintptr_t)a.x2 & 15) == 0 &&
@@ -1925,6 +1972,9 @@ size_t mfma_decode_workspace_bytes(const Linear &a) {
         MLin m;
         const size_t b = plan_linear(a, s, false, &m);
         if (b > need) need = b;
+        Linear c = a;                  // the one-launch form (mfma_decode_forward takes it when it applies)
+        c.y_dtype = yd;
+        need = std::max(need, mfma_inline_workspace_bytes(&c, 1));
     }
     return need;
 }
@@ -1959,6 +2009,7 @@ int single_setup(const Linear &a, void *ws, Shape *s, MLin *m, MRun *run, Lds *l
 }  // namespace
 
 int mfma_decode_forward(const Linear &a, void *ws, hipStream_t st) {
+    if (mfma_inline_pass(&a, 1)) return mfma_inline_forward(&a, 1, ws, st);   // one launch after a clear
     Shape s;
     MLin m;
     MRun run;
@@ -2033,7 +2084,7 @@ Grain group_grain(const Linear *ls, int n, const Shape &s) {
     Grain g;
     g.tsplit = fused1(s) && tsplit_for(ls, n) ? 1 : 0;
     const int kc_floor = pass_form(ls, n, s) ? kPassMinKcg : 4;
-    for (int pass = 0; pass < 8; ++pass) {
+    for (int pass = 0; pass < 16; ++pass) {
         int64_t i1 = 0, i2 = 0, kc_min = kMaxKcf;
         for (int j = 0; j < n; ++j) {
             MLin m;
@@ -2046,6 +2097,16 @@ Grain group_grain(const Linear *ls, int n, const Shape &s) {
         if (fused1(s) && i1 < kMinGroupItems && kc_min > kc_floor && g.fused_bytes > 4096) {
             g.fused_bytes /= 2;
             changed = true;
+        } else if (fused1(s) && i1 < kMinGroupItems) {
+            // then fewer latent tiles per item (down to one per wave)
+            int64_t f = imin(g.f_cap, flush1_for(ls[0].T, g.tsplit)), tiles = 1;
+            for (int j = 0; j < n; ++j) tiles = imax(tiles, cdiv(ls[j].r_p, kTile));
+            f = imin(f, tiles);
+            const int64_t fmin = g.tsplit ? kWaves : 1;
+            if (f > fmin) {
+                g.f_cap = (int)imax(fmin, f / 2);
+                changed = true;
+            }
         }
         if (i2 < kMinGroupItems && g.tiles2 > 1) {
             g.tiles2 /= 2;
@@ -2148,7 +2209,7 @@ int mfma_group_plan(const Linear *ls, int n, int64_t T, int y_dtype, void *ws, s
     int64_t ntile_max = 1;
     for (int j = 0; j < n; ++j) ntile_max = imax(ntile_max, cdiv(tab[(size_t)j].r_p, kTile));
     run.tsplit = gr.tsplit;
-    run.flush1 = (int)imin(flush1_for(T, run.tsplit), ntile_max);
+    run.flush1 = (int)imin(imin(flush1_for(T, run.tsplit), ntile_max), gr.f_cap);
     for (int j = 0; j < n; ++j) lds_add(&hs->lds, tab[(size_t)j], hs->s, run.ops2, T, run.flush1, run.tsplit);
     auto put = [&](size_t off, const void *src, size_t bytes) { if (bytes) memcpy(im.data() + off, src, bytes); };
     std::vector<int32_t> h0((size_t)i0), h1((size_t)i1), hF((size_t)iF), h2((size_t)i2);
@@ -2306,14 +2367,19 @@ int mfma_group_run(const void *host_state, hipStream_t st, int stage_mask) {
 
 namespace {
 // The schedule of up to kMaxInline linears in the kernel arguments; returns
-// the workspace bytes (each linear's scratch, back to back).
-size_t inline_setup(const Linear *ls, int n, uint8_t *ws, Shape *s, MRun *run, Lds *lds) {
+// the workspace bytes (each linear's scratch, back to back, then, for the
+// one-launch form, the latent-group and per-linear counters).  The one-launch
+// form (k_pass) is taken under the same conditions as for a group; its
+// workspace must be all zero when the launch starts (the caller clears it;
+// the pass leaves the counters at zero, not the rest).
+size_t inline_setup(const Linear *ls, int n, uint8_t *ws, Shape *s, MRun *run, Lds *lds, size_t *lds_pass) {
     *run = MRun{};
     *lds = Lds{};
+    *lds_pass = 0;
     if (n < 1 || n > kMaxInline || !shape_for(ls[0].T, ls[0].y_dtype, s)) return 0;
     const Grain gr = group_grain(ls, n, *s);
     size_t off = 0;
-    int64_t i0 = 0, i1 = 0, iF = 0, i2 = 0;
+    int64_t i0 = 0, i1 = 0, iF = 0, i2 = 0, nf = 0;
     int steps_max = 1;
     int64_t ntile_max = 1;
     for (int j = 0; j < n; ++j) {
@@ -2325,10 +2391,12 @@ size_t inline_setup(const Linear *ls, int n, uint8_t *ws, Shape *s, MRun *run, L
         m.item1 = i1;
         m.itemF = iF;
         m.item2 = i2;
+        m.fin0 = nf;
         i0 += items0_of(m);
         i1 += items1_of(m);
         iF += itemsF_of(m);
         i2 += m.n2;
+        nf += groups_of(m);
         steps_max = (int)imax(steps_max, m.kgs);
         ntile_max = imax(ntile_max, cdiv(m.r_p, kTile));
     }
@@ -2345,24 +2413,76 @@ size_t inline_setup(const Linear *ls, int n, uint8_t *ws, Shape *s, MRun *run, L
     run->itemsF = iF;
     run->items2 = i2;
     run->tsplit = gr.tsplit;
-    run->flush1 = (int)imin(flush1_for(ls[0].T, run->tsplit), ntile_max);
+    run->flush1 = (int)imin(imin(flush1_for(ls[0].T, run->tsplit), ntile_max), gr.f_cap);
     for (int j = 0; j < n; ++j) lds_add(lds, run->inl[j], *s, run->ops2, ls[0].T, run->flush1, run->tsplit);
+    // the one-launch form: as a group takes it (pass_form, the 16-bit event
+    // halves, the LDS of one CU)
+    const int64_t T = ls[0].T;
+    bool pass = pass_tokens(*s, T) && run->dma2 && i1 > 0 && i2 > 0;
+    for (int j = 0; j < n; ++j)
+        if ((int64_t)run->inl[j].P * run->inl[j].nrg + run->inl[j].n2 >= 0xffff) pass = false;
+    size_t lp = 0;
+    if (pass) {
+        const size_t l2 = ops2r_bytes(run->ops2, s->NB2, rows2(*s, T)) + 2 * kHRows * 2 +
+                          (run->ystage ? (size_t)T * kHRows * run->yst : 0);
+        const size_t lat = (size_t)T * run->flush1 * 2 * s->NL * kRec;
+        lp = std::max(std::max(lds->s1, lat), l2);
+        if (lp > 160 * 1024 - 64) pass = false;
+    }
+    if (pass) {
+        const size_t ctrl = rup256(off), arrive = rup256((size_t)nf * kFlagStride * 4);
+        if (ws) {
+            run->arrive = (uint32_t *)(ws + ctrl);
+            run->sync = (uint32_t *)(ws + ctrl + arrive);
+        }
+        run->pass = 1;
+        run->items2P = i2;
+        run->spin_limit = kSpinLimit;
+        *lds_pass = lp;
+        off = ctrl + arrive + rup256((size_t)n * kFlagStride * 4);
+    }
     return off;
 }
+
+int launch_pass_shape(const Shape &s, const MRun &run, size_t lds, hipStream_t st) {
+    switch (s.NL * 10 + s.NB2) {
+        case 21: return launch_pass<2, 1>(run, lds, st);
+        case 22: return launch_pass<2, 2>(run, lds, st);
+        case 31: return launch_pass<3, 1>(run, lds, st);
+        case 32: return launch_pass<3, 2>(run, lds, st);
+    }
+    return LB_EUNSUPPORTED;
+}
 }  // namespace
+
+bool mfma_inline_pass(const Linear *ls, int n) {
+    Shape s;
+    MRun run;
+    Lds lds;
+    size_t lp;
+    return inline_setup(ls, n, nullptr, &s, &run, &lds, &lp) > 0 && run.pass;
+}
 
 size_t mfma_inline_workspace_bytes(const Linear *ls, int n) {
     Shape s;
     MRun run;
     Lds lds;
-    return inline_setup(ls, n, nullptr, &s, &run, &lds);
+    size_t lp;
+    return inline_setup(ls, n, nullptr, &s, &run, &lds, &lp);
 }
 
-int mfma_inline_forward(const Linear *ls, int n, void *ws, hipStream_t st) {
+int mfma_inline_forward(const Linear *ls, int n, void *ws, hipStream_t st, bool zeroed) {
     Shape s;
     MRun run;
     Lds lds;
-    if (inline_setup(ls, n, (uint8_t *)ws, &s, &run, &lds) == 0) return LB_EUNSUPPORTED;
+    size_t lp;
+    const size_t bytes = inline_setup(ls, n, (uint8_t *)ws, &s, &run, &lds, &lp);
+    if (bytes == 0) return LB_EUNSUPPORTED;
+    if (run.pass) {
+        if (!zeroed)
+            if (int rc = fill_words(ws, bytes, 0u, st)) return rc;
+        return launch_pass_shape(s, run, lp, st);
+    }
     MLin dummy{};
     return launch_shape(s, run, dummy, lds, st);
 }

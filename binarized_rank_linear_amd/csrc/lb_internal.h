@@ -105,12 +105,16 @@ bool mfma_decode_supported(int64_t T, int y_dtype);
 bool mfma_decode_shape_ok(const Linear &a);
 size_t mfma_decode_workspace_bytes(const Linear &a);
 int mfma_decode_forward(const Linear &a, void *ws, hipStream_t s);
-// Up to kMaxInline linears (same T and dtypes) in one three-launch run, with
-// their schedule in the kernel arguments instead of device tables: nothing to
-// set up, so a stateless call can use it.
+// Up to kMaxInline linears (same T and dtypes) in one run, with their
+// schedule in the kernel arguments instead of device tables: nothing to set
+// up, so a stateless call can use it.  Where the one-launch pass applies
+// (mfma_inline_pass) the run is a clear of the workspace and one launch (or
+// the launch alone when the caller has cleared it: zeroed); else the
+// three-launch form.
 constexpr int kMaxInline = 3;
+bool mfma_inline_pass(const Linear *ls, int n);
 size_t mfma_inline_workspace_bytes(const Linear *ls, int n);
-int mfma_inline_forward(const Linear *ls, int n, void *ws, hipStream_t s);
+int mfma_inline_forward(const Linear *ls, int n, void *ws, hipStream_t s, bool zeroed = false);
 // Groups of independent linears on the matrix-core decode path.
 size_t mfma_group_workspace_bytes(const Linear *ls, int n, int64_t T, int y_dtype);
 size_t mfma_group_state_bytes();

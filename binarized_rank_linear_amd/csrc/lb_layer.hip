@@ -59,7 +59,8 @@ size_t rup256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 struct LayerPlan {
     Linear q, k, v, o, gate, up, down;
-    size_t off_s, off_q, off_k, off_v, off_oin, off_x1, off_g, off_u, off_lin, total;
+    size_t off_s, off_q, off_k, off_v, off_oin, off_x1, off_g, off_u;
+    size_t off_qkv, off_o, off_gu, off_dn, total;   // the four runs' scratch (cleared together)
 };
 
 int check_factors_of(const lb_factors *w, Linear *a) {
@@ -120,11 +121,10 @@ int plan_layer(const lb_decoder_layer *L, int64_t T, bool with_factors, LayerPla
     p->off_g = take((size_t)(T * L->d_ff) * 2);
     p->off_u = take((size_t)(T * L->d_ff) * 2);
     const Linear qkv[3] = {p->q, p->k, p->v}, gu[2] = {p->gate, p->up};
-    size_t lin = mfma_inline_workspace_bytes(qkv, 3);
-    lin = std::max(lin, mfma_inline_workspace_bytes(gu, 2));
-    lin = std::max(lin, mfma_decode_workspace_bytes(p->o));
-    lin = std::max(lin, mfma_decode_workspace_bytes(p->down));
-    p->off_lin = take(lin);
+    p->off_qkv = take(mfma_inline_workspace_bytes(qkv, 3));
+    p->off_o = take(mfma_inline_workspace_bytes(&p->o, 1));
+    p->off_gu = take(mfma_inline_workspace_bytes(gu, 2));
+    p->off_dn = take(mfma_inline_workspace_bytes(&p->down, 1));
     p->total = at;
     return LB_OK;
 }
@@ -162,8 +162,9 @@ extern "C" int lb_decoder_layer_forward(const lb_decoder_layer *L, const void *x
     uint16_t *q = (uint16_t *)(w + p.off_q), *k = (uint16_t *)(w + p.off_k), *v = (uint16_t *)(w + p.off_v);
     uint16_t *oin = (uint16_t *)(w + p.off_oin), *x1 = (uint16_t *)(w + p.off_x1);
     uint16_t *yg = (uint16_t *)(w + p.off_g), *yu = (uint16_t *)(w + p.off_u);
-    void *lws = w + p.off_lin;
     const int64_t dh = L->d_model / L->n_heads, dkv = dh * L->n_kv_heads;
+    // the runs' one-launch forms start from zeroed scratch: one clear for all four
+    if ((rc = fill_words(w + p.off_qkv, p.total - p.off_qkv, 0u, s))) return rc;
 
     // a = x / rms(x); q, k, v
     k_rms<<<(unsigned)T, kT, 0, s>>>((const uint16_t *)x, L->d_model, L->eps, inv);
@@ -174,7 +175,7 @@ extern "C" int lb_decoder_layer_forward(const lb_decoder_layer *L, const void *x
     p.k.y = k;
     p.v.y = v;
     const Linear qkv[3] = {p.q, p.k, p.v};
-    if ((rc = mfma_inline_forward(qkv, 3, lws, s))) return rc;
+    if ((rc = mfma_inline_forward(qkv, 3, w + p.off_qkv, s, true))) return rc;
     // attention over one token, then x1 = x + O(o_in)
     k_expand_heads<<<(unsigned)cdiv(T * L->d_model, kT), kT, 0, s>>>(v, oin, T, L->d_model, dkv, dh,
                                                                      L->n_heads / L->n_kv_heads);
@@ -182,7 +183,7 @@ extern "C" int lb_decoder_layer_forward(const lb_decoder_layer *L, const void *x
     p.o.x = oin;
     p.o.resid = x;
     p.o.y = x1;
-    if ((rc = mfma_decode_forward(p.o, lws, s))) return rc;
+    if ((rc = mfma_inline_forward(&p.o, 1, w + p.off_o, s, true))) return rc;
     // b = x1 / rms(x1); gate, up; y = x1 + Down(silu(gate) * up)
     k_rms<<<(unsigned)T, kT, 0, s>>>(x1, L->d_model, L->eps, inv);
     if ((rc = last_launch_status())) return rc;
@@ -191,10 +192,10 @@ extern "C" int lb_decoder_layer_forward(const lb_decoder_layer *L, const void *x
     p.gate.y = yg;
     p.up.y = yu;
     const Linear gu[2] = {p.gate, p.up};
-    if ((rc = mfma_inline_forward(gu, 2, lws, s))) return rc;
+    if ((rc = mfma_inline_forward(gu, 2, w + p.off_gu, s, true))) return rc;
     p.down.x = yg;
     p.down.x2 = yu;
     p.down.resid = x1;
     p.down.y = y;
-    return mfma_decode_forward(p.down, lws, s);
+    return mfma_inline_forward(&p.down, 1, w + p.off_dn, s, true);
 }

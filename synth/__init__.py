@@ -134,6 +134,7 @@ class Workload:
     dtype: str            # activation dtype in and out: 'f32' or 'bf16'
     layers: int           # stack depth (1 = single layer)
     mlp: bool = False     # gate/up/down form one SwiGLU block
+    heads: Tuple[int, int] = (0, 0)   # attention heads and kv heads of the model (decoder layers)
 
 
 def _llama_like(d: int, ff: int, kv: int) -> Tuple[LinearShape, ...]:
@@ -149,11 +150,14 @@ WORKLOADS: Dict[str, Workload] = {
                    (LinearShape("gate", 1024, 3072), LinearShape("up", 1024, 3072),
                     LinearShape("down", 3072, 1024)), 55, 100, True, (1, 16), "bf16", 1, mlp=True),
     "c3": Workload("c3", "Llama2-7B-shaped decoder-layer linears, 1.0 bpw + residual, 32-layer stack",
-                   _llama_like(4096, 11008, 4096), 1, 1, True, (1, 4, 32), "bf16", 32),
+                   _llama_like(4096, 11008, 4096), 1, 1, True, (1, 4, 32), "bf16", 32,
+                   heads=(32, 32)),
     "c4": Workload("c4", "Qwen3-14B-shaped layer linears, 0.55 bpw + residual, 40-layer stack",
-                   _llama_like(5120, 17408, 1024), 55, 100, True, (1, 2048), "bf16", 40),
+                   _llama_like(5120, 17408, 1024), 55, 100, True, (1, 2048), "bf16", 40,
+                   heads=(40, 8)),
     "c5": Workload("c5", "Llama2-70B-shaped layer linears, 0.1 bpw + residual, 80-layer stack",
-                   _llama_like(8192, 28672, 1024), 1, 10, True, (1, 2048), "bf16", 80),
+                   _llama_like(8192, 28672, 1024), 1, 10, True, (1, 2048), "bf16", 80,
+                   heads=(64, 8)),
 }
 
 
