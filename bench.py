@@ -385,7 +385,7 @@ def decoder_stack_leg(key, T, steps, layers=0):
     torch.cuda.empty_cache()
     return {"workload": "%s, %d decoder layers chained at decode T=%d (one HIP graph)" % (w.title, L, T),
             "us_per_pass": t * 1e6, "us_per_layer": t * 1e6 / L, "tok_per_s": T / t,
-            "launches_per_layer": 15, "algorithmic_bytes": nbytes, "GBs": nbytes / t / 1e9,
+            "algorithmic_bytes": nbytes, "GBs": nbytes / t / 1e9,
             "hbm_frac": nbytes / t / 1e9 / HBM_PEAK_GBS, "output_finite": finite}
 
 

@@ -111,6 +111,7 @@ struct MLin {
     int32_t n2;           // stage-2 items
     int32_t R1, R2;       // activation rows in use (compact records per operand)
     int32_t xvec;         // fused stage 1: x and g read as 16-byte pieces (d_in % 8 == 0, aligned)
+    int32_t xm_dh, xm_grp;   // fused stage 1: the input map of Linear (xm_dh = 0: none)
     int64_t item0, item1, itemF, item2;   // first item of this linear in each launch
     int64_t fin0;         // the one-launch pass: first (path, latent group) counter of this linear
     float *part;          // [nchunks][T][P*r_p]
@@ -158,6 +159,7 @@ struct MRun {
     int t_dtype;
     int t_mode;
     // inline groups: the linears themselves (no device tables; table null)
+    int xmap;                  // some linear of the launch reads x through an input map (xm_dh)
     int ninl;
     MLin inl[kMaxInline];
 };
@@ -732,7 +734,7 @@ __device__ __forceinline__ void emit_piece(const float (&v)[8], uint8_t *rec0, i
 // order.
 // COHERENT: the partial sums are read back inside the same launch by another
 // workgroup (the one-launch pass), so they are stored at device scope.
-template <int NL, bool COHERENT>
+template <int NL, bool COHERENT, bool XM = false>
 __device__ __forceinline__ void stage1f_item(const MRun &run, const MLin &L, int64_t item, uint8_t *smem) {
     using R = Rows<NL>;
     const int64_t local = item - L.item1;
@@ -759,9 +761,18 @@ __device__ __forceinline__ void stage1f_item(const MRun &run, const MLin &L, int
     const bool vec = L.xvec != 0;
     const bool glu = L.x2 != nullptr;                                  // SwiGLU input (bf16 x only)
     const __amdgpu_buffer_rsrc_t rgs = make_rsrc(L.g + (int64_t)p * L.d_in, L.d_in * 2);
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(L.x, (int64_t)T * L.d_in * xb);
+    // the input map (uniform): channel i of the linear's input is channel
+    // xoff(i) of a row of x, rows dsrc apart
+    // (instantiated apart (XM), so the plain form keeps its registers)
+    const int64_t dsrc = XM ? L.d_in / L.xm_grp : L.d_in;
+    auto xoff = [&](int64_t i) -> int64_t {
+        if constexpr (!XM) return i;
+        const uint32_t h = (uint32_t)i / (uint32_t)L.xm_dh;
+        return (int64_t)(h / (uint32_t)L.xm_grp) * L.xm_dh + ((uint32_t)i - h * (uint32_t)L.xm_dh);
+    };
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(L.x, (int64_t)T * dsrc * xb);
     // second piece of each input: the high half of fp32 x, or the up input x2
-    const __amdgpu_buffer_rsrc_t rx2 = make_rsrc(glu ? L.x2 : L.x, (int64_t)T * L.d_in * xb);
+    const __amdgpu_buffer_rsrc_t rx2 = make_rsrc(glu ? L.x2 : L.x, (int64_t)T * dsrc * xb);
     auto second = [&](bool ok, int64_t e) -> uint32_t {         // byte offset of element e's second piece
         return ok && (xf32 || glu) ? (uint32_t)(xf32 ? e * 4 + 16 : e * 2) : kOOB;
     };
@@ -771,9 +782,10 @@ __device__ __forceinline__ void stage1f_item(const MRun &run, const MLin &L, int
         const int pc = tid + j * kThreads;
         const int64_t i = i_chunk + (int64_t)pc * 8;
         const bool ok = vec && pc < npc && i < L.d_in;
+        const int64_t xi = xoff(i);
         gr[j] = __builtin_amdgcn_raw_buffer_load_b128(rgs, ok ? (uint32_t)(i * 2) : kOOB, 0, 0);
-        xr[j][0] = __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? (uint32_t)(i * xb) : kOOB, 0, 0);
-        xr[j][1] = __builtin_amdgcn_raw_buffer_load_b128(rx2, second(ok, i), 0, 0);
+        xr[j][0] = __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? (uint32_t)(xi * xb) : kOOB, 0, 0);
+        xr[j][1] = __builtin_amdgcn_raw_buffer_load_b128(rx2, second(ok, xi), 0, 0);
     }
 
     // ---- first plane loads ----------------------------------------------------
@@ -845,7 +857,7 @@ __device__ __forceinline__ void stage1f_item(const MRun &run, const MLin &L, int
                     const int pc = tid + j * kThreads;
                     const int64_t i = i_chunk + (int64_t)pc * 8;
                     const bool in = n0 + u < T && pc < npc && i < L.d_in;
-                    const int64_t e = (int64_t)(n0 + u) * L.d_in + i;
+                    const int64_t e = (int64_t)(n0 + u) * dsrc + xoff(i);
                     xa[u][j][0] = __builtin_amdgcn_raw_buffer_load_b128(rx, in ? (uint32_t)(e * xb) : kOOB, 0, 0);
                     xa[u][j][1] = __builtin_amdgcn_raw_buffer_load_b128(rx2, second(in, e), 0, 0);
                 }
@@ -880,7 +892,7 @@ __device__ __forceinline__ void stage1f_item(const MRun &run, const MLin &L, int
                 for (int t = 0; t < 8; ++t) {
                     const bool in = pc < npc && i + t < L.d_in;
                     const uint32_t go = in ? (uint32_t)((i + t) * 2) : kOOB;
-                    const uint32_t xo = in ? (uint32_t)(((int64_t)n * L.d_in + i + t) * xb) : kOOB;
+                    const uint32_t xo = in ? (uint32_t)(((int64_t)n * dsrc + xoff(i + t)) * xb) : kOOB;
                     const float gf = f16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rgs, go, 0, 0));
                     float xf = xf32 ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rx, xo, 0, 0))
                                     : bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rx, xo, 0, 0));
@@ -962,12 +974,12 @@ __device__ __forceinline__ void stage1f_item(const MRun &run, const MLin &L, int
     }
 }
 
-template <int NL>
+template <int NL, bool XM = false>
 __global__ __launch_bounds__(kThreads) void k_stage1f(MRun run, MLin single) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     if (stale_ws(run)) return;
     const int64_t item = item_of(run.ord1, run.base1);
-    stage1f_item<NL, false>(run, pick<kKindStage1>(run, single, run.lin1, item), item, smem);
+    stage1f_item<NL, false, XM>(run, pick<kKindStage1>(run, single, run.lin1, item), item, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -1633,7 +1645,7 @@ __global__ __launch_bounds__(kThreads) void k_stage2r(MRun run, MLin single) {
 // bounded (spin_limit polls): a wave that gives up reports
 // LB_FAULT_HANDOFF_TIMEOUT in the fault word (its outputs are wrong) and the
 // launch still ends; the counters still return to zero.
-template <int NL, int NB2>
+template <int NL, int NB2, bool XM = false>
 __global__ __launch_bounds__(kThreads) void k_pass(MRun run, MLin single) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     __shared__ uint32_t s_count;
@@ -1645,7 +1657,7 @@ __global__ __launch_bounds__(kThreads) void k_pass(MRun run, MLin single) {
         const int j = run.table ? __builtin_amdgcn_readfirstlane(run.lin1[item])
                                 : run.ninl ? inline_index<kKindStage1>(run, item) : 0;
         const MLin L = pick<kKindStage1>(run, single, run.lin1, item);
-        stage1f_item<NL, true>(run, L, item, smem);
+        stage1f_item<NL, true, XM>(run, L, item, smem);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // this wave's partial sums are stored
         __syncthreads();
         const int f = (int)((item - L.item1) / L.nchunks);          // latent group: path * nrg + rg
@@ -1804,7 +1816,9 @@ size_t plan_linear(const Linear &a, const Shape &s, bool many, MLin *m, Grain gr
         m->kcp = 0;
         m->nprep = 0;
         m->xvec = (a.d_in % 8 == 0 && ((uintptr_t)a.x & 15) == 0 && ((uintptr_t)a.x2 & 15) == 0 &&
-                   ((uintptr_t)a.g & 15) == 0) ? 1 : 0;
+                   ((uintptr_t)a.g & 15) == 0 && a.xm_dh % 8 == 0) ? 1 : 0;
+        m->xm_dh = a.xm_dh;
+        m->xm_grp = a.xm_dh ? a.xm_grp : 1;
     } else {
         int kcg = kcg_cap(s);
         if (!many)   // a lone linear: smaller chunks until the chip has work
@@ -1857,7 +1871,12 @@ int launch_all(const MRun &run, const MLin &single, const Lds &lds, hipStream_t 
     // launches with no items (a chunk of a group may have none of a kind) are skipped
     if ((stage_mask & 1) && NB1 == 1) {
         if (run.items1 > 0) {
-            k_stage1f<NL><<<(unsigned)run.items1, kThreads, lds.s1, st>>>(run, single);
+            if (run.xmap) {                // input maps: bf16 out only
+                if constexpr (NL == 2) k_stage1f<NL, true><<<(unsigned)run.items1, kThreads, lds.s1, st>>>(run, single);
+                else return LB_EUNSUPPORTED;
+            } else {
+                k_stage1f<NL><<<(unsigned)run.items1, kThreads, lds.s1, st>>>(run, single);
+            }
             if (int rc = last_launch_status()) return rc;
         }
     } else if (stage_mask & 1) {
@@ -1937,6 +1956,11 @@ void lds_add(Lds *l, const MLin &m, const Shape &s, int ops2, int64_t T, int F, 
 
 }  // namespace
 
+bool mfma_fused_stage1(int64_t T, int y_dtype) {
+    Shape s;
+    return shape_for(T, y_dtype, &s) && fused1(s);
+}
+
 bool mfma_decode_supported(int64_t T, int y_dtype) {
     Shape s;
     return shape_for(T, y_dtype, &s);
@@ -1988,6 +2012,8 @@ int single_setup(const Linear &a, void *ws, Shape *s, MLin *m, MRun *run, Lds *l
     plan_linear(a, *s, false, m, gr);
     bind_ws(m, a, *s, (uint8_t *)ws);
     *run = MRun{};
+    if (a.xm_dh && !(fused1(*s) && s->NL == 2)) return LB_EUNSUPPORTED;   // input maps: fused stage 1, bf16 out
+    run->xmap = a.xm_dh ? 1 : 0;
     run->T = (int)a.T;
     run->x_dtype = a.x_dtype;
     run->y_dtype = a.y_dtype;
@@ -2327,17 +2353,17 @@ int mfma_group_plan(const Linear *ls, int n, int64_t T, int y_dtype, void *ws, s
 
 size_t mfma_group_state_bytes() { return sizeof(MGroupHost); }
 
-template <int NL, int NB2>
+template <int NL, int NB2, bool XM = false>
 int launch_pass(const MRun &run, size_t lds, hipStream_t st) {
     static bool raised = false;        // once per instantiation (idempotent if raced)
     if (!raised) {
-        if (hipFuncSetAttribute((const void *)k_pass<NL, NB2>, hipFuncAttributeMaxDynamicSharedMemorySize,
+        if (hipFuncSetAttribute((const void *)k_pass<NL, NB2, XM>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                 160 * 1024 - 64) != hipSuccess)
             return hip_status(hipGetLastError());
         raised = true;
     }
     MLin dummy{};
-    k_pass<NL, NB2><<<(unsigned)(run.items1 + run.items2P), kThreads, lds, st>>>(run, dummy);
+    k_pass<NL, NB2, XM><<<(unsigned)(run.items1 + run.items2P), kThreads, lds, st>>>(run, dummy);
     return last_launch_status();
 }
 
@@ -2401,6 +2427,9 @@ size_t inline_setup(const Linear *ls, int n, uint8_t *ws, Shape *s, MRun *run, L
         ntile_max = imax(ntile_max, cdiv(m.r_p, kTile));
     }
     run->ninl = n;
+    for (int j = 0; j < n; ++j)
+        if (ls[j].xm_dh) run->xmap = 1;
+    if (run->xmap && !(fused1(*s) && s->NL == 2)) return 0;    // input maps: fused stage 1, bf16 out
     run->T = (int)ls[0].T;
     run->x_dtype = ls[0].x_dtype;
     run->y_dtype = ls[0].y_dtype;
@@ -2445,6 +2474,7 @@ size_t inline_setup(const Linear *ls, int n, uint8_t *ws, Shape *s, MRun *run, L
 }
 
 int launch_pass_shape(const Shape &s, const MRun &run, size_t lds, hipStream_t st) {
+    if (run.xmap) return s.NL == 2 && s.NB2 == 1 ? launch_pass<2, 1, true>(run, lds, st) : LB_EUNSUPPORTED;
     switch (s.NL * 10 + s.NB2) {
         case 21: return launch_pass<2, 1>(run, lds, st);
         case 22: return launch_pass<2, 2>(run, lds, st);

@@ -24,6 +24,11 @@ struct Linear {
     // RMSNorm's 1/rms), and a residual [T][d_out] (y's dtype) added to y
     const float *xs = nullptr;
     const void *resid = nullptr;
+    // decode kernels, fused stage 1 only (mfma_fused_stage1): input channel i
+    // reads x[n][(i / xm_dh / xm_grp) * xm_dh + i % xm_dh] from rows of
+    // d_in / xm_grp (each head of xm_dh channels of x serves xm_grp heads);
+    // xm_dh = 0: x as it is
+    int32_t xm_dh = 0, xm_grp = 1;
     int x_dtype, y_dtype;
     const uint32_t *v_bits;   // [P][kw_v][ld_v]
     const uint32_t *u_bits;   // [P][kw_u][ld_u]
@@ -101,6 +106,8 @@ struct GroupImage {
 
 // Matrix-core decode path (fp4 signs x fp8 activation limbs).
 bool mfma_decode_supported(int64_t T, int y_dtype);
+// Whether stage 1 runs in its fused form at this T (input maps apply there).
+bool mfma_fused_stage1(int64_t T, int y_dtype);
 // Whether the decode kernels' 32-bit buffer offsets cover this linear.
 bool mfma_decode_shape_ok(const Linear &a);
 size_t mfma_decode_workspace_bytes(const Linear &a);

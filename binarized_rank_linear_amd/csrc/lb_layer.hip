@@ -24,24 +24,61 @@ namespace {
 
 constexpr int kT = 256;
 
-// inv[n] = 1 / sqrt(mean(x[n]^2) + eps), bf16 x [T][d]; one workgroup per token.
-__global__ __launch_bounds__(kT) void k_rms(const uint16_t *__restrict__ x, int64_t d, float eps,
-                                            float *__restrict__ inv) {
-    const int64_t n = blockIdx.x;
-    const uint16_t *xr = x + n * d;
+// inv[n] = 1 / sqrt(mean(x[n]^2) + eps), bf16 x [T][d]: workgroup n < T sums
+// token n's squares (16-byte loads, all in flight, when rows are 16-byte
+// aligned), the waves by shuffles, then across the waves in LDS.  Workgroups
+// from T on clear `zn` 32-bit words at `zero` (a run's scratch) meanwhile.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__global__ __launch_bounds__(kT) void k_rms(const uint16_t *__restrict__ x, int64_t T, int64_t d, float eps,
+                                            float *__restrict__ inv, uint32_t *__restrict__ zero, int64_t zn) {
+    const int64_t b = blockIdx.x;
+    if (b >= T) {                                             // the clearing workgroups
+        const int64_t nz = (int64_t)gridDim.x - T;
+        for (int64_t i = (b - T) * kT + threadIdx.x; i < zn; i += nz * kT) zero[i] = 0u;
+        return;
+    }
+    const uint16_t *xr = x + b * d;
     float s = 0.0f;
-    for (int64_t i = threadIdx.x; i < d; i += kT) {
-        const float v = bf16_to_f32(xr[i]);
-        s += v * v;
+    if ((d & 7) == 0 && ((uintptr_t)x & 15) == 0) {
+        const uint4 *xv = (const uint4 *)xr;
+        const int64_t nv = d >> 3;
+        for (int64_t i0 = 0; i0 < nv; i0 += 4 * kT) {
+            uint4 q[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int64_t i = i0 + k * kT + threadIdx.x;
+                q[k] = i < nv ? xv[i] : make_uint4(0u, 0u, 0u, 0u);
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t w[4] = {q[k].x, q[k].y, q[k].z, q[k].w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float lo = __uint_as_float(w[j] << 16), hi = __uint_as_float(w[j] & 0xffff0000u);
+                    s += lo * lo + hi * hi;
+                }
+            }
+        }
+    } else {
+        for (int64_t i = threadIdx.x; i < d; i += kT) {
+            const float v = bf16_to_f32(xr[i]);
+            s += v * v;
+        }
     }
-    __shared__ float red[kT];
-    red[threadIdx.x] = s;
+    __shared__ float red[kT / 64];
+    s = wave_sum(s);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
     __syncthreads();
-    for (int w = kT / 2; w > 0; w >>= 1) {
-        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
-        __syncthreads();
+    if (threadIdx.x == 0) {
+        float t = 0.0f;
+        for (int w = 0; w < kT / 64; ++w) t += red[w];
+        inv[b] = 1.0f / sqrtf(t / (float)d + eps);
     }
-    if (threadIdx.x == 0) inv[n] = 1.0f / sqrtf(red[0] / (float)d + eps);
 }
 
 // o_in[n][h*dh + e] = v[n][(h / grp)*dh + e]: each kv head serves grp query heads.
@@ -163,11 +200,11 @@ extern "C" int lb_decoder_layer_forward(const lb_decoder_layer *L, const void *x
     uint16_t *oin = (uint16_t *)(w + p.off_oin), *x1 = (uint16_t *)(w + p.off_x1);
     uint16_t *yg = (uint16_t *)(w + p.off_g), *yu = (uint16_t *)(w + p.off_u);
     const int64_t dh = L->d_model / L->n_heads, dkv = dh * L->n_kv_heads;
-    // the runs' one-launch forms start from zeroed scratch: one clear for all four
-    if ((rc = fill_words(w + p.off_qkv, p.total - p.off_qkv, 0u, s))) return rc;
-
-    // a = x / rms(x); q, k, v
-    k_rms<<<(unsigned)T, kT, 0, s>>>((const uint16_t *)x, L->d_model, L->eps, inv);
+    // a = x / rms(x); the same launch clears the four runs' scratch (their
+    // one-launch forms start from zero); q, k, v
+    const int64_t zn = (int64_t)(p.total - p.off_qkv) / 4;
+    k_rms<<<(unsigned)(T + imin(512, cdiv(zn, kT))), kT, 0, s>>>((const uint16_t *)x, T, L->d_model, L->eps, inv,
+                                                                 (uint32_t *)(w + p.off_qkv), zn);
     if ((rc = last_launch_status())) return rc;
     p.q.x = p.k.x = p.v.x = x;
     p.q.xs = p.k.xs = p.v.xs = inv;
@@ -176,16 +213,26 @@ extern "C" int lb_decoder_layer_forward(const lb_decoder_layer *L, const void *x
     p.v.y = v;
     const Linear qkv[3] = {p.q, p.k, p.v};
     if ((rc = mfma_inline_forward(qkv, 3, w + p.off_qkv, s, true))) return rc;
-    // attention over one token, then x1 = x + O(o_in)
-    k_expand_heads<<<(unsigned)cdiv(T * L->d_model, kT), kT, 0, s>>>(v, oin, T, L->d_model, dkv, dh,
-                                                                     L->n_heads / L->n_kv_heads);
-    if ((rc = last_launch_status())) return rc;
-    p.o.x = oin;
+    // attention over one token, then x1 = x + O(o_in): without kv grouping
+    // o_in is v; with it, the fused stage 1 of o reads v through the head map,
+    // else the heads are expanded into o_in first
+    const int64_t grp = L->n_heads / L->n_kv_heads;
+    if (grp == 1) {
+        p.o.x = v;
+    } else if (mfma_fused_stage1(T, LB_BF16)) {
+        p.o.x = v;
+        p.o.xm_dh = (int32_t)dh;
+        p.o.xm_grp = (int32_t)grp;
+    } else {
+        k_expand_heads<<<(unsigned)cdiv(T * L->d_model, kT), kT, 0, s>>>(v, oin, T, L->d_model, dkv, dh, grp);
+        if ((rc = last_launch_status())) return rc;
+        p.o.x = oin;
+    }
     p.o.resid = x;
     p.o.y = x1;
     if ((rc = mfma_inline_forward(&p.o, 1, w + p.off_o, s, true))) return rc;
     // b = x1 / rms(x1); gate, up; y = x1 + Down(silu(gate) * up)
-    k_rms<<<(unsigned)T, kT, 0, s>>>(x1, L->d_model, L->eps, inv);
+    k_rms<<<(unsigned)T, kT, 0, s>>>(x1, T, L->d_model, L->eps, inv, nullptr, 0);
     if ((rc = last_launch_status())) return rc;
     p.gate.x = p.up.x = x1;
     p.gate.xs = p.up.xs = inv;

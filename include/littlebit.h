@@ -249,10 +249,14 @@ int lb_linear_stage2(const void *t, int t_dtype, void *y, int y_dtype, const lb_
  * every linear the residual path.  x, y: bf16 [T][d_model] device, 16-byte
  * aligned, not overlapping; 0 <= T <= 32 (the decode kernels;
  * LB_EUNSUPPORTED beyond; T = 0 checks the layer and does nothing; the
- * workspace query returns 0 for it and for bad arguments).  Runs 15 launches on `stream` (2 norms, q/k/v as
- * one group, the head expansion, o, gate/up as one group, down), with every
- * intermediate in ws (>= lb_decoder_layer_workspace_bytes, 256-byte aligned,
- * no contents needed).  Layers chain by passing one's y as the next one's x. */
+ * workspace query returns 0 for it and for bad arguments).  Work on `stream`:
+ * an RMS kernel (which also clears the runs' scratch), q/k/v as one group,
+ * o (reading v through the kv-head map, or after an expansion kernel when
+ * T > 8 and heads are grouped), a second RMS kernel, gate/up as one group,
+ * down; each group or linear is one launch at T <= 2 and three beyond.  Every
+ * intermediate lives in ws (>= lb_decoder_layer_workspace_bytes, 256-byte
+ * aligned, no contents needed).  Layers chain by passing one's y as the next
+ * one's x. */
 typedef struct lb_decoder_layer {
     lb_factors q, k, v, o, gate, up, down;
     int64_t d_model, d_ff, n_heads, n_kv_heads;
