@@ -916,9 +916,31 @@ struct GLayout {
 // turn, so each block of 8 * kRun items in that order is dealt out as kRun
 // consecutive items per XCD (consecutive items share activation rows in the
 // XCD's L2).
-std::vector<int32_t> dispatch_order(const std::vector<int64_t> &len) {
-    constexpr int kRun = 4;
+//
+// When every token tile's items can go to one XCD (the items split evenly
+// over the 8 XCDs by token tile modulo 8, e.g. T = 2048: 8 tiles of 256
+// tokens), they do: XCD x runs the items of token tiles x, x + 8, ...,
+// longest first, so each XCD's L2 holds its tiles' activation rows (x for
+// stage 1, t for stage 2) for all their column tiles and linears, instead of
+// fetching them again for every run of kRun items.
+std::vector<int32_t> dispatch_order(const std::vector<int64_t> &len, const std::vector<int32_t> &tok) {
     const int64_t n = (int64_t)len.size();
+    {
+        std::vector<std::vector<int32_t>> per(8);
+        for (int64_t i = 0; i < n; ++i) per[(size_t)(tok[(size_t)i] & 7)].push_back((int32_t)i);
+        bool even = n > 0;
+        for (const auto &v : per) even = even && v.size() == per[0].size();
+        if (even) {
+            std::vector<int32_t> D((size_t)n);
+            for (int x = 0; x < 8; ++x) {
+                auto &v = per[(size_t)x];
+                std::stable_sort(v.begin(), v.end(), [&](int32_t a, int32_t b) { return len[(size_t)a] > len[(size_t)b]; });
+                for (size_t j = 0; j < v.size(); ++j) D[j * 8 + (size_t)x] = v[j];
+            }
+            return D;
+        }
+    }
+    constexpr int kRun = 4;
     std::vector<int32_t> L((size_t)n);
     for (int64_t i = 0; i < n; ++i) L[(size_t)i] = (int32_t)i;
     std::stable_sort(L.begin(), L.end(), [&](int32_t a, int32_t b) { return len[(size_t)a] > len[(size_t)b]; });
@@ -1004,16 +1026,22 @@ int gemm_group_plan(const Linear *ls, int n, void *ws, size_t ws_bytes, uint64_t
     put(G.linR, hR.data(), (size_t)G.iR * 4);
     put(G.lin2, h2.data(), (size_t)G.i2 * 4);
     // item lengths in K-tiles of 64: stage 1 the item's piece of d_in, stage 2 the latents
+    // and their token tiles (item = (piece, token tile, column tile), column fastest)
     std::vector<int64_t> len1((size_t)G.i1), len2((size_t)G.i2);
+    std::vector<int32_t> tok1((size_t)G.i1), tok2((size_t)G.i2);
     for (int j = 0; j < n; ++j) {
         const GLin &m = tab[(size_t)j];
         for (int64_t k = 0; k < items1_of(m); ++k) {
             const int64_t split = k / ((int64_t)m.nt1 * m.mt);
             len1[(size_t)(m.item1 + k)] = split + 1 < m.nsplit ? m.ktps : m.nkt1 - (int64_t)(m.nsplit - 1) * m.ktps;
+            tok1[(size_t)(m.item1 + k)] = (int32_t)((k / m.nt1) % m.mt);
         }
-        for (int64_t k = 0; k < items2_of(m); ++k) len2[(size_t)(m.item2 + k)] = m.nkt2;
+        for (int64_t k = 0; k < items2_of(m); ++k) {
+            len2[(size_t)(m.item2 + k)] = m.nkt2;
+            tok2[(size_t)(m.item2 + k)] = (int32_t)((k / m.nt2) % m.mt);
+        }
     }
-    const std::vector<int32_t> o1 = dispatch_order(len1), o2 = dispatch_order(len2);
+    const std::vector<int32_t> o1 = dispatch_order(len1, tok1), o2 = dispatch_order(len2, tok2);
     put(G.ord1, o1.data(), (size_t)G.i1 * 4);
     put(G.ord2, o2.data(), (size_t)G.i2 * 4);
     // the scratch needs no initial contents (every byte a run reads it writes first)
