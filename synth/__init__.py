@@ -95,6 +95,22 @@ def unit_gain_l(d_in: int, r_path: int, paths: int) -> float:
     return 1.0 / float(np.sqrt(d_in * r_path * paths))
 
 
+def dense_weight(seed: int, d_out: int, d_in: int, decay: float = 0.6, rms: float = 0.02) -> np.ndarray:
+    """A dense fp32 weight [d_out][d_in] to initialise a layer from: random
+    orthonormal singular vectors (QR of Gaussian draws) and singular values
+    (1 + i)^-decay, scaled to the given entry RMS (a decaying spectrum, as
+    trained weights have; distinct values, so the top singular vectors are
+    well defined)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    k = min(d_out, d_in)
+    a, _ = np.linalg.qr(rng.standard_normal((d_out, k)))
+    b, _ = np.linalg.qr(rng.standard_normal((d_in, k)))
+    s = (1.0 + np.arange(k)) ** -decay
+    W = (a * s[None, :]) @ b.T
+    W *= rms / np.sqrt(np.mean(W * W))
+    return W.astype(np.float32)
+
+
 def activations(seed: int, T: int, d: int, dtype: str) -> np.ndarray:
     """x [T][d]: float32 array for dtype 'f32', uint16 bf16 bits for 'bf16'."""
     rng = np.random.Generator(np.random.PCG64(seed))

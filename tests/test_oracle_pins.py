@@ -474,3 +474,86 @@ def test_decoder_layer_norm_scale_invariance():
         y1 = oracle.decoder_layer_forward(x, lin, 4, 4, 0.0)
         yc = oracle.decoder_layer_forward(c * x, lin, 4, 4, 0.0)
         assert np.allclose(yc - c * x, y1 - x, rtol=1e-12, atol=1e-12)
+
+
+# ---- Dual-SVID initialisation (oracle/svid.py) ------------------------------
+
+def _orthonormal(rng, n, k):
+    q, _ = np.linalg.qr(rng.standard_normal((n, k)))
+    return q
+
+
+def _sylvester(n):
+    H = np.ones((1, 1))
+    while H.shape[0] < n:
+        H = np.block([[H, H], [H, -H]])
+    return H
+
+
+def test_svid_truncation_keeps_the_top_singular_values():
+    """Eckart-Young closed form on W = A diag(s) B^T with orthonormal A, B and
+    known distinct s: ||W - U' V'^T||_F^2 = sum of the dropped s_i^2, and the
+    even split gives both factors column norms^2 equal to the kept s_i."""
+    from oracle import svid
+    rng = np.random.default_rng(31)
+    s = 1.0 / np.sqrt(1.0 + np.arange(24))
+    W = _orthonormal(rng, 40, 24) @ np.diag(s) @ _orthonormal(rng, 30, 24).T
+    for r in (1, 6, 17):
+        Up, Vp = svid.truncated_factors(W, r)
+        assert np.linalg.norm(W - Up @ Vp.T) ** 2 == pytest.approx(np.sum(s[r:] ** 2), rel=1e-10)
+        assert np.allclose(np.sum(Up * Up, axis=0), s[:r], rtol=1e-12)
+        assert np.allclose(np.sum(Vp * Vp, axis=0), s[:r], rtol=1e-12)
+
+
+def test_svid_rank1_fit_of_an_exact_rank1_matrix():
+    """A nonnegative rank-1 matrix is its own best rank-1 fit; the factors come
+    back nonnegative with the singular value split evenly."""
+    from oracle import svid
+    rng = np.random.default_rng(32)
+    a, b = rng.uniform(0.1, 2.0, 23), rng.uniform(0.1, 2.0, 9)
+    x, y = svid.rank1_nonneg(np.outer(a, b))
+    assert np.allclose(np.outer(x, y), np.outer(a, b), rtol=1e-12, atol=0)
+    assert (x >= 0).all() and (y >= 0).all()
+    assert np.linalg.norm(x) == pytest.approx(np.linalg.norm(y), rel=1e-12)
+
+
+@pytest.mark.parametrize("d_out,d_in,r", [(16, 32, 4), (32, 16, 8), (64, 64, 16)])
+def test_svid_reproduces_a_hadamard_layer(d_out, d_in, r):
+    """A layer whose sign factors are orthogonal Hadamard columns and whose
+    row and column scales are constant is a rank-r matrix whose singular
+    vectors are those columns and whose factor magnitudes are exactly rank 1,
+    so the initialisation reproduces it: exactly in fp64 arithmetic, and within
+    the fp16 rounding of three scales (3 x 2^-11 per entry) as stored.  Its
+    remainder for the residual path is then zero."""
+    from oracle import svid
+    lam = 2.0 ** -np.arange(r)                       # distinct latent scales
+    W = 0.5 * _sylvester(d_out)[:, :r] @ np.diag(lam) @ _sylvester(d_in)[:, :r].T * 0.25
+    U, V, h, g, l = svid.dual_svid(W, r, residual=False, f16=False)
+    assert oracle.rel_l2(svid.reconstruction(U, V, h, g, l), W) < 1e-12
+    U, V, h, g, l = svid.dual_svid(W, r, residual=True, f16=True)
+    W1 = svid.reconstruction(U[:1], V[:1], h[:1], g[:1], l[:1])
+    assert np.max(np.abs(W1 - W) / np.abs(W)) <= 3 * 2.0 ** -11
+    assert oracle.rel_l2(svid.reconstruction(U, V, h, g, l), W) <= 3 * 2.0 ** -11
+
+
+def test_svid_scale_covariance():
+    """Scaling W by 16 scales each factor magnitude by 4, each rank-1 vector
+    by 2 and so h, g by 2 and l by 4 (powers of two: the fp16 rounding
+    commutes), so the stored layer is exactly 16 times the layer of W."""
+    from oracle import svid
+    rng = np.random.default_rng(33)
+    W = rng.standard_normal((48, 40))
+    a = svid.reconstruction(*svid.dual_svid(W, 12, residual=True))
+    b = svid.reconstruction(*svid.dual_svid(16.0 * W, 12, residual=True))
+    assert np.allclose(b, 16.0 * a, rtol=1e-12, atol=1e-12)
+
+
+def test_svid_rank1_fit_is_optimal():
+    """On a nonnegative matrix of full rank the fit's error is the smallest a
+    rank-1 matrix can have: ||M||_F^2 - ||M||_2^2 (the spectral norm computed
+    by numpy's norm routine)."""
+    from oracle import svid
+    M = np.abs(np.random.default_rng(34).standard_normal((30, 12)))
+    x, y = svid.rank1_nonneg(M)
+    err = np.linalg.norm(M - np.outer(x, y)) ** 2
+    assert err == pytest.approx(np.linalg.norm(M) ** 2 - np.linalg.norm(M, 2) ** 2, rel=1e-9)
