@@ -389,6 +389,45 @@ def decoder_stack_leg(key, T, steps, layers=0):
             "hbm_frac": nbytes / t / 1e9 / HBM_PEAK_GBS, "output_finite": finite}
 
 
+def dual_svid_leg(reps=3):
+    """The Dual-SVID initialisation (NEXT-3) of two linears from seeded dense
+    weights with a decaying spectrum: the 1024 x 1024 configuration-1 linear
+    (rank 512, one path) and a Qwen3-0.6B-shaped gate projection (1024 ->
+    3072, 0.55 bpw, with the residual path).  Seconds per linear by the host
+    clock around the synchronous call (after one untimed call), and the fp64
+    oracle's time for the same (numpy SVD on the host cores)."""
+    import torch
+    import synth
+    import oracle
+    from oracle import svid
+    import binarized_rank_linear_amd as lb
+    out = []
+    for (d_out, d_in, bn, bd, res, name) in ((1024, 1024, 1, 1, False, "1024 x 1024 linear, 1.0 bpw"),
+                                             (3072, 1024, 55, 100, True, "Qwen3-0.6B-shaped gate 1024 -> 3072, 0.55 bpw + residual")):
+        r, rp = lb.rank_for_budget(d_in, d_out, bn, bd, res)
+        W = synth.dense_weight(5, d_out, d_in)
+        Wd = torch.from_numpy(W).cuda()
+        ws = lb.workspace(lb.lib().lb_dual_svid_workspace_bytes(d_out, d_in, r, int(res)))
+        lb.dual_svid(Wd, r, res, ws=ws)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            lin = lb.dual_svid(Wd, r, res, ws=ws)
+        torch.cuda.synchronize()
+        t = (time.perf_counter() - t0) / reps
+        t0 = time.perf_counter()
+        U, V, h, g, l = svid.dual_svid(W, rp, res)
+        t_cpu = time.perf_counter() - t0
+        err = oracle.rel_l2(svid.reconstruction(U, V, h, g, l), W)
+        out.append({"workload": "Dual-SVID initialisation, %s (r = %d)" % (name, r), "s_per_linear": t,
+                    "weights_per_s": d_out * d_in / t, "relative_error_of_the_layer": err,
+                    "cpu_baseline": {"s_per_linear": t_cpu, "kind": "oracle", "cores": oracle.max_threads(),
+                                     "sample": "the same linear, numpy SVD (fp64)"}})
+        del lin, ws, Wd
+    torch.cuda.empty_cache()
+    return out
+
+
 def cache_resident_legs(reps=2000):
     """The two small configurations, whose factors stay in the caches: the
     1024 x 1024 linear at 1.0 bit per weight (fp32, T = 1 and 8) and the
@@ -586,6 +625,8 @@ def main():
                     help="only run the T=2048 prefill leg and print its JSON")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain MIB-MiB device copy (counter calibration) and exit")
+    ap.add_argument("--svid-only", action="store_true",
+                    help="only run the Dual-SVID initialisation leg and print its JSON")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other decode legs (32-layer stack at T=4 and T=32), the "
                          "cache-resident configurations and the measured ceilings")
@@ -600,6 +641,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy, max(1, args.steps))
+        return
+    if args.svid_only:
+        print(json.dumps(dual_svid_leg()), flush=True)
         return
     if args.prefill_only:
         w = synth.WORKLOADS[args.workload]
@@ -672,6 +716,7 @@ def main():
         out["decoder_chain"] = [decoder_stack_leg(args.workload, T, max(10, args.steps // 10)),
                                 decoder_stack_leg("c3", 1, max(10, args.steps // 10))]
         out["cache_resident"] = cache_resident_legs()
+        out["dual_svid"] = dual_svid_leg()
         c = ceilings()
         out["ceilings"] = c
         out["roofline"]["frac_of_measured_ceiling"] = bw / c["stream_read_GBs"]

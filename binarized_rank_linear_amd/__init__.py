@@ -149,6 +149,11 @@ def lib() -> ctypes.CDLL:
         L.lb_decoder_layer_workspace_bytes.restype = _sz
         L.lb_decoder_layer_forward.argtypes = [ctypes.POINTER(lb_decoder_layer), _vp, _vp, _i64, _vp, _sz, _vp]
         L.lb_decoder_layer_forward.restype = ctypes.c_int
+        L.lb_dual_svid_workspace_bytes.argtypes = [_i64, _i64, _i64, ctypes.c_int]
+        L.lb_dual_svid_workspace_bytes.restype = _sz
+        L.lb_dual_svid.argtypes = [_vp, _i64, _i64, _i64, ctypes.c_int, ctypes.POINTER(lb_factors), _vp, _vp,
+                                   _vp, _sz, _vp]
+        L.lb_dual_svid.restype = ctypes.c_int
         L.lb_ceiling_stream_read.argtypes = [_vp, _sz, _vp, ctypes.c_int, _vp]
         L.lb_ceiling_stream_read.restype = ctypes.c_int
         L.lb_ceiling_mfma_bf16.argtypes = [ctypes.c_int, _vp, ctypes.c_int, _vp]
@@ -454,6 +459,38 @@ class DecoderLayer:
                                               ws.data_ptr(), ws.numel(), _stream_ptr(stream)),
                "lb_decoder_layer_forward")
         return out
+
+
+def dual_svid(W, r: int, residual: bool, float_factors: bool = False, ws=None, stream=None):
+    """Dual-SVID initialisation (lb_dual_svid) of a LittleBit linear from a
+    dense fp32 weight W [d_out][d_in] on the GPU.  Returns the PackedLinear,
+    and with float_factors also the fp32 U' [P][d_out][r_p] and V' [P][d_in][r_p]."""
+    torch = _torch()
+    _dev_check(W)
+    if W.dtype != torch.float32 or W.dim() != 2:
+        raise ValueError("W must be a 2-D float32 tensor")
+    W = W.contiguous()
+    d_out, d_in = W.shape
+    P = 2 if residual else 1
+    r_p = r // P
+    ld_v, ld_u = packed_ld_aligned(r_p), packed_ld_aligned(d_out)
+    dev = W.device
+    v_bits = torch.empty((P, (d_in + 31) // 32, ld_v), dtype=torch.int32, device=dev)
+    u_bits = torch.empty((P, (r_p + 31) // 32, ld_u), dtype=torch.int32, device=dev)
+    g = torch.empty((P, d_in), dtype=torch.int16, device=dev)
+    l = torch.empty((P, r_p), dtype=torch.int16, device=dev)
+    h = torch.empty((P, d_out), dtype=torch.int16, device=dev)
+    lin = PackedLinear(d_in, d_out, r, residual, v_bits, u_bits, g, l, h, ld_v, ld_u)
+    U = torch.empty((P, d_out, r_p), dtype=torch.float32, device=dev) if float_factors else None
+    V = torch.empty((P, d_in, r_p), dtype=torch.float32, device=dev) if float_factors else None
+    need = lib().lb_dual_svid_workspace_bytes(d_out, d_in, r, int(residual))
+    if ws is None or ws.numel() < need:
+        ws = workspace(max(need, 1), dev)
+    f = lin.struct()
+    _check(lib().lb_dual_svid(W.data_ptr(), d_out, d_in, r, int(residual), ctypes.byref(f),
+                              U.data_ptr() if U is not None else None, V.data_ptr() if V is not None else None,
+                              ws.data_ptr(), ws.numel(), _stream_ptr(stream)), "lb_dual_svid")
+    return (lin, U, V) if float_factors else lin
 
 
 def device_faults(stream=None) -> int:

@@ -269,6 +269,36 @@ size_t lb_decoder_layer_workspace_bytes(const lb_decoder_layer *layer, int64_t T
 int lb_decoder_layer_forward(const lb_decoder_layer *layer, const void *x, void *y, int64_t T,
                              void *ws, size_t ws_bytes, void *stream);
 
+/* Dual-SVID initialisation of a LittleBit linear from a dense weight
+ * (sesamedisk, "How low-rank binarization works", the Dual-SVID paragraph;
+ * mlsanity, abstract).  Off the forward path: it writes the factors the
+ * forward calls read.
+ *   1. truncated SVD W ~ U_r S_r V_r^T (r_p = r / P triplets), the singular
+ *      values split evenly: U' = U_r sqrt(S_r), V' = V_r sqrt(S_r);
+ *   2. binary factors sign(U'), sign(V') (bit = value < 0);
+ *   3. |U'| ~ h l_u^T and |V'| ~ g l_v^T, best rank-1 fits (their top
+ *      singular pair, nonnegative, sqrt(sigma_1) in each vector); l = l_u (.) l_v;
+ *      h, g, l stored as fp16 (round to nearest even);
+ *   4. residual != 0: path 1 is the same on W - W_1, W_1 being path 0 as stored.
+ * w: fp32 [d_out][d_in] row-major, device, 4-byte aligned, not modified.
+ * r: total rank (even with the residual), r / P <= min(d_out, d_in).
+ * out: where the factors go, in the layout lb_linear_forward reads (the
+ *   buffers it points to are written: v_bits [P][ceil(d_in/32)][ld_v],
+ *   u_bits [P][ceil(r_p/32)][ld_u], g, l, h fp16 bits), ld_v >= r_p,
+ *   ld_u >= d_out.  u_out / v_out: optional fp32 [P][d_out][r_p] and
+ *   [P][d_in][r_p] copies of U' and V' (null: not written).  A singular
+ *   vector's sign is arbitrary: U' and V' columns may come out negated
+ *   together, which leaves the layer unchanged.
+ * ws: >= lb_dual_svid_workspace_bytes, 256-byte aligned, no contents needed.
+ * The SVD is one-sided Jacobi on the GPU; the call waits for the stream after
+ * each sweep to test convergence, so it returns with the work done (not
+ * capturable).  LB_EUNSUPPORTED if 40 sweeps do not converge or
+ * d_out * d_in >= 2^31. */
+size_t lb_dual_svid_workspace_bytes(int64_t d_out, int64_t d_in, int64_t r, int residual);
+int lb_dual_svid(const float *w, int64_t d_out, int64_t d_in, int64_t r, int residual,
+                 const lb_factors *out, float *u_out, float *v_out, void *ws, size_t ws_bytes,
+                 void *stream);
+
 /* Workspace bytes lb_mlp_forward needs.  0 on bad arguments. */
 size_t lb_mlp_workspace_bytes(int64_t d_model, int64_t d_ff, int64_t r_gu, int64_t r_down,
                               int64_t T, int residual, unsigned flags);
