@@ -154,6 +154,15 @@ def lib() -> ctypes.CDLL:
         L.lb_dual_svid.argtypes = [_vp, _i64, _i64, _i64, ctypes.c_int, ctypes.POINTER(lb_factors), _vp, _vp,
                                    _vp, _sz, _vp]
         L.lb_dual_svid.restype = ctypes.c_int
+        L.lb_dual_svid_itq_workspace_bytes.argtypes = [_i64, _i64, _i64, ctypes.c_int]
+        L.lb_dual_svid_itq_workspace_bytes.restype = _sz
+        L.lb_dual_svid_itq.argtypes = [_vp, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int,
+                                       ctypes.POINTER(lb_factors), _vp, _vp, _vp, _sz, _vp]
+        L.lb_dual_svid_itq.restype = ctypes.c_int
+        L.lb_joint_itq_workspace_bytes.argtypes = [_i64, _i64, _i64]
+        L.lb_joint_itq_workspace_bytes.restype = _sz
+        L.lb_joint_itq.argtypes = [_vp, _vp, _i64, _i64, _i64, ctypes.c_int, _vp, _vp, _vp, _vp, _sz, _vp]
+        L.lb_joint_itq.restype = ctypes.c_int
         L.lb_ceiling_stream_read.argtypes = [_vp, _sz, _vp, ctypes.c_int, _vp]
         L.lb_ceiling_stream_read.restype = ctypes.c_int
         L.lb_ceiling_mfma_bf16.argtypes = [ctypes.c_int, _vp, ctypes.c_int, _vp]
@@ -461,10 +470,13 @@ class DecoderLayer:
         return out
 
 
-def dual_svid(W, r: int, residual: bool, float_factors: bool = False, ws=None, stream=None):
-    """Dual-SVID initialisation (lb_dual_svid) of a LittleBit linear from a
-    dense fp32 weight W [d_out][d_in] on the GPU.  Returns the PackedLinear,
-    and with float_factors also the fp32 U' [P][d_out][r_p] and V' [P][d_in][r_p]."""
+def dual_svid(W, r: int, residual: bool, float_factors: bool = False, ws=None, stream=None,
+              itq_iters: int = 0):
+    """Dual-SVID initialisation (lb_dual_svid, or lb_dual_svid_itq with
+    itq_iters > 0: the LittleBit-2 Joint-ITQ rotation of each path's factors
+    first) of a LittleBit linear from a dense fp32 weight W [d_out][d_in] on
+    the GPU.  Returns the PackedLinear, and with float_factors also the fp32
+    U' [P][d_out][r_p] and V' [P][d_in][r_p]."""
     torch = _torch()
     _dev_check(W)
     if W.dtype != torch.float32 or W.dim() != 2:
@@ -483,14 +495,54 @@ def dual_svid(W, r: int, residual: bool, float_factors: bool = False, ws=None, s
     lin = PackedLinear(d_in, d_out, r, residual, v_bits, u_bits, g, l, h, ld_v, ld_u)
     U = torch.empty((P, d_out, r_p), dtype=torch.float32, device=dev) if float_factors else None
     V = torch.empty((P, d_in, r_p), dtype=torch.float32, device=dev) if float_factors else None
-    need = lib().lb_dual_svid_workspace_bytes(d_out, d_in, r, int(residual))
+    if itq_iters > 0:
+        need = lib().lb_dual_svid_itq_workspace_bytes(d_out, d_in, r, int(residual))
+    else:
+        need = lib().lb_dual_svid_workspace_bytes(d_out, d_in, r, int(residual))
     if ws is None or ws.numel() < need:
         ws = workspace(max(need, 1), dev)
     f = lin.struct()
-    _check(lib().lb_dual_svid(W.data_ptr(), d_out, d_in, r, int(residual), ctypes.byref(f),
-                              U.data_ptr() if U is not None else None, V.data_ptr() if V is not None else None,
-                              ws.data_ptr(), ws.numel(), _stream_ptr(stream)), "lb_dual_svid")
+    up = U.data_ptr() if U is not None else None
+    vp = V.data_ptr() if V is not None else None
+    if itq_iters > 0:
+        _check(lib().lb_dual_svid_itq(W.data_ptr(), d_out, d_in, r, int(residual), int(itq_iters),
+                                      ctypes.byref(f), up, vp, ws.data_ptr(), ws.numel(), _stream_ptr(stream)),
+               "lb_dual_svid_itq")
+    else:
+        _check(lib().lb_dual_svid(W.data_ptr(), d_out, d_in, r, int(residual), ctypes.byref(f), up, vp,
+                                  ws.data_ptr(), ws.numel(), _stream_ptr(stream)), "lb_dual_svid")
     return (lin, U, V) if float_factors else lin
+
+
+def joint_itq(U, V, iters: int, rot0=None, ws=None, stream=None):
+    """Joint-ITQ (lb_joint_itq) of one path's float factors U' [d_out][r_p]
+    and V' [d_in][r_p] (fp32 device tensors, rotated in place).  Returns
+    (R [r_p][r_p] fp32, objective [iters + 1] fp64): the final rotation and the
+    objective at the start and after each alternation."""
+    torch = _torch()
+    _dev_check(U, V)
+    if U.dtype != torch.float32 or V.dtype != torch.float32 or U.dim() != 2 or V.dim() != 2:
+        raise ValueError("U and V must be 2-D float32 tensors")
+    if not (U.is_contiguous() and V.is_contiguous()):
+        raise ValueError("U and V must be contiguous (they are rotated in place)")
+    d_out, r_p = U.shape
+    d_in = V.shape[0]
+    if V.shape[1] != r_p:
+        raise ValueError("U and V must have the same number of columns")
+    if rot0 is not None:
+        _dev_check(rot0)
+        if rot0.dtype != torch.float32 or tuple(rot0.shape) != (r_p, r_p):
+            raise ValueError("rot0 must be a float32 [r_p][r_p] tensor")
+        rot0 = rot0.contiguous()
+    R = torch.empty((r_p, r_p), dtype=torch.float32, device=U.device)
+    obj = torch.empty((iters + 1,), dtype=torch.float64, device=U.device)
+    need = lib().lb_joint_itq_workspace_bytes(d_out, d_in, r_p)
+    if ws is None or ws.numel() < need:
+        ws = workspace(max(need, 1), U.device)
+    _check(lib().lb_joint_itq(U.data_ptr(), V.data_ptr(), d_out, d_in, r_p, int(iters),
+                              rot0.data_ptr() if rot0 is not None else None, R.data_ptr(), obj.data_ptr(),
+                              ws.data_ptr(), ws.numel(), _stream_ptr(stream)), "lb_joint_itq")
+    return R, obj
 
 
 def device_faults(stream=None) -> int:

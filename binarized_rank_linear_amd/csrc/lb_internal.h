@@ -156,6 +156,15 @@ int gemm_group_run(const void *host_state, hipStream_t s, int stage_mask = 3);
 // through this pointer).
 uint32_t *fault_word_ptr();
 
+// Joint-ITQ (lb_itq.hip): F = [U'; V'] ([D][r] fp32, D = d_out + d_in) is
+// replaced by F R, R the rotation after `iters` alternations from rot0 (the
+// identity when null).  rot_out ([r][r]) and objective ([iters + 1] fp64)
+// are optional.  ws: itq_workspace_bytes(D, r), 256-byte aligned.  Waits for
+// the stream; LB_EUNSUPPORTED when a polar decomposition did not converge.
+size_t itq_workspace_bytes(int64_t D, int64_t r);
+int itq_rotate(float *F, int64_t D, int64_t r, int iters, const float *rot0, float *rot_out, double *objective,
+               void *ws, hipStream_t s);
+
 // SwiGLU gate: a = silu(gate) * up, elementwise over n values (fp32 in place).
 int launch_swiglu_f32(float *gate_io, const float *up, int64_t n, hipStream_t s);
 

@@ -279,10 +279,11 @@ size_t rup256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 struct SvidLayout {
     int64_t m, n;
-    size_t a, v, sigma, order, up, vp, rem, x, y, s, h32, g32, l32, flag, zero, total;
+    size_t a, v, sigma, order, up, vp, rem, x, y, s, h32, g32, l32, flag, zero, itq, total;
 };
 
-SvidLayout svid_layout(int64_t d_out, int64_t d_in, int64_t r_p, bool residual) {
+// up and vp are adjacent (U' then V': the matrix F = [U'; V'] Joint-ITQ turns).
+SvidLayout svid_layout(int64_t d_out, int64_t d_in, int64_t r_p, bool residual, bool itq) {
     SvidLayout L;
     L.m = d_out >= d_in ? d_out : d_in;
     L.n = d_out >= d_in ? d_in : d_out;
@@ -292,8 +293,8 @@ SvidLayout svid_layout(int64_t d_out, int64_t d_in, int64_t r_p, bool residual) 
     L.v = take((size_t)(L.n * L.n) * 4);
     L.sigma = take((size_t)L.n * 4);
     L.order = take((size_t)L.n * 4);
-    L.up = take((size_t)(d_out * r_p) * 4);
-    L.vp = take((size_t)(d_in * r_p) * 4);
+    L.up = take((size_t)((d_out + d_in) * r_p) * 4);
+    L.vp = L.up + (size_t)(d_out * r_p) * 4;
     L.rem = residual ? take((size_t)(d_out * d_in) * 4) : 0;
     L.x = take((size_t)(d_out + d_in) * 4);               // a (rows of U') then c (rows of V')
     L.y = take((size_t)(2 * r_p) * 4);                   // b then d
@@ -303,6 +304,7 @@ SvidLayout svid_layout(int64_t d_out, int64_t d_in, int64_t r_p, bool residual) 
     L.l32 = take((size_t)r_p * 4);
     L.flag = take(4);
     L.zero = take(8);
+    L.itq = itq ? take(itq_workspace_bytes(d_out + d_in, r_p)) : 0;
     L.total = at;
     return L;
 }
@@ -325,7 +327,7 @@ int rank1_fit(const float *mtx, int64_t rows, int64_t cols, float *x, float *y, 
 // One path on the weight at `w` (row-major [d_out][d_in]): factors, scales and
 // packed signs of path p of `out`.
 int svid_path(const float *w, int64_t d_out, int64_t d_in, int64_t r_p, int p, const lb_factors *out,
-              float *u_out, float *v_out, uint8_t *ws, const SvidLayout &L, hipStream_t st) {
+              float *u_out, float *v_out, int itq_iters, uint8_t *ws, const SvidLayout &L, hipStream_t st) {
     float *a = (float *)(ws + L.a), *v = (float *)(ws + L.v), *sigma = (float *)(ws + L.sigma);
     int32_t *order = (int32_t *)(ws + L.order);
     float *up = (float *)(ws + L.up), *vp = (float *)(ws + L.vp);
@@ -355,6 +357,10 @@ int svid_path(const float *w, int64_t d_out, int64_t d_in, int64_t r_p, int p, c
     k_take_factors<<<grid_of((d_out + d_in) * r_p), kT, 0, st>>>(a, v, sigma, order, m, n, transpose, d_out, d_in,
                                                                    r_p, up, vp);
     if (int rc = last_launch_status()) return rc;
+    // LittleBit-2: turn both factors by the Joint-ITQ rotation before the signs
+    if (itq_iters > 0)
+        if (int rc = itq_rotate(up, d_out + d_in, r_p, itq_iters, nullptr, nullptr, nullptr, ws + L.itq, st))
+            return rc;
     // rank-1 fits of |U'| and |V'|
     float *xa = (float *)(ws + L.x), *xc = xa + d_out, *yb = (float *)(ws + L.y), *yd = yb + r_p;
     float *s = (float *)(ws + L.s);
@@ -398,23 +404,20 @@ int svid_check(const float *w, int64_t d_out, int64_t d_in, int64_t r, int resid
 }  // namespace
 }  // namespace lb
 
-extern "C" size_t lb_dual_svid_workspace_bytes(int64_t d_out, int64_t d_in, int64_t r, int residual) {
-    if (d_out <= 0 || d_in <= 0 || r <= 0 || r % (residual ? 2 : 1)) return 0;
-    return lb::svid_layout(d_out, d_in, r / (residual ? 2 : 1), residual != 0).total;
-}
+namespace lb {
+namespace {
 
-extern "C" int lb_dual_svid(const float *w, int64_t d_out, int64_t d_in, int64_t r, int residual,
-                            const lb_factors *out, float *u_out, float *v_out, void *ws, size_t ws_bytes,
-                            void *stream) {
-    using namespace lb;
+int dual_svid_run(const float *w, int64_t d_out, int64_t d_in, int64_t r, int residual, int itq_iters,
+                  const lb_factors *out, float *u_out, float *v_out, void *ws, size_t ws_bytes, void *stream) {
     if (int rc = svid_check(w, d_out, d_in, r, residual, out)) return rc;
+    if (itq_iters < 0) return LB_EINVAL;
     const int64_t r_p = r / (residual ? 2 : 1);
-    const SvidLayout L = svid_layout(d_out, d_in, r_p, residual != 0);
+    const SvidLayout L = svid_layout(d_out, d_in, r_p, residual != 0, itq_iters > 0);
     if (!ws || ws_bytes < L.total) return LB_EWORKSPACE;
     if ((uintptr_t)ws & 255) return LB_EALIGN;
     hipStream_t st = (hipStream_t)stream;
     uint8_t *wsb = (uint8_t *)ws;
-    if (int rc = svid_path(w, d_out, d_in, r_p, 0, out, u_out, v_out, wsb, L, st)) return rc;
+    if (int rc = svid_path(w, d_out, d_in, r_p, 0, out, u_out, v_out, itq_iters, wsb, L, st)) return rc;
     if (!residual) return LB_OK;
     float *rem = (float *)(wsb + L.rem);
     dim3 grid((unsigned)cdiv(d_in, kRT), (unsigned)cdiv(d_out, kRT));
@@ -422,5 +425,30 @@ extern "C" int lb_dual_svid(const float *w, int64_t d_out, int64_t d_in, int64_t
                                      (const float *)(wsb + L.h32), (const float *)(wsb + L.g32),
                                      (const float *)(wsb + L.l32), d_out, d_in, r_p, rem);
     if (int rc = last_launch_status()) return rc;
-    return svid_path(rem, d_out, d_in, r_p, 1, out, u_out, v_out, wsb, L, st);
+    return svid_path(rem, d_out, d_in, r_p, 1, out, u_out, v_out, itq_iters, wsb, L, st);
+}
+
+}  // namespace
+}  // namespace lb
+
+extern "C" size_t lb_dual_svid_workspace_bytes(int64_t d_out, int64_t d_in, int64_t r, int residual) {
+    if (d_out <= 0 || d_in <= 0 || r <= 0 || r % (residual ? 2 : 1)) return 0;
+    return lb::svid_layout(d_out, d_in, r / (residual ? 2 : 1), residual != 0, false).total;
+}
+
+extern "C" int lb_dual_svid(const float *w, int64_t d_out, int64_t d_in, int64_t r, int residual,
+                            const lb_factors *out, float *u_out, float *v_out, void *ws, size_t ws_bytes,
+                            void *stream) {
+    return lb::dual_svid_run(w, d_out, d_in, r, residual, 0, out, u_out, v_out, ws, ws_bytes, stream);
+}
+
+extern "C" size_t lb_dual_svid_itq_workspace_bytes(int64_t d_out, int64_t d_in, int64_t r, int residual) {
+    if (d_out <= 0 || d_in <= 0 || r <= 0 || r % (residual ? 2 : 1)) return 0;
+    return lb::svid_layout(d_out, d_in, r / (residual ? 2 : 1), residual != 0, true).total;
+}
+
+extern "C" int lb_dual_svid_itq(const float *w, int64_t d_out, int64_t d_in, int64_t r, int residual,
+                                int itq_iters, const lb_factors *out, float *u_out, float *v_out, void *ws,
+                                size_t ws_bytes, void *stream) {
+    return lb::dual_svid_run(w, d_out, d_in, r, residual, itq_iters, out, u_out, v_out, ws, ws_bytes, stream);
 }

@@ -299,6 +299,44 @@ int lb_dual_svid(const float *w, int64_t d_out, int64_t d_in, int64_t r, int res
                  const lb_factors *out, float *u_out, float *v_out, void *ws, size_t ws_bytes,
                  void *stream);
 
+/* Joint-ITQ rotation of a path's latent factors (LittleBit-2: littlebitllm,
+ * hero and "The method"; trove, "How it works", step 2; deniz.in,
+ * "LittleBit-2 fixes the initialization": a rotation of the latent space that
+ * lines the SVD-derived factors up with the binary hypercube and folds into
+ * them).  Off the forward path.  For an orthogonal R, (U'R)(V'R)^T = U'V'^T;
+ * R is chosen to minimise
+ *     Q(R) = ||sign(U'R) - U'R||_F^2 + ||sign(V'R) - V'R||_F^2
+ * by `iters` alternations of: codes B = sign of the rotated factors (+1 for
+ * zero), then R = the orthogonal polar factor of U'^T B_u + V'^T B_v (the
+ * orthogonal Procrustes solution, computed by Newton-Schulz iteration in fp32).
+ * u: fp32 [d_out][r_p] U', v: fp32 [d_in][r_p] V' (device, row-major), both
+ *   replaced by the rotated factors U'R, V'R.  r_p <= min(d_out, d_in).
+ * rot0: optional fp32 [r_p][r_p] starting rotation (null: the identity, the
+ *   unrotated factors); rot: optional fp32 [r_p][r_p] output, the final R.
+ * objective: optional fp64 [iters + 1] device array: Q at the start and after
+ *   each alternation (never increasing, up to fp32 rounding).
+ * ws: >= lb_joint_itq_workspace_bytes, 256-byte aligned, no contents needed.
+ * The call waits for the stream (it reads the polar iteration's progress) and
+ * returns with the work done; not capturable.  LB_EUNSUPPORTED when a polar
+ * decomposition did not converge in 64 iterations (u, v hold the factors
+ * rotated by the last R that did), or (d_out + d_in) * r_p >= 2^31. */
+size_t lb_joint_itq_workspace_bytes(int64_t d_out, int64_t d_in, int64_t r_p);
+int lb_joint_itq(float *u, float *v, int64_t d_out, int64_t d_in, int64_t r_p, int iters,
+                 const float *rot0, float *rot, double *objective, void *ws, size_t ws_bytes, void *stream);
+
+/* Dual-SVID initialisation with the Joint-ITQ rotation (LittleBit-2): as
+ * lb_dual_svid, with each path's U' and V' turned by lb_joint_itq's rotation
+ * (itq_iters alternations from the identity) between the SVD split and the
+ * signs and scales; the residual path is fitted to what the first path, as
+ * stored, leaves.  itq_iters = 0 gives lb_dual_svid's result.  u_out / v_out
+ * receive the rotated factors.  ws: >= lb_dual_svid_itq_workspace_bytes.
+ * Waits for the stream; LB_EUNSUPPORTED as lb_dual_svid, or when a polar
+ * decomposition did not converge. */
+size_t lb_dual_svid_itq_workspace_bytes(int64_t d_out, int64_t d_in, int64_t r, int residual);
+int lb_dual_svid_itq(const float *w, int64_t d_out, int64_t d_in, int64_t r, int residual, int itq_iters,
+                     const lb_factors *out, float *u_out, float *v_out, void *ws, size_t ws_bytes,
+                     void *stream);
+
 /* Workspace bytes lb_mlp_forward needs.  0 on bad arguments. */
 size_t lb_mlp_workspace_bytes(int64_t d_model, int64_t d_ff, int64_t r_gu, int64_t r_down,
                               int64_t T, int residual, unsigned flags);

@@ -261,3 +261,41 @@ def test_decoder_layer_argument_errors():
     assert run(n=need - 1) == lb.LB_EWORKSPACE
     assert run(ws=WS + 16) == lb.LB_EALIGN
     assert run(ws=X - 256) == lb.LB_EINVAL                   # ws overlaps x
+
+
+def test_joint_itq_argument_errors():
+    """lb_joint_itq and lb_dual_svid_itq reject bad arguments before any
+    launch or copy (fake device addresses)."""
+    L = lb.lib()
+    U, V, R0, OBJ, WS = FAKE + 0x100000, FAKE + 0x900000, FAKE + 0x1100000, FAKE + 0x1200000, FAKE + 0x2000000
+    need = L.lb_joint_itq_workspace_bytes(96, 64, 16)
+    assert need >= (96 + 64) * 16 * 4 * 2
+    assert L.lb_joint_itq_workspace_bytes(0, 64, 16) == 0
+    assert L.lb_joint_itq_workspace_bytes(96, 64, 0) == 0
+    run = lambda **k: L.lb_joint_itq(k.get("u", U), k.get("v", V), k.get("d_out", 96), k.get("d_in", 64),
+                                     k.get("r_p", 16), k.get("iters", 4), k.get("rot0", None), k.get("rot", None),
+                                     k.get("obj", None), k.get("ws", WS), k.get("n", need), None)
+    assert run(u=None) == lb.LB_EINVAL
+    assert run(v=None) == lb.LB_EINVAL
+    assert run(iters=-1) == lb.LB_EINVAL
+    assert run(r_p=65) == lb.LB_EINVAL                      # more latents than min(d_out, d_in)
+    assert run(r_p=0) == lb.LB_EINVAL
+    assert run(u=U + 2) == lb.LB_EALIGN
+    assert run(rot0=R0 + 1) == lb.LB_EALIGN
+    assert run(obj=OBJ + 4) == lb.LB_EALIGN                 # fp64 objective
+    assert run(ws=None) == lb.LB_EWORKSPACE
+    assert run(n=need - 1) == lb.LB_EWORKSPACE
+    assert run(ws=WS + 64) == lb.LB_EALIGN
+    assert run(d_out=1 << 20, d_in=1 << 20, r_p=1024, n=1 << 40) == lb.LB_EUNSUPPORTED
+    f = _factors(ld_v=16, ld_u=96)
+    Wp = FAKE + 0x3000000
+    nsv = L.lb_dual_svid_itq_workspace_bytes(96, 64, 32, 1)
+    assert nsv > L.lb_dual_svid_workspace_bytes(96, 64, 32, 1)
+    assert L.lb_dual_svid_itq_workspace_bytes(96, 64, 33, 1) == 0      # odd rank with the residual
+    sv = lambda **k: L.lb_dual_svid_itq(k.get("w", Wp), 96, 64, k.get("r", 32), 1, k.get("iters", 5),
+                                        ctypes.byref(f), None, None, k.get("ws", WS), k.get("n", nsv), None)
+    assert sv(iters=-1) == lb.LB_EINVAL
+    assert sv(w=None) == lb.LB_EINVAL
+    assert sv(r=33) == lb.LB_EINVAL
+    assert sv(n=nsv - 1) == lb.LB_EWORKSPACE
+    assert sv(ws=WS + 8) == lb.LB_EALIGN
