@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
+FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector
 METRIC = "LittleBit layer tok/s at T=1 and T=2048; % HBM BW / % MFMA peak"
 # a decode group at T <= 8 (bf16 out) runs one launch per pass: k_pass holds
 # stage 1, the latents and stage 2 of every linear
@@ -390,12 +391,15 @@ def decoder_stack_leg(key, T, steps, layers=0):
 
 
 def dual_svid_leg(reps=3):
-    """The Dual-SVID initialisation (NEXT-3) of two linears from seeded dense
+    """The Dual-SVID initialisation of two linears from seeded dense
     weights with a decaying spectrum: the 1024 x 1024 configuration-1 linear
     (rank 512, one path) and a Qwen3-0.6B-shaped gate projection (1024 ->
     3072, 0.55 bpw, with the residual path).  Seconds per linear by the host
     clock around the synchronous call (after one untimed call), and the fp64
-    oracle's time for the same (numpy SVD on the host cores)."""
+    oracle's time for the same (numpy SVD on the host cores); the same with
+    the Joint-ITQ rotation of each path (20 alternations) and the layer's
+    relative error with it."""
+    import numpy as np
     import torch
     import synth
     import oracle
@@ -419,11 +423,84 @@ def dual_svid_leg(reps=3):
         U, V, h, g, l = svid.dual_svid(W, rp, res)
         t_cpu = time.perf_counter() - t0
         err = oracle.rel_l2(svid.reconstruction(U, V, h, g, l), W)
+        # with the Joint-ITQ rotation (LittleBit-2), 20 alternations per path
+        wsi = lb.workspace(lb.lib().lb_dual_svid_itq_workspace_bytes(d_out, d_in, r, int(res)))
+        lb.dual_svid(Wd, r, res, ws=wsi, itq_iters=20)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        lin_i, Ui, Vi = lb.dual_svid(Wd, r, res, ws=wsi, itq_iters=20, float_factors=True)
+        torch.cuda.synchronize()
+        t_itq = time.perf_counter() - t0
+        err_itq = oracle.rel_l2(svid.reconstruction(
+            Ui.cpu().numpy().astype(np.float64), Vi.cpu().numpy().astype(np.float64),
+            lin_i.h.cpu().numpy().view(np.uint16), lin_i.g.cpu().numpy().view(np.uint16),
+            lin_i.l.cpu().numpy().view(np.uint16)), W)
         out.append({"workload": "Dual-SVID initialisation, %s (r = %d)" % (name, r), "s_per_linear": t,
                     "weights_per_s": d_out * d_in / t, "relative_error_of_the_layer": err,
+                    "with_joint_itq": {"alternations": 20, "s_per_linear": t_itq,
+                                       "relative_error_of_the_layer": err_itq},
                     "cpu_baseline": {"s_per_linear": t_cpu, "kind": "oracle", "cores": oracle.max_threads(),
                                      "sample": "the same linear, numpy SVD (fp64)"}})
-        del lin, ws, Wd
+        del lin, ws, Wd, wsi, lin_i, Ui, Vi
+    torch.cuda.empty_cache()
+    return out
+
+
+def blas_threads():
+    """Threads numpy's BLAS and LAPACK calls may use (the OpenMP setting)."""
+    return int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+
+def joint_itq_leg(iters=10):
+    """The Joint-ITQ rotation (LittleBit-2 initialisation) of one path's
+    factors at two layer shapes: a Llama2-7B-shaped gate projection (4096 ->
+    11008, 1.0 bpw with the residual: r_p = 1488) and a Llama2-70B-shaped
+    down projection (28672 -> 8192, 0.1 bpw with the residual: r_p = 304).
+    The factors are seeded on the GPU: Gaussian columns scaled to unit norm
+    times sqrt(s_k), s_k = (1 + k)^-0.6 (the shape of an SVD split of a
+    weight with a decaying spectrum).  Seconds per alternation by the host
+    clock around one synchronous call of `iters` alternations (after a call
+    of one); the rate counts the two GEMMs over the long side (4 D r_p^2
+    flops per alternation, D = d_out + d_in), not the polar step's, against
+    the fp32 vector peak; the oracle (numpy fp64) runs two alternations on the
+    same factors."""
+    import numpy as np
+    import torch
+    from oracle import itq
+    import binarized_rank_linear_amd as lb
+    out = []
+    for (d_out, d_in, r_p, name) in ((11008, 4096, 1488, "Llama2-7B-shaped gate 4096 -> 11008, 1.0 bpw + residual"),
+                                     (8192, 28672, 304, "Llama2-70B-shaped down 28672 -> 8192, 0.1 bpw + residual")):
+        g = torch.Generator(device="cuda").manual_seed(7)
+        sk = (1.0 + torch.arange(r_p, device="cuda", dtype=torch.float32)) ** -0.3
+        U = torch.randn((d_out, r_p), device="cuda", generator=g) * (sk / float(np.sqrt(d_out)))
+        V = torch.randn((d_in, r_p), device="cuda", generator=g) * (sk / float(np.sqrt(d_in)))
+        ws = lb.workspace(lb.lib().lb_joint_itq_workspace_bytes(d_out, d_in, r_p))
+        lb.joint_itq(U.clone(), V.clone(), 1, ws=ws)
+        torch.cuda.synchronize()
+        Ua, Va = U.clone(), V.clone()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        R, obj = lb.joint_itq(Ua, Va, iters, ws=ws)
+        torch.cuda.synchronize()
+        t = (time.perf_counter() - t0) / iters
+        o = obj.cpu().numpy()
+        D = d_out + d_in
+        rate = 4.0 * D * r_p * r_p / t / 1e12
+        Uh, Vh = U.cpu().numpy().astype(np.float64), V.cpu().numpy().astype(np.float64)
+        t0 = time.perf_counter()
+        _, qo = itq.joint_itq(Uh, Vh, 2)
+        t_cpu = (time.perf_counter() - t0) / 2
+        out.append({"workload": "Joint-ITQ rotation, %s: one path's factors (r_p = %d), %d alternations"
+                                % (name, r_p, iters),
+                    "s_per_alternation": t, "objective_start": float(o[0]), "objective_end": float(o[-1]),
+                    "oracle_objective_after_2": float(qo[-1]), "gpu_objective_after_2": float(o[2]),
+                    "roofline": {"bound": "alu", "achieved": rate, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                 "frac": rate / FP32_PEAK_TFLOPS,
+                                 "counts": "4 D r_p^2 flops per alternation (the two GEMMs over the long side)"},
+                    "cpu_baseline": {"s_per_alternation": t_cpu, "kind": "oracle", "cores": blas_threads(),
+                                     "sample": "two alternations on the same factors, numpy fp64"}})
+        del U, V, Ua, Va, ws
     torch.cuda.empty_cache()
     return out
 
@@ -627,6 +704,8 @@ def main():
                     help="only run a plain MIB-MiB device copy (counter calibration) and exit")
     ap.add_argument("--svid-only", action="store_true",
                     help="only run the Dual-SVID initialisation leg and print its JSON")
+    ap.add_argument("--itq-only", action="store_true",
+                    help="only run the Joint-ITQ leg and print its JSON")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other decode legs (32-layer stack at T=4 and T=32), the "
                          "cache-resident configurations and the measured ceilings")
@@ -644,6 +723,9 @@ def main():
         return
     if args.svid_only:
         print(json.dumps(dual_svid_leg()), flush=True)
+        return
+    if args.itq_only:
+        print(json.dumps(joint_itq_leg()), flush=True)
         return
     if args.prefill_only:
         w = synth.WORKLOADS[args.workload]
@@ -717,6 +799,7 @@ def main():
                                 decoder_stack_leg("c3", 1, max(10, args.steps // 10))]
         out["cache_resident"] = cache_resident_legs()
         out["dual_svid"] = dual_svid_leg()
+        out["joint_itq"] = joint_itq_leg()
         c = ceilings()
         out["ceilings"] = c
         out["roofline"]["frac_of_measured_ceiling"] = bw / c["stream_read_GBs"]

@@ -12,8 +12,8 @@
 // orthogonal Procrustes solution).  The two factors are kept as one matrix
 // F = [U'; V'] ([D][r], D = d_out + d_in), so each step is
 //     A = F R,  Z = F^T sign(A),  R = polar(Z)
-// -- two fp32 GEMMs over the long side and a polar decomposition of an r x r
-// matrix.  The polar factor comes from the Newton-Schulz iteration
+// -- two fp32 GEMMs over the long side (on the fp32 matrix cores) and a polar
+// decomposition of an r x r matrix.  The polar factor comes from the Newton-Schulz iteration
 // X <- X (3 I - X^T X) / 2, started from Z / ||Z^T Z||_F^(1/2) (largest
 // singular value at most 1): GEMMs only, no SVD.
 #include <math.h>
@@ -33,12 +33,17 @@ constexpr float kPolarNear = 1e-2f;     // max |X^T X - I| below which two more 
 // Polar-iteration states (one int in the workspace).
 enum : int { kRunning = 0, kStop = 3, kKeep = 4 };
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
 // C = alpha * op(A) * s(B) over the K range of this split (blockIdx.z):
 // op(A) = A ([M][K], lda) or, with TA, A^T with A stored [K][M] (lda); B is
 // [K][N] (ldb); s(B) = B, or its signs (+1 for zero) with SIGNB.  128 x 128
-// outputs per workgroup, 8 x 8 per thread (rows ty*4+i and 64+ty*4+i, columns
-// likewise with tx), K in steps of 16 through double-buffered LDS.  Split z
-// writes C + z * split_stride.  Does nothing once *stop >= kStop.
+// outputs per workgroup, K in steps of 16 through double-buffered LDS; each
+// wave computes 64 x 64 of them as 2 x 2 blocks of v_mfma_f32_32x32x2_f32
+// (fp32 matrix cores: lane l supplies row l%32 of the A block and column
+// l%32 of the B block at k = l/32; it holds D[8(v/4) + 4(l/32) + v%4][l%32]
+// in accumulator v).  Split z writes C + z * split_stride.  Does nothing
+// once *stop >= kStop.
 template <bool TA, bool SIGNB>
 __global__ __launch_bounds__(NT) void k_sgemm(int64_t M, int64_t N, int64_t K, int64_t kchunk,
                                               const float *__restrict__ A, int64_t lda,
@@ -48,7 +53,10 @@ __global__ __launch_bounds__(NT) void k_sgemm(int64_t M, int64_t N, int64_t K, i
     if (stop && *stop >= kStop) return;
     __shared__ __align__(16) float As[2][BK][BM + 4];
     __shared__ __align__(16) float Bs[2][BK][BN + 4];
-    const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = (wave & 1) * 64, wn = (wave >> 1) * 64;
+    const int l32 = lane & 31, kh = lane >> 5;
     const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
     const int64_t kb = (int64_t)blockIdx.z * kchunk;
     const int64_t ke = kb + kchunk < K ? kb + kchunk : K;
@@ -88,11 +96,13 @@ __global__ __launch_bounds__(NT) void k_sgemm(int64_t M, int64_t N, int64_t K, i
             Bs[buf][e / BN][e % BN] = rb[i];
         }
     };
-    float acc[8][8];
+    f32x16 acc[2][2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
     load(kb);
     store(0);
     __syncthreads();
@@ -101,32 +111,30 @@ __global__ __launch_bounds__(NT) void k_sgemm(int64_t M, int64_t N, int64_t K, i
         const bool more = k0 + BK < ke;
         if (more) load(k0 + BK);
 #pragma unroll
-        for (int kk = 0; kk < BK; ++kk) {
-            const float4 a0 = *(const float4 *)&As[buf][kk][ty * 4];
-            const float4 a1 = *(const float4 *)&As[buf][kk][64 + ty * 4];
-            const float4 b0 = *(const float4 *)&Bs[buf][kk][tx * 4];
-            const float4 b1 = *(const float4 *)&Bs[buf][kk][64 + tx * 4];
-            const float a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-            const float b[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+        for (int kk = 0; kk < BK; kk += 2) {
+            const float a0 = As[buf][kk + kh][wm + l32], a1 = As[buf][kk + kh][wm + 32 + l32];
+            const float b0 = Bs[buf][kk + kh][wn + l32], b1 = Bs[buf][kk + kh][wn + 32 + l32];
+            acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
+            acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
+            acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
+            acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
         }
         if (more) store(buf ^ 1);
         __syncthreads();
         buf ^= 1;
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int64_t row = m0 + (i < 4 ? ty * 4 + i : 64 + ty * 4 + i - 4);
-        if (row >= M) continue;
+    for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int64_t col = n0 + (j < 4 ? tx * 4 + j : 64 + tx * 4 + j - 4);
-            if (col < N) C[row * ldc + col] = alpha * acc[i][j];
+        for (int bj = 0; bj < 2; ++bj) {
+            const int64_t col = n0 + wn + 32 * bj + l32;
+            if (col >= N) continue;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int64_t row = m0 + wm + 32 * bi + 8 * (v >> 2) + 4 * kh + (v & 3);
+                if (row < M) C[row * ldc + col] = alpha * acc[bi][bj][v];
+            }
         }
-    }
 }
 
 // C[i][j] = alpha * sum_z parts[z][i][j] (z in order).
