@@ -375,22 +375,36 @@ __global__ __launch_bounds__(kThreads, NBW == 4 ? 1 : 2) void k_gemm(GRun run, G
         const uint8_t *A = smem + slot * Slot;
         const uint8_t *Xw = A + kABytes + wave * (XWave + kGWave);
         const uint8_t *G = Xw + XWave;
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
+        // operands of step st+1 are read from LDS before step st's matrix
+        // instructions (two register sets), so their latency hides behind them
+        u32x4 act[2][4], scr[2][NBW];
+        uint32_t xsr[2][NBW];
+        auto fetch = [&](int st, int bi) {
             const int w2 = st >> 1, s = st & 1;
-            u32x4 act[4];
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb) {
                 const int row = wm * 128 + mb * 32 + l32;
                 const int chunk = 2 * st + hh;
-                act[mb] = *(const u32x4 *)(A + row * kRowBytes + ((chunk ^ swz(row)) << 4));
+                act[bi][mb] = *(const u32x4 *)(A + row * kRowBytes + ((chunk ^ swz(row)) << 4));
             }
 #pragma unroll
             for (int b = 0; b < NBW; ++b) {
-                const uint32_t xs = ((const uint32_t *)Xw)[w2 * NBW * 32 + b * 32 + l32] << xshift;
+                xsr[bi][b] = ((const uint32_t *)Xw)[w2 * NBW * 32 + b * 32 + l32];
+                if (STAGE == 1) scr[bi][b] = *(const u32x4 *)(G + gofs[b] + (32 * w2 + 16 * s) * 2);
+            }
+        };
+        fetch(0, 0);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const int w2 = st >> 1, s = st & 1, bi = st & 1;
+            if (st < 3) fetch(st + 1, bi ^ 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int b = 0; b < NBW; ++b) {
+                const uint32_t xs = xsr[bi][b] << xshift;
                 u32x4 sc;
                 if (STAGE == 1) {
-                    sc = *(const u32x4 *)(G + gofs[b] + (32 * w2 + 16 * s) * 2);
+                    sc = scr[bi][b];
                 } else {
                     const uint32_t hp = (kt * 2 + w2) >= L.kw ? hpair[b][1] : hpair[b][0];
                     sc = u32x4{hp, hp, hp, hp};
@@ -400,7 +414,7 @@ __global__ __launch_bounds__(kThreads, NBW == 4 ? 1 : 2) void k_gemm(GRun run, G
                 for (int jj = 0; jj < 4; ++jj)
                     sg[jj] = sc[jj] ^ ((xs << (11 - 8 * s - jj)) & 0x80008000u);
 #pragma unroll
-                for (int mb = 0; mb < 4; ++mb) acc[b][mb] = mfma(sg, act[mb], acc[b][mb]);
+                for (int mb = 0; mb < 4; ++mb) acc[b][mb] = mfma(sg, act[bi][mb], acc[b][mb]);
             }
         }
     };

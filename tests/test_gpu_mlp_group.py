@@ -103,10 +103,11 @@ def test_small_stack_all_layers(key, T):
     _stack_check(key, 2, T, {0, 1})
 
 
-@pytest.mark.parametrize("key,T", [("c5", 100), ("c4", 300), ("c3", 64)])
+@pytest.mark.parametrize("key,T", [("c5", 100), ("c4", 300), ("c3", 64), ("c5", 2048), ("c4", 1800), ("c3", 2000)])
 def test_prefill_layer_group(key, T):
     """One decoder layer's linears as one GEMM-path group (one launch per
-    stage for all seven), sampled tokens and rows."""
+    stage for all seven), sampled tokens and rows; also at the prefill
+    length (T = 2048) and with a partial last token tile (1800, 2000)."""
     _stack_check(key, 1, T, {0}, rows_per=256, tokens=[0, 1, T // 2, T - 2, T - 1])
 
 
