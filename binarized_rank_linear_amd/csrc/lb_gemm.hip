@@ -21,9 +21,9 @@
 // operand), so the accumulator quad of a lane holds 4 consecutive output
 // columns of one token: one 8-byte store of bf16.
 //
-// Tiles: 256 tokens x 128 columns, K-tiles of 64 elements double-buffered in
-// LDS (activations with a 16-byte XOR swizzle, unzipped sign words, scales),
-// 4 waves of 128 x 64.  Stage 1 splits d_in into pieces of at most 8192 when
+// Tiles: 256 tokens (stage 1) or 128 tokens (stage 2) x 128 columns, K-tiles
+// of 64 elements double-buffered in LDS (activations with a 16-byte XOR
+// swizzle, unzipped sign words, scales), 4 waves of 128 (64) x 64.  Stage 1 splits d_in into pieces of at most 8192 when
 // it is longer; a reduce pass then adds the pieces in order.  A launch covers
 // every linear of a group (a table maps work items to linears), and work items
 // are renumbered so that each of the 8 XCDs (own L2) gets a contiguous range:
@@ -48,28 +48,36 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 namespace {
 
-constexpr int kBM = 256;                     // tokens per tile
+// Tokens per tile: 256 in stage 1 (long K: the sign operand a wave builds
+// serves 128 tokens), 128 in stage 2 (short K, the latents: smaller tiles let
+// three workgroups share a CU, whose tiles' epilogues and prologues overlap
+// each other's matrix work).
+constexpr int kBM1 = 256, kBM2 = 128;
 constexpr int kBK = 64;                      // contraction elements per K-tile (two packed words)
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kRowBytes = kBK * 2;           // one activation row of a K-tile (bf16)
-constexpr int kABytes = kBM * kRowBytes;     // 32 KB
 constexpr int kGWave = 2 * kBK * 2;          // a wave's bf16 g: [2 paths][kBK]
 
-// Two tile shapes, by n-blocks (32 columns) per wave NBW; waves are 2 x 2:
-//   NBW = 2: 256 x 128 tiles, 128 x 64 per wave, 2-slot ring (70 KB): two
-//            workgroups per CU (stage 1: few, long tiles)
+// Tile shapes by n-blocks (32 columns) per wave NBW and tokens per tile BM;
+// waves are 2 x 2:
+//   NBW = 2: BM x 128 tiles, BM/2 x 64 per wave, 2-slot ring (70 KB at BM =
+//            256: two workgroups per CU; 38 KB at BM = 128: three)
 //   NBW = 4: 256 x 256 tiles, 128 x 128 per wave (accumulators in AGPRs),
 //            4-slot ring (148 KB): one workgroup per CU, three K-tiles in flight
-template <int NBW> struct Shape {
+template <int NBW, int BM> struct Shape {
     static constexpr int BN = 64 * NBW;
+    static constexpr int ABytes = BM * kRowBytes;      // activation rows of a K-tile
     static constexpr int XWave = 2 * NBW * 32 * 4;     // a wave's sign words: [2 words][NBW*32]
-    static constexpr int Slot = kABytes + kWaves * (XWave + kGWave);
+    static constexpr int Slot = ABytes + kWaves * (XWave + kGWave);
     static constexpr int Stages = NBW == 4 ? 4 : 2;
     static constexpr int Lds = Stages * Slot;
+    static constexpr int MinWG = NBW == 4 ? 1 : (BM == 256 ? 2 : 3);   // workgroups per CU
 };
 constexpr int kNBW1 = 2, kNBW2 = 2;          // stage 1, stage 2
-constexpr int kBN1 = Shape<kNBW1>::BN, kBN2 = Shape<kNBW2>::BN;
+using Shape1 = Shape<kNBW1, kBM1>;
+using Shape2 = Shape<kNBW2, kBM2>;
+constexpr int kBN1 = Shape1::BN, kBN2 = Shape2::BN;
 constexpr int kWG1 = 512;                    // stage-1 workgroups a launch aims for: two per
                                              // CU on 256 CUs, so no CU runs a second round
 constexpr uint32_t kOOB = 0x7ffffff0u;       // a buffer offset past every range: reads as zero
@@ -92,7 +100,8 @@ struct GLin {
     int32_t ldt;          // latent row stride: P*kw*32 rounded up to kBK
     int32_t nsplit, ktps; // stage-1 pieces and K-tiles per piece
     int32_t nkt1, nkt2;   // K-tiles of stage 1 (d_in) and stage 2 (ldt)
-    int32_t mt, nt1, nt2; // token tiles; column tiles of stage 1 (ldt) and stage 2 (d_out)
+    int32_t mt, nt1, nt2; // token tiles of stage 1; column tiles of stage 1 (ldt) and stage 2 (d_out)
+    int32_t mt2;          // token tiles of stage 2
     int32_t nred;         // reduce items (nsplit > 1), 0 otherwise
     int32_t ngp;          // prep items
     int64_t itemG, item1, itemR, item2;
@@ -209,10 +218,13 @@ __device__ __forceinline__ f32x16 mfma(const u32x4 &s, const u32x4 &a, f32x16 c)
 // STAGE 1: A = x (bf16), sign words of V, scales g; output t (bf16, l applied)
 //          or fp32 pieces.
 // STAGE 2: A = t (bf16), sign words of U, scales h; output y.
-template <int STAGE, int NBW>
-__global__ __launch_bounds__(kThreads, NBW == 4 ? 1 : 2) void k_gemm(GRun run, GLin single) {
-    using SH = Shape<NBW>;
+template <int STAGE, int NBW, int BM>
+__global__ __launch_bounds__(kThreads, (Shape<NBW, BM>::MinWG)) void k_gemm(GRun run, GLin single) {
+    using SH = Shape<NBW, BM>;
     constexpr int BN = SH::BN, XWave = SH::XWave, Slot = SH::Slot, Stages = SH::Stages;
+    constexpr int kABytes = SH::ABytes;
+    constexpr int MB = BM / 64;                   // 32-token blocks per wave
+    constexpr int ER = BM == 256 ? 64 : 32;       // epilogue rows per wave and round
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     if (stale_ws(run)) return;
     const int64_t items = STAGE == 1 ? run.items1 : run.items2;
@@ -223,10 +235,11 @@ __global__ __launch_bounds__(kThreads, NBW == 4 ? 1 : 2) void k_gemm(GRun run, G
     // item = (piece of d_in [stage 1], token tile, column tile)
     const int nt = STAGE == 1 ? L.nt1 : L.nt2;
     const int ni = (int)(local % nt);
-    const int mi = (int)((local / nt) % L.mt);
-    const int split = STAGE == 1 ? (int)(local / ((int64_t)nt * L.mt)) : 0;
+    const int mt = STAGE == 1 ? L.mt : L.mt2;
+    const int mi = (int)((local / nt) % mt);
+    const int split = STAGE == 1 ? (int)(local / ((int64_t)nt * mt)) : 0;
     const int T = run.T;
-    const int64_t m0 = (int64_t)mi * kBM;
+    const int64_t m0 = (int64_t)mi * BM;
     const int n0 = ni * BN;
     const int kt0 = STAGE == 1 ? split * L.ktps : 0;
     const int kt1 = STAGE == 1 ? (int)imin(L.nkt1, kt0 + L.ktps) : L.nkt2;
@@ -241,11 +254,11 @@ __global__ __launch_bounds__(kThreads, NBW == 4 ? 1 : 2) void k_gemm(GRun run, G
     // activations: wave w fills rows 64w .. 64w+63, 8 rows (1 KB) per DMA; lane i
     // lands in row r = r0 + i/8 at position i%8, which holds chunk (i%8) ^ swz(r)
     const int64_t K = STAGE == 1 ? L.d_in : L.ldt;
-    const int rows = (int)imin(kBM, (int64_t)T - m0);
+    const int rows = (int)imin(BM, (int64_t)T - m0);
     const uint8_t *abase = STAGE == 1 ? (const uint8_t *)L.x : (const uint8_t *)L.t;
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(abase + m0 * K * 2, (int64_t)rows * K * 2);
     // (rows r0 .. r0+7 with r0 = 64w + 8i: swz(r) = (i/8 % 8) ^ (i & 1))
-    const int arow0 = wave * 64 + (lane >> 3);               // + 8i
+    const int arow0 = wave * (BM / 4) + (lane >> 3);         // + 8i
     const int ach0 = (lane & 7) ^ ((lane >> 3) & 7);          // chunk for even i
     const int ach1 = ach0 ^ 1;                                // chunk for odd i
     const uint32_t aoffe = (uint32_t)(arow0 * K * 2) + (uint32_t)(ach0 * 16);
@@ -286,10 +299,10 @@ __global__ __launch_bounds__(kThreads, NBW == 4 ? 1 : 2) void k_gemm(GRun run, G
         const bool kine = kt * kBK + 8 * ach0 < K;            // chunk inside the row
         const bool kino = kt * kBK + 8 * ach1 < K;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < BM / 32; ++i) {
             const bool kin = (i & 1) ? kino : kine;
             const uint32_t off = ((i & 1) ? aoffo : aoffe) + i * astep + (uint32_t)(kt * kBK * 2);
-            dma<16>(ra, S + (wave * 64 + 8 * i) * kRowBytes, kin ? off : kOOB);
+            dma<16>(ra, S + (wave * (BM / 4) + 8 * i) * kRowBytes, kin ? off : kOOB);
         }
         uint8_t *X = S + kABytes + wave * (XWave + kGWave);
 #pragma unroll
@@ -305,7 +318,7 @@ __global__ __launch_bounds__(kThreads, NBW == 4 ? 1 : 2) void k_gemm(GRun run, G
             dma<4>(rg, X + XWave, e < L.d_in ? (uint32_t)((gpath * L.d_in + e) * 2) : kOOB);
         }
     };
-    constexpr int kIssued = 8 + NBW + (STAGE == 1 ? 1 : 0);   // DMAs per K-tile per wave
+    constexpr int kIssued = BM / 32 + NBW + (STAGE == 1 ? 1 : 0);   // DMAs per K-tile per wave
 
     // ---- per-lane constants of the sign operands ----
     int gofs[NBW];           // stage 1: byte offset of this lane's g run (path of the column)
@@ -362,11 +375,11 @@ __global__ __launch_bounds__(kThreads, NBW == 4 ? 1 : 2) void k_gemm(GRun run, G
         }
     }
 
-    f32x16 acc[NBW][4];
+    f32x16 acc[NBW][MB];
 #pragma unroll
     for (int b = 0; b < NBW; ++b)
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[b][mb][i] = 0.0f;
 
@@ -377,13 +390,13 @@ __global__ __launch_bounds__(kThreads, NBW == 4 ? 1 : 2) void k_gemm(GRun run, G
         const uint8_t *G = Xw + XWave;
         // operands of step st+1 are read from LDS before step st's matrix
         // instructions (two register sets), so their latency hides behind them
-        u32x4 act[2][4], scr[2][NBW];
+        u32x4 act[2][MB], scr[2][NBW];
         uint32_t xsr[2][NBW];
         auto fetch = [&](int st, int bi) {
             const int w2 = st >> 1, s = st & 1;
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
-                const int row = wm * 128 + mb * 32 + l32;
+            for (int mb = 0; mb < MB; ++mb) {
+                const int row = wm * (BM / 2) + mb * 32 + l32;
                 const int chunk = 2 * st + hh;
                 act[bi][mb] = *(const u32x4 *)(A + row * kRowBytes + ((chunk ^ swz(row)) << 4));
             }
@@ -414,7 +427,7 @@ __global__ __launch_bounds__(kThreads, NBW == 4 ? 1 : 2) void k_gemm(GRun run, G
                 for (int jj = 0; jj < 4; ++jj)
                     sg[jj] = sc[jj] ^ ((xs << (11 - 8 * s - jj)) & 0x80008000u);
 #pragma unroll
-                for (int mb = 0; mb < 4; ++mb) acc[b][mb] = mfma(sg, act[bi][mb], acc[b][mb]);
+                for (int mb = 0; mb < MB; ++mb) acc[b][mb] = mfma(sg, act[bi][mb], acc[b][mb]);
             }
         }
     };
@@ -436,7 +449,7 @@ __global__ __launch_bounds__(kThreads, NBW == 4 ? 1 : 2) void k_gemm(GRun run, G
 
     // ---- epilogue ----
     // The lane holds columns n .. n+3 of token m per accumulator quad.  Each
-    // wave stages 64 rows of its tile at a time in its own part of the (now
+    // wave stages ER rows of its tile at a time in its own part of the (now
     // idle) ring and writes them back as whole 16-byte chunks of rows, through
     // a buffer descriptor over this token tile's rows: rows past T fall outside
     // the range and are dropped.
@@ -449,16 +462,17 @@ __global__ __launch_bounds__(kThreads, NBW == 4 ? 1 : 2) void k_gemm(GRun run, G
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(obase + m0 * ld_out * osz, (int64_t)rows * ld_out * osz);
     constexpr int WC = NBW * 32;                               // columns of a wave
     const int rbytes = WC * osz + 16;                          // staged row (padded)
-    uint8_t *stage = smem + wave * 64 * (WC * 4 + 16);         // room for the fp32 case
+    uint8_t *stage = smem + wave * ER * (WC * 4 + 16);         // room for the fp32 case
+    static_assert(kWaves * ER * (WC * 4 + 16) <= SH::Lds, "epilogue staging fits the ring");
     // whole 16-byte chunks only when every row starts 16-byte aligned
     const bool chunky = ((ld_out * osz) % 16) == 0 && ((uintptr_t)obase % 16) == 0;
     wait_and_meet<0>();                                        // every wave is done with the ring
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int half = 0; half < MB * 32 / ER; ++half) {
         // accumulators -> LDS (l applied for stage-1 latents)
 #pragma unroll
-        for (int mh = 0; mh < 2; ++mh) {
-            const int mb = 2 * half + mh;
+        for (int mh = 0; mh < ER / 32; ++mh) {
+            const int mb = (ER / 32) * half + mh;
             uint8_t *rowp = stage + (mh * 32 + l32) * rbytes;
 #pragma unroll
             for (int b = 0; b < NBW; ++b)
@@ -482,16 +496,16 @@ __global__ __launch_bounds__(kThreads, NBW == 4 ? 1 : 2) void k_gemm(GRun run, G
                 }
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave's LDS writes land
-        // LDS -> global: 64 rows x WC columns in 16-byte chunks, lane order row-major
+        // LDS -> global: ER rows x WC columns in 16-byte chunks, lane order row-major
         const int cpr = WC * osz / 16;                         // chunks per row
-        const int nchunks = 64 * cpr;
+        const int nchunks = ER * cpr;
         for (int ci = lane; ci < nchunks; ci += 64) {
             const int r = ci / cpr, ch = ci - r * cpr;
             const int col = ch * (16 / osz);                   // first column of the chunk
             const int n = nw0 + col;
             const u32x4 val = *(const u32x4 *)(stage + r * rbytes + ch * 16);
             const uint32_t off =
-                (uint32_t)(((wm * 128 + half * 64 + r) * ld_out + n) * osz);
+                (uint32_t)(((wm * (BM / 2) + half * ER + r) * ld_out + n) * osz);
             const int per = 16 / osz;
             if (chunky && n + per <= n_lim) {
                 // non-temporal: the outputs stream out instead of filling the L2
@@ -719,7 +733,7 @@ void stage1_splits(const Linear *ls, int n, std::vector<int> &splits) {
         const int64_t ldt = rup((int64_t)a.P * cdiv(a.r_p, 32) * 32, kBK);
         const int64_t nkt = cdiv(a.d_in, kBK);
         m.nkt.push_back(nkt);
-        m.tiles.push_back(cdiv(ldt, kBN1) * cdiv(a.T, kBM));
+        m.tiles.push_back(cdiv(ldt, kBN1) * cdiv(a.T, kBM1));
         m.red_bytes.push_back(a.T * ldt * 4);
         for (int64_t sp = 1; sp <= 64; ++sp) {
             const int64_t l = cdiv(nkt, sp);
@@ -767,7 +781,8 @@ size_t plan(const Linear &a, GLin *m, int nsplit) {
     m->ktps = (int32_t)cdiv(m->nkt1, m->nsplit);
     m->nsplit = (int32_t)cdiv(m->nkt1, m->ktps);
     m->nkt2 = m->ldt / kBK;
-    m->mt = (int32_t)cdiv(a.T, kBM);
+    m->mt = (int32_t)cdiv(a.T, kBM1);
+    m->mt2 = (int32_t)cdiv(a.T, kBM2);
     m->nt1 = (int32_t)cdiv(m->ldt, kBN1);
     m->nt2 = (int32_t)cdiv(a.d_out, kBN2);
     m->nred = m->nsplit > 1 ? (int32_t)cdiv(a.T * (m->ldt / 4), kThreads) : 0;
@@ -797,7 +812,7 @@ uint16_t *bind(GLin *m, const Linear &a, uint8_t *ws) {
 }
 
 int64_t items1_of(const GLin &m) { return (int64_t)m.nsplit * m.nt1 * m.mt; }
-int64_t items2_of(const GLin &m) { return (int64_t)m.nt2 * m.mt; }
+int64_t items2_of(const GLin &m) { return (int64_t)m.nt2 * m.mt2; }
 
 template <typename K>
 int raise_lds(K kern, int bytes) {
@@ -819,8 +834,8 @@ int launch_gemms(const GRun &run, const GLin &single, hipStream_t st) {
         if ((rc = last_launch_status())) return rc;
     }
     if (run.items1 > 0) {
-        if ((rc = raise_lds(k_gemm<1, kNBW1>, Shape<kNBW1>::Lds))) return rc;
-        k_gemm<1, kNBW1><<<(unsigned)run.items1, kThreads, Shape<kNBW1>::Lds, st>>>(run, single);
+        if ((rc = raise_lds(k_gemm<1, kNBW1, kBM1>, Shape1::Lds))) return rc;
+        k_gemm<1, kNBW1, kBM1><<<(unsigned)run.items1, kThreads, Shape1::Lds, st>>>(run, single);
         if ((rc = last_launch_status())) return rc;
     }
     if (run.itemsR > 0) {
@@ -828,8 +843,8 @@ int launch_gemms(const GRun &run, const GLin &single, hipStream_t st) {
         if ((rc = last_launch_status())) return rc;
     }
     if (run.items2 > 0) {
-        if ((rc = raise_lds(k_gemm<2, kNBW2>, Shape<kNBW2>::Lds))) return rc;
-        k_gemm<2, kNBW2><<<(unsigned)run.items2, kThreads, Shape<kNBW2>::Lds, st>>>(run, single);
+        if ((rc = raise_lds(k_gemm<2, kNBW2, kBM2>, Shape2::Lds))) return rc;
+        k_gemm<2, kNBW2, kBM2><<<(unsigned)run.items2, kThreads, Shape2::Lds, st>>>(run, single);
         if ((rc = last_launch_status())) return rc;
     }
     return LB_OK;
@@ -1052,7 +1067,7 @@ int gemm_group_plan(const Linear *ls, int n, void *ws, size_t ws_bytes, uint64_t
         }
         for (int64_t k = 0; k < items2_of(m); ++k) {
             len2[(size_t)(m.item2 + k)] = m.nkt2;
-            tok2[(size_t)(m.item2 + k)] = (int32_t)((k / m.nt2) % m.mt);
+            tok2[(size_t)(m.item2 + k)] = (int32_t)((k / m.nt2) % m.mt2);
         }
     }
     const std::vector<int32_t> o1 = dispatch_order(len1, tok1), o2 = dispatch_order(len2, tok2);
