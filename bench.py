@@ -322,7 +322,12 @@ def decode_stack_leg(key, T, steps, layers=0):
     step_s, kern_s = time_decode(st, steps, 5, 0.2)
     del st
     torch.cuda.empty_cache()
-    out = {"workload": "%s, decode T=%d, %d-layer stack as one group" % (w.title, T, L),
+    import binarized_rank_linear_amd as lb
+    s0 = w.linears[0]
+    r0, _ = lb.rank_for_budget(s0.d_in, s0.d_out, w.b_num, w.b_den, w.residual)
+    path = lb.linear_path(s0.d_in, s0.d_out, r0, T, w.residual, torch.bfloat16, torch.bfloat16)
+    kernels = {lb.LB_PATH_DECODE: "decode kernels", lb.LB_PATH_PREFILL: "GEMM kernels"}.get(path, "vector-ALU kernels")
+    out = {"workload": "%s, T=%d, %d-layer stack as one group (%s)" % (w.title, T, L, kernels),
            "us_per_pass": kern_s * 1e6, "tok_per_s": T / step_s, "algorithmic_bytes": nbytes,
            "GBs": nbytes / kern_s / 1e9, "hbm_frac": nbytes / kern_s / 1e9 / HBM_PEAK_GBS,
            "dense_equivalent_TFLOPs": flops / kern_s / 1e12,

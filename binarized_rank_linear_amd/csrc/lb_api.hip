@@ -17,6 +17,12 @@ using namespace lb;
 namespace {
 
 constexpr int64_t kDecodeMaxT = 32;     // token count served by the decode kernels
+// With bf16 outputs AUTO takes the GEMM kernels from this many tokens on: the
+// decode kernels' matrix work grows with the activation rows while their
+// streaming stays, and above about 16 tokens the bf16 GEMMs on 64-token tiles
+// are faster (a 32-layer Llama2-7B-shaped stack at T = 32: 0.88 against 2.09
+// ms per pass; at T = 16 0.84 against 0.80 ms).
+constexpr int64_t kGemmFromT = 17;
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -43,7 +49,8 @@ int choose_path(unsigned flags, int64_t T, int y_dtype, Path *out, const Linear 
     const bool mfma_ok = mfma_decode_supported(T, y_dtype) && (!a || mfma_decode_shape_ok(*a));
     switch (flags & LB_PATH_MASK) {
         case LB_PATH_AUTO:
-            if (T <= kDecodeMaxT)
+            if (T <= kDecodeMaxT &&
+                (T < kGemmFromT || y_dtype != LB_BF16 || (a && !gemm_linear_supported(*a))))
                 *out = mfma_ok ? Path::MfmaDecode : Path::Valu;
             else
                 *out = y_dtype == LB_BF16 ? Path::Gemm : Path::Valu;

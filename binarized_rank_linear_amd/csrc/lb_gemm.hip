@@ -48,11 +48,22 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 namespace {
 
-// Tokens per tile: 256 in stage 1 (long K: the sign operand a wave builds
-// serves 128 tokens), 128 in stage 2 (short K, the latents: smaller tiles let
-// three workgroups share a CU, whose tiles' epilogues and prologues overlap
-// each other's matrix work).
+// Tokens per tile, by the launch's token count T:
+//   T > 128: 256 in stage 1 (long K: the sign operand a wave builds serves 128
+//            tokens), 128 in stage 2 (short K, the latents: smaller tiles let
+//            three workgroups share a CU, whose tiles' epilogues and prologues
+//            overlap each other's matrix work);
+//   64 < T <= 128: 128 in both; T <= 64: 64 in both (a tile is mostly padding
+//            otherwise: the matrix work follows the tile, not T).
 constexpr int kBM1 = 256, kBM2 = 128;
+struct TileRows {
+    int bm1, bm2;
+};
+TileRows tile_rows(int64_t T) {
+    if (T <= 64) return {64, 64};
+    if (T <= 128) return {128, 128};
+    return {kBM1, kBM2};
+}
 constexpr int kBK = 64;                      // contraction elements per K-tile (two packed words)
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
@@ -71,13 +82,13 @@ template <int NBW, int BM> struct Shape {
     static constexpr int XWave = 2 * NBW * 32 * 4;     // a wave's sign words: [2 words][NBW*32]
     static constexpr int Slot = ABytes + kWaves * (XWave + kGWave);
     static constexpr int Stages = NBW == 4 ? 4 : 2;
-    static constexpr int Lds = Stages * Slot;
-    static constexpr int MinWG = NBW == 4 ? 1 : (BM == 256 ? 2 : 3);   // workgroups per CU
+    static constexpr int ER = BM == 256 ? 64 : 32;     // epilogue rows per wave and round
+    static constexpr int Staging = kWaves * ER * (BN / 2 * 4 + 16);   // room for fp32 outputs
+    static constexpr int Lds = Stages * Slot > Staging ? Stages * Slot : Staging;
+    static constexpr int MinWG = NBW == 4 ? 1 : (BM == 256 ? 2 : (BM == 128 ? 3 : 4));   // workgroups per CU
 };
 constexpr int kNBW1 = 2, kNBW2 = 2;          // stage 1, stage 2
-using Shape1 = Shape<kNBW1, kBM1>;
-using Shape2 = Shape<kNBW2, kBM2>;
-constexpr int kBN1 = Shape1::BN, kBN2 = Shape2::BN;
+constexpr int kBN1 = 64 * kNBW1, kBN2 = 64 * kNBW2;
 constexpr int kWG1 = 512;                    // stage-1 workgroups a launch aims for: two per
                                              // CU on 256 CUs, so no CU runs a second round
 constexpr uint32_t kOOB = 0x7ffffff0u;       // a buffer offset past every range: reads as zero
@@ -224,7 +235,7 @@ __global__ __launch_bounds__(kThreads, (Shape<NBW, BM>::MinWG)) void k_gemm(GRun
     constexpr int BN = SH::BN, XWave = SH::XWave, Slot = SH::Slot, Stages = SH::Stages;
     constexpr int kABytes = SH::ABytes;
     constexpr int MB = BM / 64;                   // 32-token blocks per wave
-    constexpr int ER = BM == 256 ? 64 : 32;       // epilogue rows per wave and round
+    constexpr int ER = SH::ER;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     if (stale_ws(run)) return;
     const int64_t items = STAGE == 1 ? run.items1 : run.items2;
@@ -733,7 +744,7 @@ void stage1_splits(const Linear *ls, int n, std::vector<int> &splits) {
         const int64_t ldt = rup((int64_t)a.P * cdiv(a.r_p, 32) * 32, kBK);
         const int64_t nkt = cdiv(a.d_in, kBK);
         m.nkt.push_back(nkt);
-        m.tiles.push_back(cdiv(ldt, kBN1) * cdiv(a.T, kBM1));
+        m.tiles.push_back(cdiv(ldt, kBN1) * cdiv(a.T, tile_rows(a.T).bm1));
         m.red_bytes.push_back(a.T * ldt * 4);
         for (int64_t sp = 1; sp <= 64; ++sp) {
             const int64_t l = cdiv(nkt, sp);
@@ -781,8 +792,9 @@ size_t plan(const Linear &a, GLin *m, int nsplit) {
     m->ktps = (int32_t)cdiv(m->nkt1, m->nsplit);
     m->nsplit = (int32_t)cdiv(m->nkt1, m->ktps);
     m->nkt2 = m->ldt / kBK;
-    m->mt = (int32_t)cdiv(a.T, kBM1);
-    m->mt2 = (int32_t)cdiv(a.T, kBM2);
+    const TileRows tr = tile_rows(a.T);
+    m->mt = (int32_t)cdiv(a.T, tr.bm1);
+    m->mt2 = (int32_t)cdiv(a.T, tr.bm2);
     m->nt1 = (int32_t)cdiv(m->ldt, kBN1);
     m->nt2 = (int32_t)cdiv(a.d_out, kBN2);
     m->nred = m->nsplit > 1 ? (int32_t)cdiv(a.T * (m->ldt / 4), kThreads) : 0;
@@ -814,12 +826,13 @@ uint16_t *bind(GLin *m, const Linear &a, uint8_t *ws) {
 int64_t items1_of(const GLin &m) { return (int64_t)m.nsplit * m.nt1 * m.mt; }
 int64_t items2_of(const GLin &m) { return (int64_t)m.nt2 * m.mt2; }
 
-template <typename K>
-int raise_lds(K kern, int bytes) {
-    // > 64 KB of dynamic LDS needs an explicit opt-in (once per kernel; idempotent)
+// > 64 KB of dynamic LDS needs an explicit opt-in, once per kernel (the flag
+// is per instantiation, so per kernel).
+template <auto KERN>
+int raise_lds(int bytes) {
     static bool done = false;
     if (!done) {
-        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) !=
+        if (hipFuncSetAttribute((const void *)KERN, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) !=
             hipSuccess)
             return hip_status(hipGetLastError());
         done = true;
@@ -827,25 +840,36 @@ int raise_lds(K kern, int bytes) {
     return LB_OK;
 }
 
+template <int STAGE, int BM>
+int launch_stage(const GRun &run, const GLin &single, int64_t items, hipStream_t st) {
+    constexpr int NBW = STAGE == 1 ? kNBW1 : kNBW2;
+    using SH = Shape<NBW, BM>;
+    if (int rc = raise_lds<k_gemm<STAGE, NBW, BM>>(SH::Lds)) return rc;
+    k_gemm<STAGE, NBW, BM><<<(unsigned)items, kThreads, SH::Lds, st>>>(run, single);
+    return last_launch_status();
+}
+
 int launch_gemms(const GRun &run, const GLin &single, hipStream_t st) {
     int rc;
+    const TileRows tr = tile_rows(run.T);
     if (run.itemsG > 0) {
         k_prep<<<(unsigned)run.itemsG, kThreads, 0, st>>>(run, single);
         if ((rc = last_launch_status())) return rc;
     }
     if (run.items1 > 0) {
-        if ((rc = raise_lds(k_gemm<1, kNBW1, kBM1>, Shape1::Lds))) return rc;
-        k_gemm<1, kNBW1, kBM1><<<(unsigned)run.items1, kThreads, Shape1::Lds, st>>>(run, single);
-        if ((rc = last_launch_status())) return rc;
+        rc = tr.bm1 == 64 ? launch_stage<1, 64>(run, single, run.items1, st)
+           : tr.bm1 == 128 ? launch_stage<1, 128>(run, single, run.items1, st)
+           : launch_stage<1, kBM1>(run, single, run.items1, st);
+        if (rc) return rc;
     }
     if (run.itemsR > 0) {
         k_reduce<<<(unsigned)run.itemsR, kThreads, 0, st>>>(run, single);
         if ((rc = last_launch_status())) return rc;
     }
     if (run.items2 > 0) {
-        if ((rc = raise_lds(k_gemm<2, kNBW2, kBM2>, Shape2::Lds))) return rc;
-        k_gemm<2, kNBW2, kBM2><<<(unsigned)run.items2, kThreads, Shape2::Lds, st>>>(run, single);
-        if ((rc = last_launch_status())) return rc;
+        rc = tr.bm2 == 64 ? launch_stage<2, 64>(run, single, run.items2, st)
+                          : launch_stage<2, 128>(run, single, run.items2, st);
+        if (rc) return rc;
     }
     return LB_OK;
 }

@@ -66,7 +66,7 @@ extern "C" {
 #define LB_BF16 1
 
 /* flags: path selection (low 4 bits) */
-#define LB_PATH_AUTO        0u  /* decode kernels for T <= 32, MFMA GEMMs above */
+#define LB_PATH_AUTO        0u  /* decode kernels for T <= 16 (fp32 out: T <= 32), MFMA GEMMs above */
 #define LB_PATH_DECODE      1u  /* force the matrix-core token-streaming decode kernels */
 #define LB_PATH_PREFILL     2u  /* force the MFMA GEMM (prefill) kernels */
 #define LB_PATH_DECODE_VALU 3u  /* force the plain vector-ALU decode kernels */
@@ -180,8 +180,10 @@ size_t lb_linear_workspace_bytes(int64_t d_in, int64_t d_out, int64_t r, int64_t
  * ws: device workspace of at least lb_linear_workspace_bytes(...) bytes,
  * 256-byte aligned, contents need not be initialised and are clobbered.
  * x and y must not overlap each other or ws (LB_EINVAL).
- * Path choice (flags): AUTO uses the decode kernels for T <= 32 and the MFMA
- * GEMM kernels above; PREFILL with y_dtype LB_F32 is LB_EUNSUPPORTED (the
+ * Path choice (flags): AUTO uses the decode kernels for T <= 16 and the MFMA
+ * GEMM kernels above for bf16 outputs (the GEMMs are faster from about 17
+ * tokens on), the decode kernels for T <= 32 for fp32 outputs; DECODE forces
+ * the decode kernels up to 32 tokens; PREFILL with y_dtype LB_F32 is LB_EUNSUPPORTED (the
  * GEMM path rounds its operands, including g and h, to bf16, outside the fp32
  * tolerance).  Shapes the GEMM kernels do not take (d_in % 8 != 0, x not
  * 16-byte or g not 4-byte aligned) run on the vector-ALU decode kernels.
@@ -198,7 +200,7 @@ int lb_linear_forward(const void *x, int x_dtype, void *y, int y_dtype,
  * until the process ends).  Allocates nothing.  Same arguments, results and
  * errors as lb_linear_forward, except that a request whose kernels need more
  * workspace than the array holds returns LB_EWORKSPACE (every configuration
- * linear fits at T <= 32 on the decode kernels; compare
+ * linear fits at T <= 32; compare
  * lb_linear_workspace_bytes with LB_NOALLOC_SCRATCH_BYTES).  Every call on a
  * GPU shares that GPU's array: calls that overlap on one GPU (on different
  * streams, or from different threads without ordering) race.  The array keeps
@@ -414,9 +416,11 @@ size_t lb_grouped_workspace_bytes(const lb_linear_desc *descs, int n, int64_t T,
  * of n descriptors; it is copied and may be freed afterwards.  All linears use
  * x_dtype / y_dtype and T tokens.  The pointers in descs are captured: later
  * runs read and write the same buffers.  The kernels a group runs:
- *  - 1 <= T <= 32: the matrix-core decode kernels (stage 1 = activation
- *    operands, first contractions and latents; stage 2 = second contractions);
- *  - T > 32, bf16 output, bf16 input and shapes the GEMM kernels take
+ *  - the matrix-core decode kernels where lb_linear_forward's path choice
+ *    picks them (1 <= T <= 16, or up to 32 with fp32 outputs or the DECODE
+ *    flag) (stage 1 = activation operands, first contractions and latents;
+ *    stage 2 = second contractions);
+ *  - where it picks the GEMM kernels (bf16 output), bf16 input and shapes they take
  *    (d_in % 8 == 0, x 16-byte and g 4-byte aligned): the GEMM kernels
  *    (stage 1 = first contractions and the d_in-piece reduction; stage 2 =
  *    second contractions).  For these, prepare also derives a bf16 copy of g

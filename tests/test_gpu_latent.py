@@ -21,7 +21,8 @@ def _bits(torch, y):
     ((1024, 700, 96, 2), 1, "bf16", "bf16", "f32", "auto"),      # decode kernels, two limbs
     ((4096, 4096, 1024, 2), 4, "bf16", "bf16", "f32", "auto"),
     ((2080, 515, 200, 2), 3, "f32", "f32", "f32", "auto"),       # decode kernels, three limbs
-    ((8192, 1024, 32, 2), 20, "bf16", "bf16", "f32", "auto"),    # unfused stage 1 (prep + stage 1)
+    ((8192, 1024, 32, 2), 20, "bf16", "bf16", "f32", "decode"),  # unfused stage 1 (prep + stage 1)
+    ((8192, 1024, 32, 2), 20, "bf16", "bf16", "f32", "auto"),    # GEMM kernels, 64-token tiles
     ((2048, 1536, 160, 2), 300, "bf16", "bf16", "bf16", "auto"),  # GEMM kernels: bf16 latents
     ((2048, 1100, 304, 2), 64, "bf16", "bf16", "f32", "auto"),
     ((1000, 700, 48, 2), 40, "f32", "f32", "f32", "auto"),       # vector-ALU kernels (fp32 out, T > 32)

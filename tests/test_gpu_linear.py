@@ -114,6 +114,16 @@ def test_config_linears_decode(key, name, T, path):
     _check(inp, x, w.dtype, path, rows=rows)
 
 
+@pytest.mark.parametrize("key,name,T", [("c3", "q", 20), ("c3", "q", 32), ("c3", "down", 32), ("c5", "gate", 24)])
+def test_config_linears_decode_kernels_above_16(key, name, T):
+    """The decode kernels keep serving 17 to 32 tokens when asked for (AUTO
+    takes the GEMM kernels there for bf16 outputs)."""
+    w, sh, inp = _cfg_linear(key, name)
+    x = synth.activations(synth.activation_seed(T), T, sh.d_in, w.dtype)
+    rows = None if sh.d_out * T <= 8192 * 4 else np.linspace(0, sh.d_out - 1, 2048).astype(np.int64)
+    _check(inp, x, w.dtype, "decode", rows=rows)
+
+
 @pytest.mark.parametrize("key,name", [("c4", "q"), ("c4", "k"), ("c4", "gate"), ("c4", "down"),
                                       ("c5", "q"), ("c5", "k"), ("c5", "gate"), ("c5", "down")])
 def test_config_linears_prefill_sampled(key, name):
