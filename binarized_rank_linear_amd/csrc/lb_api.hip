@@ -17,12 +17,14 @@ using namespace lb;
 namespace {
 
 constexpr int64_t kDecodeMaxT = 32;     // token count served by the decode kernels
-// With bf16 outputs AUTO takes the GEMM kernels from this many tokens on: the
-// decode kernels' matrix work grows with the activation rows while their
-// streaming stays, and above about 16 tokens the bf16 GEMMs on 64-token tiles
-// are faster (a 32-layer Llama2-7B-shaped stack at T = 32: 0.88 against 2.09
-// ms per pass; at T = 16 0.84 against 0.80 ms).
-constexpr int64_t kGemmFromT = 17;
+// With bf16 outputs AUTO takes the GEMM kernels from this many tokens on:
+// above 8 tokens the decode kernels' stage 1 no longer runs fused (its
+// activation operands take a launch of their own) and their matrix work grows
+// with the activation rows, while the bf16 GEMMs on 32-token tiles cost about
+// the same from 8 to 32 tokens (a 32-layer Llama2-7B-shaped stack: 0.34 against
+// 0.47 ms per pass at T = 8, 0.73 against 0.49 ms at T = 12, 2.09 against 0.55
+// ms at T = 32).
+constexpr int64_t kGemmFromT = 9;
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 

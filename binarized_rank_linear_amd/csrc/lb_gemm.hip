@@ -53,13 +53,15 @@ namespace {
 //            tokens), 128 in stage 2 (short K, the latents: smaller tiles let
 //            three workgroups share a CU, whose tiles' epilogues and prologues
 //            overlap each other's matrix work);
-//   64 < T <= 128: 128 in both; T <= 64: 64 in both (a tile is mostly padding
+//   64 < T <= 128: 128 in both; 32 < T <= 64: 64 in both; T <= 32: 32 in
+//            both, each wave 32 tokens x 32 columns (a tile is mostly padding
 //            otherwise: the matrix work follows the tile, not T).
 constexpr int kBM1 = 256, kBM2 = 128;
 struct TileRows {
     int bm1, bm2;
 };
 TileRows tile_rows(int64_t T) {
+    if (T <= 32) return {32, 32};
     if (T <= 64) return {64, 64};
     if (T <= 128) return {128, 128};
     return {kBM1, kBM2};
@@ -70,20 +72,23 @@ constexpr int kWaves = 4;
 constexpr int kRowBytes = kBK * 2;           // one activation row of a K-tile (bf16)
 constexpr int kGWave = 2 * kBK * 2;          // a wave's bf16 g: [2 paths][kBK]
 
-// Tile shapes by n-blocks (32 columns) per wave NBW and tokens per tile BM;
-// waves are 2 x 2:
-//   NBW = 2: BM x 128 tiles, BM/2 x 64 per wave, 2-slot ring (70 KB at BM =
-//            256: two workgroups per CU; 38 KB at BM = 128: three)
-//   NBW = 4: 256 x 256 tiles, 128 x 128 per wave (accumulators in AGPRs),
-//            4-slot ring (148 KB): one workgroup per CU, three K-tiles in flight
-template <int NBW, int BM> struct Shape {
-    static constexpr int BN = 64 * NBW;
+// Tile shapes by n-blocks (32 columns) per wave NBW, tokens per tile BM and
+// wave rows WR (the 4 waves are WR x 4/WR):
+//   NBW = 2, WR = 2: BM x 128 tiles, BM/2 x 64 per wave, 2-slot ring (70 KB
+//            at BM = 256: two workgroups per CU; 38 KB at BM = 128: three)
+//   NBW = 1, WR = 1: 32 x 128 tiles, 32 x 32 per wave: no two waves build the
+//            same sign operand (the form for at most 32 tokens)
+//   NBW = 4, WR = 2: 256 x 256 tiles, 128 x 128 per wave (accumulators in
+//            AGPRs), 4-slot ring (148 KB): one workgroup per CU
+template <int NBW, int BM, int WR = 2> struct Shape {
+    static constexpr int BN = (4 / WR) * NBW * 32;
     static constexpr int ABytes = BM * kRowBytes;      // activation rows of a K-tile
-    static constexpr int XWave = 2 * NBW * 32 * 4;     // a wave's sign words: [2 words][NBW*32]
+    static constexpr int XS = (NBW < 2 ? 2 : NBW) * 32;   // sign-word slots per word and wave
+    static constexpr int XWave = 2 * XS * 4;           // a wave's sign words: [2 words][XS]
     static constexpr int Slot = ABytes + kWaves * (XWave + kGWave);
     static constexpr int Stages = NBW == 4 ? 4 : 2;
     static constexpr int ER = BM == 256 ? 64 : 32;     // epilogue rows per wave and round
-    static constexpr int Staging = kWaves * ER * (BN / 2 * 4 + 16);   // room for fp32 outputs
+    static constexpr int Staging = kWaves * ER * (NBW * 32 * 4 + 16);   // room for fp32 outputs
     static constexpr int Lds = Stages * Slot > Staging ? Stages * Slot : Staging;
     static constexpr int MinWG = NBW == 4 ? 1 : (BM == 256 ? 2 : (BM == 128 ? 3 : 4));   // workgroups per CU
 };
@@ -229,12 +234,13 @@ __device__ __forceinline__ f32x16 mfma(const u32x4 &s, const u32x4 &a, f32x16 c)
 // STAGE 1: A = x (bf16), sign words of V, scales g; output t (bf16, l applied)
 //          or fp32 pieces.
 // STAGE 2: A = t (bf16), sign words of U, scales h; output y.
-template <int STAGE, int NBW, int BM>
-__global__ __launch_bounds__(kThreads, (Shape<NBW, BM>::MinWG)) void k_gemm(GRun run, GLin single) {
-    using SH = Shape<NBW, BM>;
-    constexpr int BN = SH::BN, XWave = SH::XWave, Slot = SH::Slot, Stages = SH::Stages;
+template <int STAGE, int NBW, int BM, int WR>
+__global__ __launch_bounds__(kThreads, (Shape<NBW, BM, WR>::MinWG)) void k_gemm(GRun run, GLin single) {
+    using SH = Shape<NBW, BM, WR>;
+    constexpr int BN = SH::BN, XWave = SH::XWave, XS = SH::XS, Slot = SH::Slot, Stages = SH::Stages;
+    constexpr int XC = NBW < 2 ? 1 : NBW / 2;     // sign-word DMAs per word (64 lanes each)
     constexpr int kABytes = SH::ABytes;
-    constexpr int MB = BM / 64;                   // 32-token blocks per wave
+    constexpr int MB = BM / (32 * WR);            // 32-token blocks per wave
     constexpr int ER = SH::ER;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     if (stale_ws(run)) return;
@@ -258,45 +264,50 @@ __global__ __launch_bounds__(kThreads, (Shape<NBW, BM>::MinWG)) void k_gemm(GRun
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hh = lane >> 5, l32 = lane & 31;
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wm = WR == 2 ? (wave & 1) : 0, wn = WR == 2 ? (wave >> 1) : wave;
     const int nw0 = n0 + wn * NBW * 32;                       // this wave's first column
 
-    // ---- loads of one K-tile (per wave: 8 activation DMAs, NBW sign-word DMAs, 1 g DMA) ----
-    // activations: wave w fills rows 64w .. 64w+63, 8 rows (1 KB) per DMA; lane i
-    // lands in row r = r0 + i/8 at position i%8, which holds chunk (i%8) ^ swz(r)
+    // ---- loads of one K-tile (per wave: BM/32 activation DMAs, 2 XC sign-word DMAs, 1 g DMA) ----
+    // activations: wave w fills rows (BM/4) w .. (BM/4) w + BM/4 - 1, 8 rows (1 KB)
+    // per DMA; lane i lands in row r = r0 + i/8 at position i%8, which holds
+    // chunk (i%8) ^ swz(r)
     const int64_t K = STAGE == 1 ? L.d_in : L.ldt;
     const int rows = (int)imin(BM, (int64_t)T - m0);
     const uint8_t *abase = STAGE == 1 ? (const uint8_t *)L.x : (const uint8_t *)L.t;
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(abase + m0 * K * 2, (int64_t)rows * K * 2);
     // (rows r0 .. r0+7 with r0 = 64w + 8i: swz(r) = (i/8 % 8) ^ (i & 1))
     const int arow0 = wave * (BM / 4) + (lane >> 3);         // + 8i
-    const int ach0 = (lane & 7) ^ ((lane >> 3) & 7);          // chunk for even i
+    // (row >> 3) & 1 of DMA i's rows is (wave * BM / 32 + i) & 1: i's parity,
+    // and the wave's own for 8-row waves (BM = 32)
+    const int ach0 = (lane & 7) ^ ((lane >> 3) & 7) ^ ((wave * (BM / 32)) & 1);   // chunk for even i
     const int ach1 = ach0 ^ 1;                                // chunk for odd i
     const uint32_t aoffe = (uint32_t)(arow0 * K * 2) + (uint32_t)(ach0 * 16);
     const uint32_t aoffo = (uint32_t)(arow0 * K * 2) + (uint32_t)(ach1 * 16);
     const uint32_t astep = (uint32_t)(8 * K * 2);            // 8 rows
-    // sign words: this wave's columns nw0 + 64c + lane, c < NBW/2, both words of the K-tile
+    // sign words: this wave's columns nw0 + 64c + lane, c < XC, both words of
+    // the K-tile (with one n-block per wave, lanes 32..63 load nothing)
     __amdgpu_buffer_rsrc_t rx;
-    uint32_t xoff[NBW / 2], xstep;
+    uint32_t xoff[XC], xstep;
+    const bool xlane = NBW >= 2 || lane < 32;
     int xwords;
     if (STAGE == 1) {
         rx = make_rsrc(L.vz, (int64_t)L.P * L.kw_v * L.zld_v * 4);
 #pragma unroll
-        for (int c = 0; c < NBW / 2; ++c) {
+        for (int c = 0; c < XC; ++c) {
             const int xn = nw0 + 64 * c + lane;
             const int qn = xn >> 5;
             const int p = qn / L.kw;
             const int k = (qn - p * L.kw) * 32 + (xn & 31);
-            xoff[c] = (p < L.P && k < L.r_p) ? (uint32_t)(((int64_t)p * L.kw_v * L.zld_v + k) * 4) : kOOB;
+            xoff[c] = (xlane && p < L.P && k < L.r_p) ? (uint32_t)(((int64_t)p * L.kw_v * L.zld_v + k) * 4) : kOOB;
         }
         xstep = (uint32_t)(L.zld_v * 4);
         xwords = L.kw_v;
     } else {
         rx = make_rsrc(L.uz, (int64_t)L.P * L.kw * L.zld_u * 4);
 #pragma unroll
-        for (int c = 0; c < NBW / 2; ++c) {
+        for (int c = 0; c < XC; ++c) {
             const int xn = nw0 + 64 * c + lane;
-            xoff[c] = xn < L.d_out ? (uint32_t)(xn * 4) : kOOB;
+            xoff[c] = (xlane && xn < L.d_out) ? (uint32_t)(xn * 4) : kOOB;
         }
         xstep = (uint32_t)(L.zld_u * 4);
         xwords = L.P * L.kw;
@@ -320,8 +331,8 @@ __global__ __launch_bounds__(kThreads, (Shape<NBW, BM>::MinWG)) void k_gemm(GRun
         for (int wd = 0; wd < 2; ++wd) {
             const int q = kt * 2 + wd;
 #pragma unroll
-            for (int c = 0; c < NBW / 2; ++c)
-                dma<4>(rx, X + (wd * NBW * 32 + 64 * c) * 4,
+            for (int c = 0; c < XC; ++c)
+                dma<4>(rx, X + (wd * XS + 64 * c) * 4,
                        (xoff[c] != kOOB && q < xwords) ? xoff[c] + (uint32_t)q * xstep : kOOB);
         }
         if (STAGE == 1) {
@@ -329,7 +340,7 @@ __global__ __launch_bounds__(kThreads, (Shape<NBW, BM>::MinWG)) void k_gemm(GRun
             dma<4>(rg, X + XWave, e < L.d_in ? (uint32_t)((gpath * L.d_in + e) * 2) : kOOB);
         }
     };
-    constexpr int kIssued = BM / 32 + NBW + (STAGE == 1 ? 1 : 0);   // DMAs per K-tile per wave
+    constexpr int kIssued = BM / 32 + 2 * XC + (STAGE == 1 ? 1 : 0);   // DMAs per K-tile per wave
 
     // ---- per-lane constants of the sign operands ----
     int gofs[NBW];           // stage 1: byte offset of this lane's g run (path of the column)
@@ -407,13 +418,13 @@ __global__ __launch_bounds__(kThreads, (Shape<NBW, BM>::MinWG)) void k_gemm(GRun
             const int w2 = st >> 1, s = st & 1;
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
-                const int row = wm * (BM / 2) + mb * 32 + l32;
+                const int row = wm * (BM / WR) + mb * 32 + l32;
                 const int chunk = 2 * st + hh;
                 act[bi][mb] = *(const u32x4 *)(A + row * kRowBytes + ((chunk ^ swz(row)) << 4));
             }
 #pragma unroll
             for (int b = 0; b < NBW; ++b) {
-                xsr[bi][b] = ((const uint32_t *)Xw)[w2 * NBW * 32 + b * 32 + l32];
+                xsr[bi][b] = ((const uint32_t *)Xw)[w2 * XS + b * 32 + l32];
                 if (STAGE == 1) scr[bi][b] = *(const u32x4 *)(G + gofs[b] + (32 * w2 + 16 * s) * 2);
             }
         };
@@ -516,7 +527,7 @@ __global__ __launch_bounds__(kThreads, (Shape<NBW, BM>::MinWG)) void k_gemm(GRun
             const int n = nw0 + col;
             const u32x4 val = *(const u32x4 *)(stage + r * rbytes + ch * 16);
             const uint32_t off =
-                (uint32_t)(((wm * (BM / 2) + half * ER + r) * ld_out + n) * osz);
+                (uint32_t)(((wm * (BM / WR) + half * ER + r) * ld_out + n) * osz);
             const int per = 16 / osz;
             if (chunky && n + per <= n_lim) {
                 // non-temporal: the outputs stream out instead of filling the L2
@@ -842,10 +853,12 @@ int raise_lds(int bytes) {
 
 template <int STAGE, int BM>
 int launch_stage(const GRun &run, const GLin &single, int64_t items, hipStream_t st) {
-    constexpr int NBW = STAGE == 1 ? kNBW1 : kNBW2;
-    using SH = Shape<NBW, BM>;
-    if (int rc = raise_lds<k_gemm<STAGE, NBW, BM>>(SH::Lds)) return rc;
-    k_gemm<STAGE, NBW, BM><<<(unsigned)items, kThreads, SH::Lds, st>>>(run, single);
+    constexpr int NBW = BM == 32 ? 1 : (STAGE == 1 ? kNBW1 : kNBW2);
+    constexpr int WR = BM == 32 ? 1 : 2;
+    using SH = Shape<NBW, BM, WR>;
+    static_assert(SH::BN == (STAGE == 1 ? kBN1 : kBN2), "column tiles as planned");
+    if (int rc = raise_lds<k_gemm<STAGE, NBW, BM, WR>>(SH::Lds)) return rc;
+    k_gemm<STAGE, NBW, BM, WR><<<(unsigned)items, kThreads, SH::Lds, st>>>(run, single);
     return last_launch_status();
 }
 
@@ -857,7 +870,8 @@ int launch_gemms(const GRun &run, const GLin &single, hipStream_t st) {
         if ((rc = last_launch_status())) return rc;
     }
     if (run.items1 > 0) {
-        rc = tr.bm1 == 64 ? launch_stage<1, 64>(run, single, run.items1, st)
+        rc = tr.bm1 == 32 ? launch_stage<1, 32>(run, single, run.items1, st)
+           : tr.bm1 == 64 ? launch_stage<1, 64>(run, single, run.items1, st)
            : tr.bm1 == 128 ? launch_stage<1, 128>(run, single, run.items1, st)
            : launch_stage<1, kBM1>(run, single, run.items1, st);
         if (rc) return rc;
@@ -867,7 +881,8 @@ int launch_gemms(const GRun &run, const GLin &single, hipStream_t st) {
         if ((rc = last_launch_status())) return rc;
     }
     if (run.items2 > 0) {
-        rc = tr.bm2 == 64 ? launch_stage<2, 64>(run, single, run.items2, st)
+        rc = tr.bm2 == 32 ? launch_stage<2, 32>(run, single, run.items2, st)
+           : tr.bm2 == 64 ? launch_stage<2, 64>(run, single, run.items2, st)
                           : launch_stage<2, 128>(run, single, run.items2, st);
         if (rc) return rc;
     }

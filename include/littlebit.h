@@ -66,7 +66,7 @@ extern "C" {
 #define LB_BF16 1
 
 /* flags: path selection (low 4 bits) */
-#define LB_PATH_AUTO        0u  /* decode kernels for T <= 16 (fp32 out: T <= 32), MFMA GEMMs above */
+#define LB_PATH_AUTO        0u  /* decode kernels for T <= 8 (fp32 out: T <= 32), MFMA GEMMs above */
 #define LB_PATH_DECODE      1u  /* force the matrix-core token-streaming decode kernels */
 #define LB_PATH_PREFILL     2u  /* force the MFMA GEMM (prefill) kernels */
 #define LB_PATH_DECODE_VALU 3u  /* force the plain vector-ALU decode kernels */
@@ -180,9 +180,9 @@ size_t lb_linear_workspace_bytes(int64_t d_in, int64_t d_out, int64_t r, int64_t
  * ws: device workspace of at least lb_linear_workspace_bytes(...) bytes,
  * 256-byte aligned, contents need not be initialised and are clobbered.
  * x and y must not overlap each other or ws (LB_EINVAL).
- * Path choice (flags): AUTO uses the decode kernels for T <= 16 and the MFMA
- * GEMM kernels above for bf16 outputs (the GEMMs are faster from about 17
- * tokens on), the decode kernels for T <= 32 for fp32 outputs; DECODE forces
+ * Path choice (flags): AUTO uses the decode kernels for T <= 8 and the MFMA
+ * GEMM kernels above for bf16 outputs (the GEMMs are faster from 9 tokens
+ * on), the decode kernels for T <= 32 for fp32 outputs; DECODE forces
  * the decode kernels up to 32 tokens; PREFILL with y_dtype LB_F32 is LB_EUNSUPPORTED (the
  * GEMM path rounds its operands, including g and h, to bf16, outside the fp32
  * tolerance).  Shapes the GEMM kernels do not take (d_in % 8 != 0, x not
@@ -417,7 +417,7 @@ size_t lb_grouped_workspace_bytes(const lb_linear_desc *descs, int n, int64_t T,
  * x_dtype / y_dtype and T tokens.  The pointers in descs are captured: later
  * runs read and write the same buffers.  The kernels a group runs:
  *  - the matrix-core decode kernels where lb_linear_forward's path choice
- *    picks them (1 <= T <= 16, or up to 32 with fp32 outputs or the DECODE
+ *    picks them (1 <= T <= 8, or up to 32 with fp32 outputs or the DECODE
  *    flag) (stage 1 = activation operands, first contractions and latents;
  *    stage 2 = second contractions);
  *  - where it picks the GEMM kernels (bf16 output), bf16 input and shapes they take

@@ -143,7 +143,7 @@ def test_mlp_and_group_argument_errors():
 
 def test_linear_path_choice():
     """Which kernel family a request takes (host only): the decode kernels up
-    to 16 tokens, the bf16 GEMM kernels above for bf16 outputs, the decode
+    to 8 tokens, the bf16 GEMM kernels above for bf16 outputs, the decode
     kernels up to 32 tokens for fp32 outputs (or with the decode flag) and the
     vector-ALU kernels above, for shapes the GEMM kernels do not take, and for
     buffers the decode kernels' 32-bit offsets cannot address."""
@@ -151,8 +151,9 @@ def test_linear_path_choice():
     bf, f32 = torch.bfloat16, torch.float32
     D, G, V = lb.LB_PATH_DECODE, lb.LB_PATH_PREFILL, lb.LB_PATH_DECODE_VALU
     assert lb.linear_path(8192, 28672, 608, 1, True, bf, bf) == D
-    assert lb.linear_path(8192, 28672, 608, 16, True, bf, bf) == D
-    assert lb.linear_path(8192, 28672, 608, 17, True, bf, bf) == G
+    assert lb.linear_path(8192, 28672, 608, 8, True, bf, bf) == D
+    assert lb.linear_path(8192, 28672, 608, 9, True, bf, bf) == G
+    assert lb.linear_path(8192, 28672, 608, 16, True, bf, bf) == G
     assert lb.linear_path(8192, 28672, 608, 32, True, bf, bf) == G
     assert lb.linear_path(8192, 28672, 608, 32, True, bf, bf, lb.LB_PATH_DECODE) == D
     assert lb.linear_path(8192, 28672, 608, 16, True, f32, f32) == D   # fp32 outputs: no GEMM
