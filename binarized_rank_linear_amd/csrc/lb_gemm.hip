@@ -92,8 +92,8 @@ template <int NBW, int BM, int WR = 2> struct Shape {
     static constexpr int Lds = Stages * Slot > Staging ? Stages * Slot : Staging;
     static constexpr int MinWG = NBW == 4 ? 1 : (BM == 256 ? 2 : (BM == 128 ? 3 : 4));   // workgroups per CU
 };
-constexpr int kNBW1 = 2, kNBW2 = 2;          // stage 1, stage 2
-constexpr int kBN1 = 64 * kNBW1, kBN2 = 64 * kNBW2;
+constexpr int kNBW1 = 2;                     // stage 1 on 256-token tiles (2 x 2 waves)
+constexpr int kBN1 = 128, kBN2 = 128;        // output columns per tile, every shape
 constexpr int kWG1 = 512;                    // stage-1 workgroups a launch aims for: two per
                                              // CU on 256 CUs, so no CU runs a second round
 constexpr uint32_t kOOB = 0x7ffffff0u;       // a buffer offset past every range: reads as zero
@@ -853,8 +853,11 @@ int raise_lds(int bytes) {
 
 template <int STAGE, int BM>
 int launch_stage(const GRun &run, const GLin &single, int64_t items, hipStream_t st) {
-    constexpr int NBW = BM == 32 ? 1 : (STAGE == 1 ? kNBW1 : kNBW2);
-    constexpr int WR = BM == 32 ? 1 : 2;
+    // waves 1 x 4 (32 columns each: no two waves build the same sign operand)
+    // except stage 1 on 256-token tiles, whose long K favours 2 x 2 waves of
+    // 64 columns (half the activation reads per matrix instruction)
+    constexpr int NBW = STAGE == 1 && BM == 256 ? kNBW1 : 1;
+    constexpr int WR = STAGE == 1 && BM == 256 ? 2 : 1;
     using SH = Shape<NBW, BM, WR>;
     static_assert(SH::BN == (STAGE == 1 ? kBN1 : kBN2), "column tiles as planned");
     if (int rc = raise_lds<k_gemm<STAGE, NBW, BM, WR>>(SH::Lds)) return rc;
