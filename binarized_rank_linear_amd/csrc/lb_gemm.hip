@@ -54,17 +54,18 @@ namespace {
 //            three workgroups share a CU, whose tiles' epilogues and prologues
 //            overlap each other's matrix work);
 //   64 < T <= 128: 128 in both; 32 < T <= 64: 64 in both; T <= 32: 32 in
-//            both, each wave 32 tokens x 32 columns (a tile is mostly padding
-//            otherwise: the matrix work follows the tile, not T).
+//            both (a tile is mostly padding otherwise: the matrix work
+//            follows the tile, not T); these small tiles are 256 columns
+//            wide, the others 128.
 constexpr int kBM1 = 256, kBM2 = 128;
 struct TileRows {
-    int bm1, bm2;
+    int bm1, bm2, bn;    // tokens per tile of each stage; output columns per tile
 };
 TileRows tile_rows(int64_t T) {
-    if (T <= 32) return {32, 32};
-    if (T <= 64) return {64, 64};
-    if (T <= 128) return {128, 128};
-    return {kBM1, kBM2};
+    if (T <= 32) return {32, 32, 256};
+    if (T <= 64) return {64, 64, 256};
+    if (T <= 128) return {128, 128, 128};
+    return {kBM1, kBM2, 128};
 }
 constexpr int kBK = 64;                      // contraction elements per K-tile (two packed words)
 constexpr int kThreads = 256;
@@ -90,10 +91,9 @@ template <int NBW, int BM, int WR = 2> struct Shape {
     static constexpr int ER = BM == 256 ? 64 : 32;     // epilogue rows per wave and round
     static constexpr int Staging = kWaves * ER * (NBW * 32 * 4 + 16);   // room for fp32 outputs
     static constexpr int Lds = Stages * Slot > Staging ? Stages * Slot : Staging;
-    static constexpr int MinWG = NBW == 4 ? 1 : (BM == 256 ? 2 : (BM == 128 ? 3 : 4));   // workgroups per CU
+    static constexpr int MinWG = NBW == 4 ? 1 : (BM == 256 ? 2 : (BM == 128 || NBW == 2 ? 3 : 4));   // workgroups per CU
 };
 constexpr int kNBW1 = 2;                     // stage 1 on 256-token tiles (2 x 2 waves)
-constexpr int kBN1 = 128, kBN2 = 128;        // output columns per tile, every shape
 constexpr int kWG1 = 512;                    // stage-1 workgroups a launch aims for: two per
                                              // CU on 256 CUs, so no CU runs a second round
 constexpr uint32_t kOOB = 0x7ffffff0u;       // a buffer offset past every range: reads as zero
@@ -755,7 +755,7 @@ void stage1_splits(const Linear *ls, int n, std::vector<int> &splits) {
         const int64_t ldt = rup((int64_t)a.P * cdiv(a.r_p, 32) * 32, kBK);
         const int64_t nkt = cdiv(a.d_in, kBK);
         m.nkt.push_back(nkt);
-        m.tiles.push_back(cdiv(ldt, kBN1) * cdiv(a.T, tile_rows(a.T).bm1));
+        m.tiles.push_back(cdiv(ldt, tile_rows(a.T).bn) * cdiv(a.T, tile_rows(a.T).bm1));
         m.red_bytes.push_back(a.T * ldt * 4);
         for (int64_t sp = 1; sp <= 64; ++sp) {
             const int64_t l = cdiv(nkt, sp);
@@ -806,8 +806,8 @@ size_t plan(const Linear &a, GLin *m, int nsplit) {
     const TileRows tr = tile_rows(a.T);
     m->mt = (int32_t)cdiv(a.T, tr.bm1);
     m->mt2 = (int32_t)cdiv(a.T, tr.bm2);
-    m->nt1 = (int32_t)cdiv(m->ldt, kBN1);
-    m->nt2 = (int32_t)cdiv(a.d_out, kBN2);
+    m->nt1 = (int32_t)cdiv(m->ldt, tile_rows(a.T).bn);
+    m->nt2 = (int32_t)cdiv(a.d_out, tile_rows(a.T).bn);
     m->nred = m->nsplit > 1 ? (int32_t)cdiv(a.T * (m->ldt / 4), kThreads) : 0;
     const int64_t nv = (int64_t)a.P * m->kw_v * m->zld_v, nu = (int64_t)a.P * m->kw * m->zld_u;
     m->ngp = (int32_t)cdiv((int64_t)a.P * a.d_in / 2 + nv + nu, kPrep);
@@ -853,13 +853,15 @@ int raise_lds(int bytes) {
 
 template <int STAGE, int BM>
 int launch_stage(const GRun &run, const GLin &single, int64_t items, hipStream_t st) {
-    // waves 1 x 4 (32 columns each: no two waves build the same sign operand)
-    // except stage 1 on 256-token tiles, whose long K favours 2 x 2 waves of
-    // 64 columns (half the activation reads per matrix instruction)
-    constexpr int NBW = STAGE == 1 && BM == 256 ? kNBW1 : 1;
+    // waves 1 x 4 (no two waves build the same sign operand) except stage 1
+    // on 256-token tiles, whose long K favours 2 x 2 waves of 64 columns (half
+    // the activation reads per matrix instruction); tiles of up to 64 tokens
+    // are 256 columns wide (64 per wave: more sign words per K-tile behind
+    // each wait)
+    constexpr int NBW = STAGE == 1 && BM == 256 ? kNBW1 : (BM <= 64 ? 2 : 1);
     constexpr int WR = STAGE == 1 && BM == 256 ? 2 : 1;
     using SH = Shape<NBW, BM, WR>;
-    static_assert(SH::BN == (STAGE == 1 ? kBN1 : kBN2), "column tiles as planned");
+    static_assert(SH::BN == (BM <= 64 ? 256 : 128), "column tiles as planned");
     if (int rc = raise_lds<k_gemm<STAGE, NBW, BM, WR>>(SH::Lds)) return rc;
     k_gemm<STAGE, NBW, BM, WR><<<(unsigned)items, kThreads, SH::Lds, st>>>(run, single);
     return last_launch_status();
