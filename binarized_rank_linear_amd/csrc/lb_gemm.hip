@@ -59,14 +59,16 @@ namespace {
 //            wide, the others 128.
 constexpr int kBM1 = 256, kBM2 = 128;
 struct TileRows {
-    int bm1, bm2, bn;    // tokens per tile of each stage; output columns per tile
+    int bm1, bm2, bn1, bn2;    // tokens per tile of each stage; output columns per tile
 };
 TileRows tile_rows(int64_t T) {
-    if (T <= 32) return {32, 32, 256};
-    if (T <= 64) return {64, 64, 256};
-    if (T <= 128) return {128, 128, 128};
-    return {kBM1, kBM2, 128};
+    if (T <= 32) return {32, 32, 256, 256};
+    if (T <= 64) return {64, 64, 256, 256};
+    if (T <= 128) return {128, 128, 128, 128};
+    return {kBM1, kBM2, 128, 128};
 }
+// Columns per tile of a stage's kernel with BM token rows (as tile_rows plans).
+constexpr int tile_cols(int stage, int bm) { return bm <= 64 ? 256 : 128; }
 constexpr int kBK = 64;                      // contraction elements per K-tile (two packed words)
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
@@ -755,7 +757,7 @@ void stage1_splits(const Linear *ls, int n, std::vector<int> &splits) {
         const int64_t ldt = rup((int64_t)a.P * cdiv(a.r_p, 32) * 32, kBK);
         const int64_t nkt = cdiv(a.d_in, kBK);
         m.nkt.push_back(nkt);
-        m.tiles.push_back(cdiv(ldt, tile_rows(a.T).bn) * cdiv(a.T, tile_rows(a.T).bm1));
+        m.tiles.push_back(cdiv(ldt, tile_rows(a.T).bn1) * cdiv(a.T, tile_rows(a.T).bm1));
         m.red_bytes.push_back(a.T * ldt * 4);
         for (int64_t sp = 1; sp <= 64; ++sp) {
             const int64_t l = cdiv(nkt, sp);
@@ -806,8 +808,8 @@ size_t plan(const Linear &a, GLin *m, int nsplit) {
     const TileRows tr = tile_rows(a.T);
     m->mt = (int32_t)cdiv(a.T, tr.bm1);
     m->mt2 = (int32_t)cdiv(a.T, tr.bm2);
-    m->nt1 = (int32_t)cdiv(m->ldt, tile_rows(a.T).bn);
-    m->nt2 = (int32_t)cdiv(a.d_out, tile_rows(a.T).bn);
+    m->nt1 = (int32_t)cdiv(m->ldt, tr.bn1);
+    m->nt2 = (int32_t)cdiv(a.d_out, tr.bn2);
     m->nred = m->nsplit > 1 ? (int32_t)cdiv(a.T * (m->ldt / 4), kThreads) : 0;
     const int64_t nv = (int64_t)a.P * m->kw_v * m->zld_v, nu = (int64_t)a.P * m->kw * m->zld_u;
     m->ngp = (int32_t)cdiv((int64_t)a.P * a.d_in / 2 + nv + nu, kPrep);
@@ -861,7 +863,7 @@ int launch_stage(const GRun &run, const GLin &single, int64_t items, hipStream_t
     constexpr int NBW = STAGE == 1 && BM == 256 ? kNBW1 : (BM <= 64 ? 2 : 1);
     constexpr int WR = STAGE == 1 && BM == 256 ? 2 : 1;
     using SH = Shape<NBW, BM, WR>;
-    static_assert(SH::BN == (BM <= 64 ? 256 : 128), "column tiles as planned");
+    static_assert(SH::BN == tile_cols(STAGE, BM), "column tiles as planned");
     if (int rc = raise_lds<k_gemm<STAGE, NBW, BM, WR>>(SH::Lds)) return rc;
     k_gemm<STAGE, NBW, BM, WR><<<(unsigned)items, kThreads, SH::Lds, st>>>(run, single);
     return last_launch_status();
