@@ -224,20 +224,113 @@ def ceilings():
 
     iters, mblocks = 4000, 256 * 4
 
-    def mfma():
-        assert L.lb_ceiling_mfma_bf16(iters, out.data_ptr(), mblocks, s.cuda_stream) == 0
+    def mfma(rnd):
+        assert L.lb_ceiling_mfma_bf16(iters, rnd, out.data_ptr(), mblocks, s.cuda_stream) == 0
 
     t_read = timed(read, 20)
-    t_mfma = timed(mfma, 5)
+    t_mfma = timed(lambda: mfma(0), 5)
+    t_mfma_r = timed(lambda: mfma(1), 5)
     gbs = nbytes / t_read / 1e9
     tfl = mblocks * 4 * iters * 8 * 32768 / t_mfma / 1e12
+    tfl_r = mblocks * 4 * iters * 8 * 32768 / t_mfma_r / 1e12
     del buf
     torch.cuda.empty_cache()
     return {"stream_read_GBs": gbs, "stream_read_frac": gbs / HBM_PEAK_GBS,
             "mfma_bf16_TFLOPs": tfl, "mfma_bf16_frac": tfl / BF16_PEAK_TFLOPS,
+            "mfma_bf16_random_TFLOPs": tfl_r, "mfma_bf16_random_frac": tfl_r / BF16_PEAK_TFLOPS,
             "how": "2 GiB read by 2048 workgroups (a contiguous share each), 16-byte non-temporal loads, "
                    "8 in flight per thread; "
-                   "1024 workgroups x 4 waves x %d x 8 independent v_mfma_f32_32x32x16_bf16" % iters}
+                   "1024 workgroups x 4 waves x %d x 8 independent v_mfma_f32_32x32x16_bf16 on constant "
+                   "operands, and (random) cycling through four pseudo-random operands each" % iters}
+
+
+def clock_probe(w, secs=3.0):
+    """The GPU clock and socket power under each load: the load runs back to
+    back for `secs` seconds while a thread samples `rocm-smi --showmetrics`
+    (a child process per sample; the metrics refresh about once a second, so
+    samples from the load's first second are dropped).  Loads: the decode
+    pass of the workload's stack (T = 1), the bf16 matrix-rate ceiling on
+    constant and on pseudo-random operands, one prefill layer of the workload
+    at T = 2048, and the vendor library's bf16 GEMM of 8192 x 8192 x 8192 on
+    random data.  Reports the median clock (MHz), the median power (W) and
+    the load's time per call."""
+    import re
+    import shutil
+    import statistics
+    import subprocess
+    import threading
+    import torch
+    import synth
+    import binarized_rank_linear_amd as lb
+    if shutil.which("rocm-smi") is None:
+        return {"error": "rocm-smi not found"}
+    pat_c = re.compile(r"current_gfxclk \(MHz\):\s*(\d+)")
+    pat_p = re.compile(r"current_socket_power \(W\):\s*(\d+)")
+
+    def run(name, fn, calls_per_sync=4):
+        samples, stop = [], threading.Event()
+
+        def sample():
+            while not stop.is_set():
+                t = time.perf_counter()
+                r = subprocess.run(["rocm-smi", "--showmetrics"], capture_output=True, text=True, timeout=30)
+                c, p = pat_c.search(r.stdout), pat_p.search(r.stdout)
+                if c and p:
+                    samples.append((t, int(c.group(1)), int(p.group(1))))
+                stop.wait(0.1)
+        torch.cuda.synchronize()
+        th = threading.Thread(target=sample)
+        t0 = time.perf_counter()
+        th.start()
+        n = 0
+        while time.perf_counter() - t0 < secs:
+            fn()
+            n += 1
+            if n % calls_per_sync == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        stop.set()
+        th.join()
+        kept = [x for x in samples if x[0] - t0 >= 1.0]
+        _log("clocks: %s %d calls, %d samples kept" % (name, n, len(kept)))
+        return {"load": name, "ms_per_call": el / n * 1e3,
+                "gfxclk_MHz": statistics.median(x[1] for x in kept) if kept else None,
+                "socket_power_W": statistics.median(x[2] for x in kept) if kept else None,
+                "samples": len(kept)}
+
+    L = lb.lib()
+    s = torch.cuda.current_stream()
+    res = []
+    st, _ = build_stack(w, w.layers, 1)
+    res.append(run("decode pass, %d-layer stack, T=1" % w.layers, st.group.run, 20))
+    del st
+    torch.cuda.empty_cache()
+    out = torch.empty(1024 * 256, dtype=torch.float32, device="cuda")
+    for rnd, nm in ((0, "constant"), (1, "pseudo-random")):
+        res.append(run("bf16 matrix-rate ceiling, %s operands" % nm,
+                       lambda: L.lb_ceiling_mfma_bf16(4000, rnd, out.data_ptr(), 1024, s.cuda_stream)))
+    T = 2048
+    layer = []
+    for i, sh in enumerate(w.linears):
+        r, rp = lb.rank_for_budget(sh.d_in, sh.d_out, w.b_num, w.b_den, w.residual)
+        U, V, h, g, l = synth.device_layer(synth.layer_seed(0, i), sh.d_in, sh.d_out, rp, 2 if w.residual else 1)
+        layer.append(lb.PackedLinear.from_factors(U, V, h, g, l))
+        del U, V
+    xs = {d: synth.device_activations(synth.activation_seed(d), T, d, "bf16") for d in {q.d_in for q in w.linears}}
+    ys = [torch.empty((T, lin.d_out), dtype=torch.bfloat16, device="cuda") for lin in layer]
+    grp = lb.Group([(xs[lin.d_in], y, lin) for lin, y in zip(layer, ys)], T, torch.bfloat16, torch.bfloat16)
+
+    def pf():
+        grp.run_stage(1)
+        grp.run_stage(2)
+    res.append(run("prefill, one layer, T=2048", pf))
+    del grp, layer, xs, ys
+    torch.cuda.empty_cache()
+    a = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    res.append(run("vendor bf16 GEMM 8192^3, random data", lambda: torch.mm(a, b)))
+    return {"workload": w.title, "clocks": res}
 
 
 def measured_traffic(kernel, workload, T):
@@ -637,10 +730,14 @@ def prefill_per_linear(layer, xs, T, steps, P):
     return out
 
 
-def prefill_leg(w, T, steps):
+def prefill_leg(w, T, steps, settle_s=0.3):
     """One layer of the workload's linears at T tokens as one GEMM-path group:
     stage 1 (and the d_in-piece reduce) for all linears in one launch, then
-    stage 2 in one launch; HIP events bracket each on the launch stream."""
+    stage 2 in one launch.  After untimed passes for settle_s seconds (the
+    clocks leave idle and reach their loaded state), HIP events on the launch
+    stream bracket `steps` back-to-back passes (the figure and the roofline);
+    a second run of `steps` passes with an event between the stages gives
+    the split between them."""
     import torch
     import synth
     import binarized_rank_linear_amd as lb
@@ -661,6 +758,21 @@ def prefill_leg(w, T, steps):
         grp.run_stage(1)
         grp.run_stage(2)
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < settle_s:
+        for _ in range(8):
+            grp.run_stage(1)
+            grp.run_stage(2)
+        torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(steps):
+        grp.run_stage(1)
+        grp.run_stage(2)
+    e1.record(s)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / steps * 1e-3
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     for k in range(steps):
         ev[k][0].record(s)
@@ -671,14 +783,14 @@ def prefill_leg(w, T, steps):
     torch.cuda.synchronize()
     t1 = sum(e[0].elapsed_time(e[1]) for e in ev) / steps * 1e-3
     t2 = sum(e[1].elapsed_time(e[2]) for e in ev) / steps * 1e-3
-    t = t1 + t2
     f1 = sum(2 * T * lin.r * lin.d_in for lin in layer)
     f2 = sum(2 * T * lin.r * lin.d_out for lin in layer)
     flops = f1 + f2
     return {"workload": "%s, one layer (%d linears) as one group, T=%d (GEMM path)"
                         % (w.title, len(layer), T), "T": T,
             "tok_per_s": T / t, "ms_per_layer": t * 1e3,
-            "stage1_us": t1 * 1e6, "stage2_us": t2 * 1e6,
+            "stage1_us": t1 * 1e6, "stage2_us": t2 * 1e6, "split_note": "stage times from passes with an "
+            "event between the stages (their sum exceeds the back-to-back pass)",
             "stage1_TFLOPs": f1 / t1 / 1e12, "stage2_TFLOPs": f2 / t2 / 1e12,
             "roofline": {"bound": "mfma", "achieved": flops / t / 1e12, "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": flops / t / 1e12 / BF16_PEAK_TFLOPS},
@@ -711,6 +823,8 @@ def main():
                     help="only run the Dual-SVID initialisation leg and print its JSON")
     ap.add_argument("--itq-only", action="store_true",
                     help="only run the Joint-ITQ leg and print its JSON")
+    ap.add_argument("--clocks", action="store_true",
+                    help="only sample the GPU clock and power (rocm-smi) under each load and print them")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other decode legs (32-layer stack at T=4 and T=32), the "
                          "cache-resident configurations and the measured ceilings")
@@ -732,9 +846,12 @@ def main():
     if args.itq_only:
         print(json.dumps(joint_itq_leg()), flush=True)
         return
+    if args.clocks:
+        print(json.dumps(clock_probe(synth.WORKLOADS[args.workload])), flush=True)
+        return
     if args.prefill_only:
         w = synth.WORKLOADS[args.workload]
-        print(json.dumps(prefill_leg(w, args.prefill_tokens, max(1, args.steps))), flush=True)
+        print(json.dumps(prefill_leg(w, args.prefill_tokens, max(1, args.steps), args.settle)), flush=True)
         return
     w = synth.WORKLOADS[args.workload]
     layers = args.layers or w.layers
@@ -794,7 +911,7 @@ def main():
         out["decode_single_layer"] = single_layer_leg(w, T)
     if not args.no_prefill and args.prefill_tokens > 32:
         try:
-            out["prefill"] = prefill_leg(w, args.prefill_tokens, max(10, args.steps // 10))
+            out["prefill"] = prefill_leg(w, args.prefill_tokens, max(50, args.steps // 4), args.settle)
         except Exception as e:  # report, do not hide
             out["prefill"] = {"error": repr(e)}
     if not args.no_extra:
@@ -811,6 +928,8 @@ def main():
         if isinstance(out.get("prefill"), dict) and "roofline" in out["prefill"]:
             out["prefill"]["roofline"]["frac_of_measured_ceiling"] = \
                 out["prefill"]["roofline"]["achieved"] / c["mfma_bf16_TFLOPs"]
+            out["prefill"]["roofline"]["frac_of_random_operand_ceiling"] = \
+                out["prefill"]["roofline"]["achieved"] / c["mfma_bf16_random_TFLOPs"]
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, T, layers)
         if isinstance(out.get("prefill"), dict) and "roofline" in out["prefill"]:

@@ -165,7 +165,7 @@ def lib() -> ctypes.CDLL:
         L.lb_joint_itq.restype = ctypes.c_int
         L.lb_ceiling_stream_read.argtypes = [_vp, _sz, _vp, ctypes.c_int, _vp]
         L.lb_ceiling_stream_read.restype = ctypes.c_int
-        L.lb_ceiling_mfma_bf16.argtypes = [ctypes.c_int, _vp, ctypes.c_int, _vp]
+        L.lb_ceiling_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, _vp, ctypes.c_int, _vp]
         L.lb_ceiling_mfma_bf16.restype = ctypes.c_int
         _lib = L
     return _lib

@@ -473,9 +473,13 @@ int lb_ceiling_stream_read(const void *buf, size_t bytes, void *out, int blocks,
 
 /* `blocks` workgroups of 4 waves, each wave issuing iters x 8 independent
  * v_mfma_f32_32x32x16_bf16 (32768 flops each) on register operands: the
- * bf16 matrix rate the prefill GEMMs can reach.  out (device) receives
- * blocks * 256 floats.  Enqueued on stream.  LB_EINVAL on bad arguments. */
-int lb_ceiling_mfma_bf16(int iters, void *out, int blocks, void *stream);
+ * bf16 matrix rate the prefill GEMMs can reach.  random_operands 0: the same
+ * few, mostly constant operand words in every instruction; 1: the
+ * instructions cycle through four pseudo-random A and B operands each (random
+ * signs and mantissas), whose toggling inputs draw the power a GEMM on real
+ * data draws.  out (device) receives blocks * 256 floats.  Enqueued on
+ * stream.  LB_EINVAL on bad arguments (random_operands other than 0 or 1). */
+int lb_ceiling_mfma_bf16(int iters, int random_operands, void *out, int blocks, void *stream);
 
 #ifdef __cplusplus
 }
