@@ -32,6 +32,7 @@
 #include <cstring>
 #include <functional>
 #include <map>
+#include <type_traits>
 #include <vector>
 
 #include "lb_internal.h"
@@ -90,7 +91,7 @@ template <int NBW, int BM, int WR = 2> struct Shape {
     static constexpr int XWave = 2 * XS * 4;           // a wave's sign words: [2 words][XS]
     static constexpr int Slot = ABytes + kWaves * (XWave + kGWave);
     static constexpr int Stages = NBW == 4 ? 4 : 2;
-    static constexpr int ER = BM == 256 ? 64 : 32;     // epilogue rows per wave and round
+    static constexpr int ER = BM >= 128 ? 64 : 32;     // epilogue rows per wave and round
     static constexpr int Staging = kWaves * ER * (NBW * 32 * 4 + 16);   // room for fp32 outputs
     static constexpr int Lds = Stages * Slot > Staging ? Stages * Slot : Staging;
     static constexpr int MinWG = NBW == 4 ? 1 : (BM == 256 ? 2 : (BM == 128 || NBW == 2 ? 3 : 4));   // workgroups per CU
@@ -250,13 +251,16 @@ __global__ __launch_bounds__(kThreads, (Shape<NBW, BM, WR>::MinWG)) void k_gemm(
     const int32_t *ord = STAGE == 1 ? run.ord1 : run.ord2;
     const int64_t v = ord ? (int64_t)__builtin_amdgcn_readfirstlane(ord[blockIdx.x]) : xcd_order(blockIdx.x, items);
     const GLin L = pick(run, single, STAGE == 1 ? run.lin1 : run.lin2, v);
-    const int64_t local = v - (STAGE == 1 ? L.item1 : L.item2);
-    // item = (piece of d_in [stage 1], token tile, column tile)
-    const int nt = STAGE == 1 ? L.nt1 : L.nt2;
-    const int ni = (int)(local % nt);
-    const int mt = STAGE == 1 ? L.mt : L.mt2;
-    const int mi = (int)((local / nt) % mt);
-    const int split = STAGE == 1 ? (int)(local / ((int64_t)nt * mt)) : 0;
+    // item = (piece of d_in [stage 1], token tile, column tile); a launch has
+    // fewer than 2^31 items, so the decode runs in 32 bits
+    const uint32_t local = (uint32_t)(v - (STAGE == 1 ? L.item1 : L.item2));
+    const uint32_t nt = (uint32_t)(STAGE == 1 ? L.nt1 : L.nt2);
+    const uint32_t mt = (uint32_t)(STAGE == 1 ? L.mt : L.mt2);
+    const uint32_t lq = local / nt;
+    const int ni = (int)(local - lq * nt);
+    const uint32_t lq2 = lq / mt;
+    const int mi = (int)(lq - lq2 * mt);
+    const int split = STAGE == 1 ? (int)lq2 : 0;
     const int T = run.T;
     const int64_t m0 = (int64_t)mi * BM;
     const int n0 = ni * BN;
@@ -485,70 +489,79 @@ __global__ __launch_bounds__(kThreads, (Shape<NBW, BM, WR>::MinWG)) void k_gemm(
         : (const uint8_t *)L.y;
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(obase + m0 * ld_out * osz, (int64_t)rows * ld_out * osz);
     constexpr int WC = NBW * 32;                               // columns of a wave
-    const int rbytes = WC * osz + 16;                          // staged row (padded)
     uint8_t *stage = smem + wave * ER * (WC * 4 + 16);         // room for the fp32 case
     static_assert(kWaves * ER * (WC * 4 + 16) <= SH::Lds, "epilogue staging fits the ring");
     // whole 16-byte chunks only when every row starts 16-byte aligned
     const bool chunky = ((ld_out * osz) % 16) == 0 && ((uintptr_t)obase % 16) == 0;
+    // buffer offsets stay below 2^31 (the descriptor's range), so 32 bits hold them
+    const uint32_t ld32 = (uint32_t)ld_out, nlim32 = (uint32_t)n_lim;
     wait_and_meet<0>();                                        // every wave is done with the ring
+    auto epilogue = [&](auto osz_c) {
+        constexpr int OSZ = decltype(osz_c)::value;
+        constexpr int rbytes = WC * OSZ + 16;                  // staged row (padded)
 #pragma unroll
-    for (int half = 0; half < MB * 32 / ER; ++half) {
-        // accumulators -> LDS (l applied for stage-1 latents)
+        for (int half = 0; half < MB * 32 / ER; ++half) {
+            // accumulators -> LDS (l applied for stage-1 latents)
 #pragma unroll
-        for (int mh = 0; mh < ER / 32; ++mh) {
-            const int mb = (ER / 32) * half + mh;
-            uint8_t *rowp = stage + (mh * 32 + l32) * rbytes;
+            for (int mh = 0; mh < ER / 32; ++mh) {
+                const int mb = (ER / 32) * half + mh;
+                uint8_t *rowp = stage + (mh * 32 + l32) * rbytes;
 #pragma unroll
-            for (int b = 0; b < NBW; ++b)
+                for (int b = 0; b < NBW; ++b)
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const f32x16 &a = acc[b][mb];
-                    float o0 = a[4 * q4], o1 = a[4 * q4 + 1], o2 = a[4 * q4 + 2], o3 = a[4 * q4 + 3];
-                    const int c = b * 32 + 8 * q4 + 4 * hh;          // column within the wave
-                    if (STAGE == 1 && L.nsplit == 1) {
-                        const u32x2 w = lsc[b][q4];
-                        const bool ok = (lok >> (4 * b + q4)) & 1u;   // padding columns stay zero
-                        o0 = ok ? f16_to_f32((uint16_t)(w[0] & 0xffffu)) * o0 : 0.0f;
-                        o1 = ok ? f16_to_f32((uint16_t)(w[0] >> 16)) * o1 : 0.0f;
-                        o2 = ok ? f16_to_f32((uint16_t)(w[1] & 0xffffu)) * o2 : 0.0f;
-                        o3 = ok ? f16_to_f32((uint16_t)(w[1] >> 16)) * o3 : 0.0f;
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const f32x16 &a = acc[b][mb];
+                        float o0 = a[4 * q4], o1 = a[4 * q4 + 1], o2 = a[4 * q4 + 2], o3 = a[4 * q4 + 3];
+                        const int c = b * 32 + 8 * q4 + 4 * hh;          // column within the wave
+                        if (STAGE == 1 && L.nsplit == 1) {
+                            const u32x2 w = lsc[b][q4];
+                            const bool ok = (lok >> (4 * b + q4)) & 1u;   // padding columns stay zero
+                            o0 = ok ? f16_to_f32((uint16_t)(w[0] & 0xffffu)) * o0 : 0.0f;
+                            o1 = ok ? f16_to_f32((uint16_t)(w[0] >> 16)) * o1 : 0.0f;
+                            o2 = ok ? f16_to_f32((uint16_t)(w[1] & 0xffffu)) * o2 : 0.0f;
+                            o3 = ok ? f16_to_f32((uint16_t)(w[1] >> 16)) * o3 : 0.0f;
+                        }
+                        if constexpr (OSZ == 2)
+                            *(u32x2 *)(rowp + c * 2) = u32x2{bf16_pair(o0, o1), bf16_pair(o2, o3)};
+                        else
+                            *(f32x4 *)(rowp + c * 4) = f32x4{o0, o1, o2, o3};
                     }
-                    if (osz == 2)
-                        *(u32x2 *)(rowp + c * 2) = u32x2{bf16_pair(o0, o1), bf16_pair(o2, o3)};
-                    else
-                        *(f32x4 *)(rowp + c * 4) = f32x4{o0, o1, o2, o3};
-                }
-        }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave's LDS writes land
-        // LDS -> global: ER rows x WC columns in 16-byte chunks, lane order row-major
-        const int cpr = WC * osz / 16;                         // chunks per row
-        const int nchunks = ER * cpr;
-        for (int ci = lane; ci < nchunks; ci += 64) {
-            const int r = ci / cpr, ch = ci - r * cpr;
-            const int col = ch * (16 / osz);                   // first column of the chunk
-            const int n = nw0 + col;
-            const u32x4 val = *(const u32x4 *)(stage + r * rbytes + ch * 16);
-            const uint32_t off =
-                (uint32_t)(((wm * (BM / WR) + half * ER + r) * ld_out + n) * osz);
-            const int per = 16 / osz;
-            if (chunky && n + per <= n_lim) {
-                // non-temporal: the outputs stream out instead of filling the L2
-                // that holds the activation rows other tiles still read
-                __builtin_amdgcn_raw_buffer_store_b128(val, ro, (int)off, 0, 2);
-            } else {
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave's LDS writes land
+            // LDS -> global: ER rows x WC columns in 16-byte chunks, lane order row-major
+            constexpr int cpr = WC * OSZ / 16;                     // chunks per row
+            constexpr int per = 16 / OSZ;                          // columns per chunk
+            static_assert((ER * cpr) % 64 == 0, "whole rounds of 64 chunks");
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    if (e >= per || n + e >= n_lim) break;
-                    if (osz == 2)
-                        __builtin_amdgcn_raw_buffer_store_b16(
-                            (unsigned short)((val[e >> 1] >> (16 * (e & 1))) & 0xffffu), ro, (int)(off + 2 * e), 0, 0);
-                    else
-                        __builtin_amdgcn_raw_buffer_store_b32(val[e], ro, (int)(off + 4 * e), 0, 0);
+            for (int i = 0; i < ER * cpr / 64; ++i) {
+                const int ci = lane + 64 * i;
+                const int r = ci / cpr, ch = ci % cpr;
+                const uint32_t n = (uint32_t)(nw0 + ch * per);    // first column of the chunk
+                const u32x4 val = *(const u32x4 *)(stage + r * rbytes + ch * 16);
+                const uint32_t off = ((uint32_t)(wm * (BM / WR) + half * ER + r) * ld32 + n) * OSZ;
+                if (chunky && n + per <= nlim32) {
+                    // non-temporal: the outputs stream out instead of filling the L2
+                    // that holds the activation rows other tiles still read
+                    __builtin_amdgcn_raw_buffer_store_b128(val, ro, (int)off, 0, 2);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < per; ++e) {
+                        if (n + e >= nlim32) break;
+                        if constexpr (OSZ == 2)
+                            __builtin_amdgcn_raw_buffer_store_b16(
+                                (unsigned short)((val[e >> 1] >> (16 * (e & 1))) & 0xffffu), ro, (int)(off + 2 * e), 0, 0);
+                        else
+                            __builtin_amdgcn_raw_buffer_store_b32(val[e], ro, (int)(off + 4 * e), 0, 0);
+                    }
                 }
             }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the next half
         }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the next half
-    }
+    };
+    if (osz == 2)
+        epilogue(std::integral_constant<int, 2>{});
+    else
+        epilogue(std::integral_constant<int, 4>{});
 }
 
 // Per-call operand preparation: g -> bf16 (round to nearest even) for the
