@@ -345,12 +345,21 @@ def measured_traffic(kernel, workload, T):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    src = os.path.join(ROOT, "binarized_rank_linear_amd", "csrc", kv.get("source", ""))
-    if not os.path.exists(src):
-        return None
-    if hashlib.sha256(open(src, "rb").read()).hexdigest() != kv.get("source_sha256"):
+    if source_sha256(kv.get("source", "")) != kv.get("source_sha256"):
         return None
     return float(kv["traffic_bytes_per_launch"])
+
+
+def source_sha256(names):
+    """sha256 over the named csrc files (space-separated), in that order; None
+    when one is missing."""
+    h = hashlib.sha256()
+    for name in names.split():
+        src = os.path.join(ROOT, "binarized_rank_linear_amd", "csrc", name)
+        if not os.path.exists(src):
+            return None
+        h.update(open(src, "rb").read())
+    return h.hexdigest() if names.split() else None
 
 
 def calibrate_copy(mib, reps):

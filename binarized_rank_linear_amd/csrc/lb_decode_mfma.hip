@@ -605,10 +605,11 @@ __global__ __launch_bounds__(kThreads) void k_stage1(MRun run, MLin single) {
             ao[b] = load_op(ops + b * kOpS);
             sa[b] = ops[b * kOpS + kOp + lane];
         }
-        const uint32_t ws[4] = {w[j][0], w[j][1], w[j][2], w[j][3]};
+        v8i sgq[4];
+        unpack_quad(w[j], nib, sgq);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const v8i sg = unpack_word(ws[m], nib);
+            const v8i sg = sgq[m];
 #pragma unroll
             for (int b = 0; b < NB1; ++b) acc[m][b] = mfma(ao[b], sg, acc[m][b], sa[b]);
         }
@@ -941,8 +942,10 @@ __device__ __forceinline__ void stage1f_item(const MRun &run, const MLin &L, int
         const uint8_t *rec = recs + ((size_t)(ka + pk) * R1 + rr) * kRec;
         const v8i ao = load_op_at(rec + gq * 32);
         const int sa = rec[128 + gq];
+        v8i sgq[4];
+        unpack_quad(w, nib, sgq);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) acc[m] = mfma(ao, unpack_word(w[m], nib), acc[m], sa);
+        for (int m = 0; m < 4; ++m) acc[m] = mfma(ao, sgq[m], acc[m], sa);
         if (++pk == nk) {
             tile_end(pt);
             pk = 0;
@@ -1296,10 +1299,11 @@ __global__ __launch_bounds__(kThreads) void k_stage2(MRun run, MLin single) {
                 ao[b] = load_op(opp + b * kOpS);
                 sa[b] = opp[b * kOpS + kOp + lane];
             }
-            const uint32_t ws[4] = {wc[j][0], wc[j][1], wc[j][2], wc[j][3]};
+            v8i sgq[4];
+            unpack_quad(wc[j], nib, sgq);
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                const v8i sg = unpack_word(ws[m], nib);
+                const v8i sg = sgq[m];
 #pragma unroll
                 for (int b = 0; b < NB2; ++b) acc[m][b] = mfma(ao[b], sg, acc[m][b], sa[b]);
             }
@@ -1471,9 +1475,11 @@ __device__ __forceinline__ void stage2r_item(const MRun &run, const MLin &L, int
             sa[b] = sl[so + b * sb];
         }
         so += ss;
+        v8i sgq[4];
+        unpack_quad(w, nib, sgq);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const v8i sg = unpack_word(w[m], nib);
+            const v8i sg = sgq[m];
 #pragma unroll
             for (int b = 0; b < NB2; ++b) acc[m][b] = mfma(ao[b], sg, acc[m][b], sa[b]);
         }

@@ -99,6 +99,33 @@ __device__ __forceinline__ v8i unpack_word(uint32_t w, const Nib &k) {
     return a;
 }
 
+// The fp4 sign operands of four plane words, two words per 64-bit shift: the
+// bits a shift carries from the low word into the high one land at nibble bits
+// 0..2, which the mask clears, so each word's operand is unpack_word's.  Three
+// v_lshlrev_b64 replace six 32-bit shifts (written out: the compiler splits a
+// 64-bit shift into a 32-bit shift and a v_alignbit_b32, two instructions).
+__device__ __forceinline__ void unpack_quad(const v4u &w, const Nib &k, v8i sg[4]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint64_t W = ((uint64_t)w[2 * h + 1] << 32) | (uint64_t)w[2 * h];
+        uint64_t W3, W2, W1;
+        asm("v_lshlrev_b64 %0, 3, %1" : "=v"(W3) : "v"(W));
+        asm("v_lshlrev_b64 %0, 2, %1" : "=v"(W2) : "v"(W));
+        asm("v_lshlrev_b64 %0, 1, %1" : "=v"(W1) : "v"(W));
+        v8i &lo = sg[2 * h], &hi = sg[2 * h + 1];
+        lo[0] = (int)sign_nibbles((uint32_t)W3, k);
+        lo[1] = (int)sign_nibbles((uint32_t)W2, k);
+        lo[2] = (int)sign_nibbles((uint32_t)W1, k);
+        lo[3] = (int)sign_nibbles((uint32_t)W, k);
+        hi[0] = (int)sign_nibbles((uint32_t)(W3 >> 32), k);
+        hi[1] = (int)sign_nibbles((uint32_t)(W2 >> 32), k);
+        hi[2] = (int)sign_nibbles((uint32_t)(W1 >> 32), k);
+        hi[3] = (int)sign_nibbles((uint32_t)(W >> 32), k);
+        lo[4] = lo[5] = lo[6] = lo[7] = 0;
+        hi[4] = hi[5] = hi[6] = hi[7] = 0;
+    }
+}
+
 // 32 bytes at p (16-byte aligned) as an fp8 operand
 __device__ __forceinline__ v8i load_op_at(const uint8_t *p) {
     const v4u lo = *(const v4u *)p, hi = *(const v4u *)(p + 16);
