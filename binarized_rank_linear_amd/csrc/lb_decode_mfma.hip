@@ -938,10 +938,15 @@ __device__ __forceinline__ void stage1f_item(const MRun &run, const MLin &L, int
         for (int m = 0; m < 4; ++m) acc[m] = v4f{0.f, 0.f, 0.f, 0.f};
     };
     int pk = 0, pt = 0;
+    // this lane's operand quarter and scale in the record of row rr; records of
+    // successive K-groups are R1 * kRec bytes apart (a scalar step)
+    const uint8_t *rec_a = recs + (size_t)rr * kRec + gq * 32;
+    const uint8_t *rec_s = recs + (size_t)rr * kRec + 128 + gq;
+    const int rec_step = R1 * kRec;
     auto process = [&](const v4u &w) {
-        const uint8_t *rec = recs + ((size_t)(ka + pk) * R1 + rr) * kRec;
-        const v8i ao = load_op_at(rec + gq * 32);
-        const int sa = rec[128 + gq];
+        const int ro = (ka + pk) * rec_step;
+        const v8i ao = load_op_at(rec_a + ro);
+        const int sa = rec_s[ro];
         v8i sgq[4];
         unpack_quad(w, nib, sgq);
 #pragma unroll
