@@ -321,7 +321,8 @@ int lb_dual_svid(const float *w, int64_t d_out, int64_t d_in, int64_t r, int res
  * The call waits for the stream (it reads the polar iteration's progress) and
  * returns with the work done; not capturable.  LB_EUNSUPPORTED when a polar
  * decomposition did not converge in 64 iterations (u, v hold the factors
- * rotated by the last R that did), or (d_out + d_in) * r_p >= 2^31. */
+ * rotated by the last R that did), or (d_out + d_in) * r_p >= 2^31, or
+ * r_p >= 2^15. */
 size_t lb_joint_itq_workspace_bytes(int64_t d_out, int64_t d_in, int64_t r_p);
 int lb_joint_itq(float *u, float *v, int64_t d_out, int64_t d_in, int64_t r_p, int iters,
                  const float *rot0, float *rot, double *objective, void *ws, size_t ws_bytes, void *stream);
