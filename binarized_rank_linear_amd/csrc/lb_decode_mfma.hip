@@ -216,11 +216,29 @@ __device__ __forceinline__ int64_t item_start(const MLin &m, int kind) {
     return kind == kKindPrep ? m.item0 : kind == kKindStage1 ? m.item1 : kind == kKindLatent ? m.itemF : m.item2;
 }
 
-template <int KIND>
+// Element i of a table the launch only reads (orders, linear maps, linear
+// tables: written before the launch) at a uniform index, through the
+// constant address space, so the compiler reads it with scalar loads.
+template <typename T>
+__device__ __forceinline__ T table_at(const T *p, int64_t i) {
+    static_assert(sizeof(T) % 4 == 0, "tables are read as 32-bit words");
+    typedef const __attribute__((address_space(4))) uint32_t cword;
+    cword *q = (cword *)(p + i);
+    uint32_t w[sizeof(T) / 4];
+#pragma unroll
+    for (int k = 0; k < (int)(sizeof(T) / 4); ++k) w[k] = q[k];
+    T r;
+    __builtin_memcpy(&r, w, sizeof(T));
+    return r;
+}
+
+// SCALAR: the table entry through scalar loads (the standalone kernels; in
+// the one-launch pass the whole entry in scalar registers would spill them).
+template <int KIND, bool SCALAR = false>
 __device__ __forceinline__ MLin pick(const MRun &run, const MLin &single, const int32_t *map, int64_t item) {
     MLin m;
     if (run.table) {
-        m = run.table[map[item]];
+        m = SCALAR ? table_at(run.table, (int64_t)table_at(map, item)) : run.table[map[item]];
     } else if (run.ninl) {
         // inline groups: the last linear starting at or before item (constant
         // indices only: a variable index into the kernel arguments would copy
@@ -272,9 +290,11 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 
 // The item a workgroup runs: launches of a group start their largest items
 // first (ord), so the last workgroups to start are short ones.
+template <bool SCALAR = false>
 __device__ __forceinline__ int64_t item_of(const int32_t *ord, int64_t base) {
     const int64_t w = (int64_t)blockIdx.x + base;
-    return ord ? (int64_t)__builtin_amdgcn_readfirstlane(ord[w]) : w;
+    if (!ord) return w;
+    return SCALAR ? (int64_t)table_at(ord, w) : (int64_t)__builtin_amdgcn_readfirstlane(ord[w]);
 }
 
 // silu(z) = z / (1 + exp(-z)); -0 for very negative z, no NaN for finite z
@@ -457,7 +477,7 @@ __global__ __launch_bounds__(kThreads) void k_prep(MRun run, MLin single) {
     if (stale_ws(run)) return;
     using R = Rows<NL>;
     const int64_t item = (int64_t)blockIdx.x + run.base0;
-    const MLin L = pick<kKindPrep>(run, single, run.lin0, item);
+    const MLin L = pick<kKindPrep, true>(run, single, run.lin0, item);
     const int64_t local = item - L.item0;
     const int c = (int)(local % L.nprep);
     const int p = (int)(local / L.nprep);
@@ -550,8 +570,8 @@ __global__ __launch_bounds__(kThreads) void k_stage1(MRun run, MLin single) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     if (stale_ws(run)) return;
     using R = Rows<NL>;
-    const int64_t item = item_of(run.ord1, run.base1);
-    const MLin L = pick<kKindStage1>(run, single, run.lin1, item);
+    const int64_t item = item_of<true>(run.ord1, run.base1);
+    const MLin L = pick<kKindStage1, true>(run, single, run.lin1, item);
     const int64_t local = item - L.item1;
     const int rg = (int)(local % L.nrg);
     const int c = (int)((local / L.nrg) % L.nchunks);
@@ -986,8 +1006,8 @@ template <int NL, bool XM = false>
 __global__ __launch_bounds__(kThreads) void k_stage1f(MRun run, MLin single) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     if (stale_ws(run)) return;
-    const int64_t item = item_of(run.ord1, run.base1);
-    stage1f_item<NL, false, XM>(run, pick<kKindStage1>(run, single, run.lin1, item), item, smem);
+    const int64_t item = item_of<true>(run.ord1, run.base1);
+    stage1f_item<NL, false, XM>(run, pick<kKindStage1, true>(run, single, run.lin1, item), item, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -1192,7 +1212,7 @@ __global__ __launch_bounds__(kThreads) void k_latent(MRun run, MLin single) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     if (stale_ws(run)) return;
     const int64_t item = (int64_t)blockIdx.x + run.baseF;
-    const MLin L = pick<kKindLatent>(run, single, run.linF, item);
+    const MLin L = pick<kKindLatent, true>(run, single, run.linF, item);
     const int kg_first = (int)(item - L.itemF) * 2;               // 2 K-groups = 8 planes per item
     latent_item<NL, NB2>(run, L, kg_first, (int)imin(2, L.kgs - kg_first), smem);
 }
@@ -1209,8 +1229,8 @@ __global__ __launch_bounds__(kThreads) void k_stage2(MRun run, MLin single) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     if (stale_ws(run)) return;
     using R = Rows<NL>;
-    const int64_t item = item_of(run.ord2, run.base2);
-    const MLin L = pick<kKindStage2>(run, single, run.lin2, item);
+    const int64_t item = item_of<true>(run.ord2, run.base2);
+    const MLin L = pick<kKindStage2, true>(run, single, run.lin2, item);
     const int64_t local = item - L.item2;
     const int T = run.T;
     const int lane = threadIdx.x & 63, wave = wave_id();
@@ -1619,8 +1639,8 @@ template <int NL, int NB2>
 __global__ __launch_bounds__(kThreads) void k_stage2r(MRun run, MLin single) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     if (stale_ws(run)) return;
-    const int64_t item = item_of(run.ord2, run.base2);
-    const MLin L = pick<kKindStage2>(run, single, run.lin2, item);
+    const int64_t item = item_of<true>(run.ord2, run.base2);
+    const MLin L = pick<kKindStage2, true>(run, single, run.lin2, item);
     const int64_t row_begin = (item - L.item2) * L.rows2;
     const int tiles = (int)imin(L.rows2 / kRG, cdiv(L.d_out - row_begin, kRG));
     stage2r_item<NL, NB2, false>(run, L, row_begin, tiles, smem, nullptr);
