@@ -291,3 +291,39 @@ def test_outlier_activations(path, T, dt):
     if dt == "bf16":
         x = synth.f32_to_bf16_bits(x)
     _check(inp, x, dt, path)
+
+
+# ---- stage-1 pieces of a prepared group ----
+
+@pytest.mark.parametrize("d_in,d_out,r_p,P,T", [(16384, 1024, 128, 2, 500), (28672, 1536, 304, 2, 2048),
+                                                (9000, 300, 96, 1, 100)])
+def test_prefill_pieces_group_equals_single(d_in, d_out, r_p, P, T):
+    """A group of one long-d_in linear on the GEMM kernels: stage 1 splits
+    d_in into pieces (up to 32 here) that a reduce launch adds in piece order;
+    the single-linear call plans the same split.  Every run of the prepared
+    group, with other inputs in between, equals the single call on its own
+    inputs bit for bit, and the oracle on sampled tokens and rows."""
+    torch = torch_or_skip()
+    import binarized_rank_linear_amd as lb
+    inp = synth.layer_inputs(d_in + 5 * d_out + r_p, d_in, d_out, r_p, P)
+    layer = dev_layer(inp)
+    xh = [synth.activations(T + 11 * k + d_in, T, d_in, "bf16") for k in range(2)]
+    xs = [x_to_dev(x) for x in xh]
+    say("pieces", d_in, d_out, r_p, P, "T", T)
+    refs = [lb.linear_forward(x, layer, torch.bfloat16, PATH_FLAG["prefill"]) for x in xs]
+    x = xs[0].clone()
+    y = torch.empty(T, d_out, dtype=torch.bfloat16, device="cuda")
+    grp = lb.Group([(x, y, layer)], T, torch.bfloat16, torch.bfloat16, PATH_FLAG["prefill"])
+    torch.cuda.synchronize()
+    assert not torch.equal(refs[0].view(torch.int16), refs[1].view(torch.int16))
+    for k in (0, 1, 1, 0):
+        x.copy_(xs[k])
+        y.fill_(float("nan"))
+        grp.run()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), refs[k].view(torch.int16)), k
+    grp.release()
+    tokens = np.unique(np.array([0, 1, T // 2, T - 2, T - 1]))
+    rows = np.unique(np.linspace(0, d_out - 1, 256).astype(np.int64))
+    ref = oracle.linear_forward_rows(xh[0][tokens], inp.U, inp.V, inp.h, inp.g, inp.l, rows)
+    assert_close(y_to_np(refs[0])[tokens][:, rows], ref, TOL["bf16"], ("pieces", d_in, T))
