@@ -39,6 +39,7 @@
 //            paths back to back, so no plane is read twice.
 //   stage 2: item = (linear, block of output rows): each wave walks 64-row
 //            tiles, streaming the U planes of both paths into one accumulator set.
+#include <atomic>
 #include <algorithm>
 #include <cstdlib>
 #include <cstring>
@@ -2006,16 +2007,20 @@ bool mfma_decode_shape_ok(const Linear &a) {
            kgv * a.T * a.P * a.r_p * 4 < lim && kgs * 8 * 16 * kRec < lim;
 }
 
+// The fault word's address on the current device, looked up once per device
+// (threads that race on the first lookup store the same address).
 uint32_t *fault_word_ptr() {
-    static uint32_t *ptr[64] = {};
+    static std::atomic<uint32_t *> ptr[64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-    if (!ptr[dev]) {
+    uint32_t *q = ptr[dev].load(std::memory_order_acquire);
+    if (!q) {
         void *p = nullptr;
         if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_lb_faults)) != hipSuccess) return nullptr;
-        ptr[dev] = (uint32_t *)p;
+        q = (uint32_t *)p;
+        ptr[dev].store(q, std::memory_order_release);
     }
-    return ptr[dev];
+    return q;
 }
 
 size_t mfma_decode_workspace_bytes(const Linear &a) {
