@@ -368,11 +368,14 @@ __global__ __launch_bounds__(kThreads, (Shape<NBW, BM, WR>::MinWG)) void k_gemm(
     const uint32_t xshift = 4u - 4u * (uint32_t)hh;
 
     // stage 1 without pieces: l for this lane's output columns (4 per accumulator
-    // quad), loaded before the K loop.  r_p is a multiple of 16, so a run of 4
-    // columns is all real latents or all padding.
+    // quad), loaded before the K loop.  A run of 4 columns whose first one is a
+    // padding latent is all padding (bit of lok clear: zeros out); a run that
+    // crosses r_p (r_p not a multiple of 4) takes l = 0 past it, so its padding
+    // columns come out zero too.
     u32x2 lsc[NBW][4];
-    uint32_t lok = 0;                                  // bit 4b+q4: run of real latents
+    uint32_t lok = 0;                                  // bit 4b+q4: run starts at a real latent
     if (STAGE == 1 && L.nsplit == 1) {
+        int lk[NBW][4];                                // the run's first latent of its path, or -1
         const uint16_t *lp[NBW][4];
 #pragma unroll
         for (int b = 0; b < NBW; ++b)
@@ -384,9 +387,10 @@ __global__ __launch_bounds__(kThreads, (Shape<NBW, BM, WR>::MinWG)) void k_gemm(
                 const int k = (qn - p * L.kw) * 32 + (n & 31);
                 const bool ok = n < L.ldt && p < L.P && k < L.r_p;
                 lok |= (ok ? 1u : 0u) << (4 * b + q4);
+                lk[b][q4] = ok ? k : -1;
                 lp[b][q4] = L.l + (ok ? (int64_t)p * L.r_p + k : 0);
             }
-        if (((uintptr_t)L.l & 7) == 0) {
+        if (((uintptr_t)L.l & 7) == 0 && (L.r_p & 3) == 0) {     // uniform: whole runs, 8-byte aligned
 #pragma unroll
             for (int b = 0; b < NBW; ++b)
 #pragma unroll
@@ -397,8 +401,11 @@ __global__ __launch_bounds__(kThreads, (Shape<NBW, BM, WR>::MinWG)) void k_gemm(
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     const uint16_t *q = lp[b][q4];
-                    lsc[b][q4] = u32x2{(uint32_t)q[0] | ((uint32_t)q[1] << 16),
-                                       (uint32_t)q[2] | ((uint32_t)q[3] << 16)};
+                    const int k = lk[b][q4];
+                    uint32_t e[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) e[i] = (k >= 0 && k + i < L.r_p) ? (uint32_t)q[i] : 0u;
+                    lsc[b][q4] = u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
                 }
         }
     }

@@ -327,3 +327,16 @@ def test_prefill_pieces_group_equals_single(d_in, d_out, r_p, P, T):
     rows = np.unique(np.linspace(0, d_out - 1, 256).astype(np.int64))
     ref = oracle.linear_forward_rows(xh[0][tokens], inp.U, inp.V, inp.h, inp.g, inp.l, rows)
     assert_close(y_to_np(refs[0])[tokens][:, rows], ref, TOL["bf16"], ("pieces", d_in, T))
+
+
+@pytest.mark.parametrize("d_in,d_out,r_p,P,T", [(1000, 700, 17, 2, 40), (520, 130, 6, 1, 100), (9000, 300, 30, 2, 64),
+                                                (256, 96, 2, 2, 300), (2048, 1100, 21, 1, 257), (16384, 200, 5, 2, 20)])
+def test_prefill_ranks_off_the_rank_grid(d_in, d_out, r_p, P, T):
+    """GEMM path with path ranks that the bit-budget rule never gives (not
+    multiples of 16, most not of 4): the run of 4 latent columns that crosses
+    r_p takes l = 0 past it, so the padding latents of t stay zero and add
+    nothing in stage 2; unsplit and split d_in (9000, 16384), every token-tile
+    size."""
+    inp = synth.layer_inputs(d_in + 7 * d_out + r_p, d_in, d_out, r_p, P)
+    x = synth.activations(T + 13 * d_in, T, d_in, "bf16")
+    _check(inp, x, "bf16", "prefill")
