@@ -340,3 +340,26 @@ def test_prefill_ranks_off_the_rank_grid(d_in, d_out, r_p, P, T):
     inp = synth.layer_inputs(d_in + 7 * d_out + r_p, d_in, d_out, r_p, P)
     x = synth.activations(T + 13 * d_in, T, d_in, "bf16")
     _check(inp, x, "bf16", "prefill")
+
+
+# ---- the largest d_in the kernels take ----
+
+_BIG_D_IN = (1 << 21) - 64          # the GEMM kernels take d_in below 2^21
+
+
+@pytest.fixture(scope="module")
+def big_d_in_layer():
+    return synth.layer_inputs(2 ** 21, _BIG_D_IN, 80, 16, 2)
+
+
+@pytest.mark.parametrize("path,T", [("decode", 1), ("decode", 3), ("valu", 1), ("prefill", 40)])
+def test_largest_d_in(big_d_in_layer, path, T):
+    """d_in just under the GEMM kernels' limit (2^21 - 64, 4 MB of V planes
+    per path at r_p = 16): the decode kernels sum about 512 stage-1 chunk
+    partials per latent, the GEMM kernels split d_in into their largest number
+    of pieces, and the 32-bit buffer offsets over x (168 MB at T = 40) and over
+    the planes stay in range; sampled tokens against the oracle."""
+    inp = big_d_in_layer
+    x = synth.activations(T + 5, T, _BIG_D_IN, "bf16")
+    tokens = None if T <= 3 else np.array([0, 17, T - 1])
+    _check(inp, x, "bf16", path, tokens=tokens)
