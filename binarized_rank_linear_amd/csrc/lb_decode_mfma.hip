@@ -638,7 +638,9 @@ __global__ __launch_bounds__(kThreads) void k_stage1(MRun run, MLin single) {
 
     // ---- partial latent sums: lane (gq, r16) holds latents row0+4*r16+m -------
     const int64_t Rtot = (int64_t)L.P * L.r_p;
-    const OutBuf ob = out_buf(L.part, LB_F32, (int64_t)L.nchunks * T * Rtot, 4);
+    // whole aligned groups of 4 latents only when r_p is a multiple of 4:
+    // otherwise the group crossing r_p would spill into the next path's latents
+    const OutBuf ob = out_buf(L.part, LB_F32, (int64_t)L.nchunks * T * Rtot, L.r_p);
 #pragma unroll
     for (int b = 0; b < NB1; ++b) {
 #pragma unroll

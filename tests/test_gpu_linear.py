@@ -363,3 +363,59 @@ def test_largest_d_in(big_d_in_layer, path, T):
     x = synth.activations(T + 5, T, _BIG_D_IN, "bf16")
     tokens = None if T <= 3 else np.array([0, 17, T - 1])
     _check(inp, x, "bf16", path, tokens=tokens)
+
+
+# ---- caller-chosen strides of the packed factors ----
+
+def _dev_layer_ld(inp, pad_v, pad_u):
+    """The layer packed with plane strides ld_v = packed_ld(r_p) + pad_v and
+    ld_u = packed_ld(d_out) + pad_u (multiples of 4 words, not of 32)."""
+    import torch
+    import binarized_rank_linear_amd as lb
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    U, V = t(inp.U), t(inp.V)
+    P, d_out, r_p = U.shape
+    d_in = V.shape[1]
+    ld_v, ld_u = lb.packed_ld(r_p) + pad_v, lb.packed_ld(d_out) + pad_u
+    v_bits = torch.empty((P, (d_in + 31) // 32, ld_v), dtype=torch.int32, device="cuda")
+    u_bits = torch.empty((P, (r_p + 31) // 32, ld_u), dtype=torch.int32, device="cuda")
+    for p in range(P):
+        lb.pack_signs(V[p], 0, ld_v, out=v_bits[p])
+        lb.pack_signs(U[p], 1, ld_u, out=u_bits[p])
+    h16 = lambda a: t(a.view(np.int16))
+    return lb.PackedLinear(d_in, d_out, P * r_p, P == 2, v_bits, u_bits, h16(inp.g), h16(inp.l), h16(inp.h),
+                           ld_v, ld_u)
+
+
+@pytest.mark.parametrize("path,T", [("decode", 1), ("decode", 4), ("decode", 24), ("valu", 2), ("valu", 24),
+                                    ("prefill", 40)])
+@pytest.mark.parametrize("d_in,d_out,r_p,P,pad_v,pad_u", [(1000, 700, 48, 2, 4, 12), (520, 130, 17, 2, 0, 4),
+                                                          (2048, 1100, 304, 2, 8, 0)])
+def test_packed_strides_not_aligned(d_in, d_out, r_p, P, pad_v, pad_u, path, T):
+    """Plane strides the caller picks (any multiple of 4 words at least the
+    packed length; the binding's default is a multiple of 32): every kernel
+    family addresses the planes through ld_v / ld_u."""
+    torch = torch_or_skip()
+    import binarized_rank_linear_amd as lb
+    inp = synth.layer_inputs(d_in + 3 * d_out + pad_v, d_in, d_out, r_p, P)
+    x = synth.activations(T + d_in, T, d_in, "bf16")
+    layer = _dev_layer_ld(inp, pad_v, pad_u)
+    say("strides", d_in, d_out, r_p, P, layer.ld_v, layer.ld_u, path, "T", T)
+    y = lb.linear_forward(x_to_dev(x), layer, torch.bfloat16, PATH_FLAG[path])
+    torch.cuda.synchronize()
+    ref = oracle.linear_forward(x, inp.U, inp.V, inp.h, inp.g, inp.l)
+    assert_close(y_to_np(y), ref, TOL["bf16"], ("strides", d_in, r_p, path, T))
+
+
+@pytest.mark.parametrize("d_in,d_out,r_p,P", [(33, 65, 17, 2), (520, 130, 17, 2), (1000, 300, 30, 1), (96, 40, 6, 2)])
+@pytest.mark.parametrize("T", [9, 17, 32])
+@pytest.mark.parametrize("path", DECODE_PATHS)
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_decode_kernels_odd_ranks_many_tokens(d_in, d_out, r_p, P, T, path, dt):
+    """Path ranks that are not multiples of 4 above 8 tokens, where the decode
+    kernels run stage 1 unfused: each latent's partial sum is stored on its
+    own, so the 4-latent group crossing r_p does not spill into the next
+    path's latents (as it did while the stores took whole groups of 4)."""
+    inp = synth.layer_inputs(d_in + 2 * d_out + r_p, d_in, d_out, r_p, P)
+    x = synth.activations(T + d_in + 1, T, d_in, dt)
+    _check(inp, x, dt, path)
