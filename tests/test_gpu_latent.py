@@ -27,6 +27,12 @@ def _bits(torch, y):
     ((2048, 1100, 304, 2), 64, "bf16", "bf16", "f32", "auto"),
     ((1000, 700, 48, 2), 40, "f32", "f32", "f32", "auto"),       # vector-ALU kernels (fp32 out, T > 32)
     ((520, 130, 16, 1), 5, "bf16", "bf16", "f32", "valu"),
+    # path ranks off the 16-multiple grid (not multiples of 4) on each kernel family
+    ((1000, 700, 17, 2), 1, "bf16", "bf16", "f32", "auto"),
+    ((1000, 700, 17, 2), 20, "bf16", "bf16", "f32", "decode"),
+    ((1000, 700, 17, 2), 40, "bf16", "bf16", "bf16", "auto"),
+    ((9000, 300, 30, 2), 64, "bf16", "bf16", "bf16", "auto"),
+    ((520, 130, 6, 1), 5, "f32", "f32", "f32", "valu"),
 ])
 def test_stages_compose_to_the_layer(shape, T, xdt, ydt, tdt, path):
     """stage 2 of stage 1's latents gives lb_linear_forward's bits when t

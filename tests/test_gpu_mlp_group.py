@@ -236,20 +236,31 @@ RAGGED = {
               (1024, 333, 64, 2), (4096, 257, 304, 2), (1024, 512, 1696, 2), (640, 384, 2000, 1)],
     "wide": [(1000, 700, 304, 2), (520, 130, 208, 1), (2048, 1536, 416, 2), (600, 1100, 1456, 1),
              (1024, 333, 1040, 2)],
+    # path ranks off the 16-multiple grid (none a multiple of 4): "odd" mixed
+    # sizes, "odd_wide" every rank at least 4 latent tiles (the tile split)
+    "odd": [(1000, 700, 17, 2), (520, 130, 6, 1), (2048, 1536, 150, 2), (96, 1100, 5, 2), (1024, 333, 1001, 2)],
+    "odd_wide": [(1000, 700, 301, 2), (520, 130, 257, 1), (600, 1100, 1457, 1)],
 }
 
 
 @pytest.mark.parametrize("T,out,kind", [(1, "bf16", "mixed"), (2, "bf16", "mixed"), (5, "bf16", "mixed"),
                                         (8, "bf16", "mixed"), (1, "f32", "mixed"), (3, "f32", "mixed"),
                                         (1, "bf16", "wide"), (2, "bf16", "wide"), (6, "bf16", "wide"),
-                                        (1, "f32", "wide"), (4, "f32", "wide")])
+                                        (1, "f32", "wide"), (4, "f32", "wide"),
+                                        (1, "bf16", "odd"), (2, "bf16", "odd"), (5, "bf16", "odd"),
+                                        (1, "f32", "odd"), (3, "f32", "odd"), (12, "bf16", "odd"),
+                                        (40, "bf16", "odd"), (1, "bf16", "odd_wide"), (2, "bf16", "odd_wide"),
+                                        (6, "bf16", "odd_wide"), (1, "f32", "odd_wide"), (4, "f32", "odd_wide"),
+                                        (24, "bf16", "odd_wide")])
 def test_pass_ragged_mixed_group(T, out, kind):
     """A decode group of ragged linears, with and without the residual path
     (d_in, d_out and r_p off every tile size), runs as one launch per pass
     (bf16 T <= 2, fp32 T = 1; three launches beyond): every run equals the
     staged run bit for bit, and the oracle within the tolerance.  In the mixed
     set the last two ranks span two stage-1 latent groups per path at T = 1
-    (more than 24 tiles of 64 latents), the second one ragged."""
+    (more than 24 tiles of 64 latents), the second one ragged.  The odd sets
+    take ranks that are not multiples of 4, also at 12 to 40 tokens (GEMM
+    kernels)."""
     torch = torch_or_skip()
     import binarized_rank_linear_amd as lb
     say("pass ragged group T", T, out, kind)
