@@ -57,6 +57,21 @@ def test_decoder_layer_ragged_gqa(T):
     assert_close(y_to_np(y), ref, TOL["bf16"], ("layer ragged", T))
 
 
+@pytest.mark.parametrize("T", [1, 2, 5, 12, 32])
+def test_decoder_layer_odd_ranks(T):
+    """Path ranks that are not multiples of 4 (17, 6, 30 and 21 for q/o, k/v,
+    gate/up and down) through every step of the layer, with the fused (T <= 8)
+    and separate stage-1 forms."""
+    torch = torch_or_skip()
+    dev, host = _layer(5, 520, 1100, 130, (17, 6, 30, 21))
+    x = synth.activations(60 + T, T, 520, "bf16")
+    say("decoder layer odd ranks T", T)
+    y = _decoder(dev, 8, 2, 1e-6).forward(x_to_dev(x))
+    torch.cuda.synchronize()
+    ref = oracle.decoder_layer_forward(x, host, 8, 2, 1e-6)
+    assert_close(y_to_np(y), ref, TOL["bf16"], ("layer odd ranks", T))
+
+
 @pytest.mark.parametrize("T", [1, 4])
 def test_decoder_layer_llama2_7b_shape(T):
     """A Llama2-7B-shaped layer (4096, 11008, 32 heads, no kv grouping) at

@@ -57,7 +57,8 @@ def _close_f16(got_bits, want_bits, what):
 
 
 @pytest.mark.parametrize("d_out,d_in,r,residual", [(96, 64, 32, True), (64, 96, 48, True), (256, 256, 128, False),
-                                                   (1024, 1024, 512, False), (384, 1024, 208, True)])
+                                                   (1024, 1024, 512, False), (384, 1024, 208, True),
+                                                   (96, 64, 34, True), (130, 70, 13, False)])
 def test_dual_svid_against_oracle(d_out, d_in, r, residual):
     torch = torch_or_skip()
     import binarized_rank_linear_amd as lb
