@@ -209,19 +209,27 @@ size_t lb_linear_workspace_bytes(int64_t d_in, int64_t d_out, int64_t r, int64_t
                                  int residual, unsigned flags) {
     Linear a{};
     if (check_shape(d_in, d_out, r, T, residual, &a)) return 0;
-    a.x_dtype = a.y_dtype = LB_BF16;
     if (flags & ~kLinearFlags) return 0;
+    a.ld_v = lb_packed_ld_aligned(a.r_p);
+    a.ld_u = lb_packed_ld_aligned(d_out);
     size_t need = 0;
-    // AUTO may pick either path for T > 32 depending on the output dtype, and
-    // the vector-ALU kernels for strides the decode kernels do not address.
-    const int ys[2] = {LB_BF16, LB_F32};
-    for (int yi = 0; yi < 2; ++yi) {
-        Path p;
-        if (choose_path(flags, T, ys[yi], &p)) continue;
-        size_t b = path_workspace(p, a);
-        if (p == Path::MfmaDecode) b = std::max(b, path_workspace(Path::Valu, a));
-        if (b > need) need = b;
-    }
+    // Every path a call of this shape can take, for either activation and
+    // output dtype: AUTO picks by the output dtype, and by the shape and the
+    // pointers when the GEMM kernels do not take them (so both the choice
+    // without the linear and the one with its shape count), and the
+    // vector-ALU kernels serve strides the decode kernels do not address.
+    for (int xd : {LB_BF16, LB_F32})
+        for (int yd : {LB_BF16, LB_F32}) {
+            a.x_dtype = xd;
+            a.y_dtype = yd;
+            for (int with_shape = 0; with_shape < 2; ++with_shape) {
+                Path p;
+                if (choose_path(flags, T, yd, &p, with_shape ? &a : nullptr)) continue;
+                size_t b = path_workspace(p, a);
+                if (p == Path::MfmaDecode) b = std::max(b, path_workspace(Path::Valu, a));
+                if (b > need) need = b;
+            }
+        }
     return rup256(need);
 }
 
@@ -369,10 +377,14 @@ int lb_mlp_forward(const void *x, int x_dtype, void *y, int y_dtype, const lb_fa
     if ((rc = check_factors(gate, &ag)) || (rc = check_factors(up, &au)) ||
         (rc = check_factors(down, &ad)))
         return rc;
-    if ((rc = check_io(x, x_dtype, y, y_dtype, &ad))) return rc;
-    if (overlap(x, (size_t)(T * d_model) * act_size(x_dtype), y,
-                (size_t)(T * d_model) * act_size(y_dtype)))
-        return LB_EINVAL;
+    // x and y are the block's [T][d_model] (down's own input is the SwiGLU,
+    // in the workspace)
+    Linear io{};
+    io.T = T;
+    io.d_in = io.d_out = d_model;
+    if ((rc = check_io(x, x_dtype, y, y_dtype, &io))) return rc;
+    ad.y = y;
+    ad.y_dtype = y_dtype;
     Path p;
     if (flags & ~kLinearFlags) return LB_EINVAL;
     if ((rc = choose_path(flags, T, y_dtype, &p, &ad))) return rc;

@@ -141,6 +141,45 @@ def test_mlp_and_group_argument_errors():
     assert L.lb_grouped_release(FAKE) == lb.LB_EINVAL                     # never prepared
 
 
+def test_workspace_query_covers_every_path_a_call_can_take():
+    """lb_linear_workspace_bytes (flags AUTO) is at least what each path the
+    call may end on needs: AUTO sends bf16 outputs of 9-32 tokens to the GEMM
+    kernels, but a d_in they do not take (not a multiple of 8) goes to the
+    decode kernels, whose workspace is larger here; the query once sized only
+    the GEMM form, and the call then refused its own query's workspace."""
+    import torch
+    L = lb.lib()
+    bf, f32 = torch.bfloat16, torch.float32
+    for d_in, d_out, r, T, res in [(25, 1662, 692, 19, 1), (1001, 600, 96, 24, 0), (4095, 190, 4, 55, 1),
+                                   (1024, 1024, 512, 16, 0), (7, 3000, 40, 32, 1)]:
+        auto = L.lb_linear_workspace_bytes(d_in, d_out, r, T, res, 0)
+        for flags in (lb.LB_PATH_DECODE, lb.LB_PATH_DECODE_VALU, lb.LB_PATH_PREFILL):
+            forced = L.lb_linear_workspace_bytes(d_in, d_out, r, T, res, flags)
+            if flags == lb.LB_PATH_PREFILL and d_in % 8:
+                continue            # forced GEMM requests of such shapes run the vector-ALU kernels
+            if lb.linear_path(d_in, d_out, r, T, bool(res), bf, bf) == flags or \
+                    lb.linear_path(d_in, d_out, r, T, bool(res), f32, f32) == flags:
+                assert auto >= forced, (d_in, d_out, r, T, res, flags, auto, forced)
+
+
+def test_mlp_checks_x_and_y_at_the_block_width():
+    """The block's x and y are [T][d_model]: a y placed right after x is not
+    an overlap, even when d_ff > d_model (the check once sized x as down's
+    input, [T][d_ff], and refused such a y as overlapping)."""
+    L = lb.lib()
+    T, d_model, d_ff = 115, 641, 2045
+    f = _factors(ld_v=68, ld_u=2048)
+    fd = _factors(ld_v=12, ld_u=644)
+    x = FAKE + 0x5000000
+    for y in (x + T * d_model * 4, x + T * d_model * 4 + 4096):
+        rc = L.lb_mlp_forward(x, lb.LB_F32, y, lb.LB_F32, ctypes.byref(f), ctypes.byref(f), ctypes.byref(fd),
+                              d_model, d_ff, 68, 10, T, 1, None, 0, 0, None)
+        assert rc == lb.LB_EWORKSPACE, rc
+    rc = L.lb_mlp_forward(x, lb.LB_F32, x + T * d_model * 4 - 4, lb.LB_F32, ctypes.byref(f), ctypes.byref(f),
+                          ctypes.byref(fd), d_model, d_ff, 68, 10, T, 1, None, 0, 0, None)
+    assert rc == lb.LB_EINVAL                                            # a real overlap
+
+
 def test_linear_path_choice():
     """Which kernel family a request takes (host only): the decode kernels up
     to 8 tokens, the bf16 GEMM kernels above for bf16 outputs, the decode
