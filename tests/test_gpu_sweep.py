@@ -1,0 +1,238 @@
+"""Seeded sweep of the forward against the fp64 oracle over shapes, ranks,
+token counts, activation and output dtypes, scale signs and kernel paths.
+
+The fixed cases elsewhere pin each kernel family at chosen sizes; this file
+draws many more combinations from one seed, so that an edge the fixed cases
+miss (a rank off a tile grid, a d_in off the vector width, a token count
+between two tile sizes) meets the oracle too.  Scales g, h and l are drawn
+with both signs in a third of the cases: the method's scales are magnitudes,
+but the layer's formula (sesamedisk page, "What the method actually
+computes", Proposition 1) and the boundary accept any fp16 value.
+
+Tolerances are the parity bounds of the other GPU tests: relative L2 1e-3
+(fp32 outputs) or 8e-3 (bf16 outputs), and every element within 8 x bound x
+rms(reference).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import TOL, assert_close, dev_layer, say, torch_or_skip, x_to_dev, y_to_np
+
+pytestmark = pytest.mark.gpu
+
+PATH_FLAG = {"auto": 0, "decode": 1, "prefill": 2, "valu": 3}
+MAX_WORK = 1.2e8          # oracle multiply-adds per case, so the CPU side stays fast
+
+
+def _dim(rng):
+    kind = rng.integers(4)
+    if kind == 0:
+        return int(rng.integers(1, 64))
+    if kind == 1:
+        return int(rng.integers(64, 700))
+    if kind == 2:
+        return int(rng.integers(700, 2600))
+    return int(rng.choice([128, 256, 512, 1024, 2048, 4096]) + rng.integers(-3, 4))
+
+
+def _single_cases(seed=20261204, n=160):
+    rng = np.random.default_rng(seed)
+    paths = ["auto", "decode", "valu", "prefill"]
+    cases = []
+    while len(cases) < n:
+        path = paths[len(cases) % 4]
+        d_in, d_out = max(1, _dim(rng)), max(1, _dim(rng))
+        P = int(rng.integers(1, 3))
+        r_p = int(rng.choice([rng.integers(1, 40), rng.integers(40, 400)]))
+        if path == "decode":
+            T = int(rng.integers(1, 33))
+        elif path == "valu":
+            T = int(rng.integers(1, 41))
+        else:
+            T = int(rng.choice([rng.integers(1, 40), rng.integers(40, 300)]))
+        x_dt = str(rng.choice(["f32", "bf16"]))
+        y_dt = "bf16" if path == "prefill" else str(rng.choice(["f32", "bf16"]))
+        signed = bool(rng.integers(3) == 0)
+        if T * P * r_p * (d_in + d_out) > MAX_WORK:
+            continue
+        cases.append((len(cases), path, d_in, d_out, r_p, P, T, x_dt, y_dt, signed))
+    return cases
+
+
+SINGLE = _single_cases()
+
+
+def _inputs(i, d_in, d_out, r_p, P, signed):
+    lo = -1.5 if signed else 0.5
+    inp = synth.layer_inputs(7000 + i, d_in, d_out, r_p, P, scale_lo=lo, scale_hi=1.5)
+    return inp
+
+
+@pytest.mark.parametrize("case", SINGLE, ids=lambda c: "%d-%s-%dx%d-r%dx%d-T%d-%s-%s%s" % (
+    c[0], c[1], c[2], c[3], c[5], c[4], c[6], c[7], c[8], "-signed" if c[9] else ""))
+def test_single_linear_sweep(case):
+    torch = torch_or_skip()
+    import binarized_rank_linear_amd as lb
+    i, path, d_in, d_out, r_p, P, T, x_dt, y_dt, signed = case
+    inp = _inputs(i, d_in, d_out, r_p, P, signed)
+    x = synth.activations(8000 + i, T, d_in, x_dt)
+    layer = dev_layer(inp)
+    xd = x_to_dev(x)
+    od = torch.float32 if y_dt == "f32" else torch.bfloat16
+    say("sweep", case)
+    y = lb.linear_forward(xd, layer, od, PATH_FLAG[path])
+    torch.cuda.synchronize()
+    ref = oracle.linear_forward(x, inp.U, inp.V, inp.h, inp.g, inp.l)
+    assert_close(y_to_np(y), ref, TOL[y_dt], case)
+    assert lb.device_faults() == 0
+
+
+def _group_cases(seed=20261205, n=24):
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        k = len(cases)
+        T = int(rng.choice([1, 2, int(rng.integers(3, 9)), int(rng.integers(9, 33)),
+                            int(rng.integers(33, 200))]))
+        y_dt = "bf16" if k % 2 == 0 else str(rng.choice(["f32", "bf16"]))
+        P = int(rng.integers(1, 3))
+        d_x = _dim(rng)                              # one shared input width, as in a layer
+        lins = []
+        for j in range(int(rng.integers(2, 7))):
+            d_in = d_x if rng.integers(2) else max(1, _dim(rng))
+            d_out = max(1, _dim(rng))
+            r_p = int(rng.choice([rng.integers(1, 40), rng.integers(40, 300)]))
+            lins.append((d_in, d_out, r_p))
+        if sum(T * P * r * (a + b) for a, b, r in lins) > 3 * MAX_WORK:
+            continue
+        cases.append((k, T, y_dt, P, tuple(lins), bool(rng.integers(3) == 0)))
+    return cases
+
+
+GROUPS = _group_cases()
+
+
+@pytest.mark.parametrize("case", GROUPS, ids=lambda c: "%d-T%d-%s-P%d-n%d%s" % (
+    c[0], c[1], c[2], c[3], len(c[4]), "-signed" if c[5] else ""))
+def test_group_sweep(case):
+    """The same linears through the stateless grouped call and as a prepared
+    group (run twice): each output within the bound of the oracle, and the
+    two forms bit for bit equal."""
+    torch = torch_or_skip()
+    import binarized_rank_linear_amd as lb
+    k, T, y_dt, P, lins, signed = case
+    od = torch.float32 if y_dt == "f32" else torch.bfloat16
+    say("group sweep", case)
+    items, refs = [], []
+    xs = {}
+    for j, (d_in, d_out, r_p) in enumerate(lins):
+        inp = _inputs(100 * k + j, d_in, d_out, r_p, P, signed)
+        if d_in not in xs:
+            x = synth.activations(9000 + 10 * k + len(xs), T, d_in, "bf16")
+            xs[d_in] = (x, x_to_dev(x))
+        x, xd = xs[d_in]
+        items.append((xd, torch.empty((T, d_out), dtype=od, device="cuda"), dev_layer(inp)))
+        refs.append(oracle.linear_forward(x, inp.U, inp.V, inp.h, inp.g, inp.l))
+    lb.linear_forward_grouped(items)
+    torch.cuda.synchronize()
+    for j, it in enumerate(items):
+        assert_close(y_to_np(it[1]), refs[j], TOL[y_dt], (case, j))
+    grp = lb.Group([(x, torch.empty_like(y), l) for x, y, l in items], T, torch.bfloat16, od)
+    for rep in range(2):
+        grp.run()
+        torch.cuda.synchronize()
+        for j, it in enumerate(items):
+            a, b = it[1], grp.items[j][1]
+            bits = (lambda t: t.view(torch.int16)) if od == torch.bfloat16 else (lambda t: t.view(torch.int32))
+            assert torch.equal(bits(a), bits(b)), (case, rep, j)
+    grp.release()
+    assert lb.device_faults() == 0
+
+
+def _latent_cases(seed=20261206, n=24):
+    rng = np.random.default_rng(seed)
+    paths = ["auto", "decode", "valu", "prefill"]
+    cases = []
+    while len(cases) < n:
+        path = paths[len(cases) % 4]
+        d_in, d_out = max(1, _dim(rng)), max(1, _dim(rng))
+        P = int(rng.integers(1, 3))
+        r_p = int(rng.choice([rng.integers(1, 40), rng.integers(40, 300)]))
+        T = int(rng.integers(1, 33)) if path in ("decode", "valu") else int(rng.integers(1, 200))
+        if T * P * r_p * (d_in + d_out) > MAX_WORK:
+            continue
+        cases.append((len(cases), path, d_in, d_out, r_p, P, T))
+    return cases
+
+
+LATENT = _latent_cases()
+
+
+@pytest.mark.parametrize("case", LATENT, ids=lambda c: "%d-%s-%dx%d-r%dx%d-T%d" % (
+    c[0], c[1], c[2], c[3], c[5], c[4], c[6]))
+def test_latent_sweep(case):
+    """lb_linear_stage1 then lb_linear_stage2 equals lb_linear_forward bit for
+    bit (bf16 outputs) when t holds the kernels' own latent precision (bf16 on
+    the GEMM kernels, fp32 on the decode and vector-ALU kernels: the path the
+    library reports for the call), and the latents are within the bf16 bound
+    of the oracle's
+    t = l * sign(V)^T (g * x)."""
+    torch = torch_or_skip()
+    import binarized_rank_linear_amd as lb
+    i, path, d_in, d_out, r_p, P, T = case
+    inp = _inputs(500 + i, d_in, d_out, r_p, P, i % 3 == 0)
+    x = synth.activations(600 + i, T, d_in, "bf16")
+    layer = dev_layer(inp)
+    xd = x_to_dev(x)
+    say("latent sweep", case)
+    fl = PATH_FLAG[path]
+    gemm = lb.linear_path(d_in, d_out, P * r_p, T, P == 2, torch.bfloat16, torch.bfloat16, fl) == lb.LB_PATH_PREFILL
+    tt = torch.bfloat16 if gemm else torch.float32
+    y = lb.linear_forward(xd, layer, torch.bfloat16, fl)
+    t = lb.linear_stage1(xd, layer, tt, torch.bfloat16, fl)
+    y2 = lb.linear_stage2(t, layer, torch.bfloat16, fl)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), case
+    tref = oracle.linear_latents(x, inp.V, inp.g, inp.l)
+    assert_close(y_to_np(t), tref, TOL["bf16"], case)
+    assert lb.device_faults() == 0
+
+
+def _mlp_cases(seed=20261207, n=12):
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        d_model, d_ff = max(1, _dim(rng)), max(1, _dim(rng))
+        P = int(rng.integers(1, 3))
+        r_gu, r_dn = (int(rng.choice([rng.integers(1, 40), rng.integers(40, 300)])) for _ in range(2))
+        T = int(rng.choice([1, 2, int(rng.integers(3, 9)), int(rng.integers(9, 33)), int(rng.integers(33, 120))]))
+        x_dt = str(rng.choice(["f32", "bf16"]))
+        y_dt = "bf16" if len(cases) % 3 else "f32"
+        if T * P * (2 * r_gu * (d_model + d_ff) + r_dn * (d_ff + d_model)) > 2 * MAX_WORK:
+            continue
+        cases.append((len(cases), d_model, d_ff, r_gu, r_dn, P, T, x_dt, y_dt))
+    return cases
+
+
+MLP = _mlp_cases()
+
+
+@pytest.mark.parametrize("case", MLP, ids=lambda c: "%d-%dx%d-r%d-%d-P%d-T%d-%s-%s" % c)
+def test_mlp_sweep(case):
+    """The SwiGLU block down(silu(gate(x)) * up(x)) against the oracle's fp64
+    composition (no intermediate rounding), within the output dtype's bound."""
+    torch = torch_or_skip()
+    import binarized_rank_linear_amd as lb
+    i, d_model, d_ff, r_gu, r_dn, P, T, x_dt, y_dt = case
+    g = _inputs(300 + 3 * i, d_model, d_ff, r_gu, P, False)
+    u = _inputs(301 + 3 * i, d_model, d_ff, r_gu, P, i % 2 == 1)
+    d = _inputs(302 + 3 * i, d_ff, d_model, r_dn, P, False)
+    x = synth.activations(400 + i, T, d_model, x_dt)
+    od = torch.float32 if y_dt == "f32" else torch.bfloat16
+    say("mlp sweep", case)
+    y = lb.mlp_forward(x_to_dev(x), dev_layer(g), dev_layer(u), dev_layer(d), od)
+    torch.cuda.synchronize()
+    assert_close(y_to_np(y), oracle.mlp_forward(x, g, u, d), TOL[y_dt], case)
+    assert lb.device_faults() == 0
