@@ -42,6 +42,26 @@ def dev_layer(inp):
     return lb.PackedLinear.from_factors(t(inp.U), t(inp.V), h16(inp.h), h16(inp.g), h16(inp.l))
 
 
+def dev_layer_ld(inp, pad_v, pad_u):
+    """The layer packed with plane strides ld_v = packed_ld(r_p) + pad_v and
+    ld_u = packed_ld(d_out) + pad_u (multiples of 4 words, not of 32)."""
+    import torch
+    import binarized_rank_linear_amd as lb
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    U, V = t(inp.U), t(inp.V)
+    P, d_out, r_p = U.shape
+    d_in = V.shape[1]
+    ld_v, ld_u = lb.packed_ld(r_p) + pad_v, lb.packed_ld(d_out) + pad_u
+    v_bits = torch.empty((P, (d_in + 31) // 32, ld_v), dtype=torch.int32, device="cuda")
+    u_bits = torch.empty((P, (r_p + 31) // 32, ld_u), dtype=torch.int32, device="cuda")
+    for p in range(P):
+        lb.pack_signs(V[p], 0, ld_v, out=v_bits[p])
+        lb.pack_signs(U[p], 1, ld_u, out=u_bits[p])
+    h16 = lambda a: t(a.view(np.int16))
+    return lb.PackedLinear(d_in, d_out, P * r_p, P == 2, v_bits, u_bits, h16(inp.g), h16(inp.l), h16(inp.h),
+                           ld_v, ld_u)
+
+
 def host_layer_from_dev(U, V, h, g, l):
     """Copy GPU-generated float factors back for the oracle."""
     d = lambda a: a.detach().cpu().numpy()

@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import TOL, assert_close, dev_layer, say, torch_or_skip, x_to_dev, y_to_np
+from gpu_util import TOL, assert_close, dev_layer, dev_layer_ld, say, torch_or_skip, x_to_dev, y_to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -367,26 +367,6 @@ def test_largest_d_in(big_d_in_layer, path, T):
 
 # ---- caller-chosen strides of the packed factors ----
 
-def _dev_layer_ld(inp, pad_v, pad_u):
-    """The layer packed with plane strides ld_v = packed_ld(r_p) + pad_v and
-    ld_u = packed_ld(d_out) + pad_u (multiples of 4 words, not of 32)."""
-    import torch
-    import binarized_rank_linear_amd as lb
-    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
-    U, V = t(inp.U), t(inp.V)
-    P, d_out, r_p = U.shape
-    d_in = V.shape[1]
-    ld_v, ld_u = lb.packed_ld(r_p) + pad_v, lb.packed_ld(d_out) + pad_u
-    v_bits = torch.empty((P, (d_in + 31) // 32, ld_v), dtype=torch.int32, device="cuda")
-    u_bits = torch.empty((P, (r_p + 31) // 32, ld_u), dtype=torch.int32, device="cuda")
-    for p in range(P):
-        lb.pack_signs(V[p], 0, ld_v, out=v_bits[p])
-        lb.pack_signs(U[p], 1, ld_u, out=u_bits[p])
-    h16 = lambda a: t(a.view(np.int16))
-    return lb.PackedLinear(d_in, d_out, P * r_p, P == 2, v_bits, u_bits, h16(inp.g), h16(inp.l), h16(inp.h),
-                           ld_v, ld_u)
-
-
 @pytest.mark.parametrize("path,T", [("decode", 1), ("decode", 4), ("decode", 24), ("valu", 2), ("valu", 24),
                                     ("prefill", 40)])
 @pytest.mark.parametrize("d_in,d_out,r_p,P,pad_v,pad_u", [(1000, 700, 48, 2, 4, 12), (520, 130, 17, 2, 0, 4),
@@ -399,7 +379,7 @@ def test_packed_strides_not_aligned(d_in, d_out, r_p, P, pad_v, pad_u, path, T):
     import binarized_rank_linear_amd as lb
     inp = synth.layer_inputs(d_in + 3 * d_out + pad_v, d_in, d_out, r_p, P)
     x = synth.activations(T + d_in, T, d_in, "bf16")
-    layer = _dev_layer_ld(inp, pad_v, pad_u)
+    layer = dev_layer_ld(inp, pad_v, pad_u)
     say("strides", d_in, d_out, r_p, P, layer.ld_v, layer.ld_u, path, "T", T)
     y = lb.linear_forward(x_to_dev(x), layer, torch.bfloat16, PATH_FLAG[path])
     torch.cuda.synchronize()

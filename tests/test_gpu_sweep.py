@@ -18,7 +18,8 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import TOL, assert_close, dev_layer, say, torch_or_skip, x_to_dev, y_to_np
+from gpu_util import (TOL, assert_close, dev_layer, dev_layer_ld, host_layer_from_dev, say, torch_or_skip,
+                      x_to_dev, y_to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -235,4 +236,147 @@ def test_mlp_sweep(case):
     y = lb.mlp_forward(x_to_dev(x), dev_layer(g), dev_layer(u), dev_layer(d), od)
     torch.cuda.synchronize()
     assert_close(y_to_np(y), oracle.mlp_forward(x, g, u, d), TOL[y_dt], case)
+    assert lb.device_faults() == 0
+
+
+def _strided_cases(seed=20261208, n=32):
+    rng = np.random.default_rng(seed)
+    paths = ["auto", "decode", "valu", "prefill"]
+    cases = []
+    while len(cases) < n:
+        path = paths[len(cases) % 4]
+        d_in, d_out = max(1, _dim(rng)), max(1, _dim(rng))
+        P = int(rng.integers(1, 3))
+        r_p = int(rng.choice([rng.integers(1, 40), rng.integers(40, 300)]))
+        T = int(rng.integers(1, 33)) if path in ("decode", "valu") else int(rng.integers(1, 200))
+        pad_v, pad_u = (4 * int(rng.integers(0, 16)) for _ in range(2))
+        if T * P * r_p * (d_in + d_out) > MAX_WORK:
+            continue
+        cases.append((len(cases), path, d_in, d_out, r_p, P, T, pad_v, pad_u))
+    return cases
+
+
+STRIDED = _strided_cases()
+
+
+@pytest.mark.parametrize("case", STRIDED, ids=lambda c: "%d-%s-%dx%d-r%dx%d-T%d-pad%d-%d" % (
+    c[0], c[1], c[2], c[3], c[5], c[4], c[6], c[7], c[8]))
+def test_strided_sweep(case):
+    """Plane strides the caller picks (the packed length plus any multiple of
+    4 words) on every kernel family, bf16 in and out."""
+    torch = torch_or_skip()
+    import binarized_rank_linear_amd as lb
+    i, path, d_in, d_out, r_p, P, T, pad_v, pad_u = case
+    inp = _inputs(1100 + i, d_in, d_out, r_p, P, i % 3 == 1)
+    x = synth.activations(1200 + i, T, d_in, "bf16")
+    layer = dev_layer_ld(inp, pad_v, pad_u)
+    say("strided sweep", case)
+    y = lb.linear_forward(x_to_dev(x), layer, torch.bfloat16, PATH_FLAG[path])
+    torch.cuda.synchronize()
+    assert_close(y_to_np(y), oracle.linear_forward(x, inp.U, inp.V, inp.h, inp.g, inp.l), TOL["bf16"], case)
+    assert lb.device_faults() == 0
+
+
+def _layer_cases(seed=20261209, n=16):
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        n_kv = int(rng.choice([1, 2, 4]))
+        grp = int(rng.choice([1, 2, 3, 4]))
+        n_heads = n_kv * grp
+        dh = int(rng.choice([int(rng.integers(1, 40)), int(rng.integers(40, 140))]))
+        d_model = n_heads * dh
+        d_ff = max(1, _dim(rng))
+        P = int(rng.integers(1, 3))
+        rps = tuple(int(rng.choice([rng.integers(1, 24), rng.integers(24, 160)])) for _ in range(4))
+        T = int(rng.choice([1, 2, int(rng.integers(3, 9)), int(rng.integers(9, 33))]))
+        eps = float(rng.choice([0.0, 1e-6, 1e-5]))
+        if d_model < 2:
+            continue
+        work = T * P * (2 * rps[0] * 2 * d_model + 2 * rps[1] * (d_model + n_kv * dh) +
+                        2 * rps[2] * (d_model + d_ff) + rps[3] * (d_ff + d_model))
+        if work > 2 * MAX_WORK:
+            continue
+        cases.append((len(cases), d_model, d_ff, n_heads, n_kv, rps, P, T, eps))
+    return cases
+
+
+LAYERS = _layer_cases()
+NAMES = ("q", "k", "v", "o", "gate", "up", "down")
+
+
+@pytest.mark.parametrize("case", LAYERS, ids=lambda c: "%d-d%d-ff%d-h%d:%d-r%s-P%d-T%d-eps%g" % (
+    c[0], c[1], c[2], c[3], c[4], "/".join(map(str, c[5])), c[6], c[7], c[8]))
+def test_decoder_layer_sweep(case):
+    """One decoder layer at decode time (RMSNorm, q/k/v, one-token attention
+    with grouped kv heads, o with the residual, RMSNorm, SwiGLU with the
+    residual) against the oracle's composition with the same bf16 hand-offs."""
+    torch = torch_or_skip()
+    import binarized_rank_linear_amd as lb
+    i, d, ff, n_heads, n_kv, rps, P, T, eps = case
+    dkv = d // n_heads * n_kv
+    shapes = dict(q=(d, d, rps[0]), k=(d, dkv, rps[1]), v=(d, dkv, rps[1]), o=(d, d, rps[0]),
+                  gate=(d, ff, rps[2]), up=(d, ff, rps[2]), down=(ff, d, rps[3]))
+    dev, host = {}, {}
+    for j, name in enumerate(NAMES):
+        di, do, rp = shapes[name]
+        U, V, h, g, l = synth.device_layer(synth.layer_seed(1300 + i, j), di, do, rp, P)
+        l = (l.float() * synth.unit_gain_l(di, rp, P)).half()
+        host[name] = host_layer_from_dev(U, V, h, g, l)
+        dev[name] = lb.PackedLinear.from_factors(U, V, h, g, l)
+    x = synth.activations(1400 + i, T, d, "bf16")
+    say("decoder layer sweep", case)
+    layer = lb.DecoderLayer(*(dev[n] for n in NAMES), n_heads=n_heads, n_kv_heads=n_kv, eps=eps)
+    y = layer.forward(x_to_dev(x))
+    torch.cuda.synchronize()
+    assert_close(y_to_np(y), oracle.decoder_layer_forward(x, host, n_heads, n_kv, eps), TOL["bf16"], case)
+    assert lb.device_faults() == 0
+
+
+def _mixed_cases(seed=20261210, n=10):
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        calls = []
+        for j in range(int(rng.integers(2, 8))):
+            T = int(rng.choice([0, 1, 2, int(rng.integers(3, 9)), int(rng.integers(9, 33)),
+                                int(rng.integers(33, 120))]))
+            x_dt = str(rng.choice(["f32", "bf16"]))
+            y_dt = str(rng.choice(["f32", "bf16"]))
+            d_in, d_out = max(1, _dim(rng)), max(1, _dim(rng))
+            r_p = int(rng.choice([rng.integers(1, 40), rng.integers(40, 200)]))
+            P = int(rng.integers(1, 3))
+            calls.append((T, x_dt, y_dt, d_in, d_out, r_p, P))
+        if sum(c[0] * c[6] * c[5] * (c[3] + c[4]) for c in calls) > 3 * MAX_WORK:
+            continue
+        cases.append((len(cases), tuple(calls)))
+    return cases
+
+
+MIXED = _mixed_cases()
+
+
+@pytest.mark.parametrize("case", MIXED, ids=lambda c: "%d-n%d" % (c[0], len(c[1])))
+def test_mixed_grouped_call_sweep(case):
+    """One stateless grouped call holding linears of different token counts
+    (empty ones too), activation and output dtypes and shapes: it splits them
+    into sub-groups, and every output is within its dtype's bound of the
+    oracle; an empty call's output is left as it was."""
+    torch = torch_or_skip()
+    import binarized_rank_linear_amd as lb
+    k, calls = case
+    say("mixed grouped sweep", case)
+    items, refs = [], []
+    for j, (T, x_dt, y_dt, d_in, d_out, r_p, P) in enumerate(calls):
+        inp = _inputs(1500 + 10 * k + j, d_in, d_out, r_p, P, j % 2 == 1)
+        x = synth.activations(1600 + 10 * k + j, T, d_in, x_dt)
+        od = torch.float32 if y_dt == "f32" else torch.bfloat16
+        y = torch.full((T, d_out), 7.0, dtype=od, device="cuda")
+        items.append((x_to_dev(x), y, dev_layer(inp)))
+        refs.append(oracle.linear_forward(x, inp.U, inp.V, inp.h, inp.g, inp.l) if T else None)
+    lb.linear_forward_grouped(items)
+    torch.cuda.synchronize()
+    for j, (T, x_dt, y_dt, *_ ) in enumerate(calls):
+        if T:
+            assert_close(y_to_np(items[j][1]), refs[j], TOL[y_dt], (case, j))
     assert lb.device_faults() == 0
