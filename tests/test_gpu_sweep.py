@@ -380,3 +380,81 @@ def test_mixed_grouped_call_sweep(case):
         if T:
             assert_close(y_to_np(items[j][1]), refs[j], TOL[y_dt], (case, j))
     assert lb.device_faults() == 0
+
+
+def _pack_cases(seed=20261211, n=24):
+    rng = np.random.default_rng(seed)
+    return [(k, max(1, _dim(rng)), max(1, _dim(rng)), int(rng.integers(2)), 4 * int(rng.integers(0, 12)))
+            for k in range(n)]
+
+
+PACKS = _pack_cases()
+
+
+@pytest.mark.parametrize("case", PACKS, ids=lambda c: "%d-%dx%d-axis%d-pad%d" % c)
+def test_pack_sweep(case):
+    """Sign packing bit for bit against the oracle's packer, with zeros of
+    both signs, NaN, infinities and a negative subnormal among the values."""
+    torch = torch_or_skip()
+    import binarized_rank_linear_amd as lb
+    k, rows, cols, axis, pad = case
+    rng = np.random.default_rng(1700 + k)
+    M = rng.standard_normal((rows, cols)).astype(np.float32)
+    flat = M.reshape(-1)
+    for step, v in ((13, 0.0), (17, -0.0), (19, np.nan), (23, -np.inf), (29, np.inf), (31, -1e-40)):
+        flat[int(rng.integers(step))::step] = v
+    ld = lb.packed_ld(cols if axis == 0 else rows) + pad
+    say("pack sweep", case)
+    got = lb.pack_signs(torch.from_numpy(M).cuda(), axis, ld)
+    torch.cuda.synchronize()
+    want = oracle.pack_signs(M, axis, ld)
+    got = got.cpu().numpy().view(np.uint32)
+    assert got.shape == want.shape and np.array_equal(got, want), case
+
+
+def _noalloc_cases(seed=20261212, n=16):
+    rng = np.random.default_rng(seed)
+    paths = ["auto", "decode", "valu", "prefill"]
+    cases = []
+    while len(cases) < n:
+        path = paths[len(cases) % 4]
+        d_in, d_out = max(1, _dim(rng)), max(1, _dim(rng))
+        P = int(rng.integers(1, 3))
+        r_p = int(rng.choice([rng.integers(1, 40), rng.integers(40, 400)]))
+        T1 = int(rng.integers(2, 33)) if path in ("decode", "valu") else int(rng.integers(2, 300))
+        T2 = int(rng.integers(1, T1))
+        y_dt = "bf16" if path == "prefill" else str(rng.choice(["f32", "bf16"]))
+        cases.append((len(cases), path, d_in, d_out, r_p, P, T1, T2, y_dt))
+    return cases
+
+
+NOALLOC = _noalloc_cases()
+
+
+@pytest.mark.parametrize("case", NOALLOC, ids=lambda c: "%d-%s-%dx%d-r%dx%d-T%d-then-%d-%s" % c)
+def test_noalloc_sweep(case):
+    """lb_linear_forward_noalloc bit for bit equal to lb_linear_forward with
+    a caller workspace, on two calls in a row (the second with fewer tokens);
+    a request may be refused (LB_EWORKSPACE) only when its workspace can
+    exceed the fixed one."""
+    torch = torch_or_skip()
+    import binarized_rank_linear_amd as lb
+    i, path, d_in, d_out, r_p, P, T1, T2, y_dt = case
+    inp = _inputs(1800 + i, d_in, d_out, r_p, P, i % 3 == 2)
+    layer = dev_layer(inp)
+    od = torch.float32 if y_dt == "f32" else torch.bfloat16
+    bits = (lambda t: t.view(torch.int16)) if od == torch.bfloat16 else (lambda t: t.view(torch.int32))
+    for k, T in enumerate((T1, T2)):
+        say("noalloc sweep", case, "call", k)
+        x = x_to_dev(synth.activations(1900 + 2 * i + k, T, d_in, "bf16"))
+        want = lb.linear_forward(x, layer, od, PATH_FLAG[path])
+        got = torch.full((T, d_out), float("nan"), dtype=od, device="cuda")
+        try:
+            lb.linear_forward_noalloc(x, layer, od, PATH_FLAG[path], out=got)
+        except lb.LBError as e:
+            # refused only when the request's workspace can exceed the fixed one
+            assert e.status == lb.LB_EWORKSPACE, (case, k, e.status)
+            assert lb.linear_workspace_bytes(layer, T, PATH_FLAG[path]) > lb.NOALLOC_SCRATCH_BYTES, (case, k)
+            continue
+        torch.cuda.synchronize()
+        assert torch.equal(bits(got), bits(want)), (case, k)
