@@ -169,7 +169,12 @@ typedef struct lb_factors {
 } lb_factors;
 
 /* Workspace bytes lb_linear_forward needs for these sizes and flags
- * (latent partial sums, the rank-r intermediate).  0 on bad arguments. */
+ * (latent partial sums, the rank-r intermediate): the most that any path a
+ * call of these sizes may take needs, for either activation and output dtype
+ * and for any pointers (AUTO, for example, sends a shape or a pointer the
+ * GEMM kernels do not take to the decode or vector-ALU kernels).  Enough for
+ * every lb_linear_forward, lb_linear_stage1 and lb_linear_stage2 call of these
+ * sizes and flags.  0 on bad arguments. */
 size_t lb_linear_workspace_bytes(int64_t d_in, int64_t d_out, int64_t r, int64_t T,
                                  int residual, unsigned flags);
 
