@@ -227,6 +227,13 @@ size_t lb_linear_workspace_bytes(int64_t d_in, int64_t d_out, int64_t r, int64_t
                 if (choose_path(flags, T, yd, &p, with_shape ? &a : nullptr)) continue;
                 size_t b = path_workspace(p, a);
                 if (p == Path::MfmaDecode) b = std::max(b, path_workspace(Path::Valu, a));
+                // a misaligned x or g at run time sends AUTO's GEMM requests of
+                // up to kDecodeMaxT tokens to the decode kernels
+                if (p == Path::Gemm && (flags & LB_PATH_MASK) == LB_PATH_AUTO && T <= kDecodeMaxT) {
+                    if (mfma_decode_supported(T, yd) && mfma_decode_shape_ok(a))
+                        b = std::max(b, path_workspace(Path::MfmaDecode, a));
+                    b = std::max(b, path_workspace(Path::Valu, a));
+                }
                 if (b > need) need = b;
             }
         }

@@ -160,6 +160,9 @@ def test_workspace_query_covers_every_path_a_call_can_take():
             if lb.linear_path(d_in, d_out, r, T, bool(res), bf, bf) == flags or \
                     lb.linear_path(d_in, d_out, r, T, bool(res), f32, f32) == flags:
                 assert auto >= forced, (d_in, d_out, r, T, res, flags, auto, forced)
+        if 9 <= T <= 32:
+            # a misaligned x sends even a d_in the GEMM kernels take to the decode kernels
+            assert auto >= L.lb_linear_workspace_bytes(d_in, d_out, r, T, res, lb.LB_PATH_DECODE), (d_in, T)
 
 
 def test_mlp_checks_x_and_y_at_the_block_width():
